@@ -1,0 +1,259 @@
+"""Plain fp64 CPU oracle for the large-chunk TTT-KVB layer and its linear reduction.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import or call this module: only the
+tests, the smoke check and the CPU-baseline leg of the benchmark do.  It shares no code with the
+HIP library and imports nothing from it.
+
+Sources (cited by title and equation; "LaCT notes" is the PaperTrace page
+"5.2.1 LaCT and TTT-E2E", "TTT-as-LA" is the paper "Test-Time Training with KV Binding Is
+Secretly Linear Attention", "LA-to-TTT" is the blog post "From Linear Attention to Test-Time
+Training"):
+
+* chunk update g = grad_W sum_i eta_i L(f_W(k_i), v_i) ........ LaCT notes, Eq. (2)
+* apply o_i = f_W(q_i), all queries of a chunk share one W ...... LaCT notes, text after Eq. (2)
+* f_W(x) = W2 [SiLU(W1 x) o (W3 x)], bias-free SwiGLU ........... LaCT notes, Eq. (3)
+* L(f_W(k), v) = -f_W(k)^T v ..................................... LaCT notes, Eq. (4);
+                                                                   TTT-as-LA, App. E.2
+* W <- L2-Normalize(W - g), along the input dimension ........... LaCT notes, Eq. (5)
+* W <- L2-Normalize(W - Muon(g)), Newton-Schulz, per matrix ..... LaCT notes, Eq. (6)
+* momentum M <- beta M + sum_i eta_i grad L_i, Muon applied to M  LaCT notes, text after Eq. (6)
+* the four update/apply orders and their masks ................... LaCT notes, section 1.1
+* apply-then-update recurrence O_j, G_j, W_j ..................... LaCT notes, Eq. (10)
+* linear bias-free fast weight + GD = linear attention ........... TTT-as-LA, Thm. 5.2 and
+                                                                   Sec. 6.1 Step 6; LA-to-TTT,
+                                                                   "Causal Linear Attention"
+
+Readings taken where the pages are silent or garbled (each is also listed in the design notes):
+
+* orientation: W1, W3 are m x d (gate, up), W2 is d x m (down); tokens are rows, so a chunk's
+  outputs are rows of f applied to rows of Q;
+* mask "chunk = whole sequence" is taken as update-then-apply with one chunk (the only reading
+  that mixes tokens bidirectionally); STRIDED is apply-then-update that skips the update on
+  chunks whose flag is 0;
+* L2-Normalize scales each row (one output unit over its input dimension) to unit norm,
+  w / max(||w||_2, 1e-6); W0 is used as given;
+* Muon is the cubic Newton-Schulz polar iteration X <- 1.5 X - 0.5 (X X^T) X, started from
+  U / (||U||_F + 1e-7) and run on the side with the smaller Gram matrix;
+* eta sits inside the gradient sum (before Muon); the gradient is a sum (not a mean) over the
+  chunk; momentum is per chunk with M0 = 0 and no dampening;
+* a partial last chunk (N not a multiple of the chunk) simply holds fewer tokens.
+
+Parity status: every function here is pinned by the CPU tests (finite differences, closed forms
+of the linear and last-layer reductions, the SVD polar factor, invariants).  The full SwiGLU
+L2 / Muon recurrences have no closed form; they are pinned through their separately pinned parts.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# mask orders (LaCT notes, section 1.1)
+MASK_FULL = 0                # chunk = whole sequence, update then apply -> bidirectional
+MASK_UPDATE_THEN_APPLY = 1   # block-causal, own chunk visible
+MASK_APPLY_THEN_UPDATE = 2   # only earlier chunks visible (Eq. (10), language modelling)
+MASK_STRIDED = 3             # update on flagged chunks only, apply on all
+MASK_TOKEN_CAUSAL = 4        # linear model only: every token sees itself and all earlier tokens
+
+# update rules
+UPD_GD = 0        # W <- W - U (no normalisation)
+UPD_GD_L2 = 1     # Eq. (5)
+UPD_MUON_L2 = 2   # Eq. (6)
+
+ROW_NORM_EPS = 1e-6
+NS_EPS = 1e-7
+
+
+def _f64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def sigmoid(x):
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def silu(x):
+    """SiLU(a) = a * sigmoid(a)."""
+    return x * sigmoid(x)
+
+
+def swiglu_apply(W1, W3, W2, X):
+    """Rows of f_W(X) for the bias-free SwiGLU fast weight, LaCT notes Eq. (3).
+
+    X is [n, d]; W1, W3 are [m, d]; W2 is [d, m].  Returns [n, d].
+    """
+    A = X @ W1.T
+    C = X @ W3.T
+    return (silu(A) * C) @ W2.T
+
+
+def chunk_gradients(W1, W3, W2, K, V, eta):
+    """Gradients of sum_i eta_i * (-f_W(k_i)^T v_i) w.r.t. W1, W3, W2 (LaCT notes Eqs. (2)-(4)).
+
+    The loss derivative w.r.t. f_W(k_i) is -eta_i v_i (TTT-as-LA App. E.2); the rest is the
+    chain rule through W2, the product and the SiLU.  Returns (G1, G3, G2) with the shapes of
+    (W1, W3, W2).
+    """
+    A = K @ W1.T                   # [b, m] pre-activation of the gate
+    C = K @ W3.T                   # [b, m] up projection
+    s = sigmoid(A)
+    Hk = A * s * C                 # hidden features of the keys
+    Df = -eta[:, None] * V         # dLoss/df(k_i), [b, d]
+    G2 = Df.T @ Hk                 # [d, m]
+    DH = Df @ W2                   # dLoss/dH, [b, m]
+    dsilu = s * (1.0 + A * (1.0 - s))
+    G1 = (DH * C * dsilu).T @ K    # [m, d]
+    G3 = (DH * A * s).T @ K        # [m, d]
+    return G1, G3, G2
+
+
+def l2_normalize_rows(W, eps=ROW_NORM_EPS):
+    """L2-Normalize of LaCT notes Eq. (5): each row (an output unit over its inputs) to unit norm."""
+    n = np.sqrt(np.sum(W * W, axis=1, keepdims=True))
+    return W / np.maximum(n, eps)
+
+
+def newton_schulz(U, iters, eps=NS_EPS):
+    """Muon(U) of LaCT notes Eq. (6): the cubic Newton-Schulz approximation of the polar factor.
+
+    X0 = U / (||U||_F + eps); then `iters` times X <- 1.5 X - 0.5 (X X^T) X on the side whose Gram
+    matrix is smaller (U is transposed first when it has more rows than columns, and back after).
+    """
+    U = _f64(U)
+    tr = U.shape[0] > U.shape[1]
+    X = U.T if tr else U
+    X = X / (np.sqrt(np.sum(X * X)) + eps)
+    for _ in range(iters):
+        X = 1.5 * X - 0.5 * ((X @ X.T) @ X)
+    return X.T if tr else X
+
+
+def chunk_bounds(N, chunk):
+    """Token ranges [lo, hi) of the chunks; the last one may be shorter."""
+    return [(lo, min(lo + chunk, N)) for lo in range(0, N, chunk)]
+
+
+def _weight_update(W, G, Mx, rule, ns_iters, momentum):
+    """One fast-weight update of one matrix: optional momentum, optional Muon, W - U, optional norm."""
+    U = G
+    if momentum != 0.0:
+        Mx = momentum * Mx + G
+        U = Mx
+    if rule == UPD_MUON_L2:
+        U = newton_schulz(U, ns_iters)
+    W = W - U
+    if rule in (UPD_GD_L2, UPD_MUON_L2):
+        W = l2_normalize_rows(W)
+    return W, Mx
+
+
+def ttt_scan_ref(q, k, v, eta, W1, W3, W2, chunk, mask, rule, ns_iters=5, momentum=0.0,
+                 last_layer_only=False, update_chunks=None, M=None):
+    """One (batch, head) scan of the TTT-KVB layer.
+
+    q, k, v [N, d]; eta [N]; W1, W3 [m, d]; W2 [d, m]; M optional (M1, M3, M2) momentum state.
+    Returns (o [N, d], (W1, W3, W2), (M1, M3, M2)).  The apply/update order per chunk follows
+    LaCT notes section 1.1 and Eq. (10).
+    """
+    q, k, v, eta = _f64(q), _f64(k), _f64(v), _f64(eta)
+    W = [_f64(W1).copy(), _f64(W3).copy(), _f64(W2).copy()]
+    N, d = q.shape
+    if M is None:
+        Ms = [np.zeros_like(W[0]), np.zeros_like(W[1]), np.zeros_like(W[2])]
+    else:
+        Ms = [_f64(x).copy() for x in M]
+    o = np.zeros((N, W[2].shape[0]))
+    bounds = chunk_bounds(N, chunk)
+    if mask == MASK_FULL and len(bounds) > 1:
+        raise ValueError("MASK_FULL needs chunk >= N")
+    if mask == MASK_TOKEN_CAUSAL:
+        raise ValueError("MASK_TOKEN_CAUSAL is defined for the linear model only")
+    for j, (lo, hi) in enumerate(bounds):
+        update = True
+        if mask == MASK_STRIDED:
+            update = bool(update_chunks[j])
+        apply_first = mask in (MASK_APPLY_THEN_UPDATE, MASK_STRIDED)
+        if apply_first:
+            o[lo:hi] = swiglu_apply(W[0], W[1], W[2], q[lo:hi])
+        if update:
+            G = chunk_gradients(W[0], W[1], W[2], k[lo:hi], v[lo:hi], eta[lo:hi])
+            which = (2,) if last_layer_only else (0, 1, 2)
+            for i in which:
+                W[i], Ms[i] = _weight_update(W[i], G[i], Ms[i], rule, ns_iters, momentum)
+        if not apply_first:
+            o[lo:hi] = swiglu_apply(W[0], W[1], W[2], q[lo:hi])
+    return o, tuple(W), tuple(Ms)
+
+
+def ttt_forward_ref(q, k, v, eta, W1, W3, W2, chunk, mask, rule, ns_iters=5, momentum=0.0,
+                    last_layer_only=False, update_chunks=None, M=None, slices=None):
+    """The TTT-KVB layer over [B, H, N, d] inputs; every (batch, head) scan is independent.
+
+    W1, W3, W2 are per head ([H, ...]) or per (batch, head) ([B, H, ...]).  M, if given, is a
+    tuple of three [B, H, ...] momentum arrays.  ``slices`` restricts the work to a list of
+    (b, h) pairs (the other outputs stay zero).  Returns (o, (W1, W3, W2), (M1, M3, M2)) with
+    [B, H, ...] weight and momentum stacks.
+    """
+    B, H, N, d = q.shape
+    m = W1.shape[-2]
+    o = np.zeros((B, H, N, d))
+    Wo = [np.zeros((B, H, m, d)), np.zeros((B, H, m, d)), np.zeros((B, H, d, m))]
+    Mo = [np.zeros_like(x) for x in Wo]
+    todo = [(b, h) for b in range(B) for h in range(H)] if slices is None else list(slices)
+    for b, h in todo:
+        ws = [x[h] if x.ndim == 3 else x[b, h] for x in (W1, W3, W2)]
+        Mi = None if M is None else tuple(x[b, h] for x in M)
+        ob, Wb, Mb = ttt_scan_ref(q[b, h], k[b, h], v[b, h], eta[b, h], *ws, chunk, mask, rule,
+                                  ns_iters, momentum, last_layer_only, update_chunks, Mi)
+        o[b, h] = ob
+        for i in range(3):
+            Wo[i][b, h] = Wb[i]
+            Mo[i][b, h] = Mb[i]
+    return o, tuple(Wo), tuple(Mo)
+
+
+def linattn_scan_ref(q, k, v, eta, S0, chunk, mask, update_chunks=None):
+    """One (batch, head) scan of the linear fast weight trained by plain GD on the dot-product loss.
+
+    With f_S(x) = S x (S is d_v x d_k), L = -(S k)^T v gives grad = -v k^T, so one chunk's GD step
+    is S <- S + sum_i eta_i v_i k_i^T (TTT-as-LA Thm. 5.2, Sec. 6.1 Step 6).  The apply/update
+    order per chunk is the same as the SwiGLU layer's; MASK_TOKEN_CAUSAL is the one-token-chunk
+    update-then-apply limit (LA-to-TTT, "Causal Linear Attention").  Returns (o, S).
+    """
+    q, k, v, eta = _f64(q), _f64(k), _f64(v), _f64(eta)
+    S = _f64(S0).copy()
+    N = q.shape[0]
+    o = np.zeros((N, S.shape[0]))
+    if mask == MASK_TOKEN_CAUSAL:
+        chunk = 1
+        mask = MASK_UPDATE_THEN_APPLY
+    bounds = chunk_bounds(N, chunk)
+    if mask == MASK_FULL and len(bounds) > 1:
+        raise ValueError("MASK_FULL needs chunk >= N")
+    for j, (lo, hi) in enumerate(bounds):
+        update = True if mask != MASK_STRIDED else bool(update_chunks[j])
+        apply_first = mask in (MASK_APPLY_THEN_UPDATE, MASK_STRIDED)
+        if apply_first:
+            o[lo:hi] = q[lo:hi] @ S.T
+        if update:
+            S = S + (eta[lo:hi, None] * v[lo:hi]).T @ k[lo:hi]
+        if not apply_first:
+            o[lo:hi] = q[lo:hi] @ S.T
+    return o, S
+
+
+def linattn_forward_ref(q, k, v, eta, chunk, mask, S0=None, update_chunks=None, slices=None):
+    """Linear attention over [B, H, N, d] inputs.  S0 is [B, H, d_v, d_k] or None (zeros)."""
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    o = np.zeros((B, H, N, dv))
+    S = np.zeros((B, H, dv, dk))
+    todo = [(b, h) for b in range(B) for h in range(H)] if slices is None else list(slices)
+    for b, h in todo:
+        s0 = np.zeros((dv, dk)) if S0 is None else S0[b, h]
+        o[b, h], S[b, h] = linattn_scan_ref(q[b, h], k[b, h], v[b, h], eta[b, h], s0, chunk, mask,
+                                            update_chunks)
+    return o, S
+
+
+def gemm_intensity(h, b):
+    """LaCT notes Eq. (1): FLOP per byte of an h x h bf16 weight times a b x h chunk."""
+    return (2.0 * h * h * b) / (2.0 * h * h + 4.0 * h * b)

@@ -1,0 +1,122 @@
+"""Seeded synthetic inputs for the large-chunk TTT-KVB layer and chunked linear attention.
+
+This module only draws random numbers and rounds them to the storage precision.  It contains
+none of the layer's arithmetic, so both the fp64 CPU oracle and the HIP path can be fed from it
+without sharing any compute code.
+
+Recipe (per (batch, head) slice, so any slice can be regenerated on its own):
+  * ``numpy.random.default_rng([seed, b, h])`` draws, in this order, q, k, v as
+    N(0, 1) / sqrt(d) arrays of shape [N, d], then one standard-normal ``eta_raw`` per token;
+  * eta = 0.01 * softplus(eta_raw) (LaCT layer workloads) or 0.05 * sigmoid(eta_raw)
+    (linear-attention workload); eta is a per-token, per-head learning rate, kept in fp32;
+  * the initial fast weights of head h come from ``default_rng([seed, 10**6 + h])``, drawing
+    W1 (m x d), W3 (m x d), W2 (d x m) with entries N(0, 1/d), stored fp32;
+  * q, k, v are rounded once, round-to-nearest-even, to bfloat16 when the workload runs in bf16;
+    the rounded values (held in float32 arrays) are what every consumer sees.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "round_to_bf16",
+    "bf16_bits",
+    "slice_inputs",
+    "head_weights",
+    "make_ttt_inputs",
+    "make_linattn_inputs",
+]
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even); returns float32 holding them."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    bits = x.view(np.uint32)
+    # add 0x7FFF plus the lowest kept bit, then truncate: the usual RNE for 16 dropped bits
+    rounded = (bits + np.uint32(0x7FFF) + ((bits >> np.uint32(16)) & np.uint32(1))) & np.uint32(0xFFFF0000)
+    out = rounded.view(np.float32).copy()
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = np.float32("nan")
+    return out
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """The upper 16 bits of float32 values that are already bf16-representable."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    return (x.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def _softplus(x: np.ndarray) -> np.ndarray:
+    return np.logaddexp(0.0, x)
+
+
+def _sigmoid(x: np.ndarray) -> np.ndarray:
+    return 0.5 * (1.0 + np.tanh(0.5 * x))
+
+
+def slice_inputs(seed: int, b: int, h: int, N: int, d_k: int, d_v: int | None = None,
+                 eta_kind: str = "softplus", eta_scale: float = 0.01, bf16: bool = True):
+    """q, k [N, d_k], v [N, d_v] and eta [N] for one (batch, head) slice."""
+    d_v = d_k if d_v is None else d_v
+    rng = np.random.default_rng([seed, b, h])
+    q = (rng.standard_normal((N, d_k), dtype=np.float32) / np.float32(np.sqrt(d_k))).astype(np.float32)
+    k = (rng.standard_normal((N, d_k), dtype=np.float32) / np.float32(np.sqrt(d_k))).astype(np.float32)
+    v = (rng.standard_normal((N, d_v), dtype=np.float32) / np.float32(np.sqrt(d_k))).astype(np.float32)
+    raw = rng.standard_normal(N).astype(np.float32)
+    if eta_kind == "softplus":
+        eta = (eta_scale * _softplus(raw.astype(np.float64))).astype(np.float32)
+    elif eta_kind == "sigmoid":
+        eta = (eta_scale * _sigmoid(raw.astype(np.float64))).astype(np.float32)
+    elif eta_kind == "const":
+        eta = np.full(N, eta_scale, dtype=np.float32)
+    else:
+        raise ValueError(f"unknown eta_kind {eta_kind!r}")
+    if bf16:
+        q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
+    return q, k, v, eta
+
+
+def head_weights(seed: int, h: int, d: int, m: int):
+    """Initial fast weights W1 (m x d), W3 (m x d), W2 (d x m) of head h, entries N(0, 1/d), fp32."""
+    rng = np.random.default_rng([seed, 10**6 + h])
+    s = np.float32(1.0 / np.sqrt(d))
+    W1 = (rng.standard_normal((m, d), dtype=np.float32) * s).astype(np.float32)
+    W3 = (rng.standard_normal((m, d), dtype=np.float32) * s).astype(np.float32)
+    W2 = (rng.standard_normal((d, m), dtype=np.float32) * s).astype(np.float32)
+    return W1, W3, W2
+
+
+def make_ttt_inputs(seed: int, B: int, H: int, N: int, d: int, m: int, bf16: bool = True,
+                    eta_kind: str = "softplus", eta_scale: float = 0.01, slices=None):
+    """Full [B, H, N, d] q, k, v, [B, H, N] eta and per-head W1, W3, W2 stacks [H, ...].
+
+    ``slices`` optionally restricts generation to a list of (b, h) pairs (others stay zero);
+    every generated slice is identical to the one a full generation would give.
+    """
+    q = np.zeros((B, H, N, d), np.float32)
+    k = np.zeros_like(q)
+    v = np.zeros_like(q)
+    eta = np.zeros((B, H, N), np.float32)
+    todo = [(b, h) for b in range(B) for h in range(H)] if slices is None else list(slices)
+    for b, h in todo:
+        q[b, h], k[b, h], v[b, h], eta[b, h] = slice_inputs(seed, b, h, N, d, d, eta_kind, eta_scale, bf16)
+    W1 = np.zeros((H, m, d), np.float32)
+    W3 = np.zeros((H, m, d), np.float32)
+    W2 = np.zeros((H, d, m), np.float32)
+    for h in range(H):
+        W1[h], W3[h], W2[h] = head_weights(seed, h, d, m)
+    return q, k, v, eta, W1, W3, W2
+
+
+def make_linattn_inputs(seed: int, B: int, H: int, N: int, d_k: int, d_v: int, bf16: bool = True,
+                        eta_kind: str = "sigmoid", eta_scale: float = 0.05, slices=None):
+    """q, k [B, H, N, d_k], v [B, H, N, d_v], eta [B, H, N] for the linear-attention workload."""
+    q = np.zeros((B, H, N, d_k), np.float32)
+    k = np.zeros_like(q)
+    v = np.zeros((B, H, N, d_v), np.float32)
+    eta = np.zeros((B, H, N), np.float32)
+    todo = [(b, h) for b in range(B) for h in range(H)] if slices is None else list(slices)
+    for b, h in todo:
+        q[b, h], k[b, h], v[b, h], eta[b, h] = slice_inputs(seed, b, h, N, d_k, d_v, eta_kind, eta_scale, bf16)
+    return q, k, v, eta

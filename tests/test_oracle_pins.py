@@ -1,0 +1,439 @@
+"""Pins of the fp64 oracle against what the pages and mathematics fix (CPU only).
+
+Every expected value here is computed by a route independent of the oracle's own formulas:
+per-token scalar loops of Eq. (3), central finite differences of the Eq. (2)/(4) loss, the SVD
+of the matrix for Newton-Schulz, and the closed forms of the linear and last-layer reductions
+(TTT-as-LA Thm. 5.2/5.3, App. H).  A dropped term, a flipped sign, a wrong index or a transposed
+operand in the oracle fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------------------------------------
+# independent helpers (scalar loops, finite differences, SVD)
+
+def f_token(W1, W3, W2, x):
+    """f_W(x) = W2 [SiLU(W1 x) o (W3 x)] by explicit loops (LaCT notes Eq. (3))."""
+    m, d = W1.shape
+    hid = []
+    for r in range(m):
+        a = sum(W1[r, c] * x[c] for c in range(d))
+        u = sum(W3[r, c] * x[c] for c in range(d))
+        hid.append(a / (1.0 + math.exp(-a)) * u)
+    return np.array([sum(W2[e, r] * hid[r] for r in range(m)) for e in range(W2.shape[0])])
+
+
+def chunk_loss(W1, W3, W2, K, V, eta):
+    """sum_i eta_i * L(f_W(k_i), v_i) with L = -f^T v (LaCT notes Eqs. (2), (4))."""
+    tot = 0.0
+    for i in range(K.shape[0]):
+        f = f_token(W1, W3, W2, K[i])
+        tot += eta[i] * (-float(np.dot(f, V[i])))
+    return tot
+
+
+def fd_gradients(W1, W3, W2, K, V, eta, h=1e-5):
+    Ws = [W1.copy(), W3.copy(), W2.copy()]
+    grads = []
+    for wi in range(3):
+        g = np.zeros_like(Ws[wi])
+        for idx in np.ndindex(*Ws[wi].shape):
+            old = Ws[wi][idx]
+            Ws[wi][idx] = old + h
+            lp = chunk_loss(*Ws, K, V, eta)
+            Ws[wi][idx] = old - h
+            lm = chunk_loss(*Ws, K, V, eta)
+            Ws[wi][idx] = old
+            g[idx] = (lp - lm) / (2 * h)
+        grads.append(g)
+    return grads  # G1, G3, G2
+
+
+def ns_via_svd(U, iters, eps=1e-7):
+    """Newton-Schulz written on the singular values: U = P diag(s) Q^T, and the cubic
+    x <- 1.5 x - 0.5 x^3 acts on each normalised singular value separately."""
+    P, s, Qt = np.linalg.svd(U, full_matrices=False)
+    x = s / (np.sqrt(np.sum(s * s)) + eps)
+    for _ in range(iters):
+        x = 1.5 * x - 0.5 * x ** 3
+    return (P * x) @ Qt
+
+
+def rownorm_loops(W, eps=1e-6):
+    out = np.empty_like(W)
+    for r in range(W.shape[0]):
+        n = math.sqrt(sum(float(w) * float(w) for w in W[r]))
+        out[r] = W[r] / max(n, eps)
+    return out
+
+
+def rel(a, b):
+    return float(np.linalg.norm(np.asarray(a) - np.asarray(b)) / max(np.linalg.norm(np.asarray(b)), 1e-300))
+
+
+def tiny_problem(seed, N=8, d=4, m=6, eta_scale=0.3):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((N, d)) / math.sqrt(d)
+    k = rng.standard_normal((N, d)) / math.sqrt(d)
+    v = rng.standard_normal((N, d)) / math.sqrt(d)
+    eta = eta_scale * np.log1p(np.exp(rng.standard_normal(N)))
+    W1 = rng.standard_normal((m, d)) / math.sqrt(d)
+    W3 = rng.standard_normal((m, d)) / math.sqrt(d)
+    W2 = rng.standard_normal((d, m)) / math.sqrt(d)
+    return q, k, v, eta, W1, W3, W2
+
+
+# ----------------------------------------------------------------------------------------------
+# Eq. (3) forward and Eqs. (2)/(4) gradients
+
+def test_swiglu_apply_matches_scalar_loops():
+    q, k, v, eta, W1, W3, W2 = tiny_problem(1)
+    got = O.swiglu_apply(W1, W3, W2, q)
+    want = np.stack([f_token(W1, W3, W2, x) for x in q])
+    assert rel(got, want) < 1e-13
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_chunk_gradients_match_finite_differences(seed):
+    q, k, v, eta, W1, W3, W2 = tiny_problem(seed, N=5)
+    eta = eta - 0.1  # includes negative rates (gradient ascent is allowed)
+    G1, G3, G2 = O.chunk_gradients(W1, W3, W2, k, v, eta)
+    F1, F3, F2 = fd_gradients(W1, W3, W2, k, v, eta)
+    assert rel(G1, F1) < 1e-7
+    assert rel(G3, F3) < 1e-7
+    assert rel(G2, F2) < 1e-7
+
+
+def test_last_layer_gradient_closed_form():
+    """TTT-as-LA App. E.2: the last layer's gradient is -phi(K)^T (eta V), phi = SiLU(W1 k) o W3 k."""
+    q, k, v, eta, W1, W3, W2 = tiny_problem(3)
+    phi = np.stack([[a / (1 + math.exp(-a)) * u for a, u in zip(W1 @ x, W3 @ x)] for x in k])
+    want = -(eta[:, None] * v).T @ phi
+    assert rel(O.chunk_gradients(W1, W3, W2, k, v, eta)[2], want) < 1e-13
+
+
+# ----------------------------------------------------------------------------------------------
+# Newton-Schulz (Eq. (6))
+
+def test_newton_schulz_converges_to_polar_factor():
+    rng = np.random.default_rng(7)
+    P, _ = np.linalg.qr(rng.standard_normal((6, 6)))
+    Q, _ = np.linalg.qr(rng.standard_normal((10, 10)))
+    s = np.linspace(1.0, 2.5, 6)
+    U = (P * s) @ Q[:6]
+    want = P @ Q[:6]
+    assert rel(O.newton_schulz(U, 100), want) < 1e-10
+    assert rel(O.newton_schulz(U.T, 100), want.T) < 1e-10
+
+
+@pytest.mark.parametrize("shape", [(5, 9), (9, 5), (7, 7)])
+def test_newton_schulz_five_steps_on_singular_values(shape):
+    rng = np.random.default_rng(11)
+    U = rng.standard_normal(shape)
+    assert rel(O.newton_schulz(U, 5), ns_via_svd(U, 5)) < 1e-12
+    assert rel(O.newton_schulz(U, 1), ns_via_svd(U, 1)) < 1e-13
+
+
+def test_newton_schulz_invariants():
+    rng = np.random.default_rng(5)
+    U = rng.standard_normal((6, 10))
+    base = O.newton_schulz(U, 5)
+    assert rel(O.newton_schulz(3.7 * U, 5), base) < 1e-6  # eps makes scale invariance approximate
+    assert rel(O.newton_schulz(-U, 5), -base) < 1e-14
+    assert rel(O.newton_schulz(U.T, 5), base.T) < 1e-13
+    P, _ = np.linalg.qr(rng.standard_normal((6, 6)))
+    Q, _ = np.linalg.qr(rng.standard_normal((10, 10)))
+    assert rel(O.newton_schulz(P @ U @ Q, 5), P @ base @ Q) < 1e-12
+    assert np.all(O.newton_schulz(np.zeros((3, 4)), 5) == 0.0)
+
+
+# ----------------------------------------------------------------------------------------------
+# L2-Normalize (Eq. (5))
+
+def test_l2_normalize_rows_definition():
+    rng = np.random.default_rng(2)
+    W = rng.standard_normal((5, 7))
+    got = O.l2_normalize_rows(W)
+    assert rel(got, rownorm_loops(W)) < 1e-14
+    assert np.allclose(np.linalg.norm(got, axis=1), 1.0, atol=1e-14)
+    assert rel(O.l2_normalize_rows(got), got) < 1e-14
+    # columns are not normalised
+    assert not np.allclose(np.linalg.norm(got, axis=0), 1.0)
+
+
+# ----------------------------------------------------------------------------------------------
+# an independent stepper: FD gradients + SVD Newton-Schulz + loop row norms, following the
+# order of the mask (LaCT notes section 1.1, Eq. (10))
+
+def stepper(q, k, v, eta, W1, W3, W2, chunk, mask, rule, ns_iters=5, beta=0.0, last_only=False,
+            upd=None):
+    W = [W1.copy(), W3.copy(), W2.copy()]
+    M = [np.zeros_like(x) for x in W]
+    N = q.shape[0]
+    o = np.zeros((N, W2.shape[0]))
+    for j, lo in enumerate(range(0, N, chunk)):
+        hi = min(lo + chunk, N)
+        first = mask in (O.MASK_APPLY_THEN_UPDATE, O.MASK_STRIDED)
+        if first:
+            o[lo:hi] = np.stack([f_token(*W, x) for x in q[lo:hi]])
+        if mask != O.MASK_STRIDED or upd[j]:
+            G = fd_gradients(*W, k[lo:hi], v[lo:hi], eta[lo:hi])
+            for i in ([2] if last_only else [0, 1, 2]):
+                U = G[i]
+                if beta:
+                    M[i] = beta * M[i] + G[i]
+                    U = M[i]
+                if rule == O.UPD_MUON_L2:
+                    U = ns_via_svd(U, ns_iters)
+                W[i] = W[i] - U
+                if rule != O.UPD_GD:
+                    W[i] = rownorm_loops(W[i])
+        if not first:
+            o[lo:hi] = np.stack([f_token(*W, x) for x in q[lo:hi]])
+    return o, W, M
+
+
+CASES = [
+    # (mask, rule, beta, last_only, chunk)
+    (O.MASK_APPLY_THEN_UPDATE, O.UPD_GD_L2, 0.0, False, 3),
+    (O.MASK_APPLY_THEN_UPDATE, O.UPD_MUON_L2, 0.9, False, 3),
+    (O.MASK_APPLY_THEN_UPDATE, O.UPD_GD, 0.0, False, 4),
+    (O.MASK_UPDATE_THEN_APPLY, O.UPD_GD_L2, 0.0, False, 3),
+    (O.MASK_UPDATE_THEN_APPLY, O.UPD_MUON_L2, 0.0, True, 3),
+    (O.MASK_STRIDED, O.UPD_MUON_L2, 0.0, False, 3),
+    (O.MASK_FULL, O.UPD_GD_L2, 0.0, False, 8),
+]
+
+
+@pytest.mark.parametrize("mask,rule,beta,last_only,chunk", CASES)
+def test_scan_matches_independent_stepper(mask, rule, beta, last_only, chunk):
+    q, k, v, eta, W1, W3, W2 = tiny_problem(21, N=8)
+    upd = [1, 1, 0] if mask == O.MASK_STRIDED else None
+    o, W, M = O.ttt_scan_ref(q, k, v, eta, W1, W3, W2, chunk, mask, rule, 5, beta, last_only, upd)
+    o2, W2s, M2 = stepper(q, k, v, eta, W1, W3, W2, chunk, mask, rule, 5, beta, last_only, upd)
+    assert rel(o, o2) < 1e-6
+    for a, b in zip(W, W2s):
+        assert rel(a, b) < 1e-6
+    if beta:
+        for a, b in zip(M, M2):
+            assert rel(a, b) < 1e-6
+
+
+def test_first_chunk_apply_then_update_uses_initial_weights():
+    q, k, v, eta, W1, W3, W2 = tiny_problem(4, N=8)
+    o, _, _ = O.ttt_scan_ref(q, k, v, eta, W1, W3, W2, 4, O.MASK_APPLY_THEN_UPDATE, O.UPD_GD_L2)
+    want = np.stack([f_token(W1, W3, W2, x) for x in q[:4]])
+    assert rel(o[:4], want) < 1e-13
+
+
+def test_l2_rows_unit_after_update():
+    q, k, v, eta, W1, W3, W2 = tiny_problem(6, N=8)
+    _, W, _ = O.ttt_scan_ref(q, k, v, eta, W1, W3, W2, 4, O.MASK_APPLY_THEN_UPDATE, O.UPD_GD_L2)
+    assert np.allclose(np.linalg.norm(W[0], axis=1), 1.0, atol=1e-14)  # W1 rows over d
+    assert np.allclose(np.linalg.norm(W[1], axis=1), 1.0, atol=1e-14)  # W3 rows over d
+    assert np.allclose(np.linalg.norm(W[2], axis=1), 1.0, atol=1e-14)  # W2 rows over m
+
+
+# ----------------------------------------------------------------------------------------------
+# closed forms of the reductions (TTT-as-LA Thm. 5.2 / 5.3, App. H)
+
+def visible(t, s, chunk, mask, upd=None):
+    """Does token s's key/value reach token t's output under the mask?"""
+    ct, cs = t // chunk, s // chunk
+    if mask == O.MASK_FULL:
+        return True
+    if mask == O.MASK_TOKEN_CAUSAL:
+        return s <= t
+    if mask == O.MASK_UPDATE_THEN_APPLY:
+        return cs <= ct
+    if mask == O.MASK_APPLY_THEN_UPDATE:
+        return cs < ct
+    if mask == O.MASK_STRIDED:
+        return cs < ct and bool(upd[cs])
+    raise ValueError
+
+
+@pytest.mark.parametrize("mask,chunk,N", [
+    (O.MASK_APPLY_THEN_UPDATE, 4, 13), (O.MASK_UPDATE_THEN_APPLY, 4, 13), (O.MASK_TOKEN_CAUSAL, 4, 13),
+    (O.MASK_FULL, 13, 13), (O.MASK_STRIDED, 4, 16), (O.MASK_APPLY_THEN_UPDATE, 1, 6),
+])
+def test_linear_model_closed_form(mask, chunk, N):
+    """o_t = S0 q_t + sum_{s visible} eta_s v_s (k_s . q_t)  (Thm. 5.2; LA-to-TTT causal form)."""
+    rng = np.random.default_rng(N + chunk + mask)
+    dk, dv = 3, 5
+    q = rng.standard_normal((N, dk))
+    k = rng.standard_normal((N, dk))
+    v = rng.standard_normal((N, dv))
+    eta = rng.standard_normal(N)
+    S0 = rng.standard_normal((dv, dk))
+    upd = [1, 0, 1, 0] if mask == O.MASK_STRIDED else None
+    o, S = O.linattn_scan_ref(q, k, v, eta, S0, chunk, mask, upd)
+    for t in range(N):
+        want = [sum(S0[e, c] * q[t, c] for c in range(dk)) for e in range(dv)]
+        for s in range(N):
+            if visible(t, s, chunk, mask, upd):
+                dot = sum(k[s, c] * q[t, c] for c in range(dk))
+                for e in range(dv):
+                    want[e] += eta[s] * v[s, e] * dot
+        assert rel(o[t], np.array(want)) < 1e-12
+    # final state sums every updating chunk
+    Sw = S0.copy()
+    for s in range(N):
+        if mask != O.MASK_STRIDED or upd[s // chunk]:
+            Sw += eta[s] * np.outer(v[s], k[s])
+    assert rel(S, Sw) < 1e-12
+
+
+def test_linear_full_mask_is_bidirectional_attention_form():
+    rng = np.random.default_rng(9)
+    N, d = 10, 4
+    q, k, v = rng.standard_normal((3, N, d))
+    eta = rng.random(N)
+    S0 = rng.standard_normal((d, d))
+    o, _ = O.linattn_scan_ref(q, k, v, eta, S0, N, O.MASK_FULL)
+    assert rel(o, q @ S0.T + (q @ k.T) @ (eta[:, None] * v)) < 1e-13
+
+
+def test_linear_sign_flip_negates_accumulated_term():
+    """TTT-as-LA Sec. 5.2: gradient ascent flips the sign of the effective value."""
+    rng = np.random.default_rng(12)
+    q, k, v = rng.standard_normal((3, 12, 4))
+    eta = rng.random(12)
+    S0 = rng.standard_normal((4, 4))
+    o1, _ = O.linattn_scan_ref(q, k, v, eta, S0, 4, O.MASK_APPLY_THEN_UPDATE)
+    o2, _ = O.linattn_scan_ref(q, k, v, -eta, S0, 4, O.MASK_APPLY_THEN_UPDATE)
+    base = q @ S0.T
+    assert rel(o1 - base, -(o2 - base)) < 1e-13
+
+
+def phi_rows(W1, W3, X):
+    return np.stack([[a / (1 + math.exp(-a)) * u for a, u in zip(W1 @ x, W3 @ x)] for x in X])
+
+
+@pytest.mark.parametrize("mask", [O.MASK_APPLY_THEN_UPDATE, O.MASK_UPDATE_THEN_APPLY, O.MASK_FULL])
+@pytest.mark.parametrize("beta", [0.0, 0.9])
+def test_last_layer_gd_momentum_parallel_form(mask, beta):
+    """Static kernel phi, plain GD on the last layer with chunk momentum: the masked parallel form
+    O = phi(Q) W2^T + sum_{i <= J(t)} c(J, i) (phi(Q) phi(K_i)^T) diag(eta_i) V_i with
+    c(J, i) = sum_{j=i..J} beta^(j-i)  (TTT-as-LA Thm. 5.3 / App. H, written per chunk)."""
+    N, chunk = 12, 4
+    if mask == O.MASK_FULL:
+        chunk = N
+    q, k, v, eta, W1, W3, W2 = tiny_problem(30, N=N)
+    o, W, _ = O.ttt_scan_ref(q, k, v, eta, W1, W3, W2, chunk, mask, O.UPD_GD, 5, beta, True)
+    PQ, PK = phi_rows(W1, W3, q), phi_rows(W1, W3, k)
+    want = PQ @ W2.T
+    for t in range(N):
+        J = t // chunk - (1 if mask == O.MASK_APPLY_THEN_UPDATE else 0)
+        for s in range(N):
+            i = s // chunk
+            if i <= J:
+                c = sum(beta ** (j - i) for j in range(i, J + 1))
+                want[t] += c * eta[s] * np.dot(PQ[t], PK[s]) * v[s]
+    assert rel(o, want) < 1e-12
+    assert rel(W[0], W1) == 0.0 and rel(W[1], W3) == 0.0  # only the last layer moves
+
+
+def test_weight_norm_breaks_parallel_form():
+    """Negative control, TTT-as-LA App. I.2: with L2-Normalize the state is not a sum over history."""
+    N, chunk = 12, 4
+    q, k, v, eta, W1, W3, W2 = tiny_problem(31, N=N, eta_scale=2.0)
+    o, _, _ = O.ttt_scan_ref(q, k, v, eta, W1, W3, W2, chunk, O.MASK_APPLY_THEN_UPDATE, O.UPD_GD_L2, 5,
+                             0.0, True)
+    PQ, PK = phi_rows(W1, W3, q), phi_rows(W1, W3, k)
+    par = PQ @ W2.T
+    for t in range(N):
+        for s in range(N):
+            if s // chunk < t // chunk:
+                par[t] += eta[s] * np.dot(PQ[t], PK[s]) * v[s]
+    assert rel(o, par) > 1e-2
+
+
+def test_full_mask_all_layers_gd_is_update_then_apply():
+    """Thm. 5.1 with one chunk: o = W2' phi'(q), where W' = W - G and G is the chunk gradient
+    (taken here by finite differences)."""
+    q, k, v, eta, W1, W3, W2 = tiny_problem(32, N=6)
+    o, W, _ = O.ttt_scan_ref(q, k, v, eta, W1, W3, W2, 6, O.MASK_FULL, O.UPD_GD)
+    G1, G3, G2 = fd_gradients(W1, W3, W2, k, v, eta)
+    want = np.stack([f_token(W1 - G1, W3 - G3, W2 - G2, x) for x in q])
+    assert rel(o, want) < 1e-8
+
+
+# ----------------------------------------------------------------------------------------------
+# order relations, chaining, degenerate cases
+
+def test_update_then_apply_is_apply_then_update_shifted_by_one_chunk():
+    """Both orders share the W_j sequence; UTA reads W_j for chunk j, ATU reads it for chunk j+1."""
+    N, chunk = 12, 4
+    q, k, v, eta, W1, W3, W2 = tiny_problem(33, N=N)
+    o_uta, W_uta, _ = O.ttt_scan_ref(q, k, v, eta, W1, W3, W2, chunk, O.MASK_UPDATE_THEN_APPLY, O.UPD_GD_L2)
+    q_shift = np.concatenate([np.zeros((chunk, q.shape[1])), q[:-chunk]])
+    o_atu, W_atu, _ = O.ttt_scan_ref(q_shift, k, v, eta, W1, W3, W2, chunk, O.MASK_APPLY_THEN_UPDATE,
+                                     O.UPD_GD_L2)
+    assert rel(o_atu[chunk:], o_uta[:-chunk]) < 1e-13
+    for a, b in zip(W_uta, W_atu):
+        assert rel(a, b) < 1e-14
+
+
+@pytest.mark.parametrize("rule,beta", [(O.UPD_GD_L2, 0.0), (O.UPD_MUON_L2, 0.9)])
+def test_two_calls_equal_one(rule, beta):
+    N, chunk = 12, 4
+    q, k, v, eta, W1, W3, W2 = tiny_problem(34, N=N)
+    mask = O.MASK_APPLY_THEN_UPDATE
+    o, W, M = O.ttt_scan_ref(q, k, v, eta, W1, W3, W2, chunk, mask, rule, 5, beta)
+    oa, Wa, Ma = O.ttt_scan_ref(q[:8], k[:8], v[:8], eta[:8], W1, W3, W2, chunk, mask, rule, 5, beta)
+    ob, Wb, Mb = O.ttt_scan_ref(q[8:], k[8:], v[8:], eta[8:], *Wa, chunk, mask, rule, 5, beta, M=Ma)
+    assert rel(np.concatenate([oa, ob]), o) < 1e-14
+    for a, b in zip(Wb, W):
+        assert rel(a, b) < 1e-14
+
+
+def test_strided_degenerate_flags():
+    N, chunk = 12, 4
+    q, k, v, eta, W1, W3, W2 = tiny_problem(35, N=N)
+    o_all, W_all, _ = O.ttt_scan_ref(q, k, v, eta, W1, W3, W2, chunk, O.MASK_STRIDED, O.UPD_GD_L2,
+                                     update_chunks=[1, 1, 1])
+    o_atu, W_atu, _ = O.ttt_scan_ref(q, k, v, eta, W1, W3, W2, chunk, O.MASK_APPLY_THEN_UPDATE, O.UPD_GD_L2)
+    assert rel(o_all, o_atu) == 0.0
+    o_none, W_none, _ = O.ttt_scan_ref(q, k, v, eta, W1, W3, W2, chunk, O.MASK_STRIDED, O.UPD_GD_L2,
+                                       update_chunks=[0, 0, 0])
+    assert rel(o_none, np.stack([f_token(W1, W3, W2, x) for x in q])) < 1e-13
+    assert rel(W_none[2], W2) == 0.0
+
+
+def test_zero_eta_leaves_weights_unchanged_under_gd():
+    q, k, v, eta, W1, W3, W2 = tiny_problem(36, N=8)
+    o, W, _ = O.ttt_scan_ref(q, k, v, 0 * eta, W1, W3, W2, 4, O.MASK_APPLY_THEN_UPDATE, O.UPD_GD)
+    assert rel(W[0], W1) == 0.0 and rel(W[2], W2) == 0.0
+    assert rel(o, np.stack([f_token(W1, W3, W2, x) for x in q])) < 1e-13
+
+
+def test_forward_ref_batches_match_scans():
+    q, k, v, eta, W1, W3, W2 = tiny_problem(37, N=8)
+    Q = np.stack([np.stack([q, k]), np.stack([v, q])])
+    K = np.stack([np.stack([k, v]), np.stack([q, k])])
+    V = np.stack([np.stack([v, q]), np.stack([k, v])])
+    E = np.stack([np.stack([eta, eta[::-1]]), np.stack([eta * 2, eta])])
+    Ws = [np.stack([W, W * 0.5]) for W in (W1, W3, W2)]
+    o, W, _ = O.ttt_forward_ref(Q, K, V, E, *Ws, 4, O.MASK_APPLY_THEN_UPDATE, O.UPD_GD_L2)
+    for b in range(2):
+        for h in range(2):
+            ob, Wb, _ = O.ttt_scan_ref(Q[b, h], K[b, h], V[b, h], E[b, h], Ws[0][h], Ws[1][h], Ws[2][h], 4,
+                                       O.MASK_APPLY_THEN_UPDATE, O.UPD_GD_L2)
+            assert rel(o[b, h], ob) == 0.0
+
+
+def test_eq1_intensity_table():
+    with open(os.path.join(GOLDEN, "eq1_intensity.json")) as f:
+        g = json.load(f)
+    for row in g["rows"]:
+        assert abs(O.gemm_intensity(row["h"], row["b"]) - row["r"]) <= g["rounding"]
