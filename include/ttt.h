@@ -1,0 +1,147 @@
+/*
+ * ttt.h -- C ABI of the MI355X (gfx950) large-chunk TTT-KVB layer and chunked linear attention.
+ *
+ * The layer is the one described in the PaperTrace notes "5.2.1 LaCT and TTT-E2E" (Eqs. (2)-(6)
+ * and (10), section 1.1 on mask orders) and shown to be learned linear attention in
+ * "Test-Time Training with KV Binding Is Secretly Linear Attention" (Thm. 5.1-5.3, Sec. 6.1,
+ * App. E and H).  Per (batch, head) and per chunk of `chunk` tokens it
+ *   - applies the bias-free SwiGLU fast weight f_W(x) = W2 [SiLU(W1 x) o (W3 x)] to the queries
+ *     (Eq. (3); all queries of a chunk see one W),
+ *   - takes the gradient g of sum_i eta_i * (-f_W(k_i)^T v_i) over the chunk (Eqs. (2), (4)),
+ *   - updates W <- W - g, W <- L2-Normalize(W - g) (Eq. (5)) or
+ *     W <- L2-Normalize(W - Muon(g)) (Eq. (6), Newton-Schulz, optional chunk momentum),
+ *   - carries W to the next chunk, in the order the mask selects (section 1.1, Eq. (10)).
+ * linattn_forward computes the linear, bias-free reduction: S <- S + sum_i eta_i v_i k_i^T,
+ * o = S q (paper Thm. 5.2 and Sec. 6.1 Step 6).
+ *
+ * Conventions shared by every entry point
+ *   - Layout: q, k, v, o are [B][H][N][d] row-major (token rows, feature columns); eta is
+ *     [B][H][N] fp32.  A head's fast weight is one fp32 block [W1 | W3 | W2]: W1 and W3 are
+ *     m_h x d_h row-major (output unit, input feature), W2 is d_h x m_h row-major.
+ *     L2-Normalize scales each row (an output unit over its inputs) to unit norm.
+ *   - Memory: every pointer except `desc` and `update_chunks` is a device pointer on the
+ *     current HIP device.  The caller allocates every buffer, including the workspace, and
+ *     keeps it alive until the stream reaches the end of the call; the library allocates no
+ *     device memory and keeps no pointer after a call returns.
+ *   - Streams: work is enqueued on `stream` (a hipStream_t; NULL = the null stream); the call
+ *     returns before the work finishes.
+ *   - Errors: arguments are checked before anything is enqueued, so a call that returns an
+ *     error has written nothing.  A failed launch returns TTT_ERR_DEVICE; a device fault shows
+ *     up at the caller's next synchronisation.  ttt_last_error() gives a message for the
+ *     latest failed call on the calling thread.
+ *   - Aliasing: o must not overlap q, k, v or eta.  W_out may not overlap W0.
+ *   - Thread safety: calls on different streams may run concurrently; the library has no
+ *     mutable global state besides the per-thread error message.
+ */
+#ifndef TTT_MI355X_H
+#define TTT_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TTT_ABI_VERSION 1
+
+typedef enum {
+    TTT_OK = 0,
+    TTT_ERR_INVALID_ARGUMENT = 1, /* a size, pointer, alignment or enum value is out of range     */
+    TTT_ERR_UNSUPPORTED = 2,      /* a valid combination this build does not implement          */
+    TTT_ERR_WORKSPACE = 3,        /* workspace pointer missing or smaller than *_workspace_bytes  */
+    TTT_ERR_DEVICE = 4            /* a HIP call or kernel launch failed                          */
+} ttt_status;
+
+typedef enum { TTT_F32 = 0, TTT_BF16 = 1 } ttt_dtype;
+
+/* The update/apply orders of the notes' section 1.1 ("the order of update and apply decides the
+ * mask").  Chunk j covers tokens [j*chunk, min((j+1)*chunk, N)); the last chunk may be shorter. */
+typedef enum {
+    TTT_MASK_FULL = 0,              /* one chunk (chunk >= N): update, then apply -> bidirectional */
+    TTT_MASK_UPDATE_THEN_APPLY = 1, /* per chunk: update, then apply -> own chunk visible           */
+    TTT_MASK_APPLY_THEN_UPDATE = 2, /* per chunk: apply, then update -> earlier chunks only, Eq.(10)*/
+    TTT_MASK_STRIDED = 3,           /* apply then update, update only where update_chunks[j] != 0  */
+    TTT_MASK_TOKEN_CAUSAL = 4       /* linattn_forward only: token t sees tokens s <= t            */
+} ttt_mask_mode;
+
+typedef enum {
+    TTT_UPD_GD = 0,      /* W <- W - U                                                         */
+    TTT_UPD_GD_L2 = 1,   /* W <- L2-Normalize(W - U), Eq. (5)                                   */
+    TTT_UPD_MUON_L2 = 2, /* W <- L2-Normalize(W - Muon(U)), Eq. (6)                             */
+    TTT_UPD_MUON = 3     /* W <- W - Muon(U): Muon without the weight norm (paper Table 2, V2)  */
+} ttt_update_rule;
+/* U is the chunk gradient g, or the momentum M <- momentum * M + g when momentum != 0 (the
+ * notes' text after Eq. (6)).  Muon(U): X <- U / (||U||_F + 1e-7), then ns_iters steps of
+ * X <- 1.5 X - 0.5 (X X^T) X taken on the side with the smaller Gram matrix. */
+
+typedef struct ttt_desc {
+    int32_t B, H, N;          /* batch, heads, tokens per sequence (any may be 0: nothing to do) */
+    int32_t d_h, m_h;         /* head width and SwiGLU hidden width: multiples of 32, <= 2048   */
+    int32_t chunk;            /* tokens per chunk, >= 1                                         */
+    int32_t io_dtype;         /* ttt_dtype of q, k, v, o.  Fast weights are always fp32.        */
+    int32_t mask;             /* ttt_mask_mode, not TOKEN_CAUSAL                                */
+    int32_t rule;             /* ttt_update_rule                                                */
+    int32_t ns_iters;         /* Newton-Schulz steps for the Muon rules, 0..32                  */
+    float momentum;           /* beta of the chunk momentum; 0 = none                           */
+    int32_t last_layer_only;  /* 1: only W2 is updated (paper Sec. 6.1 Step 1)                  */
+    int32_t w0_per_batch;     /* 0: W0 is [H][3*d_h*m_h]; 1: W0 is [B][H][3*d_h*m_h]            */
+    const uint8_t* update_chunks; /* host, ceil(N/chunk) flags; read only for TTT_MASK_STRIDED  */
+} ttt_desc;
+
+typedef struct linattn_desc {
+    int32_t B, H, N;
+    int32_t d_k, d_v;         /* multiples of 32, <= 256                                        */
+    int32_t chunk;            /* tokens per chunk, >= 1 (ignored by TOKEN_CAUSAL)               */
+    int32_t io_dtype;         /* ttt_dtype of q, k, v, o; the state S is fp32                   */
+    int32_t mask;             /* any ttt_mask_mode                                              */
+    const uint8_t* update_chunks; /* host, ceil(N/chunk) flags; read only for TTT_MASK_STRIDED  */
+} linattn_desc;
+
+/* Version of this ABI (TTT_ABI_VERSION of the build). */
+int32_t ttt_abi_version(void);
+
+/* Static description of a status code; never NULL. */
+const char* ttt_status_string(ttt_status s);
+
+/* Message for the latest failed call on this thread ("" if none). */
+const char* ttt_last_error(void);
+
+/* Device workspace that ttt_forward needs for `desc`, in bytes (written to *bytes). */
+ttt_status ttt_workspace_bytes(const ttt_desc* desc, size_t* bytes);
+
+/*
+ * The TTT-KVB layer (notes Eqs. (2)-(6), (10); paper App. E).
+ *   q, k, v   [B][H][N][d_h] of io_dtype, 16-byte aligned
+ *   eta       [B][H][N] fp32 per-token learning rates (any sign; negative = gradient ascent)
+ *   W0        initial fast weights, fp32, [H] or [B][H] blocks of [W1 | W3 | W2], 16-byte aligned
+ *   o         [B][H][N][d_h] of io_dtype, output
+ *   W_out     nullable; [B][H][3*d_h*m_h] fp32 fast weights after the last chunk
+ *   M_inout   nullable; [B][H][3*d_h*m_h] fp32 momentum, read at the start and written at the
+ *             end (NULL: momentum starts at zero and is dropped).  Used only if momentum != 0.
+ *   workspace device buffer of at least ttt_workspace_bytes(desc) bytes, 256-byte aligned
+ */
+ttt_status ttt_forward(const ttt_desc* desc, const void* q, const void* k, const void* v,
+                       const float* eta, const float* W0, void* o, float* W_out, float* M_inout,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Device workspace that linattn_forward needs, in bytes. */
+ttt_status linattn_workspace_bytes(const linattn_desc* desc, size_t* bytes);
+
+/*
+ * Chunked linear attention, the linear bias-free fast weight under plain GD with the dot-product
+ * loss (paper Thm. 5.2, Sec. 6.1 Step 6; "From Linear Attention to Test-Time Training",
+ * causal linear attention).  Per (batch, head): S is d_v x d_k fp32; a chunk's update is
+ * S <- S + sum_i eta_i v_i k_i^T and its apply is o_i = S q_i, ordered by `mask`.
+ *   q, k      [B][H][N][d_k] of io_dtype; v, o [B][H][N][d_v]; eta [B][H][N] fp32
+ *   S0        nullable; [B][H][d_v][d_k] fp32 initial state (NULL = zeros)
+ *   S_out     nullable; [B][H][d_v][d_k] fp32 state after the last chunk
+ */
+ttt_status linattn_forward(const linattn_desc* desc, const void* q, const void* k, const void* v,
+                           const float* eta, const float* S0, void* o, float* S_out,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TTT_MI355X_H */

@@ -1,0 +1,86 @@
+"""ctypes declarations of the C ABI in include/ttt.h (libttt.so, built in-tree for gfx950).
+
+There is no fallback: if the library is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import c_float, c_int32, c_size_t, c_void_p, POINTER
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libttt.so")
+
+# enums of include/ttt.h
+TTT_OK, TTT_ERR_INVALID_ARGUMENT, TTT_ERR_UNSUPPORTED, TTT_ERR_WORKSPACE, TTT_ERR_DEVICE = range(5)
+TTT_F32, TTT_BF16 = 0, 1
+MASK_FULL, MASK_UPDATE_THEN_APPLY, MASK_APPLY_THEN_UPDATE, MASK_STRIDED, MASK_TOKEN_CAUSAL = range(5)
+UPD_GD, UPD_GD_L2, UPD_MUON_L2, UPD_MUON = range(4)
+
+# every function include/ttt.h declares
+EXPORTS = (
+    "ttt_abi_version", "ttt_status_string", "ttt_last_error",
+    "ttt_workspace_bytes", "ttt_forward",
+    "linattn_workspace_bytes", "linattn_forward",
+)
+
+
+class TttDesc(ctypes.Structure):
+    _fields_ = [
+        ("B", c_int32), ("H", c_int32), ("N", c_int32),
+        ("d_h", c_int32), ("m_h", c_int32), ("chunk", c_int32),
+        ("io_dtype", c_int32), ("mask", c_int32), ("rule", c_int32),
+        ("ns_iters", c_int32), ("momentum", c_float), ("last_layer_only", c_int32),
+        ("w0_per_batch", c_int32), ("update_chunks", c_void_p),
+    ]
+
+
+class LinattnDesc(ctypes.Structure):
+    _fields_ = [
+        ("B", c_int32), ("H", c_int32), ("N", c_int32),
+        ("d_k", c_int32), ("d_v", c_int32), ("chunk", c_int32),
+        ("io_dtype", c_int32), ("mask", c_int32), ("update_chunks", c_void_p),
+    ]
+
+
+class TttError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libttt.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m linear_attention_chunk_amd.build_lib`")
+    L = ctypes.CDLL(LIB_PATH)
+    L.ttt_abi_version.restype = c_int32
+    L.ttt_abi_version.argtypes = []
+    L.ttt_status_string.restype = ctypes.c_char_p
+    L.ttt_status_string.argtypes = [c_int32]
+    L.ttt_last_error.restype = ctypes.c_char_p
+    L.ttt_last_error.argtypes = []
+    L.ttt_workspace_bytes.restype = c_int32
+    L.ttt_workspace_bytes.argtypes = [POINTER(TttDesc), POINTER(c_size_t)]
+    L.ttt_forward.restype = c_int32
+    L.ttt_forward.argtypes = [POINTER(TttDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                              c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+    L.linattn_workspace_bytes.restype = c_int32
+    L.linattn_workspace_bytes.argtypes = [POINTER(LinattnDesc), POINTER(c_size_t)]
+    L.linattn_forward.restype = c_int32
+    L.linattn_forward.argtypes = [POINTER(LinattnDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                  c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+    _lib = L
+    return L
+
+
+def check(status: int) -> None:
+    if status != TTT_OK:
+        L = lib()
+        msg = L.ttt_last_error().decode() or L.ttt_status_string(status).decode()
+        raise TttError(status, msg)

@@ -1,0 +1,601 @@
+// The large-chunk TTT-KVB layer on gfx950: SwiGLU fast weight f_W(x) = W2 [SiLU(W1 x) o (W3 x)]
+// (PaperTrace "5.2.1 LaCT and TTT-E2E", Eq. (3)), dot-product loss (Eq. (4)), one gradient step per
+// chunk (Eq. (2)) followed by W - U, L2-Normalize(W - U) (Eq. (5)) or Muon (Eq. (6)), in the
+// update/apply order of the notes' section 1.1 and Eq. (10).
+//
+// Every (batch, head) scan is independent; all scans advance one chunk per step in lock-step, and a
+// step is a short sequence of grid-wide launches on one stream:
+//   up    [Q_a; K_u] x [W1; W3]^T and V_u x W2 on MFMA, with the SwiGLU forward and backward in
+//         the epilogue -> Hq = SiLU(Aq) o Cq, HkE = -eta o Hk, DA, DC (token-major, io dtype)
+//   down  O_a = Hq W2^T (queries of the apply chunk) and the chunk gradients
+//         G1 = DA^T K, G3 = DC^T K, G2 = V^T HkE (contractions over the chunk's tokens)
+//   [muon] momentum + Frobenius partial sums, scale, ns_iters x (Gram, polynomial step)
+//   update W <- [norm](W - U) row-wise, fp32 master copy plus io-dtype shadows for the MFMAs
+// The fp32 fast weights live in a ping-pong pair in the workspace; the shadows (W1, W3, W2, W2^T)
+// are what the next chunk's MFMAs read.
+#include <algorithm>
+
+#include "host_common.hpp"
+#include "tile.hpp"
+
+namespace ttt {
+
+template <typename T> struct StepArgs {
+    const T* q; const T* k; const T* v; const float* eta; T* o;
+    int64_t N; int d, m;
+    T* Hq; T* HkE; T* DA; T* DC; int64_t inter_stride;  // per-scan [chunk][m] intermediates
+    const T* sh; int64_t sh_stride;                       // shadows [W1 | W3 | W2 | W2^T]
+    float* G; int64_t g_stride;                           // [G1 | G3 | G2] fp32
+    int64_t a0; int la;                                   // apply chunk: first token, length
+    int64_t u0; int lu;                                   // update chunk
+    int nQ, nK;                                           // up-kernel tiles per scan
+    int nG1, nG2, nO;                                     // down-kernel tiles per scan
+};
+
+// ---------------------------------------------------------------------------------------------
+// up: SwiGLU forward of the queries, forward + backward of the keys
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_up(StepArgs<T> a) {
+    using TQ = Tile<T, 128, 64, 1, 2, 1, 2, 2>;
+    using TK = Tile<T, 128, 64, 1, 2, 2, 3, 3>;
+    constexpr int LDSB = TQ::LDS > TK::LDS ? TQ::LDS : TK::LDS;
+    __shared__ __attribute__((aligned(16))) char smem[LDSB];
+
+    const int per = a.nQ + a.nK;
+    const int s = blockIdx.x / per, t = blockIdx.x % per;
+    const int nct = (a.m + 63) / 64;
+    const int64_t dm = (int64_t)a.d * a.m;
+    const T* sh = a.sh + s * a.sh_stride;
+    const T* W1s = sh;
+    const T* W3s = sh + dm;
+    const T* W2Ts = sh + 3 * dm;
+    const int64_t ioff = s * a.inter_stride;
+
+    if (t < a.nQ) {
+        const int r0 = (t / nct) * 128, c0 = (t % nct) * 64;
+        const int64_t tok = (int64_t)s * a.N + a.a0 + r0;
+        const Opnd<T> A[1] = {{a.q + tok * a.d, a.d, a.la - r0, a.d}};
+        const Opnd<T> B[2] = {{W1s + (int64_t)c0 * a.d, a.d, a.m - c0, a.d},
+                              {W3s + (int64_t)c0 * a.d, a.d, a.m - c0, a.d}};
+        TQ tl;
+        tl.template run<PMQ, false, false>(A, B, a.d, smem);
+        T* Hq = a.Hq + ioff;
+        tl.for_each([&](const float (&v)[2], int row, int col) {
+            const int tr = r0 + row, tc = c0 + col;
+            if (tr < a.la && tc < a.m) Hq[(int64_t)tr * a.m + tc] = Elt<T>::st(v[0] * sigmoidf_(v[0]) * v[1]);
+        });
+    } else {
+        const int tt = t - a.nQ;
+        const int r0 = (tt / nct) * 128, c0 = (tt % nct) * 64;
+        const int64_t tok = (int64_t)s * a.N + a.u0 + r0;
+        const Opnd<T> A[2] = {{a.k + tok * a.d, a.d, a.lu - r0, a.d}, {a.v + tok * a.d, a.d, a.lu - r0, a.d}};
+        const Opnd<T> B[3] = {{W1s + (int64_t)c0 * a.d, a.d, a.m - c0, a.d},
+                              {W3s + (int64_t)c0 * a.d, a.d, a.m - c0, a.d},
+                              {W2Ts + (int64_t)c0 * a.d, a.d, a.m - c0, a.d}};
+        TK tl;
+        tl.template run<PMK, false, false>(A, B, a.d, smem);
+        const float* eta = a.eta + tok;
+        T* HkE = a.HkE + ioff;
+        T* DA = a.DA + ioff;
+        T* DC = a.DC + ioff;
+        tl.for_each([&](const float (&v)[3], int row, int col) {
+            const int tr = r0 + row, tc = c0 + col;
+            if (tr < a.lu && tc < a.m) {
+                const float e = eta[row];
+                const float x = v[0], c = v[1], sg = sigmoidf_(x);
+                const float dh = -e * v[2];  // dLoss/dH = -eta (V W2)
+                const int64_t off = (int64_t)tr * a.m + tc;
+                HkE[off] = Elt<T>::st(-e * x * sg * c);
+                DA[off] = Elt<T>::st(dh * c * sg * (1.f + x * (1.f - sg)));
+                DC[off] = Elt<T>::st(dh * x * sg);
+            }
+        });
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// down: chunk gradients (contractions over tokens) and the apply chunk's outputs
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_down(StepArgs<T> a) {
+    using TT = Tile<T, 128, 128, 2, 2, 1, 1, 1>;
+    __shared__ __attribute__((aligned(16))) char smem[TT::LDS];
+
+    const int per = 2 * a.nG1 + a.nG2 + a.nO;
+    const int s = blockIdx.x / per;
+    int t = blockIdx.x % per;
+    const int64_t dm = (int64_t)a.d * a.m;
+    const int ndt = (a.d + 127) / 128, nmt = (a.m + 127) / 128;
+    const int64_t ioff = s * a.inter_stride;
+    TT tl;
+    if (t < 2 * a.nG1) {  // G1 = DA^T K or G3 = DC^T K: rows c of m, cols e of d
+        const int which = t / a.nG1;
+        t %= a.nG1;
+        const int r0 = (t / ndt) * 128, c0 = (t % ndt) * 128;
+        const T* D = (which == 0 ? a.DA : a.DC) + ioff;
+        const T* K = a.k + ((int64_t)s * a.N + a.u0) * a.d;
+        const Opnd<T> A[1] = {{D + r0, a.m, a.m - r0, a.lu}};
+        const Opnd<T> B[1] = {{K + c0, a.d, a.d - c0, a.lu}};
+        tl.template run<PM1, true, true>(A, B, a.lu, smem);
+        float* G = a.G + s * a.g_stride + which * dm;
+        tl.for_each([&](const float (&v)[1], int row, int col) {
+            const int gr = r0 + row, gc = c0 + col;
+            if (gr < a.m && gc < a.d) G[(int64_t)gr * a.d + gc] = v[0];
+        });
+        return;
+    }
+    t -= 2 * a.nG1;
+    if (t < a.nG2) {  // G2 = V^T HkE: rows e of d, cols c of m
+        const int r0 = (t / nmt) * 128, c0 = (t % nmt) * 128;
+        const T* V = a.v + ((int64_t)s * a.N + a.u0) * a.d;
+        const Opnd<T> A[1] = {{V + r0, a.d, a.d - r0, a.lu}};
+        const Opnd<T> B[1] = {{a.HkE + ioff + c0, a.m, a.m - c0, a.lu}};
+        tl.template run<PM1, true, true>(A, B, a.lu, smem);
+        float* G = a.G + s * a.g_stride + 2 * dm;
+        tl.for_each([&](const float (&v)[1], int row, int col) {
+            const int gr = r0 + row, gc = c0 + col;
+            if (gr < a.d && gc < a.m) G[(int64_t)gr * a.m + gc] = v[0];
+        });
+        return;
+    }
+    t -= a.nG2;
+    {  // O = Hq W2^T: rows t of the apply chunk, cols e of d
+        const int r0 = (t / ndt) * 128, c0 = (t % ndt) * 128;
+        const T* W2s = a.sh + s * a.sh_stride + 2 * dm;
+        const Opnd<T> A[1] = {{a.Hq + ioff + (int64_t)r0 * a.m, a.m, a.la - r0, a.m}};
+        const Opnd<T> B[1] = {{W2s + (int64_t)c0 * a.m, a.m, a.d - c0, a.m}};
+        tl.template run<PM1, false, false>(A, B, a.m, smem);
+        T* O = a.o + ((int64_t)s * a.N + a.a0) * a.d;
+        tl.for_each([&](const float (&v)[1], int row, int col) {
+            const int tr = r0 + row, tc = c0 + col;
+            if (tr < a.la && tc < a.d) O[(int64_t)tr * a.d + tc] = Elt<T>::st(v[0]);
+        });
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// update: W <- [L2-Normalize](W - U) for blocks of 16 rows; writes the fp32 master copy and the
+// io-dtype shadows W1, W3, W2 and W2^T.  With U == nullptr and norm == 0 it copies (initial W0).
+template <typename T> struct UpdArgs {
+    const float* src; int64_t src_stride; int src_per_head; int H;
+    const float* U; int64_t u_stride;
+    float* dst; int64_t dst_stride;
+    T* sh; int64_t sh_stride;
+    int d, m, norm, last_only;
+};
+
+constexpr int kUpdRows = 16;
+constexpr int kMaxDim = 2048;
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_update(UpdArgs<T> a) {
+    __shared__ __attribute__((aligned(16))) T tileT[kUpdRows * kMaxDim];
+    const int per = (2 * a.m + a.d) / kUpdRows;
+    const int s = blockIdx.x / per, rb = blockIdx.x % per;
+    const int64_t dm = (int64_t)a.d * a.m;
+    int mat, row0, L;
+    if (rb < a.m / kUpdRows) { mat = 0; row0 = rb * kUpdRows; L = a.d; }
+    else if (rb < 2 * a.m / kUpdRows) { mat = 1; row0 = rb * kUpdRows - a.m; L = a.d; }
+    else { mat = 2; row0 = rb * kUpdRows - 2 * a.m; L = a.m; }
+    const bool frozen = a.last_only && mat != 2;
+    const int64_t moff = mat * dm;
+    const int hs = a.src_per_head ? (s % a.H) : s;
+    const float* src = a.src + hs * a.src_stride + moff;
+    const float* U = (a.U && !frozen) ? a.U + s * a.u_stride + moff : nullptr;
+    const bool norm = a.norm && !frozen;
+    float* dst = a.dst + s * a.dst_stride + moff;
+    T* shm = a.sh + s * a.sh_stride + moff;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int rr = 0; rr < kUpdRows / 4; ++rr) {
+        const int row = wave * (kUpdRows / 4) + rr;
+        const int64_t ro = (int64_t)(row0 + row) * L;
+        float ss = 0.f;
+        if (norm) {
+            for (int c = lane; c < L; c += 64) {
+                float x = src[ro + c];
+                if (U) x -= U[ro + c];
+                ss += x * x;
+            }
+            ss = wave_sum(ss);
+        }
+        const float sc = norm ? 1.0f / fmaxf(sqrtf(ss), 1e-6f) : 1.0f;
+        for (int c = lane; c < L; c += 64) {
+            float x = src[ro + c];
+            if (U) x -= U[ro + c];
+            x *= sc;
+            dst[ro + c] = x;
+            const T y = Elt<T>::st(x);
+            shm[ro + c] = y;
+            if (mat == 2) tileT[row * L + c] = y;
+        }
+    }
+    if (mat == 2) {  // W2^T [m][d]: column c of this 16-row block is 16 consecutive elements
+        __syncthreads();
+        T* w2t = a.sh + s * a.sh_stride + 3 * dm;
+        for (int c = threadIdx.x; c < L; c += kThreads) {
+            T* out = w2t + (int64_t)c * a.d + row0;
+#pragma unroll
+            for (int j = 0; j < kUpdRows; ++j) out[j] = tileT[j * L + c];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Muon.  prep: U = G, or M <- beta M + G and U = M; per-block partial sums of U^2.
+// init: X = U / (||U||_F + 1e-7) in fp32 and io dtype.  gram / step: one cubic Newton-Schulz
+// step X <- 1.5 X - 0.5 (X X^T) X, taken as X - ... on the side with the smaller Gram matrix.
+constexpr int kPrepElems = 4096;
+
+struct PrepArgs {
+    const float* G; int64_t g_stride;
+    float* M; int64_t m_stride; float beta;
+    float* part; int nblk;
+    int64_t dm; int mat0, nmat;
+};
+
+__device__ __forceinline__ float block_sum(float x, float* red) {
+    x = wave_sum(x);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __syncthreads();
+    if (lane == 0) red[wave] = x;
+    __syncthreads();
+    return red[0] + red[1] + red[2] + red[3];
+}
+
+__global__ __launch_bounds__(kThreads) void k_muon_prep(PrepArgs a) {
+    __shared__ float red[4];
+    const int per = a.nmat * a.nblk;
+    const int s = blockIdx.x / per, t = blockIdx.x % per;
+    const int mat = a.mat0 + t / a.nblk, blk = t % a.nblk;
+    const float* G = a.G + s * a.g_stride + mat * a.dm;
+    float* M = a.M ? a.M + s * a.m_stride + mat * a.dm : nullptr;
+    float ss = 0.f;
+    const int64_t e0 = (int64_t)blk * kPrepElems;
+    for (int i = threadIdx.x; i < kPrepElems; i += kThreads) {
+        const int64_t e = e0 + i;
+        if (e < a.dm) {
+            float u = G[e];
+            if (M) {
+                u = a.beta * M[e] + u;
+                M[e] = u;
+            }
+            ss += u * u;
+        }
+    }
+    const float tot = block_sum(ss, red);
+    if (threadIdx.x == 0) a.part[((int64_t)s * 3 + mat) * a.nblk + blk] = tot;
+}
+
+template <typename T> struct NSArgs {
+    const float* U; int64_t u_stride;     // G or M (init only)
+    const float* part; int nblk;          // partial sums (init only)
+    float* Xf; int64_t x_stride;          // fp32 iterate
+    const T* Xin; T* Xout;                // io-dtype copies (ping-pong), stride x_stride
+    T* Gram; int64_t gram_stride;         // 3 x p*p
+    int d, m, mat0, nmat, tiles;          // tiles per matrix
+};
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_ns_init(NSArgs<T> a) {
+    __shared__ float tot_s;
+    const int64_t dm = (int64_t)a.d * a.m;
+    const int per = a.nmat * a.nblk;
+    const int s = blockIdx.x / per, t = blockIdx.x % per;
+    const int mat = a.mat0 + t / a.nblk, blk = t % a.nblk;
+    if (threadIdx.x == 0) {
+        const float* p = a.part + ((int64_t)s * 3 + mat) * a.nblk;
+        float tot = 0.f;
+        for (int i = 0; i < a.nblk; ++i) tot += p[i];
+        tot_s = tot;
+    }
+    __syncthreads();
+    const float inv = 1.0f / (sqrtf(tot_s) + 1e-7f);
+    const float* U = a.U + s * a.u_stride + mat * dm;
+    float* Xf = a.Xf + s * a.x_stride + mat * dm;
+    T* Xo = a.Xout + s * a.x_stride + mat * dm;
+    const int64_t e0 = (int64_t)blk * kPrepElems;
+    for (int i = threadIdx.x; i < kPrepElems; i += kThreads) {
+        const int64_t e = e0 + i;
+        if (e < dm) {
+            const float x = U[e] * inv;
+            Xf[e] = x;
+            Xo[e] = Elt<T>::st(x);
+        }
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_ns_gram(NSArgs<T> a) {
+    using TT = Tile<T, 128, 128, 2, 2, 1, 1, 1>;
+    __shared__ __attribute__((aligned(16))) char smem[TT::LDS];
+    const int64_t dm = (int64_t)a.d * a.m;
+    const int per = a.nmat * a.tiles;
+    const int s = blockIdx.x / per;
+    int t = blockIdx.x % per;
+    const int mat = a.mat0 + t / a.tiles;
+    t %= a.tiles;
+    const int r = mat < 2 ? a.m : a.d, c = mat < 2 ? a.d : a.m;
+    const int p = r < c ? r : c;
+    const int np = (p + 127) / 128;
+    const int i0 = (t / np) * 128, j0 = (t % np) * 128;
+    const T* X = a.Xin + s * a.x_stride + mat * dm;
+    TT tl;
+    if (r > c) {  // Gram = X^T X (c x c), contracted over the r rows
+        const Opnd<T> A[1] = {{X + i0, c, c - i0, r}};
+        const Opnd<T> B[1] = {{X + j0, c, c - j0, r}};
+        tl.template run<PM1, true, true>(A, B, r, smem);
+    } else {      // Gram = X X^T (r x r), contracted over the c columns
+        const Opnd<T> A[1] = {{X + (int64_t)i0 * c, c, r - i0, c}};
+        const Opnd<T> B[1] = {{X + (int64_t)j0 * c, c, r - j0, c}};
+        tl.template run<PM1, false, false>(A, B, c, smem);
+    }
+    T* Gm = a.Gram + s * a.gram_stride + (int64_t)mat * p * p;
+    tl.for_each([&](const float (&v)[1], int row, int col) {
+        const int gi = i0 + row, gj = j0 + col;
+        if (gi < p && gj < p) Gm[(int64_t)gi * p + gj] = Elt<T>::st(v[0]);
+    });
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_ns_step(NSArgs<T> a) {
+    using TT = Tile<T, 128, 128, 2, 2, 1, 1, 1>;
+    __shared__ __attribute__((aligned(16))) char smem[TT::LDS];
+    const int64_t dm = (int64_t)a.d * a.m;
+    const int per = a.nmat * a.tiles;
+    const int s = blockIdx.x / per;
+    int t = blockIdx.x % per;
+    const int mat = a.mat0 + t / a.tiles;
+    t %= a.tiles;
+    const int r = mat < 2 ? a.m : a.d, c = mat < 2 ? a.d : a.m;
+    const int p = r < c ? r : c;
+    const int nct = (c + 127) / 128;
+    const int r0 = (t / nct) * 128, c0 = (t % nct) * 128;
+    const T* X = a.Xin + s * a.x_stride + mat * dm;
+    const T* Gm = a.Gram + s * a.gram_stride + (int64_t)mat * p * p;
+    TT tl;
+    if (r > c) {  // P = X Gram; Gram is symmetric, so its rows serve as the B operand
+        const Opnd<T> A[1] = {{X + (int64_t)r0 * c, c, r - r0, c}};
+        const Opnd<T> B[1] = {{Gm + (int64_t)c0 * p, p, c - c0, p}};
+        tl.template run<PM1, false, false>(A, B, c, smem);
+    } else {      // P = Gram X; B[j][i] = X[i][j] is read k-strided
+        const Opnd<T> A[1] = {{Gm + (int64_t)r0 * p, p, r - r0, p}};
+        const Opnd<T> B[1] = {{X + c0, c, c - c0, r}};
+        tl.template run<PM1, false, true>(A, B, r, smem);
+    }
+    float* Xf = a.Xf + s * a.x_stride + mat * dm;
+    T* Xo = a.Xout + s * a.x_stride + mat * dm;
+    tl.for_each([&](const float (&v)[1], int row, int col) {
+        const int gr = r0 + row, gc = c0 + col;
+        if (gr < r && gc < c) {
+            const int64_t e = (int64_t)gr * c + gc;
+            const float xn = 1.5f * Xf[e] - 0.5f * v[0];
+            Xf[e] = xn;
+            Xo[e] = Elt<T>::st(xn);
+        }
+    });
+}
+
+// ---------------------------------------------------------------------------------------------
+// host driver
+
+struct Layout {
+    size_t wf[2], sh[2], hq, hke, da, dc, g, xf, xb[2], gram, part, mom, total;
+    int64_t wf_stride, sh_stride, inter_stride, g_stride, x_stride, gram_stride;
+    int nblk;
+};
+
+static Layout make_layout(const ttt_desc& D, bool muon, bool own_m) {
+    Layout L{};
+    const int64_t S = (int64_t)D.B * D.H, d = D.d_h, m = D.m_h, dm = d * m;
+    const int64_t bmax = D.N < D.chunk ? D.N : D.chunk;
+    const size_t es = D.io_dtype == TTT_BF16 ? 2 : 4;
+    const int64_t p = d < m ? d : m;
+    L.wf_stride = 3 * dm;
+    L.sh_stride = 4 * dm;
+    L.inter_stride = bmax * m;
+    L.g_stride = 3 * dm;
+    L.x_stride = 3 * dm;
+    L.gram_stride = 3 * p * p;
+    L.nblk = (int)cdiv(dm, kPrepElems);
+    size_t off = 0;
+    auto take = [&](size_t bytes) { const size_t o = off; off += align256(bytes); return o; };
+    L.wf[0] = take(S * L.wf_stride * 4);
+    L.wf[1] = take(S * L.wf_stride * 4);
+    L.sh[0] = take(S * L.sh_stride * es);
+    L.sh[1] = take(S * L.sh_stride * es);
+    L.hq = take(S * L.inter_stride * es);
+    L.hke = take(S * L.inter_stride * es);
+    L.da = take(S * L.inter_stride * es);
+    L.dc = take(S * L.inter_stride * es);
+    L.g = take(S * L.g_stride * 4);
+    L.part = take(S * 3 * (size_t)L.nblk * 4);
+    if (muon) {
+        L.xf = take(S * L.x_stride * 4);
+        L.xb[0] = take(S * L.x_stride * es);
+        L.xb[1] = take(S * L.x_stride * es);
+        L.gram = take(S * L.gram_stride * es);
+    }
+    if (own_m) L.mom = take(S * 3 * dm * 4);
+    L.total = off;
+    return L;
+}
+
+static ttt_status validate(const ttt_desc* D) {
+    if (!D) return fail(TTT_ERR_INVALID_ARGUMENT, "desc is NULL");
+    if (D->B < 0 || D->H < 0 || D->N < 0) return fail(TTT_ERR_INVALID_ARGUMENT, "B, H, N must be >= 0");
+    if (D->d_h < 32 || D->d_h > kMaxDim || D->d_h % 32)
+        return fail(TTT_ERR_INVALID_ARGUMENT, "d_h=%d must be a multiple of 32 in [32, %d]", D->d_h, kMaxDim);
+    if (D->m_h < 32 || D->m_h > kMaxDim || D->m_h % 32)
+        return fail(TTT_ERR_INVALID_ARGUMENT, "m_h=%d must be a multiple of 32 in [32, %d]", D->m_h, kMaxDim);
+    if (D->chunk < 1) return fail(TTT_ERR_INVALID_ARGUMENT, "chunk must be >= 1");
+    if (D->io_dtype != TTT_F32 && D->io_dtype != TTT_BF16) return fail(TTT_ERR_INVALID_ARGUMENT, "bad io_dtype");
+    if (D->mask < TTT_MASK_FULL || D->mask > TTT_MASK_TOKEN_CAUSAL) return fail(TTT_ERR_INVALID_ARGUMENT, "bad mask");
+    if (D->mask == TTT_MASK_TOKEN_CAUSAL)
+        return fail(TTT_ERR_UNSUPPORTED, "TOKEN_CAUSAL is defined for the linear model (linattn_forward) only");
+    if (D->mask == TTT_MASK_FULL && D->chunk < D->N)
+        return fail(TTT_ERR_INVALID_ARGUMENT, "MASK_FULL needs chunk >= N (one chunk)");
+    if (D->mask == TTT_MASK_STRIDED && !D->update_chunks && D->N > 0)
+        return fail(TTT_ERR_INVALID_ARGUMENT, "MASK_STRIDED needs update_chunks");
+    if (D->rule < TTT_UPD_GD || D->rule > TTT_UPD_MUON) return fail(TTT_ERR_INVALID_ARGUMENT, "bad update rule");
+    if (D->ns_iters < 0 || D->ns_iters > 32) return fail(TTT_ERR_INVALID_ARGUMENT, "ns_iters must be in [0, 32]");
+    if (!(D->momentum == D->momentum) || D->momentum > 1e30f || D->momentum < -1e30f)
+        return fail(TTT_ERR_INVALID_ARGUMENT, "momentum must be finite");
+    if (D->last_layer_only != 0 && D->last_layer_only != 1) return fail(TTT_ERR_INVALID_ARGUMENT, "last_layer_only must be 0/1");
+    if (D->w0_per_batch != 0 && D->w0_per_batch != 1) return fail(TTT_ERR_INVALID_ARGUMENT, "w0_per_batch must be 0/1");
+    const int64_t S = (int64_t)D->B * D->H;
+    if (S > (1 << 20) || (int64_t)D->N > (1LL << 31) / 2) return fail(TTT_ERR_INVALID_ARGUMENT, "B*H or N too large");
+    return TTT_OK;
+}
+
+static bool is_muon(const ttt_desc& D) { return D.rule == TTT_UPD_MUON_L2 || D.rule == TTT_UPD_MUON; }
+
+template <typename T>
+static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const T* k, const T* v,
+                          const float* eta, const float* W0, T* o, float* W_out, float* M_inout,
+                          char* ws, hipStream_t st) {
+    const int S = D.B * D.H, d = D.d_h, m = D.m_h;
+    const int64_t dm = (int64_t)d * m;
+    const bool muon = is_muon(D);
+    const bool mom = D.momentum != 0.0f;
+    float* Wf[2] = {(float*)(ws + L.wf[0]), (float*)(ws + L.wf[1])};
+    T* sh[2] = {(T*)(ws + L.sh[0]), (T*)(ws + L.sh[1])};
+    float* G = (float*)(ws + L.g);
+    float* part = (float*)(ws + L.part);
+    float* M = mom ? (M_inout ? M_inout : (float*)(ws + L.mom)) : nullptr;
+    ttt_status rc;
+
+    if (mom && !M_inout) {
+        hipError_t e = hipMemsetAsync(M, 0, (size_t)S * 3 * dm * 4, st);
+        if (e != hipSuccess) return fail(TTT_ERR_DEVICE, "zeroing momentum: %s", hipGetErrorString(e));
+    }
+    const int upd_blocks = (2 * m + d) / kUpdRows;
+    {  // W0 -> master copy and shadows
+        UpdArgs<T> u{W0, 3 * dm, D.w0_per_batch ? 0 : 1, D.H, nullptr, 0, Wf[0], L.wf_stride, sh[0], L.sh_stride,
+                     d, m, 0, 0};
+        hipLaunchKernelGGL(k_update<T>, dim3(S * upd_blocks), dim3(kThreads), 0, st, u);
+        if ((rc = check_launch("k_update(init)")) != TTT_OK) return rc;
+    }
+    int cur = 0;
+    const int nc = (int)cdiv(D.N, D.chunk);
+    const bool uta = D.mask == TTT_MASK_FULL || D.mask == TTT_MASK_UPDATE_THEN_APPLY;
+    const int nsteps = D.N == 0 ? 0 : (uta ? nc + 1 : nc);
+    const int ntm = (int)cdiv(m, 128), ntd = (int)cdiv(d, 128), nc64 = (int)cdiv(m, 64);
+    for (int step = 0; step < nsteps; ++step) {
+        int ja = uta ? step - 1 : step;
+        int ju = step < nc ? step : -1;
+        if (D.mask == TTT_MASK_STRIDED && ju >= 0 && !D.update_chunks[ju]) ju = -1;
+        StepArgs<T> a{};
+        a.q = q; a.k = k; a.v = v; a.eta = eta; a.o = o;
+        a.N = D.N; a.d = d; a.m = m;
+        a.Hq = (T*)(ws + L.hq); a.HkE = (T*)(ws + L.hke); a.DA = (T*)(ws + L.da); a.DC = (T*)(ws + L.dc);
+        a.inter_stride = L.inter_stride;
+        a.sh = sh[cur]; a.sh_stride = L.sh_stride;
+        a.G = G; a.g_stride = L.g_stride;
+        a.a0 = ja >= 0 ? (int64_t)ja * D.chunk : 0;
+        a.la = ja >= 0 ? (int)(std::min<int64_t>((int64_t)(ja + 1) * D.chunk, D.N) - a.a0) : 0;
+        a.u0 = ju >= 0 ? (int64_t)ju * D.chunk : 0;
+        a.lu = ju >= 0 ? (int)(std::min<int64_t>((int64_t)(ju + 1) * D.chunk, D.N) - a.u0) : 0;
+        a.nQ = a.la ? (int)cdiv(a.la, 128) * nc64 : 0;
+        a.nK = a.lu ? (int)cdiv(a.lu, 128) * nc64 : 0;
+        a.nG1 = (a.lu && !D.last_layer_only) ? ntm * ntd : 0;
+        a.nG2 = a.lu ? ntd * ntm : 0;
+        a.nO = a.la ? (int)cdiv(a.la, 128) * ntd : 0;
+        if (a.nQ + a.nK) {
+            hipLaunchKernelGGL(k_up<T>, dim3(S * (a.nQ + a.nK)), dim3(kThreads), 0, st, a);
+            if ((rc = check_launch("k_up")) != TTT_OK) return rc;
+        }
+        if (2 * a.nG1 + a.nG2 + a.nO) {
+            hipLaunchKernelGGL(k_down<T>, dim3(S * (2 * a.nG1 + a.nG2 + a.nO)), dim3(kThreads), 0, st, a);
+            if ((rc = check_launch("k_down")) != TTT_OK) return rc;
+        }
+        if (a.lu == 0) continue;
+        const int mat0 = D.last_layer_only ? 2 : 0, nmat = D.last_layer_only ? 1 : 3;
+        const float* U = G;
+        if (muon || mom) {
+            PrepArgs pa{G, L.g_stride, M, 3 * dm, D.momentum, part, L.nblk, dm, mat0, nmat};
+            hipLaunchKernelGGL(k_muon_prep, dim3(S * nmat * L.nblk), dim3(kThreads), 0, st, pa);
+            if ((rc = check_launch("k_muon_prep")) != TTT_OK) return rc;
+            if (mom) U = M;
+        }
+        if (muon) {
+            T* Xb[2] = {(T*)(ws + L.xb[0]), (T*)(ws + L.xb[1])};
+            float* Xf = (float*)(ws + L.xf);
+            NSArgs<T> na{U, 3 * dm, part, L.nblk, Xf, L.x_stride, Xb[1], Xb[0], (T*)(ws + L.gram), L.gram_stride,
+                         d, m, mat0, nmat, 0};
+            hipLaunchKernelGGL(k_ns_init<T>, dim3(S * nmat * L.nblk), dim3(kThreads), 0, st, na);
+            if ((rc = check_launch("k_ns_init")) != TTT_OK) return rc;
+            const int p = d < m ? d : m;
+            const int gt = (int)(cdiv(p, 128) * cdiv(p, 128));
+            const int stt = ntm * ntd;
+            for (int it = 0; it < D.ns_iters; ++it) {
+                na.Xin = Xb[it & 1];
+                na.Xout = Xb[(it + 1) & 1];
+                na.tiles = gt;
+                hipLaunchKernelGGL(k_ns_gram<T>, dim3(S * nmat * gt), dim3(kThreads), 0, st, na);
+                if ((rc = check_launch("k_ns_gram")) != TTT_OK) return rc;
+                na.tiles = stt;
+                hipLaunchKernelGGL(k_ns_step<T>, dim3(S * nmat * stt), dim3(kThreads), 0, st, na);
+                if ((rc = check_launch("k_ns_step")) != TTT_OK) return rc;
+            }
+            U = Xf;
+        }
+        const int norm = (D.rule == TTT_UPD_GD_L2 || D.rule == TTT_UPD_MUON_L2) ? 1 : 0;
+        UpdArgs<T> u{Wf[cur], L.wf_stride, 0, D.H, U, 3 * dm, Wf[cur ^ 1], L.wf_stride, sh[cur ^ 1], L.sh_stride,
+                     d, m, norm, D.last_layer_only};
+        hipLaunchKernelGGL(k_update<T>, dim3(S * upd_blocks), dim3(kThreads), 0, st, u);
+        if ((rc = check_launch("k_update")) != TTT_OK) return rc;
+        cur ^= 1;
+    }
+    if (W_out) {
+        hipError_t e = hipMemcpyAsync(W_out, Wf[cur], (size_t)S * 3 * dm * 4, hipMemcpyDeviceToDevice, st);
+        if (e != hipSuccess) return fail(TTT_ERR_DEVICE, "copying W_out: %s", hipGetErrorString(e));
+    }
+    return TTT_OK;
+}
+
+}  // namespace ttt
+
+using namespace ttt;
+
+extern "C" ttt_status ttt_workspace_bytes(const ttt_desc* desc, size_t* bytes) {
+    clear_error();
+    ttt_status rc = validate(desc);
+    if (rc != TTT_OK) return rc;
+    if (!bytes) return fail(TTT_ERR_INVALID_ARGUMENT, "bytes is NULL");
+    *bytes = make_layout(*desc, is_muon(*desc), desc->momentum != 0.0f).total;
+    return TTT_OK;
+}
+
+extern "C" ttt_status ttt_forward(const ttt_desc* desc, const void* q, const void* k, const void* v,
+                                  const float* eta, const float* W0, void* o, float* W_out, float* M_inout,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+    clear_error();
+    ttt_status rc = validate(desc);
+    if (rc != TTT_OK) return rc;
+    const ttt_desc& D = *desc;
+    const int64_t S = (int64_t)D.B * D.H;
+    if (S == 0) return TTT_OK;
+    const size_t es = D.io_dtype == TTT_BF16 ? 2 : 4;
+    const size_t io_bytes = (size_t)S * D.N * D.d_h * es;
+    const size_t w_bytes = (size_t)S * 3 * D.d_h * D.m_h * 4;
+    const size_t w0_bytes = (size_t)(D.w0_per_batch ? S : D.H) * 3 * D.d_h * D.m_h * 4;
+    if (!W0) return fail(TTT_ERR_INVALID_ARGUMENT, "W0 is NULL");
+    if (D.N > 0 && (!q || !k || !v || !eta || !o)) return fail(TTT_ERR_INVALID_ARGUMENT, "q, k, v, eta and o are required");
+    const void* p16[] = {q, k, v, o, W0, W_out, M_inout};
+    for (const void* p : p16)
+        if (p && !aligned(p, 16)) return fail(TTT_ERR_INVALID_ARGUMENT, "q, k, v, o, W0, W_out, M must be 16-byte aligned");
+    if (eta && !aligned(eta, 4)) return fail(TTT_ERR_INVALID_ARGUMENT, "eta must be 4-byte aligned");
+    if (overlaps(o, io_bytes, q, io_bytes) || overlaps(o, io_bytes, k, io_bytes) || overlaps(o, io_bytes, v, io_bytes) ||
+        overlaps(o, io_bytes, eta, (size_t)S * D.N * 4))
+        return fail(TTT_ERR_INVALID_ARGUMENT, "o overlaps an input");
+    if (overlaps(W_out, w_bytes, W0, w0_bytes)) return fail(TTT_ERR_INVALID_ARGUMENT, "W_out overlaps W0");
+    const Layout L = make_layout(D, is_muon(D), D.momentum != 0.0f && !M_inout);
+    if (L.total > 0 && (!workspace || workspace_bytes < L.total))
+        return fail(TTT_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", L.total, workspace_bytes);
+    if (workspace && !aligned(workspace, 256)) return fail(TTT_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    hipStream_t st = (hipStream_t)stream;
+    if (D.io_dtype == TTT_BF16)
+        return run_ttt<uint16_t>(D, L, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, eta, W0,
+                                 (uint16_t*)o, W_out, M_inout, (char*)workspace, st);
+    return run_ttt<float>(D, L, (const float*)q, (const float*)k, (const float*)v, eta, W0, (float*)o, W_out,
+                          M_inout, (char*)workspace, st);
+}

@@ -6,7 +6,7 @@ leg, never by the product path.  It imports nothing from the HIP library.
 from .ttt_ref import *  # noqa: F401,F403
 from .ttt_ref import (  # noqa: F401
     MASK_FULL, MASK_UPDATE_THEN_APPLY, MASK_APPLY_THEN_UPDATE, MASK_STRIDED, MASK_TOKEN_CAUSAL,
-    UPD_GD, UPD_GD_L2, UPD_MUON_L2,
+    UPD_GD, UPD_GD_L2, UPD_MUON_L2, UPD_MUON,
     swiglu_apply, chunk_gradients, l2_normalize_rows, newton_schulz, chunk_bounds,
     ttt_scan_ref, ttt_forward_ref, linattn_scan_ref, linattn_forward_ref, gemm_intensity,
 )

@@ -57,6 +57,7 @@ MASK_TOKEN_CAUSAL = 4        # linear model only: every token sees itself and al
 UPD_GD = 0        # W <- W - U (no normalisation)
 UPD_GD_L2 = 1     # Eq. (5)
 UPD_MUON_L2 = 2   # Eq. (6)
+UPD_MUON = 3      # W <- W - Muon(U), no weight norm (TTT-as-LA Table 2, Variant 2 recurrence)
 
 ROW_NORM_EPS = 1e-6
 NS_EPS = 1e-7
@@ -137,7 +138,7 @@ def _weight_update(W, G, Mx, rule, ns_iters, momentum):
     if momentum != 0.0:
         Mx = momentum * Mx + G
         U = Mx
-    if rule == UPD_MUON_L2:
+    if rule in (UPD_MUON_L2, UPD_MUON):
         U = newton_schulz(U, ns_iters)
     W = W - U
     if rule in (UPD_GD_L2, UPD_MUON_L2):

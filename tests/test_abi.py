@@ -1,0 +1,154 @@
+"""CPU checks of the C ABI: libttt.so loads, exports what include/ttt.h declares, and rejects bad
+arguments before touching any device (only argument-validation paths are exercised here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from linear_attention_chunk_amd import _lib as C
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ttt.h")
+
+# fake device addresses: never dereferenced, because every call below fails validation first
+P16 = 0x7F0000000000
+P16B = 0x7F0100000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ttt_\w+|linattn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_exports():
+    assert declared_functions() == sorted(C.EXPORTS)
+
+
+def test_library_loads_and_exports_every_symbol():
+    L = C.lib()
+    for name in C.EXPORTS:
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", C.LIB_PATH], capture_output=True, text=True).stdout
+    syms = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    for name in C.EXPORTS:
+        assert name in syms, name
+
+
+def test_version_and_status_strings():
+    L = C.lib()
+    assert L.ttt_abi_version() == 1
+    for s in range(5):
+        assert L.ttt_status_string(s)
+    assert L.ttt_status_string(99) == b"unknown status"
+
+
+def desc(**kw):
+    base = dict(B=2, H=4, N=256, d_h=64, m_h=128, chunk=64, io_dtype=C.TTT_BF16, mask=C.MASK_APPLY_THEN_UPDATE,
+                rule=C.UPD_GD_L2, ns_iters=5, momentum=0.0, last_layer_only=0, w0_per_batch=0, update_chunks=None)
+    base.update(kw)
+    return C.TttDesc(**base)
+
+
+def ws_bytes(D):
+    n = ctypes.c_size_t(0)
+    st = C.lib().ttt_workspace_bytes(ctypes.byref(D), ctypes.byref(n))
+    return st, n.value
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d_h=48), C.TTT_ERR_INVALID_ARGUMENT),
+    (dict(d_h=4096), C.TTT_ERR_INVALID_ARGUMENT),
+    (dict(m_h=0), C.TTT_ERR_INVALID_ARGUMENT),
+    (dict(chunk=0), C.TTT_ERR_INVALID_ARGUMENT),
+    (dict(N=-1), C.TTT_ERR_INVALID_ARGUMENT),
+    (dict(io_dtype=7), C.TTT_ERR_INVALID_ARGUMENT),
+    (dict(mask=9), C.TTT_ERR_INVALID_ARGUMENT),
+    (dict(mask=C.MASK_TOKEN_CAUSAL), C.TTT_ERR_UNSUPPORTED),
+    (dict(mask=C.MASK_FULL, chunk=64), C.TTT_ERR_INVALID_ARGUMENT),
+    (dict(mask=C.MASK_STRIDED), C.TTT_ERR_INVALID_ARGUMENT),
+    (dict(rule=4), C.TTT_ERR_INVALID_ARGUMENT),
+    (dict(ns_iters=-1), C.TTT_ERR_INVALID_ARGUMENT),
+    (dict(momentum=float("nan")), C.TTT_ERR_INVALID_ARGUMENT),
+    (dict(last_layer_only=2), C.TTT_ERR_INVALID_ARGUMENT),
+])
+def test_desc_validation(kw, status):
+    st, _ = ws_bytes(desc(**kw))
+    assert st == status
+    assert C.lib().ttt_last_error()
+
+
+def test_workspace_sizes():
+    st, gd = ws_bytes(desc())
+    assert st == C.TTT_OK and gd > 0
+    _, muon = ws_bytes(desc(rule=C.UPD_MUON_L2))
+    _, mom = ws_bytes(desc(rule=C.UPD_MUON_L2, momentum=0.9))
+    assert muon > gd and mom > muon
+    _, big = ws_bytes(desc(chunk=256))
+    assert big > gd
+    st, z = ws_bytes(desc(N=0))
+    assert st == C.TTT_OK
+    assert C.lib().ttt_last_error() == b""
+    # a FULL mask needs one chunk covering the sequence
+    assert ws_bytes(desc(mask=C.MASK_FULL, chunk=256))[0] == C.TTT_OK
+
+
+def call_forward(D, q=P16, k=P16, v=P16, eta=P16, W0=P16B, o=P16 + (1 << 30), W_out=None, M=None, ws=None, nws=0):
+    return C.lib().ttt_forward(ctypes.byref(D), q, k, v, eta, W0, o, W_out, M, ws, nws, None)
+
+
+def test_forward_rejects_before_enqueueing():
+    D = desc()
+    _, need = ws_bytes(D)
+    assert call_forward(D, q=None) == C.TTT_ERR_INVALID_ARGUMENT
+    assert call_forward(D, W0=None) == C.TTT_ERR_INVALID_ARGUMENT
+    assert call_forward(D, q=P16 + 2) == C.TTT_ERR_INVALID_ARGUMENT          # misaligned
+    assert call_forward(D, o=P16 + 64) == C.TTT_ERR_INVALID_ARGUMENT         # o overlaps q
+    assert call_forward(D, ws=None, nws=0) == C.TTT_ERR_WORKSPACE
+    assert call_forward(D, ws=P16 + (1 << 34), nws=need - 1) == C.TTT_ERR_WORKSPACE
+    assert call_forward(D, ws=P16 + (1 << 34) + 16, nws=need) == C.TTT_ERR_WORKSPACE  # not 256-aligned
+    assert call_forward(D, W_out=P16B + 64) == C.TTT_ERR_INVALID_ARGUMENT    # W_out overlaps W0
+    assert b"workspace" in C.lib().ttt_last_error() or b"overlaps" in C.lib().ttt_last_error()
+    # no (batch, head): nothing to do, no pointer is touched
+    assert call_forward(desc(B=0), q=None, k=None, v=None, eta=None, o=None) == C.TTT_OK
+
+
+def lin_desc(**kw):
+    base = dict(B=1, H=2, N=128, d_k=64, d_v=64, chunk=32, io_dtype=C.TTT_BF16, mask=C.MASK_APPLY_THEN_UPDATE,
+                update_chunks=None)
+    base.update(kw)
+    return C.LinattnDesc(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d_k=48), C.TTT_ERR_INVALID_ARGUMENT),
+    (dict(d_k=512), C.TTT_ERR_INVALID_ARGUMENT),
+    (dict(d_v=16), C.TTT_ERR_INVALID_ARGUMENT),
+    (dict(chunk=0), C.TTT_ERR_INVALID_ARGUMENT),
+    (dict(mask=5), C.TTT_ERR_INVALID_ARGUMENT),
+    (dict(mask=C.MASK_FULL), C.TTT_ERR_INVALID_ARGUMENT),
+    (dict(mask=C.MASK_STRIDED), C.TTT_ERR_INVALID_ARGUMENT),
+])
+def test_linattn_validation(kw, status):
+    n = ctypes.c_size_t(1)
+    assert C.lib().linattn_workspace_bytes(ctypes.byref(lin_desc(**kw)), ctypes.byref(n)) == status
+
+
+def test_linattn_forward_rejects():
+    L = C.lib()
+    D = lin_desc()
+    assert L.linattn_forward(ctypes.byref(D), None, P16, P16, P16, None, P16B, None, None, 0, None) == \
+        C.TTT_ERR_INVALID_ARGUMENT
+    assert L.linattn_forward(ctypes.byref(D), P16, P16, P16, P16, None, P16 + 32, None, None, 0, None) == \
+        C.TTT_ERR_INVALID_ARGUMENT
+    n = ctypes.c_size_t(1)
+    assert L.linattn_workspace_bytes(ctypes.byref(D), ctypes.byref(n)) == C.TTT_OK and n.value == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(C, "_lib", None)
+    monkeypatch.setattr(C, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        C.lib()

@@ -1,0 +1,156 @@
+"""GPU parity of ttt_forward (through the C ABI) against the fp64 oracle.
+
+Tolerances: relative L2 over the compared tensor <= 1e-5 with fp32 inputs and <= 2e-2 with bf16
+inputs (fp32 fast weights in both), for the outputs o and the final fast weights W_out.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle as O
+import linear_attention_chunk_amd as T
+from gpu_util import bulk_ttt_inputs, full_ttt_inputs, host, rel, say
+
+pytestmark = pytest.mark.gpu
+
+TOL = {False: 1e-5, True: 2e-2}
+
+
+def split_w(Wout, d, m):
+    W = host(Wout)
+    dm = d * m
+    return W[..., :dm].reshape(*W.shape[:-1], m, d), W[..., dm:2 * dm].reshape(*W.shape[:-1], m, d), \
+        W[..., 2 * dm:].reshape(*W.shape[:-1], d, m)
+
+
+def check(o_gpu, W_gpu, o_ref, W_ref, d, m, tol, slices=None, label=""):
+    og = host(o_gpu)
+    Wg = split_w(W_gpu, d, m)
+    if slices is not None:
+        idx = tuple(np.array(s) for s in zip(*slices))
+        og, o_ref = og[idx], o_ref[idx]
+        Wg = [w[idx] for w in Wg]
+        W_ref = [w[idx] for w in W_ref]
+    eo = rel(og, o_ref)
+    ew = max(rel(a, b) for a, b in zip(Wg, W_ref))
+    say(f"  {label} rel_o={eo:.3e} rel_W={ew:.3e} tol={tol}")
+    assert np.isfinite(og).all()
+    assert eo <= tol, f"output rel L2 {eo} > {tol}"
+    assert ew <= tol, f"W_out rel L2 {ew} > {tol}"
+
+
+def run_small(seed, B, H, N, d, m, chunk, mask, rule, bf16, momentum=0.0, last=False, flags=None, ns=5):
+    say(f"ttt case B{B} H{H} N{N} d{d} m{m} b{chunk} mask{mask} rule{rule} mom{momentum} last{last} bf16={bf16}")
+    (q, k, v, eta, W0), (hq, hk, hv, he, W1, W3, W2) = full_ttt_inputs(seed, B, H, N, d, m, bf16)
+    o, Wout = T.ttt_forward(q, k, v, eta, W0, chunk, mask, rule, m_h=m, ns_iters=ns, momentum=momentum,
+                            last_layer_only=last, update_chunks=flags)
+    torch.cuda.synchronize()
+    o_ref, W_ref, _ = O.ttt_forward_ref(hq, hk, hv, he, W1, W3, W2, chunk, mask, rule, ns, momentum, last, flags)
+    check(o, Wout, o_ref, W_ref, d, m, TOL[bf16], label="all slices")
+
+
+def test_config1_tiny_fp32():
+    """B1 H1 N256 b64 d32 m32, fp32, apply-then-update, L2-Normalize(W - g), seed 0."""
+    run_small(0, 1, 1, 256, 32, 32, 64, O.MASK_APPLY_THEN_UPDATE, O.UPD_GD_L2, False)
+
+
+CASES = [
+    # mask, rule, momentum, last_layer_only
+    (O.MASK_APPLY_THEN_UPDATE, O.UPD_GD, 0.0, False),
+    (O.MASK_APPLY_THEN_UPDATE, O.UPD_GD_L2, 0.0, False),
+    (O.MASK_APPLY_THEN_UPDATE, O.UPD_MUON_L2, 0.9, False),
+    (O.MASK_UPDATE_THEN_APPLY, O.UPD_GD_L2, 0.0, False),
+    (O.MASK_UPDATE_THEN_APPLY, O.UPD_MUON, 0.5, True),
+    (O.MASK_APPLY_THEN_UPDATE, O.UPD_GD, 0.9, True),
+]
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("mask,rule,mom,last", CASES)
+def test_modes_ragged(mask, rule, mom, last, bf16):
+    # 3 full chunks of 96 and a tail of 20; m = 160 leaves partial MFMA tiles in every kernel
+    run_small(3, 1, 2, 308, 64, 160, 96, mask, rule, bf16, mom, last)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_full_mask_and_strided(bf16):
+    run_small(4, 2, 1, 200, 32, 96, 200, O.MASK_FULL, O.UPD_GD_L2, bf16)
+    run_small(5, 1, 2, 256, 64, 64, 64, O.MASK_STRIDED, O.UPD_MUON_L2, bf16, flags=[1, 0, 1, 0])
+
+
+def test_tall_and_wide_muon_fp32():
+    # d > m exercises the other Gram side for W1/W3 and W2
+    run_small(6, 1, 1, 128, 96, 32, 64, O.MASK_APPLY_THEN_UPDATE, O.UPD_MUON_L2, False, ns=3)
+
+
+def test_zero_tokens_returns_w0():
+    (q, k, v, eta, W0), (hq, hk, hv, he, W1, W3, W2) = full_ttt_inputs(0, 2, 2, 0, 32, 64, True)
+    o, Wout = T.ttt_forward(q, k, v, eta, W0, 16, O.MASK_APPLY_THEN_UPDATE, O.UPD_GD_L2, m_h=64)
+    torch.cuda.synchronize()
+    assert o.numel() == 0
+    Wg = host(Wout)
+    ref = host(W0)
+    assert np.array_equal(Wg[0], ref) and np.array_equal(Wg[1], ref)
+
+
+def test_deterministic_and_chained():
+    say("determinism + chaining")
+    B, H, N, d, m, chunk = 1, 2, 256, 64, 128, 64
+    (q, k, v, eta, W0), _ = full_ttt_inputs(7, B, H, N, d, m, True)
+    M = torch.zeros((B, H, 3 * d * m), dtype=torch.float32, device="cuda")
+    o1, W1 = T.ttt_forward(q, k, v, eta, W0, chunk, O.MASK_APPLY_THEN_UPDATE, O.UPD_MUON_L2, m_h=m, momentum=0.9,
+                           M=M)
+    M2 = torch.zeros_like(M)
+    o2, W2 = T.ttt_forward(q, k, v, eta, W0, chunk, O.MASK_APPLY_THEN_UPDATE, O.UPD_MUON_L2, m_h=m, momentum=0.9,
+                           M=M2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(W1, W2) and torch.equal(M, M2)
+    # first half, then second half from (W_out, M) of the first: identical to one call
+    h = N // 2
+    Ma = torch.zeros_like(M)
+    oa, Wa = T.ttt_forward(q[:, :, :h].contiguous(), k[:, :, :h].contiguous(), v[:, :, :h].contiguous(),
+                           eta[:, :, :h].contiguous(), W0, chunk, O.MASK_APPLY_THEN_UPDATE, O.UPD_MUON_L2, m_h=m,
+                           momentum=0.9, M=Ma)
+    ob, Wb = T.ttt_forward(q[:, :, h:].contiguous(), k[:, :, h:].contiguous(), v[:, :, h:].contiguous(),
+                           eta[:, :, h:].contiguous(), Wa, chunk, O.MASK_APPLY_THEN_UPDATE, O.UPD_MUON_L2, m_h=m,
+                           momentum=0.9, M=Ma)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([oa, ob], dim=2), o1)
+    assert torch.equal(Wb, W1) and torch.equal(Ma, M)
+
+
+FULL = {
+    # the LaCT language-model layer: B8 H4 N32768 d384 m768, chunk 2048, GD + L2
+    "lact_lm_gd_l2": dict(B=8, H=4, N=32768, d=384, m=768, chunk=2048, mask=O.MASK_APPLY_THEN_UPDATE,
+                          rule=O.UPD_GD_L2, mom=0.0, flags=None),
+    # the same shapes with momentum 0.9 and Muon (5 Newton-Schulz steps) before L2
+    "lact_lm_muon": dict(B=8, H=4, N=32768, d=384, m=768, chunk=2048, mask=O.MASK_APPLY_THEN_UPDATE,
+                         rule=O.UPD_MUON_L2, mom=0.9, flags=None),
+    # view-synthesis strided mask: 16 chunks of 4096, updates on the first 12, Muon, no momentum
+    "nvs_strided_muon": dict(B=2, H=4, N=65536, d=256, m=512, chunk=4096, mask=O.MASK_STRIDED,
+                             rule=O.UPD_MUON_L2, mom=0.0, flags=[1] * 12 + [0] * 4),
+}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_full_size_sampled_slices(name):
+    c = FULL[name]
+    B, H, N, d, m = c["B"], c["H"], c["N"], c["d"], c["m"]
+    sample = [(0, 0), (B - 1, H - 1)]
+    say(f"full-size {name}: sampled slices {sample}")
+    q, k, v, eta, W0, ex, W = bulk_ttt_inputs(0, B, H, N, d, m, True, exact=sample)
+    o, Wout = T.ttt_forward(q, k, v, eta, W0, c["chunk"], c["mask"], c["rule"], m_h=m, momentum=c["mom"],
+                            update_chunks=c["flags"])
+    torch.cuda.synchronize()
+    say("  gpu done; oracle on sampled slices")
+    for (b, h) in sample:
+        qs, ks, vs, es = ex[(b, h)]
+        o_ref, W_ref, _ = O.ttt_scan_ref(qs, ks, vs, es, W[0][h], W[1][h], W[2][h], c["chunk"], c["mask"], c["rule"],
+                                         5, c["mom"], False, c["flags"])
+        og = host(o[b, h])
+        Wg = split_w(Wout[b, h], d, m)
+        eo = rel(og, o_ref)
+        ew = max(rel(a, bb) for a, bb in zip(Wg, W_ref))
+        say(f"  slice ({b},{h}) rel_o={eo:.3e} rel_W={ew:.3e}")
+        assert eo <= 2e-2 and ew <= 2e-2

@@ -192,10 +192,10 @@ def stepper(q, k, v, eta, W1, W3, W2, chunk, mask, rule, ns_iters=5, beta=0.0, l
                 if beta:
                     M[i] = beta * M[i] + G[i]
                     U = M[i]
-                if rule == O.UPD_MUON_L2:
+                if rule in (O.UPD_MUON_L2, O.UPD_MUON):
                     U = ns_via_svd(U, ns_iters)
                 W[i] = W[i] - U
-                if rule != O.UPD_GD:
+                if rule in (O.UPD_GD_L2, O.UPD_MUON_L2):
                     W[i] = rownorm_loops(W[i])
         if not first:
             o[lo:hi] = np.stack([f_token(*W, x) for x in q[lo:hi]])
@@ -211,6 +211,7 @@ CASES = [
     (O.MASK_UPDATE_THEN_APPLY, O.UPD_MUON_L2, 0.0, True, 3),
     (O.MASK_STRIDED, O.UPD_MUON_L2, 0.0, False, 3),
     (O.MASK_FULL, O.UPD_GD_L2, 0.0, False, 8),
+    (O.MASK_APPLY_THEN_UPDATE, O.UPD_MUON, 0.5, False, 3),
 ]
 
 
