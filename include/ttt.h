@@ -30,8 +30,8 @@
  *     up at the caller's next synchronisation.  ttt_last_error() gives a message for the
  *     latest failed call on the calling thread.
  *   - Aliasing: o must not overlap q, k, v or eta.  W_out may not overlap W0.
- *   - Thread safety: calls on different streams may run concurrently; the library has no
- *     mutable global state besides the per-thread error message.
+ *   - Thread safety: calls on different streams may run concurrently; the only mutable global
+ *     state is the per-thread error message and the optional launch profiler below.
  */
 #ifndef TTT_MI355X_H
 #define TTT_MI355X_H
@@ -140,6 +140,20 @@ ttt_status linattn_workspace_bytes(const linattn_desc* desc, size_t* bytes);
 ttt_status linattn_forward(const linattn_desc* desc, const void* q, const void* k, const void* v,
                            const float* eta, const float* S0, void* o, float* S_out,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+
+/*
+ * Optional per-kernel timing for measurement tools (not needed for normal use).  While enabled,
+ * every kernel launch this library makes is bracketed by two HIP events recorded on the stream
+ * it is launched on.  ttt_profile_read waits for the recorded events, writes for each kernel
+ * class i < n the summed milliseconds ms[i] and the launch count count[i] since the previous
+ * read, and forgets them.  Kernel classes are numbered 0 .. TTT_PROF_KERNELS-1 and named by
+ * ttt_profile_kernel_name.  Enabling or reading while another thread launches is allowed.
+ */
+#define TTT_PROF_KERNELS 8
+ttt_status ttt_profile_enable(int32_t on);
+ttt_status ttt_profile_read(float* ms, int32_t* count, int32_t n);
+const char* ttt_profile_kernel_name(int32_t i);
 
 #ifdef __cplusplus
 }

@@ -21,7 +21,9 @@ EXPORTS = (
     "ttt_abi_version", "ttt_status_string", "ttt_last_error",
     "ttt_workspace_bytes", "ttt_forward",
     "linattn_workspace_bytes", "linattn_forward",
+    "ttt_profile_enable", "ttt_profile_read", "ttt_profile_kernel_name",
 )
+PROF_KERNELS = 8
 
 
 class TttDesc(ctypes.Structure):
@@ -75,8 +77,26 @@ def lib() -> ctypes.CDLL:
     L.linattn_forward.restype = c_int32
     L.linattn_forward.argtypes = [POINTER(LinattnDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                   c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+    L.ttt_profile_enable.restype = c_int32
+    L.ttt_profile_enable.argtypes = [c_int32]
+    L.ttt_profile_read.restype = c_int32
+    L.ttt_profile_read.argtypes = [POINTER(c_float), POINTER(c_int32), c_int32]
+    L.ttt_profile_kernel_name.restype = ctypes.c_char_p
+    L.ttt_profile_kernel_name.argtypes = [c_int32]
     _lib = L
     return L
+
+
+def profile_enable(on: bool) -> None:
+    check(lib().ttt_profile_enable(1 if on else 0))
+
+
+def profile_read() -> dict:
+    """{kernel name: (total ms, launches)} since the previous read (waits for the events)."""
+    ms = (c_float * PROF_KERNELS)()
+    cnt = (c_int32 * PROF_KERNELS)()
+    check(lib().ttt_profile_read(ms, cnt, PROF_KERNELS))
+    return {lib().ttt_profile_kernel_name(i).decode(): (float(ms[i]), int(cnt[i])) for i in range(PROF_KERNELS)}
 
 
 def check(status: int) -> None:

@@ -22,6 +22,18 @@ inline ttt_status fail(ttt_status s, const char* fmt, ...) {
     return s;
 }
 
+// kernel classes of the optional launch profiler (ttt_profile_*)
+enum ProfKernel { PK_UP = 0, PK_DOWN, PK_UPDATE, PK_MUON_PREP, PK_NS_INIT, PK_NS_GRAM, PK_NS_STEP, PK_LINATTN };
+
+// Brackets one launch with events on its stream while profiling is enabled; no-op otherwise.
+struct ProfScope {
+    int id;
+    hipStream_t st;
+    hipEvent_t a = nullptr, b = nullptr;
+    ProfScope(int id_, hipStream_t st_);
+    ~ProfScope();
+};
+
 inline ttt_status check_launch(const char* what) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(TTT_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));

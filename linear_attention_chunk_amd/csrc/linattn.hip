@@ -297,7 +297,10 @@ static ttt_status validate_lin(const linattn_desc* D) {
 
 template <typename T, int DK>
 static ttt_status launch_lin(LinArgs<T>& a, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((k_linattn<T, DK>), dim3(grid), dim3(kThreads), 0, st, a);
+    {
+        ProfScope ps(PK_LINATTN, st);
+        hipLaunchKernelGGL((k_linattn<T, DK>), dim3(grid), dim3(kThreads), 0, st, a);
+    }
     return check_launch("k_linattn");
 }
 

@@ -471,7 +471,10 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
     {  // W0 -> master copy and shadows
         UpdArgs<T> u{W0, 3 * dm, D.w0_per_batch ? 0 : 1, D.H, nullptr, 0, Wf[0], L.wf_stride, sh[0], L.sh_stride,
                      d, m, 0, 0};
-        hipLaunchKernelGGL(k_update<T>, dim3(S * upd_blocks), dim3(kThreads), 0, st, u);
+        {
+            ProfScope ps(PK_UPDATE, st);
+            hipLaunchKernelGGL(k_update<T>, dim3(S * upd_blocks), dim3(kThreads), 0, st, u);
+        }
         if ((rc = check_launch("k_update(init)")) != TTT_OK) return rc;
     }
     int cur = 0;
@@ -500,11 +503,17 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
         a.nG2 = a.lu ? ntd * ntm : 0;
         a.nO = a.la ? (int)cdiv(a.la, 128) * ntd : 0;
         if (a.nQ + a.nK) {
-            hipLaunchKernelGGL(k_up<T>, dim3(S * (a.nQ + a.nK)), dim3(kThreads), 0, st, a);
+            {
+                ProfScope ps(PK_UP, st);
+                hipLaunchKernelGGL(k_up<T>, dim3(S * (a.nQ + a.nK)), dim3(kThreads), 0, st, a);
+            }
             if ((rc = check_launch("k_up")) != TTT_OK) return rc;
         }
         if (2 * a.nG1 + a.nG2 + a.nO) {
-            hipLaunchKernelGGL(k_down<T>, dim3(S * (2 * a.nG1 + a.nG2 + a.nO)), dim3(kThreads), 0, st, a);
+            {
+                ProfScope ps(PK_DOWN, st);
+                hipLaunchKernelGGL(k_down<T>, dim3(S * (2 * a.nG1 + a.nG2 + a.nO)), dim3(kThreads), 0, st, a);
+            }
             if ((rc = check_launch("k_down")) != TTT_OK) return rc;
         }
         if (a.lu == 0) continue;
@@ -512,7 +521,10 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
         const float* U = G;
         if (muon || mom) {
             PrepArgs pa{G, L.g_stride, M, 3 * dm, D.momentum, part, L.nblk, dm, mat0, nmat};
-            hipLaunchKernelGGL(k_muon_prep, dim3(S * nmat * L.nblk), dim3(kThreads), 0, st, pa);
+            {
+                ProfScope ps(PK_MUON_PREP, st);
+                hipLaunchKernelGGL(k_muon_prep, dim3(S * nmat * L.nblk), dim3(kThreads), 0, st, pa);
+            }
             if ((rc = check_launch("k_muon_prep")) != TTT_OK) return rc;
             if (mom) U = M;
         }
@@ -521,7 +533,10 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
             float* Xf = (float*)(ws + L.xf);
             NSArgs<T> na{U, 3 * dm, part, L.nblk, Xf, L.x_stride, Xb[1], Xb[0], (T*)(ws + L.gram), L.gram_stride,
                          d, m, mat0, nmat, 0};
-            hipLaunchKernelGGL(k_ns_init<T>, dim3(S * nmat * L.nblk), dim3(kThreads), 0, st, na);
+            {
+                ProfScope ps(PK_NS_INIT, st);
+                hipLaunchKernelGGL(k_ns_init<T>, dim3(S * nmat * L.nblk), dim3(kThreads), 0, st, na);
+            }
             if ((rc = check_launch("k_ns_init")) != TTT_OK) return rc;
             const int p = d < m ? d : m;
             const int gt = (int)(cdiv(p, 128) * cdiv(p, 128));
@@ -530,10 +545,16 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
                 na.Xin = Xb[it & 1];
                 na.Xout = Xb[(it + 1) & 1];
                 na.tiles = gt;
-                hipLaunchKernelGGL(k_ns_gram<T>, dim3(S * nmat * gt), dim3(kThreads), 0, st, na);
+                {
+                    ProfScope ps(PK_NS_GRAM, st);
+                    hipLaunchKernelGGL(k_ns_gram<T>, dim3(S * nmat * gt), dim3(kThreads), 0, st, na);
+                }
                 if ((rc = check_launch("k_ns_gram")) != TTT_OK) return rc;
                 na.tiles = stt;
-                hipLaunchKernelGGL(k_ns_step<T>, dim3(S * nmat * stt), dim3(kThreads), 0, st, na);
+                {
+                    ProfScope ps(PK_NS_STEP, st);
+                    hipLaunchKernelGGL(k_ns_step<T>, dim3(S * nmat * stt), dim3(kThreads), 0, st, na);
+                }
                 if ((rc = check_launch("k_ns_step")) != TTT_OK) return rc;
             }
             U = Xf;
@@ -541,7 +562,10 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
         const int norm = (D.rule == TTT_UPD_GD_L2 || D.rule == TTT_UPD_MUON_L2) ? 1 : 0;
         UpdArgs<T> u{Wf[cur], L.wf_stride, 0, D.H, U, 3 * dm, Wf[cur ^ 1], L.wf_stride, sh[cur ^ 1], L.sh_stride,
                      d, m, norm, D.last_layer_only};
-        hipLaunchKernelGGL(k_update<T>, dim3(S * upd_blocks), dim3(kThreads), 0, st, u);
+        {
+            ProfScope ps(PK_UPDATE, st);
+            hipLaunchKernelGGL(k_update<T>, dim3(S * upd_blocks), dim3(kThreads), 0, st, u);
+        }
         if ((rc = check_launch("k_update")) != TTT_OK) return rc;
         cur ^= 1;
     }
