@@ -7,10 +7,12 @@
 // one whose source is k-strided (token-major data contracted over tokens) is transposed in
 // registers, one VEC x VEC block per thread, on its way into LDS.
 //
-// MFMA fragments: for v_mfma_f32_16x16x32_bf16 lane l supplies row (l % 16) and the 8 k-values of
-// group (l / 16); for fp32 four v_mfma_f32_16x16x4_f32 consume the 4 k-values of a lane's 16-byte
-// read one at a time.  A and B use the same lane-to-k assignment, so the contraction is complete
-// whatever order the hardware walks k in.  Result element r of lane l is C[4*(l/16) + r][l % 16].
+// MFMA fragments.  The tile engine works in 32 x 32 output blocks: for v_mfma_f32_32x32x16_bf16
+// lane l supplies row (l % 32) and the 8 k-values of group (l / 32) of a 16-wide k window; in fp32
+// four v_mfma_f32_32x32x2_f32 consume the 4 k-values of a lane's 16-byte read one at a time.  A and
+// B use the same lane-to-k assignment, so the contraction is complete whatever order the hardware
+// walks k in.  Result element r of lane l is C[8*(r/4) + 4*(l/32) + r%4][l % 32].  (The 16 x 16
+// helpers, Elt<T>::mma, follow the same scheme with 16-row blocks: C[4*(l/16) + r][l % 16].)
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -20,6 +22,7 @@ namespace ttt {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;
 
@@ -27,6 +30,13 @@ __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint
 __device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+// Workgroup barrier for handing LDS tiles between waves.  It waits for this wave's own LDS
+// operations (lgkmcnt) and meets at s_barrier, but leaves global loads in flight: __syncthreads()
+// adds a release fence that also drains every outstanding global load (vmcnt(0)), which would
+// cancel the prefetch of later stages.  The asm is a compiler memory barrier, so no LDS access
+// moves across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <typename T> struct Elt;
 
@@ -66,6 +76,22 @@ template <> struct Elt<float> {
     }
 };
 
+// 32 x 32 blocks: one 32-byte k window per call (16 bf16 / 8 fp32 values of k)
+template <typename T> struct Mma32;
+template <> struct Mma32<uint16_t> {
+    __device__ static void mma(f32x16_t& c, const u32x4_t& a, const u32x4_t& b) {
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    }
+};
+template <> struct Mma32<float> {
+    __device__ static void mma(f32x16_t& c, const u32x4_t& a, const u32x4_t& b) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[s]), __uint_as_float(b[s]), c, 0, 0, 0);
+    }
+};
+
 // One operand of a tile.  Element (row, k) of the tile is p[row * ld + k] for a k-contiguous
 // source and p[k * ld + row] for a k-strided one.  Rows at or beyond `rows` and k at or beyond
 // `kvalid` read as zero and are never dereferenced.
@@ -87,17 +113,37 @@ template <typename T, int R, int SEG> struct Stager<T, R, SEG, false> {
     static constexpr int NV = R * VPR;
     static constexpr int PER = (NV + kThreads - 1) / kThreads;
     static constexpr int PITCH = Pitch<SEG>::value;
+    // Vector v goes to (row, c).  With one 64-byte segment per row (SEG == 1) four lanes fill a
+    // row; the second four lanes of each group of eight take the row 4 further on (80-byte pitch:
+    // 4 rows = 320 bytes, which lands on the other 16 of the 32 banks), so every 8-lane store is
+    // bank-conflict-free while each row is still read as 64 contiguous bytes.
+    static_assert(SEG != 1 || R % 8 == 0, "tile rows must be a multiple of 8");
+    __device__ static void place(int v, int& row, int& c) {
+        if constexpr (SEG == 1) {
+            const int q = v >> 2, g = q >> 1, h = q & 1;
+            row = (g & 3) + 4 * h + 8 * (g >> 2);
+            c = v & 3;
+        } else {
+            row = v / VPR;
+            c = v % VPR;
+        }
+    }
     u32x4_t r[PER];
+    uint32_t ok;  // bit i: r[i] is in range
+    // Branch-free loads: an out-of-range vector is loaded from the operand's first element (always
+    // valid) and zeroed only when stored, so no load result is consumed before the LDS store and
+    // the loads of a later stage can stay in flight.
     __device__ __forceinline__ void load(const Opnd<T>& o, int k0) {
+        ok = 0;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int v = threadIdx.x + i * kThreads;
-            const int row = v / VPR, c = v % VPR;
+            int row, c;
+            place(v, row, c);
             const int k = k0 + c * VEC;
-            u32x4_t val = {0u, 0u, 0u, 0u};
-            if ((NV % kThreads == 0 || v < NV) && row < o.rows && k < o.kvalid)
-                val = *reinterpret_cast<const u32x4_t*>(o.p + (int64_t)row * o.ld + k);
-            r[i] = val;
+            const bool in = (NV % kThreads == 0 || v < NV) && row < o.rows && k < o.kvalid;
+            r[i] = *reinterpret_cast<const u32x4_t*>(o.p + (in ? (int64_t)row * o.ld + k : 0));
+            ok |= (uint32_t)in << i;
         }
     }
     __device__ __forceinline__ void store(char* lds) const {
@@ -105,143 +151,296 @@ template <typename T, int R, int SEG> struct Stager<T, R, SEG, false> {
         for (int i = 0; i < PER; ++i) {
             const int v = threadIdx.x + i * kThreads;
             if (NV % kThreads == 0 || v < NV) {
-                const int row = v / VPR, c = v % VPR;
-                *reinterpret_cast<u32x4_t*>(lds + row * PITCH + c * 16) = r[i];
+                int row, c;
+                place(v, row, c);
+                *reinterpret_cast<u32x4_t*>(lds + row * PITCH + c * 16) =
+                    ((ok >> i) & 1u) ? r[i] : u32x4_t{0u, 0u, 0u, 0u};
             }
         }
     }
 };
 
-// k-strided source: each thread loads VEC k-rows of VEC row-elements and transposes them
+// k-strided source.  A thread takes a unit of KPT consecutive k-rows by VEC row-elements (KPT 16-byte
+// loads), and writes, for each of its VEC rows, the KPT k-values as one 4/8/16-byte LDS store.  All
+// threads take part (KPT is chosen so that there are about as many units as threads).  The rows
+// are stored permuted: logical row rb*VEC + j lives in LDS row j*RB + rb, so that the lanes of one
+// store (consecutive rb) hit consecutive LDS rows and distinct banks.  Fragment reads stay on
+// consecutive LDS rows; the tile maps result rows back through row_of().
 template <typename T, int R, int SEG> struct Stager<T, R, SEG, true> {
+    static constexpr int ES = (int)sizeof(T);
     static constexpr int VEC = Elt<T>::VEC;
-    static constexpr int KB = SEG * 4;     // k-blocks of VEC per stage (SEG*64 bytes of k)
-    static constexpr int RB = R / VEC;     // row blocks
-    static constexpr int NB = KB * RB;
-    static constexpr int PER = (NB + kThreads - 1) / kThreads;
+    static constexpr int KSTEP = SEG * 64 / ES;   // k per stage
+    static constexpr int RB = R / VEC;            // row blocks
+    static constexpr int KMIN = ES == 2 ? 2 : 1;  // at least one 32-bit word per store
+    static constexpr int KWANT = KSTEP * RB / kThreads;
+    static constexpr int KPT = KWANT <= KMIN ? KMIN : (KWANT >= VEC ? VEC : (KWANT >= 4 ? 4 : 2));
+    static constexpr int KC = KSTEP / KPT;
+    static constexpr int NU = KC * RB;
+    static constexpr int PER = (NU + kThreads - 1) / kThreads;
     static constexpr int PITCH = Pitch<SEG>::value;
-    static_assert(R % VEC == 0, "tile rows must be a multiple of the vector width");
-    u32x4_t r[PER][VEC];
+    static constexpr int WORDS = KPT * ES / 4;   // 32-bit words per row piece
+    // lanes of one LDS store cycle (128 bytes): 8 consecutive row blocks x KG k-chunks, which puts
+    // the group's pieces on 32 distinct banks (rows are 20 dwords apart, chunks KPT*ES bytes apart)
+    static constexpr int KG = 128 / (KPT * ES) / 8;
+    static_assert(R % VEC == 0 && KSTEP % KPT == 0 && RB % 8 == 0 && KC % KG == 0, "bad k-strided staging shape");
+    __device__ static int row_of(int lds_row) { return (lds_row % RB) * VEC + lds_row / RB; }
+    __device__ static void place(int u, int& rb, int& kc) {
+        const int rb_lo = u % 8;
+        int t = u / 8;
+        const int kc_lo = t % KG;
+        t /= KG;
+        rb = (t % (RB / 8)) * 8 + rb_lo;
+        kc = (t / (RB / 8)) * KG + kc_lo;
+    }
+
+    u32x4_t r[PER][KPT];
+    uint32_t ok;  // bit i * KPT + e: r[i][e] is in range (see the k-contiguous stager)
+    static_assert(PER * KPT <= 32, "too many vectors per thread");
     __device__ __forceinline__ void load(const Opnd<T>& o, int k0) {
+        ok = 0;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int blk = threadIdx.x + i * kThreads;
-            const int kb = blk / RB, rb = blk % RB;
-            const bool live = (NB % kThreads == 0 || blk < NB) && rb * VEC < o.rows;
+            const int u = threadIdx.x + i * kThreads;
+            int rb, kc;
+            place(u, rb, kc);
+            const bool live = (NU % kThreads == 0 || u < NU) && rb * VEC < o.rows;
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                const int k = k0 + kb * VEC + e;
-                u32x4_t val = {0u, 0u, 0u, 0u};
-                if (live && k < o.kvalid)
-                    val = *reinterpret_cast<const u32x4_t*>(o.p + (int64_t)k * o.ld + rb * VEC);
-                r[i][e] = val;
+            for (int e = 0; e < KPT; ++e) {
+                const int k = k0 + kc * KPT + e;
+                const bool in = live && k < o.kvalid;
+                r[i][e] = *reinterpret_cast<const u32x4_t*>(o.p + (in ? (int64_t)k * o.ld + rb * VEC : 0));
+                ok |= (uint32_t)in << (i * KPT + e);
             }
+        }
+    }
+    __device__ __forceinline__ uint32_t elt(int i, int e, int w) const {
+        return ((ok >> (i * KPT + e)) & 1u) ? r[i][e][w] : 0u;
+    }
+    __device__ __forceinline__ uint32_t word(int i, int j, int w) const {
+        if constexpr (ES == 2) {
+            const uint32_t x = elt(i, 2 * w, j >> 1), y = elt(i, 2 * w + 1, j >> 1);
+            return (j & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
+        } else {
+            return elt(i, w, j);
         }
     }
     __device__ __forceinline__ void store(char* lds) const {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int blk = threadIdx.x + i * kThreads;
-            if (NB % kThreads == 0 || blk < NB) {
-                const int kb = blk / RB, rb = blk % RB;
-                u32x4_t t[VEC];
-                Elt<T>::transpose(r[i], t);
+            const int u = threadIdx.x + i * kThreads;
+            if (NU % kThreads == 0 || u < NU) {
+                int rb, kc;
+                place(u, rb, kc);
 #pragma unroll
-                for (int j = 0; j < VEC; ++j)
-                    *reinterpret_cast<u32x4_t*>(lds + (rb * VEC + j) * PITCH + kb * 16) = t[j];
+                for (int j = 0; j < VEC; ++j) {
+                    char* dst = lds + (j * RB + rb) * PITCH + kc * KPT * ES;
+                    if constexpr (WORDS == 1) {
+                        *reinterpret_cast<uint32_t*>(dst) = word(i, j, 0);
+                    } else if constexpr (WORDS == 2) {
+                        typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+                        *reinterpret_cast<u2*>(dst) = u2{word(i, j, 0), word(i, j, 1)};
+                    } else {
+                        *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{word(i, j, 0), word(i, j, 1), word(i, j, 2), word(i, j, 3)};
+                    }
+                }
             }
         }
     }
 };
 
-// Tile engine.  NA A-operands of BM rows and NB B-operands of BN rows are staged per k-step;
-// accumulator p is A[PM::a[p]] x B[PM::b[p]].  Waves form a WGM x (4/WGM) grid over the tile.
-template <typename T, int BM_, int BN_, int SEG, int WGM, int NA, int NB, int NP>
+template <typename T, int R, int SEG, bool KS> struct RowMap {
+    __device__ static int row_of(int r) { return r; }
+};
+template <typename T, int R, int SEG> struct RowMap<T, R, SEG, true> {
+    __device__ static int row_of(int r) { return Stager<T, R, SEG, true>::row_of(r); }
+};
+
+// Tile engine.  NA A-operands of BM rows and NB B-operands of BN rows are staged per k-step
+// (k-strided sources when KSA / KSB); accumulator p is A[PM::a[p]] x B[PM::b[p]].  Waves form a
+// WGM x (4/WGM) grid over the tile and each wave owns (WM/32) x (WN/32) blocks of 32 x 32 per
+// accumulator.  Global loads run two stages ahead of the MFMAs (two register sets), LDS is
+// double-buffered, one barrier per stage.
+template <typename T, int BM_, int BN_, int SEG, int WGM, int NA, int NB, int NP, bool KSA, bool KSB>
 struct Tile {
     static constexpr int BM = BM_, BN = BN_;
     static constexpr int WGN = 4 / WGM;
     static constexpr int WM = BM / WGM, WN = BN / WGN;
-    static constexpr int FM = WM / 16, FN = WN / 16;
+    static constexpr int FM = WM / 32, FN = WN / 32;
     static constexpr int PITCH = Pitch<SEG>::value;
     static constexpr int A_BYTES = BM * PITCH, B_BYTES = BN * PITCH;
     static constexpr int STAGE = NA * A_BYTES + NB * B_BYTES;
     static constexpr int LDS = 2 * STAGE;
     static constexpr int KSTEP = SEG * 64 / (int)sizeof(T);  // k elements per stage
-    static_assert(WGM * WGN == 4 && FM >= 1 && FN >= 1, "bad wave grid");
+    static_assert(WGM * WGN == 4 && FM >= 1 && FN >= 1 && WM % 32 == 0 && WN % 32 == 0, "bad wave grid");
+    using SA = Stager<T, BM, SEG, KSA>;
+    using SB = Stager<T, BN, SEG, KSB>;
 
-    f32x4_t acc[NP][FM][FN];
+    f32x16_t acc[NP][FM][FN];
 
-    template <class PM, bool KSA, bool KSB>
-    __device__ __forceinline__ void run(const Opnd<T> (&A)[NA], const Opnd<T> (&B)[NB], int K, char* lds) {
+    struct Regs {
+        SA a[NA];
+        SB b[NB];
+    };
+
+    __device__ __forceinline__ static void issue(Regs& g, const Opnd<T> (&A)[NA], const Opnd<T> (&B)[NB], int k0) {
+#pragma unroll
+        for (int a = 0; a < NA; ++a) g.a[a].load(A[a], k0);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) g.b[b].load(B[b], k0);
+    }
+    __device__ __forceinline__ static void put(const Regs& g, char* st) {
+#pragma unroll
+        for (int a = 0; a < NA; ++a) g.a[a].store(st + a * A_BYTES);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) g.b[b].store(st + NA * A_BYTES + b * B_BYTES);
+    }
+
+    __device__ __forceinline__ void zero() {
 #pragma unroll
         for (int p = 0; p < NP; ++p)
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j) acc[p][i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        Stager<T, BM, SEG, KSA> sa[NA];
-        Stager<T, BN, SEG, KSB> sb[NB];
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[p][i][j][r] = 0.f;
+    }
+
+    // One output tile: acc = sum over k of the staged products.  Global loads run two stages
+    // ahead (register sets g0 / g1), LDS is double-buffered, one LDS-only barrier per stage.
+    template <class PM>
+    __device__ __forceinline__ void run(const Opnd<T> (&A)[NA], const Opnd<T> (&B)[NB], int K, char* lds) {
+        zero();
         const int nk = (K + KSTEP - 1) / KSTEP;
         if (nk <= 0) return;
-#pragma unroll
-        for (int a = 0; a < NA; ++a) sa[a].load(A[a], 0);
-#pragma unroll
-        for (int b = 0; b < NB; ++b) sb[b].load(B[b], 0);
-#pragma unroll
-        for (int a = 0; a < NA; ++a) sa[a].store(lds + a * A_BYTES);
-#pragma unroll
-        for (int b = 0; b < NB; ++b) sb[b].store(lds + NA * A_BYTES + b * B_BYTES);
-        __syncthreads();
-        for (int it = 0; it < nk; ++it) {
-            const bool more = it + 1 < nk;
-            if (more) {
-#pragma unroll
-                for (int a = 0; a < NA; ++a) sa[a].load(A[a], (it + 1) * KSTEP);
-#pragma unroll
-                for (int b = 0; b < NB; ++b) sb[b].load(B[b], (it + 1) * KSTEP);
-            }
-            compute<PM>(lds + (it & 1) * STAGE);
-            if (more) {
-                char* nxt = lds + ((it + 1) & 1) * STAGE;
-#pragma unroll
-                for (int a = 0; a < NA; ++a) sa[a].store(nxt + a * A_BYTES);
-#pragma unroll
-                for (int b = 0; b < NB; ++b) sb[b].store(nxt + NA * A_BYTES + b * B_BYTES);
-            }
-            __syncthreads();
+        Regs g0, g1;
+        issue(g0, A, B, 0);
+        put(g0, lds);
+        if (nk > 1) issue(g0, A, B, KSTEP);
+        if (nk > 2) issue(g1, A, B, 2 * KSTEP);
+        lds_barrier();
+        int s = 0;
+        for (; s + 4 < nk; s += 2) {  // steady state: no tail conditions inside
+            compute<PM>(lds);
+            put(g0, lds + STAGE);
+            issue(g0, A, B, (s + 3) * KSTEP);
+            lds_barrier();
+            compute<PM>(lds + STAGE);
+            put(g1, lds);
+            issue(g1, A, B, (s + 4) * KSTEP);
+            lds_barrier();
         }
+        auto step = [&](Regs& g, int st) {
+            compute<PM>(lds + (st & 1) * STAGE);
+            if (st + 1 < nk) put(g, lds + ((st + 1) & 1) * STAGE);
+            if (st + 3 < nk) issue(g, A, B, (st + 3) * KSTEP);
+            lds_barrier();
+        };
+        for (; s + 1 < nk; s += 2) {
+            step(g0, s);
+            step(g1, s + 1);
+        }
+        if (s < nk) step(g0, s);
+    }
+
+    // A sequence of ntiles output tiles with the same contraction length K, walked as one
+    // continuous pipeline: the loads for the next tile's first stages are in flight while the
+    // current tile finishes and while epi(t) (which reads acc through for_each) runs.
+    // ops(t, A, B) fills the operand descriptors of tile t.
+    template <class PM, class Ops, class Epi>
+    __device__ __forceinline__ void run_tiles(int ntiles, Ops&& ops, int K, char* lds, Epi&& epi) {
+        zero();
+        const int nk = (K + KSTEP - 1) / KSTEP;
+        if (nk <= 0 || ntiles <= 0) {
+            for (int t = 0; t < ntiles; ++t) epi(t);
+            return;
+        }
+        const int total = ntiles * nk;
+        Opnd<T> A[NA], B[NB];
+        int cur_t = -1;
+        auto issue_stage = [&](Regs& g, int s) {
+            const int t = s / nk;
+            if (t != cur_t) {
+                ops(t, A, B);
+                cur_t = t;
+            }
+            issue(g, A, B, (s - t * nk) * KSTEP);
+        };
+        Regs g0, g1;
+        issue_stage(g0, 0);
+        put(g0, lds);
+        if (total > 1) issue_stage(g0, 1);
+        if (total > 2) issue_stage(g1, 2);
+        lds_barrier();
+        // invariant at the top of stage s: LDS[s & 1] holds stage s; the register set of parity
+        // (s & 1) holds stage s + 1 and the other set holds stage s + 2 (each if it exists)
+        auto finish = [&](int s) {
+            if ((s + 1) % nk == 0) {
+                epi(s / nk);
+                if (s + 1 < total) zero();  // the last tile's acc stays readable after return
+            }
+        };
+        int s = 0;
+        // steady state, free of tail conditions so that the compiler can track which loads are
+        // still in flight: every stage stores stage s + 1 and issues stage s + 3
+        for (; s + 4 < total; s += 2) {
+            compute<PM>(lds);
+            finish(s);
+            put(g0, lds + STAGE);
+            issue_stage(g0, s + 3);
+            lds_barrier();
+            compute<PM>(lds + STAGE);
+            finish(s + 1);
+            put(g1, lds);
+            issue_stage(g1, s + 4);
+            lds_barrier();
+        }
+        // the last (at most four) stages
+        auto step = [&](Regs& g, int st) {
+            compute<PM>(lds + (st & 1) * STAGE);
+            finish(st);
+            if (st + 1 < total) put(g, lds + ((st + 1) & 1) * STAGE);
+            if (st + 3 < total) issue_stage(g, st + 3);
+            lds_barrier();
+        };
+        for (; s + 1 < total; s += 2) {
+            step(g0, s);
+            step(g1, s + 1);
+        }
+        if (s < total) step(g0, s);
     }
 
     template <class PM>
     __device__ __forceinline__ void compute(const char* st) {
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
         const int wm = wave / WGN, wn = wave % WGN;
-        const int lrow = lane & 15, lk = (lane >> 4) * 16;
+        const int lrow = lane & 31, lk = (lane >> 5) * 16;
 #pragma unroll
-        for (int seg = 0; seg < SEG; ++seg) {
+        for (int win = 0; win < SEG * 2; ++win) {  // 32-byte k windows
             u32x4_t af[NA][FM], bfr[NB][FN];
 #pragma unroll
             for (int a = 0; a < NA; ++a)
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
                     af[a][i] = *reinterpret_cast<const u32x4_t*>(
-                        st + a * A_BYTES + (wm * WM + i * 16 + lrow) * PITCH + seg * 64 + lk);
+                        st + a * A_BYTES + (wm * WM + i * 32 + lrow) * PITCH + win * 32 + lk);
 #pragma unroll
             for (int b = 0; b < NB; ++b)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
                     bfr[b][j] = *reinterpret_cast<const u32x4_t*>(
-                        st + NA * A_BYTES + b * B_BYTES + (wn * WN + j * 16 + lrow) * PITCH + seg * 64 + lk);
+                        st + NA * A_BYTES + b * B_BYTES + (wn * WN + j * 32 + lrow) * PITCH + win * 32 + lk);
 #pragma unroll
             for (int p = 0; p < NP; ++p)
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
-                    for (int j = 0; j < FN; ++j) Elt<T>::mma(acc[p][i][j], af[PM::a[p]][i], bfr[PM::b[p]][j]);
+                    for (int j = 0; j < FN; ++j) Mma32<T>::mma(acc[p][i][j], af[PM::a[p]][i], bfr[PM::b[p]][j]);
         }
     }
 
-    // f(const float (&v)[NP], int row, int col) for every accumulator element of this thread
+    // f(const float (&v)[NP], int row, int col) for every accumulator element of this thread,
+    // with row / col the logical tile coordinates
     template <class F>
     __device__ __forceinline__ void for_each(F&& f) const {
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -249,20 +448,32 @@ struct Tile {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
+            for (int j = 0; j < FN; ++j) {
+                const int col = RowMap<T, BN, SEG, KSB>::row_of(wn * WN + j * 32 + (lane & 31));
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
+                for (int r = 0; r < 16; ++r) {
                     float v[NP];
 #pragma unroll
                     for (int p = 0; p < NP; ++p) v[p] = acc[p][i][j][r];
-                    f(v, wm * WM + i * 16 + (lane >> 4) * 4 + r, wn * WN + j * 16 + (lane & 15));
+                    f(v, RowMap<T, BM, SEG, KSA>::row_of(wm * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)), col);
                 }
+            }
     }
 };
 
 struct PM1 { static constexpr int a[1] = {0}; static constexpr int b[1] = {0}; };
 struct PMQ { static constexpr int a[2] = {0, 0}; static constexpr int b[2] = {0, 1}; };
 struct PMK { static constexpr int a[3] = {0, 0, 1}; static constexpr int b[3] = {0, 1, 2}; };
+struct PMG { static constexpr int a[2] = {0, 1}; static constexpr int b[2] = {0, 0}; };
+
+// Workgroups are dispatched to the 8 XCDs round-robin (block b runs on XCD b % 8).  Renumbering so
+// that the blocks one XCD receives are consecutive logical blocks keeps tiles that share operands
+// (the same scan, the same rows) in the same L2.
+__device__ __forceinline__ int xcd_block(int nblocks) {
+    const int b = blockIdx.x;
+    if (nblocks % 8 != 0) return b;
+    return (b % 8) * (nblocks / 8) + b / 8;
+}
 
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll

@@ -20,6 +20,9 @@
 
 namespace ttt {
 
+constexpr int kUpQRows = 256, kUpKRows = 128;  // token rows per up-kernel tile (query / key)
+constexpr int kORows = 256;                      // token rows per output tile
+
 template <typename T> struct StepArgs {
     const T* q; const T* k; const T* v; const float* eta; T* o;
     int64_t N; int d, m;
@@ -28,21 +31,23 @@ template <typename T> struct StepArgs {
     float* G; int64_t g_stride;                           // [G1 | G3 | G2] fp32
     int64_t a0; int la;                                   // apply chunk: first token, length
     int64_t u0; int lu;                                   // update chunk
-    int nQ, nK;                                           // up-kernel tiles per scan
-    int nG1, nG2, nO;                                     // down-kernel tiles per scan
+    int nQ, nK;                                           // up-kernel workgroups per scan
+    int nG13, nG2, nO;                                    // down-kernel tiles per scan
 };
 
 // ---------------------------------------------------------------------------------------------
 // up: SwiGLU forward of the queries, forward + backward of the keys
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k_up(StepArgs<T> a) {
-    using TQ = Tile<T, 128, 64, 1, 2, 1, 2, 2>;
-    using TK = Tile<T, 128, 64, 1, 2, 2, 3, 3>;
+__global__ __launch_bounds__(kThreads, 2) void k_up(StepArgs<T> a) {
+    using TQ = Tile<T, kUpQRows, 64, 1, 2, 1, 2, 2, false, false>;   // wave: 128 tokens x 32 hidden x {A, C}
+    using TK = Tile<T, kUpKRows, 64, 1, 2, 2, 3, 3, false, false>;   // wave: 64 tokens x 32 hidden x {A, C, DH}
     constexpr int LDSB = TQ::LDS > TK::LDS ? TQ::LDS : TK::LDS;
     __shared__ __attribute__((aligned(16))) char smem[LDSB];
 
+    // a workgroup takes one block of token rows and walks a group of 64-wide hidden tiles
     const int per = a.nQ + a.nK;
-    const int s = blockIdx.x / per, t = blockIdx.x % per;
+    const int lb = xcd_block(gridDim.x);
+    const int s = lb / per, t = lb % per;
     const int nct = (a.m + 63) / 64;
     const int64_t dm = (int64_t)a.d * a.m;
     const T* sh = a.sh + s * a.sh_stride;
@@ -52,13 +57,13 @@ __global__ __launch_bounds__(kThreads) void k_up(StepArgs<T> a) {
     const int64_t ioff = s * a.inter_stride;
 
     if (t < a.nQ) {
-        const int r0 = (t / nct) * 128, c0 = (t % nct) * 64;
-        const int64_t tok = (int64_t)s * a.N + a.a0 + r0;
-        const Opnd<T> A[1] = {{a.q + tok * a.d, a.d, a.la - r0, a.d}};
+        const int r0 = (t / nct) * kUpQRows, c0 = (t % nct) * 64;
+        const T* Q = a.q + ((int64_t)s * a.N + a.a0 + r0) * a.d;
+        const Opnd<T> A[1] = {{Q, a.d, a.la - r0, a.d}};
         const Opnd<T> B[2] = {{W1s + (int64_t)c0 * a.d, a.d, a.m - c0, a.d},
                               {W3s + (int64_t)c0 * a.d, a.d, a.m - c0, a.d}};
         TQ tl;
-        tl.template run<PMQ, false, false>(A, B, a.d, smem);
+        tl.template run<PMQ>(A, B, a.d, smem);
         T* Hq = a.Hq + ioff;
         tl.for_each([&](const float (&v)[2], int row, int col) {
             const int tr = r0 + row, tc = c0 + col;
@@ -66,14 +71,14 @@ __global__ __launch_bounds__(kThreads) void k_up(StepArgs<T> a) {
         });
     } else {
         const int tt = t - a.nQ;
-        const int r0 = (tt / nct) * 128, c0 = (tt % nct) * 64;
+        const int r0 = (tt / nct) * kUpKRows, c0 = (tt % nct) * 64;
         const int64_t tok = (int64_t)s * a.N + a.u0 + r0;
         const Opnd<T> A[2] = {{a.k + tok * a.d, a.d, a.lu - r0, a.d}, {a.v + tok * a.d, a.d, a.lu - r0, a.d}};
         const Opnd<T> B[3] = {{W1s + (int64_t)c0 * a.d, a.d, a.m - c0, a.d},
                               {W3s + (int64_t)c0 * a.d, a.d, a.m - c0, a.d},
                               {W2Ts + (int64_t)c0 * a.d, a.d, a.m - c0, a.d}};
         TK tl;
-        tl.template run<PMK, false, false>(A, B, a.d, smem);
+        tl.template run<PMK>(A, B, a.d, smem);
         const float* eta = a.eta + tok;
         T* HkE = a.HkE + ioff;
         T* DA = a.DA + ioff;
@@ -96,40 +101,46 @@ __global__ __launch_bounds__(kThreads) void k_up(StepArgs<T> a) {
 // ---------------------------------------------------------------------------------------------
 // down: chunk gradients (contractions over tokens) and the apply chunk's outputs
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k_down(StepArgs<T> a) {
-    using TT = Tile<T, 128, 128, 2, 2, 1, 1, 1>;
-    __shared__ __attribute__((aligned(16))) char smem[TT::LDS];
+__global__ __launch_bounds__(kThreads, 2) void k_down(StepArgs<T> a) {
+    using TG13 = Tile<T, 128, 128, 1, 2, 2, 1, 2, true, true>;  // G1 and G3 share the K operand
+    using TG2 = Tile<T, 128, 256, 1, 2, 1, 1, 1, true, true>;
+    using TO = Tile<T, kORows, 128, 1, 2, 1, 1, 1, false, false>;
+    constexpr int L1 = TG13::LDS > TG2::LDS ? TG13::LDS : TG2::LDS;
+    constexpr int LDSB = L1 > TO::LDS ? L1 : TO::LDS;
+    __shared__ __attribute__((aligned(16))) char smem[LDSB];
 
-    const int per = 2 * a.nG1 + a.nG2 + a.nO;
-    const int s = blockIdx.x / per;
-    int t = blockIdx.x % per;
+    const int per = a.nG13 + a.nG2 + a.nO;
+    const int lb = xcd_block(gridDim.x);
+    const int s = lb / per;
+    int t = lb % per;
     const int64_t dm = (int64_t)a.d * a.m;
-    const int ndt = (a.d + 127) / 128, nmt = (a.m + 127) / 128;
+    const int ndt = (a.d + 127) / 128, nmt2 = (a.m + 255) / 256;
     const int64_t ioff = s * a.inter_stride;
-    TT tl;
-    if (t < 2 * a.nG1) {  // G1 = DA^T K or G3 = DC^T K: rows c of m, cols e of d
-        const int which = t / a.nG1;
-        t %= a.nG1;
+    if (t < a.nG13) {  // G1 = DA^T K and G3 = DC^T K: rows c of m, cols e of d
         const int r0 = (t / ndt) * 128, c0 = (t % ndt) * 128;
-        const T* D = (which == 0 ? a.DA : a.DC) + ioff;
         const T* K = a.k + ((int64_t)s * a.N + a.u0) * a.d;
-        const Opnd<T> A[1] = {{D + r0, a.m, a.m - r0, a.lu}};
+        const Opnd<T> A[2] = {{a.DA + ioff + r0, a.m, a.m - r0, a.lu}, {a.DC + ioff + r0, a.m, a.m - r0, a.lu}};
         const Opnd<T> B[1] = {{K + c0, a.d, a.d - c0, a.lu}};
-        tl.template run<PM1, true, true>(A, B, a.lu, smem);
-        float* G = a.G + s * a.g_stride + which * dm;
-        tl.for_each([&](const float (&v)[1], int row, int col) {
+        TG13 tl;
+        tl.template run<PMG>(A, B, a.lu, smem);
+        float* G = a.G + s * a.g_stride;
+        tl.for_each([&](const float (&v)[2], int row, int col) {
             const int gr = r0 + row, gc = c0 + col;
-            if (gr < a.m && gc < a.d) G[(int64_t)gr * a.d + gc] = v[0];
+            if (gr < a.m && gc < a.d) {
+                G[(int64_t)gr * a.d + gc] = v[0];
+                G[dm + (int64_t)gr * a.d + gc] = v[1];
+            }
         });
         return;
     }
-    t -= 2 * a.nG1;
+    t -= a.nG13;
     if (t < a.nG2) {  // G2 = V^T HkE: rows e of d, cols c of m
-        const int r0 = (t / nmt) * 128, c0 = (t % nmt) * 128;
+        const int r0 = (t / nmt2) * 128, c0 = (t % nmt2) * 256;
         const T* V = a.v + ((int64_t)s * a.N + a.u0) * a.d;
         const Opnd<T> A[1] = {{V + r0, a.d, a.d - r0, a.lu}};
         const Opnd<T> B[1] = {{a.HkE + ioff + c0, a.m, a.m - c0, a.lu}};
-        tl.template run<PM1, true, true>(A, B, a.lu, smem);
+        TG2 tl;
+        tl.template run<PM1>(A, B, a.lu, smem);
         float* G = a.G + s * a.g_stride + 2 * dm;
         tl.for_each([&](const float (&v)[1], int row, int col) {
             const int gr = r0 + row, gc = c0 + col;
@@ -139,11 +150,12 @@ __global__ __launch_bounds__(kThreads) void k_down(StepArgs<T> a) {
     }
     t -= a.nG2;
     {  // O = Hq W2^T: rows t of the apply chunk, cols e of d
-        const int r0 = (t / ndt) * 128, c0 = (t % ndt) * 128;
+        const int r0 = (t / ndt) * kORows, c0 = (t % ndt) * 128;
         const T* W2s = a.sh + s * a.sh_stride + 2 * dm;
         const Opnd<T> A[1] = {{a.Hq + ioff + (int64_t)r0 * a.m, a.m, a.la - r0, a.m}};
         const Opnd<T> B[1] = {{W2s + (int64_t)c0 * a.m, a.m, a.d - c0, a.m}};
-        tl.template run<PM1, false, false>(A, B, a.m, smem);
+        TO tl;
+        tl.template run<PM1>(A, B, a.m, smem);
         T* O = a.o + ((int64_t)s * a.N + a.a0) * a.d;
         tl.for_each([&](const float (&v)[1], int row, int col) {
             const int tr = r0 + row, tc = c0 + col;
@@ -166,9 +178,24 @@ template <typename T> struct UpdArgs {
 constexpr int kUpdRows = 16;
 constexpr int kMaxDim = 2048;
 
+template <typename T> struct Vec4;
+template <> struct Vec4<uint16_t> {
+    typedef uint32_t raw __attribute__((ext_vector_type(2)));
+    __device__ static void store(uint16_t* p, float4 v) {
+        *reinterpret_cast<raw*>(p) = raw{(uint32_t)f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16),
+                                         (uint32_t)f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16)};
+    }
+};
+template <> struct Vec4<float> {
+    __device__ static void store(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
+};
+
+// One pass per row: the row of W - U is held in registers (4 floats per lane per 256 columns).
+// W2's rows are also written to LDS so that W2^T can be stored 16 consecutive elements at a time.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_update(UpdArgs<T> a) {
-    __shared__ __attribute__((aligned(16))) T tileT[kUpdRows * kMaxDim];
+    extern __shared__ __attribute__((aligned(16))) char dyn_lds[];
+    T* tileT = reinterpret_cast<T*>(dyn_lds);  // [kUpdRows][m], used by W2 blocks
     const int per = (2 * a.m + a.d) / kUpdRows;
     const int s = blockIdx.x / per, rb = blockIdx.x % per;
     const int64_t dm = (int64_t)a.d * a.m;
@@ -185,38 +212,70 @@ __global__ __launch_bounds__(kThreads) void k_update(UpdArgs<T> a) {
     float* dst = a.dst + s * a.dst_stride + moff;
     T* shm = a.sh + s * a.sh_stride + moff;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int L4 = L / 4;
+    constexpr int kMaxV = kMaxDim / 256;  // float4 per lane per row
     for (int rr = 0; rr < kUpdRows / 4; ++rr) {
         const int row = wave * (kUpdRows / 4) + rr;
         const int64_t ro = (int64_t)(row0 + row) * L;
+        const float4* s4 = reinterpret_cast<const float4*>(src + ro);
+        const float4* u4 = U ? reinterpret_cast<const float4*>(U + ro) : nullptr;
+        float4 x[kMaxV];
         float ss = 0.f;
-        if (norm) {
-            for (int c = lane; c < L; c += 64) {
-                float x = src[ro + c];
-                if (U) x -= U[ro + c];
-                ss += x * x;
+#pragma unroll
+        for (int i = 0; i < kMaxV; ++i) {
+            const int c4 = lane + 64 * i;
+            if (c4 < L4) {
+                float4 w = s4[c4];
+                if (u4) {
+                    const float4 u = u4[c4];
+                    w.x -= u.x; w.y -= u.y; w.z -= u.z; w.w -= u.w;
+                }
+                x[i] = w;
+                ss += w.x * w.x + w.y * w.y + w.z * w.z + w.w * w.w;
             }
-            ss = wave_sum(ss);
         }
-        const float sc = norm ? 1.0f / fmaxf(sqrtf(ss), 1e-6f) : 1.0f;
-        for (int c = lane; c < L; c += 64) {
-            float x = src[ro + c];
-            if (U) x -= U[ro + c];
-            x *= sc;
-            dst[ro + c] = x;
-            const T y = Elt<T>::st(x);
-            shm[ro + c] = y;
-            if (mat == 2) tileT[row * L + c] = y;
+        float sc = 1.0f;
+        if (norm) sc = 1.0f / fmaxf(sqrtf(wave_sum(ss)), 1e-6f);
+        float4* d4 = reinterpret_cast<float4*>(dst + ro);
+#pragma unroll
+        for (int i = 0; i < kMaxV; ++i) {
+            const int c4 = lane + 64 * i;
+            if (c4 < L4) {
+                const float4 w = make_float4(x[i].x * sc, x[i].y * sc, x[i].z * sc, x[i].w * sc);
+                d4[c4] = w;
+                Vec4<T>::store(shm + ro + 4 * c4, w);
+                if (mat == 2) Vec4<T>::store(tileT + row * L + 4 * c4, w);
+            }
         }
     }
     if (mat == 2) {  // W2^T [m][d]: column c of this 16-row block is 16 consecutive elements
         __syncthreads();
         T* w2t = a.sh + s * a.sh_stride + 3 * dm;
         for (int c = threadIdx.x; c < L; c += kThreads) {
-            T* out = w2t + (int64_t)c * a.d + row0;
+            constexpr int NQ = kUpdRows * (int)sizeof(T) / 16;
+            union { T e[kUpdRows]; u32x4_t q[NQ]; } vals;
 #pragma unroll
-            for (int j = 0; j < kUpdRows; ++j) out[j] = tileT[j * L + c];
+            for (int j = 0; j < kUpdRows; ++j) vals.e[j] = tileT[j * L + c];
+            u32x4_t* out = reinterpret_cast<u32x4_t*>(w2t + (int64_t)c * a.d + row0);
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) out[q] = vals.q[q];
         }
     }
+}
+
+template <typename T>
+static ttt_status launch_update(const UpdArgs<T>& u, int grid, hipStream_t st) {
+    const size_t lds = (size_t)kUpdRows * u.m * sizeof(T);
+    if (lds > 65536) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_update<T>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return fail(TTT_ERR_DEVICE, "k_update LDS attribute: %s", hipGetErrorString(e));
+    }
+    {
+        ProfScope ps(PK_UPDATE, st);
+        hipLaunchKernelGGL(k_update<T>, dim3(grid), dim3(kThreads), lds, st, u);
+    }
+    return check_launch("k_update");
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -303,10 +362,12 @@ __global__ __launch_bounds__(kThreads) void k_ns_init(NSArgs<T> a) {
     }
 }
 
+template <typename T, bool KS> using NSTile = Tile<T, 128, 128, 1, 2, 1, 1, 1, KS, KS>;
+template <typename T> using NSTileStepWide = Tile<T, 128, 128, 1, 2, 1, 1, 1, false, true>;
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_ns_gram(NSArgs<T> a) {
-    using TT = Tile<T, 128, 128, 2, 2, 1, 1, 1>;
-    __shared__ __attribute__((aligned(16))) char smem[TT::LDS];
+    __shared__ __attribute__((aligned(16))) char smem[NSTile<T, false>::LDS];
     const int64_t dm = (int64_t)a.d * a.m;
     const int per = a.nmat * a.tiles;
     const int s = blockIdx.x / per;
@@ -318,27 +379,29 @@ __global__ __launch_bounds__(kThreads) void k_ns_gram(NSArgs<T> a) {
     const int np = (p + 127) / 128;
     const int i0 = (t / np) * 128, j0 = (t % np) * 128;
     const T* X = a.Xin + s * a.x_stride + mat * dm;
-    TT tl;
-    if (r > c) {  // Gram = X^T X (c x c), contracted over the r rows
-        const Opnd<T> A[1] = {{X + i0, c, c - i0, r}};
-        const Opnd<T> B[1] = {{X + j0, c, c - j0, r}};
-        tl.template run<PM1, true, true>(A, B, r, smem);
-    } else {      // Gram = X X^T (r x r), contracted over the c columns
-        const Opnd<T> A[1] = {{X + (int64_t)i0 * c, c, r - i0, c}};
-        const Opnd<T> B[1] = {{X + (int64_t)j0 * c, c, r - j0, c}};
-        tl.template run<PM1, false, false>(A, B, c, smem);
-    }
     T* Gm = a.Gram + s * a.gram_stride + (int64_t)mat * p * p;
-    tl.for_each([&](const float (&v)[1], int row, int col) {
+    auto store = [&](const float (&v)[1], int row, int col) {
         const int gi = i0 + row, gj = j0 + col;
         if (gi < p && gj < p) Gm[(int64_t)gi * p + gj] = Elt<T>::st(v[0]);
-    });
+    };
+    if (r > c) {  // Gram = X^T X (c x c), contracted over the r rows
+        NSTile<T, true> tl;
+        const Opnd<T> A[1] = {{X + i0, c, c - i0, r}};
+        const Opnd<T> B[1] = {{X + j0, c, c - j0, r}};
+        tl.template run<PM1>(A, B, r, smem);
+        tl.for_each(store);
+    } else {      // Gram = X X^T (r x r), contracted over the c columns
+        NSTile<T, false> tl;
+        const Opnd<T> A[1] = {{X + (int64_t)i0 * c, c, r - i0, c}};
+        const Opnd<T> B[1] = {{X + (int64_t)j0 * c, c, r - j0, c}};
+        tl.template run<PM1>(A, B, c, smem);
+        tl.for_each(store);
+    }
 }
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_ns_step(NSArgs<T> a) {
-    using TT = Tile<T, 128, 128, 2, 2, 1, 1, 1>;
-    __shared__ __attribute__((aligned(16))) char smem[TT::LDS];
+    __shared__ __attribute__((aligned(16))) char smem[NSTile<T, false>::LDS];
     const int64_t dm = (int64_t)a.d * a.m;
     const int per = a.nmat * a.tiles;
     const int s = blockIdx.x / per;
@@ -351,19 +414,9 @@ __global__ __launch_bounds__(kThreads) void k_ns_step(NSArgs<T> a) {
     const int r0 = (t / nct) * 128, c0 = (t % nct) * 128;
     const T* X = a.Xin + s * a.x_stride + mat * dm;
     const T* Gm = a.Gram + s * a.gram_stride + (int64_t)mat * p * p;
-    TT tl;
-    if (r > c) {  // P = X Gram; Gram is symmetric, so its rows serve as the B operand
-        const Opnd<T> A[1] = {{X + (int64_t)r0 * c, c, r - r0, c}};
-        const Opnd<T> B[1] = {{Gm + (int64_t)c0 * p, p, c - c0, p}};
-        tl.template run<PM1, false, false>(A, B, c, smem);
-    } else {      // P = Gram X; B[j][i] = X[i][j] is read k-strided
-        const Opnd<T> A[1] = {{Gm + (int64_t)r0 * p, p, r - r0, p}};
-        const Opnd<T> B[1] = {{X + c0, c, c - c0, r}};
-        tl.template run<PM1, false, true>(A, B, r, smem);
-    }
     float* Xf = a.Xf + s * a.x_stride + mat * dm;
     T* Xo = a.Xout + s * a.x_stride + mat * dm;
-    tl.for_each([&](const float (&v)[1], int row, int col) {
+    auto store = [&](const float (&v)[1], int row, int col) {
         const int gr = r0 + row, gc = c0 + col;
         if (gr < r && gc < c) {
             const int64_t e = (int64_t)gr * c + gc;
@@ -371,7 +424,20 @@ __global__ __launch_bounds__(kThreads) void k_ns_step(NSArgs<T> a) {
             Xf[e] = xn;
             Xo[e] = Elt<T>::st(xn);
         }
-    });
+    };
+    if (r > c) {  // P = X Gram; Gram is symmetric, so its rows serve as the B operand
+        NSTile<T, false> tl;
+        const Opnd<T> A[1] = {{X + (int64_t)r0 * c, c, r - r0, c}};
+        const Opnd<T> B[1] = {{Gm + (int64_t)c0 * p, p, c - c0, p}};
+        tl.template run<PM1>(A, B, c, smem);
+        tl.for_each(store);
+    } else {      // P = Gram X; B[j][i] = X[i][j] is read k-strided
+        NSTileStepWide<T> tl;
+        const Opnd<T> A[1] = {{Gm + (int64_t)r0 * p, p, r - r0, p}};
+        const Opnd<T> B[1] = {{X + c0, c, c - c0, r}};
+        tl.template run<PM1>(A, B, r, smem);
+        tl.for_each(store);
+    }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -471,11 +537,7 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
     {  // W0 -> master copy and shadows
         UpdArgs<T> u{W0, 3 * dm, D.w0_per_batch ? 0 : 1, D.H, nullptr, 0, Wf[0], L.wf_stride, sh[0], L.sh_stride,
                      d, m, 0, 0};
-        {
-            ProfScope ps(PK_UPDATE, st);
-            hipLaunchKernelGGL(k_update<T>, dim3(S * upd_blocks), dim3(kThreads), 0, st, u);
-        }
-        if ((rc = check_launch("k_update(init)")) != TTT_OK) return rc;
+        if ((rc = launch_update<T>(u, S * upd_blocks, st)) != TTT_OK) return rc;
     }
     int cur = 0;
     const int nc = (int)cdiv(D.N, D.chunk);
@@ -497,11 +559,11 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
         a.la = ja >= 0 ? (int)(std::min<int64_t>((int64_t)(ja + 1) * D.chunk, D.N) - a.a0) : 0;
         a.u0 = ju >= 0 ? (int64_t)ju * D.chunk : 0;
         a.lu = ju >= 0 ? (int)(std::min<int64_t>((int64_t)(ju + 1) * D.chunk, D.N) - a.u0) : 0;
-        a.nQ = a.la ? (int)cdiv(a.la, 128) * nc64 : 0;
-        a.nK = a.lu ? (int)cdiv(a.lu, 128) * nc64 : 0;
-        a.nG1 = (a.lu && !D.last_layer_only) ? ntm * ntd : 0;
-        a.nG2 = a.lu ? ntd * ntm : 0;
-        a.nO = a.la ? (int)cdiv(a.la, 128) * ntd : 0;
+        a.nQ = a.la ? (int)cdiv(a.la, kUpQRows) * nc64 : 0;
+        a.nK = a.lu ? (int)cdiv(a.lu, kUpKRows) * nc64 : 0;
+        a.nG13 = (a.lu && !D.last_layer_only) ? ntm * ntd : 0;
+        a.nG2 = a.lu ? ntd * (int)cdiv(m, 256) : 0;
+        a.nO = a.la ? (int)cdiv(a.la, kORows) * ntd : 0;
         if (a.nQ + a.nK) {
             {
                 ProfScope ps(PK_UP, st);
@@ -509,10 +571,10 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
             }
             if ((rc = check_launch("k_up")) != TTT_OK) return rc;
         }
-        if (2 * a.nG1 + a.nG2 + a.nO) {
+        if (a.nG13 + a.nG2 + a.nO) {
             {
                 ProfScope ps(PK_DOWN, st);
-                hipLaunchKernelGGL(k_down<T>, dim3(S * (2 * a.nG1 + a.nG2 + a.nO)), dim3(kThreads), 0, st, a);
+                hipLaunchKernelGGL(k_down<T>, dim3(S * (a.nG13 + a.nG2 + a.nO)), dim3(kThreads), 0, st, a);
             }
             if ((rc = check_launch("k_down")) != TTT_OK) return rc;
         }
@@ -562,11 +624,7 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
         const int norm = (D.rule == TTT_UPD_GD_L2 || D.rule == TTT_UPD_MUON_L2) ? 1 : 0;
         UpdArgs<T> u{Wf[cur], L.wf_stride, 0, D.H, U, 3 * dm, Wf[cur ^ 1], L.wf_stride, sh[cur ^ 1], L.sh_stride,
                      d, m, norm, D.last_layer_only};
-        {
-            ProfScope ps(PK_UPDATE, st);
-            hipLaunchKernelGGL(k_update<T>, dim3(S * upd_blocks), dim3(kThreads), 0, st, u);
-        }
-        if ((rc = check_launch("k_update")) != TTT_OK) return rc;
+        if ((rc = launch_update<T>(u, S * upd_blocks, st)) != TTT_OK) return rc;
         cur ^= 1;
     }
     if (W_out) {
