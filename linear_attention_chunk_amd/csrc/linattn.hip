@@ -9,7 +9,8 @@
 // whole sequence; the update is an MFMA accumulation over the sub-block's tokens.  The apply reads
 // S from LDS, where it is kept as a bf16 hi + lo pair (fp32 in fp32 mode) refreshed at chunk ends,
 // so the query products see S to about 16 bits.  Token-causal mode adds the masked intra-block term
-// tril(Q K^T) (eta o V) and refreshes S after every sub-block.
+// tril(Q K^T) (eta o V) and refreshes S after every sub-block.  The next sub-block's q, k, v and eta
+// are loaded into registers while the current one is computed.
 #include <algorithm>
 
 #include "host_common.hpp"
@@ -21,29 +22,6 @@ template <typename T> struct LinArgs {
     const T* q; const T* k; const T* v; const float* eta; const float* S0; T* o; float* Sout;
     int64_t N; int dv; int chunk; int mode; int nvt;
     uint32_t flags[32];  // STRIDED: bit j = chunk j updates
-};
-
-template <typename T, int DK> struct LinCfg {
-    static constexpr int ES = (int)sizeof(T);
-    static constexpr int VEC = 16 / ES;
-    static constexpr int TB = ES == 2 ? 64 : 32;  // tokens per sub-block
-    static constexpr int VT = 32;                  // d_v rows of S per workgroup
-    static constexpr int PQ = DK * ES + 16;        // LDS pitch of rows of DK elements
-    static constexpr int PT = TB * ES + 16;        // LDS pitch of rows of TB elements
-    static constexpr int OFF_Q = 0;
-    static constexpr int OFF_K = OFF_Q + TB * PQ;
-    static constexpr int OFF_KT = OFF_K + TB * PQ;
-    static constexpr int OFF_VT = OFF_KT + DK * PT;
-    static constexpr int OFF_SH = OFF_VT + VT * PT;
-    static constexpr int OFF_SL = OFF_SH + VT * PQ;
-    static constexpr int OFF_P = OFF_SL + (ES == 2 ? VT * PQ : 0);
-    static constexpr int LDS = OFF_P + TB * PT;
-    // apply / intra-block tiling: 16 token rows per wave, AWN waves across columns
-    static constexpr int AWN = TB == 64 ? 1 : 2;
-    static constexpr int AFN = VT / 16 / AWN;
-    static constexpr int PFN = TB / 16 / AWN;
-    // state tiling: 2 x 2 waves over VT x DK
-    static constexpr int SFN = DK / 32;
 };
 
 // C[i][j] += sum_k A[i][k] B[j][k]; A, B k-contiguous in LDS (pitches pa, pb), kbytes % 64 == 0
@@ -65,19 +43,6 @@ __device__ __forceinline__ void lds_mma(f32x4_t (&acc)[FM][FN], const char* A, i
     }
 }
 
-// rows [0, ROWS) of a k-contiguous source (row length K elements) into LDS; rows >= valid are zero
-template <typename T, int ROWS, int K>
-__device__ __forceinline__ void stage_rows(char* lds, int pitch, const T* src, int64_t ld, int valid) {
-    constexpr int VPR = K * (int)sizeof(T) / 16;
-    constexpr int VEC = Elt<T>::VEC;
-    for (int v = threadIdx.x; v < ROWS * VPR; v += kThreads) {
-        const int row = v / VPR, c = v % VPR;
-        u32x4_t val = {0u, 0u, 0u, 0u};
-        if (row < valid) val = *reinterpret_cast<const u32x4_t*>(src + (int64_t)row * ld + c * VEC);
-        *reinterpret_cast<u32x4_t*>(lds + row * pitch + c * 16) = val;
-    }
-}
-
 __device__ __forceinline__ u32x4_t scale_vec(const u32x4_t& x, float s, uint16_t) {
     u32x4_t r;
 #pragma unroll
@@ -94,45 +59,223 @@ __device__ __forceinline__ u32x4_t scale_vec(const u32x4_t& x, float s, float) {
     return r;
 }
 
-// a k-strided source (element (row, k) at src[k * ld + row]) transposed into LDS rows of KT
-// k-values; k >= kvalid is zero; with SCALE every k-row is multiplied by scale[k] first
-template <typename T, int ROWS, int KT, bool SCALE>
-__device__ __forceinline__ void stage_trans(char* lds, int pitch, const T* src, int64_t ld, int kvalid,
-                                            const float* scale) {
-    constexpr int VEC = Elt<T>::VEC, RB = ROWS / VEC, KB = KT / VEC;
-    for (int blk = threadIdx.x; blk < RB * KB; blk += kThreads) {
-        const int kb = blk / RB, rb = blk % RB;
-        u32x4_t in[VEC], out[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const int k = kb * VEC + e;
-            u32x4_t val = {0u, 0u, 0u, 0u};
-            if (k < kvalid) {
-                val = *reinterpret_cast<const u32x4_t*>(src + (int64_t)k * ld + rb * VEC);
-                if (SCALE) val = scale_vec(val, scale[k], T{});
-            }
-            in[e] = val;
-        }
-        Elt<T>::transpose(in, out);
-#pragma unroll
-        for (int j = 0; j < VEC; ++j) *reinterpret_cast<u32x4_t*>(lds + (rb * VEC + j) * pitch + kb * 16) = out[j];
-    }
-}
+template <typename T, int DK, bool CAUSAL> struct LinCfg {
+    static constexpr int ES = (int)sizeof(T);
+    static constexpr int VEC = 16 / ES;
+    static constexpr int TB = ES == 2 ? 64 : 32;  // tokens per sub-block
+    static constexpr int VT = 32;                  // d_v rows of S per workgroup
+    static constexpr int PQ = DK * ES + 16;        // LDS pitch of rows of DK elements
+    static constexpr int PT = TB * ES + 16;        // LDS pitch of rows of TB elements
+    static constexpr int OFF_Q = 0;
+    static constexpr int OFF_KT = OFF_Q + TB * PQ;
+    static constexpr int OFF_VT = OFF_KT + DK * PT;
+    static constexpr int OFF_SH = OFF_VT + VT * PT;
+    static constexpr int OFF_SL = OFF_SH + VT * PQ;
+    static constexpr int OFF_K = OFF_SL + (ES == 2 ? VT * PQ : 0);  // causal only
+    static constexpr int OFF_P = OFF_K + (CAUSAL ? TB * PQ : 0);     // causal only
+    static constexpr int LDS = OFF_P + (CAUSAL ? TB * PT : 0);
+    // apply / intra-block tiling: 16 token rows per wave, AWN waves across columns
+    static constexpr int AWN = TB == 64 ? 1 : 2;
+    static constexpr int AFN = VT / 16 / AWN;
+    static constexpr int PFN = TB / 16 / AWN;
+    // state tiling: 2 x 2 waves over VT x DK
+    static constexpr int SFN = DK / 32;
+    // register staging of one sub-block: q rows, and k and v in VEC x VEC (token x feature) blocks
+    static constexpr int QV = TB * DK * ES / 16;
+    static constexpr int QPER = (QV + kThreads - 1) / kThreads;
+    static constexpr int KU = (TB / VEC) * (DK / VEC);
+    static constexpr int KPER = (KU + kThreads - 1) / kThreads;
+    static constexpr int VU = (TB / VEC) * (VT / VEC);
+    static_assert(VU <= kThreads, "v staging");
+};
 
-template <typename T, int DK>
+// One unit of work of a workgroup: a sub-block of at most TB tokens of one chunk, applied and/or
+// used for the update, in the order the mask fixes (notes section 1.1).  Apply-then-update walks
+// each chunk once; update-then-apply walks a chunk's sub-blocks for the update, then again for
+// the apply; token-causal treats every sub-block as its own chunk with the intra-block term.
+struct LinTask {
+    int64_t sb;
+    int n;
+    bool apply, update, causal, refresh;
+};
+
+struct LinIter {
+    int64_t N, chunk, j, lo, hi, sb;
+    int mode, tb, phase;
+    bool done;
+    const uint32_t* flags;
+    __device__ void begin_chunk() {
+        lo = j * chunk;
+        hi = lo + chunk < N ? lo + chunk : N;
+        sb = lo;
+        phase = 0;
+    }
+    __device__ void init(int64_t N_, int chunk_, int mode_, int tb_, const uint32_t* flags_) {
+        N = N_;
+        mode = mode_;
+        tb = tb_;
+        flags = flags_;
+        chunk = mode == TTT_MASK_TOKEN_CAUSAL ? tb : chunk_;
+        j = 0;
+        done = N <= 0;
+        if (!done) begin_chunk();
+    }
+    __device__ bool updates(int64_t jj) const {
+        return mode != TTT_MASK_STRIDED || ((flags[jj >> 5] >> (jj & 31)) & 1u);
+    }
+    __device__ LinTask cur() const {
+        LinTask t;
+        t.sb = sb;
+        t.n = (int)(hi - sb < tb ? hi - sb : tb);
+        const bool last = sb + tb >= hi;
+        t.causal = false;
+        if (mode == TTT_MASK_TOKEN_CAUSAL) {
+            t.apply = t.update = t.causal = t.refresh = true;
+        } else if (mode == TTT_MASK_APPLY_THEN_UPDATE || mode == TTT_MASK_STRIDED) {
+            const bool u = updates(j);
+            t.apply = true;
+            t.update = u;
+            t.refresh = u && last;
+        } else {  // update then apply, and the one-chunk FULL mask
+            t.apply = phase == 1;
+            t.update = phase == 0;
+            t.refresh = phase == 0 && last;
+        }
+        return t;
+    }
+    __device__ void next() {
+        sb += tb;
+        if (sb < hi) return;
+        if ((mode == TTT_MASK_UPDATE_THEN_APPLY || mode == TTT_MASK_FULL) && phase == 0) {
+            phase = 1;
+            sb = lo;
+            return;
+        }
+        ++j;
+        if (j * chunk >= N) {
+            done = true;
+            return;
+        }
+        begin_chunk();
+    }
+};
+
+// The next sub-block's q, k, v and eta, held in registers while the current one is computed.
+template <typename T, int DK, bool CAUSAL> struct LinStage {
+    using C = LinCfg<T, DK, CAUSAL>;
+    static constexpr int VEC = C::VEC, TB = C::TB, VT = C::VT;
+    u32x4_t q[C::QPER];
+    u32x4_t k[C::KPER][VEC];
+    u32x4_t v[VEC];
+    float e[VEC];
+
+    __device__ __forceinline__ void load(const LinTask& t, const T* Q, const T* K, const T* V, int64_t dv,
+                                         const float* eta) {
+        const int tid = threadIdx.x;
+        if (t.apply) {
+#pragma unroll
+            for (int i = 0; i < C::QPER; ++i) {
+                const int idx = tid + i * kThreads;
+                const int row = idx / (DK / VEC), c = idx % (DK / VEC);
+                u32x4_t x = {0u, 0u, 0u, 0u};
+                if ((C::QV % kThreads == 0 || idx < C::QV) && row < t.n)
+                    x = *reinterpret_cast<const u32x4_t*>(Q + (t.sb + row) * DK + c * VEC);
+                q[i] = x;
+            }
+        }
+        if (t.update) {
+#pragma unroll
+            for (int i = 0; i < C::KPER; ++i) {
+                const int u = tid + i * kThreads;
+                const int tb = u % (TB / VEC), db = u / (TB / VEC);
+#pragma unroll
+                for (int r = 0; r < VEC; ++r) {
+                    const int si = tb * VEC + r;
+                    u32x4_t x = {0u, 0u, 0u, 0u};
+                    if ((C::KU % kThreads == 0 || u < C::KU) && si < t.n)
+                        x = *reinterpret_cast<const u32x4_t*>(K + (t.sb + si) * DK + db * VEC);
+                    k[i][r] = x;
+                }
+            }
+            if (tid < C::VU) {
+                const int tb = tid % (TB / VEC), vb = tid / (TB / VEC);
+#pragma unroll
+                for (int r = 0; r < VEC; ++r) {
+                    const int si = tb * VEC + r;
+                    u32x4_t x = {0u, 0u, 0u, 0u};
+                    float ev = 0.f;
+                    if (si < t.n) {
+                        x = *reinterpret_cast<const u32x4_t*>(V + (t.sb + si) * dv + vb * VEC);
+                        ev = eta[t.sb + si];
+                    }
+                    v[r] = x;
+                    e[r] = ev;
+                }
+            }
+        }
+    }
+
+    // q rows into Qs; k transposed into Kt (feature rows, token columns) and, for the causal
+    // intra-block term, as token rows into Ks; eta o v transposed into Vt
+    __device__ __forceinline__ void store(const LinTask& t, char* smem) const {
+        const int tid = threadIdx.x;
+        if (t.apply) {
+#pragma unroll
+            for (int i = 0; i < C::QPER; ++i) {
+                const int idx = tid + i * kThreads;
+                if (C::QV % kThreads == 0 || idx < C::QV) {
+                    const int row = idx / (DK / VEC), c = idx % (DK / VEC);
+                    *reinterpret_cast<u32x4_t*>(smem + C::OFF_Q + row * C::PQ + c * 16) = q[i];
+                }
+            }
+        }
+        if (t.update) {
+#pragma unroll
+            for (int i = 0; i < C::KPER; ++i) {
+                const int u = tid + i * kThreads;
+                if (C::KU % kThreads == 0 || u < C::KU) {
+                    const int tb = u % (TB / VEC), db = u / (TB / VEC);
+                    u32x4_t tr[VEC];
+                    Elt<T>::transpose(k[i], tr);
+#pragma unroll
+                    for (int r = 0; r < VEC; ++r)
+                        *reinterpret_cast<u32x4_t*>(smem + C::OFF_KT + (db * VEC + r) * C::PT + tb * 16) = tr[r];
+                    if constexpr (CAUSAL) {
+#pragma unroll
+                        for (int r = 0; r < VEC; ++r)
+                            *reinterpret_cast<u32x4_t*>(smem + C::OFF_K + (tb * VEC + r) * C::PQ + db * 16) = k[i][r];
+                    }
+                }
+            }
+            if (tid < C::VU) {
+                const int tb = tid % (TB / VEC), vb = tid / (TB / VEC);
+                u32x4_t sc[VEC], tr[VEC];
+#pragma unroll
+                for (int r = 0; r < VEC; ++r) sc[r] = scale_vec(v[r], e[r], T{});
+                Elt<T>::transpose(sc, tr);
+#pragma unroll
+                for (int r = 0; r < VEC; ++r)
+                    *reinterpret_cast<u32x4_t*>(smem + C::OFF_VT + (vb * VEC + r) * C::PT + tb * 16) = tr[r];
+            }
+        }
+    }
+};
+
+template <typename T, int DK, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void k_linattn(LinArgs<T> a) {
-    using C = LinCfg<T, DK>;
+    using C = LinCfg<T, DK, CAUSAL>;
     constexpr int ES = C::ES, TB = C::TB, VT = C::VT, PQ = C::PQ, PT = C::PT;
     __shared__ __attribute__((aligned(16))) char smem[C::LDS];
     char* Qs = smem + C::OFF_Q;
-    char* Ks = smem + C::OFF_K;
     char* Kt = smem + C::OFF_KT;
     char* Vt = smem + C::OFF_VT;
     char* Sh = smem + C::OFF_SH;
     char* Sl = smem + C::OFF_SL;
+    char* Ks = smem + C::OFF_K;
     char* Ps = smem + C::OFF_P;
 
-    const int scan = blockIdx.x / a.nvt, v0 = (blockIdx.x % a.nvt) * VT;
+    const int lb = xcd_block(gridDim.x);
+    const int scan = lb / a.nvt, v0 = (lb % a.nvt) * VT;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t N = a.N;
     const T* Q = a.q + (int64_t)scan * N * DK;
@@ -168,19 +311,18 @@ __global__ __launch_bounds__(kThreads) void k_linattn(LinArgs<T> a) {
             }
     };
     refresh();
-    __syncthreads();
 
     const int at0 = (wave / C::AWN) * 16;
     const int av0 = (wave % C::AWN) * (VT / C::AWN);
     const int pc0 = (wave % C::AWN) * (TB / C::AWN);
 
-    auto apply = [&](int64_t sb, int n, bool causal) {
+    auto apply = [&](const LinTask& t) {
         f32x4_t oacc[1][C::AFN];
 #pragma unroll
         for (int j = 0; j < C::AFN; ++j) oacc[0][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         lds_mma<T, 1, C::AFN>(oacc, Qs, PQ, at0, Sh, PQ, av0, DK * ES);
         if constexpr (ES == 2) lds_mma<T, 1, C::AFN>(oacc, Qs, PQ, at0, Sl, PQ, av0, DK * ES);
-        if (causal) {
+        if constexpr (CAUSAL) {
             f32x4_t pacc[1][C::PFN];
 #pragma unroll
             for (int j = 0; j < C::PFN; ++j) pacc[0][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -189,79 +331,48 @@ __global__ __launch_bounds__(kThreads) void k_linattn(LinArgs<T> a) {
             for (int j = 0; j < C::PFN; ++j)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int t = at0 + 4 * (lane >> 4) + r, s = pc0 + j * 16 + (lane & 15);
-                    const float val = (s <= t && s < n) ? pacc[0][j][r] : 0.f;
-                    *reinterpret_cast<T*>(Ps + t * PT + s * ES) = Elt<T>::st(val);
+                    const int tt = at0 + 4 * (lane >> 4) + r, ss = pc0 + j * 16 + (lane & 15);
+                    const float val = (ss <= tt && ss < t.n) ? pacc[0][j][r] : 0.f;
+                    *reinterpret_cast<T*>(Ps + tt * PT + ss * ES) = Elt<T>::st(val);
                 }
-            __syncthreads();
+            lds_barrier();
             lds_mma<T, 1, C::AFN>(oacc, Ps, PT, at0, Vt, PT, av0, TB * ES);
         }
 #pragma unroll
         for (int j = 0; j < C::AFN; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int t = at0 + 4 * (lane >> 4) + r, vv = av0 + j * 16 + (lane & 15);
-                if (t < n) O[(sb + t) * a.dv + vv] = Elt<T>::st(oacc[0][j][r]);
+                const int tt = at0 + 4 * (lane >> 4) + r, vv = av0 + j * 16 + (lane & 15);
+                if (tt < t.n) O[(t.sb + tt) * a.dv + vv] = Elt<T>::st(oacc[0][j][r]);
             }
-    };
-    auto update = [&]() { lds_mma<T, 1, C::SFN>(sacc, Vt, PT, 16 * wv, Kt, PT, wk * (DK / 2), TB * ES); };
-    auto stage_kv = [&](int64_t sb, int n) {
-        stage_trans<T, DK, TB, false>(Kt, PT, K + sb * DK, DK, n, nullptr);
-        stage_trans<T, VT, TB, true>(Vt, PT, V + sb * a.dv, a.dv, n, eta + sb);
     };
 
-    if (a.mode == TTT_MASK_TOKEN_CAUSAL) {
-        for (int64_t sb = 0; sb < N; sb += TB) {
-            const int n = (int)std::min<int64_t>(TB, N - sb);
-            stage_rows<T, TB, DK>(Qs, PQ, Q + sb * DK, DK, n);
-            stage_rows<T, TB, DK>(Ks, PQ, K + sb * DK, DK, n);
-            stage_kv(sb, n);
-            __syncthreads();
-            apply(sb, n, true);
-            update();
-            __syncthreads();
+    LinIter it;
+    it.init(N, a.chunk, a.mode, TB, a.flags);
+    LinStage<T, DK, CAUSAL> g;
+    LinTask cur{};
+    if (!it.done) {
+        cur = it.cur();
+        g.load(cur, Q, K, V, a.dv, eta);
+    }
+    lds_barrier();  // S is in LDS
+    while (!it.done) {
+        g.store(cur, smem);
+        lds_barrier();
+        it.next();
+        LinTask nxt{};
+        if (!it.done) {  // the next sub-block's loads are in flight while this one is computed
+            nxt = it.cur();
+            g.load(nxt, Q, K, V, a.dv, eta);
+        }
+        if (cur.apply) apply(cur);
+        if (cur.update) lds_mma<T, 1, C::SFN>(sacc, Vt, PT, 16 * wv, Kt, PT, wk * (DK / 2), TB * ES);
+        if (cur.refresh) {
+            lds_barrier();  // every wave is done reading S for this sub-block
             refresh();
-            __syncthreads();
         }
-    } else {
-        const int64_t nc = (N + a.chunk - 1) / a.chunk;
-        const bool apply_first = a.mode == TTT_MASK_APPLY_THEN_UPDATE || a.mode == TTT_MASK_STRIDED;
-        for (int64_t j = 0; j < nc; ++j) {
-            const int64_t lo = j * a.chunk, hi = std::min<int64_t>(lo + a.chunk, N);
-            const bool upd = a.mode != TTT_MASK_STRIDED || ((a.flags[j >> 5] >> (j & 31)) & 1u);
-            if (apply_first) {
-                for (int64_t sb = lo; sb < hi; sb += TB) {
-                    const int n = (int)std::min<int64_t>(TB, hi - sb);
-                    stage_rows<T, TB, DK>(Qs, PQ, Q + sb * DK, DK, n);
-                    if (upd) stage_kv(sb, n);
-                    __syncthreads();
-                    apply(sb, n, false);
-                    if (upd) update();
-                    __syncthreads();
-                }
-            } else {
-                for (int64_t sb = lo; sb < hi; sb += TB) {
-                    const int n = (int)std::min<int64_t>(TB, hi - sb);
-                    stage_kv(sb, n);
-                    __syncthreads();
-                    update();
-                    __syncthreads();
-                }
-            }
-            if (upd) {
-                refresh();
-                __syncthreads();
-            }
-            if (!apply_first) {
-                for (int64_t sb = lo; sb < hi; sb += TB) {
-                    const int n = (int)std::min<int64_t>(TB, hi - sb);
-                    stage_rows<T, TB, DK>(Qs, PQ, Q + sb * DK, DK, n);
-                    __syncthreads();
-                    apply(sb, n, false);
-                    __syncthreads();
-                }
-            }
-        }
+        lds_barrier();
+        cur = nxt;
     }
     if (a.Sout) {
 #pragma unroll
@@ -299,7 +410,10 @@ template <typename T, int DK>
 static ttt_status launch_lin(LinArgs<T>& a, int grid, hipStream_t st) {
     {
         ProfScope ps(PK_LINATTN, st);
-        hipLaunchKernelGGL((k_linattn<T, DK>), dim3(grid), dim3(kThreads), 0, st, a);
+        if (a.mode == TTT_MASK_TOKEN_CAUSAL)
+            hipLaunchKernelGGL((k_linattn<T, DK, true>), dim3(grid), dim3(kThreads), 0, st, a);
+        else
+            hipLaunchKernelGGL((k_linattn<T, DK, false>), dim3(grid), dim3(kThreads), 0, st, a);
     }
     return check_launch("k_linattn");
 }

@@ -29,7 +29,8 @@ constexpr int kThreads = 256;
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 __device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// sigmoid with the hardware exp2 and reciprocal (v_exp_f32, v_rcp_f32: about 1 ulp each)
+__device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 // Workgroup barrier for handing LDS tiles between waves.  It waits for this wave's own LDS
 // operations (lgkmcnt) and meets at s_barrier, but leaves global loads in flight: __syncthreads()
@@ -437,6 +438,26 @@ struct Tile {
 #pragma unroll
                     for (int j = 0; j < FN; ++j) Mma32<T>::mma(acc[p][i][j], af[PM::a[p]][i], bfr[PM::b[p]][j]);
         }
+    }
+
+    static constexpr int ELEMS = FM * FN * 16;  // accumulator elements per thread and accumulator
+
+    // f(int idx, int row, int col) over the positions for_each visits, in the same order
+    // (idx = 0 .. ELEMS-1); usable before run(), e.g. to prefetch epilogue operands
+    template <class F>
+    __device__ __forceinline__ static void for_each_pos(F&& f) {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int wm = wave / WGN, wn = wave % WGN;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int col = RowMap<T, BN, SEG, KSB>::row_of(wn * WN + j * 32 + (lane & 31));
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    f((i * FN + j) * 16 + r,
+                      RowMap<T, BM, SEG, KSA>::row_of(wm * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)), col);
+            }
     }
 
     // f(const float (&v)[NP], int row, int col) for every accumulator element of this thread,

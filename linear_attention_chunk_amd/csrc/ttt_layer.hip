@@ -14,6 +14,7 @@
 // The fp32 fast weights live in a ping-pong pair in the workspace; the shadows (W1, W3, W2, W2^T)
 // are what the next chunk's MFMAs read.
 #include <algorithm>
+#include <type_traits>
 
 #include "host_common.hpp"
 #include "tile.hpp"
@@ -363,15 +364,18 @@ __global__ __launch_bounds__(kThreads) void k_ns_init(NSArgs<T> a) {
 }
 
 template <typename T, bool KS> using NSTile = Tile<T, 128, 128, 1, 2, 1, 1, 1, KS, KS>;
-template <typename T> using NSTileStepWide = Tile<T, 128, 128, 1, 2, 1, 1, 1, false, true>;
+template <typename T> using NSStepTall = Tile<T, 128, 64, 1, 2, 1, 1, 1, false, false>;
+template <typename T> using NSStepWide = Tile<T, 128, 64, 1, 2, 1, 1, 1, false, true>;
+constexpr int kNSStepRows = 128, kNSStepCols = 64;
 
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k_ns_gram(NSArgs<T> a) {
+__global__ __launch_bounds__(kThreads, 2) void k_ns_gram(NSArgs<T> a) {
     __shared__ __attribute__((aligned(16))) char smem[NSTile<T, false>::LDS];
     const int64_t dm = (int64_t)a.d * a.m;
     const int per = a.nmat * a.tiles;
-    const int s = blockIdx.x / per;
-    int t = blockIdx.x % per;
+    const int lb = xcd_block(gridDim.x);
+    const int s = lb / per;
+    int t = lb % per;
     const int mat = a.mat0 + t / a.tiles;
     t %= a.tiles;
     const int r = mat < 2 ? a.m : a.d, c = mat < 2 ? a.d : a.m;
@@ -399,44 +403,56 @@ __global__ __launch_bounds__(kThreads) void k_ns_gram(NSArgs<T> a) {
     }
 }
 
+// X <- 1.5 X - 0.5 P with P = X Gram (tall) or Gram X (wide).  The fp32 iterate values this thread
+// updates are loaded before the contraction, so their latency hides behind it.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k_ns_step(NSArgs<T> a) {
-    __shared__ __attribute__((aligned(16))) char smem[NSTile<T, false>::LDS];
+__global__ __launch_bounds__(kThreads, 2) void k_ns_step(NSArgs<T> a) {
+    __shared__ __attribute__((aligned(16))) char smem[NSStepTall<T>::LDS];
     const int64_t dm = (int64_t)a.d * a.m;
     const int per = a.nmat * a.tiles;
-    const int s = blockIdx.x / per;
-    int t = blockIdx.x % per;
+    const int lb = xcd_block(gridDim.x);
+    const int s = lb / per;
+    int t = lb % per;
     const int mat = a.mat0 + t / a.tiles;
     t %= a.tiles;
     const int r = mat < 2 ? a.m : a.d, c = mat < 2 ? a.d : a.m;
     const int p = r < c ? r : c;
-    const int nct = (c + 127) / 128;
-    const int r0 = (t / nct) * 128, c0 = (t % nct) * 128;
+    const int nct = (c + kNSStepCols - 1) / kNSStepCols;
+    const int r0 = (t / nct) * kNSStepRows, c0 = (t % nct) * kNSStepCols;
+    if (r0 >= r) return;  // a.tiles covers the larger of the tall and wide tilings
     const T* X = a.Xin + s * a.x_stride + mat * dm;
     const T* Gm = a.Gram + s * a.gram_stride + (int64_t)mat * p * p;
     float* Xf = a.Xf + s * a.x_stride + mat * dm;
     T* Xo = a.Xout + s * a.x_stride + mat * dm;
-    auto store = [&](const float (&v)[1], int row, int col) {
-        const int gr = r0 + row, gc = c0 + col;
-        if (gr < r && gc < c) {
-            const int64_t e = (int64_t)gr * c + gc;
-            const float xn = 1.5f * Xf[e] - 0.5f * v[0];
-            Xf[e] = xn;
-            Xo[e] = Elt<T>::st(xn);
-        }
+    auto body = [&](auto& tl, const auto& A, const auto& B, int K) {
+        using TT = typename std::remove_reference<decltype(tl)>::type;
+        float xv[TT::ELEMS];
+        TT::for_each_pos([&](int idx, int row, int col) {
+            const int gr = r0 + row, gc = c0 + col;
+            xv[idx] = (gr < r && gc < c) ? Xf[(int64_t)gr * c + gc] : 0.f;
+        });
+        tl.template run<PM1>(A, B, K, smem);
+        int idx = 0;
+        tl.for_each([&](const float (&v)[1], int row, int col) {
+            const int gr = r0 + row, gc = c0 + col;
+            const float xn = 1.5f * xv[idx++] - 0.5f * v[0];
+            if (gr < r && gc < c) {
+                const int64_t e = (int64_t)gr * c + gc;
+                Xf[e] = xn;
+                Xo[e] = Elt<T>::st(xn);
+            }
+        });
     };
     if (r > c) {  // P = X Gram; Gram is symmetric, so its rows serve as the B operand
-        NSTile<T, false> tl;
+        NSStepTall<T> tl;
         const Opnd<T> A[1] = {{X + (int64_t)r0 * c, c, r - r0, c}};
         const Opnd<T> B[1] = {{Gm + (int64_t)c0 * p, p, c - c0, p}};
-        tl.template run<PM1>(A, B, c, smem);
-        tl.for_each(store);
+        body(tl, A, B, c);
     } else {      // P = Gram X; B[j][i] = X[i][j] is read k-strided
-        NSTileStepWide<T> tl;
+        NSStepWide<T> tl;
         const Opnd<T> A[1] = {{Gm + (int64_t)r0 * p, p, r - r0, p}};
         const Opnd<T> B[1] = {{X + c0, c, c - c0, r}};
-        tl.template run<PM1>(A, B, r, smem);
-        tl.for_each(store);
+        body(tl, A, B, r);
     }
 }
 
@@ -602,7 +618,9 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
             if ((rc = check_launch("k_ns_init")) != TTT_OK) return rc;
             const int p = d < m ? d : m;
             const int gt = (int)(cdiv(p, 128) * cdiv(p, 128));
-            const int stt = ntm * ntd;
+            // step tiles: the larger of the tall (m x d) and wide (d x m) tilings
+            const int stt = (int)std::max(cdiv(m, kNSStepRows) * cdiv(d, kNSStepCols),
+                                          cdiv(d, kNSStepRows) * cdiv(m, kNSStepCols));
             for (int it = 0; it < D.ns_iters; ++it) {
                 na.Xin = Xb[it & 1];
                 na.Xout = Xb[(it + 1) & 1];
