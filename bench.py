@@ -9,7 +9,7 @@ Inputs are seeded synthetic tensors already resident in HBM.
 
 Prints one JSON line.  Besides the headline figure it reports the dominant kernel against its
 roofline (timed with HIP events on the launching stream), the fp64 oracle timed on host cores on a
-bounded sample, parity of sampled slices against that oracle, and the other workloads (Muon with
+bounded sample of scans, parity of those scans against that oracle, and the other workloads (Muon with
 momentum, the strided view-synthesis mask, chunked linear attention) as extra measurements.
 """
 import argparse
@@ -25,6 +25,34 @@ sys.path.insert(0, ROOT)
 METRIC = "TTT-layer fwd tokens/sec at chunk 2048 + % of bf16 MFMA peak on 1 MI355X"
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+
+
+# HBM bytes per launch at the headline workload from rocprofv3 FETCH_SIZE and WRITE_SIZE, each scaled
+# by what the counter reads for a 1 GiB device copy, with the hash of the kernel sources they were
+# taken on.  They are reported only while those sources are unchanged.
+TRAFFIC_SOURCES = ("linear_attention_chunk_amd/csrc/ttt_layer.hip", "linear_attention_chunk_amd/csrc/tile.hpp")
+MEASURED_TRAFFIC = {
+    "source_sha": "820f024c0d40f2f4",
+    "k_up": {"read": 293.1e6, "write": 475.1e6},
+    "k_down": {"read": 706.6e6, "write": 238.0e6},
+    "k_update": {"read": 217.1e6, "write": 188.9e6},
+}
+
+
+def sources_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    t = MEASURED_TRAFFIC.get(kernel)
+    if t is None or sources_sha() != MEASURED_TRAFFIC["source_sha"]:
+        return None
+    return round(t["read"] + t["write"])
 
 
 def lact_flops(B, H, N, d, m, upd_tokens=None, ns_iters=0, n_updates=0):
@@ -105,7 +133,13 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
-    ap.add_argument("--oracle-seconds", type=float, default=12.0, help="stop sampling oracle slices after this")
+    ap.add_argument("--oracle-seconds", type=float, default=25.0,
+                    help="stop the oracle after the scan that passes this many seconds")
+    ap.add_argument("--update", choices=["gd_l2", "muon_momentum"], default="gd_l2",
+                    help="update rule of the timed layer (the headline metric uses gd_l2)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="first copy a 1 GiB device buffer three times (a known-size kernel that scales "
+                         "hardware byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -125,27 +159,47 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
 
+    if args.copy_probe:
+        src = torch.empty(1 << 29, dtype=torch.float16, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        print("[bench] copy probe: 3 x 1 GiB device copies done", file=sys.stderr, flush=True)
+
     # ---------------- headline workload: LaCT LM layer, GD + L2 ----------------
     B, H, N, d, m, chunk = 8, 4, 32768, 384, 768, 2048
     print(f"[bench] generating inputs B{B} H{H} N{N} d{d} m{m}", file=sys.stderr, flush=True)
-    q, k, v, eta, _ = gpu_inputs(torch, B, H, N, d, m, 1000 + args.seed)
-    sample = [(0, 0), (B - 1, H - 1), (3, 1), (5, 2)]
     exact = {}
-    for (b, h) in sample:
-        qs, ks, vs, es = synth.slice_inputs(args.seed, b, h, N, d, d, "softplus", 0.01, True)
-        exact[(b, h)] = (qs, ks, vs, es)
-        for t, x in ((q, qs), (k, ks), (v, vs)):
-            t[b, h] = torch.from_numpy(x).to("cuda").to(torch.bfloat16)
-        eta[b, h] = torch.from_numpy(es).to("cuda")
+    if args.no_cpu_baseline:  # same distributions, drawn on the device (nothing to check them against)
+        q, k, v, eta, _ = gpu_inputs(torch, B, H, N, d, 0, 1000 + args.seed)
+    else:  # every (batch, head) scan from the seeded per-slice recipe, so the oracle can check any of them
+        q = torch.empty((B, H, N, d), dtype=torch.bfloat16, device="cuda")
+        k = torch.empty_like(q)
+        v = torch.empty_like(q)
+        eta = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        for b in range(B):
+            for h in range(H):
+                qs, ks, vs, es = synth.slice_inputs(args.seed, b, h, N, d, d, "softplus", 0.01, True)
+                exact[(b, h)] = (qs, ks, vs, es)
+                for t, x in ((q, qs), (k, ks), (v, vs)):
+                    t[b, h] = torch.from_numpy(x).to("cuda").to(torch.bfloat16)
+                eta[b, h] = torch.from_numpy(es).to("cuda")
+            print(f"[bench] inputs of batch {b} ready", file=sys.stderr, flush=True)
     Wh = [synth.head_weights(args.seed, h, d, m) for h in range(H)]
     W0 = torch.from_numpy(np.stack([np.concatenate([w[0].ravel(), w[1].ravel(), w[2].ravel()]) for w in Wh])).cuda()
-    D, keep = T.ttt_desc(B, H, N, d, m, chunk, C.TTT_BF16, C.MASK_APPLY_THEN_UPDATE, C.UPD_GD_L2)
+    rule, beta = (C.UPD_GD_L2, 0.0) if args.update == "gd_l2" else (C.UPD_MUON_L2, 0.9)
+    D, keep = T.ttt_desc(B, H, N, d, m, chunk, C.TTT_BF16, C.MASK_APPLY_THEN_UPDATE, rule, 5, beta)
     ws = torch.empty(T.ttt_workspace_bytes(D), dtype=torch.uint8, device="cuda")
     o = torch.empty_like(q)
+    Mom = torch.zeros((B, H, 3 * d * m), dtype=torch.float32, device="cuda") if beta else None
 
     def call():
-        return T.ttt_forward(q, k, v, eta, W0, chunk, C.MASK_APPLY_THEN_UPDATE, C.UPD_GD_L2, m_h=m, out=o,
-                             workspace=ws)
+        if Mom is not None:
+            Mom.zero_()
+        return T.ttt_forward(q, k, v, eta, W0, chunk, C.MASK_APPLY_THEN_UPDATE, rule, m_h=m, momentum=beta, M=Mom,
+                             out=o, workspace=ws)
 
     print("[bench] warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -168,47 +222,72 @@ def main():
     tokens = B * N
     value = tokens / (ms * 1e-3)
     nchunks = N // chunk
-    flops = lact_flops(B, H, N, d, m, n_updates=nchunks)
+    flops = lact_flops(B, H, N, d, m, ns_iters=5 if beta else 0, n_updates=nchunks)
     layer_tflops = flops / (ms * 1e-3) / 1e12
 
-    # dominant kernel against its roofline: per-launch algorithmic FLOPs / average launch time
-    per_launch = {  # FLOP per launch = per-token-head FLOP x token-heads in one launch
-        "k_up": 10 * d * m * B * H * chunk,    # [Q; K] x [W1; W3]^T (4dm + 4dm) and V x W2 (2dm)
-        "k_down": 8 * d * m * B * H * chunk,   # O = Hq W2^T (2dm), G1, G3, G2 (6dm)
+    # dominant kernel against its roofline: algorithmic work per launch / average launch time
+    S, dm, p_ns, q_ns, es = B * H, d * m, min(d, m), max(d, m), 2
+    work = {  # kernel: (bound, FLOP or HBM bytes per launch)
+        # [Q; K] x [W1; W3]^T (4dm + 4dm) and V x W2 (2dm) per token-head, one chunk of every scan
+        "k_up": ("mfma", 10 * dm * S * chunk),
+        # O = Hq W2^T (2dm), gradient sums G1, G3, G2 (6dm) per token-head
+        "k_down": ("mfma", 8 * dm * S * chunk),
+        # read W and G in fp32, write W in fp32 and the bf16 copies of W1, W3, W2, W2^T
+        "k_update": ("hbm", (4 + 4 + 4) * 3 * dm * S + es * 4 * dm * S),
+        # read G (and read/write M) in fp32
+        "k_muon_prep": ("hbm", (12 if beta else 4) * 3 * dm * S),
+        # read U in fp32, write the fp32 iterate and its bf16 copy
+        "k_ns_init": ("hbm", (4 + 4 + es) * 3 * dm * S),
+        # Gram p x p from the bf16 iterate: 2 p^2 q per matrix
+        "k_ns_gram": ("mfma", 2 * p_ns * p_ns * q_ns * 3 * S),
+        # read bf16 iterate, bf16 Gram and fp32 iterate; write fp32 iterate and bf16 copy
+        "k_ns_step": ("hbm", ((es + 4 + 4 + es) * dm + es * p_ns * p_ns) * 3 * S),
     }
     dom = max(prof.items(), key=lambda kv: kv[1][0])[0]
     dom_ms, dom_n = prof[dom]
     avg = dom_ms / max(dom_n, 1)
-    if dom in per_launch:
-        ach = per_launch[dom] / (avg * 1e-3) / 1e12
-        roofline = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None,
-                    "avg_launch_us": round(avg * 1e3, 2), "launches": dom_n,
-                    "flop_per_launch": per_launch[dom]}
+    bound, amount = work[dom]
+    if bound == "mfma":
+        ach = amount / (avg * 1e-3) / 1e12
+        peak, unit, key = BF16_PEAK_TFLOPS, "TFLOP/s", "flop_per_launch"
     else:
-        roofline = {"kernel": dom, "bound": "hbm", "achieved": None, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": None, "traffic": None, "avg_launch_us": round(avg * 1e3, 2), "launches": dom_n}
-    kernels = {kname: {"ms_per_step": round(t / args.steps, 4), "launches_per_step": n / args.steps}
-               for kname, (t, n) in prof.items() if n}
+        ach = amount / (avg * 1e-3) / 1e9
+        peak, unit, key = HBM_PEAK_GBS, "GB/s", "bytes_per_launch"
+    roofline = {"kernel": dom, "bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
+                "frac": round(ach / peak, 4), "traffic": measured_traffic(dom), "traffic_unit": "bytes/launch", "avg_launch_us": round(avg * 1e3, 2),
+                "launches": dom_n, key: amount}
+    kernels = {}
+    for kname, (t, n) in prof.items():
+        if not n:
+            continue
+        kb, kw = work.get(kname, (None, None))
+        kernels[kname] = {"ms_per_step": round(t / args.steps, 4), "launches_per_step": n / args.steps}
+        if kb is not None:
+            rate = kw / (t / n * 1e-3) / (1e12 if kb == "mfma" else 1e9)
+            kernels[kname]["frac_of_" + ("bf16_mfma" if kb == "mfma" else "hbm")] = round(
+                rate / (BF16_PEAK_TFLOPS if kb == "mfma" else HBM_PEAK_GBS), 4)
 
     # ---------------- parity of sampled slices + CPU baseline (fp64 oracle) ----------------
     out = {}
     parity = None
     cpu = None
-    o_host = {s: o[s[0], s[1]].float().cpu().numpy() for s in sample}
-    W_host = {s: W_out[s[0], s[1]].cpu().numpy() for s in sample}
     if not args.no_cpu_baseline:
         import oracle as O
-        print("[bench] oracle on sampled slices", file=sys.stderr, flush=True)
+        # scans in an order that visits every batch and head early; the oracle stops at the time cap
+        order = [(i % B, (i + i // B) % H) for i in range(B * H)]
+        print(f"[bench] fp64 oracle on up to {len(order)} scans ({args.oracle_seconds:.0f} s cap)",
+              file=sys.stderr, flush=True)
+        o_host = o.float().cpu().numpy()
+        W_host = W_out.cpu().numpy()
         errs_o, errs_w, done = [], [], []
         t0 = time.perf_counter()
-        for (b, h) in sample:
+        for (b, h) in order:
             qs, ks, vs, es = exact[(b, h)]
-            o_ref, W_ref, _ = O.ttt_scan_ref(qs, ks, vs, es, *Wh[h], chunk, O.MASK_APPLY_THEN_UPDATE, O.UPD_GD_L2)
+            o_ref, W_ref, _ = O.ttt_scan_ref(qs, ks, vs, es, *Wh[h], chunk, O.MASK_APPLY_THEN_UPDATE, rule, 5, beta)
             done.append((b, h))
-            og = o_host[(b, h)].astype(np.float64)
+            og = o_host[b, h].astype(np.float64)
             errs_o.append(float(np.linalg.norm(og - o_ref) / np.linalg.norm(o_ref)))
-            Wg = W_host[(b, h)].astype(np.float64)
+            Wg = W_host[b, h].astype(np.float64)
             dm = d * m
             parts = (Wg[:dm].reshape(m, d), Wg[dm:2 * dm].reshape(m, d), Wg[2 * dm:].reshape(d, m))
             errs_w.append(max(float(np.linalg.norm(a - r) / np.linalg.norm(r)) for a, r in zip(parts, W_ref)))
@@ -220,8 +299,9 @@ def main():
                "sample": f"{len(done)} of {B * H} (batch, head) scans, each the full {N}-token sequence "
                          f"({nchunks} chunks), numpy fp64; scaled to the whole workload",
                "seconds": round(t_cpu, 2), "cpu": cpu_model()}
-        parity = {"slices": [list(s) for s in done], "max_rel_l2_o": max(errs_o), "max_rel_l2_W": max(errs_w),
+        parity = {"scans": len(done), "max_rel_l2_o": max(errs_o), "max_rel_l2_W": max(errs_w),
                   "tol": 2e-2, "ok": max(errs_o) <= 2e-2 and max(errs_w) <= 2e-2}
+        del exact, o_host, W_host
 
     # ---------------- other workloads (extra measurements, not the headline) ----------------
     extras = {}
@@ -280,8 +360,9 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic: seeded N(0,1)/sqrt(d) q,k,v in bf16, eta = 0.01 softplus(N(0,1)), W0 ~ N(0,1/d) per head",
-        "config": {"workload": "lact_lm_layer_b8_h4_n32768_d384_m768_chunk2048_gd_l2", "B": B, "H": H, "seq_len": N,
-                   "d_h": d, "m_h": m, "chunk": chunk, "mask": "apply_then_update", "update": "L2-Normalize(W - g)",
+        "config": {"workload": "lact_lm_layer_b8_h4_n32768_d384_m768_chunk2048_" + args.update, "B": B, "H": H,
+                   "seq_len": N, "d_h": d, "m_h": m, "chunk": chunk, "mask": "apply_then_update",
+                   "update": "L2-Normalize(W - g)" if not beta else "L2-Normalize(W - Muon(M)), M <- 0.9 M + g, 5 NS steps",
                    "parallelism": "none (one GPU)"},
         "mfma_frac_layer": round(layer_tflops / BF16_PEAK_TFLOPS, 4),
         "layer_tflops": round(layer_tflops, 2),

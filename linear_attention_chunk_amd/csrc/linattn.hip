@@ -20,7 +20,7 @@ namespace ttt {
 
 template <typename T> struct LinArgs {
     const T* q; const T* k; const T* v; const float* eta; const float* S0; T* o; float* Sout;
-    int64_t N; int dv; int chunk; int mode; int nvt;
+    int64_t N; int dv; int chunk; int mode; int nvt; int vt;
     uint32_t flags[32];  // STRIDED: bit j = chunk j updates
 };
 
@@ -59,11 +59,11 @@ __device__ __forceinline__ u32x4_t scale_vec(const u32x4_t& x, float s, float) {
     return r;
 }
 
-template <typename T, int DK, bool CAUSAL> struct LinCfg {
+template <typename T, int DK, bool CAUSAL, int VT_> struct LinCfg {
     static constexpr int ES = (int)sizeof(T);
     static constexpr int VEC = 16 / ES;
     static constexpr int TB = ES == 2 ? 64 : 32;  // tokens per sub-block
-    static constexpr int VT = 32;                  // d_v rows of S per workgroup
+    static constexpr int VT = VT_;                 // d_v rows of S per workgroup (16 or 32)
     static constexpr int PQ = DK * ES + 16;        // LDS pitch of rows of DK elements
     static constexpr int PT = TB * ES + 16;        // LDS pitch of rows of TB elements
     static constexpr int OFF_Q = 0;
@@ -78,8 +78,10 @@ template <typename T, int DK, bool CAUSAL> struct LinCfg {
     static constexpr int AWN = TB == 64 ? 1 : 2;
     static constexpr int AFN = VT / 16 / AWN;
     static constexpr int PFN = TB / 16 / AWN;
-    // state tiling: 2 x 2 waves over VT x DK
-    static constexpr int SFN = DK / 32;
+    // state tiling: WSV x WSK waves over VT x DK, 16-wide MFMA blocks
+    static constexpr int WSV = VT / 16, WSK = 4 / WSV;
+    static constexpr int SFN = DK / 16 / WSK;
+    static_assert(DK % (16 * WSK) == 0 && (VT == 32 || TB == 64), "state tiling");
     // register staging of one sub-block: q rows, and k and v in VEC x VEC (token x feature) blocks
     static constexpr int QV = TB * DK * ES / 16;
     static constexpr int QPER = (QV + kThreads - 1) / kThreads;
@@ -161,8 +163,8 @@ struct LinIter {
 };
 
 // The next sub-block's q, k, v and eta, held in registers while the current one is computed.
-template <typename T, int DK, bool CAUSAL> struct LinStage {
-    using C = LinCfg<T, DK, CAUSAL>;
+template <typename T, int DK, bool CAUSAL, int VT_> struct LinStage {
+    using C = LinCfg<T, DK, CAUSAL, VT_>;
     static constexpr int VEC = C::VEC, TB = C::TB, VT = C::VT;
     u32x4_t q[C::QPER];
     u32x4_t k[C::KPER][VEC];
@@ -261,9 +263,9 @@ template <typename T, int DK, bool CAUSAL> struct LinStage {
     }
 };
 
-template <typename T, int DK, bool CAUSAL>
+template <typename T, int DK, bool CAUSAL, int VT_>
 __global__ __launch_bounds__(kThreads) void k_linattn(LinArgs<T> a) {
-    using C = LinCfg<T, DK, CAUSAL>;
+    using C = LinCfg<T, DK, CAUSAL, VT_>;
     constexpr int ES = C::ES, TB = C::TB, VT = C::VT, PQ = C::PQ, PT = C::PT;
     __shared__ __attribute__((aligned(16))) char smem[C::LDS];
     char* Qs = smem + C::OFF_Q;
@@ -284,14 +286,14 @@ __global__ __launch_bounds__(kThreads) void k_linattn(LinArgs<T> a) {
     const float* eta = a.eta + (int64_t)scan * N;
     T* O = a.o + (int64_t)scan * N * a.dv + v0;
 
-    // state slice: wave (wv, wk) holds rows [16 wv, +16) x cols [wk DK/2, +DK/2)
-    const int wv = wave >> 1, wk = wave & 1;
+    // state slice: wave (wv, wk) holds rows [16 wv, +16) x cols [wk DK/WSK, +DK/WSK)
+    const int wv = wave / C::WSK, wk = wave % C::WSK;
     f32x4_t sacc[1][C::SFN];
 #pragma unroll
     for (int j = 0; j < C::SFN; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int vv = 16 * wv + 4 * (lane >> 4) + r, kk = wk * (DK / 2) + j * 16 + (lane & 15);
+            const int vv = 16 * wv + 4 * (lane >> 4) + r, kk = wk * (DK / C::WSK) + j * 16 + (lane & 15);
             sacc[0][j][r] = a.S0 ? a.S0[((int64_t)scan * a.dv + v0 + vv) * DK + kk] : 0.f;
         }
     auto refresh = [&]() {
@@ -299,7 +301,7 @@ __global__ __launch_bounds__(kThreads) void k_linattn(LinArgs<T> a) {
         for (int j = 0; j < C::SFN; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int vv = 16 * wv + 4 * (lane >> 4) + r, kk = wk * (DK / 2) + j * 16 + (lane & 15);
+                const int vv = 16 * wv + 4 * (lane >> 4) + r, kk = wk * (DK / C::WSK) + j * 16 + (lane & 15);
                 const float x = sacc[0][j][r];
                 if constexpr (ES == 2) {
                     const uint16_t hi = f2bf(x);
@@ -349,7 +351,7 @@ __global__ __launch_bounds__(kThreads) void k_linattn(LinArgs<T> a) {
 
     LinIter it;
     it.init(N, a.chunk, a.mode, TB, a.flags);
-    LinStage<T, DK, CAUSAL> g;
+    LinStage<T, DK, CAUSAL, VT_> g;
     LinTask cur{};
     if (!it.done) {
         cur = it.cur();
@@ -366,7 +368,7 @@ __global__ __launch_bounds__(kThreads) void k_linattn(LinArgs<T> a) {
             g.load(nxt, Q, K, V, a.dv, eta);
         }
         if (cur.apply) apply(cur);
-        if (cur.update) lds_mma<T, 1, C::SFN>(sacc, Vt, PT, 16 * wv, Kt, PT, wk * (DK / 2), TB * ES);
+        if (cur.update) lds_mma<T, 1, C::SFN>(sacc, Vt, PT, 16 * wv, Kt, PT, wk * (DK / C::WSK), TB * ES);
         if (cur.refresh) {
             lds_barrier();  // every wave is done reading S for this sub-block
             refresh();
@@ -379,7 +381,7 @@ __global__ __launch_bounds__(kThreads) void k_linattn(LinArgs<T> a) {
         for (int j = 0; j < C::SFN; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int vv = 16 * wv + 4 * (lane >> 4) + r, kk = wk * (DK / 2) + j * 16 + (lane & 15);
+                const int vv = 16 * wv + 4 * (lane >> 4) + r, kk = wk * (DK / C::WSK) + j * 16 + (lane & 15);
                 a.Sout[((int64_t)scan * a.dv + v0 + vv) * DK + kk] = sacc[0][j][r];
             }
     }
@@ -410,10 +412,18 @@ template <typename T, int DK>
 static ttt_status launch_lin(LinArgs<T>& a, int grid, hipStream_t st) {
     {
         ProfScope ps(PK_LINATTN, st);
-        if (a.mode == TTT_MASK_TOKEN_CAUSAL)
-            hipLaunchKernelGGL((k_linattn<T, DK, true>), dim3(grid), dim3(kThreads), 0, st, a);
-        else
-            hipLaunchKernelGGL((k_linattn<T, DK, false>), dim3(grid), dim3(kThreads), 0, st, a);
+        if (a.vt == 16) {
+            if constexpr (sizeof(T) == 2 && DK % 64 == 0) {
+                if (a.mode == TTT_MASK_TOKEN_CAUSAL)
+                    hipLaunchKernelGGL((k_linattn<T, DK, true, 16>), dim3(grid), dim3(kThreads), 0, st, a);
+                else
+                    hipLaunchKernelGGL((k_linattn<T, DK, false, 16>), dim3(grid), dim3(kThreads), 0, st, a);
+            }
+        } else if (a.mode == TTT_MASK_TOKEN_CAUSAL) {
+            hipLaunchKernelGGL((k_linattn<T, DK, true, 32>), dim3(grid), dim3(kThreads), 0, st, a);
+        } else {
+            hipLaunchKernelGGL((k_linattn<T, DK, false, 32>), dim3(grid), dim3(kThreads), 0, st, a);
+        }
     }
     return check_launch("k_linattn");
 }
@@ -473,17 +483,20 @@ extern "C" ttt_status linattn_forward(const linattn_desc* desc, const void* q, c
     const size_t sb = (size_t)S * D.d_v * D.d_k * 4;
     if (overlaps(S_out, sb, S0, sb)) return fail(TTT_ERR_INVALID_ARGUMENT, "S_out overlaps S0");
     hipStream_t st = (hipStream_t)stream;
-    const int nvt = D.d_v / 32;
+    // 32-row slices of S: measured faster than 16-row slices, whose extra workgroups double the
+    // re-reads of q and k (the 16-row instantiation is kept for the bf16 kernel)
+    const int vt = 32;
+    const int nvt = D.d_v / vt;
     if (D.io_dtype == TTT_BF16) {
         LinArgs<uint16_t> a{(const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, eta, S0, (uint16_t*)o, S_out,
-                            D.N, D.d_v, D.chunk, D.mask, nvt, {}};
+                            D.N, D.d_v, D.chunk, D.mask, nvt, vt, {}};
         if (D.mask == TTT_MASK_STRIDED)
             for (int64_t j = 0; j < cdiv(D.N, D.chunk); ++j)
                 if (D.update_chunks[j]) a.flags[j >> 5] |= 1u << (j & 31);
         return run_lin<uint16_t>(D, a, st);
     }
     LinArgs<float> a{(const float*)q, (const float*)k, (const float*)v, eta, S0, (float*)o, S_out, D.N, D.d_v,
-                     D.chunk, D.mask, nvt, {}};
+                     D.chunk, D.mask, nvt, vt, {}};
     if (D.mask == TTT_MASK_STRIDED)
         for (int64_t j = 0; j < cdiv(D.N, D.chunk); ++j)
             if (D.update_chunks[j]) a.flags[j >> 5] |= 1u << (j & 31);

@@ -33,8 +33,12 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
     x = np.ascontiguousarray(x, dtype=np.float32)
     bits = x.view(np.uint32)
     # add 0x7FFF plus the lowest kept bit, then truncate: the usual RNE for 16 dropped bits
-    rounded = (bits + np.uint32(0x7FFF) + ((bits >> np.uint32(16)) & np.uint32(1))) & np.uint32(0xFFFF0000)
-    out = rounded.view(np.float32).copy()
+    out = np.right_shift(bits, np.uint32(16))
+    np.bitwise_and(out, np.uint32(1), out=out)
+    np.add(out, np.uint32(0x7FFF), out=out)
+    np.add(out, bits, out=out)
+    np.bitwise_and(out, np.uint32(0xFFFF0000), out=out)
+    out = out.view(np.float32)
     nan = np.isnan(x)
     if nan.any():
         out[nan] = np.float32("nan")
@@ -60,9 +64,10 @@ def slice_inputs(seed: int, b: int, h: int, N: int, d_k: int, d_v: int | None = 
     """q, k [N, d_k], v [N, d_v] and eta [N] for one (batch, head) slice."""
     d_v = d_k if d_v is None else d_v
     rng = np.random.default_rng([seed, b, h])
-    q = (rng.standard_normal((N, d_k), dtype=np.float32) / np.float32(np.sqrt(d_k))).astype(np.float32)
-    k = (rng.standard_normal((N, d_k), dtype=np.float32) / np.float32(np.sqrt(d_k))).astype(np.float32)
-    v = (rng.standard_normal((N, d_v), dtype=np.float32) / np.float32(np.sqrt(d_k))).astype(np.float32)
+    scale = np.float32(np.sqrt(d_k))
+    q = np.divide(rng.standard_normal((N, d_k), dtype=np.float32), scale, dtype=np.float32)
+    k = np.divide(rng.standard_normal((N, d_k), dtype=np.float32), scale, dtype=np.float32)
+    v = np.divide(rng.standard_normal((N, d_v), dtype=np.float32), scale, dtype=np.float32)
     raw = rng.standard_normal(N).astype(np.float32)
     if eta_kind == "softplus":
         eta = (eta_scale * _softplus(raw.astype(np.float64))).astype(np.float32)
