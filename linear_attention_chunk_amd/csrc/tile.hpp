@@ -96,11 +96,21 @@ template <> struct Mma32<float> {
 // One operand of a tile.  Element (row, k) of the tile is p[row * ld + k] for a k-contiguous
 // source and p[k * ld + row] for a k-strided one.  Rows at or beyond `rows` and k at or beyond
 // `kvalid` read as zero and are never dereferenced.
+//
+// Panels: the contiguous index (k, or row for a k-strided source) may be split into panels of
+// 2^ps elements that lie pstride elements apart, i.e. index i is found at (i >> ps) * pstride +
+// (i & (2^ps - 1)) instead of i.  A 16-byte vector never straddles two panels (2^ps is a multiple
+// of it), and the default ps = 30 means one panel.
 template <typename T> struct Opnd {
     const T* p;
     int64_t ld;
     int rows;
     int kvalid;
+    int ps = 30;
+    int64_t pstride = 0;
+    __device__ __forceinline__ int64_t inner(int i) const {
+        return (int64_t)(i >> ps) * pstride + (i & ((1 << ps) - 1));
+    }
 };
 
 template <int SEG> struct Pitch { static constexpr int value = SEG * 64 + 16; };
@@ -133,7 +143,9 @@ template <typename T, int R, int SEG> struct Stager<T, R, SEG, false> {
     uint32_t ok;  // bit i: r[i] is in range
     // Branch-free loads: an out-of-range vector is loaded from the operand's first element (always
     // valid) and zeroed only when stored, so no load result is consumed before the LDS store and
-    // the loads of a later stage can stay in flight.
+    // the loads of a later stage can stay in flight.  FULL: the caller guarantees that every row
+    // and k of the tile is in range, and the masking is left out.
+    template <bool FULL>
     __device__ __forceinline__ void load(const Opnd<T>& o, int k0) {
         ok = 0;
 #pragma unroll
@@ -142,11 +154,17 @@ template <typename T, int R, int SEG> struct Stager<T, R, SEG, false> {
             int row, c;
             place(v, row, c);
             const int k = k0 + c * VEC;
-            const bool in = (NV % kThreads == 0 || v < NV) && row < o.rows && k < o.kvalid;
-            r[i] = *reinterpret_cast<const u32x4_t*>(o.p + (in ? (int64_t)row * o.ld + k : 0));
-            ok |= (uint32_t)in << i;
+            if constexpr (FULL) {
+                if (NV % kThreads == 0 || v < NV)
+                    r[i] = *reinterpret_cast<const u32x4_t*>(o.p + (int64_t)row * o.ld + o.inner(k));
+            } else {
+                const bool in = (NV % kThreads == 0 || v < NV) && row < o.rows && k < o.kvalid;
+                r[i] = *reinterpret_cast<const u32x4_t*>(o.p + (in ? (int64_t)row * o.ld + o.inner(k) : 0));
+                ok |= (uint32_t)in << i;
+            }
         }
     }
+    template <bool FULL>
     __device__ __forceinline__ void store(char* lds) const {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
@@ -155,7 +173,7 @@ template <typename T, int R, int SEG> struct Stager<T, R, SEG, false> {
                 int row, c;
                 place(v, row, c);
                 *reinterpret_cast<u32x4_t*>(lds + row * PITCH + c * 16) =
-                    ((ok >> i) & 1u) ? r[i] : u32x4_t{0u, 0u, 0u, 0u};
+                    (FULL || ((ok >> i) & 1u)) ? r[i] : u32x4_t{0u, 0u, 0u, 0u};
             }
         }
     }
@@ -197,6 +215,7 @@ template <typename T, int R, int SEG> struct Stager<T, R, SEG, true> {
     u32x4_t r[PER][KPT];
     uint32_t ok;  // bit i * KPT + e: r[i][e] is in range (see the k-contiguous stager)
     static_assert(PER * KPT <= 32, "too many vectors per thread");
+    template <bool FULL>
     __device__ __forceinline__ void load(const Opnd<T>& o, int k0) {
         ok = 0;
 #pragma unroll
@@ -204,27 +223,35 @@ template <typename T, int R, int SEG> struct Stager<T, R, SEG, true> {
             const int u = threadIdx.x + i * kThreads;
             int rb, kc;
             place(u, rb, kc);
-            const bool live = (NU % kThreads == 0 || u < NU) && rb * VEC < o.rows;
+            const bool live = (NU % kThreads == 0 || u < NU) && (FULL || rb * VEC < o.rows);
 #pragma unroll
             for (int e = 0; e < KPT; ++e) {
                 const int k = k0 + kc * KPT + e;
-                const bool in = live && k < o.kvalid;
-                r[i][e] = *reinterpret_cast<const u32x4_t*>(o.p + (in ? (int64_t)k * o.ld + rb * VEC : 0));
-                ok |= (uint32_t)in << (i * KPT + e);
+                if constexpr (FULL) {
+                    if (NU % kThreads == 0 || u < NU)
+                        r[i][e] = *reinterpret_cast<const u32x4_t*>(o.p + (int64_t)k * o.ld + o.inner(rb * VEC));
+                } else {
+                    const bool in = live && k < o.kvalid;
+                    r[i][e] = *reinterpret_cast<const u32x4_t*>(o.p + (in ? (int64_t)k * o.ld + o.inner(rb * VEC) : 0));
+                    ok |= (uint32_t)in << (i * KPT + e);
+                }
             }
         }
     }
+    template <bool FULL>
     __device__ __forceinline__ uint32_t elt(int i, int e, int w) const {
-        return ((ok >> (i * KPT + e)) & 1u) ? r[i][e][w] : 0u;
+        return (FULL || ((ok >> (i * KPT + e)) & 1u)) ? r[i][e][w] : 0u;
     }
+    template <bool FULL>
     __device__ __forceinline__ uint32_t word(int i, int j, int w) const {
         if constexpr (ES == 2) {
-            const uint32_t x = elt(i, 2 * w, j >> 1), y = elt(i, 2 * w + 1, j >> 1);
+            const uint32_t x = elt<FULL>(i, 2 * w, j >> 1), y = elt<FULL>(i, 2 * w + 1, j >> 1);
             return (j & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
         } else {
-            return elt(i, w, j);
+            return elt<FULL>(i, w, j);
         }
     }
+    template <bool FULL>
     __device__ __forceinline__ void store(char* lds) const {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
@@ -236,12 +263,13 @@ template <typename T, int R, int SEG> struct Stager<T, R, SEG, true> {
                 for (int j = 0; j < VEC; ++j) {
                     char* dst = lds + (j * RB + rb) * PITCH + kc * KPT * ES;
                     if constexpr (WORDS == 1) {
-                        *reinterpret_cast<uint32_t*>(dst) = word(i, j, 0);
+                        *reinterpret_cast<uint32_t*>(dst) = word<FULL>(i, j, 0);
                     } else if constexpr (WORDS == 2) {
                         typedef uint32_t u2 __attribute__((ext_vector_type(2)));
-                        *reinterpret_cast<u2*>(dst) = u2{word(i, j, 0), word(i, j, 1)};
+                        *reinterpret_cast<u2*>(dst) = u2{word<FULL>(i, j, 0), word<FULL>(i, j, 1)};
                     } else {
-                        *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{word(i, j, 0), word(i, j, 1), word(i, j, 2), word(i, j, 3)};
+                        *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{word<FULL>(i, j, 0), word<FULL>(i, j, 1),
+                                                                   word<FULL>(i, j, 2), word<FULL>(i, j, 3)};
                     }
                 }
             }
@@ -259,7 +287,7 @@ template <typename T, int R, int SEG> struct RowMap<T, R, SEG, true> {
 // Tile engine.  NA A-operands of BM rows and NB B-operands of BN rows are staged per k-step
 // (k-strided sources when KSA / KSB); accumulator p is A[PM::a[p]] x B[PM::b[p]].  Waves form a
 // WGM x (4/WGM) grid over the tile and each wave owns (WM/32) x (WN/32) blocks of 32 x 32 per
-// accumulator.  Global loads run two stages ahead of the MFMAs (two register sets), LDS is
+// accumulator.  Global loads run one stage ahead of the LDS stores (one register set), LDS is
 // double-buffered, one barrier per stage.
 template <typename T, int BM_, int BN_, int SEG, int WGM, int NA, int NB, int NP, bool KSA, bool KSB>
 struct Tile {
@@ -283,17 +311,30 @@ struct Tile {
         SB b[NB];
     };
 
+    template <bool FULL>
     __device__ __forceinline__ static void issue(Regs& g, const Opnd<T> (&A)[NA], const Opnd<T> (&B)[NB], int k0) {
 #pragma unroll
-        for (int a = 0; a < NA; ++a) g.a[a].load(A[a], k0);
+        for (int a = 0; a < NA; ++a) g.a[a].template load<FULL>(A[a], k0);
 #pragma unroll
-        for (int b = 0; b < NB; ++b) g.b[b].load(B[b], k0);
+        for (int b = 0; b < NB; ++b) g.b[b].template load<FULL>(B[b], k0);
     }
+    template <bool FULL>
     __device__ __forceinline__ static void put(const Regs& g, char* st) {
 #pragma unroll
-        for (int a = 0; a < NA; ++a) g.a[a].store(st + a * A_BYTES);
+        for (int a = 0; a < NA; ++a) g.a[a].template store<FULL>(st + a * A_BYTES);
 #pragma unroll
-        for (int b = 0; b < NB; ++b) g.b[b].store(st + NA * A_BYTES + b * B_BYTES);
+        for (int b = 0; b < NB; ++b) g.b[b].template store<FULL>(st + NA * A_BYTES + b * B_BYTES);
+    }
+
+    // Whether every row and k of a tile over these operands is in range (then the stagers need
+    // no masking): all operands hold full tiles and K is a whole number of stages.
+    __device__ __forceinline__ static bool full(const Opnd<T> (&A)[NA], const Opnd<T> (&B)[NB], int K) {
+        bool f = K % KSTEP == 0;
+#pragma unroll
+        for (int a = 0; a < NA; ++a) f = f && A[a].rows >= BM && A[a].kvalid >= K;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) f = f && B[b].rows >= BN && B[b].kvalid >= K;
+        return f;
     }
 
     __device__ __forceinline__ void zero() {
@@ -307,108 +348,33 @@ struct Tile {
                     for (int r = 0; r < 16; ++r) acc[p][i][j][r] = 0.f;
     }
 
-    // One output tile: acc = sum over k of the staged products.  Global loads run two stages
-    // ahead (register sets g0 / g1), LDS is double-buffered, one LDS-only barrier per stage.
-    template <class PM>
-    __device__ __forceinline__ void run(const Opnd<T> (&A)[NA], const Opnd<T> (&B)[NB], int K, char* lds) {
+    // One output tile: acc = sum over k of the staged products.  LDS is double-buffered and one
+    // register set carries the global loads: while stage s is in the MFMAs, stage s + 1 is in LDS
+    // and the loads of stage s + 2 are in flight.  With a single set, every load outstanding when a
+    // stage is stored belongs to that stage, so the compiler's wait before the LDS store is exact
+    // (with two sets its conservative count across the loop edge also waited for the newer set).
+    template <class PM, bool FULL>
+    __device__ __forceinline__ void run_(const Opnd<T> (&A)[NA], const Opnd<T> (&B)[NB], int K, char* lds) {
         zero();
         const int nk = (K + KSTEP - 1) / KSTEP;
         if (nk <= 0) return;
-        Regs g0, g1;
-        issue(g0, A, B, 0);
-        put(g0, lds);
-        if (nk > 1) issue(g0, A, B, KSTEP);
-        if (nk > 2) issue(g1, A, B, 2 * KSTEP);
+        Regs g;
+        issue<FULL>(g, A, B, 0);
+        put<FULL>(g, lds);
+        if (nk > 1) issue<FULL>(g, A, B, KSTEP);
         lds_barrier();
-        int s = 0;
-        for (; s + 4 < nk; s += 2) {  // steady state: no tail conditions inside
-            compute<PM>(lds);
-            put(g0, lds + STAGE);
-            issue(g0, A, B, (s + 3) * KSTEP);
-            lds_barrier();
-            compute<PM>(lds + STAGE);
-            put(g1, lds);
-            issue(g1, A, B, (s + 4) * KSTEP);
+        for (int s = 0; s < nk; ++s) {
+            compute<PM>(lds + (s & 1) * STAGE);
+            if (s + 1 < nk) put<FULL>(g, lds + ((s + 1) & 1) * STAGE);
+            if (s + 2 < nk) issue<FULL>(g, A, B, (s + 2) * KSTEP);
             lds_barrier();
         }
-        auto step = [&](Regs& g, int st) {
-            compute<PM>(lds + (st & 1) * STAGE);
-            if (st + 1 < nk) put(g, lds + ((st + 1) & 1) * STAGE);
-            if (st + 3 < nk) issue(g, A, B, (st + 3) * KSTEP);
-            lds_barrier();
-        };
-        for (; s + 1 < nk; s += 2) {
-            step(g0, s);
-            step(g1, s + 1);
-        }
-        if (s < nk) step(g0, s);
     }
-
-    // A sequence of ntiles output tiles with the same contraction length K, walked as one
-    // continuous pipeline: the loads for the next tile's first stages are in flight while the
-    // current tile finishes and while epi(t) (which reads acc through for_each) runs.
-    // ops(t, A, B) fills the operand descriptors of tile t.
-    template <class PM, class Ops, class Epi>
-    __device__ __forceinline__ void run_tiles(int ntiles, Ops&& ops, int K, char* lds, Epi&& epi) {
-        zero();
-        const int nk = (K + KSTEP - 1) / KSTEP;
-        if (nk <= 0 || ntiles <= 0) {
-            for (int t = 0; t < ntiles; ++t) epi(t);
-            return;
-        }
-        const int total = ntiles * nk;
-        Opnd<T> A[NA], B[NB];
-        int cur_t = -1;
-        auto issue_stage = [&](Regs& g, int s) {
-            const int t = s / nk;
-            if (t != cur_t) {
-                ops(t, A, B);
-                cur_t = t;
-            }
-            issue(g, A, B, (s - t * nk) * KSTEP);
-        };
-        Regs g0, g1;
-        issue_stage(g0, 0);
-        put(g0, lds);
-        if (total > 1) issue_stage(g0, 1);
-        if (total > 2) issue_stage(g1, 2);
-        lds_barrier();
-        // invariant at the top of stage s: LDS[s & 1] holds stage s; the register set of parity
-        // (s & 1) holds stage s + 1 and the other set holds stage s + 2 (each if it exists)
-        auto finish = [&](int s) {
-            if ((s + 1) % nk == 0) {
-                epi(s / nk);
-                if (s + 1 < total) zero();  // the last tile's acc stays readable after return
-            }
-        };
-        int s = 0;
-        // steady state, free of tail conditions so that the compiler can track which loads are
-        // still in flight: every stage stores stage s + 1 and issues stage s + 3
-        for (; s + 4 < total; s += 2) {
-            compute<PM>(lds);
-            finish(s);
-            put(g0, lds + STAGE);
-            issue_stage(g0, s + 3);
-            lds_barrier();
-            compute<PM>(lds + STAGE);
-            finish(s + 1);
-            put(g1, lds);
-            issue_stage(g1, s + 4);
-            lds_barrier();
-        }
-        // the last (at most four) stages
-        auto step = [&](Regs& g, int st) {
-            compute<PM>(lds + (st & 1) * STAGE);
-            finish(st);
-            if (st + 1 < total) put(g, lds + ((st + 1) & 1) * STAGE);
-            if (st + 3 < total) issue_stage(g, st + 3);
-            lds_barrier();
-        };
-        for (; s + 1 < total; s += 2) {
-            step(g0, s);
-            step(g1, s + 1);
-        }
-        if (s < total) step(g0, s);
+    // Full tiles (the common case) take the unmasked path; the branch is uniform per workgroup.
+    template <class PM>
+    __device__ __forceinline__ void run(const Opnd<T> (&A)[NA], const Opnd<T> (&B)[NB], int K, char* lds) {
+        if (full(A, B, K)) run_<PM, true>(A, B, K, lds);
+        else run_<PM, false>(A, B, K, lds);
     }
 
     template <class PM>

@@ -21,13 +21,22 @@
 
 namespace ttt {
 
-constexpr int kUpQRows = 256, kUpKRows = 128;  // token rows per up-kernel tile (query / key)
-constexpr int kORows = 256;                      // token rows per output tile
+constexpr int kUpQRows = 256;   // token rows per query tile
+constexpr int kUpKRows = 128;   // token rows per key tile
+constexpr int kUpCols = 64;     // hidden units per up-kernel tile
+constexpr int kORows = 256;     // token rows per output tile
+constexpr int kPanelShift = 6;  // intermediates are stored in panels of 64 hidden units
+constexpr int kPanel = 1 << kPanelShift;
 
+// The chunk intermediates Hq, HkE, DA, DC of one scan are stored in panels: hidden unit h of token t
+// is element (h / 64) * pan + t * 64 + h % 64, with pan = 64 x (chunk capacity).  An up-kernel
+// tile (128 or 256 tokens x 64 hidden units) then writes one contiguous block, which the memory
+// system absorbs far better than row pieces spread over a [chunk][m] array.
 template <typename T> struct StepArgs {
     const T* q; const T* k; const T* v; const float* eta; T* o;
     int64_t N; int d, m;
-    T* Hq; T* HkE; T* DA; T* DC; int64_t inter_stride;  // per-scan [chunk][m] intermediates
+    T* Hq; T* HkE; T* DA; T* DC; int64_t inter_stride;  // per-scan panel-layout intermediates
+    int64_t pan;                                          // panel stride (elements)
     const T* sh; int64_t sh_stride;                       // shadows [W1 | W3 | W2 | W2^T]
     float* G; int64_t g_stride;                           // [G1 | G3 | G2] fp32
     int64_t a0; int la;                                   // apply chunk: first token, length
@@ -36,20 +45,24 @@ template <typename T> struct StepArgs {
     int nG13, nG2, nO;                                    // down-kernel tiles per scan
 };
 
+template <typename T> __device__ __forceinline__ int64_t panel_off(const StepArgs<T>& a, int t, int h) {
+    return (int64_t)(h >> kPanelShift) * a.pan + (int64_t)t * kPanel + (h & (kPanel - 1));
+}
+
 // ---------------------------------------------------------------------------------------------
-// up: SwiGLU forward of the queries, forward + backward of the keys
+// up: SwiGLU forward of the queries, forward + backward of the keys.  Two workgroups per CU, so
+// that one's epilogue (the SwiGLU forward/backward arithmetic and the stores) overlaps the other's
+// MFMA main loop.
 template <typename T>
 __global__ __launch_bounds__(kThreads, 2) void k_up(StepArgs<T> a) {
-    using TQ = Tile<T, kUpQRows, 64, 1, 2, 1, 2, 2, false, false>;   // wave: 128 tokens x 32 hidden x {A, C}
-    using TK = Tile<T, kUpKRows, 64, 1, 2, 2, 3, 3, false, false>;   // wave: 64 tokens x 32 hidden x {A, C, DH}
+    using TQ = Tile<T, kUpQRows, kUpCols, 1, 2, 1, 2, 2, false, false>;  // wave: 128 tokens x 32 hidden x {A, C}
+    using TK = Tile<T, kUpKRows, kUpCols, 1, 2, 2, 3, 3, false, false>;  // wave: 64 tokens x 32 hidden x {A, C, DH}
     constexpr int LDSB = TQ::LDS > TK::LDS ? TQ::LDS : TK::LDS;
     __shared__ __attribute__((aligned(16))) char smem[LDSB];
 
-    // a workgroup takes one block of token rows and walks a group of 64-wide hidden tiles
     const int per = a.nQ + a.nK;
     const int lb = xcd_block(gridDim.x);
     const int s = lb / per, t = lb % per;
-    const int nct = (a.m + 63) / 64;
     const int64_t dm = (int64_t)a.d * a.m;
     const T* sh = a.sh + s * a.sh_stride;
     const T* W1s = sh;
@@ -58,7 +71,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_up(StepArgs<T> a) {
     const int64_t ioff = s * a.inter_stride;
 
     if (t < a.nQ) {
-        const int r0 = (t / nct) * kUpQRows, c0 = (t % nct) * 64;
+        const int nct = (a.m + kUpCols - 1) / kUpCols;
+        const int r0 = (t / nct) * kUpQRows, c0 = (t % nct) * kUpCols;
         const T* Q = a.q + ((int64_t)s * a.N + a.a0 + r0) * a.d;
         const Opnd<T> A[1] = {{Q, a.d, a.la - r0, a.d}};
         const Opnd<T> B[2] = {{W1s + (int64_t)c0 * a.d, a.d, a.m - c0, a.d},
@@ -66,13 +80,19 @@ __global__ __launch_bounds__(kThreads, 2) void k_up(StepArgs<T> a) {
         TQ tl;
         tl.template run<PMQ>(A, B, a.d, smem);
         T* Hq = a.Hq + ioff;
-        tl.for_each([&](const float (&v)[2], int row, int col) {
-            const int tr = r0 + row, tc = c0 + col;
-            if (tr < a.la && tc < a.m) Hq[(int64_t)tr * a.m + tc] = Elt<T>::st(v[0] * sigmoidf_(v[0]) * v[1]);
-        });
+        auto epi = [&](auto check) {
+            tl.for_each([&](const float (&v)[2], int row, int col) {
+                const int tr = r0 + row, tc = c0 + col;
+                if (!decltype(check)::value || (tr < a.la && tc < a.m))
+                    Hq[panel_off(a, tr, tc)] = Elt<T>::st(v[0] * sigmoidf_(v[0]) * v[1]);
+            });
+        };
+        if (r0 + kUpQRows <= a.la && c0 + kUpCols <= a.m) epi(std::false_type{});
+        else epi(std::true_type{});
     } else {
+        const int nct = (a.m + kUpCols - 1) / kUpCols;
         const int tt = t - a.nQ;
-        const int r0 = (tt / nct) * kUpKRows, c0 = (tt % nct) * 64;
+        const int r0 = (tt / nct) * kUpKRows, c0 = (tt % nct) * kUpCols;
         const int64_t tok = (int64_t)s * a.N + a.u0 + r0;
         const Opnd<T> A[2] = {{a.k + tok * a.d, a.d, a.lu - r0, a.d}, {a.v + tok * a.d, a.d, a.lu - r0, a.d}};
         const Opnd<T> B[3] = {{W1s + (int64_t)c0 * a.d, a.d, a.m - c0, a.d},
@@ -84,18 +104,22 @@ __global__ __launch_bounds__(kThreads, 2) void k_up(StepArgs<T> a) {
         T* HkE = a.HkE + ioff;
         T* DA = a.DA + ioff;
         T* DC = a.DC + ioff;
-        tl.for_each([&](const float (&v)[3], int row, int col) {
-            const int tr = r0 + row, tc = c0 + col;
-            if (tr < a.lu && tc < a.m) {
-                const float e = eta[row];
-                const float x = v[0], c = v[1], sg = sigmoidf_(x);
-                const float dh = -e * v[2];  // dLoss/dH = -eta (V W2)
-                const int64_t off = (int64_t)tr * a.m + tc;
-                HkE[off] = Elt<T>::st(-e * x * sg * c);
-                DA[off] = Elt<T>::st(dh * c * sg * (1.f + x * (1.f - sg)));
-                DC[off] = Elt<T>::st(dh * x * sg);
-            }
-        });
+        auto epi = [&](auto check) {
+            tl.for_each([&](const float (&v)[3], int row, int col) {
+                const int tr = r0 + row, tc = c0 + col;
+                if (!decltype(check)::value || (tr < a.lu && tc < a.m)) {
+                    const float e = eta[row];
+                    const float x = v[0], c = v[1], sg = sigmoidf_(x);
+                    const float dh = -e * v[2];  // dLoss/dH = -eta (V W2)
+                    const int64_t off = panel_off(a, tr, tc);
+                    HkE[off] = Elt<T>::st(-e * x * sg * c);
+                    DA[off] = Elt<T>::st(dh * c * sg * (1.f + x * (1.f - sg)));
+                    DC[off] = Elt<T>::st(dh * x * sg);
+                }
+            });
+        };
+        if (r0 + kUpKRows <= a.lu && c0 + kUpCols <= a.m) epi(std::false_type{});
+        else epi(std::true_type{});
     }
 }
 
@@ -120,7 +144,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_down(StepArgs<T> a) {
     if (t < a.nG13) {  // G1 = DA^T K and G3 = DC^T K: rows c of m, cols e of d
         const int r0 = (t / ndt) * 128, c0 = (t % ndt) * 128;
         const T* K = a.k + ((int64_t)s * a.N + a.u0) * a.d;
-        const Opnd<T> A[2] = {{a.DA + ioff + r0, a.m, a.m - r0, a.lu}, {a.DC + ioff + r0, a.m, a.m - r0, a.lu}};
+        const int64_t hoff = ioff + panel_off(a, 0, r0);
+        const Opnd<T> A[2] = {{a.DA + hoff, kPanel, a.m - r0, a.lu, kPanelShift, a.pan},
+                              {a.DC + hoff, kPanel, a.m - r0, a.lu, kPanelShift, a.pan}};
         const Opnd<T> B[1] = {{K + c0, a.d, a.d - c0, a.lu}};
         TG13 tl;
         tl.template run<PMG>(A, B, a.lu, smem);
@@ -139,7 +165,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_down(StepArgs<T> a) {
         const int r0 = (t / nmt2) * 128, c0 = (t % nmt2) * 256;
         const T* V = a.v + ((int64_t)s * a.N + a.u0) * a.d;
         const Opnd<T> A[1] = {{V + r0, a.d, a.d - r0, a.lu}};
-        const Opnd<T> B[1] = {{a.HkE + ioff + c0, a.m, a.m - c0, a.lu}};
+        const Opnd<T> B[1] = {{a.HkE + ioff + panel_off(a, 0, c0), kPanel, a.m - c0, a.lu, kPanelShift, a.pan}};
         TG2 tl;
         tl.template run<PM1>(A, B, a.lu, smem);
         float* G = a.G + s * a.g_stride + 2 * dm;
@@ -153,7 +179,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_down(StepArgs<T> a) {
     {  // O = Hq W2^T: rows t of the apply chunk, cols e of d
         const int r0 = (t / ndt) * kORows, c0 = (t % ndt) * 128;
         const T* W2s = a.sh + s * a.sh_stride + 2 * dm;
-        const Opnd<T> A[1] = {{a.Hq + ioff + (int64_t)r0 * a.m, a.m, a.la - r0, a.m}};
+        const Opnd<T> A[1] = {{a.Hq + ioff + panel_off(a, r0, 0), kPanel, a.la - r0, a.m, kPanelShift, a.pan}};
         const Opnd<T> B[1] = {{W2s + (int64_t)c0 * a.m, a.m, a.d - c0, a.m}};
         TO tl;
         tl.template run<PM1>(A, B, a.m, smem);
@@ -473,7 +499,7 @@ static Layout make_layout(const ttt_desc& D, bool muon, bool own_m) {
     const int64_t p = d < m ? d : m;
     L.wf_stride = 3 * dm;
     L.sh_stride = 4 * dm;
-    L.inter_stride = bmax * m;
+    L.inter_stride = bmax * cdiv(m, kPanel) * kPanel;  // panel layout, see StepArgs
     L.g_stride = 3 * dm;
     L.x_stride = 3 * dm;
     L.gram_stride = 3 * p * p;
@@ -559,7 +585,8 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
     const int nc = (int)cdiv(D.N, D.chunk);
     const bool uta = D.mask == TTT_MASK_FULL || D.mask == TTT_MASK_UPDATE_THEN_APPLY;
     const int nsteps = D.N == 0 ? 0 : (uta ? nc + 1 : nc);
-    const int ntm = (int)cdiv(m, 128), ntd = (int)cdiv(d, 128), nc64 = (int)cdiv(m, 64);
+    const int ntm = (int)cdiv(m, 128), ntd = (int)cdiv(d, 128);
+    const int64_t bmax = D.N < D.chunk ? D.N : D.chunk;
     for (int step = 0; step < nsteps; ++step) {
         int ja = uta ? step - 1 : step;
         int ju = step < nc ? step : -1;
@@ -569,14 +596,15 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
         a.N = D.N; a.d = d; a.m = m;
         a.Hq = (T*)(ws + L.hq); a.HkE = (T*)(ws + L.hke); a.DA = (T*)(ws + L.da); a.DC = (T*)(ws + L.dc);
         a.inter_stride = L.inter_stride;
+        a.pan = bmax * kPanel;
         a.sh = sh[cur]; a.sh_stride = L.sh_stride;
         a.G = G; a.g_stride = L.g_stride;
         a.a0 = ja >= 0 ? (int64_t)ja * D.chunk : 0;
         a.la = ja >= 0 ? (int)(std::min<int64_t>((int64_t)(ja + 1) * D.chunk, D.N) - a.a0) : 0;
         a.u0 = ju >= 0 ? (int64_t)ju * D.chunk : 0;
         a.lu = ju >= 0 ? (int)(std::min<int64_t>((int64_t)(ju + 1) * D.chunk, D.N) - a.u0) : 0;
-        a.nQ = a.la ? (int)cdiv(a.la, kUpQRows) * nc64 : 0;
-        a.nK = a.lu ? (int)cdiv(a.lu, kUpKRows) * nc64 : 0;
+        a.nQ = a.la ? (int)(cdiv(a.la, kUpQRows) * cdiv(m, kUpCols)) : 0;
+        a.nK = a.lu ? (int)(cdiv(a.lu, kUpKRows) * cdiv(m, kUpCols)) : 0;
         a.nG13 = (a.lu && !D.last_layer_only) ? ntm * ntd : 0;
         a.nG2 = a.lu ? ntd * (int)cdiv(m, 256) : 0;
         a.nO = a.la ? (int)cdiv(a.la, kORows) * ntd : 0;
