@@ -77,6 +77,21 @@ template <> struct Elt<float> {
     }
 };
 
+// Four consecutive elements in the storage type, as one 8-byte (bf16) or 16-byte (fp32) store.
+template <typename T> struct Pack4;
+template <> struct Pack4<uint16_t> {
+    typedef uint32_t raw __attribute__((ext_vector_type(2)));
+    __device__ static void store(uint16_t* p, float a, float b, float c, float d) {
+        *reinterpret_cast<raw*>(p) = raw{(uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16),
+                                         (uint32_t)f2bf(c) | ((uint32_t)f2bf(d) << 16)};
+    }
+};
+template <> struct Pack4<float> {
+    __device__ static void store(float* p, float a, float b, float c, float d) {
+        *reinterpret_cast<f32x4_t*>(p) = f32x4_t{a, b, c, d};
+    }
+};
+
 // 32 x 32 blocks: one 32-byte k window per call (16 bf16 / 8 fp32 values of k)
 template <typename T> struct Mma32;
 template <> struct Mma32<uint16_t> {
@@ -426,6 +441,31 @@ struct Tile {
             }
     }
 
+    // f(const float (&v)[NP][4], int row, int col) for every group of 4 accumulator elements of
+    // this thread that share a column and cover rows row .. row + 3 (row a multiple of 4).  Only
+    // for k-contiguous A operands, whose tile rows are not permuted.
+    template <class F>
+    __device__ __forceinline__ void for_each4(F&& f) const {
+        static_assert(!KSA, "row groups need unpermuted rows");
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int wm = wave / WGN, wn = wave % WGN;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int col = RowMap<T, BN, SEG, KSB>::row_of(wn * WN + j * 32 + (lane & 31));
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    float v[NP][4];
+#pragma unroll
+                    for (int p = 0; p < NP; ++p)
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) v[p][u] = acc[p][i][j][4 * g + u];
+                    f(v, wm * WM + i * 32 + 8 * g + 4 * (lane >> 5), col);
+                }
+            }
+    }
+
     // f(const float (&v)[NP], int row, int col) for every accumulator element of this thread,
     // with row / col the logical tile coordinates
     template <class F>
@@ -452,6 +492,7 @@ struct PM1 { static constexpr int a[1] = {0}; static constexpr int b[1] = {0}; }
 struct PMQ { static constexpr int a[2] = {0, 0}; static constexpr int b[2] = {0, 1}; };
 struct PMK { static constexpr int a[3] = {0, 0, 1}; static constexpr int b[3] = {0, 1, 2}; };
 struct PMG { static constexpr int a[2] = {0, 1}; static constexpr int b[2] = {0, 0}; };
+struct PMKT { static constexpr int a[3] = {0, 1, 2}; static constexpr int b[3] = {0, 0, 1}; };
 
 // Workgroups are dispatched to the 8 XCDs round-robin (block b runs on XCD b % 8).  Renumbering so
 // that the blocks one XCD receives are consecutive logical blocks keeps tiles that share operands

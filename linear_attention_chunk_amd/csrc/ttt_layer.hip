@@ -28,15 +28,19 @@ constexpr int kORows = 256;     // token rows per output tile
 constexpr int kPanelShift = 6;  // intermediates are stored in panels of 64 hidden units
 constexpr int kPanel = 1 << kPanelShift;
 
-// The chunk intermediates Hq, HkE, DA, DC of one scan are stored in panels: hidden unit h of token t
-// is element (h / 64) * pan + t * 64 + h % 64, with pan = 64 x (chunk capacity).  An up-kernel
-// tile (128 or 256 tokens x 64 hidden units) then writes one contiguous block, which the memory
-// system absorbs far better than row pieces spread over a [chunk][m] array.
+// Chunk intermediates of one scan.  Hq (read by the output GEMM, which contracts over hidden
+// units) is token-major in panels: hidden unit h of token t is element (h / 64) * pan + t * 64 +
+// h % 64, with pan = 64 x (chunk capacity), so a query tile writes one contiguous block.  HkE, DA
+// and DC (read by the gradient GEMMs, which contract over tokens) are hidden-major: element
+// h * tp + t, tp = chunk capacity rounded up to 8.  In the MFMA result layout each lane holds 4
+// consecutive tokens of one hidden unit, so the key tiles store them 4 at a time, and the
+// gradient GEMMs read them k-contiguous.
 template <typename T> struct StepArgs {
     const T* q; const T* k; const T* v; const float* eta; T* o;
     int64_t N; int d, m;
-    T* Hq; T* HkE; T* DA; T* DC; int64_t inter_stride;  // per-scan panel-layout intermediates
-    int64_t pan;                                          // panel stride (elements)
+    T* Hq; T* HkE; T* DA; T* DC; int64_t inter_stride;  // per-scan intermediates
+    int64_t pan;                                          // Hq panel stride (elements)
+    int tp;                                               // HkE / DA / DC row pitch (elements)
     const T* sh; int64_t sh_stride;                       // shadows [W1 | W3 | W2 | W2^T]
     float* G; int64_t g_stride;                           // [G1 | G3 | G2] fp32
     int64_t a0; int la;                                   // apply chunk: first token, length
@@ -52,11 +56,13 @@ template <typename T> __device__ __forceinline__ int64_t panel_off(const StepArg
 // ---------------------------------------------------------------------------------------------
 // up: SwiGLU forward of the queries, forward + backward of the keys.  Two workgroups per CU, so
 // that one's epilogue (the SwiGLU forward/backward arithmetic and the stores) overlaps the other's
-// MFMA main loop.
+// MFMA main loop.  Key tiles are computed transposed (hidden units x tokens): each lane then holds
+// consecutive tokens of one hidden unit, so the hidden-major HkE, DA, DC leave as contiguous runs,
+// and eta is one value per lane column.
 template <typename T>
 __global__ __launch_bounds__(kThreads, 2) void k_up(StepArgs<T> a) {
     using TQ = Tile<T, kUpQRows, kUpCols, 1, 2, 1, 2, 2, false, false>;  // wave: 128 tokens x 32 hidden x {A, C}
-    using TK = Tile<T, kUpKRows, kUpCols, 1, 2, 2, 3, 3, false, false>;  // wave: 64 tokens x 32 hidden x {A, C, DH}
+    using TK = Tile<T, kUpCols, kUpKRows, 1, 2, 3, 2, 3, false, false>;  // wave: 32 hidden x 64 tokens x {A, C, DH}
     constexpr int LDSB = TQ::LDS > TK::LDS ? TQ::LDS : TK::LDS;
     __shared__ __attribute__((aligned(16))) char smem[LDSB];
 
@@ -79,12 +85,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_up(StepArgs<T> a) {
                               {W3s + (int64_t)c0 * a.d, a.d, a.m - c0, a.d}};
         TQ tl;
         tl.template run<PMQ>(A, B, a.d, smem);
-        T* Hq = a.Hq + ioff;
+        // the tile's 64 hidden units are one panel: element (row, col) is row * 64 + col from its corner
+        static_assert(kUpCols == kPanel, "a query tile must cover exactly one panel");
+        T* Hq = a.Hq + ioff + panel_off(a, r0, c0);
         auto epi = [&](auto check) {
             tl.for_each([&](const float (&v)[2], int row, int col) {
-                const int tr = r0 + row, tc = c0 + col;
-                if (!decltype(check)::value || (tr < a.la && tc < a.m))
-                    Hq[panel_off(a, tr, tc)] = Elt<T>::st(v[0] * sigmoidf_(v[0]) * v[1]);
+                if (!decltype(check)::value || (r0 + row < a.la && c0 + col < a.m))
+                    Hq[(uint32_t)row * kPanel + (uint32_t)col] = Elt<T>::st(v[0] * sigmoidf_(v[0]) * v[1]);
             });
         };
         if (r0 + kUpQRows <= a.la && c0 + kUpCols <= a.m) epi(std::false_type{});
@@ -94,27 +101,34 @@ __global__ __launch_bounds__(kThreads, 2) void k_up(StepArgs<T> a) {
         const int tt = t - a.nQ;
         const int r0 = (tt / nct) * kUpKRows, c0 = (tt % nct) * kUpCols;
         const int64_t tok = (int64_t)s * a.N + a.u0 + r0;
-        const Opnd<T> A[2] = {{a.k + tok * a.d, a.d, a.lu - r0, a.d}, {a.v + tok * a.d, a.d, a.lu - r0, a.d}};
-        const Opnd<T> B[3] = {{W1s + (int64_t)c0 * a.d, a.d, a.m - c0, a.d},
+        const Opnd<T> A[3] = {{W1s + (int64_t)c0 * a.d, a.d, a.m - c0, a.d},
                               {W3s + (int64_t)c0 * a.d, a.d, a.m - c0, a.d},
                               {W2Ts + (int64_t)c0 * a.d, a.d, a.m - c0, a.d}};
+        const Opnd<T> B[2] = {{a.k + tok * a.d, a.d, a.lu - r0, a.d}, {a.v + tok * a.d, a.d, a.lu - r0, a.d}};
         TK tl;
-        tl.template run<PMK>(A, B, a.d, smem);
+        tl.template run<PMKT>(A, B, a.d, smem);
         const float* eta = a.eta + tok;
-        T* HkE = a.HkE + ioff;
-        T* DA = a.DA + ioff;
-        T* DC = a.DC + ioff;
+        T* HkE = a.HkE + ioff + (int64_t)c0 * a.tp + r0;
+        T* DA = a.DA + ioff + (int64_t)c0 * a.tp + r0;
+        T* DC = a.DC + ioff + (int64_t)c0 * a.tp + r0;
+        // SwiGLU backward at one (token, hidden unit): x = (K W1^T), c = (K W3^T), p = (V W2) there
+        auto bwd = [](float x, float c, float p, float e, float& hk, float& da, float& dc) {
+            const float sg = sigmoidf_(x), xs = x * sg;
+            const float dh = -e * p;  // dLoss/dH = -eta (V W2)
+            hk = -e * xs * c;         // -eta o SiLU(A) o C
+            da = dh * c * (sg + xs * (1.f - sg));
+            dc = dh * xs;
+        };
+        // tile row = hidden unit c0 + row, tile column = token r0 + col
         auto epi = [&](auto check) {
             tl.for_each([&](const float (&v)[3], int row, int col) {
-                const int tr = r0 + row, tc = c0 + col;
-                if (!decltype(check)::value || (tr < a.lu && tc < a.m)) {
-                    const float e = eta[row];
-                    const float x = v[0], c = v[1], sg = sigmoidf_(x);
-                    const float dh = -e * v[2];  // dLoss/dH = -eta (V W2)
-                    const int64_t off = panel_off(a, tr, tc);
-                    HkE[off] = Elt<T>::st(-e * x * sg * c);
-                    DA[off] = Elt<T>::st(dh * c * sg * (1.f + x * (1.f - sg)));
-                    DC[off] = Elt<T>::st(dh * x * sg);
+                if (!decltype(check)::value || (r0 + col < a.lu && c0 + row < a.m)) {
+                    float hk, da, dc;
+                    bwd(v[0], v[1], v[2], eta[col], hk, da, dc);
+                    const uint32_t off = (uint32_t)row * (uint32_t)a.tp + (uint32_t)col;
+                    HkE[off] = Elt<T>::st(hk);
+                    DA[off] = Elt<T>::st(da);
+                    DC[off] = Elt<T>::st(dc);
                 }
             });
         };
@@ -127,8 +141,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_up(StepArgs<T> a) {
 // down: chunk gradients (contractions over tokens) and the apply chunk's outputs
 template <typename T>
 __global__ __launch_bounds__(kThreads, 2) void k_down(StepArgs<T> a) {
-    using TG13 = Tile<T, 128, 128, 1, 2, 2, 1, 2, true, true>;  // G1 and G3 share the K operand
-    using TG2 = Tile<T, 128, 256, 1, 2, 1, 1, 1, true, true>;
+    using TG13 = Tile<T, 128, 128, 1, 2, 2, 1, 2, false, true>;  // G1 and G3 share the K operand
+    using TG2 = Tile<T, 128, 256, 1, 2, 1, 1, 1, true, false>;
     using TO = Tile<T, kORows, 128, 1, 2, 1, 1, 1, false, false>;
     constexpr int L1 = TG13::LDS > TG2::LDS ? TG13::LDS : TG2::LDS;
     constexpr int LDSB = L1 > TO::LDS ? L1 : TO::LDS;
@@ -144,9 +158,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_down(StepArgs<T> a) {
     if (t < a.nG13) {  // G1 = DA^T K and G3 = DC^T K: rows c of m, cols e of d
         const int r0 = (t / ndt) * 128, c0 = (t % ndt) * 128;
         const T* K = a.k + ((int64_t)s * a.N + a.u0) * a.d;
-        const int64_t hoff = ioff + panel_off(a, 0, r0);
-        const Opnd<T> A[2] = {{a.DA + hoff, kPanel, a.m - r0, a.lu, kPanelShift, a.pan},
-                              {a.DC + hoff, kPanel, a.m - r0, a.lu, kPanelShift, a.pan}};
+        const int64_t hoff = ioff + (int64_t)r0 * a.tp;
+        const Opnd<T> A[2] = {{a.DA + hoff, a.tp, a.m - r0, a.lu}, {a.DC + hoff, a.tp, a.m - r0, a.lu}};
         const Opnd<T> B[1] = {{K + c0, a.d, a.d - c0, a.lu}};
         TG13 tl;
         tl.template run<PMG>(A, B, a.lu, smem);
@@ -165,7 +178,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_down(StepArgs<T> a) {
         const int r0 = (t / nmt2) * 128, c0 = (t % nmt2) * 256;
         const T* V = a.v + ((int64_t)s * a.N + a.u0) * a.d;
         const Opnd<T> A[1] = {{V + r0, a.d, a.d - r0, a.lu}};
-        const Opnd<T> B[1] = {{a.HkE + ioff + panel_off(a, 0, c0), kPanel, a.m - c0, a.lu, kPanelShift, a.pan}};
+        const Opnd<T> B[1] = {{a.HkE + ioff + (int64_t)c0 * a.tp, a.tp, a.m - c0, a.lu}};
         TG2 tl;
         tl.template run<PM1>(A, B, a.lu, smem);
         float* G = a.G + s * a.g_stride + 2 * dm;
@@ -499,7 +512,7 @@ static Layout make_layout(const ttt_desc& D, bool muon, bool own_m) {
     const int64_t p = d < m ? d : m;
     L.wf_stride = 3 * dm;
     L.sh_stride = 4 * dm;
-    L.inter_stride = bmax * cdiv(m, kPanel) * kPanel;  // panel layout, see StepArgs
+    L.inter_stride = std::max<int64_t>(bmax * cdiv(m, kPanel) * kPanel, m * cdiv(bmax, 8) * 8);  // see StepArgs
     L.g_stride = 3 * dm;
     L.x_stride = 3 * dm;
     L.gram_stride = 3 * p * p;
@@ -551,6 +564,9 @@ static ttt_status validate(const ttt_desc* D) {
     if (D->w0_per_batch != 0 && D->w0_per_batch != 1) return fail(TTT_ERR_INVALID_ARGUMENT, "w0_per_batch must be 0/1");
     const int64_t S = (int64_t)D->B * D->H;
     if (S > (1 << 20) || (int64_t)D->N > (1LL << 31) / 2) return fail(TTT_ERR_INVALID_ARGUMENT, "B*H or N too large");
+    const int64_t bmax = D->N < D->chunk ? D->N : D->chunk;
+    if ((int64_t)D->m_h * ((bmax + 7) / 8 * 8) >= (1LL << 31))
+        return fail(TTT_ERR_UNSUPPORTED, "m_h x chunk must stay below 2^31 elements");
     return TTT_OK;
 }
 
@@ -597,6 +613,7 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
         a.Hq = (T*)(ws + L.hq); a.HkE = (T*)(ws + L.hke); a.DA = (T*)(ws + L.da); a.DC = (T*)(ws + L.dc);
         a.inter_stride = L.inter_stride;
         a.pan = bmax * kPanel;
+        a.tp = (int)(cdiv(bmax, 8) * 8);
         a.sh = sh[cur]; a.sh_stride = L.sh_stride;
         a.G = G; a.g_stride = L.g_stride;
         a.a0 = ja >= 0 ? (int64_t)ja * D.chunk : 0;
