@@ -125,7 +125,12 @@ ttt_status ttt_forward(const ttt_desc* desc, const void* q, const void* k, const
                        const float* eta, const float* W0, void* o, float* W_out, float* M_inout,
                        void* workspace, size_t workspace_bytes, void* stream);
 
-/* Device workspace that linattn_forward needs, in bytes. */
+/*
+ * Device workspace that linattn_forward needs, in bytes.  Zero when the call runs the sequential
+ * kernel (token-causal mode, or chunks so small that 4 d_k d_v > 2 chunk (d_k + d_v)); otherwise
+ * room for every chunk's own update and the state each chunk's queries see, 8 bytes per state
+ * element per chunk and scan (the chunk-parallel path).
+ */
 ttt_status linattn_workspace_bytes(const linattn_desc* desc, size_t* bytes);
 
 /*
@@ -136,6 +141,8 @@ ttt_status linattn_workspace_bytes(const linattn_desc* desc, size_t* bytes);
  *   q, k      [B][H][N][d_k] of io_dtype; v, o [B][H][N][d_v]; eta [B][H][N] fp32
  *   S0        nullable; [B][H][d_v][d_k] fp32 initial state (NULL = zeros)
  *   S_out     nullable; [B][H][d_v][d_k] fp32 state after the last chunk
+ *   workspace device buffer of at least linattn_workspace_bytes(desc) bytes, 256-byte aligned
+ *             (may be NULL when that is 0); TTT_ERR_WORKSPACE if it is too small
  */
 ttt_status linattn_forward(const linattn_desc* desc, const void* q, const void* k, const void* v,
                            const float* eta, const float* S0, void* o, float* S_out,
@@ -150,7 +157,7 @@ ttt_status linattn_forward(const linattn_desc* desc, const void* q, const void* 
  * read, and forgets them.  Kernel classes are numbered 0 .. TTT_PROF_KERNELS-1 and named by
  * ttt_profile_kernel_name.  Enabling or reading while another thread launches is allowed.
  */
-#define TTT_PROF_KERNELS 8
+#define TTT_PROF_KERNELS 11
 ttt_status ttt_profile_enable(int32_t on);
 ttt_status ttt_profile_read(float* ms, int32_t* count, int32_t n);
 const char* ttt_profile_kernel_name(int32_t i);

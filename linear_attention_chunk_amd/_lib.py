@@ -23,7 +23,7 @@ EXPORTS = (
     "linattn_workspace_bytes", "linattn_forward",
     "ttt_profile_enable", "ttt_profile_read", "ttt_profile_kernel_name",
 )
-PROF_KERNELS = 8
+PROF_KERNELS = 11
 
 
 class TttDesc(ctypes.Structure):

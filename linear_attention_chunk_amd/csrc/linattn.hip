@@ -4,14 +4,22 @@
 // the PaperTrace notes' section 1.1 and the token-causal limit ("From Linear Attention to Test-Time
 // Training", causal linear attention).
 //
-// One workgroup owns one (batch, head) scan and a 32-row slice of S's d_v rows, and walks the
-// sequence in sub-blocks of TB tokens.  The slice of S stays in MFMA accumulators (fp32) for the
+// Two paths.  The chunk-parallel path (large chunks, every mask but token-causal) runs three
+// launches: the chunk's own update dS_c = sum over the chunk of eta_i v_i k_i^T for every
+// (scan, chunk) in parallel, an elementwise scan over chunks that writes the state each chunk's
+// queries see (before or after its own update, as the mask orders them), and the apply
+// o = S_c q for every chunk in parallel.  The sequential path below handles token-causal mode and
+// small chunks, where the chunk states would cost more traffic than they save.
+//
+// Sequential path: one workgroup owns one (batch, head) scan and a 32-row slice of S's d_v rows,
+// and walks the sequence in sub-blocks of TB tokens.  The slice of S stays in MFMA accumulators (fp32) for the
 // whole sequence; the update is an MFMA accumulation over the sub-block's tokens.  The apply reads
 // S from LDS, where it is kept as a bf16 hi + lo pair (fp32 in fp32 mode) refreshed at chunk ends,
 // so the query products see S to about 16 bits.  Token-causal mode adds the masked intra-block term
 // tril(Q K^T) (eta o V) and refreshes S after every sub-block.  The next sub-block's q, k, v and eta
 // are loaded into registers while the current one is computed.
 #include <algorithm>
+#include <type_traits>
 
 #include "host_common.hpp"
 #include "tile.hpp"
@@ -285,6 +293,8 @@ __global__ __launch_bounds__(kThreads) void k_linattn(LinArgs<T> a) {
     const T* V = a.v + (int64_t)scan * N * a.dv + v0;
     const float* eta = a.eta + (int64_t)scan * N;
     T* O = a.o + (int64_t)scan * N * a.dv + v0;
+    const float* S0 = a.S0;
+    float* Sout = a.Sout ? a.Sout + (int64_t)scan * a.dv * DK : nullptr;
 
     // state slice: wave (wv, wk) holds rows [16 wv, +16) x cols [wk DK/WSK, +DK/WSK)
     const int wv = wave / C::WSK, wk = wave % C::WSK;
@@ -294,7 +304,7 @@ __global__ __launch_bounds__(kThreads) void k_linattn(LinArgs<T> a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int vv = 16 * wv + 4 * (lane >> 4) + r, kk = wk * (DK / C::WSK) + j * 16 + (lane & 15);
-            sacc[0][j][r] = a.S0 ? a.S0[((int64_t)scan * a.dv + v0 + vv) * DK + kk] : 0.f;
+            sacc[0][j][r] = S0 ? S0[((int64_t)scan * a.dv + v0 + vv) * DK + kk] : 0.f;
         }
     auto refresh = [&]() {
 #pragma unroll
@@ -376,15 +386,138 @@ __global__ __launch_bounds__(kThreads) void k_linattn(LinArgs<T> a) {
         lds_barrier();
         cur = nxt;
     }
-    if (a.Sout) {
+    if (Sout) {
 #pragma unroll
         for (int j = 0; j < C::SFN; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int vv = 16 * wv + 4 * (lane >> 4) + r, kk = wk * (DK / C::WSK) + j * 16 + (lane & 15);
-                a.Sout[((int64_t)scan * a.dv + v0 + vv) * DK + kk] = sacc[0][j][r];
+                Sout[(int64_t)(v0 + vv) * DK + kk] = sacc[0][j][r];
             }
     }
+}
+
+// ---------------------------------------------------------------------------------------------
+// chunk-parallel path: scan over chunks and apply
+
+// dS_c = sum over chunk c's tokens of eta_i v_i k_i^T (d_v x d_k, fp32), contracting over tokens:
+// both operands are token-major, so both go through the transposing stager, which also applies
+// eta to v.  Chunks a strided mask does not update are skipped (and never read).
+template <typename T> struct DeltaArgs {
+    const T* k; const T* v; const float* eta; float* dS;
+    int64_t N; int dk, dv, chunk, nc, ntv, ntk, mode;
+    uint32_t flags[32];
+};
+
+constexpr int kDeltaRows = 128, kDeltaCols = 128;
+
+template <typename T>
+__global__ __launch_bounds__(kThreads, 2) void k_lin_delta(DeltaArgs<T> a) {
+    using TD = Tile<T, kDeltaRows, kDeltaCols, 1, 2, 1, 1, 1, true, true, true>;
+    __shared__ __attribute__((aligned(16))) char smem[TD::LDS];
+    const int lb = xcd_block(gridDim.x);
+    const int per = a.ntv * a.ntk;
+    const int unit = lb / per, t = lb % per;
+    const int scan = unit / a.nc, c = unit % a.nc;
+    if (a.mode == TTT_MASK_STRIDED && !((a.flags[c >> 5] >> (c & 31)) & 1u)) return;
+    const int r0 = (t / a.ntk) * kDeltaRows, c0 = (t % a.ntk) * kDeltaCols;
+    const int64_t tok = (int64_t)scan * a.N + (int64_t)c * a.chunk;
+    const int nl = (int)std::min<int64_t>(a.chunk, a.N - (int64_t)c * a.chunk);
+    Opnd<T> A[1] = {{a.v + tok * a.dv + r0, a.dv, a.dv - r0, nl}};
+    A[0].kscale = a.eta + tok;
+    const Opnd<T> B[1] = {{a.k + tok * a.dk + c0, a.dk, a.dk - c0, nl}};
+    TD tl;
+    tl.template run<PM1>(A, B, nl, smem);
+    float* dS = a.dS + (int64_t)unit * a.dv * a.dk;
+    tl.for_each([&](const float (&v)[1], int row, int col) {
+        if (r0 + row < a.dv && c0 + col < a.dk) dS[(int64_t)(r0 + row) * a.dk + c0 + col] = v[0];
+    });
+}
+
+// The state each chunk's queries see, from S0 and the chunk updates dS_c: before chunk c's own
+// update (apply-then-update, strided) or after it (update-then-apply, full).  One thread owns 4
+// consecutive elements of one scan's state and walks the chunks.  bf16 io keeps the state as a
+// hi + lo pair of bf16 planes (about 16 bits), fp32 io as one fp32 plane.
+template <typename T> struct ScanArgs {
+    const float* dS; const float* S0; T* Sc; float* Sout;
+    int64_t dvk;   // d_v * d_k
+    int nc, mode, nscan;
+    uint32_t flags[32];
+};
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_lin_scan(ScanArgs<T> a) {
+    constexpr int PLANES = sizeof(T) == 2 ? 2 : 1;
+    const int64_t per = a.dvk / 4;
+    const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (g >= per * a.nscan) return;
+    const int64_t scan = g / per, e = (g % per) * 4;
+    f32x4_t st = {0.f, 0.f, 0.f, 0.f};
+    if (a.S0)  // S0 and S_out are only 4-byte aligned
+#pragma unroll
+        for (int u = 0; u < 4; ++u) st[u] = a.S0[scan * a.dvk + e + u];
+    const bool post = a.mode == TTT_MASK_UPDATE_THEN_APPLY || a.mode == TTT_MASK_FULL;
+    auto put = [&](int c) {
+        T* dst = a.Sc + ((scan * a.nc + c) * PLANES) * a.dvk + e;
+        if constexpr (PLANES == 2) {
+            float lo[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) lo[u] = st[u] - bf2f(f2bf(st[u]));
+            Pack4<T>::store(dst, st[0], st[1], st[2], st[3]);
+            Pack4<T>::store(dst + a.dvk, lo[0], lo[1], lo[2], lo[3]);
+        } else {
+            Pack4<T>::store(dst, st[0], st[1], st[2], st[3]);
+        }
+    };
+    for (int c = 0; c < a.nc; ++c) {
+        const bool upd = a.mode != TTT_MASK_STRIDED || ((a.flags[c >> 5] >> (c & 31)) & 1u);
+        if (!post) put(c);
+        if (upd) st += *reinterpret_cast<const f32x4_t*>(a.dS + (scan * a.nc + c) * a.dvk + e);
+        if (post) put(c);
+    }
+    if (a.Sout)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) a.Sout[scan * a.dvk + e + u] = st[u];
+}
+
+// o (chunk c's tokens x d_v) = q_c S_c^T, contracting over d_k: bf16 as hi and lo products summed
+template <typename T> struct ApplyArgs {
+    const T* q; const T* Sc; T* o;
+    int64_t N; int dk, dv, chunk, nc, ntt, ntv, nscan;
+};
+
+constexpr int kApplyRows = 128, kApplyCols = 128;
+
+template <typename T>
+__global__ __launch_bounds__(kThreads, 2) void k_lin_apply(ApplyArgs<T> a) {
+    constexpr int PLANES = sizeof(T) == 2 ? 2 : 1;
+    using TA = Tile<T, kApplyRows, kApplyCols, 1, 2, 1, PLANES, PLANES, false, false>;
+    using PM = typename std::conditional<PLANES == 2, PMQ, PM1>::type;
+    __shared__ __attribute__((aligned(16))) char smem[TA::LDS];
+    const int lb = xcd_block(gridDim.x);
+    const int per_chunk = a.ntt * a.ntv;
+    const int unit = lb / per_chunk, t = lb % per_chunk;
+    const int scan = unit / a.nc, c = unit % a.nc;
+    const int r0 = (t / a.ntv) * kApplyRows, c0 = (t % a.ntv) * kApplyCols;
+    const int64_t tok = (int64_t)scan * a.N + (int64_t)c * a.chunk;
+    const int nl = (int)std::min<int64_t>(a.chunk, a.N - (int64_t)c * a.chunk);
+    if (r0 >= nl) return;  // a ragged last chunk has fewer token tiles (uniform per workgroup)
+    const int64_t dvk = (int64_t)a.dv * a.dk;
+    const T* S = a.Sc + (int64_t)unit * PLANES * dvk + (int64_t)c0 * a.dk;
+    const Opnd<T> A[1] = {{a.q + (tok + r0) * a.dk, a.dk, nl - r0, a.dk}};
+    Opnd<T> B[PLANES];
+#pragma unroll
+    for (int p = 0; p < PLANES; ++p) B[p] = Opnd<T>{S + p * dvk, a.dk, a.dv - c0, a.dk};
+    TA tl;
+    tl.template run<PM>(A, B, a.dk, smem);
+    T* O = a.o + (tok + r0) * a.dv + c0;
+    tl.for_each([&](const float (&v)[PLANES], int row, int col) {
+        if (r0 + row < nl && c0 + col < a.dv) {
+            float x = v[0];
+            if constexpr (PLANES == 2) x += v[1];
+            O[(int64_t)row * a.dv + col] = Elt<T>::st(x);
+        }
+    });
 }
 
 static ttt_status validate_lin(const linattn_desc* D) {
@@ -444,6 +577,87 @@ static ttt_status run_lin(const linattn_desc& D, LinArgs<T>& a, hipStream_t st) 
     return fail(TTT_ERR_UNSUPPORTED, "d_k=%d", D.d_k);
 }
 
+// The chunk-parallel path writes dS_c and S_c, 2 x 4 bytes per state element per chunk, on top of
+// the algorithmic q, k, v, o traffic of 2 (d_k + d_v) bytes (bf16) per token: that extra is
+// 4 d_k d_v / (chunk (d_k + d_v)) of it.  It is taken while that ratio is at most 2 (chunk >= 128
+// at d_k = d_v = 128), where it runs well ahead of the sequential kernel; token-causal mode always
+// takes the sequential kernel.
+static bool lin_parallel(const linattn_desc& D) {
+    if (D.mask == TTT_MASK_TOKEN_CAUSAL || D.N == 0) return false;
+    const int64_t chunk = std::min<int64_t>(D.chunk, D.N);
+    return 4LL * D.d_k * D.d_v <= 2LL * chunk * (D.d_k + D.d_v);
+}
+
+static size_t lin_ws_bytes(const linattn_desc& D) {
+    if (!lin_parallel(D)) return 0;
+    const int64_t S = (int64_t)D.B * D.H, nc = cdiv(D.N, D.chunk), dvk = (int64_t)D.d_v * D.d_k;
+    return align256((size_t)(S * nc * dvk * 4)) * 2;  // dS_c (fp32), then S_c (bf16 hi + lo, or fp32)
+}
+
+template <typename T>
+static ttt_status run_lin_parallel(const linattn_desc& D, LinArgs<T> a, char* ws, hipStream_t st) {
+    const int64_t S = (int64_t)D.B * D.H, nc = cdiv(D.N, D.chunk), dvk = (int64_t)D.d_v * D.d_k;
+    float* dS = (float*)ws;
+    T* Sc = (T*)(ws + align256((size_t)(S * nc * dvk * 4)));
+    float* Sout = a.Sout;
+    const float* S0 = a.S0;  // read by the scan
+    // 1. per-chunk updates
+    DeltaArgs<T> da{};
+    da.k = a.k;
+    da.v = a.v;
+    da.eta = a.eta;
+    da.dS = dS;
+    da.N = D.N;
+    da.dk = D.d_k;
+    da.dv = D.d_v;
+    da.chunk = D.chunk;
+    da.nc = (int)nc;
+    da.ntv = (int)cdiv(D.d_v, kDeltaRows);
+    da.ntk = (int)cdiv(D.d_k, kDeltaCols);
+    da.mode = D.mask;
+    for (int w = 0; w < 32; ++w) da.flags[w] = a.flags[w];
+    {
+        ProfScope ps(PK_LIN_DELTA, st);
+        hipLaunchKernelGGL(k_lin_delta<T>, dim3((unsigned)(S * nc * da.ntv * da.ntk)), dim3(kThreads), 0, st, da);
+    }
+    ttt_status rc = check_launch("k_lin_delta");
+    if (rc != TTT_OK) return rc;
+    // 2. states seen by each chunk, and S_out
+    ScanArgs<T> sa{};
+    sa.dS = dS;
+    sa.S0 = S0;
+    sa.Sc = Sc;
+    sa.Sout = Sout;
+    sa.dvk = dvk;
+    sa.nc = (int)nc;
+    sa.mode = D.mask;
+    sa.nscan = (int)S;
+    for (int w = 0; w < 32; ++w) sa.flags[w] = a.flags[w];
+    {
+        ProfScope ps(PK_LIN_SCAN, st);
+        hipLaunchKernelGGL(k_lin_scan<T>, dim3((unsigned)cdiv(S * dvk / 4, kThreads)), dim3(kThreads), 0, st, sa);
+    }
+    if ((rc = check_launch("k_lin_scan")) != TTT_OK) return rc;
+    // 3. apply
+    ApplyArgs<T> aa{};
+    aa.q = a.q;
+    aa.Sc = Sc;
+    aa.o = a.o;
+    aa.N = D.N;
+    aa.dk = D.d_k;
+    aa.dv = D.d_v;
+    aa.chunk = D.chunk;
+    aa.nc = (int)nc;
+    aa.ntt = (int)cdiv(std::min<int64_t>(D.chunk, D.N), kApplyRows);
+    aa.ntv = (int)cdiv(D.d_v, kApplyCols);
+    aa.nscan = (int)S;
+    {
+        ProfScope ps(PK_LIN_APPLY, st);
+        hipLaunchKernelGGL(k_lin_apply<T>, dim3((unsigned)(S * nc * aa.ntt * aa.ntv)), dim3(kThreads), 0, st, aa);
+    }
+    return check_launch("k_lin_apply");
+}
+
 }  // namespace ttt
 
 using namespace ttt;
@@ -453,15 +667,13 @@ extern "C" ttt_status linattn_workspace_bytes(const linattn_desc* desc, size_t* 
     ttt_status rc = validate_lin(desc);
     if (rc != TTT_OK) return rc;
     if (!bytes) return fail(TTT_ERR_INVALID_ARGUMENT, "bytes is NULL");
-    *bytes = 0;
+    *bytes = lin_ws_bytes(*desc);
     return TTT_OK;
 }
 
 extern "C" ttt_status linattn_forward(const linattn_desc* desc, const void* q, const void* k, const void* v,
                                       const float* eta, const float* S0, void* o, float* S_out, void* workspace,
                                       size_t workspace_bytes, void* stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     clear_error();
     ttt_status rc = validate_lin(desc);
     if (rc != TTT_OK) return rc;
@@ -482,23 +694,25 @@ extern "C" ttt_status linattn_forward(const linattn_desc* desc, const void* q, c
         return fail(TTT_ERR_INVALID_ARGUMENT, "o overlaps an input");
     const size_t sb = (size_t)S * D.d_v * D.d_k * 4;
     if (overlaps(S_out, sb, S0, sb)) return fail(TTT_ERR_INVALID_ARGUMENT, "S_out overlaps S0");
+    const size_t need = lin_ws_bytes(D);
+    if (need && (!workspace || workspace_bytes < need))
+        return fail(TTT_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+    if (need && !aligned(workspace, 256)) return fail(TTT_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
     hipStream_t st = (hipStream_t)stream;
     // 32-row slices of S: measured faster than 16-row slices, whose extra workgroups double the
     // re-reads of q and k (the 16-row instantiation is kept for the bf16 kernel)
     const int vt = 32;
     const int nvt = D.d_v / vt;
-    if (D.io_dtype == TTT_BF16) {
-        LinArgs<uint16_t> a{(const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, eta, S0, (uint16_t*)o, S_out,
-                            D.N, D.d_v, D.chunk, D.mask, nvt, vt, {}};
+    auto go = [&](auto* tag) -> ttt_status {
+        using T = typename std::remove_pointer<decltype(tag)>::type;
+        LinArgs<T> a{(const T*)q, (const T*)k, (const T*)v, eta, S0, (T*)o, S_out, D.N, D.d_v, D.chunk, D.mask,
+                     nvt, vt, {}};
         if (D.mask == TTT_MASK_STRIDED)
             for (int64_t j = 0; j < cdiv(D.N, D.chunk); ++j)
                 if (D.update_chunks[j]) a.flags[j >> 5] |= 1u << (j & 31);
-        return run_lin<uint16_t>(D, a, st);
-    }
-    LinArgs<float> a{(const float*)q, (const float*)k, (const float*)v, eta, S0, (float*)o, S_out, D.N, D.d_v,
-                     D.chunk, D.mask, nvt, vt, {}};
-    if (D.mask == TTT_MASK_STRIDED)
-        for (int64_t j = 0; j < cdiv(D.N, D.chunk); ++j)
-            if (D.update_chunks[j]) a.flags[j >> 5] |= 1u << (j & 31);
-    return run_lin<float>(D, a, st);
+        if (need) return run_lin_parallel<T>(D, a, (char*)workspace, st);
+        return run_lin<T>(D, a, st);
+    };
+    if (D.io_dtype == TTT_BF16) return go((uint16_t*)nullptr);
+    return go((float*)nullptr);
 }

@@ -123,6 +123,7 @@ template <typename T> struct Opnd {
     int kvalid;
     int ps = 30;
     int64_t pstride = 0;
+    const float* kscale = nullptr;  // per-k factors, used by a k-strided stager built with SCALE
     __device__ __forceinline__ int64_t inner(int i) const {
         return (int64_t)(i >> ps) * pstride + (i & ((1 << ps) - 1));
     }
@@ -130,10 +131,10 @@ template <typename T> struct Opnd {
 
 template <int SEG> struct Pitch { static constexpr int value = SEG * 64 + 16; };
 
-template <typename T, int R, int SEG, bool KS> struct Stager;
+template <typename T, int R, int SEG, bool KS, bool SCALE = false> struct Stager;
 
 // k-contiguous source: 16-byte vectors copied as they are
-template <typename T, int R, int SEG> struct Stager<T, R, SEG, false> {
+template <typename T, int R, int SEG> struct Stager<T, R, SEG, false, false> {
     static constexpr int VEC = Elt<T>::VEC;
     static constexpr int VPR = SEG * 4;  // vectors per row per stage
     static constexpr int NV = R * VPR;
@@ -200,7 +201,8 @@ template <typename T, int R, int SEG> struct Stager<T, R, SEG, false> {
 // are stored permuted: logical row rb*VEC + j lives in LDS row j*RB + rb, so that the lanes of one
 // store (consecutive rb) hit consecutive LDS rows and distinct banks.  Fragment reads stay on
 // consecutive LDS rows; the tile maps result rows back through row_of().
-template <typename T, int R, int SEG> struct Stager<T, R, SEG, true> {
+// SCALE: element (row, k) is multiplied by o.kscale[k] on its way into LDS (bf16: rounded once).
+template <typename T, int R, int SEG, bool SCALE> struct Stager<T, R, SEG, true, SCALE> {
     static constexpr int ES = (int)sizeof(T);
     static constexpr int VEC = Elt<T>::VEC;
     static constexpr int KSTEP = SEG * 64 / ES;   // k per stage
@@ -228,6 +230,7 @@ template <typename T, int R, int SEG> struct Stager<T, R, SEG, true> {
     }
 
     u32x4_t r[PER][KPT];
+    float sc[SCALE ? PER : 1][SCALE ? KPT : 1];
     uint32_t ok;  // bit i * KPT + e: r[i][e] is in range (see the k-contiguous stager)
     static_assert(PER * KPT <= 32, "too many vectors per thread");
     template <bool FULL>
@@ -243,11 +246,14 @@ template <typename T, int R, int SEG> struct Stager<T, R, SEG, true> {
             for (int e = 0; e < KPT; ++e) {
                 const int k = k0 + kc * KPT + e;
                 if constexpr (FULL) {
-                    if (NU % kThreads == 0 || u < NU)
+                    if (NU % kThreads == 0 || u < NU) {
                         r[i][e] = *reinterpret_cast<const u32x4_t*>(o.p + (int64_t)k * o.ld + o.inner(rb * VEC));
+                        if constexpr (SCALE) sc[i][e] = o.kscale[k];
+                    }
                 } else {
                     const bool in = live && k < o.kvalid;
                     r[i][e] = *reinterpret_cast<const u32x4_t*>(o.p + (in ? (int64_t)k * o.ld + o.inner(rb * VEC) : 0));
+                    if constexpr (SCALE) sc[i][e] = o.kscale[in ? k : 0];
                     ok |= (uint32_t)in << (i * KPT + e);
                 }
             }
@@ -255,7 +261,16 @@ template <typename T, int R, int SEG> struct Stager<T, R, SEG, true> {
     }
     template <bool FULL>
     __device__ __forceinline__ uint32_t elt(int i, int e, int w) const {
-        return (FULL || ((ok >> (i * KPT + e)) & 1u)) ? r[i][e][w] : 0u;
+        uint32_t x = r[i][e][w];
+        if constexpr (SCALE) {
+            const float f = sc[i][e];
+            if constexpr (ES == 2) {
+                x = (uint32_t)f2bf(bf2f((uint16_t)(x & 0xFFFFu)) * f) | ((uint32_t)f2bf(bf2f((uint16_t)(x >> 16)) * f) << 16);
+            } else {
+                x = __float_as_uint(__uint_as_float(x) * f);
+            }
+        }
+        return (FULL || ((ok >> (i * KPT + e)) & 1u)) ? x : 0u;
     }
     template <bool FULL>
     __device__ __forceinline__ uint32_t word(int i, int j, int w) const {
@@ -296,15 +311,17 @@ template <typename T, int R, int SEG, bool KS> struct RowMap {
     __device__ static int row_of(int r) { return r; }
 };
 template <typename T, int R, int SEG> struct RowMap<T, R, SEG, true> {
-    __device__ static int row_of(int r) { return Stager<T, R, SEG, true>::row_of(r); }
+    __device__ static int row_of(int r) { return Stager<T, R, SEG, true, false>::row_of(r); }
 };
 
 // Tile engine.  NA A-operands of BM rows and NB B-operands of BN rows are staged per k-step
-// (k-strided sources when KSA / KSB); accumulator p is A[PM::a[p]] x B[PM::b[p]].  Waves form a
+// (k-strided sources when KSA / KSB; SCALE_A multiplies the A operands' k-slices by per-k
+// factors); accumulator p is A[PM::a[p]] x B[PM::b[p]].  Waves form a
 // WGM x (4/WGM) grid over the tile and each wave owns (WM/32) x (WN/32) blocks of 32 x 32 per
 // accumulator.  Global loads run one stage ahead of the LDS stores (one register set), LDS is
 // double-buffered, one barrier per stage.
-template <typename T, int BM_, int BN_, int SEG, int WGM, int NA, int NB, int NP, bool KSA, bool KSB>
+template <typename T, int BM_, int BN_, int SEG, int WGM, int NA, int NB, int NP, bool KSA, bool KSB,
+          bool SCALE_A = false>
 struct Tile {
     static constexpr int BM = BM_, BN = BN_;
     static constexpr int WGN = 4 / WGM;
@@ -316,7 +333,8 @@ struct Tile {
     static constexpr int LDS = 2 * STAGE;
     static constexpr int KSTEP = SEG * 64 / (int)sizeof(T);  // k elements per stage
     static_assert(WGM * WGN == 4 && FM >= 1 && FN >= 1 && WM % 32 == 0 && WN % 32 == 0, "bad wave grid");
-    using SA = Stager<T, BM, SEG, KSA>;
+    static_assert(!SCALE_A || KSA, "per-k scaling is done by the k-strided stager");
+    using SA = Stager<T, BM, SEG, KSA, SCALE_A>;
     using SB = Stager<T, BN, SEG, KSB>;
 
     f32x16_t acc[NP][FM][FN];

@@ -147,6 +147,26 @@ def test_linattn_forward_rejects():
     assert L.linattn_workspace_bytes(ctypes.byref(D), ctypes.byref(n)) == C.TTT_OK and n.value == 0
 
 
+def test_linattn_workspace_choice_and_rejects():
+    """Large chunks take the chunk-parallel path, which needs 8 bytes per state element per chunk and
+    scan; token-causal mode and small chunks need none.  A short or misaligned workspace is refused
+    before anything is enqueued."""
+    L = C.lib()
+    n = ctypes.c_size_t(1)
+    D = lin_desc(B=2, H=3, N=1000, d_k=128, d_v=64, chunk=256)   # 4 chunks, 4*128*64 <= 2*256*192
+    assert L.linattn_workspace_bytes(ctypes.byref(D), ctypes.byref(n)) == C.TTT_OK
+    per = 2 * 3 * 4 * 128 * 64 * 4
+    assert n.value == 2 * ((per + 255) // 256 * 256)
+    need = n.value
+    for kw in (dict(mask=C.MASK_TOKEN_CAUSAL), dict(chunk=32)):
+        assert L.linattn_workspace_bytes(ctypes.byref(lin_desc(B=2, H=3, N=1000, d_k=128, d_v=64, **kw)),
+                                         ctypes.byref(n)) == C.TTT_OK and n.value == 0
+    args = (P16, P16 + (1 << 30), P16 + (2 << 30), P16 + (3 << 30), None, P16B, None)
+    assert L.linattn_forward(ctypes.byref(D), *args, None, 0, None) == C.TTT_ERR_WORKSPACE
+    assert L.linattn_forward(ctypes.byref(D), *args, P16 + (1 << 34), need - 1, None) == C.TTT_ERR_WORKSPACE
+    assert L.linattn_forward(ctypes.byref(D), *args, P16 + (1 << 34) + 16, need, None) == C.TTT_ERR_INVALID_ARGUMENT
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(C, "_lib", None)
     monkeypatch.setattr(C, "LIB_PATH", str(tmp_path / "missing.so"))
