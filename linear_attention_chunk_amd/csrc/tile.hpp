@@ -131,14 +131,14 @@ template <typename T> struct Opnd {
 
 template <int SEG> struct Pitch { static constexpr int value = SEG * 64 + 16; };
 
-template <typename T, int R, int SEG, bool KS, bool SCALE = false> struct Stager;
+template <typename T, int R, int SEG, bool KS, bool SCALE = false, int NT = kThreads> struct Stager;
 
 // k-contiguous source: 16-byte vectors copied as they are
-template <typename T, int R, int SEG> struct Stager<T, R, SEG, false, false> {
+template <typename T, int R, int SEG, int NT> struct Stager<T, R, SEG, false, false, NT> {
     static constexpr int VEC = Elt<T>::VEC;
     static constexpr int VPR = SEG * 4;  // vectors per row per stage
     static constexpr int NV = R * VPR;
-    static constexpr int PER = (NV + kThreads - 1) / kThreads;
+    static constexpr int PER = (NV + NT - 1) / NT;
     static constexpr int PITCH = Pitch<SEG>::value;
     // Vector v goes to (row, c).  With one 64-byte segment per row (SEG == 1) four lanes fill a
     // row; the second four lanes of each group of eight take the row 4 further on (80-byte pitch:
@@ -166,15 +166,15 @@ template <typename T, int R, int SEG> struct Stager<T, R, SEG, false, false> {
         ok = 0;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int v = threadIdx.x + i * kThreads;
+            const int v = threadIdx.x + i * NT;
             int row, c;
             place(v, row, c);
             const int k = k0 + c * VEC;
             if constexpr (FULL) {
-                if (NV % kThreads == 0 || v < NV)
+                if (NV % NT == 0 || v < NV)
                     r[i] = *reinterpret_cast<const u32x4_t*>(o.p + (int64_t)row * o.ld + o.inner(k));
             } else {
-                const bool in = (NV % kThreads == 0 || v < NV) && row < o.rows && k < o.kvalid;
+                const bool in = (NV % NT == 0 || v < NV) && row < o.rows && k < o.kvalid;
                 r[i] = *reinterpret_cast<const u32x4_t*>(o.p + (in ? (int64_t)row * o.ld + o.inner(k) : 0));
                 ok |= (uint32_t)in << i;
             }
@@ -184,8 +184,8 @@ template <typename T, int R, int SEG> struct Stager<T, R, SEG, false, false> {
     __device__ __forceinline__ void store(char* lds) const {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int v = threadIdx.x + i * kThreads;
-            if (NV % kThreads == 0 || v < NV) {
+            const int v = threadIdx.x + i * NT;
+            if (NV % NT == 0 || v < NV) {
                 int row, c;
                 place(v, row, c);
                 *reinterpret_cast<u32x4_t*>(lds + row * PITCH + c * 16) =
@@ -202,17 +202,17 @@ template <typename T, int R, int SEG> struct Stager<T, R, SEG, false, false> {
 // store (consecutive rb) hit consecutive LDS rows and distinct banks.  Fragment reads stay on
 // consecutive LDS rows; the tile maps result rows back through row_of().
 // SCALE: element (row, k) is multiplied by o.kscale[k] on its way into LDS (bf16: rounded once).
-template <typename T, int R, int SEG, bool SCALE> struct Stager<T, R, SEG, true, SCALE> {
+template <typename T, int R, int SEG, bool SCALE, int NT> struct Stager<T, R, SEG, true, SCALE, NT> {
     static constexpr int ES = (int)sizeof(T);
     static constexpr int VEC = Elt<T>::VEC;
     static constexpr int KSTEP = SEG * 64 / ES;   // k per stage
     static constexpr int RB = R / VEC;            // row blocks
     static constexpr int KMIN = ES == 2 ? 2 : 1;  // at least one 32-bit word per store
-    static constexpr int KWANT = KSTEP * RB / kThreads;
+    static constexpr int KWANT = KSTEP * RB / NT;
     static constexpr int KPT = KWANT <= KMIN ? KMIN : (KWANT >= VEC ? VEC : (KWANT >= 4 ? 4 : 2));
     static constexpr int KC = KSTEP / KPT;
     static constexpr int NU = KC * RB;
-    static constexpr int PER = (NU + kThreads - 1) / kThreads;
+    static constexpr int PER = (NU + NT - 1) / NT;
     static constexpr int PITCH = Pitch<SEG>::value;
     static constexpr int WORDS = KPT * ES / 4;   // 32-bit words per row piece
     // lanes of one LDS store cycle (128 bytes): 8 consecutive row blocks x KG k-chunks, which puts
@@ -238,15 +238,15 @@ template <typename T, int R, int SEG, bool SCALE> struct Stager<T, R, SEG, true,
         ok = 0;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int u = threadIdx.x + i * kThreads;
+            const int u = threadIdx.x + i * NT;
             int rb, kc;
             place(u, rb, kc);
-            const bool live = (NU % kThreads == 0 || u < NU) && (FULL || rb * VEC < o.rows);
+            const bool live = (NU % NT == 0 || u < NU) && (FULL || rb * VEC < o.rows);
 #pragma unroll
             for (int e = 0; e < KPT; ++e) {
                 const int k = k0 + kc * KPT + e;
                 if constexpr (FULL) {
-                    if (NU % kThreads == 0 || u < NU) {
+                    if (NU % NT == 0 || u < NU) {
                         r[i][e] = *reinterpret_cast<const u32x4_t*>(o.p + (int64_t)k * o.ld + o.inner(rb * VEC));
                         if constexpr (SCALE) sc[i][e] = o.kscale[k];
                     }
@@ -285,8 +285,8 @@ template <typename T, int R, int SEG, bool SCALE> struct Stager<T, R, SEG, true,
     __device__ __forceinline__ void store(char* lds) const {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int u = threadIdx.x + i * kThreads;
-            if (NU % kThreads == 0 || u < NU) {
+            const int u = threadIdx.x + i * NT;
+            if (NU % NT == 0 || u < NU) {
                 int rb, kc;
                 place(u, rb, kc);
 #pragma unroll
@@ -311,20 +311,22 @@ template <typename T, int R, int SEG, bool KS> struct RowMap {
     __device__ static int row_of(int r) { return r; }
 };
 template <typename T, int R, int SEG> struct RowMap<T, R, SEG, true> {
-    __device__ static int row_of(int r) { return Stager<T, R, SEG, true, false>::row_of(r); }
+    __device__ static int row_of(int r) { return Stager<T, R, SEG, true>::row_of(r); }
 };
 
-// Tile engine.  NA A-operands of BM rows and NB B-operands of BN rows are staged per k-step
+// Tile engine (NW waves, 4 by default).  NA A-operands of BM rows and NB B-operands of BN rows
+// are staged per k-step
 // (k-strided sources when KSA / KSB; SCALE_A multiplies the A operands' k-slices by per-k
 // factors); accumulator p is A[PM::a[p]] x B[PM::b[p]].  Waves form a
-// WGM x (4/WGM) grid over the tile and each wave owns (WM/32) x (WN/32) blocks of 32 x 32 per
+// WGM x (NW/WGM) grid over the tile and each wave owns (WM/32) x (WN/32) blocks of 32 x 32 per
 // accumulator.  Global loads run one stage ahead of the LDS stores (one register set), LDS is
 // double-buffered, one barrier per stage.
 template <typename T, int BM_, int BN_, int SEG, int WGM, int NA, int NB, int NP, bool KSA, bool KSB,
-          bool SCALE_A = false>
+          bool SCALE_A = false, int NW = 4>
 struct Tile {
     static constexpr int BM = BM_, BN = BN_;
-    static constexpr int WGN = 4 / WGM;
+    static constexpr int NT = 64 * NW;  // threads of the workgroup
+    static constexpr int WGN = NW / WGM;
     static constexpr int WM = BM / WGM, WN = BN / WGN;
     static constexpr int FM = WM / 32, FN = WN / 32;
     static constexpr int PITCH = Pitch<SEG>::value;
@@ -332,10 +334,10 @@ struct Tile {
     static constexpr int STAGE = NA * A_BYTES + NB * B_BYTES;
     static constexpr int LDS = 2 * STAGE;
     static constexpr int KSTEP = SEG * 64 / (int)sizeof(T);  // k elements per stage
-    static_assert(WGM * WGN == 4 && FM >= 1 && FN >= 1 && WM % 32 == 0 && WN % 32 == 0, "bad wave grid");
+    static_assert(WGM * WGN == NW && FM >= 1 && FN >= 1 && WM % 32 == 0 && WN % 32 == 0, "bad wave grid");
     static_assert(!SCALE_A || KSA, "per-k scaling is done by the k-strided stager");
-    using SA = Stager<T, BM, SEG, KSA, SCALE_A>;
-    using SB = Stager<T, BN, SEG, KSB>;
+    using SA = Stager<T, BM, SEG, KSA, SCALE_A, NT>;
+    using SB = Stager<T, BN, SEG, KSB, false, NT>;
 
     f32x16_t acc[NP][FM][FN];
 

@@ -21,9 +21,10 @@
 
 namespace ttt {
 
+constexpr int kUpWaves = 8;     // up-kernel workgroups: 8 waves, one workgroup per CU
 constexpr int kUpQRows = 256;   // token rows per query tile
-constexpr int kUpKRows = 128;   // token rows per key tile
-constexpr int kUpCols = 64;     // hidden units per up-kernel tile
+constexpr int kUpKRows = 192;   // token rows per key tile
+constexpr int kUpCols = 128;    // hidden units per up-kernel tile
 constexpr int kORows = 256;     // token rows per output tile
 constexpr int kPanelShift = 6;  // intermediates are stored in panels of 64 hidden units
 constexpr int kPanel = 1 << kPanelShift;
@@ -54,15 +55,17 @@ template <typename T> __device__ __forceinline__ int64_t panel_off(const StepArg
 }
 
 // ---------------------------------------------------------------------------------------------
-// up: SwiGLU forward of the queries, forward + backward of the keys.  Two workgroups per CU, so
-// that one's epilogue (the SwiGLU forward/backward arithmetic and the stores) overlaps the other's
-// MFMA main loop.  Key tiles are computed transposed (hidden units x tokens): each lane then holds
-// consecutive tokens of one hidden unit, so the hidden-major HkE, DA, DC leave as contiguous runs,
-// and eta is one value per lane column.
+// up: SwiGLU forward of the queries, forward + backward of the keys.  Workgroups of 8 waves (two
+// per SIMD, one workgroup per CU): each wave keeps the accumulator blocking of a 4-wave tile while
+// the workgroup tile doubles, which halves the operand bytes loaded per MFMA.  Key tiles are
+// computed transposed (hidden units x tokens): each lane then holds consecutive tokens of one
+// hidden unit, so the hidden-major HkE, DA, DC leave as contiguous runs, and eta is one value per
+// lane column.
 template <typename T>
-__global__ __launch_bounds__(kThreads, 2) void k_up(StepArgs<T> a) {
-    using TQ = Tile<T, kUpQRows, kUpCols, 1, 2, 1, 2, 2, false, false>;  // wave: 128 tokens x 32 hidden x {A, C}
-    using TK = Tile<T, kUpCols, kUpKRows, 1, 2, 3, 2, 3, false, false>;  // wave: 32 hidden x 64 tokens x {A, C, DH}
+__global__ __launch_bounds__(64 * kUpWaves, 1) void k_up(StepArgs<T> a) {
+    // query wave: 64 tokens x 64 hidden x {A, C}; key wave: 32 hidden x 96 tokens x {A, C, DH}
+    using TQ = Tile<T, kUpQRows, kUpCols, 2, 4, 1, 2, 2, false, false, false, kUpWaves>;
+    using TK = Tile<T, kUpCols, kUpKRows, 1, 4, 3, 2, 3, false, false, false, kUpWaves>;
     constexpr int LDSB = TQ::LDS > TK::LDS ? TQ::LDS : TK::LDS;
     __shared__ __attribute__((aligned(16))) char smem[LDSB];
 
@@ -85,13 +88,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_up(StepArgs<T> a) {
                               {W3s + (int64_t)c0 * a.d, a.d, a.m - c0, a.d}};
         TQ tl;
         tl.template run<PMQ>(A, B, a.d, smem);
-        // the tile's 64 hidden units are one panel: element (row, col) is row * 64 + col from its corner
-        static_assert(kUpCols == kPanel, "a query tile must cover exactly one panel");
+        // the tile's hidden units span whole panels: element (row, col) is (col / 64) * pan +
+        // row * 64 + col % 64 from the tile corner
+        static_assert(kUpCols % kPanel == 0, "a query tile must cover whole panels");
         T* Hq = a.Hq + ioff + panel_off(a, r0, c0);
         auto epi = [&](auto check) {
             tl.for_each([&](const float (&v)[2], int row, int col) {
                 if (!decltype(check)::value || (r0 + row < a.la && c0 + col < a.m))
-                    Hq[(uint32_t)row * kPanel + (uint32_t)col] = Elt<T>::st(v[0] * sigmoidf_(v[0]) * v[1]);
+                    Hq[(col >> kPanelShift) * a.pan + (uint32_t)row * kPanel + (uint32_t)(col & (kPanel - 1))] =
+                        Elt<T>::st(v[0] * sigmoidf_(v[0]) * v[1]);
             });
         };
         if (r0 + kUpQRows <= a.la && c0 + kUpCols <= a.m) epi(std::false_type{});
@@ -628,7 +633,7 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
         if (a.nQ + a.nK) {
             {
                 ProfScope ps(PK_UP, st);
-                hipLaunchKernelGGL(k_up<T>, dim3(S * (a.nQ + a.nK)), dim3(kThreads), 0, st, a);
+                hipLaunchKernelGGL(k_up<T>, dim3(S * (a.nQ + a.nK)), dim3(64 * kUpWaves), 0, st, a);
             }
             if ((rc = check_launch("k_up")) != TTT_OK) return rc;
         }
