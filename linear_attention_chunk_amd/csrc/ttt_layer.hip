@@ -153,10 +153,29 @@ __global__ __launch_bounds__(kThreads, 2) void k_down(StepArgs<T> a) {
     constexpr int LDSB = L1 > TO::LDS ? L1 : TO::LDS;
     __shared__ __attribute__((aligned(16))) char smem[LDSB];
 
+    // Each XCD (blocks b with the same b % 8) takes a contiguous group of scans, so tiles that share
+    // operands share an L2; within its group it runs the longest tiles first (the G1/G3 tiles of all
+    // its scans, then G2, then the outputs), so that short output tiles fill the end of the launch.
     const int per = a.nG13 + a.nG2 + a.nO;
-    const int lb = xcd_block(gridDim.x);
-    const int s = lb / per;
-    int t = lb % per;
+    const int S = gridDim.x / per;
+    int s, t;
+    if (S % 8 == 0) {
+        const int sp = S / 8, x = blockIdx.x % 8;
+        int i = blockIdx.x / 8;
+        if (i < sp * a.nG13) {
+            s = i / a.nG13; t = i % a.nG13;
+        } else if ((i -= sp * a.nG13) < sp * a.nG2) {
+            s = i / a.nG2; t = a.nG13 + i % a.nG2;
+        } else {
+            i -= sp * a.nG2;
+            s = i / a.nO; t = a.nG13 + a.nG2 + i % a.nO;
+        }
+        s += x * sp;
+    } else {
+        const int lb = xcd_block(gridDim.x);
+        s = lb / per;
+        t = lb % per;
+    }
     const int64_t dm = (int64_t)a.d * a.m;
     const int ndt = (a.d + 127) / 128, nmt2 = (a.m + 255) / 256;
     const int64_t ioff = s * a.inter_stride;
