@@ -79,6 +79,19 @@ def test_full_mask_and_strided(bf16):
     run_small(5, 1, 2, 256, 64, 64, 64, O.MASK_STRIDED, O.UPD_MUON_L2, bf16, flags=[1, 0, 1, 0])
 
 
+@pytest.mark.parametrize("bf16", [False, True])
+def test_multi_tile_ragged(bf16):
+    # two full chunks of 512 and a tail of 276: several full up/down tiles in every direction
+    # (d = 128, m = 384) next to partial ones, for both apply orders
+    run_small(9, 1, 2, 1300, 128, 384, 512, O.MASK_APPLY_THEN_UPDATE, O.UPD_GD_L2, bf16)
+    run_small(10, 1, 1, 1300, 128, 384, 512, O.MASK_UPDATE_THEN_APPLY, O.UPD_GD, bf16)
+
+
+def test_wide_layer_bf16():
+    # d = 512, m = 1024: more hidden tiles per scan than the LaCT LM shape
+    run_small(11, 1, 1, 600, 512, 1024, 256, O.MASK_APPLY_THEN_UPDATE, O.UPD_GD_L2, True)
+
+
 def test_tall_and_wide_muon_fp32():
     # d > m exercises the other Gram side for W1/W3 and W2
     run_small(6, 1, 1, 128, 96, 32, 64, O.MASK_APPLY_THEN_UPDATE, O.UPD_MUON_L2, False, ns=3)
