@@ -322,7 +322,7 @@ template <typename T, int R, int SEG> struct RowMap<T, R, SEG, true> {
 // accumulator.  Global loads run one stage ahead of the LDS stores (one register set), LDS is
 // double-buffered, one barrier per stage.
 template <typename T, int BM_, int BN_, int SEG, int WGM, int NA, int NB, int NP, bool KSA, bool KSB,
-          bool SCALE_A = false, int NW = 4>
+          bool SCALE_A = false, int NW = 4, int NBUF = 2>
 struct Tile {
     static constexpr int BM = BM_, BN = BN_;
     static constexpr int NT = 64 * NW;  // threads of the workgroup
@@ -332,7 +332,7 @@ struct Tile {
     static constexpr int PITCH = Pitch<SEG>::value;
     static constexpr int A_BYTES = BM * PITCH, B_BYTES = BN * PITCH;
     static constexpr int STAGE = NA * A_BYTES + NB * B_BYTES;
-    static constexpr int LDS = 2 * STAGE;
+    static constexpr int LDS = NBUF * STAGE;  // NBUF = 1: one LDS stage (two barriers per stage)
     static constexpr int KSTEP = SEG * 64 / (int)sizeof(T);  // k elements per stage
     static_assert(WGM * WGN == NW && FM >= 1 && FN >= 1 && WM % 32 == 0 && WN % 32 == 0, "bad wave grid");
     static_assert(!SCALE_A || KSA, "per-k scaling is done by the k-strided stager");
@@ -394,6 +394,24 @@ struct Tile {
         const int nk = (K + KSTEP - 1) / KSTEP;
         if (nk <= 0) return;
         Regs g;
+        if constexpr (NBUF == 1) {
+            // one LDS stage: the loads of stage s + 1 are in flight while stage s is computed; the
+            // stage is stored once every wave has finished reading the previous one
+            issue<FULL>(g, A, B, 0);
+            put<FULL>(g, lds);
+            if (nk > 1) issue<FULL>(g, A, B, KSTEP);
+            lds_barrier();
+            for (int s = 0; s < nk; ++s) {
+                compute<PM>(lds);
+                if (s + 1 < nk) {
+                    lds_barrier();
+                    put<FULL>(g, lds);
+                    if (s + 2 < nk) issue<FULL>(g, A, B, (s + 2) * KSTEP);
+                    lds_barrier();
+                }
+            }
+            return;
+        }
         issue<FULL>(g, A, B, 0);
         put<FULL>(g, lds);
         if (nk > 1) issue<FULL>(g, A, B, KSTEP);

@@ -65,7 +65,7 @@ template <typename T>
 __global__ __launch_bounds__(64 * kUpWaves, 1) void k_up(StepArgs<T> a) {
     // query wave: 64 tokens x 64 hidden x {A, C}; key wave: 32 hidden x 96 tokens x {A, C, DH}
     using TQ = Tile<T, kUpQRows, kUpCols, 2, 4, 1, 2, 2, false, false, false, kUpWaves>;
-    using TK = Tile<T, kUpCols, kUpKRows, 1, 4, 3, 2, 3, false, false, false, kUpWaves>;
+    using TK = Tile<T, kUpCols, kUpKRows, 2, 4, 3, 2, 3, false, false, false, kUpWaves, 1>;
     constexpr int LDSB = TQ::LDS > TK::LDS ? TQ::LDS : TK::LDS;
     __shared__ __attribute__((aligned(16))) char smem[LDSB];
 
@@ -146,9 +146,10 @@ __global__ __launch_bounds__(64 * kUpWaves, 1) void k_up(StepArgs<T> a) {
 // down: chunk gradients (contractions over tokens) and the apply chunk's outputs
 template <typename T>
 __global__ __launch_bounds__(kThreads, 2) void k_down(StepArgs<T> a) {
-    using TG13 = Tile<T, 128, 128, 1, 2, 2, 1, 2, false, true>;  // G1 and G3 share the K operand
-    using TG2 = Tile<T, 128, 256, 1, 2, 1, 1, 1, true, false>;
-    using TO = Tile<T, kORows, 128, 1, 2, 1, 1, 1, false, false>;
+    // 64-wide k-steps (whole 128-byte lines per row) in a single LDS stage, two workgroups per CU
+    using TG13 = Tile<T, 128, 128, 2, 2, 2, 1, 2, false, true, false, 4, 1>;  // G1 and G3 share the K operand
+    using TG2 = Tile<T, 128, 256, 2, 2, 1, 1, 1, true, false, false, 4, 1>;
+    using TO = Tile<T, kORows, 128, 2, 2, 1, 1, 1, false, false, false, 4, 1>;
     constexpr int L1 = TG13::LDS > TG2::LDS ? TG13::LDS : TG2::LDS;
     constexpr int LDSB = L1 > TO::LDS ? L1 : TO::LDS;
     __shared__ __attribute__((aligned(16))) char smem[LDSB];
