@@ -413,7 +413,7 @@ constexpr int kDeltaRows = 128, kDeltaCols = 128;
 
 template <typename T>
 __global__ __launch_bounds__(kThreads, 2) void k_lin_delta(DeltaArgs<T> a) {
-    using TD = Tile<T, kDeltaRows, kDeltaCols, 1, 2, 1, 1, 1, true, true, true>;
+    using TD = Tile<T, kDeltaRows, kDeltaCols, 2, 2, 1, 1, 1, true, true, true>;
     __shared__ __attribute__((aligned(16))) char smem[TD::LDS];
     const int lb = xcd_block(gridDim.x);
     const int per = a.ntv * a.ntk;

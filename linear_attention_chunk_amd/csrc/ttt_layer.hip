@@ -427,9 +427,9 @@ __global__ __launch_bounds__(kThreads) void k_ns_init(NSArgs<T> a) {
     }
 }
 
-template <typename T, bool KS> using NSTile = Tile<T, 128, 128, 1, 2, 1, 1, 1, KS, KS>;
-template <typename T> using NSStepTall = Tile<T, 128, 64, 1, 2, 1, 1, 1, false, false>;
-template <typename T> using NSStepWide = Tile<T, 128, 64, 1, 2, 1, 1, 1, false, true>;
+template <typename T, bool KS> using NSTile = Tile<T, 128, 128, 2, 2, 1, 1, 1, KS, KS>;
+template <typename T> using NSStepTall = Tile<T, 128, 64, 2, 2, 1, 1, 1, false, false>;
+template <typename T> using NSStepWide = Tile<T, 128, 64, 2, 2, 1, 1, 1, false, true>;
 constexpr int kNSStepRows = 128, kNSStepCols = 64;
 
 template <typename T>
