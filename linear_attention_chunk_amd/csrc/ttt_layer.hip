@@ -188,14 +188,20 @@ __global__ __launch_bounds__(kThreads, 2) void k_down(StepArgs<T> a) {
         const Opnd<T> B[1] = {{K + c0, a.d, a.d - c0, a.lu}};
         TG13 tl;
         tl.template run<PMG>(A, B, a.lu, smem);
-        float* G = a.G + s * a.g_stride;
-        tl.for_each([&](const float (&v)[2], int row, int col) {
-            const int gr = r0 + row, gc = c0 + col;
-            if (gr < a.m && gc < a.d) {
-                G[(int64_t)gr * a.d + gc] = v[0];
-                G[dm + (int64_t)gr * a.d + gc] = v[1];
-            }
-        });
+        // stores go through 32-bit offsets from the tile corner; full tiles skip the bounds checks
+        float* G1 = a.G + s * a.g_stride + (int64_t)r0 * a.d + c0;
+        float* G3 = G1 + dm;
+        auto epi = [&](auto check) {
+            tl.for_each([&](const float (&v)[2], int row, int col) {
+                if (!decltype(check)::value || (r0 + row < a.m && c0 + col < a.d)) {
+                    const uint32_t off = (uint32_t)row * (uint32_t)a.d + (uint32_t)col;
+                    G1[off] = v[0];
+                    G3[off] = v[1];
+                }
+            });
+        };
+        if (r0 + TG13::BM <= a.m && c0 + TG13::BN <= a.d) epi(std::false_type{});
+        else epi(std::true_type{});
         return;
     }
     t -= a.nG13;
@@ -206,11 +212,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_down(StepArgs<T> a) {
         const Opnd<T> B[1] = {{a.HkE + ioff + (int64_t)c0 * a.tp, a.tp, a.m - c0, a.lu}};
         TG2 tl;
         tl.template run<PM1>(A, B, a.lu, smem);
-        float* G = a.G + s * a.g_stride + 2 * dm;
-        tl.for_each([&](const float (&v)[1], int row, int col) {
-            const int gr = r0 + row, gc = c0 + col;
-            if (gr < a.d && gc < a.m) G[(int64_t)gr * a.m + gc] = v[0];
-        });
+        float* G2 = a.G + s * a.g_stride + 2 * dm + (int64_t)r0 * a.m + c0;
+        auto epi = [&](auto check) {
+            tl.for_each([&](const float (&v)[1], int row, int col) {
+                if (!decltype(check)::value || (r0 + row < a.d && c0 + col < a.m))
+                    G2[(uint32_t)row * (uint32_t)a.m + (uint32_t)col] = v[0];
+            });
+        };
+        if (r0 + TG2::BM <= a.d && c0 + TG2::BN <= a.m) epi(std::false_type{});
+        else epi(std::true_type{});
         return;
     }
     t -= a.nG2;
@@ -221,11 +231,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_down(StepArgs<T> a) {
         const Opnd<T> B[1] = {{W2s + (int64_t)c0 * a.m, a.m, a.d - c0, a.m}};
         TO tl;
         tl.template run<PM1>(A, B, a.m, smem);
-        T* O = a.o + ((int64_t)s * a.N + a.a0) * a.d;
-        tl.for_each([&](const float (&v)[1], int row, int col) {
-            const int tr = r0 + row, tc = c0 + col;
-            if (tr < a.la && tc < a.d) O[(int64_t)tr * a.d + tc] = Elt<T>::st(v[0]);
-        });
+        T* O = a.o + ((int64_t)s * a.N + a.a0 + r0) * a.d + c0;
+        auto epi = [&](auto check) {
+            tl.for_each([&](const float (&v)[1], int row, int col) {
+                if (!decltype(check)::value || (r0 + row < a.la && c0 + col < a.d))
+                    O[(uint32_t)row * (uint32_t)a.d + (uint32_t)col] = Elt<T>::st(v[0]);
+            });
+        };
+        if (r0 + TO::BM <= a.la && c0 + TO::BN <= a.d) epi(std::false_type{});
+        else epi(std::true_type{});
     }
 }
 
