@@ -339,8 +339,11 @@ def main():
         o2 = torch.empty_like(q2)
         lin_bytes = B2 * H2 * N2 * (4 * d2 * 2 + 4)
         for name, mask in (("linattn_chunked", C.MASK_APPLY_THEN_UPDATE), ("linattn_token_causal", C.MASK_TOKEN_CAUSAL)):
-            msl = time_calls(torch, lambda: T.linattn_forward(q2, k2, v2, e2, c2, mask, out=o2, want_S=False),
-                             max(st, 10), 2)
+            Dl, _ = T.linattn_desc(B2, H2, N2, d2, d2, c2, C.TTT_BF16, mask)
+            wsl = torch.empty(max(1, T.linattn_workspace_bytes(Dl)), dtype=torch.uint8, device="cuda")
+            msl = time_calls(torch, lambda: T.linattn_forward(q2, k2, v2, e2, c2, mask, out=o2, want_S=False,
+                                                              workspace=wsl), max(st, 10), 2)
+            del wsl
             extras[name] = {"tokens_per_s": round(B2 * N2 / (msl * 1e-3)), "ms_per_call": round(msl, 4),
                             "hbm_GBps": round(lin_bytes / (msl * 1e-3) / 1e9, 1),
                             "hbm_frac": round(lin_bytes / (msl * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -354,6 +357,23 @@ def main():
                                                       m_h=m2, out=o2, workspace=wss), st, 1)
         extras["swiglu_at_linattn_shape"] = {"tokens_per_s": round(B2 * N2 / (mss * 1e-3)), "ms_per_call": round(mss, 3),
                                              "m_h": m2, "linattn_speedup": round(mss / extras["linattn_chunked"]["ms_per_call"], 2)}
+        del q2, k2, v2, e2, o2, W02, wss
+        # and the reverse: linear attention at the LaCT LM layer's shape (d_k = d_v = d_h, chunk 2048),
+        # on the headline inputs, against the SwiGLU layer's time measured above
+        print("[bench] extras: linear attention at the LaCT LM shape", file=sys.stderr, flush=True)
+        Dll, _ = T.linattn_desc(B, H, N, d, d, chunk, C.TTT_BF16, C.MASK_APPLY_THEN_UPDATE)
+        wsll = torch.empty(max(1, T.linattn_workspace_bytes(Dll)), dtype=torch.uint8, device="cuda")
+        oll = torch.empty_like(q)
+        msll = time_calls(torch, lambda: T.linattn_forward(q, k, v, eta, chunk, C.MASK_APPLY_THEN_UPDATE, out=oll,
+                                                           want_S=False, workspace=wsll), max(st, 10), 2)
+        ll_bytes = B * H * N * (4 * d * 2 + 4)
+        extras["linattn_at_lact_lm_shape"] = {
+            "tokens_per_s": round(tokens / (msll * 1e-3)), "ms_per_call": round(msll, 4),
+            "hbm_GBps": round(ll_bytes / (msll * 1e-3) / 1e9, 1),
+            "hbm_frac": round(ll_bytes / (msll * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "workload": f"B{B} H{H} N{N} d_k=d_v={d} chunk {chunk} bf16, apply-then-update",
+            "swiglu_layer_ms_per_call": round(ms, 3), "linattn_speedup": round(ms / msll, 2)}
+        del wsll, oll
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,

@@ -91,7 +91,8 @@ typedef struct ttt_desc {
 
 typedef struct linattn_desc {
     int32_t B, H, N;
-    int32_t d_k, d_v;         /* multiples of 32, <= 256                                        */
+    int32_t d_k, d_v;         /* multiples of 32; d_v <= 4096; d_k <= 2048 on the chunk-parallel
+                                 path, <= 256 on the sequential one (TTT_ERR_UNSUPPORTED beyond) */
     int32_t chunk;            /* tokens per chunk, >= 1 (ignored by TOKEN_CAUSAL)               */
     int32_t io_dtype;         /* ttt_dtype of q, k, v, o; the state S is fp32                   */
     int32_t mask;             /* any ttt_mask_mode                                              */

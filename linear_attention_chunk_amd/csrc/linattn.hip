@@ -428,10 +428,16 @@ __global__ __launch_bounds__(kThreads, 2) void k_lin_delta(DeltaArgs<T> a) {
     const Opnd<T> B[1] = {{a.k + tok * a.dk + c0, a.dk, a.dk - c0, nl}};
     TD tl;
     tl.template run<PM1>(A, B, nl, smem);
-    float* dS = a.dS + (int64_t)unit * a.dv * a.dk;
-    tl.for_each([&](const float (&v)[1], int row, int col) {
-        if (r0 + row < a.dv && c0 + col < a.dk) dS[(int64_t)(r0 + row) * a.dk + c0 + col] = v[0];
-    });
+    // 32-bit offsets from the tile corner; full tiles skip the bounds checks
+    float* dS = a.dS + (int64_t)unit * a.dv * a.dk + (int64_t)r0 * a.dk + c0;
+    auto epi = [&](auto check) {
+        tl.for_each([&](const float (&v)[1], int row, int col) {
+            if (!decltype(check)::value || (r0 + row < a.dv && c0 + col < a.dk))
+                dS[(uint32_t)row * (uint32_t)a.dk + (uint32_t)col] = v[0];
+        });
+    };
+    if (r0 + TD::BM <= a.dv && c0 + TD::BN <= a.dk) epi(std::false_type{});
+    else epi(std::true_type{});
 }
 
 // The state each chunk's queries see, from S0 and the chunk updates dS_c: before chunk c's own
@@ -511,20 +517,39 @@ __global__ __launch_bounds__(kThreads, 2) void k_lin_apply(ApplyArgs<T> a) {
     TA tl;
     tl.template run<PM>(A, B, a.dk, smem);
     T* O = a.o + (tok + r0) * a.dv + c0;
-    tl.for_each([&](const float (&v)[PLANES], int row, int col) {
-        if (r0 + row < nl && c0 + col < a.dv) {
-            float x = v[0];
-            if constexpr (PLANES == 2) x += v[1];
-            O[(int64_t)row * a.dv + col] = Elt<T>::st(x);
-        }
-    });
+    auto epi = [&](auto check) {
+        tl.for_each([&](const float (&v)[PLANES], int row, int col) {
+            if (!decltype(check)::value || (r0 + row < nl && c0 + col < a.dv)) {
+                float x = v[0];
+                if constexpr (PLANES == 2) x += v[1];
+                O[(uint32_t)row * (uint32_t)a.dv + (uint32_t)col] = Elt<T>::st(x);
+            }
+        });
+    };
+    if (r0 + TA::BM <= nl && c0 + TA::BN <= a.dv) epi(std::false_type{});
+    else epi(std::true_type{});
+}
+
+// d_k limits: the sequential kernel is instantiated for d_k up to 256; the chunk-parallel kernels
+// take any multiple of 32 (their tiles loop over d_k)
+constexpr int kMaxSequentialDk = 256, kMaxParallelDk = 2048;
+
+// The chunk-parallel path writes dS_c and S_c, 2 x 4 bytes per state element per chunk, on top of
+// the algorithmic q, k, v, o traffic of 2 (d_k + d_v) bytes (bf16) per token: that extra is
+// 4 d_k d_v / (chunk (d_k + d_v)) of it.  It is taken while that ratio is at most 2 (chunk >= 128
+// at d_k = d_v = 128), where it runs well ahead of the sequential kernel; token-causal mode always
+// takes the sequential kernel.
+static bool lin_parallel(const linattn_desc& D) {
+    if (D.mask == TTT_MASK_TOKEN_CAUSAL || D.N == 0) return false;
+    const int64_t chunk = std::min<int64_t>(D.chunk, D.N);
+    return 4LL * D.d_k * D.d_v <= 2LL * chunk * (D.d_k + D.d_v);
 }
 
 static ttt_status validate_lin(const linattn_desc* D) {
     if (!D) return fail(TTT_ERR_INVALID_ARGUMENT, "desc is NULL");
     if (D->B < 0 || D->H < 0 || D->N < 0) return fail(TTT_ERR_INVALID_ARGUMENT, "B, H, N must be >= 0");
-    if (D->d_k < 32 || D->d_k > 256 || D->d_k % 32)
-        return fail(TTT_ERR_INVALID_ARGUMENT, "d_k=%d must be a multiple of 32 in [32, 256]", D->d_k);
+    if (D->d_k < 32 || D->d_k > kMaxParallelDk || D->d_k % 32)
+        return fail(TTT_ERR_INVALID_ARGUMENT, "d_k=%d must be a multiple of 32 in [32, %d]", D->d_k, kMaxParallelDk);
     if (D->d_v < 32 || D->d_v > 4096 || D->d_v % 32)
         return fail(TTT_ERR_INVALID_ARGUMENT, "d_v=%d must be a multiple of 32 in [32, 4096]", D->d_v);
     if (D->chunk < 1) return fail(TTT_ERR_INVALID_ARGUMENT, "chunk must be >= 1");
@@ -538,6 +563,10 @@ static ttt_status validate_lin(const linattn_desc* D) {
             return fail(TTT_ERR_UNSUPPORTED, "MASK_STRIDED supports at most 1024 chunks");
     }
     if ((int64_t)D->B * D->H > (1 << 20)) return fail(TTT_ERR_INVALID_ARGUMENT, "B*H too large");
+    if (D->d_k > kMaxSequentialDk && !lin_parallel(*D))
+        return fail(TTT_ERR_UNSUPPORTED,
+                    "d_k=%d > %d needs the chunk-parallel path (a chunked mask with 4 d_k d_v <= 2 chunk (d_k + d_v))",
+                    D->d_k, kMaxSequentialDk);
     return TTT_OK;
 }
 
@@ -575,17 +604,6 @@ static ttt_status run_lin(const linattn_desc& D, LinArgs<T>& a, hipStream_t st) 
         case 256: return launch_lin<T, 256>(a, grid, st);
     }
     return fail(TTT_ERR_UNSUPPORTED, "d_k=%d", D.d_k);
-}
-
-// The chunk-parallel path writes dS_c and S_c, 2 x 4 bytes per state element per chunk, on top of
-// the algorithmic q, k, v, o traffic of 2 (d_k + d_v) bytes (bf16) per token: that extra is
-// 4 d_k d_v / (chunk (d_k + d_v)) of it.  It is taken while that ratio is at most 2 (chunk >= 128
-// at d_k = d_v = 128), where it runs well ahead of the sequential kernel; token-causal mode always
-// takes the sequential kernel.
-static bool lin_parallel(const linattn_desc& D) {
-    if (D.mask == TTT_MASK_TOKEN_CAUSAL || D.N == 0) return false;
-    const int64_t chunk = std::min<int64_t>(D.chunk, D.N);
-    return 4LL * D.d_k * D.d_v <= 2LL * chunk * (D.d_k + D.d_v);
 }
 
 static size_t lin_ws_bytes(const linattn_desc& D) {

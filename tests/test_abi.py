@@ -124,7 +124,8 @@ def lin_desc(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(d_k=48), C.TTT_ERR_INVALID_ARGUMENT),
-    (dict(d_k=512), C.TTT_ERR_INVALID_ARGUMENT),
+    (dict(d_k=512), C.TTT_ERR_UNSUPPORTED),        # chunks of 32 leave only the sequential kernel
+    (dict(d_k=2080), C.TTT_ERR_INVALID_ARGUMENT),
     (dict(d_v=16), C.TTT_ERR_INVALID_ARGUMENT),
     (dict(chunk=0), C.TTT_ERR_INVALID_ARGUMENT),
     (dict(mask=5), C.TTT_ERR_INVALID_ARGUMENT),
@@ -165,6 +166,23 @@ def test_linattn_workspace_choice_and_rejects():
     assert L.linattn_forward(ctypes.byref(D), *args, None, 0, None) == C.TTT_ERR_WORKSPACE
     assert L.linattn_forward(ctypes.byref(D), *args, P16 + (1 << 34), need - 1, None) == C.TTT_ERR_WORKSPACE
     assert L.linattn_forward(ctypes.byref(D), *args, P16 + (1 << 34) + 16, need, None) == C.TTT_ERR_INVALID_ARGUMENT
+
+
+def test_linattn_wide_keys_need_the_chunk_parallel_path():
+    """d_k above 256 is accepted where the chunk-parallel kernels run (they loop over d_k tiles) and
+    refused with TTT_ERR_UNSUPPORTED where only the sequential kernel could run; d_k must stay a
+    multiple of 32 up to 2048."""
+    L = C.lib()
+    n = ctypes.c_size_t(0)
+    D = lin_desc(B=1, H=2, N=4096, d_k=384, d_v=384, chunk=2048)
+    assert L.linattn_workspace_bytes(ctypes.byref(D), ctypes.byref(n)) == C.TTT_OK and n.value > 0
+    for kw in (dict(mask=C.MASK_TOKEN_CAUSAL), dict(chunk=64)):
+        D = lin_desc(B=1, H=2, N=4096, d_k=384, d_v=384, **kw)
+        assert L.linattn_workspace_bytes(ctypes.byref(D), ctypes.byref(n)) == C.TTT_ERR_UNSUPPORTED
+        assert b"chunk-parallel" in L.ttt_last_error()
+    for dk in (2080, 400):
+        D = lin_desc(B=1, H=2, N=4096, d_k=dk, d_v=384, chunk=2048)
+        assert L.linattn_workspace_bytes(ctypes.byref(D), ctypes.byref(n)) == C.TTT_ERR_INVALID_ARGUMENT
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
