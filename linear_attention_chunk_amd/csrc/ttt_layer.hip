@@ -502,24 +502,33 @@ __global__ __launch_bounds__(kThreads, 2) void k_ns_step(NSArgs<T> a) {
     const T* Gm = a.Gram + s * a.gram_stride + (int64_t)mat * p * p;
     float* Xf = a.Xf + s * a.x_stride + mat * dm;
     T* Xo = a.Xout + s * a.x_stride + mat * dm;
+    // Offsets are 32-bit from the tile corner.  The iterate loads are unconditional (an out-of-range
+    // position reads the corner, and its result is never stored), so all of them stay in flight
+    // during the contraction instead of each waiting behind a bounds-check branch.
+    float* Xft = Xf + (int64_t)r0 * c + c0;
+    T* Xot = Xo + (int64_t)r0 * c + c0;
     auto body = [&](auto& tl, const auto& A, const auto& B, int K) {
         using TT = typename std::remove_reference<decltype(tl)>::type;
+        const bool full = r0 + TT::BM <= r && c0 + TT::BN <= c;
         float xv[TT::ELEMS];
         TT::for_each_pos([&](int idx, int row, int col) {
-            const int gr = r0 + row, gc = c0 + col;
-            xv[idx] = (gr < r && gc < c) ? Xf[(int64_t)gr * c + gc] : 0.f;
+            const bool in = full || (r0 + row < r && c0 + col < c);
+            xv[idx] = Xft[in ? (uint32_t)row * (uint32_t)c + (uint32_t)col : 0u];
         });
         tl.template run<PM1>(A, B, K, smem);
-        int idx = 0;
-        tl.for_each([&](const float (&v)[1], int row, int col) {
-            const int gr = r0 + row, gc = c0 + col;
-            const float xn = 1.5f * xv[idx++] - 0.5f * v[0];
-            if (gr < r && gc < c) {
-                const int64_t e = (int64_t)gr * c + gc;
-                Xf[e] = xn;
-                Xo[e] = Elt<T>::st(xn);
-            }
-        });
+        auto epi = [&](auto check) {
+            int idx = 0;
+            tl.for_each([&](const float (&v)[1], int row, int col) {
+                const float xn = 1.5f * xv[idx++] - 0.5f * v[0];
+                if (!decltype(check)::value || (r0 + row < r && c0 + col < c)) {
+                    const uint32_t e = (uint32_t)row * (uint32_t)c + (uint32_t)col;
+                    Xft[e] = xn;
+                    Xot[e] = Elt<T>::st(xn);
+                }
+            });
+        };
+        if (full) epi(std::false_type{});
+        else epi(std::true_type{});
     };
     if (r > c) {  // P = X Gram; Gram is symmetric, so its rows serve as the B operand
         NSStepTall<T> tl;
