@@ -269,8 +269,51 @@ template <> struct Vec4<float> {
     __device__ static void store(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
 };
 
-// One pass per row: the row of W - U is held in registers (4 floats per lane per 256 columns).
-// W2's rows are also written to LDS so that W2^T can be stored 16 consecutive elements at a time.
+// One pass per row: the row of W - U is held in registers (NV float4 per lane, NV = ceil(row / 256)).
+// Every load of a row is issued before any is used: a lane past the row's end reads the row's first
+// vector and drops the value, so no load waits behind a per-lane branch.  W2's rows are also written
+// to LDS so that W2^T can be stored 16 consecutive elements at a time.
+template <int NV, typename T>
+__device__ __forceinline__ void update_rows(const float* src, const float* U, float* dst, T* shm, T* tileT,
+                                            int row0, int L, bool norm, bool to_lds) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int L4 = L / 4;
+#pragma unroll
+    for (int rr = 0; rr < kUpdRows / 4; ++rr) {
+        const int row = wave * (kUpdRows / 4) + rr;
+        const int64_t ro = (int64_t)(row0 + row) * L;
+        const float4* s4 = reinterpret_cast<const float4*>(src + ro);
+        float4 x[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) x[i] = s4[min(lane + 64 * i, L4 - 1)];
+        if (U) {
+            const float4* u4 = reinterpret_cast<const float4*>(U + ro);
+            float4 uv[NV];
+#pragma unroll
+            for (int i = 0; i < NV; ++i) uv[i] = u4[min(lane + 64 * i, L4 - 1)];
+#pragma unroll
+            for (int i = 0; i < NV; ++i) { x[i].x -= uv[i].x; x[i].y -= uv[i].y; x[i].z -= uv[i].z; x[i].w -= uv[i].w; }
+        }
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            if (lane + 64 * i < L4) ss += x[i].x * x[i].x + x[i].y * x[i].y + x[i].z * x[i].z + x[i].w * x[i].w;
+        float sc = 1.0f;
+        if (norm) sc = 1.0f / fmaxf(sqrtf(wave_sum(ss)), 1e-6f);
+        float4* d4 = reinterpret_cast<float4*>(dst + ro);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int c4 = lane + 64 * i;
+            if (c4 < L4) {
+                const float4 w = make_float4(x[i].x * sc, x[i].y * sc, x[i].z * sc, x[i].w * sc);
+                d4[c4] = w;
+                Vec4<T>::store(shm + ro + 4 * c4, w);
+                if (to_lds) Vec4<T>::store(tileT + row * L + 4 * c4, w);
+            }
+        }
+    }
+}
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_update(UpdArgs<T> a) {
     extern __shared__ __attribute__((aligned(16))) char dyn_lds[];
@@ -290,42 +333,16 @@ __global__ __launch_bounds__(kThreads) void k_update(UpdArgs<T> a) {
     const bool norm = a.norm && !frozen;
     float* dst = a.dst + s * a.dst_stride + moff;
     T* shm = a.sh + s * a.sh_stride + moff;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int L4 = L / 4;
-    constexpr int kMaxV = kMaxDim / 256;  // float4 per lane per row
-    for (int rr = 0; rr < kUpdRows / 4; ++rr) {
-        const int row = wave * (kUpdRows / 4) + rr;
-        const int64_t ro = (int64_t)(row0 + row) * L;
-        const float4* s4 = reinterpret_cast<const float4*>(src + ro);
-        const float4* u4 = U ? reinterpret_cast<const float4*>(U + ro) : nullptr;
-        float4 x[kMaxV];
-        float ss = 0.f;
-#pragma unroll
-        for (int i = 0; i < kMaxV; ++i) {
-            const int c4 = lane + 64 * i;
-            if (c4 < L4) {
-                float4 w = s4[c4];
-                if (u4) {
-                    const float4 u = u4[c4];
-                    w.x -= u.x; w.y -= u.y; w.z -= u.z; w.w -= u.w;
-                }
-                x[i] = w;
-                ss += w.x * w.x + w.y * w.y + w.z * w.z + w.w * w.w;
-            }
-        }
-        float sc = 1.0f;
-        if (norm) sc = 1.0f / fmaxf(sqrtf(wave_sum(ss)), 1e-6f);
-        float4* d4 = reinterpret_cast<float4*>(dst + ro);
-#pragma unroll
-        for (int i = 0; i < kMaxV; ++i) {
-            const int c4 = lane + 64 * i;
-            if (c4 < L4) {
-                const float4 w = make_float4(x[i].x * sc, x[i].y * sc, x[i].z * sc, x[i].w * sc);
-                d4[c4] = w;
-                Vec4<T>::store(shm + ro + 4 * c4, w);
-                if (mat == 2) Vec4<T>::store(tileT + row * L + 4 * c4, w);
-            }
-        }
+    static_assert(kMaxDim <= 8 * 256, "update rows hold at most 8 float4 per lane");
+    switch ((L / 4 + 63) / 64) {  // uniform per workgroup
+        case 1: update_rows<1>(src, U, dst, shm, tileT, row0, L, norm, mat == 2); break;
+        case 2: update_rows<2>(src, U, dst, shm, tileT, row0, L, norm, mat == 2); break;
+        case 3: update_rows<3>(src, U, dst, shm, tileT, row0, L, norm, mat == 2); break;
+        case 4: update_rows<4>(src, U, dst, shm, tileT, row0, L, norm, mat == 2); break;
+        case 5: update_rows<5>(src, U, dst, shm, tileT, row0, L, norm, mat == 2); break;
+        case 6: update_rows<6>(src, U, dst, shm, tileT, row0, L, norm, mat == 2); break;
+        case 7: update_rows<7>(src, U, dst, shm, tileT, row0, L, norm, mat == 2); break;
+        default: update_rows<8>(src, U, dst, shm, tileT, row0, L, norm, mat == 2); break;
     }
     if (mat == 2) {  // W2^T [m][d]: column c of this 16-row block is 16 consecutive elements
         __syncthreads();
@@ -362,6 +379,7 @@ static ttt_status launch_update(const UpdArgs<T>& u, int grid, hipStream_t st) {
 // init: X = U / (||U||_F + 1e-7) in fp32 and io dtype.  gram / step: one cubic Newton-Schulz
 // step X <- 1.5 X - 0.5 (X X^T) X, taken as X - ... on the side with the smaller Gram matrix.
 constexpr int kPrepElems = 4096;
+static_assert(kPrepElems % kThreads == 0, "prep blocks take whole rounds of the workgroup");
 
 struct PrepArgs {
     const float* G; int64_t g_stride;
@@ -388,12 +406,23 @@ __global__ __launch_bounds__(kThreads) void k_muon_prep(PrepArgs a) {
     float* M = a.M ? a.M + s * a.m_stride + mat * a.dm : nullptr;
     float ss = 0.f;
     const int64_t e0 = (int64_t)blk * kPrepElems;
-    for (int i = threadIdx.x; i < kPrepElems; i += kThreads) {
-        const int64_t e = e0 + i;
+    // all loads first (an index past the matrix reads its last element and is not used), then the
+    // arithmetic and stores, so the loads are in flight together
+    constexpr int NI = kPrepElems / kThreads;
+    float g[NI], mv[NI];
+#pragma unroll
+    for (int j = 0; j < NI; ++j) g[j] = G[min(e0 + threadIdx.x + j * kThreads, a.dm - 1)];
+    if (M) {
+#pragma unroll
+        for (int j = 0; j < NI; ++j) mv[j] = M[min(e0 + threadIdx.x + j * kThreads, a.dm - 1)];
+    }
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+        const int64_t e = e0 + threadIdx.x + j * kThreads;
         if (e < a.dm) {
-            float u = G[e];
+            float u = g[j];
             if (M) {
-                u = a.beta * M[e] + u;
+                u = a.beta * mv[j] + u;
                 M[e] = u;
             }
             ss += u * u;
@@ -431,10 +460,15 @@ __global__ __launch_bounds__(kThreads) void k_ns_init(NSArgs<T> a) {
     float* Xf = a.Xf + s * a.x_stride + mat * dm;
     T* Xo = a.Xout + s * a.x_stride + mat * dm;
     const int64_t e0 = (int64_t)blk * kPrepElems;
-    for (int i = threadIdx.x; i < kPrepElems; i += kThreads) {
-        const int64_t e = e0 + i;
+    constexpr int NI = kPrepElems / kThreads;
+    float u[NI];
+#pragma unroll
+    for (int j = 0; j < NI; ++j) u[j] = U[min(e0 + threadIdx.x + j * kThreads, dm - 1)];
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+        const int64_t e = e0 + threadIdx.x + j * kThreads;
         if (e < dm) {
-            const float x = U[e] * inv;
+            const float x = u[j] * inv;
             Xf[e] = x;
             Xo[e] = Elt<T>::st(x);
         }
