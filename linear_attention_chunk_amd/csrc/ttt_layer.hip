@@ -475,14 +475,21 @@ __global__ __launch_bounds__(kThreads) void k_ns_init(NSArgs<T> a) {
     }
 }
 
-template <typename T, bool KS> using NSTile = Tile<T, 128, 128, 2, 2, 1, 1, 1, KS, KS>;
+// Gram tiles: one 64-wide LDS stage (37 KB), so three workgroups share a CU
+template <typename T, bool KS> using NSTile = Tile<T, 128, 128, 2, 2, 1, 1, 1, KS, KS, false, 4, 1>;
 template <typename T> using NSStepTall = Tile<T, 128, 64, 2, 2, 1, 1, 1, false, false>;
 template <typename T> using NSStepWide = Tile<T, 128, 64, 2, 2, 1, 1, 1, false, true>;
 constexpr int kNSStepRows = 128, kNSStepCols = 64;
 
+// The Gram matrix is symmetric: only its tiles on or above the diagonal are computed (tile t of
+// np (np + 1) / 2, row-major over the upper triangle), and an off-diagonal tile also writes its
+// mirror block, transposed through LDS so that those stores are whole rows as well.
 template <typename T>
-__global__ __launch_bounds__(kThreads, 2) void k_ns_gram(NSArgs<T> a) {
-    __shared__ __attribute__((aligned(16))) char smem[NSTile<T, false>::LDS];
+__global__ __launch_bounds__(kThreads, 3) void k_ns_gram(NSArgs<T> a) {
+    constexpr int kTP = 128 + 16 / (int)sizeof(T);  // transposed-tile pitch (elements)
+    constexpr int LDSB = NSTile<T, false>::LDS > 128 * kTP * (int)sizeof(T) ? NSTile<T, false>::LDS
+                                                                             : 128 * kTP * (int)sizeof(T);
+    __shared__ __attribute__((aligned(16))) char smem[LDSB];
     const int64_t dm = (int64_t)a.d * a.m;
     const int per = a.nmat * a.tiles;
     const int lb = xcd_block(gridDim.x);
@@ -493,25 +500,41 @@ __global__ __launch_bounds__(kThreads, 2) void k_ns_gram(NSArgs<T> a) {
     const int r = mat < 2 ? a.m : a.d, c = mat < 2 ? a.d : a.m;
     const int p = r < c ? r : c;
     const int np = (p + 127) / 128;
-    const int i0 = (t / np) * 128, j0 = (t % np) * 128;
+    int ti = 0;
+    while (t >= np - ti) t -= np - ti++;  // uniform: row ti of the upper triangle, column ti + t
+    const int i0 = ti * 128, j0 = (ti + t) * 128;
     const T* X = a.Xin + s * a.x_stride + mat * dm;
     T* Gm = a.Gram + s * a.gram_stride + (int64_t)mat * p * p;
-    auto store = [&](const float (&v)[1], int row, int col) {
-        const int gi = i0 + row, gj = j0 + col;
-        if (gi < p && gj < p) Gm[(int64_t)gi * p + gj] = Elt<T>::st(v[0]);
+    T* tT = reinterpret_cast<T*>(smem);
+    auto epi = [&](auto& tl) {
+        tl.for_each([&](const float (&v)[1], int row, int col) {
+            if (i0 + row < p && j0 + col < p) Gm[(uint32_t)(i0 + row) * (uint32_t)p + (uint32_t)(j0 + col)] = Elt<T>::st(v[0]);
+        });
+        if (i0 == j0) return;
+        lds_barrier();  // every wave is done with the LDS stage
+        tl.for_each([&](const float (&v)[1], int row, int col) { tT[col * kTP + row] = Elt<T>::st(v[0]); });
+        __syncthreads();
+        // mirror block: Gram row j0 + cc, columns i0 .. i0 + 127, from LDS row cc
+        constexpr int VEC = 16 / (int)sizeof(T), VPR = 128 / VEC;
+        for (int u = threadIdx.x; u < 128 * VPR; u += kThreads) {
+            const int cc = u / VPR, x = (u % VPR) * VEC;
+            if (j0 + cc < p && i0 + x < p)
+                *reinterpret_cast<u32x4_t*>(Gm + (uint32_t)(j0 + cc) * (uint32_t)p + (uint32_t)(i0 + x)) =
+                    *reinterpret_cast<const u32x4_t*>(tT + cc * kTP + x);
+        }
     };
     if (r > c) {  // Gram = X^T X (c x c), contracted over the r rows
         NSTile<T, true> tl;
         const Opnd<T> A[1] = {{X + i0, c, c - i0, r}};
         const Opnd<T> B[1] = {{X + j0, c, c - j0, r}};
         tl.template run<PM1>(A, B, r, smem);
-        tl.for_each(store);
+        epi(tl);
     } else {      // Gram = X X^T (r x r), contracted over the c columns
         NSTile<T, false> tl;
         const Opnd<T> A[1] = {{X + (int64_t)i0 * c, c, r - i0, c}};
         const Opnd<T> B[1] = {{X + (int64_t)j0 * c, c, r - j0, c}};
         tl.template run<PM1>(A, B, c, smem);
-        tl.for_each(store);
+        epi(tl);
     }
 }
 
@@ -744,7 +767,7 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
             }
             if ((rc = check_launch("k_ns_init")) != TTT_OK) return rc;
             const int p = d < m ? d : m;
-            const int gt = (int)(cdiv(p, 128) * cdiv(p, 128));
+            const int gt = (int)(cdiv(p, 128) * (cdiv(p, 128) + 1) / 2);  // upper-triangle Gram tiles
             // step tiles: the larger of the tall (m x d) and wide (d x m) tilings
             const int stt = (int)std::max(cdiv(m, kNSStepRows) * cdiv(d, kNSStepCols),
                                           cdiv(d, kNSStepRows) * cdiv(m, kNSStepCols));

@@ -97,6 +97,13 @@ def test_tall_and_wide_muon_fp32():
     run_small(6, 1, 1, 128, 96, 32, 64, O.MASK_APPLY_THEN_UPDATE, O.UPD_MUON_L2, False, ns=3)
 
 
+def test_muon_gram_mirror_fp32():
+    # p = min(d, m) = 160 spans two 128-wide Gram tiles, the second partial: the off-diagonal tile
+    # also writes its mirror block; both Gram sides (m > d, then d > m)
+    run_small(12, 1, 1, 256, 160, 320, 128, O.MASK_APPLY_THEN_UPDATE, O.UPD_MUON_L2, False, ns=3)
+    run_small(13, 1, 1, 256, 320, 160, 128, O.MASK_UPDATE_THEN_APPLY, O.UPD_MUON, False, ns=2)
+
+
 def test_zero_tokens_returns_w0():
     (q, k, v, eta, W0), (hq, hk, hv, he, W1, W3, W2) = full_ttt_inputs(0, 2, 2, 0, 32, 64, True)
     o, Wout = T.ttt_forward(q, k, v, eta, W0, 16, O.MASK_APPLY_THEN_UPDATE, O.UPD_GD_L2, m_h=64)
