@@ -65,8 +65,10 @@ template <typename T>
 __global__ __launch_bounds__(64 * kUpWaves, 1) void k_up(StepArgs<T> a) {
     // query wave: 64 tokens x 64 hidden x {A, C}; key wave: 32 hidden x 96 tokens x {A, C, DH}
     using TQ = Tile<T, kUpQRows, kUpCols, 2, 4, 1, 2, 2, false, false, false, kUpWaves>;
-    using TK = Tile<T, kUpCols, kUpKRows, 2, 4, 3, 2, 3, false, false, false, kUpWaves, 1>;
-    constexpr int LDSB = TQ::LDS > TK::LDS ? TQ::LDS : TK::LDS;
+    // key tiles run two passes over d, each with two 64-wide LDS stages: W1, W3 x K, then W2^T x V
+    using TK1 = Tile<T, kUpCols, kUpKRows, 2, 4, 2, 1, 2, false, false, false, kUpWaves>;
+    using TK2 = Tile<T, kUpCols, kUpKRows, 2, 4, 1, 1, 1, false, false, false, kUpWaves>;
+    constexpr int LDSB = std::max(TQ::LDS, std::max(TK1::LDS, TK2::LDS));
     __shared__ __attribute__((aligned(16))) char smem[LDSB];
 
     const int per = a.nQ + a.nK;
@@ -106,12 +108,15 @@ __global__ __launch_bounds__(64 * kUpWaves, 1) void k_up(StepArgs<T> a) {
         const int tt = t - a.nQ;
         const int r0 = (tt / nct) * kUpKRows, c0 = (tt % nct) * kUpCols;
         const int64_t tok = (int64_t)s * a.N + a.u0 + r0;
-        const Opnd<T> A[3] = {{W1s + (int64_t)c0 * a.d, a.d, a.m - c0, a.d},
-                              {W3s + (int64_t)c0 * a.d, a.d, a.m - c0, a.d},
-                              {W2Ts + (int64_t)c0 * a.d, a.d, a.m - c0, a.d}};
-        const Opnd<T> B[2] = {{a.k + tok * a.d, a.d, a.lu - r0, a.d}, {a.v + tok * a.d, a.d, a.lu - r0, a.d}};
-        TK tl;
-        tl.template run<PMKT>(A, B, a.d, smem);
+        const Opnd<T> A1[2] = {{W1s + (int64_t)c0 * a.d, a.d, a.m - c0, a.d},
+                               {W3s + (int64_t)c0 * a.d, a.d, a.m - c0, a.d}};
+        const Opnd<T> B1[1] = {{a.k + tok * a.d, a.d, a.lu - r0, a.d}};
+        const Opnd<T> A2[1] = {{W2Ts + (int64_t)c0 * a.d, a.d, a.m - c0, a.d}};
+        const Opnd<T> B2[1] = {{a.v + tok * a.d, a.d, a.lu - r0, a.d}};
+        TK1 tl;  // (K W1^T, K W3^T) transposed
+        TK2 tp;  // (V W2) transposed
+        tl.template run<PMG>(A1, B1, a.d, smem);
+        tp.template run<PM1>(A2, B2, a.d, smem);
         const float* eta = a.eta + tok;
         T* HkE = a.HkE + ioff + (int64_t)c0 * a.tp + r0;
         T* DA = a.DA + ioff + (int64_t)c0 * a.tp + r0;
@@ -125,11 +130,14 @@ __global__ __launch_bounds__(64 * kUpWaves, 1) void k_up(StepArgs<T> a) {
             dc = dh * xs;
         };
         // tile row = hidden unit c0 + row, tile column = token r0 + col
+        // both tiles have the same wave layout: accumulator element idx of one is at the same
+        // (row, col) as in the other
         auto epi = [&](auto check) {
-            tl.for_each([&](const float (&v)[3], int row, int col) {
+            TK1::for_each_pos([&](int idx, int row, int col) {
+                const int i = idx / (TK1::FN * 16), j = (idx / 16) % TK1::FN, r = idx % 16;
                 if (!decltype(check)::value || (r0 + col < a.lu && c0 + row < a.m)) {
                     float hk, da, dc;
-                    bwd(v[0], v[1], v[2], eta[col], hk, da, dc);
+                    bwd(tl.acc[0][i][j][r], tl.acc[1][i][j][r], tp.acc[0][i][j][r], eta[col], hk, da, dc);
                     const uint32_t off = (uint32_t)row * (uint32_t)a.tp + (uint32_t)col;
                     HkE[off] = Elt<T>::st(hk);
                     DA[off] = Elt<T>::st(da);
@@ -485,7 +493,7 @@ constexpr int kNSStepRows = 128, kNSStepCols = 64;
 // np (np + 1) / 2, row-major over the upper triangle), and an off-diagonal tile also writes its
 // mirror block, transposed through LDS so that those stores are whole rows as well.
 template <typename T>
-__global__ __launch_bounds__(kThreads, 3) void k_ns_gram(NSArgs<T> a) {
+__global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 3 : 2) void k_ns_gram(NSArgs<T> a) {  // fp32: 67 KB LDS
     constexpr int kTP = 128 + 16 / (int)sizeof(T);  // transposed-tile pitch (elements)
     constexpr int LDSB = NSTile<T, false>::LDS > 128 * kTP * (int)sizeof(T) ? NSTile<T, false>::LDS
                                                                              : 128 * kTP * (int)sizeof(T);
