@@ -390,14 +390,25 @@ struct Tile {
     // (with two sets its conservative count across the loop edge also waited for the newer set).
     template <class PM, bool FULL>
     __device__ __forceinline__ void run_(const Opnd<T> (&A)[NA], const Opnd<T> (&B)[NB], int K, char* lds) {
+        if (K <= 0) {
+            zero();
+            return;
+        }
+        Regs g;
+        issue<FULL>(g, A, B, 0);
+        run_issued<PM, FULL>(g, A, B, K, lds);
+    }
+    // The same with stage 0 already issued into g (issue<FULL>(g, A, B, 0) with the same FULL), so
+    // that a caller can start a tile's first loads early.  K must be positive.  On entry every wave
+    // must be done reading the LDS stages.
+    template <class PM, bool FULL>
+    __device__ __forceinline__ void run_issued(Regs& g, const Opnd<T> (&A)[NA], const Opnd<T> (&B)[NB], int K,
+                                               char* lds) {
         zero();
         const int nk = (K + KSTEP - 1) / KSTEP;
-        if (nk <= 0) return;
-        Regs g;
         if constexpr (NBUF == 1) {
             // one LDS stage: the loads of stage s + 1 are in flight while stage s is computed; the
             // stage is stored once every wave has finished reading the previous one
-            issue<FULL>(g, A, B, 0);
             put<FULL>(g, lds);
             if (nk > 1) issue<FULL>(g, A, B, KSTEP);
             lds_barrier();
@@ -412,7 +423,6 @@ struct Tile {
             }
             return;
         }
-        issue<FULL>(g, A, B, 0);
         put<FULL>(g, lds);
         if (nk > 1) issue<FULL>(g, A, B, KSTEP);
         lds_barrier();

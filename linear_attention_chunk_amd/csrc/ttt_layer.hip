@@ -115,8 +115,14 @@ __global__ __launch_bounds__(64 * kUpWaves, 1) void k_up(StepArgs<T> a) {
         const Opnd<T> B2[1] = {{a.v + tok * a.d, a.d, a.lu - r0, a.d}};
         TK1 tl;  // (K W1^T, K W3^T) transposed
         TK2 tp;  // (V W2) transposed
+        // the second pass's first stage is loaded before the first pass starts, so its latency
+        // does not open the second pass
+        typename TK2::Regs g2;
+        const bool f2 = TK2::full(A2, B2, a.d) && a.d > 0;
+        if (f2) TK2::template issue<true>(g2, A2, B2, 0);
         tl.template run<PMG>(A1, B1, a.d, smem);
-        tp.template run<PM1>(A2, B2, a.d, smem);
+        if (f2) tp.template run_issued<PM1, true>(g2, A2, B2, a.d, smem);
+        else tp.template run<PM1>(A2, B2, a.d, smem);
         const float* eta = a.eta + tok;
         T* HkE = a.HkE + ioff + (int64_t)c0 * a.tp + r0;
         T* DA = a.DA + ioff + (int64_t)c0 * a.tp + r0;
