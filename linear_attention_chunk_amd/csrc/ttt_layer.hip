@@ -177,10 +177,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_down(StepArgs<T> a) {
     if (S % 8 == 0) {
         const int sp = S / 8, x = blockIdx.x % 8;
         int i = blockIdx.x / 8;
-        if (i < sp * a.nG13) {
-            s = i / a.nG13; t = i % a.nG13;
+        if (i < sp * a.nG13) {  // last scan first: the up kernel wrote its DA, DC last
+            s = sp - 1 - i / a.nG13; t = i % a.nG13;
         } else if ((i -= sp * a.nG13) < sp * a.nG2) {
-            s = i / a.nG2; t = a.nG13 + i % a.nG2;
+            s = sp - 1 - i / a.nG2; t = a.nG13 + i % a.nG2;
         } else {
             i -= sp * a.nG2;
             s = i / a.nO; t = a.nG13 + a.nG2 + i % a.nO;
