@@ -4,12 +4,13 @@
 // the PaperTrace notes' section 1.1 and the token-causal limit ("From Linear Attention to Test-Time
 // Training", causal linear attention).
 //
-// Two paths.  The chunk-parallel path (large chunks, every mask but token-causal) runs three
-// launches: the chunk's own update dS_c = sum over the chunk of eta_i v_i k_i^T for every
+// Two paths.  The chunk-parallel path (large chunks; token-causal mode over 128-token blocks) runs
+// three launches: the chunk's own update dS_c = sum over the chunk of eta_i v_i k_i^T for every
 // (scan, chunk) in parallel, an elementwise scan over chunks that writes the state each chunk's
 // queries see (before or after its own update, as the mask orders them), and the apply
-// o = S_c q for every chunk in parallel.  The sequential path below handles token-causal mode and
-// small chunks, where the chunk states would cost more traffic than they save.
+// o = S_c q for every chunk in parallel, plus the block's own masked term in token-causal mode.
+// The sequential path below handles small chunks, where the chunk states would cost more traffic
+// than they save, and short token-causal sequences.
 //
 // Sequential path: one workgroup owns one (batch, head) scan and a 32-row slice of S's d_v rows,
 // and walks the sequence in sub-blocks of TB tokens.  The slice of S stays in MFMA accumulators (fp32) for the
@@ -489,6 +490,7 @@ __global__ __launch_bounds__(kThreads) void k_lin_scan(ScanArgs<T> a) {
 // o (chunk c's tokens x d_v) = q_c S_c^T, contracting over d_k: bf16 as hi and lo products summed
 template <typename T> struct ApplyArgs {
     const T* q; const T* Sc; T* o;
+    const T* k; const T* v; const float* eta;  // token-causal apply only
     int64_t N; int dk, dv, chunk, nc, ntt, ntv, nscan;
 };
 
@@ -530,6 +532,101 @@ __global__ __launch_bounds__(kThreads, 2) void k_lin_apply(ApplyArgs<T> a) {
     else epi(std::true_type{});
 }
 
+// Token-causal mode on the chunk-parallel path.  The sequence is cut into blocks of kCausalBlock
+// tokens; the delta and scan kernels give every block the state S_c before it (apply-then-update
+// order), and this kernel adds the block's own causal term.  For query token i of the block
+//   o_i = S_c q_i + sum over the block's tokens j <= i of eta_j (k_j . q_i) v_j,
+// that is o = q S_c^T + tril(q k^T) diag(eta) v.  One workgroup takes a block and 128 columns of
+// d_v.  The masked, eta-scaled q k^T block is rounded to the io dtype straight into the A regions
+// of the LDS stages of the P v product (v through the transposing stager), as the sequential
+// kernel rounds it.  q S_c^T sums the bf16 hi and lo state planes in one accumulator; it is added
+// through an fp32 LDS buffer, because the transposing stager leaves P v in another column order.
+constexpr int kCausalBlock = 128;
+
+template <typename T>
+__global__ __launch_bounds__(kThreads, 2) void k_lin_apply_causal(ApplyArgs<T> a) {
+    constexpr int PLANES = sizeof(T) == 2 ? 2 : 1;
+    using TP = Tile<T, kCausalBlock, kCausalBlock, 1, 2, 1, 1, 1, false, false>;  // q k^T
+    using TD = Tile<T, kCausalBlock, kApplyCols, 2, 2, 1, 1, 1, false, true>;     // P v, P in LDS
+    using TA = Tile<T, kCausalBlock, kApplyCols, 1, 2, 1, 1, 1, false, false>;    // q S_c^T per plane
+    constexpr int NST = kCausalBlock / TD::KSTEP;  // key-token stages of P v, all resident
+    constexpr int OP = kApplyCols + 4;             // fp32 combine-buffer pitch (floats)
+    constexpr int LDSB = std::max(std::max(TP::LDS, NST * TD::STAGE), std::max(TA::LDS, kCausalBlock * OP * 4));
+    static_assert(kCausalBlock % TD::KSTEP == 0 && kApplyRows == kCausalBlock, "block and tile shapes");
+    __shared__ __attribute__((aligned(16))) char smem[LDSB];
+    const int lb = xcd_block(gridDim.x);
+    const int unit = lb / a.ntv, cv = lb % a.ntv;
+    const int scan = unit / a.nc, c = unit % a.nc;
+    const int c0 = cv * kApplyCols;
+    const int64_t tok = (int64_t)scan * a.N + (int64_t)c * kCausalBlock;
+    const int nl = (int)std::min<int64_t>(kCausalBlock, a.N - (int64_t)c * kCausalBlock);
+
+    // v's stages are loaded first, so they are in flight during q k^T
+    const Opnd<T> Bv = {a.v + tok * a.dv + c0, a.dv, a.dv - c0, nl};  // rows: d_v columns; k: tokens
+    const bool vfull = a.dv - c0 >= kApplyCols && nl == kCausalBlock;
+    typename TD::SB gv[NST];
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+        if (vfull) gv[st].template load<true>(Bv, st * TD::KSTEP);
+        else gv[st].template load<false>(Bv, st * TD::KSTEP);
+    }
+    // eta of the key tokens this lane's P columns belong to (clamped to the block; masked later)
+    float ek[TP::FN];
+    TP::for_each_pos([&](int idx, int, int col) {
+        if (idx < TP::FN * 16 && idx % 16 == 0) ek[idx / 16] = a.eta[tok + std::min(col, nl - 1)];
+    });
+
+    // P = q k^T over the block (rows: query tokens, columns: key tokens)
+    const Opnd<T> Aq[1] = {{a.q + tok * a.dk, a.dk, nl, a.dk}};
+    const Opnd<T> Bk[1] = {{a.k + tok * a.dk, a.dk, nl, a.dk}};
+    TP tp;
+    tp.template run<PM1>(Aq, Bk, a.dk, smem);
+    lds_barrier();  // every wave is done with q k^T's stages
+    {
+        int idx = 0;
+        tp.for_each([&](const float (&v)[1], int row, int col) {
+            const float val = (col <= row && col < nl) ? v[0] * ek[(idx / 16) % TP::FN] : 0.f;
+            ++idx;
+            *reinterpret_cast<T*>(smem + (col / TD::KSTEP) * TD::STAGE + row * TD::PITCH +
+                                  (col % TD::KSTEP) * (int)sizeof(T)) = Elt<T>::st(val);
+        });
+    }
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+        if (vfull) gv[st].template store<true>(smem + st * TD::STAGE + TD::A_BYTES);
+        else gv[st].template store<false>(smem + st * TD::STAGE + TD::A_BYTES);
+    }
+    lds_barrier();
+    TD td;
+    td.zero();
+#pragma unroll
+    for (int st = 0; st < NST; ++st) td.template compute<PM1>(smem + st * TD::STAGE);
+    lds_barrier();  // every wave is done with P v's stages
+
+    // q S_c^T, hi then lo plane into one accumulator
+    const int64_t dvk = (int64_t)a.dv * a.dk;
+    const T* Sp = a.Sc + (int64_t)unit * PLANES * dvk + (int64_t)c0 * a.dk;
+    TA ta;
+#pragma unroll
+    for (int pl = 0; pl < PLANES; ++pl) {
+        const Opnd<T> Bs[1] = {{Sp + pl * dvk, a.dk, a.dv - c0, a.dk}};
+        ta.template run<PM1>(Aq, Bs, a.dk, smem, pl > 0);
+    }
+    lds_barrier();
+    float* buf = reinterpret_cast<float*>(smem);
+    td.for_each([&](const float (&v)[1], int row, int col) { buf[row * OP + col] = v[0]; });
+    __syncthreads();
+    T* O = a.o + tok * a.dv + c0;
+    auto epi = [&](auto check) {
+        ta.for_each([&](const float (&v)[1], int row, int col) {
+            if (!decltype(check)::value || (row < nl && c0 + col < a.dv))
+                O[(uint32_t)row * (uint32_t)a.dv + (uint32_t)col] = Elt<T>::st(v[0] + buf[row * OP + col]);
+        });
+    };
+    if (nl == kCausalBlock && c0 + kApplyCols <= a.dv) epi(std::false_type{});
+    else epi(std::true_type{});
+}
+
 // d_k limits: the sequential kernel is instantiated for d_k up to 256; the chunk-parallel kernels
 // take any multiple of 32 (their tiles loop over d_k)
 constexpr int kMaxSequentialDk = 256, kMaxParallelDk = 2048;
@@ -537,10 +634,11 @@ constexpr int kMaxSequentialDk = 256, kMaxParallelDk = 2048;
 // The chunk-parallel path writes dS_c and S_c, 2 x 4 bytes per state element per chunk, on top of
 // the algorithmic q, k, v, o traffic of 2 (d_k + d_v) bytes (bf16) per token: that extra is
 // 4 d_k d_v / (chunk (d_k + d_v)) of it.  It is taken while that ratio is at most 2 (chunk >= 128
-// at d_k = d_v = 128), where it runs well ahead of the sequential kernel; token-causal mode always
-// takes the sequential kernel.
+// at d_k = d_v = 128), where it runs well ahead of the sequential kernel.  Token-causal mode runs
+// it over blocks of kCausalBlock tokens once the sequence holds two of them.
 static bool lin_parallel(const linattn_desc& D) {
-    if (D.mask == TTT_MASK_TOKEN_CAUSAL || D.N == 0) return false;
+    if (D.N == 0) return false;
+    if (D.mask == TTT_MASK_TOKEN_CAUSAL) return D.N >= 2 * kCausalBlock;
     const int64_t chunk = std::min<int64_t>(D.chunk, D.N);
     return 4LL * D.d_k * D.d_v <= 2LL * chunk * (D.d_k + D.d_v);
 }
@@ -565,7 +663,8 @@ static ttt_status validate_lin(const linattn_desc* D) {
     if ((int64_t)D->B * D->H > (1 << 20)) return fail(TTT_ERR_INVALID_ARGUMENT, "B*H too large");
     if (D->d_k > kMaxSequentialDk && !lin_parallel(*D))
         return fail(TTT_ERR_UNSUPPORTED,
-                    "d_k=%d > %d needs the chunk-parallel path (a chunked mask with 4 d_k d_v <= 2 chunk (d_k + d_v))",
+                    "d_k=%d > %d needs the chunk-parallel path (a chunked mask with 4 d_k d_v <= 2 chunk (d_k + d_v), "
+                    "or token-causal mode with N >= 256)",
                     D->d_k, kMaxSequentialDk);
     return TTT_OK;
 }
@@ -606,15 +705,22 @@ static ttt_status run_lin(const linattn_desc& D, LinArgs<T>& a, hipStream_t st) 
     return fail(TTT_ERR_UNSUPPORTED, "d_k=%d", D.d_k);
 }
 
+// tokens per chunk of the chunk-parallel path: the mask's chunk, or the token-causal block
+static int64_t lin_block(const linattn_desc& D) {
+    return D.mask == TTT_MASK_TOKEN_CAUSAL ? kCausalBlock : D.chunk;
+}
+
 static size_t lin_ws_bytes(const linattn_desc& D) {
     if (!lin_parallel(D)) return 0;
-    const int64_t S = (int64_t)D.B * D.H, nc = cdiv(D.N, D.chunk), dvk = (int64_t)D.d_v * D.d_k;
+    const int64_t S = (int64_t)D.B * D.H, nc = cdiv(D.N, lin_block(D)), dvk = (int64_t)D.d_v * D.d_k;
     return align256((size_t)(S * nc * dvk * 4)) * 2;  // dS_c (fp32), then S_c (bf16 hi + lo, or fp32)
 }
 
 template <typename T>
 static ttt_status run_lin_parallel(const linattn_desc& D, LinArgs<T> a, char* ws, hipStream_t st) {
-    const int64_t S = (int64_t)D.B * D.H, nc = cdiv(D.N, D.chunk), dvk = (int64_t)D.d_v * D.d_k;
+    const bool causal = D.mask == TTT_MASK_TOKEN_CAUSAL;
+    const int64_t chunk = lin_block(D);
+    const int64_t S = (int64_t)D.B * D.H, nc = cdiv(D.N, chunk), dvk = (int64_t)D.d_v * D.d_k;
     float* dS = (float*)ws;
     T* Sc = (T*)(ws + align256((size_t)(S * nc * dvk * 4)));
     float* Sout = a.Sout;
@@ -628,7 +734,7 @@ static ttt_status run_lin_parallel(const linattn_desc& D, LinArgs<T> a, char* ws
     da.N = D.N;
     da.dk = D.d_k;
     da.dv = D.d_v;
-    da.chunk = D.chunk;
+    da.chunk = (int)chunk;
     da.nc = (int)nc;
     da.ntv = (int)cdiv(D.d_v, kDeltaRows);
     da.ntk = (int)cdiv(D.d_k, kDeltaCols);
@@ -648,7 +754,7 @@ static ttt_status run_lin_parallel(const linattn_desc& D, LinArgs<T> a, char* ws
     sa.Sout = Sout;
     sa.dvk = dvk;
     sa.nc = (int)nc;
-    sa.mode = D.mask;
+    sa.mode = causal ? TTT_MASK_APPLY_THEN_UPDATE : D.mask;  // a causal block sees the state before it
     sa.nscan = (int)S;
     for (int w = 0; w < 32; ++w) sa.flags[w] = a.flags[w];
     {
@@ -664,16 +770,22 @@ static ttt_status run_lin_parallel(const linattn_desc& D, LinArgs<T> a, char* ws
     aa.N = D.N;
     aa.dk = D.d_k;
     aa.dv = D.d_v;
-    aa.chunk = D.chunk;
+    aa.chunk = (int)chunk;
     aa.nc = (int)nc;
-    aa.ntt = (int)cdiv(std::min<int64_t>(D.chunk, D.N), kApplyRows);
+    aa.ntt = (int)cdiv(std::min<int64_t>(chunk, D.N), kApplyRows);
     aa.ntv = (int)cdiv(D.d_v, kApplyCols);
     aa.nscan = (int)S;
+    aa.k = a.k;
+    aa.v = a.v;
+    aa.eta = a.eta;
     {
         ProfScope ps(PK_LIN_APPLY, st);
-        hipLaunchKernelGGL(k_lin_apply<T>, dim3((unsigned)(S * nc * aa.ntt * aa.ntv)), dim3(kThreads), 0, st, aa);
+        if (causal)  // one token tile per block
+            hipLaunchKernelGGL(k_lin_apply_causal<T>, dim3((unsigned)(S * nc * aa.ntv)), dim3(kThreads), 0, st, aa);
+        else
+            hipLaunchKernelGGL(k_lin_apply<T>, dim3((unsigned)(S * nc * aa.ntt * aa.ntv)), dim3(kThreads), 0, st, aa);
     }
-    return check_launch("k_lin_apply");
+    return check_launch(causal ? "k_lin_apply_causal" : "k_lin_apply");
 }
 
 }  // namespace ttt

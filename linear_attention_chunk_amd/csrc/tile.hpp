@@ -389,22 +389,23 @@ struct Tile {
     // stage is stored belongs to that stage, so the compiler's wait before the LDS store is exact
     // (with two sets its conservative count across the loop edge also waited for the newer set).
     template <class PM, bool FULL>
-    __device__ __forceinline__ void run_(const Opnd<T> (&A)[NA], const Opnd<T> (&B)[NB], int K, char* lds) {
+    __device__ __forceinline__ void run_(const Opnd<T> (&A)[NA], const Opnd<T> (&B)[NB], int K, char* lds,
+                                         bool keep = false) {
         if (K <= 0) {
-            zero();
+            if (!keep) zero();
             return;
         }
         Regs g;
         issue<FULL>(g, A, B, 0);
-        run_issued<PM, FULL>(g, A, B, K, lds);
+        run_issued<PM, FULL>(g, A, B, K, lds, keep);
     }
     // The same with stage 0 already issued into g (issue<FULL>(g, A, B, 0) with the same FULL), so
     // that a caller can start a tile's first loads early.  K must be positive.  On entry every wave
     // must be done reading the LDS stages.
     template <class PM, bool FULL>
     __device__ __forceinline__ void run_issued(Regs& g, const Opnd<T> (&A)[NA], const Opnd<T> (&B)[NB], int K,
-                                               char* lds) {
-        zero();
+                                               char* lds, bool keep = false) {
+        if (!keep) zero();
         const int nk = (K + KSTEP - 1) / KSTEP;
         if constexpr (NBUF == 1) {
             // one LDS stage: the loads of stage s + 1 are in flight while stage s is computed; the
@@ -435,9 +436,11 @@ struct Tile {
     }
     // Full tiles (the common case) take the unmasked path; the branch is uniform per workgroup.
     template <class PM>
-    __device__ __forceinline__ void run(const Opnd<T> (&A)[NA], const Opnd<T> (&B)[NB], int K, char* lds) {
-        if (full(A, B, K)) run_<PM, true>(A, B, K, lds);
-        else run_<PM, false>(A, B, K, lds);
+    // keep: add to the accumulators instead of starting from zero
+    __device__ __forceinline__ void run(const Opnd<T> (&A)[NA], const Opnd<T> (&B)[NB], int K, char* lds,
+                                        bool keep = false) {
+        if (full(A, B, K)) run_<PM, true>(A, B, K, lds, keep);
+        else run_<PM, false>(A, B, K, lds, keep);
     }
 
     template <class PM>

@@ -159,9 +159,14 @@ def test_linattn_workspace_choice_and_rejects():
     per = 2 * 3 * 4 * 128 * 64 * 4
     assert n.value == 2 * ((per + 255) // 256 * 256)
     need = n.value
-    for kw in (dict(mask=C.MASK_TOKEN_CAUSAL), dict(chunk=32)):
-        assert L.linattn_workspace_bytes(ctypes.byref(lin_desc(B=2, H=3, N=1000, d_k=128, d_v=64, **kw)),
-                                         ctypes.byref(n)) == C.TTT_OK and n.value == 0
+    for kw in (dict(mask=C.MASK_TOKEN_CAUSAL, N=200), dict(chunk=32)):
+        kw = dict(dict(B=2, H=3, N=1000, d_k=128, d_v=64), **kw)
+        assert L.linattn_workspace_bytes(ctypes.byref(lin_desc(**kw)), ctypes.byref(n)) == C.TTT_OK and n.value == 0
+    # token-causal mode from two 128-token blocks on: the same layout over ceil(N / 128) blocks
+    D2 = lin_desc(B=2, H=3, N=1000, d_k=128, d_v=64, mask=C.MASK_TOKEN_CAUSAL)
+    assert L.linattn_workspace_bytes(ctypes.byref(D2), ctypes.byref(n)) == C.TTT_OK
+    per2 = 2 * 3 * 8 * 128 * 64 * 4
+    assert n.value == 2 * ((per2 + 255) // 256 * 256)
     args = (P16, P16 + (1 << 30), P16 + (2 << 30), P16 + (3 << 30), None, P16B, None)
     assert L.linattn_forward(ctypes.byref(D), *args, None, 0, None) == C.TTT_ERR_WORKSPACE
     assert L.linattn_forward(ctypes.byref(D), *args, P16 + (1 << 34), need - 1, None) == C.TTT_ERR_WORKSPACE
@@ -174,10 +179,11 @@ def test_linattn_wide_keys_need_the_chunk_parallel_path():
     multiple of 32 up to 2048."""
     L = C.lib()
     n = ctypes.c_size_t(0)
-    D = lin_desc(B=1, H=2, N=4096, d_k=384, d_v=384, chunk=2048)
-    assert L.linattn_workspace_bytes(ctypes.byref(D), ctypes.byref(n)) == C.TTT_OK and n.value > 0
-    for kw in (dict(mask=C.MASK_TOKEN_CAUSAL), dict(chunk=64)):
-        D = lin_desc(B=1, H=2, N=4096, d_k=384, d_v=384, **kw)
+    for kw in (dict(chunk=2048), dict(mask=C.MASK_TOKEN_CAUSAL)):
+        D = lin_desc(**dict(dict(B=1, H=2, N=4096, d_k=384, d_v=384), **kw))
+        assert L.linattn_workspace_bytes(ctypes.byref(D), ctypes.byref(n)) == C.TTT_OK and n.value > 0
+    for kw in (dict(mask=C.MASK_TOKEN_CAUSAL, N=200), dict(chunk=64)):
+        D = lin_desc(**dict(dict(B=1, H=2, N=4096, d_k=384, d_v=384), **kw))
         assert L.linattn_workspace_bytes(ctypes.byref(D), ctypes.byref(n)) == C.TTT_ERR_UNSUPPORTED
         assert b"chunk-parallel" in L.ttt_last_error()
     for dk in (2080, 400):
