@@ -128,9 +128,10 @@ ttt_status ttt_forward(const ttt_desc* desc, const void* q, const void* k, const
 
 /*
  * Device workspace that linattn_forward needs, in bytes.  Zero when the call runs the sequential
- * kernel (token-causal mode, or chunks so small that 4 d_k d_v > 2 chunk (d_k + d_v)); otherwise
- * room for every chunk's own update and the state each chunk's queries see, 8 bytes per state
- * element per chunk and scan (the chunk-parallel path).
+ * kernel (chunks so small that 4 d_k d_v > 2 chunk (d_k + d_v), or token-causal mode with N < 256);
+ * otherwise room for every chunk's own update and the state each chunk's queries see, 8 bytes per
+ * state element per chunk and scan (the chunk-parallel path; token-causal mode counts chunks of
+ * 128 tokens).
  */
 ttt_status linattn_workspace_bytes(const linattn_desc* desc, size_t* bytes);
 
