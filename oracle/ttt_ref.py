@@ -22,6 +22,8 @@ Training"):
 * linear bias-free fast weight + GD = linear attention ........... TTT-as-LA, Thm. 5.2 and
                                                                    Sec. 6.1 Step 6; LA-to-TTT,
                                                                    "Causal Linear Attention"
+* several inner-loop gradient steps per chunk (inference time) ... TTT-as-LA, Sec. 4.1
+* gradient ascent in the inner loop: the step's sign flips ....... TTT-as-LA, Sec. 4.2 and 5.2
 
 Readings taken where the pages are silent or garbled (each is also listed in the design notes):
 
@@ -36,7 +38,10 @@ Readings taken where the pages are silent or garbled (each is also listed in the
   U / (||U||_F + 1e-7) and run on the side with the smaller Gram matrix;
 * eta sits inside the gradient sum (before Muon); the gradient is a sum (not a mean) over the
   chunk; momentum is per chunk with M0 = 0 and no dampening;
-* a partial last chunk (N not a multiple of the chunk) simply holds fewer tokens.
+* a partial last chunk (N not a multiple of the chunk) simply holds fewer tokens;
+* n inner steps on a chunk repeat the whole update n times, each from the gradient at the current
+  W (momentum and Muon included, one momentum step per inner step); ascent adds the gradient
+  instead of subtracting it, everything else unchanged.
 
 Parity status: every function here is pinned by the CPU tests (finite differences, closed forms
 of the linear and last-layer reductions, the SVD polar factor, invariants).  The full SwiGLU
@@ -147,12 +152,13 @@ def _weight_update(W, G, Mx, rule, ns_iters, momentum):
 
 
 def ttt_scan_ref(q, k, v, eta, W1, W3, W2, chunk, mask, rule, ns_iters=5, momentum=0.0,
-                 last_layer_only=False, update_chunks=None, M=None):
+                 last_layer_only=False, update_chunks=None, M=None, inner_steps=1, ascent=False):
     """One (batch, head) scan of the TTT-KVB layer.
 
     q, k, v [N, d]; eta [N]; W1, W3 [m, d]; W2 [d, m]; M optional (M1, M3, M2) momentum state.
     Returns (o [N, d], (W1, W3, W2), (M1, M3, M2)).  The apply/update order per chunk follows
-    LaCT notes section 1.1 and Eq. (10).
+    LaCT notes section 1.1 and Eq. (10).  An updating chunk takes ``inner_steps`` gradient steps
+    (TTT-as-LA Sec. 4.1); ``ascent`` steps along +g instead of -g (TTT-as-LA Sec. 4.2).
     """
     q, k, v, eta = _f64(q), _f64(k), _f64(v), _f64(eta)
     W = [_f64(W1).copy(), _f64(W3).copy(), _f64(W2).copy()]
@@ -175,17 +181,21 @@ def ttt_scan_ref(q, k, v, eta, W1, W3, W2, chunk, mask, rule, ns_iters=5, moment
         if apply_first:
             o[lo:hi] = swiglu_apply(W[0], W[1], W[2], q[lo:hi])
         if update:
-            G = chunk_gradients(W[0], W[1], W[2], k[lo:hi], v[lo:hi], eta[lo:hi])
-            which = (2,) if last_layer_only else (0, 1, 2)
-            for i in which:
-                W[i], Ms[i] = _weight_update(W[i], G[i], Ms[i], rule, ns_iters, momentum)
+            for _ in range(inner_steps):
+                G = chunk_gradients(W[0], W[1], W[2], k[lo:hi], v[lo:hi], eta[lo:hi])
+                if ascent:
+                    G = tuple(-g for g in G)
+                which = (2,) if last_layer_only else (0, 1, 2)
+                for i in which:
+                    W[i], Ms[i] = _weight_update(W[i], G[i], Ms[i], rule, ns_iters, momentum)
         if not apply_first:
             o[lo:hi] = swiglu_apply(W[0], W[1], W[2], q[lo:hi])
     return o, tuple(W), tuple(Ms)
 
 
 def ttt_forward_ref(q, k, v, eta, W1, W3, W2, chunk, mask, rule, ns_iters=5, momentum=0.0,
-                    last_layer_only=False, update_chunks=None, M=None, slices=None):
+                    last_layer_only=False, update_chunks=None, M=None, slices=None, inner_steps=1,
+                    ascent=False):
     """The TTT-KVB layer over [B, H, N, d] inputs; every (batch, head) scan is independent.
 
     W1, W3, W2 are per head ([H, ...]) or per (batch, head) ([B, H, ...]).  M, if given, is a
@@ -203,7 +213,8 @@ def ttt_forward_ref(q, k, v, eta, W1, W3, W2, chunk, mask, rule, ns_iters=5, mom
         ws = [x[h] if x.ndim == 3 else x[b, h] for x in (W1, W3, W2)]
         Mi = None if M is None else tuple(x[b, h] for x in M)
         ob, Wb, Mb = ttt_scan_ref(q[b, h], k[b, h], v[b, h], eta[b, h], *ws, chunk, mask, rule,
-                                  ns_iters, momentum, last_layer_only, update_chunks, Mi)
+                                  ns_iters, momentum, last_layer_only, update_chunks, Mi, inner_steps,
+                                  ascent)
         o[b, h] = ob
         for i in range(3):
             Wo[i][b, h] = Wb[i]

@@ -438,3 +438,57 @@ def test_eq1_intensity_table():
         g = json.load(f)
     for row in g["rows"]:
         assert abs(O.gemm_intensity(row["h"], row["b"]) - row["r"]) <= g["rounding"]
+
+
+# ----------------------------------------------------------------------------------------------
+# inner-loop variants: several gradient steps per chunk (TTT-as-LA Sec. 4.1) and gradient ascent
+# (TTT-as-LA Sec. 4.2; Sec. 5.2 states that ascent only flips the sign of the step, +eta for -eta)
+
+@pytest.mark.parametrize("rule,beta,last", [(O.UPD_GD, 0.0, False), (O.UPD_GD_L2, 0.0, False),
+                                            (O.UPD_MUON_L2, 0.9, False), (O.UPD_MUON, 0.5, True)])
+def test_ascent_is_descent_with_negated_eta(rule, beta, last):
+    """The chunk gradient is linear in eta and the Newton-Schulz polynomial is odd, so an ascent
+    step with eta is a descent step with -eta, for every rule, with momentum; exactly, since every
+    operation commutes with the sign."""
+    q, k, v, eta, W1, W3, W2 = tiny_problem(40, N=12)
+    for mask in (O.MASK_APPLY_THEN_UPDATE, O.MASK_UPDATE_THEN_APPLY):
+        oa, Wa, Ma = O.ttt_scan_ref(q, k, v, eta, W1, W3, W2, 4, mask, rule, 3, beta, last, ascent=True)
+        od, Wd, Md = O.ttt_scan_ref(q, k, v, -eta, W1, W3, W2, 4, mask, rule, 3, beta, last)
+        assert rel(oa, od) == 0.0
+        for a, b in zip(Wa + Ma, Wd + Md):
+            assert np.array_equal(a, b)
+        o_desc, W_desc, _ = O.ttt_scan_ref(q, k, v, eta, W1, W3, W2, 4, mask, rule, 3, beta, last)
+        assert rel(Wa[2], W_desc[2]) > 1e-3  # and it is not descent
+
+
+@pytest.mark.parametrize("rule,beta", [(O.UPD_GD, 0.0), (O.UPD_GD_L2, 0.0), (O.UPD_MUON_L2, 0.9)])
+def test_inner_steps_equal_repeated_chunks(rule, beta):
+    """n inner steps on one chunk take the path of n consecutive chunks that hold the same tokens,
+    one step each: every step's gradient is taken at the weights the previous step left (a step
+    that reused the first gradient, or a loop that ran once, would differ)."""
+    c = 4
+    q, k, v, eta, W1, W3, W2 = tiny_problem(41, N=c)
+    rep = lambda x, n: np.concatenate([x] * n)
+    for n in (2, 3):
+        _, Wi, Mi = O.ttt_scan_ref(q, k, v, eta, W1, W3, W2, c, O.MASK_UPDATE_THEN_APPLY, rule, 3, beta,
+                                   inner_steps=n)
+        _, Wr, Mr = O.ttt_scan_ref(rep(q, n), rep(k, n), rep(v, n), rep(eta, n), W1, W3, W2, c,
+                                   O.MASK_UPDATE_THEN_APPLY, rule, 3, beta)
+        for a, b in zip(Wi + Mi, Wr + Mr):
+            assert rel(a, b) < 1e-14
+        _, W1step, _ = O.ttt_scan_ref(q, k, v, eta, W1, W3, W2, c, O.MASK_UPDATE_THEN_APPLY, rule, 3, beta)
+        assert rel(Wi[2], W1step[2]) > 1e-4
+
+
+def test_last_layer_gd_inner_steps_scale_eta():
+    """With W2 alone updated under plain GD, its chunk gradient -sum_i eta_i v_i h(k_i)^T does not
+    depend on W2 (TTT-as-LA Thm. 5.1), so n inner steps are one step with n eta: a closed form.
+    The apply order is checked through the outputs of both orders."""
+    q, k, v, eta, W1, W3, W2 = tiny_problem(42, N=12)
+    for mask in (O.MASK_APPLY_THEN_UPDATE, O.MASK_UPDATE_THEN_APPLY):
+        on, Wn, _ = O.ttt_scan_ref(q, k, v, eta, W1, W3, W2, 4, mask, O.UPD_GD, last_layer_only=True,
+                                   inner_steps=3)
+        o1, W1s, _ = O.ttt_scan_ref(q, k, v, 3 * eta, W1, W3, W2, 4, mask, O.UPD_GD, last_layer_only=True)
+        assert rel(on, o1) < 1e-13
+        assert rel(Wn[2], W1s[2]) < 1e-13
+        assert rel(Wn[0], W1) == 0.0 and rel(Wn[1], W3) == 0.0
