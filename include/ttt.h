@@ -87,6 +87,11 @@ typedef struct ttt_desc {
     int32_t last_layer_only;  /* 1: only W2 is updated (paper Sec. 6.1 Step 1)                  */
     int32_t w0_per_batch;     /* 0: W0 is [H][3*d_h*m_h]; 1: W0 is [B][H][3*d_h*m_h]            */
     const uint8_t* update_chunks; /* host, ceil(N/chunk) flags; read only for TTT_MASK_STRIDED  */
+    int32_t inner_steps;      /* gradient steps per updating chunk, 0..64 (0 means 1), each from
+                                 the gradient at the current W ("TTT with KV Binding Is Secretly
+                                 Linear Attention", Sec. 4.1)                                   */
+    int32_t ascent;           /* 1: gradient ascent, W moves along +g instead of -g (same paper,
+                                 Sec. 4.2); 0: descent                                          */
 } ttt_desc;
 
 typedef struct linattn_desc {

@@ -33,6 +33,7 @@ class TttDesc(ctypes.Structure):
         ("io_dtype", c_int32), ("mask", c_int32), ("rule", c_int32),
         ("ns_iters", c_int32), ("momentum", c_float), ("last_layer_only", c_int32),
         ("w0_per_batch", c_int32), ("update_chunks", c_void_p),
+        ("inner_steps", c_int32), ("ascent", c_int32),
     ]
 
 

@@ -48,6 +48,7 @@ template <typename T> struct StepArgs {
     int64_t u0; int lu;                                   // update chunk
     int nQ, nK;                                           // up-kernel workgroups per scan
     int nG13, nG2, nO;                                    // down-kernel tiles per scan
+    float eta_sign;                                       // -1: gradient ascent
 };
 
 template <typename T> __device__ __forceinline__ int64_t panel_off(const StepArgs<T>& a, int t, int h) {
@@ -143,7 +144,7 @@ __global__ __launch_bounds__(64 * kUpWaves, 1) void k_up(StepArgs<T> a) {
                 const int i = idx / (TK1::FN * 16), j = (idx / 16) % TK1::FN, r = idx % 16;
                 if (!decltype(check)::value || (r0 + col < a.lu && c0 + row < a.m)) {
                     float hk, da, dc;
-                    bwd(tl.acc[0][i][j][r], tl.acc[1][i][j][r], tp.acc[0][i][j][r], eta[col], hk, da, dc);
+                    bwd(tl.acc[0][i][j][r], tl.acc[1][i][j][r], tp.acc[0][i][j][r], a.eta_sign * eta[col], hk, da, dc);
                     const uint32_t off = (uint32_t)row * (uint32_t)a.tp + (uint32_t)col;
                     HkE[off] = Elt<T>::st(hk);
                     DA[off] = Elt<T>::st(da);
@@ -681,6 +682,8 @@ static ttt_status validate(const ttt_desc* D) {
         return fail(TTT_ERR_INVALID_ARGUMENT, "momentum must be finite");
     if (D->last_layer_only != 0 && D->last_layer_only != 1) return fail(TTT_ERR_INVALID_ARGUMENT, "last_layer_only must be 0/1");
     if (D->w0_per_batch != 0 && D->w0_per_batch != 1) return fail(TTT_ERR_INVALID_ARGUMENT, "w0_per_batch must be 0/1");
+    if (D->inner_steps < 0 || D->inner_steps > 64) return fail(TTT_ERR_INVALID_ARGUMENT, "inner_steps must be in [0, 64]");
+    if (D->ascent != 0 && D->ascent != 1) return fail(TTT_ERR_INVALID_ARGUMENT, "ascent must be 0/1");
     const int64_t S = (int64_t)D->B * D->H;
     if (S > (1 << 20) || (int64_t)D->N > (1LL << 31) / 2) return fail(TTT_ERR_INVALID_ARGUMENT, "B*H or N too large");
     const int64_t bmax = D->N < D->chunk ? D->N : D->chunk;
@@ -726,88 +729,95 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
         int ja = uta ? step - 1 : step;
         int ju = step < nc ? step : -1;
         if (D.mask == TTT_MASK_STRIDED && ju >= 0 && !D.update_chunks[ju]) ju = -1;
-        StepArgs<T> a{};
-        a.q = q; a.k = k; a.v = v; a.eta = eta; a.o = o;
-        a.N = D.N; a.d = d; a.m = m;
-        a.Hq = (T*)(ws + L.hq); a.HkE = (T*)(ws + L.hke); a.DA = (T*)(ws + L.da); a.DC = (T*)(ws + L.dc);
-        a.inter_stride = L.inter_stride;
-        a.pan = bmax * kPanel;
-        a.tp = (int)(cdiv(bmax, 8) * 8);
-        a.sh = sh[cur]; a.sh_stride = L.sh_stride;
-        a.G = G; a.g_stride = L.g_stride;
-        a.a0 = ja >= 0 ? (int64_t)ja * D.chunk : 0;
-        a.la = ja >= 0 ? (int)(std::min<int64_t>((int64_t)(ja + 1) * D.chunk, D.N) - a.a0) : 0;
-        a.u0 = ju >= 0 ? (int64_t)ju * D.chunk : 0;
-        a.lu = ju >= 0 ? (int)(std::min<int64_t>((int64_t)(ju + 1) * D.chunk, D.N) - a.u0) : 0;
-        a.nQ = a.la ? (int)(cdiv(a.la, kUpQRows) * cdiv(m, kUpCols)) : 0;
-        a.nK = a.lu ? (int)(cdiv(a.lu, kUpKRows) * cdiv(m, kUpCols)) : 0;
-        a.nG13 = (a.lu && !D.last_layer_only) ? ntm * ntd : 0;
-        a.nG2 = a.lu ? ntd * (int)cdiv(m, 256) : 0;
-        a.nO = a.la ? (int)cdiv(a.la, kORows) * ntd : 0;
-        if (a.nQ + a.nK) {
-            {
-                ProfScope ps(PK_UP, st);
-                hipLaunchKernelGGL(k_up<T>, dim3(S * (a.nQ + a.nK)), dim3(64 * kUpWaves), 0, st, a);
-            }
-            if ((rc = check_launch("k_up")) != TTT_OK) return rc;
-        }
-        if (a.nG13 + a.nG2 + a.nO) {
-            {
-                ProfScope ps(PK_DOWN, st);
-                hipLaunchKernelGGL(k_down<T>, dim3(S * (a.nG13 + a.nG2 + a.nO)), dim3(kThreads), 0, st, a);
-            }
-            if ((rc = check_launch("k_down")) != TTT_OK) return rc;
-        }
-        if (a.lu == 0) continue;
-        const int mat0 = D.last_layer_only ? 2 : 0, nmat = D.last_layer_only ? 1 : 3;
-        const float* U = G;
-        if (muon || mom) {
-            PrepArgs pa{G, L.g_stride, M, 3 * dm, D.momentum, part, L.nblk, dm, mat0, nmat};
-            {
-                ProfScope ps(PK_MUON_PREP, st);
-                hipLaunchKernelGGL(k_muon_prep, dim3(S * nmat * L.nblk), dim3(kThreads), 0, st, pa);
-            }
-            if ((rc = check_launch("k_muon_prep")) != TTT_OK) return rc;
-            if (mom) U = M;
-        }
-        if (muon) {
-            T* Xb[2] = {(T*)(ws + L.xb[0]), (T*)(ws + L.xb[1])};
-            float* Xf = (float*)(ws + L.xf);
-            NSArgs<T> na{U, 3 * dm, part, L.nblk, Xf, L.x_stride, Xb[1], Xb[0], (T*)(ws + L.gram), L.gram_stride,
-                         d, m, mat0, nmat, 0};
-            {
-                ProfScope ps(PK_NS_INIT, st);
-                hipLaunchKernelGGL(k_ns_init<T>, dim3(S * nmat * L.nblk), dim3(kThreads), 0, st, na);
-            }
-            if ((rc = check_launch("k_ns_init")) != TTT_OK) return rc;
-            const int p = d < m ? d : m;
-            const int gt = (int)(cdiv(p, 128) * (cdiv(p, 128) + 1) / 2);  // upper-triangle Gram tiles
-            // step tiles: the larger of the tall (m x d) and wide (d x m) tilings
-            const int stt = (int)std::max(cdiv(m, kNSStepRows) * cdiv(d, kNSStepCols),
-                                          cdiv(d, kNSStepRows) * cdiv(m, kNSStepCols));
-            for (int it = 0; it < D.ns_iters; ++it) {
-                na.Xin = Xb[it & 1];
-                na.Xout = Xb[(it + 1) & 1];
-                na.tiles = gt;
+        // an updating chunk takes inner_steps gradient steps, each from the gradient at the current
+        // W; the chunk's apply (queries and outputs) runs once, with the first of them
+        const int nin = ju >= 0 ? std::max(1, D.inner_steps) : 1;
+        for (int it = 0; it < nin; ++it) {
+            if (it > 0) ja = -1;
+            StepArgs<T> a{};
+            a.q = q; a.k = k; a.v = v; a.eta = eta; a.o = o;
+            a.N = D.N; a.d = d; a.m = m;
+            a.Hq = (T*)(ws + L.hq); a.HkE = (T*)(ws + L.hke); a.DA = (T*)(ws + L.da); a.DC = (T*)(ws + L.dc);
+            a.inter_stride = L.inter_stride;
+            a.pan = bmax * kPanel;
+            a.tp = (int)(cdiv(bmax, 8) * 8);
+            a.sh = sh[cur]; a.sh_stride = L.sh_stride;
+            a.G = G; a.g_stride = L.g_stride;
+            a.eta_sign = D.ascent ? -1.0f : 1.0f;
+            a.a0 = ja >= 0 ? (int64_t)ja * D.chunk : 0;
+            a.la = ja >= 0 ? (int)(std::min<int64_t>((int64_t)(ja + 1) * D.chunk, D.N) - a.a0) : 0;
+            a.u0 = ju >= 0 ? (int64_t)ju * D.chunk : 0;
+            a.lu = ju >= 0 ? (int)(std::min<int64_t>((int64_t)(ju + 1) * D.chunk, D.N) - a.u0) : 0;
+            a.nQ = a.la ? (int)(cdiv(a.la, kUpQRows) * cdiv(m, kUpCols)) : 0;
+            a.nK = a.lu ? (int)(cdiv(a.lu, kUpKRows) * cdiv(m, kUpCols)) : 0;
+            a.nG13 = (a.lu && !D.last_layer_only) ? ntm * ntd : 0;
+            a.nG2 = a.lu ? ntd * (int)cdiv(m, 256) : 0;
+            a.nO = a.la ? (int)cdiv(a.la, kORows) * ntd : 0;
+            if (a.nQ + a.nK) {
                 {
-                    ProfScope ps(PK_NS_GRAM, st);
-                    hipLaunchKernelGGL(k_ns_gram<T>, dim3(S * nmat * gt), dim3(kThreads), 0, st, na);
+                    ProfScope ps(PK_UP, st);
+                    hipLaunchKernelGGL(k_up<T>, dim3(S * (a.nQ + a.nK)), dim3(64 * kUpWaves), 0, st, a);
                 }
-                if ((rc = check_launch("k_ns_gram")) != TTT_OK) return rc;
-                na.tiles = stt;
-                {
-                    ProfScope ps(PK_NS_STEP, st);
-                    hipLaunchKernelGGL(k_ns_step<T>, dim3(S * nmat * stt), dim3(kThreads), 0, st, na);
-                }
-                if ((rc = check_launch("k_ns_step")) != TTT_OK) return rc;
+                if ((rc = check_launch("k_up")) != TTT_OK) return rc;
             }
-            U = Xf;
+            if (a.nG13 + a.nG2 + a.nO) {
+                {
+                    ProfScope ps(PK_DOWN, st);
+                    hipLaunchKernelGGL(k_down<T>, dim3(S * (a.nG13 + a.nG2 + a.nO)), dim3(kThreads), 0, st, a);
+                }
+                if ((rc = check_launch("k_down")) != TTT_OK) return rc;
+            }
+            if (a.lu == 0) continue;
+            const int mat0 = D.last_layer_only ? 2 : 0, nmat = D.last_layer_only ? 1 : 3;
+            const float* U = G;
+            if (muon || mom) {
+                PrepArgs pa{G, L.g_stride, M, 3 * dm, D.momentum, part, L.nblk, dm, mat0, nmat};
+                {
+                    ProfScope ps(PK_MUON_PREP, st);
+                    hipLaunchKernelGGL(k_muon_prep, dim3(S * nmat * L.nblk), dim3(kThreads), 0, st, pa);
+                }
+                if ((rc = check_launch("k_muon_prep")) != TTT_OK) return rc;
+                if (mom) U = M;
+            }
+            if (muon) {
+                T* Xb[2] = {(T*)(ws + L.xb[0]), (T*)(ws + L.xb[1])};
+                float* Xf = (float*)(ws + L.xf);
+                NSArgs<T> na{U, 3 * dm, part, L.nblk, Xf, L.x_stride, Xb[1], Xb[0], (T*)(ws + L.gram), L.gram_stride,
+                             d, m, mat0, nmat, 0};
+                {
+                    ProfScope ps(PK_NS_INIT, st);
+                    hipLaunchKernelGGL(k_ns_init<T>, dim3(S * nmat * L.nblk), dim3(kThreads), 0, st, na);
+                }
+                if ((rc = check_launch("k_ns_init")) != TTT_OK) return rc;
+                const int p = d < m ? d : m;
+                const int gt = (int)(cdiv(p, 128) * (cdiv(p, 128) + 1) / 2);  // upper-triangle Gram tiles
+                // step tiles: the larger of the tall (m x d) and wide (d x m) tilings
+                const int stt = (int)std::max(cdiv(m, kNSStepRows) * cdiv(d, kNSStepCols),
+                                              cdiv(d, kNSStepRows) * cdiv(m, kNSStepCols));
+                for (int it = 0; it < D.ns_iters; ++it) {
+                    na.Xin = Xb[it & 1];
+                    na.Xout = Xb[(it + 1) & 1];
+                    na.tiles = gt;
+                    {
+                        ProfScope ps(PK_NS_GRAM, st);
+                        hipLaunchKernelGGL(k_ns_gram<T>, dim3(S * nmat * gt), dim3(kThreads), 0, st, na);
+                    }
+                    if ((rc = check_launch("k_ns_gram")) != TTT_OK) return rc;
+                    na.tiles = stt;
+                    {
+                        ProfScope ps(PK_NS_STEP, st);
+                        hipLaunchKernelGGL(k_ns_step<T>, dim3(S * nmat * stt), dim3(kThreads), 0, st, na);
+                    }
+                    if ((rc = check_launch("k_ns_step")) != TTT_OK) return rc;
+                }
+                U = Xf;
+            }
+            const int norm = (D.rule == TTT_UPD_GD_L2 || D.rule == TTT_UPD_MUON_L2) ? 1 : 0;
+            UpdArgs<T> u{Wf[cur], L.wf_stride, 0, D.H, U, 3 * dm, Wf[cur ^ 1], L.wf_stride, sh[cur ^ 1], L.sh_stride,
+                         d, m, norm, D.last_layer_only};
+            if ((rc = launch_update<T>(u, S * upd_blocks, st)) != TTT_OK) return rc;
+            cur ^= 1;
         }
-        const int norm = (D.rule == TTT_UPD_GD_L2 || D.rule == TTT_UPD_MUON_L2) ? 1 : 0;
-        UpdArgs<T> u{Wf[cur], L.wf_stride, 0, D.H, U, 3 * dm, Wf[cur ^ 1], L.wf_stride, sh[cur ^ 1], L.sh_stride,
-                     d, m, norm, D.last_layer_only};
-        if ((rc = launch_update<T>(u, S * upd_blocks, st)) != TTT_OK) return rc;
-        cur ^= 1;
     }
     if (W_out) {
         hipError_t e = hipMemcpyAsync(W_out, Wf[cur], (size_t)S * 3 * dm * 4, hipMemcpyDeviceToDevice, st);

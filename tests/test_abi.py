@@ -71,6 +71,9 @@ def ws_bytes(D):
     (dict(mask=C.MASK_STRIDED), C.TTT_ERR_INVALID_ARGUMENT),
     (dict(rule=4), C.TTT_ERR_INVALID_ARGUMENT),
     (dict(ns_iters=-1), C.TTT_ERR_INVALID_ARGUMENT),
+    (dict(inner_steps=65), C.TTT_ERR_INVALID_ARGUMENT),
+    (dict(inner_steps=-1), C.TTT_ERR_INVALID_ARGUMENT),
+    (dict(ascent=2), C.TTT_ERR_INVALID_ARGUMENT),
     (dict(momentum=float("nan")), C.TTT_ERR_INVALID_ARGUMENT),
     (dict(last_layer_only=2), C.TTT_ERR_INVALID_ARGUMENT),
 ])

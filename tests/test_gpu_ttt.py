@@ -40,13 +40,16 @@ def check(o_gpu, W_gpu, o_ref, W_ref, d, m, tol, slices=None, label=""):
     assert ew <= tol, f"W_out rel L2 {ew} > {tol}"
 
 
-def run_small(seed, B, H, N, d, m, chunk, mask, rule, bf16, momentum=0.0, last=False, flags=None, ns=5):
-    say(f"ttt case B{B} H{H} N{N} d{d} m{m} b{chunk} mask{mask} rule{rule} mom{momentum} last{last} bf16={bf16}")
+def run_small(seed, B, H, N, d, m, chunk, mask, rule, bf16, momentum=0.0, last=False, flags=None, ns=5, inner=1,
+              ascent=False):
+    say(f"ttt case B{B} H{H} N{N} d{d} m{m} b{chunk} mask{mask} rule{rule} mom{momentum} last{last} bf16={bf16}"
+        f" inner{inner} ascent{ascent}")
     (q, k, v, eta, W0), (hq, hk, hv, he, W1, W3, W2) = full_ttt_inputs(seed, B, H, N, d, m, bf16)
     o, Wout = T.ttt_forward(q, k, v, eta, W0, chunk, mask, rule, m_h=m, ns_iters=ns, momentum=momentum,
-                            last_layer_only=last, update_chunks=flags)
+                            last_layer_only=last, update_chunks=flags, inner_steps=inner, ascent=ascent)
     torch.cuda.synchronize()
-    o_ref, W_ref, _ = O.ttt_forward_ref(hq, hk, hv, he, W1, W3, W2, chunk, mask, rule, ns, momentum, last, flags)
+    o_ref, W_ref, _ = O.ttt_forward_ref(hq, hk, hv, he, W1, W3, W2, chunk, mask, rule, ns, momentum, last, flags,
+                                        inner_steps=inner, ascent=ascent)
     check(o, Wout, o_ref, W_ref, d, m, TOL[bf16], label="all slices")
 
 
@@ -102,6 +105,28 @@ def test_muon_gram_mirror_fp32():
     # also writes its mirror block; both Gram sides (m > d, then d > m)
     run_small(12, 1, 1, 256, 160, 320, 128, O.MASK_APPLY_THEN_UPDATE, O.UPD_MUON_L2, False, ns=3)
     run_small(13, 1, 1, 256, 320, 160, 128, O.MASK_UPDATE_THEN_APPLY, O.UPD_MUON, False, ns=2)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_inner_steps_and_ascent(bf16):
+    # several gradient steps per updating chunk, and gradient ascent, against the oracle; N = 300
+    # leaves a ragged last chunk
+    run_small(14, 1, 2, 300, 64, 128, 128, O.MASK_APPLY_THEN_UPDATE, O.UPD_GD_L2, bf16, inner=3)
+    run_small(15, 1, 1, 300, 64, 128, 128, O.MASK_UPDATE_THEN_APPLY, O.UPD_MUON_L2, bf16, momentum=0.9, inner=2,
+              ascent=True, ns=3)
+    run_small(16, 1, 1, 256, 64, 64, 64, O.MASK_STRIDED, O.UPD_GD, bf16, last=True, flags=[1, 0, 1, 1],
+              ascent=True, inner=2)
+
+
+def test_ascent_is_descent_with_negated_eta():
+    """The pages reduce gradient ascent to a sign flip of the step: the library's ascent must give
+    the bits that descent gives with -eta."""
+    (q, k, v, eta, W0), _ = full_ttt_inputs(17, 1, 2, 300, 64, 128, True)
+    kw = dict(m_h=128, momentum=0.9, ns_iters=3, inner_steps=2)
+    oa, Wa = T.ttt_forward(q, k, v, eta, W0, 128, O.MASK_APPLY_THEN_UPDATE, O.UPD_MUON_L2, ascent=True, **kw)
+    od, Wd = T.ttt_forward(q, k, v, (-eta).contiguous(), W0, 128, O.MASK_APPLY_THEN_UPDATE, O.UPD_MUON_L2, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(oa, od) and torch.equal(Wa, Wd)
 
 
 def test_zero_tokens_returns_w0():
