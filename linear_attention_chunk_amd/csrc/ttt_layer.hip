@@ -32,16 +32,18 @@ constexpr int kPanel = 1 << kPanelShift;
 // Chunk intermediates of one scan.  Hq (read by the output GEMM, which contracts over hidden
 // units) is token-major in panels: hidden unit h of token t is element (h / 64) * pan + t * 64 +
 // h % 64, with pan = 64 x (chunk capacity), so a query tile writes one contiguous block.  HkE, DA
-// and DC (read by the gradient GEMMs, which contract over tokens) are hidden-major: element
-// h * tp + t, tp = chunk capacity rounded up to 8.  In the MFMA result layout each lane holds 4
-// consecutive tokens of one hidden unit, so the key tiles store them 4 at a time, and the
-// gradient GEMMs read them k-contiguous.
+// and DC (read by the gradient GEMMs, which contract over tokens) are hidden-major in blocks of
+// kHB hidden units x kTB tokens: element ((h / kHB) * ntb + t / kTB) * kHB * kTB + (h % kHB) * kTB +
+// t % kTB, with ntb token blocks per chunk capacity.  A gradient tile's k-step (128 or 256 hidden
+// units x 64 tokens) is then one contiguous 16 or 32 KB piece, where rows a chunk apart would
+// each open their own DRAM page, and a key tile writes contiguous 16 KB pieces.
+constexpr int kHB = 256, kTB = 64, kTBShift = 6, kBlk = kHB * kTB;
 template <typename T> struct StepArgs {
     const T* q; const T* k; const T* v; const float* eta; T* o;
     int64_t N; int d, m;
     T* Hq; T* HkE; T* DA; T* DC; int64_t inter_stride;  // per-scan intermediates
     int64_t pan;                                          // Hq panel stride (elements)
-    int tp;                                               // HkE / DA / DC row pitch (elements)
+    int ntb;                                              // HkE / DA / DC token blocks per chunk
     const T* sh; int64_t sh_stride;                       // shadows [W1 | W3 | W2 | W2^T]
     float* G; int64_t g_stride;                           // [G1 | G3 | G2] fp32
     int64_t a0; int la;                                   // apply chunk: first token, length
@@ -125,9 +127,13 @@ __global__ __launch_bounds__(64 * kUpWaves, 1) void k_up(StepArgs<T> a) {
         if (f2) tp.template run_issued<PM1, true>(g2, A2, B2, a.d, smem);
         else tp.template run<PM1>(A2, B2, a.d, smem);
         const float* eta = a.eta + tok;
-        T* HkE = a.HkE + ioff + (int64_t)c0 * a.tp + r0;
-        T* DA = a.DA + ioff + (int64_t)c0 * a.tp + r0;
-        T* DC = a.DC + ioff + (int64_t)c0 * a.tp + r0;
+        // the tile's hidden units lie in one block (c0 % kHB is 0 or 128) and its tokens start a
+        // token block (r0 % kTB == 0)
+        static_assert(kHB % kUpCols == 0 && kUpKRows % kTB == 0, "key tiles must align with the blocks");
+        const int64_t boff = ioff + ((int64_t)(c0 / kHB) * a.ntb + r0 / kTB) * kBlk + (int64_t)(c0 % kHB) * kTB;
+        T* HkE = a.HkE + boff;
+        T* DA = a.DA + boff;
+        T* DC = a.DC + boff;
         // SwiGLU backward at one (token, hidden unit): x = (K W1^T), c = (K W3^T), p = (V W2) there
         auto bwd = [](float x, float c, float p, float e, float& hk, float& da, float& dc) {
             const float sg = sigmoidf_(x), xs = x * sg;
@@ -145,7 +151,7 @@ __global__ __launch_bounds__(64 * kUpWaves, 1) void k_up(StepArgs<T> a) {
                 if (!decltype(check)::value || (r0 + col < a.lu && c0 + row < a.m)) {
                     float hk, da, dc;
                     bwd(tl.acc[0][i][j][r], tl.acc[1][i][j][r], tp.acc[0][i][j][r], a.eta_sign * eta[col], hk, da, dc);
-                    const uint32_t off = (uint32_t)row * (uint32_t)a.tp + (uint32_t)col;
+                    const uint32_t off = (uint32_t)(col >> kTBShift) * kBlk + (uint32_t)row * kTB + (uint32_t)(col & (kTB - 1));
                     HkE[off] = Elt<T>::st(hk);
                     DA[off] = Elt<T>::st(da);
                     DC[off] = Elt<T>::st(dc);
@@ -198,8 +204,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_down(StepArgs<T> a) {
     if (t < a.nG13) {  // G1 = DA^T K and G3 = DC^T K: rows c of m, cols e of d
         const int r0 = (t / ndt) * 128, c0 = (t % ndt) * 128;
         const T* K = a.k + ((int64_t)s * a.N + a.u0) * a.d;
-        const int64_t hoff = ioff + (int64_t)r0 * a.tp;
-        const Opnd<T> A[2] = {{a.DA + hoff, a.tp, a.m - r0, a.lu}, {a.DC + hoff, a.tp, a.m - r0, a.lu}};
+        // rows r0 .. r0 + 127 lie in one hidden block; k (tokens) runs through its token blocks
+        const int64_t hoff = ioff + (int64_t)(r0 / kHB) * a.ntb * kBlk + (int64_t)(r0 % kHB) * kTB;
+        const Opnd<T> A[2] = {{a.DA + hoff, kTB, a.m - r0, a.lu, kTBShift, kBlk},
+                              {a.DC + hoff, kTB, a.m - r0, a.lu, kTBShift, kBlk}};
         const Opnd<T> B[1] = {{K + c0, a.d, a.d - c0, a.lu}};
         TG13 tl;
         tl.template run<PMG>(A, B, a.lu, smem);
@@ -224,7 +232,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_down(StepArgs<T> a) {
         const int r0 = (t / nmt2) * 128, c0 = (t % nmt2) * 256;
         const T* V = a.v + ((int64_t)s * a.N + a.u0) * a.d;
         const Opnd<T> A[1] = {{V + r0, a.d, a.d - r0, a.lu}};
-        const Opnd<T> B[1] = {{a.HkE + ioff + (int64_t)c0 * a.tp, a.tp, a.m - c0, a.lu}};
+        static_assert(TG2::BN == kHB, "a G2 tile covers one hidden block");
+        const Opnd<T> B[1] = {{a.HkE + ioff + (int64_t)(c0 / kHB) * a.ntb * kBlk, kTB, a.m - c0, a.lu, kTBShift, kBlk}};
         TG2 tl;
         tl.template run<PM1>(A, B, a.lu, smem);
         float* G2 = a.G + s * a.g_stride + 2 * dm + (int64_t)r0 * a.m + c0;
@@ -632,7 +641,7 @@ static Layout make_layout(const ttt_desc& D, bool muon, bool own_m) {
     const int64_t p = d < m ? d : m;
     L.wf_stride = 3 * dm;
     L.sh_stride = 4 * dm;
-    L.inter_stride = std::max<int64_t>(bmax * cdiv(m, kPanel) * kPanel, m * cdiv(bmax, 8) * 8);  // see StepArgs
+    L.inter_stride = std::max<int64_t>(bmax * cdiv(m, kPanel) * kPanel, cdiv(m, kHB) * kBlk * cdiv(bmax, kTB));  // see StepArgs
     L.g_stride = 3 * dm;
     L.x_stride = 3 * dm;
     L.gram_stride = 3 * p * p;
@@ -687,7 +696,7 @@ static ttt_status validate(const ttt_desc* D) {
     const int64_t S = (int64_t)D->B * D->H;
     if (S > (1 << 20) || (int64_t)D->N > (1LL << 31) / 2) return fail(TTT_ERR_INVALID_ARGUMENT, "B*H or N too large");
     const int64_t bmax = D->N < D->chunk ? D->N : D->chunk;
-    if ((int64_t)D->m_h * ((bmax + 7) / 8 * 8) >= (1LL << 31))
+    if (cdiv(D->m_h, kHB) * kBlk * cdiv(bmax, kTB) >= (1LL << 31))
         return fail(TTT_ERR_UNSUPPORTED, "m_h x chunk must stay below 2^31 elements");
     return TTT_OK;
 }
@@ -740,7 +749,7 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
             a.Hq = (T*)(ws + L.hq); a.HkE = (T*)(ws + L.hke); a.DA = (T*)(ws + L.da); a.DC = (T*)(ws + L.dc);
             a.inter_stride = L.inter_stride;
             a.pan = bmax * kPanel;
-            a.tp = (int)(cdiv(bmax, 8) * 8);
+            a.ntb = (int)cdiv(bmax, kTB);
             a.sh = sh[cur]; a.sh_stride = L.sh_stride;
             a.G = G; a.g_stride = L.g_stride;
             a.eta_sign = D.ascent ? -1.0f : 1.0f;
