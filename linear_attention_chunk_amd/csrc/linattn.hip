@@ -544,7 +544,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_lin_apply(ApplyArgs<T> a) {
 constexpr int kCausalBlock = 128;
 
 template <typename T>
-__global__ __launch_bounds__(kThreads, 2) void k_lin_apply_causal(ApplyArgs<T> a) {
+__global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void k_lin_apply_causal(ApplyArgs<T> a) {  // fp32: 147 KB LDS
     constexpr int PLANES = sizeof(T) == 2 ? 2 : 1;
     using TP = Tile<T, kCausalBlock, kCausalBlock, 1, 2, 1, 1, 1, false, false>;  // q k^T
     using TD = Tile<T, kCausalBlock, kApplyCols, 2, 2, 1, 1, 1, false, true>;     // P v, P in LDS
