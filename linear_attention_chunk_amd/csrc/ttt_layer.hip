@@ -51,6 +51,8 @@ template <typename T> struct StepArgs {
     int nQ, nK;                                           // up-kernel workgroups per scan
     int nG13, nG2, nO;                                    // down-kernel tiles per scan
     float eta_sign;                                       // -1: gradient ascent
+    int ksplit, kpart;                                    // gradient tiles: token parts, tokens per part
+    int64_t gpart_stride;                                 // elements between partial-G buffers
 };
 
 template <typename T> __device__ __forceinline__ int64_t panel_off(const StepArgs<T>& a, int t, int h) {
@@ -201,18 +203,23 @@ __global__ __launch_bounds__(kThreads, 2) void k_down(StepArgs<T> a) {
     const int64_t dm = (int64_t)a.d * a.m;
     const int ndt = (a.d + 127) / 128, nmt2 = (a.m + 255) / 256;
     const int64_t ioff = s * a.inter_stride;
+    // With few scans the gradient tiles are split over the chunk's tokens: part p takes tokens
+    // [p kpart, (p + 1) kpart) and writes partial-G buffer p; a reduction sums the parts.
     if (t < a.nG13) {  // G1 = DA^T K and G3 = DC^T K: rows c of m, cols e of d
+        const int per13 = a.nG13 / a.ksplit, part = t / per13;
+        t %= per13;
+        const int k0 = part * a.kpart, kl = min(a.kpart, a.lu - k0);
         const int r0 = (t / ndt) * 128, c0 = (t % ndt) * 128;
-        const T* K = a.k + ((int64_t)s * a.N + a.u0) * a.d;
+        const T* K = a.k + ((int64_t)s * a.N + a.u0 + k0) * a.d;
         // rows r0 .. r0 + 127 lie in one hidden block; k (tokens) runs through its token blocks
-        const int64_t hoff = ioff + (int64_t)(r0 / kHB) * a.ntb * kBlk + (int64_t)(r0 % kHB) * kTB;
-        const Opnd<T> A[2] = {{a.DA + hoff, kTB, a.m - r0, a.lu, kTBShift, kBlk},
-                              {a.DC + hoff, kTB, a.m - r0, a.lu, kTBShift, kBlk}};
-        const Opnd<T> B[1] = {{K + c0, a.d, a.d - c0, a.lu}};
+        const int64_t hoff = ioff + ((int64_t)(r0 / kHB) * a.ntb + (k0 >> kTBShift)) * kBlk + (int64_t)(r0 % kHB) * kTB;
+        const Opnd<T> A[2] = {{a.DA + hoff, kTB, a.m - r0, kl, kTBShift, kBlk},
+                              {a.DC + hoff, kTB, a.m - r0, kl, kTBShift, kBlk}};
+        const Opnd<T> B[1] = {{K + c0, a.d, a.d - c0, kl}};
         TG13 tl;
-        tl.template run<PMG>(A, B, a.lu, smem);
+        tl.template run<PMG>(A, B, kl, smem);
         // stores go through 32-bit offsets from the tile corner; full tiles skip the bounds checks
-        float* G1 = a.G + s * a.g_stride + (int64_t)r0 * a.d + c0;
+        float* G1 = a.G + part * a.gpart_stride + s * a.g_stride + (int64_t)r0 * a.d + c0;
         float* G3 = G1 + dm;
         auto epi = [&](auto check) {
             tl.for_each([&](const float (&v)[2], int row, int col) {
@@ -229,14 +236,18 @@ __global__ __launch_bounds__(kThreads, 2) void k_down(StepArgs<T> a) {
     }
     t -= a.nG13;
     if (t < a.nG2) {  // G2 = V^T HkE: rows e of d, cols c of m
+        const int per2 = a.nG2 / a.ksplit, part = t / per2;
+        t %= per2;
+        const int k0 = part * a.kpart, kl = min(a.kpart, a.lu - k0);
         const int r0 = (t / nmt2) * 128, c0 = (t % nmt2) * 256;
-        const T* V = a.v + ((int64_t)s * a.N + a.u0) * a.d;
-        const Opnd<T> A[1] = {{V + r0, a.d, a.d - r0, a.lu}};
+        const T* V = a.v + ((int64_t)s * a.N + a.u0 + k0) * a.d;
+        const Opnd<T> A[1] = {{V + r0, a.d, a.d - r0, kl}};
         static_assert(TG2::BN == kHB, "a G2 tile covers one hidden block");
-        const Opnd<T> B[1] = {{a.HkE + ioff + (int64_t)(c0 / kHB) * a.ntb * kBlk, kTB, a.m - c0, a.lu, kTBShift, kBlk}};
+        const Opnd<T> B[1] = {{a.HkE + ioff + ((int64_t)(c0 / kHB) * a.ntb + (k0 >> kTBShift)) * kBlk, kTB, a.m - c0, kl,
+                               kTBShift, kBlk}};
         TG2 tl;
-        tl.template run<PM1>(A, B, a.lu, smem);
-        float* G2 = a.G + s * a.g_stride + 2 * dm + (int64_t)r0 * a.m + c0;
+        tl.template run<PM1>(A, B, kl, smem);
+        float* G2 = a.G + part * a.gpart_stride + s * a.g_stride + 2 * dm + (int64_t)r0 * a.m + c0;
         auto epi = [&](auto check) {
             tl.for_each([&](const float (&v)[1], int row, int col) {
                 if (!decltype(check)::value || (r0 + row < a.d && c0 + col < a.m))
@@ -627,10 +638,39 @@ __global__ __launch_bounds__(kThreads, 2) void k_ns_step(NSArgs<T> a) {
 // ---------------------------------------------------------------------------------------------
 // host driver
 
+// Sum of the partial-G buffers into the first: n float4 per buffer, parts buffers gstride apart,
+// added in buffer order (deterministic).
+__global__ __launch_bounds__(kThreads) void k_gsum(float* G, int64_t n4, int parts, int64_t gstride) {
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= n4) return;
+    float4* g = reinterpret_cast<float4*>(G) + i;
+    float4 acc = *g;
+    for (int p = 1; p < parts; ++p) {
+        const float4 x = *reinterpret_cast<const float4*>(G + p * gstride + 4 * i);
+        acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+    }
+    *g = acc;
+}
+
+// Token parts for the gradient tiles of a step over lu tokens: the largest power of two up to 8
+// that keeps the launch at most 512 gradient workgroups (two per CU on 256 CUs) and every part at
+// least 512 tokens, which also keeps every part non-empty.  Depends on the descriptor only.
+// gradient tiles per scan and step: G1/G3 (unless only W2 learns) and G2
+static int grad_tiles(const ttt_desc& D) {
+    const int64_t d = D.d_h, m = D.m_h;
+    return (int)((D.last_layer_only ? 0 : cdiv(m, 128) * cdiv(d, 128)) + cdiv(d, 128) * cdiv(m, 256));
+}
+
+static int grad_split(int64_t S, int gtiles, int64_t lu) {
+    int p = 1;
+    while (p < 8 && S * gtiles * (2 * p) <= 512 && lu >= 512 * (2 * p)) p *= 2;
+    return p;
+}
+
 struct Layout {
     size_t wf[2], sh[2], hq, hke, da, dc, g, xf, xb[2], gram, part, mom, total;
     int64_t wf_stride, sh_stride, inter_stride, g_stride, x_stride, gram_stride;
-    int nblk;
+    int nblk, gparts;
 };
 
 static Layout make_layout(const ttt_desc& D, bool muon, bool own_m) {
@@ -656,7 +696,8 @@ static Layout make_layout(const ttt_desc& D, bool muon, bool own_m) {
     L.hke = take(S * L.inter_stride * es);
     L.da = take(S * L.inter_stride * es);
     L.dc = take(S * L.inter_stride * es);
-    L.g = take(S * L.g_stride * 4);
+    L.gparts = grad_split(S, grad_tiles(D), bmax);  // partial-G buffers for the longest chunk
+    L.g = take(S * L.g_stride * 4 * L.gparts);
     L.part = take(S * 3 * (size_t)L.nblk * 4);
     if (muon) {
         L.xf = take(S * L.x_stride * 4);
@@ -759,8 +800,11 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
             a.lu = ju >= 0 ? (int)(std::min<int64_t>((int64_t)(ju + 1) * D.chunk, D.N) - a.u0) : 0;
             a.nQ = a.la ? (int)(cdiv(a.la, kUpQRows) * cdiv(m, kUpCols)) : 0;
             a.nK = a.lu ? (int)(cdiv(a.lu, kUpKRows) * cdiv(m, kUpCols)) : 0;
-            a.nG13 = (a.lu && !D.last_layer_only) ? ntm * ntd : 0;
-            a.nG2 = a.lu ? ntd * (int)cdiv(m, 256) : 0;
+            a.ksplit = a.lu ? grad_split(S, grad_tiles(D), a.lu) : 1;  // <= L.gparts: lu <= bmax
+            a.kpart = (int)(cdiv(cdiv(a.lu, a.ksplit), kTB) * kTB);
+            a.gpart_stride = (int64_t)S * L.g_stride;
+            a.nG13 = (a.lu && !D.last_layer_only) ? ntm * ntd * a.ksplit : 0;
+            a.nG2 = a.lu ? ntd * (int)cdiv(m, 256) * a.ksplit : 0;
             a.nO = a.la ? (int)cdiv(a.la, kORows) * ntd : 0;
             if (a.nQ + a.nK) {
                 {
@@ -775,6 +819,15 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
                     hipLaunchKernelGGL(k_down<T>, dim3(S * (a.nG13 + a.nG2 + a.nO)), dim3(kThreads), 0, st, a);
                 }
                 if ((rc = check_launch("k_down")) != TTT_OK) return rc;
+            }
+            if (a.lu && a.ksplit > 1) {
+                const int64_t n4 = (int64_t)S * L.g_stride / 4;
+                {
+                    ProfScope ps(PK_DOWN, st);
+                    hipLaunchKernelGGL(k_gsum, dim3((unsigned)cdiv(n4, kThreads)), dim3(kThreads), 0, st, G, n4,
+                                       a.ksplit, a.gpart_stride);
+                }
+                if ((rc = check_launch("k_gsum")) != TTT_OK) return rc;
             }
             if (a.lu == 0) continue;
             const int mat0 = D.last_layer_only ? 2 : 0, nmat = D.last_layer_only ? 1 : 3;

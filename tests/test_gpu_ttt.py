@@ -129,6 +129,15 @@ def test_ascent_is_descent_with_negated_eta():
     assert torch.equal(oa, od) and torch.equal(Wa, Wd)
 
 
+@pytest.mark.parametrize("bf16", [False, True])
+def test_few_scans_split_gradients(bf16):
+    # one scan with 4096-token chunks: the gradient tiles split the chunk into 8 token parts whose
+    # partial gradients are summed; the 904-token tail is not split
+    run_small(18, 1, 1, 5000, 64, 128, 4096, O.MASK_APPLY_THEN_UPDATE, O.UPD_GD_L2, bf16)
+    run_small(19, 1, 1, 5000, 64, 128, 4096, O.MASK_UPDATE_THEN_APPLY, O.UPD_MUON_L2, bf16, momentum=0.9, ns=3)
+    run_small(20, 1, 1, 4096, 64, 128, 4096, O.MASK_APPLY_THEN_UPDATE, O.UPD_GD, bf16, last=True)
+
+
 def test_zero_tokens_returns_w0():
     (q, k, v, eta, W0), (hq, hk, hv, he, W1, W3, W2) = full_ttt_inputs(0, 2, 2, 0, 32, 64, True)
     o, Wout = T.ttt_forward(q, k, v, eta, W0, 16, O.MASK_APPLY_THEN_UPDATE, O.UPD_GD_L2, m_h=64)
