@@ -510,20 +510,20 @@ __global__ __launch_bounds__(kThreads) void k_ns_init(NSArgs<T> a) {
     }
 }
 
-// Gram tiles: one 64-wide LDS stage (37 KB), so three workgroups share a CU
-template <typename T, bool KS> using NSTile = Tile<T, 128, 128, 2, 2, 1, 1, 1, KS, KS, false, 4, 1>;
+// Gram tiles of TS x TS: one 64-wide LDS stage (37 KB at TS = 128), so three workgroups share a CU
+template <typename T, bool KS, int TS> using NSTile = Tile<T, TS, TS, 2, 2, 1, 1, 1, KS, KS, false, 4, 1>;
 template <typename T> using NSStepTall = Tile<T, 128, 64, 2, 2, 1, 1, 1, false, false>;
 template <typename T> using NSStepWide = Tile<T, 128, 64, 2, 2, 1, 1, 1, false, true>;
 constexpr int kNSStepRows = 128, kNSStepCols = 64;
 
 // The Gram matrix is symmetric: only its tiles on or above the diagonal are computed (tile t of
 // np (np + 1) / 2, row-major over the upper triangle), and an off-diagonal tile also writes its
-// mirror block, transposed through LDS so that those stores are whole rows as well.
-template <typename T>
+// mirror block, transposed through LDS so that those stores are whole rows as well.  Tiles are
+// TS = 128 wide, or 64 when the 128-wide ones would leave most CUs idle (few, small matrices).
+template <typename T, int TS>
 __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 3 : 2) void k_ns_gram(NSArgs<T> a) {  // fp32: 67 KB LDS
-    constexpr int kTP = 128 + 16 / (int)sizeof(T);  // transposed-tile pitch (elements)
-    constexpr int LDSB = NSTile<T, false>::LDS > 128 * kTP * (int)sizeof(T) ? NSTile<T, false>::LDS
-                                                                             : 128 * kTP * (int)sizeof(T);
+    constexpr int kTP = TS + 16 / (int)sizeof(T);  // transposed-tile pitch (elements)
+    constexpr int LDSB = std::max(NSTile<T, false, TS>::LDS, TS * kTP * (int)sizeof(T));
     __shared__ __attribute__((aligned(16))) char smem[LDSB];
     const int64_t dm = (int64_t)a.d * a.m;
     const int per = a.nmat * a.tiles;
@@ -534,10 +534,10 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 3 : 2) void k_ns_gram(NS
     t %= a.tiles;
     const int r = mat < 2 ? a.m : a.d, c = mat < 2 ? a.d : a.m;
     const int p = r < c ? r : c;
-    const int np = (p + 127) / 128;
+    const int np = (p + TS - 1) / TS;
     int ti = 0;
     while (t >= np - ti) t -= np - ti++;  // uniform: row ti of the upper triangle, column ti + t
-    const int i0 = ti * 128, j0 = (ti + t) * 128;
+    const int i0 = ti * TS, j0 = (ti + t) * TS;
     const T* X = a.Xin + s * a.x_stride + mat * dm;
     T* Gm = a.Gram + s * a.gram_stride + (int64_t)mat * p * p;
     T* tT = reinterpret_cast<T*>(smem);
@@ -549,9 +549,9 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 3 : 2) void k_ns_gram(NS
         lds_barrier();  // every wave is done with the LDS stage
         tl.for_each([&](const float (&v)[1], int row, int col) { tT[col * kTP + row] = Elt<T>::st(v[0]); });
         __syncthreads();
-        // mirror block: Gram row j0 + cc, columns i0 .. i0 + 127, from LDS row cc
-        constexpr int VEC = 16 / (int)sizeof(T), VPR = 128 / VEC;
-        for (int u = threadIdx.x; u < 128 * VPR; u += kThreads) {
+        // mirror block: Gram row j0 + cc, columns i0 .. i0 + TS - 1, from LDS row cc
+        constexpr int VEC = 16 / (int)sizeof(T), VPR = TS / VEC;
+        for (int u = threadIdx.x; u < TS * VPR; u += kThreads) {
             const int cc = u / VPR, x = (u % VPR) * VEC;
             if (j0 + cc < p && i0 + x < p)
                 *reinterpret_cast<u32x4_t*>(Gm + (uint32_t)(j0 + cc) * (uint32_t)p + (uint32_t)(i0 + x)) =
@@ -559,13 +559,13 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 3 : 2) void k_ns_gram(NS
         }
     };
     if (r > c) {  // Gram = X^T X (c x c), contracted over the r rows
-        NSTile<T, true> tl;
+        NSTile<T, true, TS> tl;
         const Opnd<T> A[1] = {{X + i0, c, c - i0, r}};
         const Opnd<T> B[1] = {{X + j0, c, c - j0, r}};
         tl.template run<PM1>(A, B, r, smem);
         epi(tl);
     } else {      // Gram = X X^T (r x r), contracted over the c columns
-        NSTile<T, false> tl;
+        NSTile<T, false, TS> tl;
         const Opnd<T> A[1] = {{X + (int64_t)i0 * c, c, r - i0, c}};
         const Opnd<T> B[1] = {{X + (int64_t)j0 * c, c, r - j0, c}};
         tl.template run<PM1>(A, B, c, smem);
@@ -852,7 +852,10 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
                 }
                 if ((rc = check_launch("k_ns_init")) != TTT_OK) return rc;
                 const int p = d < m ? d : m;
-                const int gt = (int)(cdiv(p, 128) * (cdiv(p, 128) + 1) / 2);  // upper-triangle Gram tiles
+                // upper-triangle Gram tiles of 128, or of 64 when the 128-wide ones fill under 256 CUs
+                const bool gsmall = (int64_t)S * nmat * cdiv(p, 128) * (cdiv(p, 128) + 1) / 2 < 256;
+                const int gts = gsmall ? 64 : 128;
+                const int gt = (int)(cdiv(p, gts) * (cdiv(p, gts) + 1) / 2);
                 // step tiles: the larger of the tall (m x d) and wide (d x m) tilings
                 const int stt = (int)std::max(cdiv(m, kNSStepRows) * cdiv(d, kNSStepCols),
                                               cdiv(d, kNSStepRows) * cdiv(m, kNSStepCols));
@@ -862,7 +865,8 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
                     na.tiles = gt;
                     {
                         ProfScope ps(PK_NS_GRAM, st);
-                        hipLaunchKernelGGL(k_ns_gram<T>, dim3(S * nmat * gt), dim3(kThreads), 0, st, na);
+                        if (gsmall) hipLaunchKernelGGL((k_ns_gram<T, 64>), dim3(S * nmat * gt), dim3(kThreads), 0, st, na);
+                        else hipLaunchKernelGGL((k_ns_gram<T, 128>), dim3(S * nmat * gt), dim3(kThreads), 0, st, na);
                     }
                     if ((rc = check_launch("k_ns_gram")) != TTT_OK) return rc;
                     na.tiles = stt;

@@ -105,6 +105,8 @@ def test_muon_gram_mirror_fp32():
     # also writes its mirror block; both Gram sides (m > d, then d > m)
     run_small(12, 1, 1, 256, 160, 320, 128, O.MASK_APPLY_THEN_UPDATE, O.UPD_MUON_L2, False, ns=3)
     run_small(13, 1, 1, 256, 320, 160, 128, O.MASK_UPDATE_THEN_APPLY, O.UPD_MUON, False, ns=2)
+    # 32 scans: enough 128-wide Gram tiles that the kernel keeps them (fewer scans take 64-wide ones)
+    run_small(21, 8, 4, 128, 160, 320, 128, O.MASK_APPLY_THEN_UPDATE, O.UPD_MUON_L2, False, ns=2)
 
 
 @pytest.mark.parametrize("bf16", [False, True])
