@@ -32,9 +32,9 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 # taken on.  They are reported only while those sources are unchanged.
 TRAFFIC_SOURCES = ("linear_attention_chunk_amd/csrc/ttt_layer.hip", "linear_attention_chunk_amd/csrc/tile.hpp")
 MEASURED_TRAFFIC = {
-    "source_sha": "c577406df5b99a31",
-    "k_up": {"read": 307.5e6, "write": 436.8e6},
-    "k_down": {"read": 585.9e6, "write": 203.7e6},
+    "source_sha": "c788ea57138a74d6",
+    "k_up": {"read": 294.8e6, "write": 428.5e6},
+    "k_down": {"read": 583.8e6, "write": 203.3e6},
     "k_update": {"read": 218.7e6, "write": 188.8e6},
 }
 
