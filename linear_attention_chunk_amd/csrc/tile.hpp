@@ -517,6 +517,46 @@ struct Tile {
             }
     }
 
+    // Row-major view of the accumulators through LDS, for tiles whose output columns are permuted
+    // (k-strided B operand) so that a lane's elements lie 8 columns apart.  For each accumulator p
+    // and each band of WM rows (the rows of one wave row), the waves that own the band write it to
+    // LDS in logical order, then all threads read it back four columns at a time and call
+    // f(p, row, col, float4) with col a multiple of 4; a wave covers whole 128-byte row segments.
+    // Needs WM * (BN + 4) floats of LDS; every wave must be done with the tile's LDS stages.
+    static constexpr int RV_PITCH = BN + 4;  // floats: rows stay 16-byte aligned
+    static constexpr int RV_LDS = WM * RV_PITCH * 4;
+    template <class F>
+    __device__ __forceinline__ void rows_via_lds(char* lds, F&& f) const {
+        static_assert(!KSA, "row bands need unpermuted rows");
+        static_assert((WM * BN / 4) % NT == 0, "a band is a whole number of rounds of the workgroup");
+        float* band = reinterpret_cast<float*>(lds);
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int wm = wave / WGN, wn = wave % WGN;
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+#pragma unroll
+            for (int h = 0; h < WGM; ++h) {
+                lds_barrier();
+                if (wm == h) {
+#pragma unroll
+                    for (int i = 0; i < FM; ++i)
+#pragma unroll
+                        for (int j = 0; j < FN; ++j) {
+                            const int col = RowMap<T, BN, SEG, KSB>::row_of(wn * WN + j * 32 + (lane & 31));
+#pragma unroll
+                            for (int r = 0; r < 16; ++r)
+                                band[(i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * RV_PITCH + col] = acc[p][i][j][r];
+                        }
+                }
+                lds_barrier();
+#pragma unroll
+                for (int k = 0; k < WM * BN / 4 / NT; ++k) {
+                    const int q = k * NT + (int)threadIdx.x, row = q / (BN / 4), c = (q % (BN / 4)) * 4;
+                    f(p, h * WM + row, c, *reinterpret_cast<const float4*>(band + row * RV_PITCH + c));
+                }
+            }
+    }
+
     // f(const float (&v)[NP], int row, int col) for every accumulator element of this thread,
     // with row / col the logical tile coordinates
     template <class F>

@@ -218,20 +218,25 @@ __global__ __launch_bounds__(kThreads, 2) void k_down(StepArgs<T> a) {
         const Opnd<T> B[1] = {{K + c0, a.d, a.d - c0, kl}};
         TG13 tl;
         tl.template run<PMG>(A, B, kl, smem);
-        // stores go through 32-bit offsets from the tile corner; full tiles skip the bounds checks
+        // stores go through 32-bit offsets from the tile corner
         float* G1 = a.G + part * a.gpart_stride + s * a.g_stride + (int64_t)r0 * a.d + c0;
         float* G3 = G1 + dm;
-        auto epi = [&](auto check) {
+        if (r0 + TG13::BM <= a.m && c0 + TG13::BN <= a.d) {
+            // full tiles: the K operand's staging permutes the columns, so rows are gathered in LDS
+            // and leave as whole 512-byte row segments
+            static_assert(TG13::RV_LDS <= LDSB, "row bands fit the tile's LDS");
+            tl.rows_via_lds(smem, [&](int p, int row, int col, const float4& v) {
+                *reinterpret_cast<float4*>((p ? G3 : G1) + (uint32_t)row * (uint32_t)a.d + (uint32_t)col) = v;
+            });
+        } else {
             tl.for_each([&](const float (&v)[2], int row, int col) {
-                if (!decltype(check)::value || (r0 + row < a.m && c0 + col < a.d)) {
+                if (r0 + row < a.m && c0 + col < a.d) {
                     const uint32_t off = (uint32_t)row * (uint32_t)a.d + (uint32_t)col;
                     G1[off] = v[0];
                     G3[off] = v[1];
                 }
             });
-        };
-        if (r0 + TG13::BM <= a.m && c0 + TG13::BN <= a.d) epi(std::false_type{});
-        else epi(std::true_type{});
+        }
         return;
     }
     t -= a.nG13;
