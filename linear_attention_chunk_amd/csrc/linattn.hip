@@ -429,16 +429,20 @@ __global__ __launch_bounds__(kThreads, 2) void k_lin_delta(DeltaArgs<T> a) {
     const Opnd<T> B[1] = {{a.k + tok * a.dk + c0, a.dk, a.dk - c0, nl}};
     TD tl;
     tl.template run<PM1>(A, B, nl, smem);
-    // 32-bit offsets from the tile corner; full tiles skip the bounds checks
+    // 32-bit offsets from the tile corner
     float* dS = a.dS + (int64_t)unit * a.dv * a.dk + (int64_t)r0 * a.dk + c0;
-    auto epi = [&](auto check) {
-        tl.for_each([&](const float (&v)[1], int row, int col) {
-            if (!decltype(check)::value || (r0 + row < a.dv && c0 + col < a.dk))
-                dS[(uint32_t)row * (uint32_t)a.dk + (uint32_t)col] = v[0];
+    if (r0 + TD::BM <= a.dv && c0 + TD::BN <= a.dk) {
+        // full tiles: both operands' staging permutes rows and columns, so rows are gathered in
+        // LDS and leave as whole 512-byte row segments
+        static_assert(TD::RV_LDS <= TD::LDS, "row bands fit the tile's LDS");
+        tl.rows_via_lds(smem, [&](int, int, int row, int col, const float4& v) {
+            *reinterpret_cast<float4*>(dS + (uint32_t)row * (uint32_t)a.dk + (uint32_t)col) = v;
         });
-    };
-    if (r0 + TD::BM <= a.dv && c0 + TD::BN <= a.dk) epi(std::false_type{});
-    else epi(std::true_type{});
+    } else {
+        tl.for_each([&](const float (&v)[1], int row, int col) {
+            if (r0 + row < a.dv && c0 + col < a.dk) dS[(uint32_t)row * (uint32_t)a.dk + (uint32_t)col] = v[0];
+        });
+    }
 }
 
 // The state each chunk's queries see, from S0 and the chunk updates dS_c: before chunk c's own

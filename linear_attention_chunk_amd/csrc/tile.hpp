@@ -519,16 +519,36 @@ struct Tile {
 
     // Row-major view of the accumulators through LDS, for tiles whose output columns are permuted
     // (k-strided B operand) so that a lane's elements lie 8 columns apart.  For each accumulator p
-    // and each band of WM rows (the rows of one wave row), the waves that own the band write it to
-    // LDS in logical order, then all threads read it back four columns at a time and call
-    // f(p, row, col, float4) with col a multiple of 4; a wave covers whole 128-byte row segments.
-    // Needs WM * (BN + 4) floats of LDS; every wave must be done with the tile's LDS stages.
+    // and each band of WM staged rows (the rows of one wave row), the waves that own the band write
+    // it to LDS with its columns in logical order, then all threads read it back four columns at a
+    // time and call f(idx, p, row, col, float4): row is the logical tile row (k-strided A rows are
+    // mapped back), col a multiple of 4, and idx = 0 .. RV_N - 1 in the order of rows_via_lds_pos.
+    // A wave covers whole 4 * BN-byte row segments.  Needs RV_LDS bytes of LDS; every wave must be
+    // done with the tile's LDS stages.
     static constexpr int RV_PITCH = BN + 4;  // floats: rows stay 16-byte aligned
     static constexpr int RV_LDS = WM * RV_PITCH * 4;
+    static constexpr int RV_K = WM * BN / 4 / NT;  // float4 per thread per band
+    static constexpr int RV_N = NP * WGM * RV_K;   // float4 per thread in all
+    static_assert((WM * BN / 4) % NT == 0, "a band is a whole number of rounds of the workgroup");
+
+    // f(idx, p, row, col) over the positions rows_via_lds visits, in the same order; usable before
+    // run(), e.g. to prefetch epilogue operands
+    template <class F>
+    __device__ __forceinline__ static void rows_via_lds_pos(F&& f) {
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+#pragma unroll
+            for (int h = 0; h < WGM; ++h)
+#pragma unroll
+                for (int k = 0; k < RV_K; ++k) {
+                    const int q = k * NT + (int)threadIdx.x;
+                    f((p * WGM + h) * RV_K + k, p, RowMap<T, BM, SEG, KSA>::row_of(h * WM + q / (BN / 4)),
+                      (q % (BN / 4)) * 4);
+                }
+    }
+
     template <class F>
     __device__ __forceinline__ void rows_via_lds(char* lds, F&& f) const {
-        static_assert(!KSA, "row bands need unpermuted rows");
-        static_assert((WM * BN / 4) % NT == 0, "a band is a whole number of rounds of the workgroup");
         float* band = reinterpret_cast<float*>(lds);
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
         const int wm = wave / WGN, wn = wave % WGN;
@@ -550,9 +570,10 @@ struct Tile {
                 }
                 lds_barrier();
 #pragma unroll
-                for (int k = 0; k < WM * BN / 4 / NT; ++k) {
+                for (int k = 0; k < RV_K; ++k) {
                     const int q = k * NT + (int)threadIdx.x, row = q / (BN / 4), c = (q % (BN / 4)) * 4;
-                    f(p, h * WM + row, c, *reinterpret_cast<const float4*>(band + row * RV_PITCH + c));
+                    f((p * WGM + h) * RV_K + k, p, RowMap<T, BM, SEG, KSA>::row_of(h * WM + row), c,
+                      *reinterpret_cast<const float4*>(band + row * RV_PITCH + c));
                 }
             }
     }

@@ -225,7 +225,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_down(StepArgs<T> a) {
             // full tiles: the K operand's staging permutes the columns, so rows are gathered in LDS
             // and leave as whole 512-byte row segments
             static_assert(TG13::RV_LDS <= LDSB, "row bands fit the tile's LDS");
-            tl.rows_via_lds(smem, [&](int p, int row, int col, const float4& v) {
+            tl.rows_via_lds(smem, [&](int, int p, int row, int col, const float4& v) {
                 *reinterpret_cast<float4*>((p ? G3 : G1) + (uint32_t)row * (uint32_t)a.d + (uint32_t)col) = v;
             });
         } else {
@@ -633,10 +633,29 @@ __global__ __launch_bounds__(kThreads, 2) void k_ns_step(NSArgs<T> a) {
         const Opnd<T> B[1] = {{Gm + (int64_t)c0 * p, p, c - c0, p}};
         body(tl, A, B, c);
     } else {      // P = Gram X; B[j][i] = X[i][j] is read k-strided
-        NSStepWide<T> tl;
+        using TW = NSStepWide<T>;
+        TW tl;
         const Opnd<T> A[1] = {{Gm + (int64_t)r0 * p, p, r - r0, p}};
         const Opnd<T> B[1] = {{X + c0, c, c - c0, r}};
-        body(tl, A, B, r);
+        if (r0 + TW::BM <= r && c0 + TW::BN <= c) {
+            // full tiles: the k-strided staging permutes the columns, so rows are gathered in LDS
+            // and the iterate is read and written four consecutive elements at a time
+            static_assert(TW::RV_LDS <= (int)sizeof(smem), "row bands fit the tile's LDS");
+            float4 xv[TW::RV_N];
+            TW::rows_via_lds_pos([&](int idx, int, int row, int col) {
+                xv[idx] = *reinterpret_cast<const float4*>(Xft + (uint32_t)row * (uint32_t)c + (uint32_t)col);
+            });
+            tl.template run<PM1>(A, B, r, smem);
+            tl.rows_via_lds(smem, [&](int idx, int, int row, int col, const float4& v) {
+                const float x0 = 1.5f * xv[idx].x - 0.5f * v.x, x1 = 1.5f * xv[idx].y - 0.5f * v.y;
+                const float x2 = 1.5f * xv[idx].z - 0.5f * v.z, x3 = 1.5f * xv[idx].w - 0.5f * v.w;
+                const uint32_t e = (uint32_t)row * (uint32_t)c + (uint32_t)col;
+                *reinterpret_cast<float4*>(Xft + e) = make_float4(x0, x1, x2, x3);
+                Pack4<T>::store(Xot + e, x0, x1, x2, x3);
+            });
+        } else {
+            body(tl, A, B, r);
+        }
     }
 }
 
