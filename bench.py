@@ -32,10 +32,10 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 # taken on.  They are reported only while those sources are unchanged.
 TRAFFIC_SOURCES = ("linear_attention_chunk_amd/csrc/ttt_layer.hip", "linear_attention_chunk_amd/csrc/tile.hpp")
 MEASURED_TRAFFIC = {
-    "source_sha": "c788ea57138a74d6",
-    "k_up": {"read": 294.8e6, "write": 428.5e6},
-    "k_down": {"read": 583.8e6, "write": 203.3e6},
-    "k_update": {"read": 218.7e6, "write": 188.8e6},
+    "source_sha": "0eed5a178840e67a",
+    "k_up": {"read": 296.5e6, "write": 428.4e6},
+    "k_down": {"read": 575.5e6, "write": 164.0e6},
+    "k_update": {"read": 218.6e6, "write": 188.8e6},
 }
 
 
