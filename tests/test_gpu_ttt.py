@@ -95,6 +95,15 @@ def test_wide_layer_bf16():
     run_small(11, 1, 1, 600, 512, 1024, 256, O.MASK_APPLY_THEN_UPDATE, O.UPD_GD_L2, True)
 
 
+@pytest.mark.parametrize("bf16", [False, True])
+def test_maximum_widths(bf16):
+    # m_h and d_h at their maximum (2048) against a narrow other side: 16 hidden tiles per scan
+    # with one partial d tile, update rows of 2048 (8 float4 per lane, 64-128 KB of LDS for W2^T),
+    # and the other way round, 32 64-wide k-steps per up tile and 16 row blocks of W2
+    run_small(22, 1, 1, 160, 64, 2048, 128, O.MASK_APPLY_THEN_UPDATE, O.UPD_GD_L2, bf16)
+    run_small(23, 1, 1, 160, 2048, 64, 128, O.MASK_UPDATE_THEN_APPLY, O.UPD_MUON_L2, bf16, ns=2)
+
+
 def test_tall_and_wide_muon_fp32():
     # d > m exercises the other Gram side for W1/W3 and W2
     run_small(6, 1, 1, 128, 96, 32, 64, O.MASK_APPLY_THEN_UPDATE, O.UPD_MUON_L2, False, ns=3)
