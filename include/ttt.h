@@ -166,6 +166,10 @@ ttt_status linattn_forward(const linattn_desc* desc, const void* q, const void* 
  */
 #define TTT_PROF_KERNELS 11
 ttt_status ttt_profile_enable(int32_t on);
+/* Restricts the bracketing to the kernel classes i whose bit (1u << i) is set in mask; the
+ * default is every class.  Each bracket records two events on the launch's stream, which costs
+ * the stream a few microseconds, so a tool that times one kernel class selects only that one. */
+ttt_status ttt_profile_select(uint32_t mask);
 ttt_status ttt_profile_read(float* ms, int32_t* count, int32_t n);
 const char* ttt_profile_kernel_name(int32_t i);
 

@@ -21,7 +21,7 @@ EXPORTS = (
     "ttt_abi_version", "ttt_status_string", "ttt_last_error",
     "ttt_workspace_bytes", "ttt_forward",
     "linattn_workspace_bytes", "linattn_forward",
-    "ttt_profile_enable", "ttt_profile_read", "ttt_profile_kernel_name",
+    "ttt_profile_enable", "ttt_profile_select", "ttt_profile_read", "ttt_profile_kernel_name",
 )
 PROF_KERNELS = 11
 
@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
                                   c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     L.ttt_profile_enable.restype = c_int32
     L.ttt_profile_enable.argtypes = [c_int32]
+    L.ttt_profile_select.restype = c_int32
+    L.ttt_profile_select.argtypes = [ctypes.c_uint32]
     L.ttt_profile_read.restype = c_int32
     L.ttt_profile_read.argtypes = [POINTER(c_float), POINTER(c_int32), c_int32]
     L.ttt_profile_kernel_name.restype = ctypes.c_char_p
@@ -90,6 +92,18 @@ def lib() -> ctypes.CDLL:
 
 def profile_enable(on: bool) -> None:
     check(lib().ttt_profile_enable(1 if on else 0))
+
+
+def profile_select(names=None) -> None:
+    """Bracket only the named kernel classes (None: every class)."""
+    if names is None:
+        mask = 0xFFFFFFFF
+    else:
+        index = {lib().ttt_profile_kernel_name(i).decode(): i for i in range(PROF_KERNELS)}
+        mask = 0
+        for n in names:
+            mask |= 1 << index[n]
+    check(lib().ttt_profile_select(mask))
 
 
 def profile_read() -> dict:

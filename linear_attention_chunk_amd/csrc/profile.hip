@@ -8,6 +8,7 @@
 namespace ttt {
 namespace {
 std::atomic<bool> g_on{false};
+std::atomic<uint32_t> g_mask{0xFFFFFFFFu};  // kernel classes that are bracketed while enabled
 std::mutex g_mu;
 struct Rec { int id; hipEvent_t a, b; };
 std::vector<Rec> g_recs;
@@ -17,7 +18,7 @@ const char* kNames[TTT_PROF_KERNELS] = {"k_up", "k_down", "k_update", "k_muon_pr
 }  // namespace
 
 ProfScope::ProfScope(int id_, hipStream_t st_) : id(id_), st(st_) {
-    if (!g_on.load(std::memory_order_relaxed)) return;
+    if (!g_on.load(std::memory_order_relaxed) || !((g_mask.load(std::memory_order_relaxed) >> id) & 1u)) return;
     if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) { a = b = nullptr; return; }
     (void)hipEventRecord(a, st);
 }
@@ -34,6 +35,11 @@ using namespace ttt;
 
 extern "C" ttt_status ttt_profile_enable(int32_t on) {
     g_on.store(on != 0);
+    return TTT_OK;
+}
+
+extern "C" ttt_status ttt_profile_select(uint32_t mask) {
+    g_mask.store(mask);
     return TTT_OK;
 }
 
