@@ -45,6 +45,20 @@ def test_version_and_status_strings():
     assert L.ttt_status_string(99) == b"unknown status"
 
 
+def test_profiler_selection_on_the_host():
+    """Selecting kernel classes and reading with nothing recorded touch no device."""
+    L = C.lib()
+    names = [L.ttt_profile_kernel_name(i).decode() for i in range(C.PROF_KERNELS)]
+    assert names[0] == "k_up" and len(set(names)) == C.PROF_KERNELS
+    C.profile_select(["k_up", "k_ns_step"])
+    C.profile_select(None)
+    assert L.ttt_profile_select(0) == C.TTT_OK
+    assert L.ttt_profile_select(0xFFFFFFFF) == C.TTT_OK
+    assert all(v == (0.0, 0) for v in C.profile_read().values())
+    with pytest.raises(KeyError):
+        C.profile_select(["no_such_kernel"])
+
+
 def desc(**kw):
     base = dict(B=2, H=4, N=256, d_h=64, m_h=128, chunk=64, io_dtype=C.TTT_BF16, mask=C.MASK_APPLY_THEN_UPDATE,
                 rule=C.UPD_GD_L2, ns_iters=5, momentum=0.0, last_layer_only=0, w0_per_batch=0, update_chunks=None)
