@@ -143,7 +143,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures a single GPU: this build runs each (batch, head) scan on one device and "
+        print("bench.py measures a single GPU: the library runs each (batch, head) scan on one device and "
               "has no multi-GPU path; run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 

@@ -48,7 +48,7 @@ extern "C" {
 typedef enum {
     TTT_OK = 0,
     TTT_ERR_INVALID_ARGUMENT = 1, /* a size, pointer, alignment or enum value is out of range     */
-    TTT_ERR_UNSUPPORTED = 2,      /* a valid combination this build does not implement          */
+    TTT_ERR_UNSUPPORTED = 2,      /* a valid combination the library does not implement         */
     TTT_ERR_WORKSPACE = 3,        /* workspace pointer missing or smaller than *_workspace_bytes  */
     TTT_ERR_DEVICE = 4            /* a HIP call or kernel launch failed                          */
 } ttt_status;
@@ -104,7 +104,7 @@ typedef struct linattn_desc {
     const uint8_t* update_chunks; /* host, ceil(N/chunk) flags; read only for TTT_MASK_STRIDED  */
 } linattn_desc;
 
-/* Version of this ABI (TTT_ABI_VERSION of the build). */
+/* Version of this ABI (the TTT_ABI_VERSION the library was compiled with). */
 int32_t ttt_abi_version(void);
 
 /* Static description of a status code; never NULL. */
