@@ -547,8 +547,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_lin_apply(ApplyArgs<T> a) {
 // through an fp32 LDS buffer, because the transposing stager leaves P v in another column order.
 constexpr int kCausalBlock = 128;
 
+// One workgroup per CU: its three accumulators and v's early-loaded stages need about 390 VGPRs,
+// which two workgroups per CU could only hold by spilling (measured: 1.4% slower with spills).
 template <typename T>
-__global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void k_lin_apply_causal(ApplyArgs<T> a) {  // fp32: 147 KB LDS
+__global__ __launch_bounds__(kThreads, 1) void k_lin_apply_causal(ApplyArgs<T> a) {  // fp32: 147 KB LDS
     constexpr int PLANES = sizeof(T) == 2 ? 2 : 1;
     using TP = Tile<T, kCausalBlock, kCausalBlock, 1, 2, 1, 1, 1, false, false>;  // q k^T
     using TD = Tile<T, kCausalBlock, kApplyCols, 2, 2, 1, 1, 1, false, true>;     // P v, P in LDS
