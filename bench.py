@@ -13,6 +13,7 @@ bounded sample of scans, parity of those scans against that oracle, and the othe
 momentum, the strided view-synthesis mask, chunked linear attention) as extra measurements.
 """
 import argparse
+import ctypes
 import json
 import os
 import platform
@@ -102,6 +103,40 @@ def time_calls(torch, fn, steps, warmup):
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) / steps
+
+
+def measured_peaks(torch, C):
+    """Rates this device sustains, timed outside the timed region: the library's MFMA-loop probe
+    (bf16 32x32x16 MFMAs on register operands, 1024 workgroups x 512 rounds) and a 1 GiB
+    device-to-device copy (2^30 bytes read and 2^30 written).  Best of three each."""
+    out = torch.empty(1024, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    blocks, iters = 1024, 512
+    flop = blocks * 4 * iters * 4 * 32 * 32 * 16 * 2
+
+    def probe():
+        C.check(C.lib().ttt_probe_mfma_bf16(blocks, iters, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream)))
+
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    best = {}
+    for name, fn in (("mfma", probe), ("copy", lambda: dst.copy_(src))):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        best[name] = min(ts)
+    del src, dst
+    return {"bf16_mfma_TFLOPs": round(flop / (best["mfma"] * 1e-3) / 1e12, 1),
+            "copy_GBps": round(2 * (1 << 30) / (best["copy"] * 1e-3) / 1e9, 1),
+            "how": "MFMA-loop probe (register operands, 4 independent accumulators per wave) and a 1 GiB "
+                   "device copy, best of 3, outside the timed region"}
 
 
 def blas_threads():
@@ -264,6 +299,10 @@ def main():
     roofline = {"kernel": dom, "bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
                 "frac": round(ach / peak, 4), "traffic": measured_traffic(dom), "traffic_unit": "bytes/launch", "avg_launch_us": round(avg * 1e3, 2),
                 "launches": dom_n, key: amount}
+    # the same against the rates this device sustains (vendor peaks above remain the roofline)
+    peaks = measured_peaks(torch, C)
+    mpeak = peaks["bf16_mfma_TFLOPs"] if bound == "mfma" else peaks["copy_GBps"]
+    roofline.update({"measured_peak": mpeak, "frac_of_measured": round(ach / mpeak, 4)})
     # per-kernel breakdown: a short pass after the timed region with every launch bracketed
     nb = min(args.steps, 3)
     C.profile_select(None)
@@ -407,6 +446,7 @@ def main():
         "algorithmic_tflop_per_step": round(flops / 1e12, 4),
         "algorithmic_gb_per_step": round(lact_bytes(B, H, N, d, m, 2, nchunks) / 1e9, 3),
         "roofline": roofline,
+        "measured_peaks": peaks,
         "kernels": kernels,
         "cpu_baseline": cpu,
         "parity": parity,

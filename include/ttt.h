@@ -173,6 +173,16 @@ ttt_status ttt_profile_select(uint32_t mask);
 ttt_status ttt_profile_read(float* ms, int32_t* count, int32_t n);
 const char* ttt_profile_kernel_name(int32_t i);
 
+/*
+ * MFMA-loop probe for measurement tools: enqueues on `stream` one kernel of `blocks` workgroups of
+ * 256 threads in which every wave issues iters x 4 independent bf16 32x32x16 MFMAs on register
+ * operands (32768 FLOP each), and writes one float per workgroup to the device buffer out
+ * (caller-owned, blocks floats).  Timing it gives the matrix-core rate the device sustains:
+ * FLOP = blocks x 4 waves x iters x 4 x 32768.  blocks, iters >= 1 and out non-NULL, else
+ * TTT_ERR_INVALID_ARGUMENT before anything is enqueued.
+ */
+ttt_status ttt_probe_mfma_bf16(int32_t blocks, int32_t iters, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

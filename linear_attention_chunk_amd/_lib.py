@@ -22,6 +22,7 @@ EXPORTS = (
     "ttt_workspace_bytes", "ttt_forward",
     "linattn_workspace_bytes", "linattn_forward",
     "ttt_profile_enable", "ttt_profile_select", "ttt_profile_read", "ttt_profile_kernel_name",
+    "ttt_probe_mfma_bf16",
 )
 PROF_KERNELS = 11
 
@@ -86,6 +87,8 @@ def lib() -> ctypes.CDLL:
     L.ttt_profile_read.argtypes = [POINTER(c_float), POINTER(c_int32), c_int32]
     L.ttt_profile_kernel_name.restype = ctypes.c_char_p
     L.ttt_profile_kernel_name.argtypes = [c_int32]
+    L.ttt_probe_mfma_bf16.restype = c_int32
+    L.ttt_probe_mfma_bf16.argtypes = [c_int32, c_int32, ctypes.c_void_p, ctypes.c_void_p]
     _lib = L
     return L
 

@@ -1,4 +1,5 @@
-// Optional launch profiler: events recorded around each kernel launch on its own stream.
+// Optional launch profiler: events recorded around each kernel launch on its own stream.  Also an
+// MFMA-loop probe that measures the bf16 matrix-core rate the device reaches.
 #include <atomic>
 #include <mutex>
 #include <vector>
@@ -67,4 +68,44 @@ extern "C" ttt_status ttt_profile_read(float* ms, int32_t* count, int32_t n) {
 
 extern "C" const char* ttt_profile_kernel_name(int32_t i) {
     return (i >= 0 && i < TTT_PROF_KERNELS) ? kNames[i] : "";
+}
+
+namespace ttt {
+constexpr int kProbeThreads = 256;
+typedef __bf16 probe_bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float probe_f32x16_t __attribute__((ext_vector_type(16)));
+
+// Every wave runs iters rounds of four independent v_mfma_f32_32x32x16_bf16 on register operands
+// (independent accumulators, and two waves per SIMD, cover the MFMA latency), then folds its
+// accumulators into out[block] so that nothing is optimised away.  32 x 32 x 16 x 2 FLOP per MFMA.
+__global__ __launch_bounds__(kProbeThreads) void k_mfma_probe(float* out, int iters) {
+    probe_f32x16_t acc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[u][r] = 0.f;
+    probe_bf16x8_t a, b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        a[e] = (__bf16)(1e-3f * (float)((threadIdx.x + e) & 7));
+        b[e] = (__bf16)(1e-3f * (float)((threadIdx.x * 3 + e) & 7));
+    }
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[u], 0, 0, 0);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s += acc[u][r];
+    if (threadIdx.x == 0) out[blockIdx.x] = s;
+}
+}  // namespace ttt
+
+extern "C" ttt_status ttt_probe_mfma_bf16(int32_t blocks, int32_t iters, float* out, void* stream) {
+    clear_error();
+    if (blocks < 1 || iters < 1 || !out) return fail(TTT_ERR_INVALID_ARGUMENT, "ttt_probe_mfma_bf16: bad arguments");
+    hipLaunchKernelGGL(k_mfma_probe, dim3(blocks), dim3(kProbeThreads), 0, (hipStream_t)stream, out, iters);
+    return check_launch("k_mfma_probe");
 }

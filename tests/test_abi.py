@@ -59,6 +59,13 @@ def test_profiler_selection_on_the_host():
         C.profile_select(["no_such_kernel"])
 
 
+def test_mfma_probe_rejects_before_enqueueing():
+    L = C.lib()
+    assert L.ttt_probe_mfma_bf16(0, 16, P16, None) == C.TTT_ERR_INVALID_ARGUMENT
+    assert L.ttt_probe_mfma_bf16(4, 0, P16, None) == C.TTT_ERR_INVALID_ARGUMENT
+    assert L.ttt_probe_mfma_bf16(4, 16, None, None) == C.TTT_ERR_INVALID_ARGUMENT
+
+
 def desc(**kw):
     base = dict(B=2, H=4, N=256, d_h=64, m_h=128, chunk=64, io_dtype=C.TTT_BF16, mask=C.MASK_APPLY_THEN_UPDATE,
                 rule=C.UPD_GD_L2, ns_iters=5, momentum=0.0, last_layer_only=0, w0_per_batch=0, update_chunks=None)
