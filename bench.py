@@ -278,14 +278,14 @@ def main():
         "k_down": ("mfma", 8 * dm * S * chunk),
         # read W and G in fp32, write W in fp32 and the bf16 copies of W1, W3, W2, W2^T
         "k_update": ("hbm", (4 + 4 + 4) * 3 * dm * S + es * 4 * dm * S),
-        # read G (and read/write M) in fp32
-        "k_muon_prep": ("hbm", (12 if beta else 4) * 3 * dm * S),
-        # read U in fp32, write the fp32 iterate and its bf16 copy
-        "k_ns_init": ("hbm", (4 + 4 + es) * 3 * dm * S),
-        # Gram p x p from the bf16 iterate: 2 p^2 q per matrix
+        # read G (and read/write M) in fp32, write U as the bf16 hi + lo pair that starts Newton-Schulz
+        "k_muon_prep": ("hbm", ((12 if beta else 4) + 2 * es) * 3 * dm * S),
+        # zero Newton-Schulz steps only: read U, write U / ||U||_F in fp32
+        "k_ns_init": ("hbm", (4 + 4) * 3 * dm * S),
+        # Gram p x p from the bf16 hi plane: 2 p^2 q per matrix
         "k_ns_gram": ("mfma", 2 * p_ns * p_ns * q_ns * 3 * S),
-        # read bf16 iterate, bf16 Gram and fp32 iterate; write fp32 iterate and bf16 copy
-        "k_ns_step": ("hbm", ((es + 4 + 4 + es) * dm + es * p_ns * p_ns) * 3 * S),
+        # read the iterate's hi + lo planes and the bf16 Gram; write hi + lo (the last step: fp32)
+        "k_ns_step": ("hbm", ((2 * es + 2 * es) * dm + es * p_ns * p_ns) * 3 * S),
     }
     dom_ms, dom_n = prof[dom]
     avg = dom_ms / max(dom_n, 1)

@@ -415,16 +415,24 @@ static ttt_status launch_update(const UpdArgs<T>& u, int grid, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Muon.  prep: U = G, or M <- beta M + G and U = M; per-block partial sums of U^2.
-// init: X = U / (||U||_F + 1e-7) in fp32 and io dtype.  gram / step: one cubic Newton-Schulz
-// step X <- 1.5 X - 0.5 (X X^T) X, taken as X - ... on the side with the smaller Gram matrix.
+// Muon.  prep: U = G, or M <- beta M + G and U = M; per-block partial sums of U^2.  Newton-Schulz
+// starts from X_0 = U / (||U||_F + 1e-7) and takes cubic steps X <- 1.5 X - 0.5 (X X^T) X, each as
+// a Gram kernel and a step kernel on the side with the smaller Gram matrix.  The first step folds
+// the scaling in: with s = 1 / (||U||_F + 1e-7), its Gram kernel writes s^2 U U^T (or s^2 U^T U) and
+// its step kernel s (1.5 U - 0.5 Gram U), which is the step from X_0.
+// The iterate lives in two planes in bf16 mode: hi = bf16(x) is the contraction operand and
+// lo = bf16(x - hi) carries the next 8 bits, so x = hi + lo keeps about 16 bits for 4 bytes per
+// element (an fp32 plane beside a bf16 copy would take 6).  prep writes U this way; the last step
+// writes x in fp32, which the row update reads.  fp32 mode keeps one fp32 plane, and its first
+// step reads U in place.
 constexpr int kPrepElems = 4096;
 static_assert(kPrepElems % kThreads == 0, "prep blocks take whole rounds of the workgroup");
 
-struct PrepArgs {
+template <typename T> struct PrepArgs {
     const float* G; int64_t g_stride;
     float* M; int64_t m_stride; float beta;
     float* part; int nblk;
+    T* Xhi; T* Xlo; int64_t x_stride;     // bf16 mode, Newton-Schulz: U as hi + lo planes; else null
     int64_t dm; int mat0, nmat;
 };
 
@@ -437,13 +445,16 @@ __device__ __forceinline__ float block_sum(float x, float* red) {
     return red[0] + red[1] + red[2] + red[3];
 }
 
-__global__ __launch_bounds__(kThreads) void k_muon_prep(PrepArgs a) {
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_muon_prep(PrepArgs<T> a) {
     __shared__ float red[4];
     const int per = a.nmat * a.nblk;
     const int s = blockIdx.x / per, t = blockIdx.x % per;
     const int mat = a.mat0 + t / a.nblk, blk = t % a.nblk;
     const float* G = a.G + s * a.g_stride + mat * a.dm;
     float* M = a.M ? a.M + s * a.m_stride + mat * a.dm : nullptr;
+    T* Xh = a.Xhi ? a.Xhi + s * a.x_stride + mat * a.dm : nullptr;
+    T* Xl = a.Xhi ? a.Xlo + s * a.x_stride + mat * a.dm : nullptr;
     float ss = 0.f;
     const int64_t e0 = (int64_t)blk * kPrepElems;
     // all loads first (an index past the matrix reads its last element and is not used), then the
@@ -465,6 +476,13 @@ __global__ __launch_bounds__(kThreads) void k_muon_prep(PrepArgs a) {
                 u = a.beta * mv[j] + u;
                 M[e] = u;
             }
+            if constexpr (sizeof(T) == 2) {
+                if (Xh) {
+                    const uint16_t h = f2bf(u);
+                    Xh[e] = h;
+                    Xl[e] = f2bf(u - bf2f(h));
+                }
+            }
             ss += u * u;
         }
     }
@@ -473,45 +491,39 @@ __global__ __launch_bounds__(kThreads) void k_muon_prep(PrepArgs a) {
 }
 
 template <typename T> struct NSArgs {
-    const float* U; int64_t u_stride;     // G or M (init only)
-    const float* part; int nblk;          // partial sums (init only)
-    float* Xf; int64_t x_stride;          // fp32 iterate
-    const T* Xin; T* Xout;                // io-dtype copies (ping-pong), stride x_stride
+    const float* U; int64_t u_stride;     // k_ns_init only: U
+    const float* part; int nblk;          // partial sums of U^2 on the first step (and k_ns_init), else null
+    const T* Xin; T* Xout;                // hi planes (ping-pong), stride x_stride
+    T* Xlo;                               // bf16 mode: lo plane, updated in place; fp32 mode: null
+    float* Xf;                            // fp32 result (last step in bf16 mode, k_ns_init), else null
+    int64_t x_stride;
     T* Gram; int64_t gram_stride;         // 3 x p*p
     int d, m, mat0, nmat, tiles;          // tiles per matrix
 };
 
+// s = 1 / (||U||_F + 1e-7) from nblk partial sums; every lane of every wave gets the same value
+__device__ __forceinline__ float ns_scale(const float* part, int nblk) {
+    float t = 0.f;
+    for (int i = threadIdx.x & 63; i < nblk; i += 64) t += part[i];
+    return 1.0f / (sqrtf(wave_sum(t)) + 1e-7f);
+}
+
+// Zero Newton-Schulz steps: X = U / (||U||_F + 1e-7) in fp32.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_ns_init(NSArgs<T> a) {
-    __shared__ float tot_s;
     const int64_t dm = (int64_t)a.d * a.m;
     const int per = a.nmat * a.nblk;
     const int s = blockIdx.x / per, t = blockIdx.x % per;
     const int mat = a.mat0 + t / a.nblk, blk = t % a.nblk;
-    if (threadIdx.x == 0) {
-        const float* p = a.part + ((int64_t)s * 3 + mat) * a.nblk;
-        float tot = 0.f;
-        for (int i = 0; i < a.nblk; ++i) tot += p[i];
-        tot_s = tot;
-    }
-    __syncthreads();
-    const float inv = 1.0f / (sqrtf(tot_s) + 1e-7f);
+    const float inv = ns_scale(a.part + ((int64_t)s * 3 + mat) * a.nblk, a.nblk);
     const float* U = a.U + s * a.u_stride + mat * dm;
     float* Xf = a.Xf + s * a.x_stride + mat * dm;
-    T* Xo = a.Xout + s * a.x_stride + mat * dm;
     const int64_t e0 = (int64_t)blk * kPrepElems;
     constexpr int NI = kPrepElems / kThreads;
-    float u[NI];
-#pragma unroll
-    for (int j = 0; j < NI; ++j) u[j] = U[min(e0 + threadIdx.x + j * kThreads, dm - 1)];
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
         const int64_t e = e0 + threadIdx.x + j * kThreads;
-        if (e < dm) {
-            const float x = u[j] * inv;
-            Xf[e] = x;
-            Xo[e] = Elt<T>::st(x);
-        }
+        if (e < dm) Xf[e] = U[e] * inv;
     }
 }
 
@@ -547,12 +559,17 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 3 : 2) void k_ns_gram(NS
     T* Gm = a.Gram + s * a.gram_stride + (int64_t)mat * p * p;
     T* tT = reinterpret_cast<T*>(smem);
     auto epi = [&](auto& tl) {
+        float sc2 = 1.0f;
+        if (a.part) {
+            const float sc = ns_scale(a.part + ((int64_t)s * 3 + mat) * a.nblk, a.nblk);
+            sc2 = sc * sc;
+        }
         tl.for_each([&](const float (&v)[1], int row, int col) {
-            if (i0 + row < p && j0 + col < p) Gm[(uint32_t)(i0 + row) * (uint32_t)p + (uint32_t)(j0 + col)] = Elt<T>::st(v[0]);
+            if (i0 + row < p && j0 + col < p) Gm[(uint32_t)(i0 + row) * (uint32_t)p + (uint32_t)(j0 + col)] = Elt<T>::st(v[0] * sc2);
         });
         if (i0 == j0) return;
         lds_barrier();  // every wave is done with the LDS stage
-        tl.for_each([&](const float (&v)[1], int row, int col) { tT[col * kTP + row] = Elt<T>::st(v[0]); });
+        tl.for_each([&](const float (&v)[1], int row, int col) { tT[col * kTP + row] = Elt<T>::st(v[0] * sc2); });
         __syncthreads();
         // mirror block: Gram row j0 + cc, columns i0 .. i0 + TS - 1, from LDS row cc
         constexpr int VEC = 16 / (int)sizeof(T), VPR = TS / VEC;
@@ -578,10 +595,40 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 3 : 2) void k_ns_gram(NS
     }
 }
 
-// X <- 1.5 X - 0.5 P with P = X Gram (tall) or Gram X (wide).  The fp32 iterate values this thread
-// updates are loaded before the contraction, so their latency hides behind it.
+// Four consecutive iterate values at one position: hi and lo planes (bf16) or the fp32 plane.
+template <typename T> struct NSQuad;
+template <> struct NSQuad<uint16_t> {
+    typedef uint32_t raw __attribute__((ext_vector_type(2)));
+    raw h, l;
+    __device__ void load(const uint16_t* hi, const uint16_t* lo, uint32_t e) {
+        h = *reinterpret_cast<const raw*>(hi + e);
+        l = *reinterpret_cast<const raw*>(lo + e);
+    }
+    __device__ static float lo16(uint32_t w) { return __uint_as_float(w << 16); }
+    __device__ static float hi16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+    __device__ float4 value() const {
+        return make_float4(lo16(h.x) + lo16(l.x), hi16(h.x) + hi16(l.x), lo16(h.y) + lo16(l.y), hi16(h.y) + hi16(l.y));
+    }
+    __device__ static void store(uint16_t* hi, uint16_t* lo, uint32_t e, float4 x) {
+        const uint16_t h0 = f2bf(x.x), h1 = f2bf(x.y), h2 = f2bf(x.z), h3 = f2bf(x.w);
+        *reinterpret_cast<raw*>(hi + e) = raw{(uint32_t)h0 | ((uint32_t)h1 << 16), (uint32_t)h2 | ((uint32_t)h3 << 16)};
+        Pack4<uint16_t>::store(lo + e, x.x - bf2f(h0), x.y - bf2f(h1), x.z - bf2f(h2), x.w - bf2f(h3));
+    }
+};
+template <> struct NSQuad<float> {
+    float4 h;
+    __device__ void load(const float* hi, const float*, uint32_t e) { h = *reinterpret_cast<const float4*>(hi + e); }
+    __device__ float4 value() const { return h; }
+    __device__ static void store(float* hi, float*, uint32_t e, float4 x) { *reinterpret_cast<float4*>(hi + e) = x; }
+};
+
+// X <- s (1.5 X - 0.5 P) with P = X Gram (tall) or Gram X (wide), s = 1 except on the first step.
+// The iterate values this thread updates are loaded before the contraction, so their latency hides
+// behind it.  Each position belongs to one tile, so the lo plane is read and rewritten in place;
+// the hi plane is read by every tile's contraction and is written to the other buffer.
 template <typename T>
 __global__ __launch_bounds__(kThreads, 2) void k_ns_step(NSArgs<T> a) {
+    constexpr bool kLo = sizeof(T) == 2;
     __shared__ __attribute__((aligned(16))) char smem[NSStepTall<T>::LDS];
     const int64_t dm = (int64_t)a.d * a.m;
     const int per = a.nmat * a.tiles;
@@ -595,37 +642,64 @@ __global__ __launch_bounds__(kThreads, 2) void k_ns_step(NSArgs<T> a) {
     const int nct = (c + kNSStepCols - 1) / kNSStepCols;
     const int r0 = (t / nct) * kNSStepRows, c0 = (t % nct) * kNSStepCols;
     if (r0 >= r) return;  // a.tiles covers the larger of the tall and wide tilings
-    const T* X = a.Xin + s * a.x_stride + mat * dm;
+    const int64_t base = (int64_t)s * a.x_stride + (int64_t)mat * dm;
+    const T* X = a.Xin + base;
     const T* Gm = a.Gram + s * a.gram_stride + (int64_t)mat * p * p;
-    float* Xf = a.Xf + s * a.x_stride + mat * dm;
-    T* Xo = a.Xout + s * a.x_stride + mat * dm;
-    // Offsets are 32-bit from the tile corner.  The iterate loads are unconditional (an out-of-range
-    // position reads the corner, and its result is never stored), so all of them stay in flight
-    // during the contraction instead of each waiting behind a bounds-check branch.
-    float* Xft = Xf + (int64_t)r0 * c + c0;
-    T* Xot = Xo + (int64_t)r0 * c + c0;
+    // this tile's own positions, as 32-bit offsets from its corner
+    const int64_t corner = base + (int64_t)r0 * c + c0;
+    const T* Xh = a.Xin + corner;
+    T* Xl = kLo ? a.Xlo + corner : nullptr;
+    T* Xo = a.Xout + corner;
+    float* Xf = a.Xf ? a.Xf + corner : nullptr;
+    auto scale = [&]() {
+        return a.part ? ns_scale(a.part + ((int64_t)s * 3 + mat) * a.nblk, a.nblk) : 1.0f;
+    };
     auto body = [&](auto& tl, const auto& A, const auto& B, int K) {
         using TT = typename std::remove_reference<decltype(tl)>::type;
-        const bool full = r0 + TT::BM <= r && c0 + TT::BN <= c;
-        float xv[TT::ELEMS];
-        TT::for_each_pos([&](int idx, int row, int col) {
-            const bool in = full || (r0 + row < r && c0 + col < c);
-            xv[idx] = Xft[in ? (uint32_t)row * (uint32_t)c + (uint32_t)col : 0u];
-        });
-        tl.template run<PM1>(A, B, K, smem);
-        auto epi = [&](auto check) {
+        if (r0 + TT::BM <= r && c0 + TT::BN <= c) {
+            // full tiles: rows gathered in LDS, the iterate read and written four elements at a time
+            static_assert(TT::RV_LDS <= (int)sizeof(smem), "row bands fit the tile's LDS");
+            NSQuad<T> xv[TT::RV_N];
+            TT::rows_via_lds_pos([&](int idx, int, int row, int col) {
+                xv[idx].load(Xh, Xl, (uint32_t)row * (uint32_t)c + (uint32_t)col);
+            });
+            tl.template run<PM1>(A, B, K, smem);
+            const float sc = scale();
+            tl.rows_via_lds(smem, [&](int idx, int, int row, int col, const float4& v) {
+                const float4 x = xv[idx].value();
+                const float4 xn = make_float4(sc * (1.5f * x.x - 0.5f * v.x), sc * (1.5f * x.y - 0.5f * v.y),
+                                              sc * (1.5f * x.z - 0.5f * v.z), sc * (1.5f * x.w - 0.5f * v.w));
+                const uint32_t e = (uint32_t)row * (uint32_t)c + (uint32_t)col;
+                if (Xf) *reinterpret_cast<float4*>(Xf + e) = xn;
+                else NSQuad<T>::store(Xo, Xl, e, xn);
+            });
+        } else {
+            // partial tiles, element by element; a position outside the matrix reads the corner and
+            // is not stored
+            float xv[TT::ELEMS];
+            TT::for_each_pos([&](int idx, int row, int col) {
+                const bool in = r0 + row < r && c0 + col < c;
+                const uint32_t e = in ? (uint32_t)row * (uint32_t)c + (uint32_t)col : 0u;
+                if constexpr (kLo) xv[idx] = bf2f(Xh[e]) + bf2f(Xl[e]);
+                else xv[idx] = Xh[e];
+            });
+            tl.template run<PM1>(A, B, K, smem);
+            const float sc = scale();
             int idx = 0;
             tl.for_each([&](const float (&v)[1], int row, int col) {
-                const float xn = 1.5f * xv[idx++] - 0.5f * v[0];
-                if (!decltype(check)::value || (r0 + row < r && c0 + col < c)) {
+                const float xn = sc * (1.5f * xv[idx++] - 0.5f * v[0]);
+                if (r0 + row < r && c0 + col < c) {
                     const uint32_t e = (uint32_t)row * (uint32_t)c + (uint32_t)col;
-                    Xft[e] = xn;
-                    Xot[e] = Elt<T>::st(xn);
+                    if (Xf) {
+                        Xf[e] = xn;
+                    } else {
+                        const T h = Elt<T>::st(xn);
+                        Xo[e] = h;
+                        if constexpr (kLo) Xl[e] = f2bf(xn - bf2f(h));
+                    }
                 }
             });
-        };
-        if (full) epi(std::false_type{});
-        else epi(std::true_type{});
+        }
     };
     if (r > c) {  // P = X Gram; Gram is symmetric, so its rows serve as the B operand
         NSStepTall<T> tl;
@@ -633,29 +707,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_ns_step(NSArgs<T> a) {
         const Opnd<T> B[1] = {{Gm + (int64_t)c0 * p, p, c - c0, p}};
         body(tl, A, B, c);
     } else {      // P = Gram X; B[j][i] = X[i][j] is read k-strided
-        using TW = NSStepWide<T>;
-        TW tl;
+        NSStepWide<T> tl;
         const Opnd<T> A[1] = {{Gm + (int64_t)r0 * p, p, r - r0, p}};
         const Opnd<T> B[1] = {{X + c0, c, c - c0, r}};
-        if (r0 + TW::BM <= r && c0 + TW::BN <= c) {
-            // full tiles: the k-strided staging permutes the columns, so rows are gathered in LDS
-            // and the iterate is read and written four consecutive elements at a time
-            static_assert(TW::RV_LDS <= (int)sizeof(smem), "row bands fit the tile's LDS");
-            float4 xv[TW::RV_N];
-            TW::rows_via_lds_pos([&](int idx, int, int row, int col) {
-                xv[idx] = *reinterpret_cast<const float4*>(Xft + (uint32_t)row * (uint32_t)c + (uint32_t)col);
-            });
-            tl.template run<PM1>(A, B, r, smem);
-            tl.rows_via_lds(smem, [&](int idx, int, int row, int col, const float4& v) {
-                const float x0 = 1.5f * xv[idx].x - 0.5f * v.x, x1 = 1.5f * xv[idx].y - 0.5f * v.y;
-                const float x2 = 1.5f * xv[idx].z - 0.5f * v.z, x3 = 1.5f * xv[idx].w - 0.5f * v.w;
-                const uint32_t e = (uint32_t)row * (uint32_t)c + (uint32_t)col;
-                *reinterpret_cast<float4*>(Xft + e) = make_float4(x0, x1, x2, x3);
-                Pack4<T>::store(Xot + e, x0, x1, x2, x3);
-            });
-        } else {
-            body(tl, A, B, r);
-        }
+        body(tl, A, B, r);
     }
 }
 
@@ -692,7 +747,7 @@ static int grad_split(int64_t S, int gtiles, int64_t lu) {
 }
 
 struct Layout {
-    size_t wf[2], sh[2], hq, hke, da, dc, g, xf, xb[2], gram, part, mom, total;
+    size_t wf[2], sh[2], hq, hke, da, dc, g, xf, xb[2], xlo, gram, part, mom, total;
     int64_t wf_stride, sh_stride, inter_stride, g_stride, x_stride, gram_stride;
     int nblk, gparts;
 };
@@ -727,6 +782,7 @@ static Layout make_layout(const ttt_desc& D, bool muon, bool own_m) {
         L.xf = take(S * L.x_stride * 4);
         L.xb[0] = take(S * L.x_stride * es);
         L.xb[1] = take(S * L.x_stride * es);
+        if (es == 2) L.xlo = take(S * L.x_stride * es);
         L.gram = take(S * L.gram_stride * es);
     }
     if (own_m) L.mom = take(S * 3 * dm * 4);
@@ -856,25 +912,37 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
             if (a.lu == 0) continue;
             const int mat0 = D.last_layer_only ? 2 : 0, nmat = D.last_layer_only ? 1 : 3;
             const float* U = G;
+            T* Xb[2] = {(T*)(ws + L.xb[0]), (T*)(ws + L.xb[1])};
+            T* Xlo = sizeof(T) == 2 ? (T*)(ws + L.xlo) : nullptr;
+            float* Xf = (float*)(ws + L.xf);
+            // bf16 Newton-Schulz starts from U's hi + lo planes, which prep writes (hi into Xb[1])
+            const bool split = muon && sizeof(T) == 2 && D.ns_iters > 0;
             if (muon || mom) {
-                PrepArgs pa{G, L.g_stride, M, 3 * dm, D.momentum, part, L.nblk, dm, mat0, nmat};
+                PrepArgs<T> pa{G, L.g_stride, M, 3 * dm, D.momentum, part, L.nblk, split ? Xb[1] : nullptr,
+                               split ? Xlo : nullptr, L.x_stride, dm, mat0, nmat};
                 {
                     ProfScope ps(PK_MUON_PREP, st);
-                    hipLaunchKernelGGL(k_muon_prep, dim3(S * nmat * L.nblk), dim3(kThreads), 0, st, pa);
+                    hipLaunchKernelGGL(k_muon_prep<T>, dim3(S * nmat * L.nblk), dim3(kThreads), 0, st, pa);
                 }
                 if ((rc = check_launch("k_muon_prep")) != TTT_OK) return rc;
                 if (mom) U = M;
             }
-            if (muon) {
-                T* Xb[2] = {(T*)(ws + L.xb[0]), (T*)(ws + L.xb[1])};
-                float* Xf = (float*)(ws + L.xf);
-                NSArgs<T> na{U, 3 * dm, part, L.nblk, Xf, L.x_stride, Xb[1], Xb[0], (T*)(ws + L.gram), L.gram_stride,
+            if (muon && D.ns_iters == 0) {
+                NSArgs<T> na{U, 3 * dm, part, L.nblk, nullptr, nullptr, nullptr, Xf, L.x_stride, nullptr, 0,
                              d, m, mat0, nmat, 0};
                 {
                     ProfScope ps(PK_NS_INIT, st);
                     hipLaunchKernelGGL(k_ns_init<T>, dim3(S * nmat * L.nblk), dim3(kThreads), 0, st, na);
                 }
                 if ((rc = check_launch("k_ns_init")) != TTT_OK) return rc;
+                U = Xf;
+            } else if (muon) {
+                // step it reads hi plane Xin and writes Xout = Xb[it & 1]; the first step reads U's planes
+                // (fp32 mode: U itself, whose stride 3 d m is the iterate's) and scales by 1 / ||U||_F;
+                // in bf16 mode the last step writes fp32 into Xf
+                const T* first = sizeof(T) == 2 ? Xb[1] : reinterpret_cast<const T*>(U);
+                NSArgs<T> na{nullptr, 0, nullptr, L.nblk, first, Xb[0], Xlo, nullptr, L.x_stride, (T*)(ws + L.gram),
+                             L.gram_stride, d, m, mat0, nmat, 0};
                 const int p = d < m ? d : m;
                 // upper-triangle Gram tiles of 128, or of 64 when the 128-wide ones fill under 256 CUs
                 const bool gsmall = (int64_t)S * nmat * cdiv(p, 128) * (cdiv(p, 128) + 1) / 2 < 256;
@@ -884,8 +952,10 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
                 const int stt = (int)std::max(cdiv(m, kNSStepRows) * cdiv(d, kNSStepCols),
                                               cdiv(d, kNSStepRows) * cdiv(m, kNSStepCols));
                 for (int it = 0; it < D.ns_iters; ++it) {
-                    na.Xin = Xb[it & 1];
-                    na.Xout = Xb[(it + 1) & 1];
+                    na.Xin = it == 0 ? first : Xb[(it - 1) & 1];
+                    na.Xout = Xb[it & 1];
+                    na.part = it == 0 ? part : nullptr;
+                    na.Xf = (sizeof(T) == 2 && it == D.ns_iters - 1) ? Xf : nullptr;
                     na.tiles = gt;
                     {
                         ProfScope ps(PK_NS_GRAM, st);
@@ -900,7 +970,7 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
                     }
                     if ((rc = check_launch("k_ns_step")) != TTT_OK) return rc;
                 }
-                U = Xf;
+                U = sizeof(T) == 2 ? Xf : reinterpret_cast<const float*>(Xb[(D.ns_iters - 1) & 1]);
             }
             const int norm = (D.rule == TTT_UPD_GD_L2 || D.rule == TTT_UPD_MUON_L2) ? 1 : 0;
             UpdArgs<T> u{Wf[cur], L.wf_stride, 0, D.H, U, 3 * dm, Wf[cur ^ 1], L.wf_stride, sh[cur ^ 1], L.sh_stride,

@@ -118,6 +118,22 @@ def test_muon_gram_mirror_fp32():
     run_small(21, 8, 4, 128, 160, 320, 128, O.MASK_APPLY_THEN_UPDATE, O.UPD_MUON_L2, False, ns=2)
 
 
+def test_newton_schulz_tiles_bf16():
+    # d = 160, m = 320: W1/W3 take the tall step (320 x 160) and W2 the wide one (160 x 320), each
+    # with full 128 x 64 step tiles beside ragged ones; the iterate is the bf16 hi + lo pair
+    run_small(24, 1, 1, 256, 160, 320, 128, O.MASK_APPLY_THEN_UPDATE, O.UPD_MUON_L2, True, ns=3)
+    run_small(25, 1, 2, 300, 160, 320, 128, O.MASK_UPDATE_THEN_APPLY, O.UPD_MUON, True, momentum=0.9, ns=5)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("ns", [0, 1])
+def test_newton_schulz_step_counts(ns, bf16):
+    # no step (only the Frobenius scaling), and one step, which is both the first (it applies the
+    # scaling) and the last (it writes the fp32 result)
+    run_small(26 + ns, 1, 1, 256, 160, 320, 128, O.MASK_APPLY_THEN_UPDATE, O.UPD_MUON_L2, bf16, momentum=0.9,
+              ns=ns)
+
+
 @pytest.mark.parametrize("bf16", [False, True])
 def test_inner_steps_and_ascent(bf16):
     # several gradient steps per updating chunk, and gradient ascent, against the oracle; N = 300
