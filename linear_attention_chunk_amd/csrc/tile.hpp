@@ -346,19 +346,25 @@ struct Tile {
         SB b[NB];
     };
 
-    template <bool FULL>
+    // SYM: the B operand is the A operand (a tile on the diagonal of A A^T); only A is loaded and
+    // staged, and compute() reads the B fragments from A's rows
+    template <bool FULL, bool SYM = false>
     __device__ __forceinline__ static void issue(Regs& g, const Opnd<T> (&A)[NA], const Opnd<T> (&B)[NB], int k0) {
 #pragma unroll
         for (int a = 0; a < NA; ++a) g.a[a].template load<FULL>(A[a], k0);
+        if constexpr (!SYM) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b) g.b[b].template load<FULL>(B[b], k0);
+            for (int b = 0; b < NB; ++b) g.b[b].template load<FULL>(B[b], k0);
+        }
     }
-    template <bool FULL>
+    template <bool FULL, bool SYM = false>
     __device__ __forceinline__ static void put(const Regs& g, char* st) {
 #pragma unroll
         for (int a = 0; a < NA; ++a) g.a[a].template store<FULL>(st + a * A_BYTES);
+        if constexpr (!SYM) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b) g.b[b].template store<FULL>(st + NA * A_BYTES + b * B_BYTES);
+            for (int b = 0; b < NB; ++b) g.b[b].template store<FULL>(st + NA * A_BYTES + b * B_BYTES);
+        }
     }
 
     // Whether every row and k of a tile over these operands is in range (then the stagers need
@@ -388,7 +394,7 @@ struct Tile {
     // and the loads of stage s + 2 are in flight.  With a single set, every load outstanding when a
     // stage is stored belongs to that stage, so the compiler's wait before the LDS store is exact
     // (with two sets its conservative count across the loop edge also waited for the newer set).
-    template <class PM, bool FULL>
+    template <class PM, bool FULL, bool SYM = false>
     __device__ __forceinline__ void run_(const Opnd<T> (&A)[NA], const Opnd<T> (&B)[NB], int K, char* lds,
                                          bool keep = false) {
         if (K <= 0) {
@@ -396,13 +402,13 @@ struct Tile {
             return;
         }
         Regs g;
-        issue<FULL>(g, A, B, 0);
-        run_issued<PM, FULL>(g, A, B, K, lds, keep);
+        issue<FULL, SYM>(g, A, B, 0);
+        run_issued<PM, FULL, SYM>(g, A, B, K, lds, keep);
     }
     // The same with stage 0 already issued into g (issue<FULL>(g, A, B, 0) with the same FULL), so
     // that a caller can start a tile's first loads early.  K must be positive.  On entry every wave
     // must be done reading the LDS stages.
-    template <class PM, bool FULL>
+    template <class PM, bool FULL, bool SYM = false>
     __device__ __forceinline__ void run_issued(Regs& g, const Opnd<T> (&A)[NA], const Opnd<T> (&B)[NB], int K,
                                                char* lds, bool keep = false) {
         if (!keep) zero();
@@ -410,27 +416,27 @@ struct Tile {
         if constexpr (NBUF == 1) {
             // one LDS stage: the loads of stage s + 1 are in flight while stage s is computed; the
             // stage is stored once every wave has finished reading the previous one
-            put<FULL>(g, lds);
-            if (nk > 1) issue<FULL>(g, A, B, KSTEP);
+            put<FULL, SYM>(g, lds);
+            if (nk > 1) issue<FULL, SYM>(g, A, B, KSTEP);
             lds_barrier();
             for (int s = 0; s < nk; ++s) {
-                compute<PM>(lds);
+                compute<PM, SYM>(lds);
                 if (s + 1 < nk) {
                     lds_barrier();
-                    put<FULL>(g, lds);
-                    if (s + 2 < nk) issue<FULL>(g, A, B, (s + 2) * KSTEP);
+                    put<FULL, SYM>(g, lds);
+                    if (s + 2 < nk) issue<FULL, SYM>(g, A, B, (s + 2) * KSTEP);
                     lds_barrier();
                 }
             }
             return;
         }
-        put<FULL>(g, lds);
-        if (nk > 1) issue<FULL>(g, A, B, KSTEP);
+        put<FULL, SYM>(g, lds);
+        if (nk > 1) issue<FULL, SYM>(g, A, B, KSTEP);
         lds_barrier();
         for (int s = 0; s < nk; ++s) {
-            compute<PM>(lds + (s & 1) * STAGE);
-            if (s + 1 < nk) put<FULL>(g, lds + ((s + 1) & 1) * STAGE);
-            if (s + 2 < nk) issue<FULL>(g, A, B, (s + 2) * KSTEP);
+            compute<PM, SYM>(lds + (s & 1) * STAGE);
+            if (s + 1 < nk) put<FULL, SYM>(g, lds + ((s + 1) & 1) * STAGE);
+            if (s + 2 < nk) issue<FULL, SYM>(g, A, B, (s + 2) * KSTEP);
             lds_barrier();
         }
     }
@@ -442,8 +448,15 @@ struct Tile {
         if (full(A, B, K)) run_<PM, true>(A, B, K, lds, keep);
         else run_<PM, false>(A, B, K, lds, keep);
     }
-
+    // A tile on the diagonal of A A^T: run() with B = A, loading and staging A only
     template <class PM>
+    __device__ __forceinline__ void run_sym(const Opnd<T> (&A)[NA], int K, char* lds) {
+        static_assert(NA == 1 && NB == 1 && BM == BN && KSA == KSB && !SCALE_A, "B must stage exactly like A");
+        if (full(A, A, K)) run_<PM, true, true>(A, A, K, lds);
+        else run_<PM, false, true>(A, A, K, lds);
+    }
+
+    template <class PM, bool SYM = false>
     __device__ __forceinline__ void compute(const char* st) {
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
         const int wm = wave / WGN, wn = wave % WGN;
@@ -462,7 +475,7 @@ struct Tile {
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
                     bfr[b][j] = *reinterpret_cast<const u32x4_t*>(
-                        st + NA * A_BYTES + b * B_BYTES + (wn * WN + j * 32 + lrow) * PITCH + win * 32 + lk);
+                        st + (SYM ? 0 : NA * A_BYTES + b * B_BYTES) + (wn * WN + j * 32 + lrow) * PITCH + win * 32 + lk);
 #pragma unroll
             for (int p = 0; p < NP; ++p)
 #pragma unroll

@@ -580,17 +580,20 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 3 : 2) void k_ns_gram(NS
                     *reinterpret_cast<const u32x4_t*>(tT + cc * kTP + x);
         }
     };
+    // a diagonal tile's two operands are the same rows of X, staged once
     if (r > c) {  // Gram = X^T X (c x c), contracted over the r rows
         NSTile<T, true, TS> tl;
         const Opnd<T> A[1] = {{X + i0, c, c - i0, r}};
         const Opnd<T> B[1] = {{X + j0, c, c - j0, r}};
-        tl.template run<PM1>(A, B, r, smem);
+        if (i0 == j0) tl.template run_sym<PM1>(A, r, smem);
+        else tl.template run<PM1>(A, B, r, smem);
         epi(tl);
     } else {      // Gram = X X^T (r x r), contracted over the c columns
         NSTile<T, false, TS> tl;
         const Opnd<T> A[1] = {{X + (int64_t)i0 * c, c, r - i0, c}};
         const Opnd<T> B[1] = {{X + (int64_t)j0 * c, c, r - j0, c}};
-        tl.template run<PM1>(A, B, c, smem);
+        if (i0 == j0) tl.template run_sym<PM1>(A, c, smem);
+        else tl.template run<PM1>(A, B, c, smem);
         epi(tl);
     }
 }
