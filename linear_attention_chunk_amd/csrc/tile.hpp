@@ -461,6 +461,7 @@ struct Tile {
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
         const int wm = wave / WGN, wn = wave % WGN;
         const int lrow = lane & 31, lk = (lane >> 5) * 16;
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int win = 0; win < SEG * 2; ++win) {  // 32-byte k windows
             u32x4_t af[NA][FM], bfr[NB][FN];
@@ -483,6 +484,7 @@ struct Tile {
 #pragma unroll
                     for (int j = 0; j < FN; ++j) Mma32<T>::mma(acc[p][i][j], af[PM::a[p]][i], bfr[PM::b[p]][j]);
         }
+        __builtin_amdgcn_s_setprio(0);
     }
 
     static constexpr int ELEMS = FM * FN * 16;  // accumulator elements per thread and accumulator
