@@ -24,7 +24,7 @@ EXPORTS = (
     "ttt_profile_enable", "ttt_profile_select", "ttt_profile_read", "ttt_profile_kernel_name",
     "ttt_probe_mfma_bf16",
 )
-PROF_KERNELS = 11
+PROF_KERNELS = 12
 
 
 class TttDesc(ctypes.Structure):
@@ -34,7 +34,7 @@ class TttDesc(ctypes.Structure):
         ("io_dtype", c_int32), ("mask", c_int32), ("rule", c_int32),
         ("ns_iters", c_int32), ("momentum", c_float), ("last_layer_only", c_int32),
         ("w0_per_batch", c_int32), ("update_chunks", c_void_p),
-        ("inner_steps", c_int32), ("ascent", c_int32),
+        ("inner_steps", c_int32), ("ascent", c_int32), ("parallel_form", c_int32),
     ]
 
 

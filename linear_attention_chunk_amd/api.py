@@ -50,14 +50,14 @@ def unpack_weights(W: torch.Tensor, d: int, m: int):
 
 def ttt_desc(B, H, N, d_h, m_h, chunk, io_dtype, mask, rule, ns_iters=5, momentum=0.0, last_layer_only=False,
              w0_per_batch=False, update_chunks: Optional[Sequence[int]] = None, inner_steps: int = 1,
-             ascent: bool = False):
+             ascent: bool = False, parallel_form: bool = False):
     """A filled TttDesc plus the host buffer that keeps update_chunks alive."""
     flags = None
     if update_chunks is not None:
         flags = (ctypes.c_uint8 * len(update_chunks))(*[1 if f else 0 for f in update_chunks])
     D = C.TttDesc(B, H, N, d_h, m_h, chunk, io_dtype, mask, rule, ns_iters, float(momentum), int(last_layer_only),
                   int(w0_per_batch), ctypes.cast(flags, ctypes.c_void_p) if flags is not None else None,
-                  int(inner_steps), int(ascent))
+                  int(inner_steps), int(ascent), int(parallel_form))
     return D, flags
 
 
@@ -72,12 +72,13 @@ def ttt_forward(q, k, v, eta, W0, chunk: int, mask_mode: int = C.MASK_APPLY_THEN
                 momentum: float = 0.0, last_layer_only: bool = False, update_chunks=None,
                 M: Optional[torch.Tensor] = None, want_W: bool = True, out: Optional[torch.Tensor] = None,
                 workspace: Optional[torch.Tensor] = None, stream=None, inner_steps: int = 1,
-                ascent: bool = False):
+                ascent: bool = False, parallel_form: bool = False):
     """The TTT-KVB layer through ttt_forward of libttt.so.
 
     q, k, v [B, H, N, d] (bf16 or fp32, same dtype); eta [B, H, N] fp32; W0 fp32 [H, 3*d*m] or
     [B, H, 3*d*m] (see pack_weights).  M, if given, is the [B, H, 3*d*m] fp32 momentum, updated
-    in place.  Returns (o, W_out or None).
+    in place.  parallel_form (last_layer_only with plain GD only) computes the same layer as
+    chunked linear attention over the frozen SwiGLU features.  Returns (o, W_out or None).
     """
     B, H, N, d = q.shape
     dev = q.device
@@ -98,7 +99,7 @@ def ttt_forward(q, k, v, eta, W0, chunk: int, mask_mode: int = C.MASK_APPLY_THEN
             not per_batch and (W0.dim() != 2 or W0.shape[0] != H)):
         raise ValueError("W0 must be [H, 3*d*m] or [B, H, 3*d*m]")
     D, keep = ttt_desc(B, H, N, d, m_h, chunk, _DT[q.dtype], mask_mode, update_rule, ns_iters, momentum,
-                       last_layer_only, per_batch, update_chunks, inner_steps, ascent)
+                       last_layer_only, per_batch, update_chunks, inner_steps, ascent, parallel_form)
     o = torch.empty_like(q) if out is None else out
     _need(o, "out", q.dtype, dev)
     W_out = torch.empty((B, H, 3 * d * m_h), dtype=torch.float32, device=dev) if want_W else None

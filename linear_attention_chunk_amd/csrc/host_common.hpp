@@ -24,7 +24,7 @@ inline ttt_status fail(ttt_status s, const char* fmt, ...) {
 
 // kernel classes of the optional launch profiler (ttt_profile_*)
 enum ProfKernel { PK_UP = 0, PK_DOWN, PK_UPDATE, PK_MUON_PREP, PK_NS_INIT, PK_NS_GRAM, PK_NS_STEP, PK_LINATTN,
-                  PK_LIN_DELTA, PK_LIN_SCAN, PK_LIN_APPLY };
+                  PK_LIN_DELTA, PK_LIN_SCAN, PK_LIN_APPLY, PK_PHI };
 
 // Brackets one launch with events on its stream while profiling is enabled; no-op otherwise.
 struct ProfScope {
@@ -51,5 +51,31 @@ inline bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// The chunk-parallel linear-attention path (chunked masks) as a building block, also used by the
+// TTT layer's parallel form.  State of scan s on entry: S0 + (s0_heads ? s % s0_heads : s) *
+// s0_stride (zero if S0 is null); on exit it goes to Sout + s * sout_stride (if not null).  Each
+// updating chunk then adds, reps times, u = dsign * dS_c, either directly (S <- S + u) or, with
+// mom, through a running term m <- beta m + u, S <- S + m, where m starts as msign * M0[s]
+// (zero if M0 is null) and leaves as msign * m in Mout[s] (both m_stride apart).
+struct LinStateIO {
+    const float* S0 = nullptr;
+    int64_t s0_stride = 0;
+    int s0_heads = 0;
+    float* Sout = nullptr;
+    int64_t sout_stride = 0;
+    const float* M0 = nullptr;
+    float* Mout = nullptr;
+    int64_t m_stride = 0;
+    int mom = 0;
+    float beta = 0.f, msign = 1.f, dsign = 1.f;
+    int reps = 1;
+};
+// workspace of lin_chunked_run: dS_c (fp32) and S_c (bf16 hi + lo, or fp32) per chunk
+size_t lin_chunked_ws_bytes(int64_t nscan, int64_t nchunks, int d_k, int d_v);
+// D.mask is a chunked mask (not TOKEN_CAUSAL); flags holds the strided update bits (bit j = chunk j)
+template <typename T>
+ttt_status lin_chunked_run(const linattn_desc& D, const uint32_t (&flags)[32], const T* q, const T* k, const T* v,
+                           const float* eta, T* o, const LinStateIO& io, char* ws, hipStream_t st);
 
 }  // namespace ttt

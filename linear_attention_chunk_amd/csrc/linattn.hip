@@ -448,9 +448,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_lin_delta(DeltaArgs<T> a) {
 // The state each chunk's queries see, from S0 and the chunk updates dS_c: before chunk c's own
 // update (apply-then-update, strided) or after it (update-then-apply, full).  One thread owns 4
 // consecutive elements of one scan's state and walks the chunks.  bf16 io keeps the state as a
-// hi + lo pair of bf16 planes (about 16 bits), fp32 io as one fp32 plane.
+// hi + lo pair of bf16 planes (about 16 bits), fp32 io as one fp32 plane.  The entry/exit strides,
+// the momentum term, the repeats and the sign are those of LinStateIO.
 template <typename T> struct ScanArgs {
-    const float* dS; const float* S0; T* Sc; float* Sout;
+    const float* dS; T* Sc;
+    LinStateIO io;
     int64_t dvk;   // d_v * d_k
     int nc, mode, nscan;
     uint32_t flags[32];
@@ -463,10 +465,16 @@ __global__ __launch_bounds__(kThreads) void k_lin_scan(ScanArgs<T> a) {
     const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (g >= per * a.nscan) return;
     const int64_t scan = g / per, e = (g % per) * 4;
-    f32x4_t st = {0.f, 0.f, 0.f, 0.f};
-    if (a.S0)  // S0 and S_out are only 4-byte aligned
+    const LinStateIO& io = a.io;
+    f32x4_t st = {0.f, 0.f, 0.f, 0.f}, mom = {0.f, 0.f, 0.f, 0.f};
+    if (io.S0) {  // S0, S_out and the momentum are only 4-byte aligned
+        const float* s0 = io.S0 + (io.s0_heads ? scan % io.s0_heads : scan) * io.s0_stride + e;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) st[u] = a.S0[scan * a.dvk + e + u];
+        for (int u = 0; u < 4; ++u) st[u] = s0[u];
+    }
+    if (io.M0)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) mom[u] = io.msign * io.M0[scan * io.m_stride + e + u];
     const bool post = a.mode == TTT_MASK_UPDATE_THEN_APPLY || a.mode == TTT_MASK_FULL;
     auto put = [&](int c) {
         T* dst = a.Sc + ((scan * a.nc + c) * PLANES) * a.dvk + e;
@@ -483,12 +491,25 @@ __global__ __launch_bounds__(kThreads) void k_lin_scan(ScanArgs<T> a) {
     for (int c = 0; c < a.nc; ++c) {
         const bool upd = a.mode != TTT_MASK_STRIDED || ((a.flags[c >> 5] >> (c & 31)) & 1u);
         if (!post) put(c);
-        if (upd) st += *reinterpret_cast<const f32x4_t*>(a.dS + (scan * a.nc + c) * a.dvk + e);
+        if (upd) {
+            const f32x4_t d = io.dsign * *reinterpret_cast<const f32x4_t*>(a.dS + (scan * a.nc + c) * a.dvk + e);
+            for (int r = 0; r < io.reps; ++r) {
+                if (io.mom) {
+                    mom = io.beta * mom + d;
+                    st += mom;
+                } else {
+                    st += d;
+                }
+            }
+        }
         if (post) put(c);
     }
-    if (a.Sout)
+    if (io.Sout)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) a.Sout[scan * a.dvk + e + u] = st[u];
+        for (int u = 0; u < 4; ++u) io.Sout[scan * io.sout_stride + e + u] = st[u];
+    if (io.Mout)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) io.Mout[scan * io.m_stride + e + u] = io.msign * mom[u];
 }
 
 // o (chunk c's tokens x d_v) = q_c S_c^T, contracting over d_k: bf16 as hi and lo products summed
@@ -716,21 +737,23 @@ static int64_t lin_block(const linattn_desc& D) {
     return D.mask == TTT_MASK_TOKEN_CAUSAL ? kCausalBlock : D.chunk;
 }
 
+size_t lin_chunked_ws_bytes(int64_t nscan, int64_t nchunks, int d_k, int d_v) {
+    return align256((size_t)(nscan * nchunks * (int64_t)d_v * d_k * 4)) * 2;  // dS_c (fp32), then S_c
+}
+
 static size_t lin_ws_bytes(const linattn_desc& D) {
     if (!lin_parallel(D)) return 0;
-    const int64_t S = (int64_t)D.B * D.H, nc = cdiv(D.N, lin_block(D)), dvk = (int64_t)D.d_v * D.d_k;
-    return align256((size_t)(S * nc * dvk * 4)) * 2;  // dS_c (fp32), then S_c (bf16 hi + lo, or fp32)
+    return lin_chunked_ws_bytes((int64_t)D.B * D.H, cdiv(D.N, lin_block(D)), D.d_k, D.d_v);
 }
 
 template <typename T>
-static ttt_status run_lin_parallel(const linattn_desc& D, LinArgs<T> a, char* ws, hipStream_t st) {
+static ttt_status run_lin_parallel(const linattn_desc& D, LinArgs<T> a, char* ws, hipStream_t st,
+                                   const LinStateIO& io) {
     const bool causal = D.mask == TTT_MASK_TOKEN_CAUSAL;
     const int64_t chunk = lin_block(D);
     const int64_t S = (int64_t)D.B * D.H, nc = cdiv(D.N, chunk), dvk = (int64_t)D.d_v * D.d_k;
     float* dS = (float*)ws;
     T* Sc = (T*)(ws + align256((size_t)(S * nc * dvk * 4)));
-    float* Sout = a.Sout;
-    const float* S0 = a.S0;  // read by the scan
     // 1. per-chunk updates
     DeltaArgs<T> da{};
     da.k = a.k;
@@ -755,9 +778,8 @@ static ttt_status run_lin_parallel(const linattn_desc& D, LinArgs<T> a, char* ws
     // 2. states seen by each chunk, and S_out
     ScanArgs<T> sa{};
     sa.dS = dS;
-    sa.S0 = S0;
     sa.Sc = Sc;
-    sa.Sout = Sout;
+    sa.io = io;
     sa.dvk = dvk;
     sa.nc = (int)nc;
     sa.mode = causal ? TTT_MASK_APPLY_THEN_UPDATE : D.mask;  // a causal block sees the state before it
@@ -793,6 +815,19 @@ static ttt_status run_lin_parallel(const linattn_desc& D, LinArgs<T> a, char* ws
     }
     return check_launch(causal ? "k_lin_apply_causal" : "k_lin_apply");
 }
+
+template <typename T>
+ttt_status lin_chunked_run(const linattn_desc& D, const uint32_t (&flags)[32], const T* q, const T* k, const T* v,
+                           const float* eta, T* o, const LinStateIO& io, char* ws, hipStream_t st) {
+    LinArgs<T> a{q, k, v, eta, io.S0, o, io.Sout, D.N, D.d_v, D.chunk, D.mask, 0, 0, {}};
+    for (int w = 0; w < 32; ++w) a.flags[w] = flags[w];
+    return run_lin_parallel<T>(D, a, ws, st, io);
+}
+template ttt_status lin_chunked_run<uint16_t>(const linattn_desc&, const uint32_t (&)[32], const uint16_t*,
+                                              const uint16_t*, const uint16_t*, const float*, uint16_t*,
+                                              const LinStateIO&, char*, hipStream_t);
+template ttt_status lin_chunked_run<float>(const linattn_desc&, const uint32_t (&)[32], const float*, const float*,
+                                           const float*, const float*, float*, const LinStateIO&, char*, hipStream_t);
 
 }  // namespace ttt
 
@@ -846,7 +881,14 @@ extern "C" ttt_status linattn_forward(const linattn_desc* desc, const void* q, c
         if (D.mask == TTT_MASK_STRIDED)
             for (int64_t j = 0; j < cdiv(D.N, D.chunk); ++j)
                 if (D.update_chunks[j]) a.flags[j >> 5] |= 1u << (j & 31);
-        if (need) return run_lin_parallel<T>(D, a, (char*)workspace, st);
+        if (need) {
+            LinStateIO io;
+            io.S0 = S0;
+            io.s0_stride = (int64_t)D.d_v * D.d_k;
+            io.Sout = S_out;
+            io.sout_stride = io.s0_stride;
+            return run_lin_parallel<T>(D, a, (char*)workspace, st, io);
+        }
         return run_lin<T>(D, a, st);
     };
     if (D.io_dtype == TTT_BF16) return go((uint16_t*)nullptr);

@@ -718,6 +718,64 @@ __global__ __launch_bounds__(kThreads, 2) void k_ns_step(NSArgs<T> a) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// Parallel static-kernel form (last layer only, plain GD).  With W1 and W3 frozen, the features
+// phi(x) = SiLU(W1 x) * (W3 x) stay fixed along the sequence, a chunk's W2 gradient is
+// -sum_i eta_i v_i phi(k_i)^T, and W2 follows chunked linear attention with queries phi(q), keys
+// phi(k), values v and state W2 ("TTT with KV Binding Is Secretly Linear Attention", Thm. 5.2 and
+// 5.3, Sec. 6.1, Table 2 Variant 2).  One launch computes the features of every token; the
+// chunk-parallel linear-attention kernels do the rest, with the recurrence's momentum, inner steps
+// and ascent folded into their state scan.
+
+// W1 | W3 (the first 2 d m floats of each fast-weight block) in bf16, as contraction operands
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_w13_cvt(const float* W0, int64_t w_stride, T* out, int64_t n4,
+                                                      int64_t per4) {
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= n4) return;
+    const int64_t h = i / per4, j = i % per4;
+    const float4 w = *reinterpret_cast<const float4*>(W0 + h * w_stride + 4 * j);
+    Pack4<T>::store(out + 4 * i, w.x, w.y, w.z, w.w);
+}
+
+template <typename T> struct PhiArgs {
+    const T* x[2]; T* phi[2];        // q and k [S][N][d], their features [S][N][m]
+    const T* W; int64_t w_stride;    // W1 of weight block hw at W + hw * w_stride, W3 d m after it
+    int w_heads;                     // hw = s % w_heads, or s when 0 (one block per scan)
+    int64_t N; int d, m, nscan, ntt, nct;  // token and hidden tiles per scan
+};
+
+// Tiles of 256 tokens x 128 hidden units on 8 waves, products x W1^T and x W3^T, as the query
+// tiles of k_up; the epilogue writes phi row-major (hidden units contiguous).
+template <typename T>
+__global__ __launch_bounds__(64 * kUpWaves, 1) void k_phi(PhiArgs<T> a) {
+    using TQ = Tile<T, kUpQRows, kUpCols, 2, 4, 1, 2, 2, false, false, false, kUpWaves>;
+    __shared__ __attribute__((aligned(16))) char smem[TQ::LDS];
+    const int per = a.ntt * a.nct;
+    const int lb = xcd_block(gridDim.x);
+    const int u = lb / per, t = lb % per;
+    const int which = u / a.nscan, s = u % a.nscan;
+    const int hw = a.w_heads ? s % a.w_heads : s;
+    const int r0 = (t / a.nct) * kUpQRows, c0 = (t % a.nct) * kUpCols;
+    const int64_t dm = (int64_t)a.d * a.m;
+    const T* W1 = a.W + (int64_t)hw * a.w_stride;
+    const T* W3 = W1 + dm;
+    const int rows = (int)(a.N - r0);
+    const Opnd<T> A[1] = {{a.x[which] + ((int64_t)s * a.N + r0) * a.d, a.d, rows, a.d}};
+    const Opnd<T> B[2] = {{W1 + (int64_t)c0 * a.d, a.d, a.m - c0, a.d}, {W3 + (int64_t)c0 * a.d, a.d, a.m - c0, a.d}};
+    TQ tl;
+    tl.template run<PMQ>(A, B, a.d, smem);
+    T* P = a.phi[which] + ((int64_t)s * a.N + r0) * a.m + c0;
+    auto epi = [&](auto check) {
+        tl.for_each([&](const float (&v)[2], int row, int col) {
+            if (!decltype(check)::value || (row < rows && c0 + col < a.m))
+                P[(int64_t)row * a.m + col] = Elt<T>::st(v[0] * sigmoidf_(v[0]) * v[1]);
+        });
+    };
+    if (kUpQRows <= rows && c0 + kUpCols <= a.m) epi(std::false_type{});
+    else epi(std::true_type{});
+}
+
+// ---------------------------------------------------------------------------------------------
 // host driver
 
 // Sum of the partial-G buffers into the first: n float4 per buffer, parts buffers gstride apart,
@@ -793,6 +851,102 @@ static Layout make_layout(const ttt_desc& D, bool muon, bool own_m) {
     return L;
 }
 
+// Workspace of the parallel form: W1 | W3 in bf16 (bf16 io only), phi(q), phi(k), and the
+// linear-attention chunk states.
+struct PLayout {
+    size_t w13, phq, phk, lin, total;
+    int64_t nc;
+};
+
+static PLayout make_playout(const ttt_desc& D) {
+    PLayout L{};
+    const int64_t S = (int64_t)D.B * D.H, dm = (int64_t)D.d_h * D.m_h;
+    const size_t es = D.io_dtype == TTT_BF16 ? 2 : 4;
+    L.nc = D.N > 0 ? cdiv(D.N, D.chunk) : 0;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { const size_t o = off; off += align256(bytes); return o; };
+    if (es == 2) L.w13 = take((size_t)(D.w0_per_batch ? S : D.H) * 2 * dm * es);
+    L.phq = take((size_t)S * D.N * D.m_h * es);
+    L.phk = take((size_t)S * D.N * D.m_h * es);
+    L.lin = take(lin_chunked_ws_bytes(S, L.nc, D.m_h, D.d_h));
+    L.total = off;
+    return L;
+}
+
+template <typename T>
+static ttt_status run_parallel_form(const ttt_desc& D, const PLayout& L, const T* q, const T* k, const T* v,
+                                    const float* eta, const float* W0, T* o, float* W_out, float* M_inout, char* ws,
+                                    hipStream_t st) {
+    const int64_t S = (int64_t)D.B * D.H, dm = (int64_t)D.d_h * D.m_h;
+    const int64_t Hw = D.w0_per_batch ? S : D.H;  // fast-weight blocks in W0
+    ttt_status rc;
+    // W_out's frozen W1 | W3 come from W0 (all of W when there are no tokens)
+    auto copy_w0 = [&](int64_t floats) -> ttt_status {
+        if (!W_out) return TTT_OK;
+        for (int64_t b = 0; b < (D.w0_per_batch ? 1 : D.B); ++b) {
+            hipError_t e = hipMemcpy2DAsync(W_out + b * Hw * 3 * dm, 3 * dm * 4, W0, 3 * dm * 4, floats * 4, Hw,
+                                            hipMemcpyDeviceToDevice, st);
+            if (e != hipSuccess) return fail(TTT_ERR_DEVICE, "copying W0 into W_out: %s", hipGetErrorString(e));
+        }
+        return TTT_OK;
+    };
+    if (D.N == 0) return copy_w0(3 * dm);  // M_inout is left as it is
+    // 1. W1 | W3 as contraction operands
+    const T* W13;
+    int64_t w13_stride;
+    if constexpr (sizeof(T) == 2) {
+        T* w = (T*)(ws + L.w13);
+        const int64_t per4 = 2 * dm / 4, n4 = Hw * per4;
+        {
+            ProfScope ps(PK_PHI, st);
+            hipLaunchKernelGGL(k_w13_cvt<T>, dim3((unsigned)cdiv(n4, kThreads)), dim3(kThreads), 0, st, W0, 3 * dm, w,
+                               n4, per4);
+        }
+        if ((rc = check_launch("k_w13_cvt")) != TTT_OK) return rc;
+        W13 = w;
+        w13_stride = 2 * dm;
+    } else {
+        W13 = reinterpret_cast<const T*>(W0);
+        w13_stride = 3 * dm;
+    }
+    // 2. the features of every query and key
+    T* phq = (T*)(ws + L.phq);
+    T* phk = (T*)(ws + L.phk);
+    PhiArgs<T> pa{{q, k}, {phq, phk}, W13, w13_stride, D.w0_per_batch ? 0 : D.H, D.N, D.d_h, D.m_h, (int)S,
+                  (int)cdiv(D.N, kUpQRows), (int)cdiv(D.m_h, kUpCols)};
+    {
+        ProfScope ps(PK_PHI, st);
+        hipLaunchKernelGGL(k_phi<T>, dim3((unsigned)(2 * S * pa.ntt * pa.nct)), dim3(64 * kUpWaves), 0, st, pa);
+    }
+    if ((rc = check_launch("k_phi")) != TTT_OK) return rc;
+    // 3. chunked linear attention over the features, with W2 [d][m] as the state S [d_v][d_k]
+    linattn_desc LD{D.B, D.H, D.N, D.m_h, D.d_h, D.chunk, D.io_dtype, D.mask, D.update_chunks};
+    uint32_t flags[32] = {};
+    if (D.mask == TTT_MASK_STRIDED)
+        for (int64_t j = 0; j < L.nc; ++j)
+            if (D.update_chunks[j]) flags[j >> 5] |= 1u << (j & 31);
+    LinStateIO io;
+    io.S0 = W0 + 2 * dm;
+    io.s0_stride = 3 * dm;
+    io.s0_heads = D.w0_per_batch ? 0 : D.H;
+    io.Sout = W_out ? W_out + 2 * dm : nullptr;
+    io.sout_stride = 3 * dm;
+    if (D.momentum != 0.0f) {  // M <- beta M + g, W <- W - M: the running term is m = -M
+        io.mom = 1;
+        io.beta = D.momentum;
+        io.msign = -1.0f;
+        if (M_inout) {
+            io.M0 = M_inout + 2 * dm;
+            io.Mout = M_inout + 2 * dm;
+            io.m_stride = 3 * dm;
+        }
+    }
+    io.dsign = D.ascent ? -1.0f : 1.0f;
+    io.reps = D.inner_steps > 1 ? D.inner_steps : 1;
+    if ((rc = lin_chunked_run<T>(LD, flags, phq, phk, v, eta, o, io, ws + L.lin, st)) != TTT_OK) return rc;
+    return copy_w0(2 * dm);
+}
+
 static ttt_status validate(const ttt_desc* D) {
     if (!D) return fail(TTT_ERR_INVALID_ARGUMENT, "desc is NULL");
     if (D->B < 0 || D->H < 0 || D->N < 0) return fail(TTT_ERR_INVALID_ARGUMENT, "B, H, N must be >= 0");
@@ -817,6 +971,22 @@ static ttt_status validate(const ttt_desc* D) {
     if (D->w0_per_batch != 0 && D->w0_per_batch != 1) return fail(TTT_ERR_INVALID_ARGUMENT, "w0_per_batch must be 0/1");
     if (D->inner_steps < 0 || D->inner_steps > 64) return fail(TTT_ERR_INVALID_ARGUMENT, "inner_steps must be in [0, 64]");
     if (D->ascent != 0 && D->ascent != 1) return fail(TTT_ERR_INVALID_ARGUMENT, "ascent must be 0/1");
+    if (D->parallel_form != 0 && D->parallel_form != 1)
+        return fail(TTT_ERR_INVALID_ARGUMENT, "parallel_form must be 0/1");
+    if (D->parallel_form) {
+        if (!D->last_layer_only || D->rule != TTT_UPD_GD)
+            return fail(TTT_ERR_INVALID_ARGUMENT,
+                        "parallel_form needs last_layer_only = 1 and rule TTT_UPD_GD (frozen W1, W3; no norm, no Muon)");
+        const int64_t S = (int64_t)D->B * D->H, nc = D->N > 0 ? cdiv(D->N, D->chunk) : 0;
+        if (D->mask == TTT_MASK_STRIDED && nc > 32 * 32)
+            return fail(TTT_ERR_UNSUPPORTED, "parallel_form with MASK_STRIDED supports at most 1024 chunks");
+        // launch sizes: the feature tiles, and the linear-attention tiles over chunks and state
+        const int64_t nd = cdiv(D->d_h, 128), nm = cdiv(D->m_h, 128);
+        const int64_t lim = 1LL << 31;
+        if (2 * S * cdiv(D->N, kUpQRows) * cdiv(D->m_h, kUpCols) >= lim || S * nc * nd * nm >= lim ||
+            S * nc * cdiv(std::min<int64_t>(D->chunk, D->N), 128) * nd >= lim)
+            return fail(TTT_ERR_UNSUPPORTED, "parallel_form: B*H, N, d_h, m_h too large for one launch");
+    }
     const int64_t S = (int64_t)D->B * D->H;
     if (S > (1 << 20) || (int64_t)D->N > (1LL << 31) / 2) return fail(TTT_ERR_INVALID_ARGUMENT, "B*H or N too large");
     const int64_t bmax = D->N < D->chunk ? D->N : D->chunk;
@@ -998,7 +1168,8 @@ extern "C" ttt_status ttt_workspace_bytes(const ttt_desc* desc, size_t* bytes) {
     ttt_status rc = validate(desc);
     if (rc != TTT_OK) return rc;
     if (!bytes) return fail(TTT_ERR_INVALID_ARGUMENT, "bytes is NULL");
-    *bytes = make_layout(*desc, is_muon(*desc), desc->momentum != 0.0f).total;
+    *bytes = desc->parallel_form ? make_playout(*desc).total
+                                 : make_layout(*desc, is_muon(*desc), desc->momentum != 0.0f).total;
     return TTT_OK;
 }
 
@@ -1025,11 +1196,22 @@ extern "C" ttt_status ttt_forward(const ttt_desc* desc, const void* q, const voi
         overlaps(o, io_bytes, eta, (size_t)S * D.N * 4))
         return fail(TTT_ERR_INVALID_ARGUMENT, "o overlaps an input");
     if (overlaps(W_out, w_bytes, W0, w0_bytes)) return fail(TTT_ERR_INVALID_ARGUMENT, "W_out overlaps W0");
+    hipStream_t st = (hipStream_t)stream;
+    if (D.parallel_form) {
+        const PLayout PL = make_playout(D);
+        if (PL.total > 0 && (!workspace || workspace_bytes < PL.total))
+            return fail(TTT_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", PL.total, workspace_bytes);
+        if (workspace && !aligned(workspace, 256)) return fail(TTT_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+        if (D.io_dtype == TTT_BF16)
+            return run_parallel_form<uint16_t>(D, PL, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, eta,
+                                               W0, (uint16_t*)o, W_out, M_inout, (char*)workspace, st);
+        return run_parallel_form<float>(D, PL, (const float*)q, (const float*)k, (const float*)v, eta, W0, (float*)o,
+                                        W_out, M_inout, (char*)workspace, st);
+    }
     const Layout L = make_layout(D, is_muon(D), D.momentum != 0.0f && !M_inout);
     if (L.total > 0 && (!workspace || workspace_bytes < L.total))
         return fail(TTT_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", L.total, workspace_bytes);
     if (workspace && !aligned(workspace, 256)) return fail(TTT_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-    hipStream_t st = (hipStream_t)stream;
     if (D.io_dtype == TTT_BF16)
         return run_ttt<uint16_t>(D, L, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, eta, W0,
                                  (uint16_t*)o, W_out, M_inout, (char*)workspace, st);

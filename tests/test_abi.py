@@ -39,7 +39,7 @@ def test_library_loads_and_exports_every_symbol():
 
 def test_version_and_status_strings():
     L = C.lib()
-    assert L.ttt_abi_version() == 1
+    assert L.ttt_abi_version() == 2
     for s in range(5):
         assert L.ttt_status_string(s)
     assert L.ttt_status_string(99) == b"unknown status"
@@ -97,6 +97,13 @@ def ws_bytes(D):
     (dict(ascent=2), C.TTT_ERR_INVALID_ARGUMENT),
     (dict(momentum=float("nan")), C.TTT_ERR_INVALID_ARGUMENT),
     (dict(last_layer_only=2), C.TTT_ERR_INVALID_ARGUMENT),
+    (dict(parallel_form=2), C.TTT_ERR_INVALID_ARGUMENT),
+    # the parallel form needs frozen W1, W3 and plain GD
+    (dict(parallel_form=1, rule=C.UPD_GD), C.TTT_ERR_INVALID_ARGUMENT),
+    (dict(parallel_form=1, last_layer_only=1), C.TTT_ERR_INVALID_ARGUMENT),
+    (dict(parallel_form=1, last_layer_only=1, rule=C.UPD_MUON), C.TTT_ERR_INVALID_ARGUMENT),
+    (dict(parallel_form=1, last_layer_only=1, rule=C.UPD_GD, mask=C.MASK_STRIDED, N=1025 * 64,
+          update_chunks=ctypes.cast((ctypes.c_uint8 * 1025)(), ctypes.c_void_p)), C.TTT_ERR_UNSUPPORTED),
 ])
 def test_desc_validation(kw, status):
     st, _ = ws_bytes(desc(**kw))
@@ -117,6 +124,13 @@ def test_workspace_sizes():
     assert C.lib().ttt_last_error() == b""
     # a FULL mask needs one chunk covering the sequence
     assert ws_bytes(desc(mask=C.MASK_FULL, chunk=256))[0] == C.TTT_OK
+    # the parallel form holds phi(q), phi(k) ([B H N m] each) and the per-chunk linear-attention
+    # states (dS and S_c, 8 bytes per element of the d x m state per chunk)
+    st, par = ws_bytes(desc(parallel_form=1, last_layer_only=1, rule=C.UPD_GD))
+    assert st == C.TTT_OK
+    assert par >= 2 * 2 * 4 * 256 * 128 * 2 + 8 * 4 * 64 * 128 * 8
+    st, par0 = ws_bytes(desc(parallel_form=1, last_layer_only=1, rule=C.UPD_GD, N=0))
+    assert st == C.TTT_OK and par0 < par
 
 
 def call_forward(D, q=P16, k=P16, v=P16, eta=P16, W0=P16B, o=P16 + (1 << 30), W_out=None, M=None, ws=None, nws=0):

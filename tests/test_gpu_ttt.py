@@ -41,12 +41,13 @@ def check(o_gpu, W_gpu, o_ref, W_ref, d, m, tol, slices=None, label=""):
 
 
 def run_small(seed, B, H, N, d, m, chunk, mask, rule, bf16, momentum=0.0, last=False, flags=None, ns=5, inner=1,
-              ascent=False):
+              ascent=False, parallel=False):
     say(f"ttt case B{B} H{H} N{N} d{d} m{m} b{chunk} mask{mask} rule{rule} mom{momentum} last{last} bf16={bf16}"
-        f" inner{inner} ascent{ascent}")
+        f" inner{inner} ascent{ascent} parallel{parallel}")
     (q, k, v, eta, W0), (hq, hk, hv, he, W1, W3, W2) = full_ttt_inputs(seed, B, H, N, d, m, bf16)
     o, Wout = T.ttt_forward(q, k, v, eta, W0, chunk, mask, rule, m_h=m, ns_iters=ns, momentum=momentum,
-                            last_layer_only=last, update_chunks=flags, inner_steps=inner, ascent=ascent)
+                            last_layer_only=last, update_chunks=flags, inner_steps=inner, ascent=ascent,
+                            parallel_form=parallel)
     torch.cuda.synchronize()
     o_ref, W_ref, _ = O.ttt_forward_ref(hq, hk, hv, he, W1, W3, W2, chunk, mask, rule, ns, momentum, last, flags,
                                         inner_steps=inner, ascent=ascent)
@@ -163,6 +164,65 @@ def test_few_scans_split_gradients(bf16):
     run_small(18, 1, 1, 5000, 64, 128, 4096, O.MASK_APPLY_THEN_UPDATE, O.UPD_GD_L2, bf16)
     run_small(19, 1, 1, 5000, 64, 128, 4096, O.MASK_UPDATE_THEN_APPLY, O.UPD_MUON_L2, bf16, momentum=0.9, ns=3)
     run_small(20, 1, 1, 4096, 64, 128, 4096, O.MASK_APPLY_THEN_UPDATE, O.UPD_GD, bf16, last=True)
+
+
+PARALLEL_CASES = [
+    # mask, momentum, inner steps, ascent, strided flags
+    (O.MASK_APPLY_THEN_UPDATE, 0.0, 1, False, None),
+    (O.MASK_APPLY_THEN_UPDATE, 0.9, 1, False, None),
+    (O.MASK_UPDATE_THEN_APPLY, 0.5, 2, False, None),
+    (O.MASK_STRIDED, 0.0, 1, True, [1, 0, 1, 1]),
+    (O.MASK_STRIDED, 0.9, 3, True, [0, 1, 1, 0]),
+]
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("mask,mom,inner,ascent,flags", PARALLEL_CASES)
+def test_parallel_form_last_layer(mask, mom, inner, ascent, flags, bf16):
+    # the parallel static-kernel form (features phi(q), phi(k), then chunked linear attention with
+    # W2 as the state) against the oracle's chunk recurrence; N = 308 leaves a ragged last chunk
+    # of 20 tokens, and m = 160 partial feature and state tiles
+    run_small(30, 1, 2, 308, 64, 160, 96, mask, O.UPD_GD, bf16, mom, last=True, flags=flags, inner=inner,
+              ascent=ascent, parallel=True)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_parallel_form_full_mask(bf16):
+    run_small(31, 2, 1, 200, 32, 96, 200, O.MASK_FULL, O.UPD_GD, bf16, last=True, parallel=True)
+
+
+def test_parallel_form_matches_recurrence():
+    # several 256-token feature tiles and 128-wide state tiles: the parallel form with W0 given per
+    # (batch, head) against the chunk recurrence with W0 per head, momentum carried in M
+    B, H, N, d, m, chunk = 2, 2, 1100, 128, 384, 256
+    say(f"parallel form vs recurrence B{B} H{H} N{N} d{d} m{m} b{chunk}")
+    (q, k, v, eta, W0), _ = full_ttt_inputs(32, B, H, N, d, m, True)
+    M0 = 0.01 * torch.randn((B, H, 3 * d * m), dtype=torch.float32, device="cuda")
+    Mr, Mp = M0.clone(), M0.clone()
+    kw = dict(m_h=m, momentum=0.9, last_layer_only=True)
+    o_r, W_r = T.ttt_forward(q, k, v, eta, W0, chunk, O.MASK_APPLY_THEN_UPDATE, O.UPD_GD, M=Mr, **kw)
+    W0b = W0[None].expand(B, H, -1).contiguous()
+    o_p, W_p = T.ttt_forward(q, k, v, eta, W0b, chunk, O.MASK_APPLY_THEN_UPDATE, O.UPD_GD, M=Mp,
+                             parallel_form=True, **kw)
+    torch.cuda.synchronize()
+    eo, ew, em = rel(host(o_p), host(o_r)), rel(host(W_p), host(W_r)), rel(host(Mp), host(Mr))
+    say(f"  rel_o={eo:.3e} rel_W={ew:.3e} rel_M={em:.3e}")
+    assert eo <= 2e-2 and ew <= 2e-2 and em <= 2e-2
+    # the frozen W1 | W3 blocks of W_out and M come through unchanged
+    dm = d * m
+    assert torch.equal(W_p[..., :2 * dm], W0b[..., :2 * dm])
+    assert torch.equal(Mp[..., :2 * dm], M0[..., :2 * dm])
+
+
+def test_parallel_form_zero_tokens_returns_w0():
+    (q, k, v, eta, W0), _ = full_ttt_inputs(0, 2, 2, 0, 32, 64, True)
+    o, Wout = T.ttt_forward(q, k, v, eta, W0, 16, O.MASK_APPLY_THEN_UPDATE, O.UPD_GD, m_h=64, last_layer_only=True,
+                            parallel_form=True)
+    torch.cuda.synchronize()
+    assert o.numel() == 0
+    Wg = host(Wout)
+    ref = host(W0)
+    assert np.array_equal(Wg[0], ref) and np.array_equal(Wg[1], ref)
 
 
 def test_zero_tokens_returns_w0():
