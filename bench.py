@@ -56,13 +56,15 @@ def measured_traffic(kernel):
     return round(t["read"] + t["write"])
 
 
-def lact_flops(B, H, N, d, m, upd_tokens=None, ns_iters=0, n_updates=0):
+def lact_flops(B, H, N, d, m, upd_tokens=None, ns_iters=0, n_updates=0, last_only=False):
     """Algorithmic FLOPs of a ttt_forward call: 6dm per applied token-head (SwiGLU apply), 12dm per
-    updated token-head (key forward 4dm, value back-projection 2dm, three gradient sums 6dm), and
-    4 p^2 q per Newton-Schulz step per matrix (p = min(d, m), q = max(d, m))."""
+    updated token-head (key forward 4dm, value back-projection 2dm, three gradient sums 6dm; with
+    only W2 learning, key forward 4dm and the W2 gradient 2dm), and 4 p^2 q per Newton-Schulz step
+    per matrix (p = min(d, m), q = max(d, m))."""
     upd_tokens = N if upd_tokens is None else upd_tokens
     p, q = min(d, m), max(d, m)
-    return B * H * (6 * d * m * N + 12 * d * m * upd_tokens + n_updates * 3 * ns_iters * 4 * p * p * q)
+    per_upd = 6 if last_only else 12
+    return B * H * (6 * d * m * N + per_upd * d * m * upd_tokens + n_updates * 3 * ns_iters * 4 * p * p * q)
 
 
 def lact_bytes(B, H, N, d, m, es=2, n_updates=0, muon=False, momentum=False):
@@ -170,8 +172,9 @@ def main():
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--oracle-seconds", type=float, default=25.0,
                     help="stop the oracle after the scan that passes this many seconds")
-    ap.add_argument("--update", choices=["gd_l2", "muon_momentum"], default="gd_l2",
-                    help="update rule of the timed layer (the headline metric uses gd_l2)")
+    ap.add_argument("--update", choices=["gd_l2", "muon_momentum", "last_layer_gd_parallel"], default="gd_l2",
+                    help="update rule of the timed layer (the headline metric uses gd_l2); last_layer_gd_parallel: "
+                         "only W2 learns, W - g, in the parallel static-kernel form")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first copy a 1 GiB device buffer three times (a known-size kernel that scales "
                          "hardware byte counters)")
@@ -224,8 +227,11 @@ def main():
             print(f"[bench] inputs of batch {b} ready", file=sys.stderr, flush=True)
     Wh = [synth.head_weights(args.seed, h, d, m) for h in range(H)]
     W0 = torch.from_numpy(np.stack([np.concatenate([w[0].ravel(), w[1].ravel(), w[2].ravel()]) for w in Wh])).cuda()
-    rule, beta = (C.UPD_GD_L2, 0.0) if args.update == "gd_l2" else (C.UPD_MUON_L2, 0.9)
-    D, keep = T.ttt_desc(B, H, N, d, m, chunk, C.TTT_BF16, C.MASK_APPLY_THEN_UPDATE, rule, 5, beta)
+    rule, beta = {"gd_l2": (C.UPD_GD_L2, 0.0), "muon_momentum": (C.UPD_MUON_L2, 0.9),
+                  "last_layer_gd_parallel": (C.UPD_GD, 0.0)}[args.update]
+    par = args.update == "last_layer_gd_parallel"
+    D, keep = T.ttt_desc(B, H, N, d, m, chunk, C.TTT_BF16, C.MASK_APPLY_THEN_UPDATE, rule, 5, beta, last_layer_only=par,
+                         parallel_form=par)
     ws = torch.empty(T.ttt_workspace_bytes(D), dtype=torch.uint8, device="cuda")
     o = torch.empty_like(q)
     Mom = torch.zeros((B, H, 3 * d * m), dtype=torch.float32, device="cuda") if beta else None
@@ -234,7 +240,7 @@ def main():
         if Mom is not None:
             Mom.zero_()
         return T.ttt_forward(q, k, v, eta, W0, chunk, C.MASK_APPLY_THEN_UPDATE, rule, m_h=m, momentum=beta, M=Mom,
-                             out=o, workspace=ws)
+                             out=o, workspace=ws, last_layer_only=par, parallel_form=par)
 
     print("[bench] warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -266,7 +272,7 @@ def main():
     tokens = B * N
     value = tokens / (ms * 1e-3)
     nchunks = N // chunk
-    flops = lact_flops(B, H, N, d, m, ns_iters=5 if beta else 0, n_updates=nchunks)
+    flops = lact_flops(B, H, N, d, m, ns_iters=5 if beta else 0, n_updates=nchunks, last_only=par)
     layer_tflops = flops / (ms * 1e-3) / 1e12
 
     # dominant kernel against its roofline: algorithmic work per launch / average launch time
@@ -286,6 +292,15 @@ def main():
         "k_ns_gram": ("mfma", 2 * p_ns * p_ns * q_ns * 3 * S),
         # read the iterate's hi + lo planes and the bf16 Gram; write hi + lo (the last step: fp32)
         "k_ns_step": ("hbm", ((2 * es + 2 * es) * dm + es * p_ns * p_ns) * 3 * S),
+        # parallel form, one launch each per call: phi(q) and phi(k) (2 x 4dm per token-head),
+        # dS = (eta V)^T phi(K) and o = phi(Q) S^T (2dm each per token-head), and the state scan
+        # (dS read, S_c written as hi + lo: 8 bytes per state element per chunk)
+        "k_phi": ("mfma", 8 * dm * S * N),
+        "k_lin_delta": ("mfma", 2 * dm * S * N),
+        "k_lin_apply": ("mfma", 2 * dm * S * N),
+        "k_lin_scan": ("hbm", 8 * dm * S * nchunks),
+        # W1 | W3 of the H weight blocks read in fp32 and written in bf16
+        "k_w13_cvt": ("hbm", (4 + es) * 2 * dm * H),
     }
     dom_ms, dom_n = prof[dom]
     avg = dom_ms / max(dom_n, 1)
@@ -340,7 +355,8 @@ def main():
         t0 = time.perf_counter()
         for (b, h) in order:
             qs, ks, vs, es = exact[(b, h)]
-            o_ref, W_ref, _ = O.ttt_scan_ref(qs, ks, vs, es, *Wh[h], chunk, O.MASK_APPLY_THEN_UPDATE, rule, 5, beta)
+            o_ref, W_ref, _ = O.ttt_scan_ref(qs, ks, vs, es, *Wh[h], chunk, O.MASK_APPLY_THEN_UPDATE, rule, 5, beta,
+                                             par)
             done.append((b, h))
             og = o_host[b, h].astype(np.float64)
             errs_o.append(float(np.linalg.norm(og - o_ref) / np.linalg.norm(o_ref)))
@@ -431,6 +447,23 @@ def main():
             "workload": f"B{B} H{H} N{N} d_k=d_v={d} chunk {chunk} bf16, apply-then-update",
             "swiglu_layer_ms_per_call": round(ms, 3), "linattn_speedup": round(ms / msll, 2)}
         del wsll, oll
+        # last-layer-only plain GD on the headline inputs: the chunk recurrence against the parallel
+        # static-kernel form (features, then chunked linear attention with W2 as the state)
+        print("[bench] extras: last-layer GD, recurrence and parallel form", file=sys.stderr, flush=True)
+        msp = {}
+        for pf in (False, True):
+            Dp, _ = T.ttt_desc(B, H, N, d, m, chunk, C.TTT_BF16, C.MASK_APPLY_THEN_UPDATE, C.UPD_GD, 5, 0.0,
+                               last_layer_only=True, parallel_form=pf)
+            wsp = torch.empty(max(1, T.ttt_workspace_bytes(Dp)), dtype=torch.uint8, device="cuda")
+            msp[pf] = time_calls(torch, lambda: T.ttt_forward(q, k, v, eta, W0, chunk, C.MASK_APPLY_THEN_UPDATE,
+                                                              C.UPD_GD, m_h=m, last_layer_only=True, parallel_form=pf,
+                                                              out=o, workspace=wsp), st, 1)
+            del wsp
+        extras["lact_lm_last_layer_gd"] = {
+            "workload": f"B{B} H{H} N{N} d{d} m{m} chunk {chunk} bf16, apply-then-update, only W2 learns, W - g",
+            "recurrence_ms_per_call": round(msp[False], 3), "parallel_form_ms_per_call": round(msp[True], 3),
+            "parallel_form_tokens_per_s": round(tokens / (msp[True] * 1e-3)),
+            "parallel_form_speedup": round(msp[False] / msp[True], 2)}
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -439,7 +472,9 @@ def main():
         "data": "synthetic: seeded N(0,1)/sqrt(d) q,k,v in bf16, eta = 0.01 softplus(N(0,1)), W0 ~ N(0,1/d) per head",
         "config": {"workload": "lact_lm_layer_b8_h4_n32768_d384_m768_chunk2048_" + args.update, "B": B, "H": H,
                    "seq_len": N, "d_h": d, "m_h": m, "chunk": chunk, "mask": "apply_then_update",
-                   "update": "L2-Normalize(W - g)" if not beta else "L2-Normalize(W - Muon(M)), M <- 0.9 M + g, 5 NS steps",
+                   "update": {"gd_l2": "L2-Normalize(W - g)",
+                              "muon_momentum": "L2-Normalize(W - Muon(M)), M <- 0.9 M + g, 5 NS steps",
+                              "last_layer_gd_parallel": "only W2 learns, W - g, parallel static-kernel form"}[args.update],
                    "parallelism": "none (one GPU)"},
         "mfma_frac_layer": round(layer_tflops / BF16_PEAK_TFLOPS, 4),
         "layer_tflops": round(layer_tflops, 2),

@@ -898,7 +898,7 @@ static ttt_status run_parallel_form(const ttt_desc& D, const PLayout& L, const T
         T* w = (T*)(ws + L.w13);
         const int64_t per4 = 2 * dm / 4, n4 = Hw * per4;
         {
-            ProfScope ps(PK_PHI, st);
+            ProfScope ps(PK_W13, st);
             hipLaunchKernelGGL(k_w13_cvt<T>, dim3((unsigned)cdiv(n4, kThreads)), dim3(kThreads), 0, st, W0, 3 * dm, w,
                                n4, per4);
         }
