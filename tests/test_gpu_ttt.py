@@ -186,6 +186,13 @@ def test_parallel_form_last_layer(mask, mom, inner, ascent, flags, bf16):
               ascent=ascent, parallel=True)
 
 
+def test_parallel_form_many_strided_chunks_fp32():
+    # 40 chunks of 32 tokens: the strided update flags span two 32-bit words
+    flags = [(j * 7) % 3 != 0 for j in range(40)]
+    run_small(33, 1, 1, 1280, 64, 96, 32, O.MASK_STRIDED, O.UPD_GD, False, 0.9, last=True, flags=flags,
+              parallel=True)
+
+
 @pytest.mark.parametrize("bf16", [False, True])
 def test_parallel_form_full_mask(bf16):
     run_small(31, 2, 1, 200, 32, 96, 200, O.MASK_FULL, O.UPD_GD, bf16, last=True, parallel=True)
