@@ -284,14 +284,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_down(StepArgs<T> a) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// update: W <- [L2-Normalize](W - U) for blocks of 16 rows; writes the fp32 master copy and the
-// io-dtype shadows W1, W3, W2 and W2^T.  With U == nullptr and norm == 0 it copies (initial W0).
+// update: W <- [L2-Normalize](W - U) for blocks of 16 rows; writes the fp32 master copy and (unless
+// shadows == 0: the last update, when nothing applies after it) the io-dtype shadows W1, W3, W2 and
+// W2^T.  With U == nullptr and norm == 0 it copies (initial W0).
 template <typename T> struct UpdArgs {
     const float* src; int64_t src_stride; int src_per_head; int H;
     const float* U; int64_t u_stride;
     float* dst; int64_t dst_stride;
     T* sh; int64_t sh_stride;
-    int d, m, norm, last_only;
+    int d, m, norm, last_only, shadows;
 };
 
 constexpr int kUpdRows = 16;
@@ -315,7 +316,7 @@ template <> struct Vec4<float> {
 // to LDS so that W2^T can be stored 16 consecutive elements at a time.
 template <int NV, typename T>
 __device__ __forceinline__ void update_rows(const float* src, const float* U, float* dst, T* shm, T* tileT,
-                                            int row0, int L, bool norm, bool to_lds) {
+                                            int row0, int L, bool norm, bool to_lds, bool shadows) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int L4 = L / 4;
 #pragma unroll
@@ -347,8 +348,10 @@ __device__ __forceinline__ void update_rows(const float* src, const float* U, fl
             if (c4 < L4) {
                 const float4 w = make_float4(x[i].x * sc, x[i].y * sc, x[i].z * sc, x[i].w * sc);
                 d4[c4] = w;
-                Vec4<T>::store(shm + ro + 4 * c4, w);
-                if (to_lds) Vec4<T>::store(tileT + row * L + 4 * c4, w);
+                if (shadows) {
+                    Vec4<T>::store(shm + ro + 4 * c4, w);
+                    if (to_lds) Vec4<T>::store(tileT + row * L + 4 * c4, w);
+                }
             }
         }
     }
@@ -375,16 +378,16 @@ __global__ __launch_bounds__(kThreads) void k_update(UpdArgs<T> a) {
     T* shm = a.sh + s * a.sh_stride + moff;
     static_assert(kMaxDim <= 8 * 256, "update rows hold at most 8 float4 per lane");
     switch ((L / 4 + 63) / 64) {  // uniform per workgroup
-        case 1: update_rows<1>(src, U, dst, shm, tileT, row0, L, norm, mat == 2); break;
-        case 2: update_rows<2>(src, U, dst, shm, tileT, row0, L, norm, mat == 2); break;
-        case 3: update_rows<3>(src, U, dst, shm, tileT, row0, L, norm, mat == 2); break;
-        case 4: update_rows<4>(src, U, dst, shm, tileT, row0, L, norm, mat == 2); break;
-        case 5: update_rows<5>(src, U, dst, shm, tileT, row0, L, norm, mat == 2); break;
-        case 6: update_rows<6>(src, U, dst, shm, tileT, row0, L, norm, mat == 2); break;
-        case 7: update_rows<7>(src, U, dst, shm, tileT, row0, L, norm, mat == 2); break;
-        default: update_rows<8>(src, U, dst, shm, tileT, row0, L, norm, mat == 2); break;
+        case 1: update_rows<1>(src, U, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows); break;
+        case 2: update_rows<2>(src, U, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows); break;
+        case 3: update_rows<3>(src, U, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows); break;
+        case 4: update_rows<4>(src, U, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows); break;
+        case 5: update_rows<5>(src, U, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows); break;
+        case 6: update_rows<6>(src, U, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows); break;
+        case 7: update_rows<7>(src, U, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows); break;
+        default: update_rows<8>(src, U, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows); break;
     }
-    if (mat == 2) {  // W2^T [m][d]: column c of this 16-row block is 16 consecutive elements
+    if (mat == 2 && a.shadows) {  // W2^T [m][d]: column c of this 16-row block is 16 consecutive elements
         __syncthreads();
         T* w2t = a.sh + s * a.sh_stride + 3 * dm;
         for (int c = threadIdx.x; c < L; c += kThreads) {
@@ -1019,7 +1022,7 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
     const int upd_blocks = (2 * m + d) / kUpdRows;
     {  // W0 -> master copy and shadows
         UpdArgs<T> u{W0, 3 * dm, D.w0_per_batch ? 0 : 1, D.H, nullptr, 0, Wf[0], L.wf_stride, sh[0], L.sh_stride,
-                     d, m, 0, 0};
+                     d, m, 0, 0, 1};
         if ((rc = launch_update<T>(u, S * upd_blocks, st)) != TTT_OK) return rc;
     }
     int cur = 0;
@@ -1028,6 +1031,11 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
     const int nsteps = D.N == 0 ? 0 : (uta ? nc + 1 : nc);
     const int ntm = (int)cdiv(m, 128), ntd = (int)cdiv(d, 128);
     const int64_t bmax = D.N < D.chunk ? D.N : D.chunk;
+    // the last step whose chunk updates: its last update writes W_out directly (no copy at the
+    // end), and skips the shadows when no apply follows it
+    int last_upd = -1;
+    for (int step = 0; step < nsteps && step < nc; ++step)
+        if (D.mask != TTT_MASK_STRIDED || D.update_chunks[step]) last_upd = step;
     for (int step = 0; step < nsteps; ++step) {
         int ja = uta ? step - 1 : step;
         int ju = step < nc ? step : -1;
@@ -1146,13 +1154,18 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
                 U = sizeof(T) == 2 ? Xf : reinterpret_cast<const float*>(Xb[(D.ns_iters - 1) & 1]);
             }
             const int norm = (D.rule == TTT_UPD_GD_L2 || D.rule == TTT_UPD_MUON_L2) ? 1 : 0;
+            const bool final_upd = step == last_upd && it == nin - 1;
             UpdArgs<T> u{Wf[cur], L.wf_stride, 0, D.H, U, 3 * dm, Wf[cur ^ 1], L.wf_stride, sh[cur ^ 1], L.sh_stride,
-                         d, m, norm, D.last_layer_only};
+                         d, m, norm, D.last_layer_only, 1};
+            if (final_upd && W_out) {
+                u.dst = W_out;  // [B][H][3 d m], the same stride as the master copy
+                u.shadows = step < nsteps - 1;
+            }
             if ((rc = launch_update<T>(u, S * upd_blocks, st)) != TTT_OK) return rc;
             cur ^= 1;
         }
     }
-    if (W_out) {
+    if (W_out && last_upd < 0) {  // no update wrote W_out
         hipError_t e = hipMemcpyAsync(W_out, Wf[cur], (size_t)S * 3 * dm * 4, hipMemcpyDeviceToDevice, st);
         if (e != hipSuccess) return fail(TTT_ERR_DEVICE, "copying W_out: %s", hipGetErrorString(e));
     }
