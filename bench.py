@@ -283,9 +283,9 @@ def main():
         # O = Hq W2^T (2dm), gradient sums G1, G3, G2 (6dm) per token-head
         "k_down": ("mfma", 8 * dm * S * chunk),
         # read W and G in fp32, write W in fp32 and the bf16 copies of W1, W3, W2, W2^T; averaged
-        # over a call's launches: the initial copy of W0 (per head) into W and the copies, the chunk
-        # updates, and the last one, which writes W_out and no copies
-        "k_update": ("hbm", (4 * 3 * dm * H + 4 * 3 * dm * S + es * 4 * dm * S
+        # over a call's launches: the initial bf16 copies of W0 (read per head), the chunk updates
+        # (the first reads W0), and the last one, which writes W_out and no copies
+        "k_update": ("hbm", (4 * 3 * dm * H + es * 4 * dm * S
                              + (nchunks - 1) * ((4 + 4 + 4) * 3 * dm * S + es * 4 * dm * S)
                              + (4 + 4 + 4) * 3 * dm * S) / (nchunks + 1)),
         # read G (and read/write M) in fp32, write U as the bf16 hi + lo pair that starts Newton-Schulz

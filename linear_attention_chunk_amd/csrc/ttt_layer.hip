@@ -284,7 +284,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_down(StepArgs<T> a) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// update: W <- [L2-Normalize](W - U) for blocks of 16 rows; writes the fp32 master copy and (unless
+// update: W <- [L2-Normalize](W - U) for blocks of 16 rows; writes the fp32 master copy (unless dst
+// is null: the initial copy of W0 when an update follows, which then reads W0 itself) and (unless
 // shadows == 0: the last update, when nothing applies after it) the io-dtype shadows W1, W3, W2 and
 // W2^T.  With U == nullptr and norm == 0 it copies (initial W0).
 template <typename T> struct UpdArgs {
@@ -341,13 +342,13 @@ __device__ __forceinline__ void update_rows(const float* src, const float* U, fl
             if (lane + 64 * i < L4) ss += x[i].x * x[i].x + x[i].y * x[i].y + x[i].z * x[i].z + x[i].w * x[i].w;
         float sc = 1.0f;
         if (norm) sc = 1.0f / fmaxf(sqrtf(wave_sum(ss)), 1e-6f);
-        float4* d4 = reinterpret_cast<float4*>(dst + ro);
+        float4* d4 = dst ? reinterpret_cast<float4*>(dst + ro) : nullptr;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int c4 = lane + 64 * i;
             if (c4 < L4) {
                 const float4 w = make_float4(x[i].x * sc, x[i].y * sc, x[i].z * sc, x[i].w * sc);
-                d4[c4] = w;
+                if (d4) d4[c4] = w;
                 if (shadows) {
                     Vec4<T>::store(shm + ro + 4 * c4, w);
                     if (to_lds) Vec4<T>::store(tileT + row * L + 4 * c4, w);
@@ -374,7 +375,7 @@ __global__ __launch_bounds__(kThreads) void k_update(UpdArgs<T> a) {
     const float* src = a.src + hs * a.src_stride + moff;
     const float* U = (a.U && !frozen) ? a.U + s * a.u_stride + moff : nullptr;
     const bool norm = a.norm && !frozen;
-    float* dst = a.dst + s * a.dst_stride + moff;
+    float* dst = a.dst ? a.dst + s * a.dst_stride + moff : nullptr;
     T* shm = a.sh + s * a.sh_stride + moff;
     static_assert(kMaxDim <= 8 * 256, "update rows hold at most 8 float4 per lane");
     switch ((L / 4 + 63) / 64) {  // uniform per workgroup
@@ -1020,11 +1021,6 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
         if (e != hipSuccess) return fail(TTT_ERR_DEVICE, "zeroing momentum: %s", hipGetErrorString(e));
     }
     const int upd_blocks = (2 * m + d) / kUpdRows;
-    {  // W0 -> master copy and shadows
-        UpdArgs<T> u{W0, 3 * dm, D.w0_per_batch ? 0 : 1, D.H, nullptr, 0, Wf[0], L.wf_stride, sh[0], L.sh_stride,
-                     d, m, 0, 0, 1};
-        if ((rc = launch_update<T>(u, S * upd_blocks, st)) != TTT_OK) return rc;
-    }
     int cur = 0;
     const int nc = (int)cdiv(D.N, D.chunk);
     const bool uta = D.mask == TTT_MASK_FULL || D.mask == TTT_MASK_UPDATE_THEN_APPLY;
@@ -1036,6 +1032,12 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
     int last_upd = -1;
     for (int step = 0; step < nsteps && step < nc; ++step)
         if (D.mask != TTT_MASK_STRIDED || D.update_chunks[step]) last_upd = step;
+    {  // W0 -> shadows, and the master copy only if no update follows (the first update reads W0)
+        UpdArgs<T> u{W0, 3 * dm, D.w0_per_batch ? 0 : 1, D.H, nullptr, 0, last_upd < 0 ? Wf[0] : nullptr,
+                     L.wf_stride, sh[0], L.sh_stride, d, m, 0, 0, 1};
+        if ((rc = launch_update<T>(u, S * upd_blocks, st)) != TTT_OK) return rc;
+    }
+    bool w_in_master = last_upd < 0;  // whether the current W is in Wf[cur], or still only in W0
     for (int step = 0; step < nsteps; ++step) {
         int ja = uta ? step - 1 : step;
         int ju = step < nc ? step : -1;
@@ -1157,6 +1159,12 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
             const bool final_upd = step == last_upd && it == nin - 1;
             UpdArgs<T> u{Wf[cur], L.wf_stride, 0, D.H, U, 3 * dm, Wf[cur ^ 1], L.wf_stride, sh[cur ^ 1], L.sh_stride,
                          d, m, norm, D.last_layer_only, 1};
+            if (!w_in_master) {  // the first update reads W0 (per head or per scan)
+                u.src = W0;
+                u.src_stride = 3 * dm;
+                u.src_per_head = D.w0_per_batch ? 0 : 1;
+                w_in_master = true;
+            }
             if (final_upd && W_out) {
                 u.dst = W_out;  // [B][H][3 d m], the same stride as the master copy
                 u.shadows = step < nsteps - 1;
