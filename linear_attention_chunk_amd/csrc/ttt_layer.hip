@@ -434,6 +434,8 @@ static_assert(kPrepElems % kThreads == 0, "prep blocks take whole rounds of the 
 
 template <typename T> struct PrepArgs {
     const float* G; int64_t g_stride;
+    int parts; int64_t gpart_stride;      // partial-G buffers summed in buffer order (as k_gsum does)
+    float* Gsum;                          // the sum written back over G's first buffer, or null
     float* M; int64_t m_stride; float beta;
     float* part; int nblk;
     T* Xhi; T* Xlo; int64_t x_stride;     // bf16 mode, Newton-Schulz: U as hi + lo planes; else null
@@ -456,6 +458,7 @@ __global__ __launch_bounds__(kThreads) void k_muon_prep(PrepArgs<T> a) {
     const int s = blockIdx.x / per, t = blockIdx.x % per;
     const int mat = a.mat0 + t / a.nblk, blk = t % a.nblk;
     const float* G = a.G + s * a.g_stride + mat * a.dm;
+    float* Gs = a.Gsum ? a.Gsum + s * a.g_stride + mat * a.dm : nullptr;
     float* M = a.M ? a.M + s * a.m_stride + mat * a.dm : nullptr;
     T* Xh = a.Xhi ? a.Xhi + s * a.x_stride + mat * a.dm : nullptr;
     T* Xl = a.Xhi ? a.Xlo + s * a.x_stride + mat * a.dm : nullptr;
@@ -467,6 +470,13 @@ __global__ __launch_bounds__(kThreads) void k_muon_prep(PrepArgs<T> a) {
     float g[NI], mv[NI];
 #pragma unroll
     for (int j = 0; j < NI; ++j) g[j] = G[min(e0 + threadIdx.x + j * kThreads, a.dm - 1)];
+    for (int p = 1; p < a.parts; ++p) {
+        float gp[NI];
+#pragma unroll
+        for (int j = 0; j < NI; ++j) gp[j] = G[p * a.gpart_stride + min(e0 + threadIdx.x + j * kThreads, a.dm - 1)];
+#pragma unroll
+        for (int j = 0; j < NI; ++j) g[j] += gp[j];
+    }
     if (M) {
 #pragma unroll
         for (int j = 0; j < NI; ++j) mv[j] = M[min(e0 + threadIdx.x + j * kThreads, a.dm - 1)];
@@ -476,6 +486,7 @@ __global__ __launch_bounds__(kThreads) void k_muon_prep(PrepArgs<T> a) {
         const int64_t e = e0 + threadIdx.x + j * kThreads;
         if (e < a.dm) {
             float u = g[j];
+            if (Gs) Gs[e] = u;
             if (M) {
                 u = a.beta * mv[j] + u;
                 M[e] = u;
@@ -1083,7 +1094,8 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
                 }
                 if ((rc = check_launch("k_down")) != TTT_OK) return rc;
             }
-            if (a.lu && a.ksplit > 1) {
+            // with momentum or Muon the prep kernel adds the partial-G buffers itself
+            if (a.lu && a.ksplit > 1 && !(muon || mom)) {
                 const int64_t n4 = (int64_t)S * L.g_stride / 4;
                 {
                     ProfScope ps(PK_DOWN, st);
@@ -1101,8 +1113,11 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
             // bf16 Newton-Schulz starts from U's hi + lo planes, which prep writes (hi into Xb[1])
             const bool split = muon && sizeof(T) == 2 && D.ns_iters > 0;
             if (muon || mom) {
-                PrepArgs<T> pa{G, L.g_stride, M, 3 * dm, D.momentum, part, L.nblk, split ? Xb[1] : nullptr,
-                               split ? Xlo : nullptr, L.x_stride, dm, mat0, nmat};
+                // the summed G is needed again only where U = G is read in fp32 (no momentum: fp32
+                // Newton-Schulz, or zero steps)
+                const bool keep_g = a.ksplit > 1 && !mom && (sizeof(T) == 4 || D.ns_iters == 0);
+                PrepArgs<T> pa{G, L.g_stride, a.ksplit, a.gpart_stride, keep_g ? G : nullptr, M, 3 * dm, D.momentum, part,
+                               L.nblk, split ? Xb[1] : nullptr, split ? Xlo : nullptr, L.x_stride, dm, mat0, nmat};
                 {
                     ProfScope ps(PK_MUON_PREP, st);
                     hipLaunchKernelGGL(k_muon_prep<T>, dim3(S * nmat * L.nblk), dim3(kThreads), 0, st, pa);

@@ -164,6 +164,11 @@ def test_few_scans_split_gradients(bf16):
     run_small(18, 1, 1, 5000, 64, 128, 4096, O.MASK_APPLY_THEN_UPDATE, O.UPD_GD_L2, bf16)
     run_small(19, 1, 1, 5000, 64, 128, 4096, O.MASK_UPDATE_THEN_APPLY, O.UPD_MUON_L2, bf16, momentum=0.9, ns=3)
     run_small(20, 1, 1, 4096, 64, 128, 4096, O.MASK_APPLY_THEN_UPDATE, O.UPD_GD, bf16, last=True)
+    # the token parts summed by the momentum / Muon prep: Muon without momentum (fp32 then reads the
+    # summed G as its first iterate), zero Newton-Schulz steps, and momentum without Muon
+    run_small(34, 1, 1, 5000, 64, 128, 4096, O.MASK_APPLY_THEN_UPDATE, O.UPD_MUON_L2, bf16, ns=2)
+    run_small(35, 1, 1, 4096, 64, 128, 4096, O.MASK_UPDATE_THEN_APPLY, O.UPD_MUON, bf16, ns=0)
+    run_small(36, 1, 1, 5000, 64, 128, 4096, O.MASK_APPLY_THEN_UPDATE, O.UPD_GD_L2, bf16, momentum=0.5)
 
 
 PARALLEL_CASES = [
