@@ -24,7 +24,7 @@ EXPORTS = (
     "ttt_profile_enable", "ttt_profile_select", "ttt_profile_read", "ttt_profile_kernel_name",
     "ttt_probe_mfma_bf16",
 )
-PROF_KERNELS = 13
+PROF_KERNELS = 14
 
 
 class TttDesc(ctypes.Structure):

@@ -793,6 +793,13 @@ __global__ __launch_bounds__(64 * kUpWaves, 1) void k_phi(PhiArgs<T> a) {
 // ---------------------------------------------------------------------------------------------
 // host driver
 
+// Zeroes n4 float4 (a kernel rather than hipMemsetAsync, so that a caller may capture the call
+// into a HIP graph)
+__global__ __launch_bounds__(kThreads) void k_zero(float4* p, int64_t n4) {
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i < n4) p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
 // Sum of the partial-G buffers into the first: n float4 per buffer, parts buffers gstride apart,
 // added in buffer order (deterministic).
 __global__ __launch_bounds__(kThreads) void k_gsum(float* G, int64_t n4, int parts, int64_t gstride) {
@@ -1028,8 +1035,12 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
     ttt_status rc;
 
     if (mom && !M_inout) {
-        hipError_t e = hipMemsetAsync(M, 0, (size_t)S * 3 * dm * 4, st);
-        if (e != hipSuccess) return fail(TTT_ERR_DEVICE, "zeroing momentum: %s", hipGetErrorString(e));
+        const int64_t n4 = (int64_t)S * 3 * dm / 4;
+        {
+            ProfScope ps(PK_ZERO, st);
+            hipLaunchKernelGGL(k_zero, dim3((unsigned)cdiv(n4, kThreads)), dim3(kThreads), 0, st, (float4*)M, n4);
+        }
+        if ((rc = check_launch("k_zero")) != TTT_OK) return rc;
     }
     const int upd_blocks = (2 * m + d) / kUpdRows;
     int cur = 0;
