@@ -26,9 +26,15 @@
  *   - Streams: work is enqueued on `stream` (a hipStream_t; NULL = the null stream); the call
  *     returns before the work finishes.
  *   - Errors: arguments are checked before anything is enqueued, so a call that returns an
- *     error has written nothing.  A failed launch returns TTT_ERR_DEVICE; a device fault shows
- *     up at the caller's next synchronisation.  ttt_last_error() gives a message for the
- *     latest failed call on the calling thread.
+ *     error has written nothing.  Besides sizes, enums and alignment, every device pointer must
+ *     lie in an allocation that HIP made on a device and that holds all the bytes the call reads
+ *     or writes from it (hipMemGetAddressRange); otherwise TTT_ERR_INVALID_ARGUMENT, or
+ *     TTT_ERR_DEVICE when no HIP device is usable.  A failed launch returns TTT_ERR_DEVICE; a
+ *     device fault shows up at the caller's next synchronisation, or, with the environment
+ *     variable TTT_DEBUG_SYNC set (not "0"), as TTT_ERR_DEVICE from the call that launched the
+ *     kernel (every launch is then followed by a stream synchronisation: a debugging aid, not for
+ *     streams under graph capture).  ttt_last_error() gives a message for the latest failed call
+ *     on the calling thread.
  *   - Aliasing: o must not overlap q, k, v or eta.  W_out may not overlap W0.
  *   - Thread safety: calls on different streams may run concurrently; the only mutable global
  *     state is the per-thread error message and the optional launch profiler below.
@@ -50,7 +56,9 @@ typedef enum {
     TTT_ERR_INVALID_ARGUMENT = 1, /* a size, pointer, alignment or enum value is out of range     */
     TTT_ERR_UNSUPPORTED = 2,      /* a valid combination the library does not implement         */
     TTT_ERR_WORKSPACE = 3,        /* workspace pointer missing or smaller than *_workspace_bytes  */
-    TTT_ERR_DEVICE = 4            /* a HIP call or kernel launch failed                          */
+    TTT_ERR_DEVICE = 4,           /* a HIP call or kernel launch failed                          */
+    TTT_STATUS_MAX_ENUM = 0x7FFFFFFF  /* not a status: makes every value 0 .. INT32_MAX a valid
+                                         ttt_status, so ttt_status_string() may be asked about any */
 } ttt_status;
 
 typedef enum { TTT_F32 = 0, TTT_BF16 = 1 } ttt_dtype;

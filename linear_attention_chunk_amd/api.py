@@ -23,15 +23,44 @@ def _stream_handle(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _need(t: torch.Tensor, name: str, dtype=None, device=None):
+def _need(t: torch.Tensor, name: str, dtype=None, device=None, shape=None):
+    """Checks one tensor argument: exact shape and dtype first, then that it is a contiguous tensor on
+    the call's device.  The library writes through these pointers on the device, so every mismatch
+    is a ValueError here instead of a fault or wrong results there."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if dtype is not None and t.dtype != dtype:
-        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if device is not None and t.device != device:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _workspace(ws: Optional[torch.Tensor], nbytes: int, device) -> Optional[torch.Tensor]:
+    """The caller's workspace after checks (a contiguous uint8 device tensor of at least nbytes), or a
+    new one when none is given."""
+    if ws is None:
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device) if nbytes else None
+    _need(ws, "workspace", torch.uint8, device)
+    if ws.numel() < nbytes:
+        raise ValueError(f"workspace holds {ws.numel()} bytes, the call needs {nbytes}")
+    return ws
+
+
+def _flags(update_chunks, N: int, chunk: int, strided: bool, name="update_chunks"):
+    """update_chunks must hold a flag for every chunk (the library reads ceil(N / chunk) of them)."""
+    if update_chunks is None:
+        if strided and N > 0:
+            raise ValueError(f"the strided mask needs {name}")
+        return
+    need = -(-N // chunk) if chunk > 0 else 0
+    if len(update_chunks) < need:
+        raise ValueError(f"{name} has {len(update_chunks)} flags, the sequence has {need} chunks")
 
 
 def pack_weights(W1: torch.Tensor, W3: torch.Tensor, W2: torch.Tensor) -> torch.Tensor:
@@ -80,36 +109,38 @@ def ttt_forward(q, k, v, eta, W0, chunk: int, mask_mode: int = C.MASK_APPLY_THEN
     in place.  parallel_form (last_layer_only with plain GD only) computes the same layer as
     chunked linear attention over the frozen SwiGLU features.  Returns (o, W_out or None).
     """
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q must be a [B, H, N, d] tensor")
     B, H, N, d = q.shape
     dev = q.device
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n, q.dtype, dev)
-        if t.shape != q.shape:
-            raise ValueError(f"{n} has shape {tuple(t.shape)}, expected {tuple(q.shape)}")
     if q.dtype not in _DT:
         raise ValueError(f"unsupported io dtype {q.dtype}")
-    _need(eta, "eta", torch.float32, dev)
-    if tuple(eta.shape) != (B, H, N):
-        raise ValueError("eta must be [B, H, N]")
-    _need(W0, "W0", torch.float32, dev)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype, dev, q.shape)
+    _need(eta, "eta", torch.float32, dev, (B, H, N))
+    if not isinstance(W0, torch.Tensor) or W0.dim() not in (2, 3):
+        raise ValueError("W0 must be [H, 3*d*m] or [B, H, 3*d*m]")
     per_batch = W0.dim() == 3
     if m_h is None:
         m_h = W0.shape[-1] // (3 * d)
-    if W0.shape[-1] != 3 * d * m_h or (per_batch and tuple(W0.shape[:2]) != (B, H)) or (
-            not per_batch and (W0.dim() != 2 or W0.shape[0] != H)):
-        raise ValueError("W0 must be [H, 3*d*m] or [B, H, 3*d*m]")
+    _need(W0, "W0", torch.float32, dev, ((B, H) if per_batch else (H,)) + (3 * d * m_h,))
+    if chunk < 1:
+        raise ValueError("chunk must be >= 1")
+    _flags(update_chunks, N, chunk, mask_mode == C.MASK_STRIDED)
+    wshape = (B, H, 3 * d * m_h)
+    if out is not None:
+        _need(out, "out", q.dtype, dev, q.shape)
+    if M is not None:
+        _need(M, "M", torch.float32, dev, wshape)
     D, keep = ttt_desc(B, H, N, d, m_h, chunk, _DT[q.dtype], mask_mode, update_rule, ns_iters, momentum,
                        last_layer_only, per_batch, update_chunks, inner_steps, ascent, parallel_form)
-    o = torch.empty_like(q) if out is None else out
-    _need(o, "out", q.dtype, dev)
-    W_out = torch.empty((B, H, 3 * d * m_h), dtype=torch.float32, device=dev) if want_W else None
-    if M is not None:
-        _need(M, "M", torch.float32, dev)
     nbytes = ttt_workspace_bytes(D)
-    if workspace is None or workspace.numel() < nbytes:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, nbytes, dev)
+    o = torch.empty_like(q) if out is None else out
+    W_out = torch.empty(wshape, dtype=torch.float32, device=dev) if want_W else None
     st = C.lib().ttt_forward(ctypes.byref(D), _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(W0), _ptr(o), _ptr(W_out),
-                             _ptr(M), _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream_handle(stream))
+                             _ptr(M), _ptr(workspace), ctypes.c_size_t(0 if workspace is None else workspace.numel()),
+                             _stream_handle(stream))
     del keep
     C.check(st)
     return o, W_out
@@ -134,25 +165,30 @@ def linattn_forward(q, k, v, eta, chunk: int, mask_mode: int = C.MASK_APPLY_THEN
                     S0: Optional[torch.Tensor] = None, update_chunks=None, want_S: bool = True,
                     out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None):
     """Chunked linear attention through linattn_forward of libttt.so.  Returns (o, S_out or None)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        if not isinstance(t, torch.Tensor) or t.dim() != 4:
+            raise ValueError(f"{n} must be a 4-D [B, H, N, d] tensor")
     B, H, N, dk = q.shape
     dv = v.shape[-1]
     dev = q.device
-    _need(q, "q", None, dev)
-    _need(k, "k", q.dtype, dev)
-    _need(v, "v", q.dtype, dev)
-    if tuple(k.shape) != tuple(q.shape) or tuple(v.shape[:3]) != (B, H, N):
-        raise ValueError("q, k must be [B, H, N, d_k] and v [B, H, N, d_v]")
     if q.dtype not in _DT:
         raise ValueError(f"unsupported io dtype {q.dtype}")
-    _need(eta, "eta", torch.float32, dev)
+    _need(q, "q", None, dev)
+    _need(k, "k", q.dtype, dev, q.shape)
+    _need(v, "v", q.dtype, dev, (B, H, N, dv))
+    _need(eta, "eta", torch.float32, dev, (B, H, N))
     if S0 is not None:
-        _need(S0, "S0", torch.float32, dev)
+        _need(S0, "S0", torch.float32, dev, (B, H, dv, dk))
+    if out is not None:
+        _need(out, "out", q.dtype, dev, (B, H, N, dv))
+    if mask_mode != C.MASK_TOKEN_CAUSAL and chunk < 1:
+        raise ValueError("chunk must be >= 1")
+    _flags(update_chunks, N, max(chunk, 1), mask_mode == C.MASK_STRIDED)
     D, keep = linattn_desc(B, H, N, dk, dv, chunk, _DT[q.dtype], mask_mode, update_chunks)
+    nbytes = linattn_workspace_bytes(D)
+    workspace = _workspace(workspace, nbytes, dev)
     o = torch.empty((B, H, N, dv), dtype=q.dtype, device=dev) if out is None else out
     S_out = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev) if want_S else None
-    nbytes = linattn_workspace_bytes(D)
-    if nbytes and (workspace is None or workspace.numel() < nbytes):
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     st = C.lib().linattn_forward(ctypes.byref(D), _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(S0), _ptr(o),
                                  _ptr(S_out), _ptr(workspace), ctypes.c_size_t(0 if workspace is None else workspace.numel()),
                                  _stream_handle(stream))

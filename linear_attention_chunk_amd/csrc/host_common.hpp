@@ -35,11 +35,30 @@ struct ProfScope {
     ~ProfScope();
 };
 
-inline ttt_status check_launch(const char* what) {
+// Whether TTT_DEBUG_SYNC is set (to anything but "" or "0") in the environment, read once: then every
+// launch is followed by a synchronisation of its stream, so that a kernel that fails is reported by
+// the call that launched it (a debugging aid; it serialises the host with the device, and a stream
+// under graph capture cannot be synchronised, so such a call returns TTT_ERR_DEVICE).
+bool debug_sync();
+
+inline ttt_status check_launch(const char* what, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(TTT_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+    if (debug_sync()) {
+        e = hipStreamSynchronize(st);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(TTT_ERR_DEVICE, "%s (TTT_DEBUG_SYNC): %s", what, hipGetErrorString(e));
+        }
+    }
     return TTT_OK;
 }
+
+// Argument check for one device buffer: p must lie in memory that HIP allocated on a device, with at
+// least `bytes` of that allocation from p on.  A host pointer, a stale or foreign address, or a buffer
+// too short for the call is refused before anything is enqueued (a null p or zero bytes passes).
+// Without a usable HIP device the answer is TTT_ERR_DEVICE.
+ttt_status check_buffer(const void* p, size_t bytes, const char* name);
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }

@@ -713,7 +713,7 @@ static ttt_status launch_lin(LinArgs<T>& a, int grid, hipStream_t st) {
             hipLaunchKernelGGL((k_linattn<T, DK, false, 32>), dim3(grid), dim3(kThreads), 0, st, a);
         }
     }
-    return check_launch("k_linattn");
+    return check_launch("k_linattn", st);
 }
 
 template <typename T>
@@ -773,7 +773,7 @@ static ttt_status run_lin_parallel(const linattn_desc& D, LinArgs<T> a, char* ws
         ProfScope ps(PK_LIN_DELTA, st);
         hipLaunchKernelGGL(k_lin_delta<T>, dim3((unsigned)(S * nc * da.ntv * da.ntk)), dim3(kThreads), 0, st, da);
     }
-    ttt_status rc = check_launch("k_lin_delta");
+    ttt_status rc = check_launch("k_lin_delta", st);
     if (rc != TTT_OK) return rc;
     // 2. states seen by each chunk, and S_out
     ScanArgs<T> sa{};
@@ -789,7 +789,7 @@ static ttt_status run_lin_parallel(const linattn_desc& D, LinArgs<T> a, char* ws
         ProfScope ps(PK_LIN_SCAN, st);
         hipLaunchKernelGGL(k_lin_scan<T>, dim3((unsigned)cdiv(S * dvk / 4, kThreads)), dim3(kThreads), 0, st, sa);
     }
-    if ((rc = check_launch("k_lin_scan")) != TTT_OK) return rc;
+    if ((rc = check_launch("k_lin_scan", st)) != TTT_OK) return rc;
     // 3. apply
     ApplyArgs<T> aa{};
     aa.q = a.q;
@@ -813,7 +813,7 @@ static ttt_status run_lin_parallel(const linattn_desc& D, LinArgs<T> a, char* ws
         else
             hipLaunchKernelGGL(k_lin_apply<T>, dim3((unsigned)(S * nc * aa.ntt * aa.ntv)), dim3(kThreads), 0, st, aa);
     }
-    return check_launch(causal ? "k_lin_apply_causal" : "k_lin_apply");
+    return check_launch(causal ? "k_lin_apply_causal" : "k_lin_apply", st);
 }
 
 template <typename T>
@@ -869,6 +869,15 @@ extern "C" ttt_status linattn_forward(const linattn_desc* desc, const void* q, c
     if (need && (!workspace || workspace_bytes < need))
         return fail(TTT_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
     if (need && !aligned(workspace, 256)) return fail(TTT_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    {  // every buffer the call touches lies in a device allocation that holds all of it
+        const bool t = D.N > 0;
+        const struct { const void* p; size_t n; const char* name; } bufs[] = {
+            {q, t ? qb : 0, "q"}, {k, t ? qb : 0, "k"}, {v, t ? vb : 0, "v"}, {o, t ? vb : 0, "o"},
+            {eta, t ? (size_t)S * D.N * 4 : 0, "eta"}, {S0, sb, "S0"}, {S_out, sb, "S_out"},
+            {workspace, need, "workspace"}};
+        for (const auto& b : bufs)
+            if ((rc = check_buffer(b.p, b.n, b.name)) != TTT_OK) return rc;
+    }
     hipStream_t st = (hipStream_t)stream;
     // 32-row slices of S: measured faster than 16-row slices, whose extra workgroups double the
     // re-reads of q and k (the 16-row instantiation is kept for the bf16 kernel)

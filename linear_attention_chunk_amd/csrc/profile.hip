@@ -107,5 +107,5 @@ extern "C" ttt_status ttt_probe_mfma_bf16(int32_t blocks, int32_t iters, float* 
     clear_error();
     if (blocks < 1 || iters < 1 || !out) return fail(TTT_ERR_INVALID_ARGUMENT, "ttt_probe_mfma_bf16: bad arguments");
     hipLaunchKernelGGL(k_mfma_probe, dim3(blocks), dim3(kProbeThreads), 0, (hipStream_t)stream, out, iters);
-    return check_launch("k_mfma_probe");
+    return check_launch("k_mfma_probe", (hipStream_t)stream);
 }

@@ -415,7 +415,7 @@ static ttt_status launch_update(const UpdArgs<T>& u, int grid, hipStream_t st) {
         ProfScope ps(PK_UPDATE, st);
         hipLaunchKernelGGL(k_update<T>, dim3(grid), dim3(kThreads), lds, st, u);
     }
-    return check_launch("k_update");
+    return check_launch("k_update", st);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -924,7 +924,7 @@ static ttt_status run_parallel_form(const ttt_desc& D, const PLayout& L, const T
             hipLaunchKernelGGL(k_w13_cvt<T>, dim3((unsigned)cdiv(n4, kThreads)), dim3(kThreads), 0, st, W0, 3 * dm, w,
                                n4, per4);
         }
-        if ((rc = check_launch("k_w13_cvt")) != TTT_OK) return rc;
+        if ((rc = check_launch("k_w13_cvt", st)) != TTT_OK) return rc;
         W13 = w;
         w13_stride = 2 * dm;
     } else {
@@ -940,7 +940,7 @@ static ttt_status run_parallel_form(const ttt_desc& D, const PLayout& L, const T
         ProfScope ps(PK_PHI, st);
         hipLaunchKernelGGL(k_phi<T>, dim3((unsigned)(2 * S * pa.ntt * pa.nct)), dim3(64 * kUpWaves), 0, st, pa);
     }
-    if ((rc = check_launch("k_phi")) != TTT_OK) return rc;
+    if ((rc = check_launch("k_phi", st)) != TTT_OK) return rc;
     // 3. chunked linear attention over the features, with W2 [d][m] as the state S [d_v][d_k]
     linattn_desc LD{D.B, D.H, D.N, D.m_h, D.d_h, D.chunk, D.io_dtype, D.mask, D.update_chunks};
     uint32_t flags[32] = {};
@@ -1040,7 +1040,7 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
             ProfScope ps(PK_ZERO, st);
             hipLaunchKernelGGL(k_zero, dim3((unsigned)cdiv(n4, kThreads)), dim3(kThreads), 0, st, (float4*)M, n4);
         }
-        if ((rc = check_launch("k_zero")) != TTT_OK) return rc;
+        if ((rc = check_launch("k_zero", st)) != TTT_OK) return rc;
     }
     const int upd_blocks = (2 * m + d) / kUpdRows;
     int cur = 0;
@@ -1096,14 +1096,14 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
                     ProfScope ps(PK_UP, st);
                     hipLaunchKernelGGL(k_up<T>, dim3(S * (a.nQ + a.nK)), dim3(64 * kUpWaves), 0, st, a);
                 }
-                if ((rc = check_launch("k_up")) != TTT_OK) return rc;
+                if ((rc = check_launch("k_up", st)) != TTT_OK) return rc;
             }
             if (a.nG13 + a.nG2 + a.nO) {
                 {
                     ProfScope ps(PK_DOWN, st);
                     hipLaunchKernelGGL(k_down<T>, dim3(S * (a.nG13 + a.nG2 + a.nO)), dim3(kThreads), 0, st, a);
                 }
-                if ((rc = check_launch("k_down")) != TTT_OK) return rc;
+                if ((rc = check_launch("k_down", st)) != TTT_OK) return rc;
             }
             // with momentum or Muon the prep kernel adds the partial-G buffers itself
             if (a.lu && a.ksplit > 1 && !(muon || mom)) {
@@ -1113,7 +1113,7 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
                     hipLaunchKernelGGL(k_gsum, dim3((unsigned)cdiv(n4, kThreads)), dim3(kThreads), 0, st, G, n4,
                                        a.ksplit, a.gpart_stride);
                 }
-                if ((rc = check_launch("k_gsum")) != TTT_OK) return rc;
+                if ((rc = check_launch("k_gsum", st)) != TTT_OK) return rc;
             }
             if (a.lu == 0) continue;
             const int mat0 = D.last_layer_only ? 2 : 0, nmat = D.last_layer_only ? 1 : 3;
@@ -1133,7 +1133,7 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
                     ProfScope ps(PK_MUON_PREP, st);
                     hipLaunchKernelGGL(k_muon_prep<T>, dim3(S * nmat * L.nblk), dim3(kThreads), 0, st, pa);
                 }
-                if ((rc = check_launch("k_muon_prep")) != TTT_OK) return rc;
+                if ((rc = check_launch("k_muon_prep", st)) != TTT_OK) return rc;
                 if (mom) U = M;
             }
             if (muon && D.ns_iters == 0) {
@@ -1143,7 +1143,7 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
                     ProfScope ps(PK_NS_INIT, st);
                     hipLaunchKernelGGL(k_ns_init<T>, dim3(S * nmat * L.nblk), dim3(kThreads), 0, st, na);
                 }
-                if ((rc = check_launch("k_ns_init")) != TTT_OK) return rc;
+                if ((rc = check_launch("k_ns_init", st)) != TTT_OK) return rc;
                 U = Xf;
             } else if (muon) {
                 // step it reads hi plane Xin and writes Xout = Xb[it & 1]; the first step reads U's planes
@@ -1171,13 +1171,13 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
                         if (gsmall) hipLaunchKernelGGL((k_ns_gram<T, 64>), dim3(S * nmat * gt), dim3(kThreads), 0, st, na);
                         else hipLaunchKernelGGL((k_ns_gram<T, 128>), dim3(S * nmat * gt), dim3(kThreads), 0, st, na);
                     }
-                    if ((rc = check_launch("k_ns_gram")) != TTT_OK) return rc;
+                    if ((rc = check_launch("k_ns_gram", st)) != TTT_OK) return rc;
                     na.tiles = stt;
                     {
                         ProfScope ps(PK_NS_STEP, st);
                         hipLaunchKernelGGL(k_ns_step<T>, dim3(S * nmat * stt), dim3(kThreads), 0, st, na);
                     }
-                    if ((rc = check_launch("k_ns_step")) != TTT_OK) return rc;
+                    if ((rc = check_launch("k_ns_step", st)) != TTT_OK) return rc;
                 }
                 U = sizeof(T) == 2 ? Xf : reinterpret_cast<const float*>(Xb[(D.ns_iters - 1) & 1]);
             }
@@ -1244,11 +1244,25 @@ extern "C" ttt_status ttt_forward(const ttt_desc* desc, const void* q, const voi
         return fail(TTT_ERR_INVALID_ARGUMENT, "o overlaps an input");
     if (overlaps(W_out, w_bytes, W0, w0_bytes)) return fail(TTT_ERR_INVALID_ARGUMENT, "W_out overlaps W0");
     hipStream_t st = (hipStream_t)stream;
+    // every buffer the call touches lies in a device allocation that holds all of it
+    auto buffers = [&](size_t ws_need) -> ttt_status {
+        const size_t eb = D.N > 0 ? io_bytes : 0;
+        const struct { const void* p; size_t n; const char* name; } bufs[] = {
+            {q, eb, "q"}, {k, eb, "k"}, {v, eb, "v"}, {o, eb, "o"}, {eta, D.N > 0 ? (size_t)S * D.N * 4 : 0, "eta"},
+            {W0, w0_bytes, "W0"}, {W_out, w_bytes, "W_out"}, {M_inout, D.momentum != 0.0f ? w_bytes : 0, "M_inout"},
+            {workspace, ws_need, "workspace"}};
+        for (const auto& b : bufs) {
+            const ttt_status r = check_buffer(b.p, b.n, b.name);
+            if (r != TTT_OK) return r;
+        }
+        return TTT_OK;
+    };
     if (D.parallel_form) {
         const PLayout PL = make_playout(D);
         if (PL.total > 0 && (!workspace || workspace_bytes < PL.total))
             return fail(TTT_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", PL.total, workspace_bytes);
         if (workspace && !aligned(workspace, 256)) return fail(TTT_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+        if ((rc = buffers(PL.total)) != TTT_OK) return rc;
         if (D.io_dtype == TTT_BF16)
             return run_parallel_form<uint16_t>(D, PL, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, eta,
                                                W0, (uint16_t*)o, W_out, M_inout, (char*)workspace, st);
@@ -1259,6 +1273,7 @@ extern "C" ttt_status ttt_forward(const ttt_desc* desc, const void* q, const voi
     if (L.total > 0 && (!workspace || workspace_bytes < L.total))
         return fail(TTT_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", L.total, workspace_bytes);
     if (workspace && !aligned(workspace, 256)) return fail(TTT_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if ((rc = buffers(L.total)) != TTT_OK) return rc;
     if (D.io_dtype == TTT_BF16)
         return run_ttt<uint16_t>(D, L, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, eta, W0,
                                  (uint16_t*)o, W_out, M_inout, (char*)workspace, st);

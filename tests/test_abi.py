@@ -234,3 +234,28 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(C, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         C.lib()
+
+
+def _gpu_count():
+    try:
+        import torch
+        return torch.cuda.device_count()   # counts devices without initialising HIP
+    except Exception:
+        return 0
+
+
+@pytest.mark.skipif(_gpu_count() > 0, reason="checks the answer of a machine without a GPU")
+def test_valid_calls_without_a_device_report_device_error():
+    """On a machine with no usable HIP device, calls whose arguments pass validation stop at the
+    device-buffer check with TTT_ERR_DEVICE and a message; nothing is launched."""
+    L = C.lib()
+    D = desc()
+    _, need = ws_bytes(D)
+    assert call_forward(D, ws=P16 + (1 << 34), nws=need) == C.TTT_ERR_DEVICE
+    assert b"no usable HIP device" in L.ttt_last_error()
+    Dl = lin_desc()
+    assert L.linattn_forward(ctypes.byref(Dl), P16, P16 + (1 << 30), P16 + (2 << 30), P16 + (3 << 30), None, P16B,
+                             None, None, 0, None) == C.TTT_ERR_DEVICE
+    # the status table answers for any non-negative value
+    assert L.ttt_status_string(C.TTT_ERR_DEVICE) == b"HIP device or launch error"
+    assert L.ttt_status_string(0x7FFFFFFF) == b"unknown status"

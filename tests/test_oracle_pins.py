@@ -175,9 +175,9 @@ def test_l2_normalize_rows_definition():
 # order of the mask (LaCT notes section 1.1, Eq. (10))
 
 def stepper(q, k, v, eta, W1, W3, W2, chunk, mask, rule, ns_iters=5, beta=0.0, last_only=False,
-            upd=None):
+            upd=None, M0=None):
     W = [W1.copy(), W3.copy(), W2.copy()]
-    M = [np.zeros_like(x) for x in W]
+    M = [np.zeros_like(x) for x in W] if M0 is None else [x.copy() for x in M0]
     N = q.shape[0]
     o = np.zeros((N, W2.shape[0]))
     for j, lo in enumerate(range(0, N, chunk)):
@@ -492,3 +492,80 @@ def test_last_layer_gd_inner_steps_scale_eta():
         assert rel(on, o1) < 1e-13
         assert rel(Wn[2], W1s[2]) < 1e-13
         assert rel(Wn[0], W1) == 0.0 and rel(Wn[1], W3) == 0.0
+
+
+# ----------------------------------------------------------------------------------------------
+# the batched wrappers: every (batch, head) slice with its own state, each against an independent
+# route (brute-force sums for the linear model, the finite-difference stepper for the layer)
+
+@pytest.mark.parametrize("mask,chunk,N", [
+    (O.MASK_APPLY_THEN_UPDATE, 4, 13), (O.MASK_UPDATE_THEN_APPLY, 3, 13), (O.MASK_TOKEN_CAUSAL, 4, 11),
+    (O.MASK_FULL, 9, 9), (O.MASK_STRIDED, 4, 14),
+])
+def test_linattn_forward_ref_slices_closed_form(mask, chunk, N):
+    """linattn_forward_ref over B x H slices, each with its own S0 and d_k != d_v, against
+    o_t = S0[b,h] q_t + sum_{s visible} eta_s v_s (k_s . q_t) per slice (Thm. 5.2), and its final
+    states against S0[b,h] + sum over updating chunks of eta_s v_s k_s^T."""
+    B, H, dk, dv = 2, 3, 3, 5
+    rng = np.random.default_rng(100 + 7 * mask + N)
+    q = rng.standard_normal((B, H, N, dk))
+    k = rng.standard_normal((B, H, N, dk))
+    v = rng.standard_normal((B, H, N, dv))
+    eta = rng.standard_normal((B, H, N))
+    S0 = rng.standard_normal((B, H, dv, dk))
+    upd = [1, 0, 1, 1] if mask == O.MASK_STRIDED else None
+    o, S = O.linattn_forward_ref(q, k, v, eta, chunk, mask, S0, upd)
+    assert o.shape == (B, H, N, dv) and S.shape == (B, H, dv, dk)
+    for b in range(B):
+        for h in range(H):
+            for t in range(N):
+                want = [sum(S0[b, h, e, c] * q[b, h, t, c] for c in range(dk)) for e in range(dv)]
+                for s_ in range(N):
+                    if visible(t, s_, chunk, mask, upd):
+                        dot = sum(k[b, h, s_, c] * q[b, h, t, c] for c in range(dk))
+                        for e in range(dv):
+                            want[e] += eta[b, h, s_] * v[b, h, s_, e] * dot
+                assert rel(o[b, h, t], np.array(want)) < 1e-12, (b, h, t)
+            Sw = S0[b, h].copy()
+            for s_ in range(N):
+                if mask != O.MASK_STRIDED or upd[s_ // chunk]:
+                    Sw += eta[b, h, s_] * np.outer(v[b, h, s_], k[b, h, s_])
+            assert rel(S[b, h], Sw) < 1e-12, (b, h)
+    # without S0 the state starts at zero; `slices` computes only the listed slices
+    o0, S0_ = O.linattn_forward_ref(q, k, v, eta, chunk, mask, None, upd, slices=[(1, 2)])
+    o1, _ = O.linattn_forward_ref(q[1:, 2:], k[1:, 2:], v[1:, 2:], eta[1:, 2:], chunk, mask,
+                                  np.zeros((1, 1, dv, dk)), upd)
+    assert rel(o0[1, 2], o1[0, 0]) == 0.0
+    assert not o0[0].any() and not o0[1, :2].any() and not S0_[0].any()
+
+
+@pytest.mark.parametrize("rule,beta,mask", [(O.UPD_GD_L2, 0.0, O.MASK_APPLY_THEN_UPDATE),
+                                            (O.UPD_MUON_L2, 0.9, O.MASK_UPDATE_THEN_APPLY),
+                                            (O.UPD_GD, 0.5, O.MASK_APPLY_THEN_UPDATE)])
+def test_forward_ref_per_batch_weights_and_momentum(rule, beta, mask):
+    """ttt_forward_ref with W0 given per (batch, head) and a non-zero starting momentum M per
+    (batch, head): each slice against the independent finite-difference stepper started from that
+    slice's own W0 and M; `slices` computes only the listed slices."""
+    B, H, N, chunk = 2, 2, 8, 4
+    q, k, v, eta, W1, W3, W2 = tiny_problem(40, N=N)
+    rng = np.random.default_rng(41)
+    Q = np.stack([np.stack([q, k]), np.stack([v, q])])
+    K = np.stack([np.stack([k, v]), np.stack([q, k])])
+    V = np.stack([np.stack([v, q]), np.stack([k, v])])
+    E = np.stack([np.stack([eta, eta[::-1]]), np.stack([eta * 2, eta])])
+    Ws = [np.stack([np.stack([W * (1 + 0.1 * (2 * b + h)) for h in range(H)]) for b in range(B)])
+          for W in (W1, W3, W2)]
+    M = tuple(0.05 * rng.standard_normal(W.shape) for W in Ws)
+    o, W, Mo = O.ttt_forward_ref(Q, K, V, E, *Ws, chunk, mask, rule, 5, beta, M=M)
+    for b in range(B):
+        for h in range(H):
+            o2, W2s, M2 = stepper(Q[b, h], K[b, h], V[b, h], E[b, h], Ws[0][b, h], Ws[1][b, h], Ws[2][b, h], chunk,
+                                  mask, rule, 5, beta, M0=[x[b, h] for x in M])
+            assert rel(o[b, h], o2) < 1e-6, (b, h)
+            for i in range(3):
+                assert rel(W[i][b, h], W2s[i]) < 1e-6, (b, h, i)
+                if beta:
+                    assert rel(Mo[i][b, h], M2[i]) < 1e-6, (b, h, i)
+    o1, W1s, _ = O.ttt_forward_ref(Q, K, V, E, *Ws, chunk, mask, rule, 5, beta, M=M, slices=[(1, 0)])
+    assert rel(o1[1, 0], o[1, 0]) == 0.0 and rel(W1s[2][1, 0], W[2][1, 0]) == 0.0
+    assert not o1[0].any() and not o1[1, 1].any() and not W1s[0][0].any()
