@@ -148,6 +148,27 @@ ttt_status ttt_forward(const ttt_desc* desc, const void* q, const void* k, const
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * ttt_forward for callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same arguments, layout, checks and results as
+ * ttt_forward (the same kernels run), except that there is no workspace argument: the workspace is
+ * a static array of TTT_NOALLOC_SCRATCH_BYTES bytes in the library's device code, one per device,
+ * which stays allocated on every device the library runs on until the process ends.  The call
+ * itself allocates nothing (no hipMalloc, no events: the launch profiler is off for its launches).
+ *   - A call whose ttt_workspace_bytes() exceeds TTT_NOALLOC_SCRATCH_BYTES returns
+ *     TTT_ERR_WORKSPACE with a message, before anything is enqueued.
+ *   - All calls on one device share that device's array, and nothing in it carries over from one
+ *     call to the next.  Calls that overlap on one device (concurrent streams, or a second call
+ *     enqueued from another thread before the first has finished on the device) race on the array:
+ *     the caller must order them, for example by using one stream per device.
+ *   - The first call on a device looks the array's address up (hipGetSymbolAddress); it may fail
+ *     with TTT_ERR_DEVICE if the device is unusable.
+ */
+#define TTT_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+ttt_status ttt_forward_noalloc(const ttt_desc* desc, const void* q, const void* k, const void* v,
+                               const float* eta, const float* W0, void* o, float* W_out, float* M_inout,
+                               void* stream);
+
+/*
  * Device workspace that linattn_forward needs, in bytes.  Zero when the call runs the sequential
  * kernel (chunks so small that 4 d_k d_v > 2 chunk (d_k + d_v), or token-causal mode with N < 256);
  * otherwise room for every chunk's own update and the state each chunk's queries see, 8 bytes per

@@ -96,19 +96,10 @@ def ttt_workspace_bytes(desc: C.TttDesc) -> int:
     return n.value
 
 
-def ttt_forward(q, k, v, eta, W0, chunk: int, mask_mode: int = C.MASK_APPLY_THEN_UPDATE,
-                update_rule: int = C.UPD_GD_L2, *, m_h: Optional[int] = None, ns_iters: int = 5,
-                momentum: float = 0.0, last_layer_only: bool = False, update_chunks=None,
-                M: Optional[torch.Tensor] = None, want_W: bool = True, out: Optional[torch.Tensor] = None,
-                workspace: Optional[torch.Tensor] = None, stream=None, inner_steps: int = 1,
-                ascent: bool = False, parallel_form: bool = False):
-    """The TTT-KVB layer through ttt_forward of libttt.so.
-
-    q, k, v [B, H, N, d] (bf16 or fp32, same dtype); eta [B, H, N] fp32; W0 fp32 [H, 3*d*m] or
-    [B, H, 3*d*m] (see pack_weights).  M, if given, is the [B, H, 3*d*m] fp32 momentum, updated
-    in place.  parallel_form (last_layer_only with plain GD only) computes the same layer as
-    chunked linear attention over the frozen SwiGLU features.  Returns (o, W_out or None).
-    """
+def _ttt_prepare(q, k, v, eta, W0, chunk, mask_mode, update_rule, m_h, ns_iters, momentum, last_layer_only,
+                 update_chunks, M, want_W, out, inner_steps, ascent, parallel_form):
+    """Argument checks shared by ttt_forward and ttt_forward_noalloc; returns the descriptor, the
+    host buffer keeping update_chunks alive, the output and W_out tensors."""
     if not isinstance(q, torch.Tensor) or q.dim() != 4:
         raise ValueError("q must be a [B, H, N, d] tensor")
     B, H, N, d = q.shape
@@ -134,13 +125,52 @@ def ttt_forward(q, k, v, eta, W0, chunk: int, mask_mode: int = C.MASK_APPLY_THEN
         _need(M, "M", torch.float32, dev, wshape)
     D, keep = ttt_desc(B, H, N, d, m_h, chunk, _DT[q.dtype], mask_mode, update_rule, ns_iters, momentum,
                        last_layer_only, per_batch, update_chunks, inner_steps, ascent, parallel_form)
-    nbytes = ttt_workspace_bytes(D)
-    workspace = _workspace(workspace, nbytes, dev)
     o = torch.empty_like(q) if out is None else out
     W_out = torch.empty(wshape, dtype=torch.float32, device=dev) if want_W else None
+    return D, keep, o, W_out
+
+
+def ttt_forward(q, k, v, eta, W0, chunk: int, mask_mode: int = C.MASK_APPLY_THEN_UPDATE,
+                update_rule: int = C.UPD_GD_L2, *, m_h: Optional[int] = None, ns_iters: int = 5,
+                momentum: float = 0.0, last_layer_only: bool = False, update_chunks=None,
+                M: Optional[torch.Tensor] = None, want_W: bool = True, out: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None, stream=None, inner_steps: int = 1,
+                ascent: bool = False, parallel_form: bool = False):
+    """The TTT-KVB layer through ttt_forward of libttt.so.
+
+    q, k, v [B, H, N, d] (bf16 or fp32, same dtype); eta [B, H, N] fp32; W0 fp32 [H, 3*d*m] or
+    [B, H, 3*d*m] (see pack_weights).  M, if given, is the [B, H, 3*d*m] fp32 momentum, updated
+    in place.  parallel_form (last_layer_only with plain GD only) computes the same layer as
+    chunked linear attention over the frozen SwiGLU features.  Returns (o, W_out or None).
+    """
+    D, keep, o, W_out = _ttt_prepare(q, k, v, eta, W0, chunk, mask_mode, update_rule, m_h, ns_iters, momentum,
+                                     last_layer_only, update_chunks, M, want_W, out, inner_steps, ascent,
+                                     parallel_form)
+    nbytes = ttt_workspace_bytes(D)
+    workspace = _workspace(workspace, nbytes, q.device)
     st = C.lib().ttt_forward(ctypes.byref(D), _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(W0), _ptr(o), _ptr(W_out),
                              _ptr(M), _ptr(workspace), ctypes.c_size_t(0 if workspace is None else workspace.numel()),
                              _stream_handle(stream))
+    del keep
+    C.check(st)
+    return o, W_out
+
+
+def ttt_forward_noalloc(q, k, v, eta, W0, chunk: int, mask_mode: int = C.MASK_APPLY_THEN_UPDATE,
+                        update_rule: int = C.UPD_GD_L2, *, m_h: Optional[int] = None, ns_iters: int = 5,
+                        momentum: float = 0.0, last_layer_only: bool = False, update_chunks=None,
+                        M: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                        W_out: Optional[torch.Tensor] = None, stream=None, inner_steps: int = 1,
+                        ascent: bool = False, parallel_form: bool = False):
+    """ttt_forward through ttt_forward_noalloc: the library's static device scratch replaces the
+    workspace, and the library allocates nothing.  Pass `out` (and `W_out`, [B, H, 3*d*m] fp32, or
+    None to skip the final weights) to keep this wrapper from allocating too.  Returns (o, W_out)."""
+    D, keep, o, _ = _ttt_prepare(q, k, v, eta, W0, chunk, mask_mode, update_rule, m_h, ns_iters, momentum,
+                                 last_layer_only, update_chunks, M, False, out, inner_steps, ascent, parallel_form)
+    if W_out is not None:
+        _need(W_out, "W_out", torch.float32, q.device, (D.B, D.H, 3 * D.d_h * D.m_h))
+    st = C.lib().ttt_forward_noalloc(ctypes.byref(D), _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(W0), _ptr(o),
+                                     _ptr(W_out), _ptr(M), _stream_handle(stream))
     del keep
     C.check(st)
     return o, W_out

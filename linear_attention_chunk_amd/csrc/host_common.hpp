@@ -41,6 +41,14 @@ struct ProfScope {
 // under graph capture cannot be synchronised, so such a call returns TTT_ERR_DEVICE).
 bool debug_sync();
 
+// While one exists on a thread, launches on that thread are not bracketed by the profiler (whose
+// events are created per launch): used by the entry point that must not allocate.
+struct ProfSuppress {
+    bool was;
+    ProfSuppress();
+    ~ProfSuppress();
+};
+
 inline ttt_status check_launch(const char* what, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(TTT_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));

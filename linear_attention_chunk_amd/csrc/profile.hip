@@ -18,8 +18,13 @@ const char* kNames[TTT_PROF_KERNELS] = {"k_up", "k_down", "k_update", "k_muon_pr
                                         "k_lin_delta", "k_lin_scan", "k_lin_apply", "k_phi", "k_w13_cvt", "k_zero"};
 }  // namespace
 
+static thread_local bool t_prof_off = false;
+ProfSuppress::ProfSuppress() : was(t_prof_off) { t_prof_off = true; }
+ProfSuppress::~ProfSuppress() { t_prof_off = was; }
+
 ProfScope::ProfScope(int id_, hipStream_t st_) : id(id_), st(st_) {
-    if (!g_on.load(std::memory_order_relaxed) || !((g_mask.load(std::memory_order_relaxed) >> id) & 1u)) return;
+    if (t_prof_off || !g_on.load(std::memory_order_relaxed) || !((g_mask.load(std::memory_order_relaxed) >> id) & 1u))
+        return;
     if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) { a = b = nullptr; return; }
     (void)hipEventRecord(a, st);
 }

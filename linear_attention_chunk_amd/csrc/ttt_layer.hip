@@ -14,6 +14,7 @@
 // The fp32 fast weights live in a ping-pong pair in the workspace; the shadows (W1, W3, W2, W2^T)
 // are what the next chunk's MFMAs read.
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "host_common.hpp"
@@ -1220,10 +1221,13 @@ extern "C" ttt_status ttt_workspace_bytes(const ttt_desc* desc, size_t* bytes) {
     return TTT_OK;
 }
 
-extern "C" ttt_status ttt_forward(const ttt_desc* desc, const void* q, const void* k, const void* v,
-                                  const float* eta, const float* W0, void* o, float* W_out, float* M_inout,
-                                  void* workspace, size_t workspace_bytes, void* stream) {
-    clear_error();
+namespace ttt {
+// ttt_forward with the workspace either the caller's (scratch == false: checked against its HIP
+// allocation like every other buffer) or the library's static scratch array (scratch == true:
+// workspace_bytes is the array's size, and calls needing more are refused).
+static ttt_status forward_impl(const ttt_desc* desc, const void* q, const void* k, const void* v, const float* eta,
+                               const float* W0, void* o, float* W_out, float* M_inout, void* workspace,
+                               size_t workspace_bytes, void* stream, bool scratch) {
     ttt_status rc = validate(desc);
     if (rc != TTT_OK) return rc;
     const ttt_desc& D = *desc;
@@ -1250,7 +1254,7 @@ extern "C" ttt_status ttt_forward(const ttt_desc* desc, const void* q, const voi
         const struct { const void* p; size_t n; const char* name; } bufs[] = {
             {q, eb, "q"}, {k, eb, "k"}, {v, eb, "v"}, {o, eb, "o"}, {eta, D.N > 0 ? (size_t)S * D.N * 4 : 0, "eta"},
             {W0, w0_bytes, "W0"}, {W_out, w_bytes, "W_out"}, {M_inout, D.momentum != 0.0f ? w_bytes : 0, "M_inout"},
-            {workspace, ws_need, "workspace"}};
+            {scratch ? nullptr : workspace, ws_need, "workspace"}};
         for (const auto& b : bufs) {
             const ttt_status r = check_buffer(b.p, b.n, b.name);
             if (r != TTT_OK) return r;
@@ -1260,7 +1264,8 @@ extern "C" ttt_status ttt_forward(const ttt_desc* desc, const void* q, const voi
     if (D.parallel_form) {
         const PLayout PL = make_playout(D);
         if (PL.total > 0 && (!workspace || workspace_bytes < PL.total))
-            return fail(TTT_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", PL.total, workspace_bytes);
+            return fail(TTT_ERR_WORKSPACE, scratch ? "the call needs %zu bytes of scratch, the library's array holds %zu"
+                                                   : "workspace needs %zu bytes, got %zu", PL.total, workspace_bytes);
         if (workspace && !aligned(workspace, 256)) return fail(TTT_ERR_WORKSPACE, "workspace must be 256-byte aligned");
         if ((rc = buffers(PL.total)) != TTT_OK) return rc;
         if (D.io_dtype == TTT_BF16)
@@ -1271,7 +1276,8 @@ extern "C" ttt_status ttt_forward(const ttt_desc* desc, const void* q, const voi
     }
     const Layout L = make_layout(D, is_muon(D), D.momentum != 0.0f && !M_inout);
     if (L.total > 0 && (!workspace || workspace_bytes < L.total))
-        return fail(TTT_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", L.total, workspace_bytes);
+        return fail(TTT_ERR_WORKSPACE, scratch ? "the call needs %zu bytes of scratch, the library's array holds %zu"
+                                               : "workspace needs %zu bytes, got %zu", L.total, workspace_bytes);
     if (workspace && !aligned(workspace, 256)) return fail(TTT_ERR_WORKSPACE, "workspace must be 256-byte aligned");
     if ((rc = buffers(L.total)) != TTT_OK) return rc;
     if (D.io_dtype == TTT_BF16)
@@ -1279,4 +1285,57 @@ extern "C" ttt_status ttt_forward(const ttt_desc* desc, const void* q, const voi
                                  (uint16_t*)o, W_out, M_inout, (char*)workspace, st);
     return run_ttt<float>(D, L, (const float*)q, (const float*)k, (const float*)v, eta, W0, (float*)o, W_out,
                           M_inout, (char*)workspace, st);
+}
+
+// Scratch of the entry point that allocates nothing: one array per device, holding the workspace of
+// one call, kept until the process ends.  Host code never uses the array's name as an address (on
+// the host it stands for a host-side shadow); it uses the device address hipGetSymbolAddress gives
+// for the current device, looked up once per device.
+constexpr size_t kScratchBytes = TTT_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+static ttt_status scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(TTT_ERR_DEVICE, "no usable HIP device (%s)", hipGetErrorString(e));
+    }
+    if (dev < 0 || dev >= kMaxDevices) return fail(TTT_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return fail(TTT_ERR_DEVICE, "scratch array address on device %d: %s", dev, hipGetErrorString(e));
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return TTT_OK;
+}
+}  // namespace ttt
+
+extern "C" ttt_status ttt_forward(const ttt_desc* desc, const void* q, const void* k, const void* v,
+                                  const float* eta, const float* W0, void* o, float* W_out, float* M_inout,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+    clear_error();
+    return forward_impl(desc, q, k, v, eta, W0, o, W_out, M_inout, workspace, workspace_bytes, stream, false);
+}
+
+extern "C" ttt_status ttt_forward_noalloc(const ttt_desc* desc, const void* q, const void* k, const void* v,
+                                          const float* eta, const float* W0, void* o, float* W_out, float* M_inout,
+                                          void* stream) {
+    clear_error();
+    ttt_status rc = validate(desc);
+    if (rc != TTT_OK) return rc;
+    void* ws = nullptr;
+    if ((rc = scratch_address(&ws)) != TTT_OK) return rc;
+    ProfSuppress quiet;  // the profiler creates events per launch; this call creates nothing
+    return forward_impl(desc, q, k, v, eta, W0, o, W_out, M_inout, ws, kScratchBytes, stream, true);
 }
