@@ -305,6 +305,8 @@ def main():
         "k_lin_scan": ("hbm", 8 * dm * S * nchunks),
         # W1 | W3 of the H weight blocks read in fp32 and written in bf16
         "k_w13_cvt": ("hbm", (4 + es) * 2 * dm * H),
+        # parallel form with Muon: every chunk's W2 update read and its momentum written (fp32)
+        "k_par_momentum": ("hbm", 8 * dm * S * nchunks),
     }
     dom_ms, dom_n = prof[dom]
     avg = dom_ms / max(dom_n, 1)
@@ -464,10 +466,35 @@ def main():
                                                               out=o, workspace=wsp), st, 1)
             del wsp
         extras["lact_lm_last_layer_gd"] = {
-            "workload": f"B{B} H{H} N{N} d{d} m{m} chunk {chunk} bf16, apply-then-update, only W2 learns, W - g",
+            "workload": f"B{B} H{H} N{N} d{d} m{m} chunk {chunk} bf16, apply-then-update, only W2 learns, W - g "
+                        "(plain GD: no momentum, no Muon, no weight norm)",
             "recurrence_ms_per_call": round(msp[False], 3), "parallel_form_ms_per_call": round(msp[True], 3),
             "parallel_form_tokens_per_s": round(tokens / (msp[True] * 1e-3)),
             "parallel_form_speedup": round(msp[False] / msp[True], 2)}
+        # Variant 2 of the paper's ablation: only W2 learns, momentum 0.9, per-token eta and Muon (5
+        # Newton-Schulz steps) kept, no weight norm; chunk recurrence against the parallel form
+        print("[bench] extras: Variant 2 (last layer, Muon + momentum), recurrence and parallel form",
+              file=sys.stderr, flush=True)
+        msv = {}
+        for pf in (False, True):
+            Dv, _ = T.ttt_desc(B, H, N, d, m, chunk, C.TTT_BF16, C.MASK_APPLY_THEN_UPDATE, C.UPD_MUON, 5, 0.9,
+                               last_layer_only=True, parallel_form=pf)
+            wsv = torch.empty(max(1, T.ttt_workspace_bytes(Dv)), dtype=torch.uint8, device="cuda")
+            Mv = torch.zeros((B, H, 3 * d * m), dtype=torch.float32, device="cuda")
+            msv[pf] = time_calls(torch, lambda: T.ttt_forward(q, k, v, eta, W0, chunk, C.MASK_APPLY_THEN_UPDATE,
+                                                              C.UPD_MUON, m_h=m, momentum=0.9, M=Mv,
+                                                              last_layer_only=True, parallel_form=pf, out=o,
+                                                              workspace=wsv), st, 1)
+            del wsv, Mv
+        extras["lact_lm_variant2_muon"] = {
+            "workload": f"B{B} H{H} N{N} d{d} m{m} chunk {chunk} bf16, apply-then-update, only W2 learns, "
+                        "momentum 0.9 + Muon (5 steps), no weight norm",
+            "recurrence_ms_per_call": round(msv[False], 3), "parallel_form_ms_per_call": round(msv[True], 3),
+            "recurrence_tokens_per_s": round(tokens / (msv[False] * 1e-3)),
+            "parallel_form_tokens_per_s": round(tokens / (msv[True] * 1e-3)),
+            "parallel_form_speedup": round(msv[False] / msv[True], 2),
+            "pages_context": "Table 2 Variant 2 on the pages' (unstated) hardware: 11.02 M tokens/s recurrent, "
+                             "30.18 M parallel"}
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,

@@ -101,13 +101,19 @@ typedef struct ttt_desc {
     int32_t ascent;           /* 1: gradient ascent, W moves along +g instead of -g (same paper,
                                  Sec. 4.2); 0: descent                                          */
     int32_t parallel_form;    /* 1: compute the layer in its parallel static-kernel form.  Needs
-                                 last_layer_only = 1 and rule TTT_UPD_GD: W1 and W3 are then
-                                 frozen, phi(x) = SiLU(W1 x) * (W3 x) is fixed, and W2 follows
-                                 chunked linear attention with queries phi(q), keys phi(k),
-                                 values v and state W2 ("TTT with KV Binding Is Secretly Linear
-                                 Attention", Thm. 5.2-5.3, Sec. 6.1, Table 2 Variant 2).  Same
-                                 results as 0 (the chunk recurrence) up to rounding; momentum,
-                                 inner_steps and ascent included.  Other rules: INVALID_ARGUMENT */
+                                 last_layer_only = 1 and rule TTT_UPD_GD or TTT_UPD_MUON (no
+                                 weight norm): W1 and W3 are then frozen, phi(x) = SiLU(W1 x) *
+                                 (W3 x) is fixed, and a chunk's W2 gradient -sum eta v phi(k)^T
+                                 does not depend on W2, so W2 follows a prefix over chunks ("TTT
+                                 with KV Binding Is Secretly Linear Attention", Thm. 5.2-5.3,
+                                 Sec. 6.1-6.2, Table 2).  TTT_UPD_GD: chunked linear attention
+                                 with queries phi(q), keys phi(k), values v, state W2 (momentum,
+                                 inner_steps and ascent included).  TTT_UPD_MUON (Table 2's Variant
+                                 2): the chunk momentum as a scan over chunks, Newton-Schulz on
+                                 every chunk's momentum at once, W2 minus their prefix sum; one
+                                 gradient step per chunk (inner_steps > 1: UNSUPPORTED).  Same
+                                 results as 0 (the chunk recurrence) up to rounding.  Other rules:
+                                 INVALID_ARGUMENT */
 } ttt_desc;
 
 typedef struct linattn_desc {
@@ -201,7 +207,7 @@ ttt_status linattn_forward(const linattn_desc* desc, const void* q, const void* 
  * read, and forgets them.  Kernel classes are numbered 0 .. TTT_PROF_KERNELS-1 and named by
  * ttt_profile_kernel_name.  Enabling or reading while another thread launches is allowed.
  */
-#define TTT_PROF_KERNELS 14
+#define TTT_PROF_KERNELS 15
 ttt_status ttt_profile_enable(int32_t on);
 /* Restricts the bracketing to the kernel classes i whose bit (1u << i) is set in mask; the
  * default is every class.  Each bracket records two events on the launch's stream, which costs

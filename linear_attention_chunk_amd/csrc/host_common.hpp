@@ -24,7 +24,7 @@ inline ttt_status fail(ttt_status s, const char* fmt, ...) {
 
 // kernel classes of the optional launch profiler (ttt_profile_*)
 enum ProfKernel { PK_UP = 0, PK_DOWN, PK_UPDATE, PK_MUON_PREP, PK_NS_INIT, PK_NS_GRAM, PK_NS_STEP, PK_LINATTN,
-                  PK_LIN_DELTA, PK_LIN_SCAN, PK_LIN_APPLY, PK_PHI, PK_W13, PK_ZERO };
+                  PK_LIN_DELTA, PK_LIN_SCAN, PK_LIN_APPLY, PK_PHI, PK_W13, PK_ZERO, PK_PAR_MOM };
 
 // Brackets one launch with events on its stream while profiling is enabled; no-op otherwise.
 struct ProfScope {
@@ -97,6 +97,11 @@ struct LinStateIO {
     int mom = 0;
     float beta = 0.f, msign = 1.f, dsign = 1.f;
     int reps = 1;
+    // Optional step between the chunk updates and the scan: called with dS (nscan x nchunks
+    // matrices of d_v x d_k, fp32; chunks a strided mask skips hold no data), it enqueues work on
+    // the stream and sets *src to the buffer of the same layout that the scan then reads as dS.
+    ttt_status (*between)(void* ctx, float* dS, const float** src, hipStream_t st) = nullptr;
+    void* between_ctx = nullptr;
 };
 // workspace of lin_chunked_run: dS_c (fp32) and S_c (bf16 hi + lo, or fp32) per chunk
 size_t lin_chunked_ws_bytes(int64_t nscan, int64_t nchunks, int d_k, int d_v);

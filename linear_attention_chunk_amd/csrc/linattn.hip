@@ -775,9 +775,12 @@ static ttt_status run_lin_parallel(const linattn_desc& D, LinArgs<T> a, char* ws
     }
     ttt_status rc = check_launch("k_lin_delta", st);
     if (rc != TTT_OK) return rc;
+    // (the caller's step between the updates and the scan, which may hand the scan another buffer)
+    const float* scan_src = dS;
+    if (io.between && (rc = io.between(io.between_ctx, dS, &scan_src, st)) != TTT_OK) return rc;
     // 2. states seen by each chunk, and S_out
     ScanArgs<T> sa{};
-    sa.dS = dS;
+    sa.dS = scan_src;
     sa.Sc = Sc;
     sa.io = io;
     sa.dvk = dvk;

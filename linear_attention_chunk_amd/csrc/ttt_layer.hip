@@ -441,6 +441,8 @@ template <typename T> struct PrepArgs {
     float* part; int nblk;
     T* Xhi; T* Xlo; int64_t x_stride;     // bf16 mode, Newton-Schulz: U as hi + lo planes; else null
     int64_t dm; int mat0, nmat;
+    int mbase;                            // matrix index of a scan's first stored matrix (offsets are
+                                          // (mat - mbase) d m): 0 for [W1 | W3 | W2], 2 for W2 alone
 };
 
 __device__ __forceinline__ float block_sum(float x, float* red) {
@@ -458,11 +460,12 @@ __global__ __launch_bounds__(kThreads) void k_muon_prep(PrepArgs<T> a) {
     const int per = a.nmat * a.nblk;
     const int s = blockIdx.x / per, t = blockIdx.x % per;
     const int mat = a.mat0 + t / a.nblk, blk = t % a.nblk;
-    const float* G = a.G + s * a.g_stride + mat * a.dm;
-    float* Gs = a.Gsum ? a.Gsum + s * a.g_stride + mat * a.dm : nullptr;
-    float* M = a.M ? a.M + s * a.m_stride + mat * a.dm : nullptr;
-    T* Xh = a.Xhi ? a.Xhi + s * a.x_stride + mat * a.dm : nullptr;
-    T* Xl = a.Xhi ? a.Xlo + s * a.x_stride + mat * a.dm : nullptr;
+    const int64_t mo = (int64_t)(mat - a.mbase) * a.dm;
+    const float* G = a.G + s * a.g_stride + mo;
+    float* Gs = a.Gsum ? a.Gsum + s * a.g_stride + mo : nullptr;
+    float* M = a.M ? a.M + s * a.m_stride + mo : nullptr;
+    T* Xh = a.Xhi ? a.Xhi + s * a.x_stride + mo : nullptr;
+    T* Xl = a.Xhi ? a.Xlo + s * a.x_stride + mo : nullptr;
     float ss = 0.f;
     const int64_t e0 = (int64_t)blk * kPrepElems;
     // all loads first (an index past the matrix reads its last element and is not used), then the
@@ -515,6 +518,7 @@ template <typename T> struct NSArgs {
     int64_t x_stride;
     T* Gram; int64_t gram_stride;         // 3 x p*p
     int d, m, mat0, nmat, tiles;          // tiles per matrix
+    int mbase;                            // as in PrepArgs: offsets are (mat - mbase) d m, (mat - mbase) p^2
 };
 
 // s = 1 / (||U||_F + 1e-7) from nblk partial sums; every lane of every wave gets the same value
@@ -532,8 +536,8 @@ __global__ __launch_bounds__(kThreads) void k_ns_init(NSArgs<T> a) {
     const int s = blockIdx.x / per, t = blockIdx.x % per;
     const int mat = a.mat0 + t / a.nblk, blk = t % a.nblk;
     const float inv = ns_scale(a.part + ((int64_t)s * 3 + mat) * a.nblk, a.nblk);
-    const float* U = a.U + s * a.u_stride + mat * dm;
-    float* Xf = a.Xf + s * a.x_stride + mat * dm;
+    const float* U = a.U + s * a.u_stride + (mat - a.mbase) * dm;
+    float* Xf = a.Xf + s * a.x_stride + (mat - a.mbase) * dm;
     const int64_t e0 = (int64_t)blk * kPrepElems;
     constexpr int NI = kPrepElems / kThreads;
 #pragma unroll
@@ -571,8 +575,8 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 3 : 2) void k_ns_gram(NS
     int ti = 0;
     while (t >= np - ti) t -= np - ti++;  // uniform: row ti of the upper triangle, column ti + t
     const int i0 = ti * TS, j0 = (ti + t) * TS;
-    const T* X = a.Xin + s * a.x_stride + mat * dm;
-    T* Gm = a.Gram + s * a.gram_stride + (int64_t)mat * p * p;
+    const T* X = a.Xin + s * a.x_stride + (mat - a.mbase) * dm;
+    T* Gm = a.Gram + s * a.gram_stride + (int64_t)(mat - a.mbase) * p * p;
     T* tT = reinterpret_cast<T*>(smem);
     auto epi = [&](auto& tl) {
         float sc2 = 1.0f;
@@ -661,9 +665,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_ns_step(NSArgs<T> a) {
     const int nct = (c + kNSStepCols - 1) / kNSStepCols;
     const int r0 = (t / nct) * kNSStepRows, c0 = (t % nct) * kNSStepCols;
     if (r0 >= r) return;  // a.tiles covers the larger of the tall and wide tilings
-    const int64_t base = (int64_t)s * a.x_stride + (int64_t)mat * dm;
+    const int64_t base = (int64_t)s * a.x_stride + (int64_t)(mat - a.mbase) * dm;
     const T* X = a.Xin + base;
-    const T* Gm = a.Gram + s * a.gram_stride + (int64_t)mat * p * p;
+    const T* Gm = a.Gram + s * a.gram_stride + (int64_t)(mat - a.mbase) * p * p;
     // this tile's own positions, as 32-bit offsets from its corner
     const int64_t corner = base + (int64_t)r0 * c + c0;
     const T* Xh = a.Xin + corner;
@@ -875,10 +879,12 @@ static Layout make_layout(const ttt_desc& D, bool muon, bool own_m) {
 }
 
 // Workspace of the parallel form: W1 | W3 in bf16 (bf16 io only), phi(q), phi(k), and the
-// linear-attention chunk states.
+// linear-attention chunk states; with Muon also the Newton-Schulz buffers of every (scan, chunk)
+// matrix (Frobenius partial sums, iterate planes, fp32 result, Gram matrices).
 struct PLayout {
-    size_t w13, phq, phk, lin, total;
+    size_t w13, phq, phk, lin, part, xb[2], xlo, xf, gram, total;
     int64_t nc;
+    int nblk;
 };
 
 static PLayout make_playout(const ttt_desc& D) {
@@ -892,8 +898,150 @@ static PLayout make_playout(const ttt_desc& D) {
     L.phq = take((size_t)S * D.N * D.m_h * es);
     L.phk = take((size_t)S * D.N * D.m_h * es);
     L.lin = take(lin_chunked_ws_bytes(S, L.nc, D.m_h, D.d_h));
+    L.nblk = (int)cdiv(dm, kPrepElems);
+    if (D.rule == TTT_UPD_MUON) {
+        const int64_t nmx = S * L.nc, p = std::min(D.d_h, D.m_h);
+        L.part = take((size_t)nmx * 3 * L.nblk * 4);
+        L.xb[0] = take((size_t)nmx * dm * es);
+        L.xb[1] = take((size_t)nmx * dm * es);
+        if (es == 2) L.xlo = take((size_t)nmx * dm * es);
+        L.xf = take((size_t)nmx * dm * 4);
+        L.gram = take((size_t)nmx * p * p * es);
+    }
     L.total = off;
     return L;
+}
+
+// Momentum over the chunks of the parallel form with Muon (last layer only: a chunk's W2 gradient
+// g_c = -sum eta v phi(k)^T depends on the frozen phi and on v alone, never on W2, so every chunk's
+// g_c is known up front).  One thread owns 4 consecutive elements of one scan's W2 and walks the
+// chunks in order: for an updating chunk m <- beta m + g_c, and m replaces dS_c (dS_c = -g_c for
+// descent, +g_c for ascent); a chunk that does not update leaves m as it is and its slot is zeroed.
+// m starts from M0 (the W2 block of the caller's momentum) or zero, and leaves in Mout.
+struct ParMomArgs {
+    float* dS; const float* M0; float* Mout; int64_t m_stride;
+    int64_t dm; int nc, nscan, mode; float beta, gsign;  // g_c = gsign * dS_c
+    uint32_t flags[32];
+};
+
+__global__ __launch_bounds__(kThreads) void k_par_momentum(ParMomArgs a) {
+    const int64_t per = a.dm / 4;
+    const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (g >= per * a.nscan) return;
+    const int64_t scan = g / per, e = (g % per) * 4;
+    f32x4_t m = {0.f, 0.f, 0.f, 0.f};
+    if (a.M0)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) m[u] = a.M0[scan * a.m_stride + e + u];
+    for (int c = 0; c < a.nc; ++c) {
+        f32x4_t* p = reinterpret_cast<f32x4_t*>(a.dS + (scan * a.nc + c) * a.dm + e);
+        if (a.mode != TTT_MASK_STRIDED || ((a.flags[c >> 5] >> (c & 31)) & 1u)) {
+            m = a.beta * m + a.gsign * *p;
+            *p = m;
+        } else {
+            *p = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    if (a.Mout)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) a.Mout[scan * a.m_stride + e + u] = m[u];
+}
+
+// The parallel form's step between the chunk updates and the state scan, with Muon: the momentum
+// over chunks (k_par_momentum), then Newton-Schulz on every (scan, chunk) momentum matrix at once
+// with the recurrence's kernels (each such matrix is a d x m W2 block).  The scan then subtracts
+// U_c = Muon(M_c) from W2 chunk by chunk.
+template <typename T> struct ParMuon {
+    const ttt_desc* D;
+    const PLayout* L;
+    char* ws;
+    float* M_inout;
+    uint32_t flags[32];
+};
+
+template <typename T>
+static ttt_status par_muon_between(void* ctx, float* dS, const float** src, hipStream_t st) {
+    const ParMuon<T>& c = *static_cast<const ParMuon<T>*>(ctx);
+    const ttt_desc& D = *c.D;
+    const PLayout& L = *c.L;
+    const int64_t S = (int64_t)D.B * D.H, nmx = S * L.nc, d = D.d_h, m = D.m_h, dm = d * m;
+    ttt_status rc;
+    {  // 1. momentum over chunks, in place
+        ParMomArgs ma{};
+        ma.dS = dS;
+        if (D.momentum != 0.0f && c.M_inout) {
+            ma.M0 = c.M_inout + 2 * dm;
+            ma.Mout = c.M_inout + 2 * dm;
+            ma.m_stride = 3 * dm;
+        }
+        ma.dm = dm;
+        ma.nc = (int)L.nc;
+        ma.nscan = (int)S;
+        ma.mode = D.mask;
+        ma.beta = D.momentum;
+        ma.gsign = D.ascent ? 1.0f : -1.0f;
+        for (int w = 0; w < 32; ++w) ma.flags[w] = c.flags[w];
+        {
+            ProfScope ps(PK_PAR_MOM, st);
+            hipLaunchKernelGGL(k_par_momentum, dim3((unsigned)cdiv(S * dm / 4, kThreads)), dim3(kThreads), 0, st, ma);
+        }
+        if ((rc = check_launch("k_par_momentum", st)) != TTT_OK) return rc;
+    }
+    float* part = (float*)(c.ws + L.part);
+    T* Xb[2] = {(T*)(c.ws + L.xb[0]), (T*)(c.ws + L.xb[1])};
+    T* Xlo = sizeof(T) == 2 ? (T*)(c.ws + L.xlo) : nullptr;
+    float* Xf = (float*)(c.ws + L.xf);
+    const bool split = sizeof(T) == 2 && D.ns_iters > 0;
+    {  // 2. Frobenius partial sums of each matrix (and, in bf16 mode, its hi + lo planes)
+        PrepArgs<T> pa{dS, dm, 1, 0, nullptr, nullptr, 0, 0.0f, part, L.nblk, split ? Xb[1] : nullptr,
+                       split ? Xlo : nullptr, dm, dm, 2, 1, 2};
+        {
+            ProfScope ps(PK_MUON_PREP, st);
+            hipLaunchKernelGGL(k_muon_prep<T>, dim3((unsigned)(nmx * L.nblk)), dim3(kThreads), 0, st, pa);
+        }
+        if ((rc = check_launch("k_muon_prep", st)) != TTT_OK) return rc;
+    }
+    if (D.ns_iters == 0) {  // 3. U_c = M_c / (||M_c||_F + 1e-7)
+        NSArgs<T> na{dS, dm, part, L.nblk, nullptr, nullptr, nullptr, Xf, dm, nullptr, 0, (int)d, (int)m, 2, 1, 0, 2};
+        {
+            ProfScope ps(PK_NS_INIT, st);
+            hipLaunchKernelGGL(k_ns_init<T>, dim3((unsigned)(nmx * L.nblk)), dim3(kThreads), 0, st, na);
+        }
+        if ((rc = check_launch("k_ns_init", st)) != TTT_OK) return rc;
+        *src = Xf;
+        return TTT_OK;
+    }
+    // 3. ns_iters Newton-Schulz steps on every matrix (as in the recurrence: the first step folds
+    // the Frobenius scaling in; bf16 mode ends in fp32 in Xf, fp32 mode reads M_c in place first)
+    const T* first = sizeof(T) == 2 ? Xb[1] : reinterpret_cast<const T*>(dS);
+    const int64_t p = std::min(d, m);
+    NSArgs<T> na{nullptr, 0, nullptr, L.nblk, first, Xb[0], Xlo, nullptr, dm, (T*)(c.ws + L.gram), p * p, (int)d,
+                 (int)m, 2, 1, 0, 2};
+    const bool gsmall = nmx * cdiv(p, 128) * (cdiv(p, 128) + 1) / 2 < 256;
+    const int gts = gsmall ? 64 : 128;
+    const int gt = (int)(cdiv(p, gts) * (cdiv(p, gts) + 1) / 2);
+    const int stt = (int)std::max(cdiv(m, kNSStepRows) * cdiv(d, kNSStepCols), cdiv(d, kNSStepRows) * cdiv(m, kNSStepCols));
+    for (int it = 0; it < D.ns_iters; ++it) {
+        na.Xin = it == 0 ? first : Xb[(it - 1) & 1];
+        na.Xout = Xb[it & 1];
+        na.part = it == 0 ? part : nullptr;
+        na.Xf = (sizeof(T) == 2 && it == D.ns_iters - 1) ? Xf : nullptr;
+        na.tiles = gt;
+        {
+            ProfScope ps(PK_NS_GRAM, st);
+            if (gsmall) hipLaunchKernelGGL((k_ns_gram<T, 64>), dim3((unsigned)(nmx * gt)), dim3(kThreads), 0, st, na);
+            else hipLaunchKernelGGL((k_ns_gram<T, 128>), dim3((unsigned)(nmx * gt)), dim3(kThreads), 0, st, na);
+        }
+        if ((rc = check_launch("k_ns_gram", st)) != TTT_OK) return rc;
+        na.tiles = stt;
+        {
+            ProfScope ps(PK_NS_STEP, st);
+            hipLaunchKernelGGL(k_ns_step<T>, dim3((unsigned)(nmx * stt)), dim3(kThreads), 0, st, na);
+        }
+        if ((rc = check_launch("k_ns_step", st)) != TTT_OK) return rc;
+    }
+    *src = sizeof(T) == 2 ? Xf : reinterpret_cast<const float*>(Xb[(D.ns_iters - 1) & 1]);
+    return TTT_OK;
 }
 
 template <typename T>
@@ -954,6 +1102,15 @@ static ttt_status run_parallel_form(const ttt_desc& D, const PLayout& L, const T
     io.s0_heads = D.w0_per_batch ? 0 : D.H;
     io.Sout = W_out ? W_out + 2 * dm : nullptr;
     io.sout_stride = 3 * dm;
+    ParMuon<T> pm{&D, &L, ws, M_inout, {}};
+    if (D.rule == TTT_UPD_MUON) {  // W2 <- W2 - Muon(M_c): the scan subtracts what the hook leaves
+        for (int w = 0; w < 32; ++w) pm.flags[w] = flags[w];
+        io.between = &par_muon_between<T>;
+        io.between_ctx = &pm;
+        io.dsign = -1.0f;
+        if ((rc = lin_chunked_run<T>(LD, flags, phq, phk, v, eta, o, io, ws + L.lin, st)) != TTT_OK) return rc;
+        return copy_w0(2 * dm);
+    }
     if (D.momentum != 0.0f) {  // M <- beta M + g, W <- W - M: the running term is m = -M
         io.mom = 1;
         io.beta = D.momentum;
@@ -997,9 +1154,12 @@ static ttt_status validate(const ttt_desc* D) {
     if (D->parallel_form != 0 && D->parallel_form != 1)
         return fail(TTT_ERR_INVALID_ARGUMENT, "parallel_form must be 0/1");
     if (D->parallel_form) {
-        if (!D->last_layer_only || D->rule != TTT_UPD_GD)
+        if (!D->last_layer_only || (D->rule != TTT_UPD_GD && D->rule != TTT_UPD_MUON))
             return fail(TTT_ERR_INVALID_ARGUMENT,
-                        "parallel_form needs last_layer_only = 1 and rule TTT_UPD_GD (frozen W1, W3; no norm, no Muon)");
+                        "parallel_form needs last_layer_only = 1 and rule TTT_UPD_GD or TTT_UPD_MUON (frozen W1, W3; "
+                        "no weight norm)");
+        if (D->rule == TTT_UPD_MUON && D->inner_steps > 1)
+            return fail(TTT_ERR_UNSUPPORTED, "parallel_form with TTT_UPD_MUON takes one gradient step per chunk");
         const int64_t S = (int64_t)D->B * D->H, nc = D->N > 0 ? cdiv(D->N, D->chunk) : 0;
         if (D->mask == TTT_MASK_STRIDED && nc > 32 * 32)
             return fail(TTT_ERR_UNSUPPORTED, "parallel_form with MASK_STRIDED supports at most 1024 chunks");

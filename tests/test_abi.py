@@ -101,7 +101,9 @@ def ws_bytes(D):
     # the parallel form needs frozen W1, W3 and plain GD
     (dict(parallel_form=1, rule=C.UPD_GD), C.TTT_ERR_INVALID_ARGUMENT),
     (dict(parallel_form=1, last_layer_only=1), C.TTT_ERR_INVALID_ARGUMENT),
-    (dict(parallel_form=1, last_layer_only=1, rule=C.UPD_MUON), C.TTT_ERR_INVALID_ARGUMENT),
+    (dict(parallel_form=1, last_layer_only=1, rule=C.UPD_MUON_L2), C.TTT_ERR_INVALID_ARGUMENT),
+    # Variant 2 with Muon has a parallel form, with one gradient step per chunk
+    (dict(parallel_form=1, last_layer_only=1, rule=C.UPD_MUON, inner_steps=2), C.TTT_ERR_UNSUPPORTED),
     (dict(parallel_form=1, last_layer_only=1, rule=C.UPD_GD, mask=C.MASK_STRIDED, N=1025 * 64,
           update_chunks=ctypes.cast((ctypes.c_uint8 * 1025)(), ctypes.c_void_p)), C.TTT_ERR_UNSUPPORTED),
 ])
@@ -131,6 +133,10 @@ def test_workspace_sizes():
     assert par >= 2 * 2 * 4 * 256 * 128 * 2 + 8 * 4 * 64 * 128 * 8
     st, par0 = ws_bytes(desc(parallel_form=1, last_layer_only=1, rule=C.UPD_GD, N=0))
     assert st == C.TTT_OK and par0 < par
+    # with Muon it also holds every (scan, chunk) matrix's Newton-Schulz buffers: at least the fp32
+    # result and two bf16 iterate planes of d x m per chunk and scan
+    st, pm = ws_bytes(desc(parallel_form=1, last_layer_only=1, rule=C.UPD_MUON, momentum=0.9))
+    assert st == C.TTT_OK and pm >= par + 8 * 4 * (64 * 128) * (4 + 2 + 2)
 
 
 def call_forward(D, q=P16, k=P16, v=P16, eta=P16, W0=P16B, o=P16 + (1 << 30), W_out=None, M=None, ws=None, nws=0):

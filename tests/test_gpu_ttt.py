@@ -294,6 +294,49 @@ def test_parallel_form_last_layer(mask, mom, inner, ascent, flags, bf16):
               ascent=ascent, parallel=True)
 
 
+PARALLEL_MUON_CASES = [
+    # mask, momentum, ascent, strided flags, Newton-Schulz steps
+    (O.MASK_APPLY_THEN_UPDATE, 0.9, False, None, 5),
+    (O.MASK_APPLY_THEN_UPDATE, 0.0, False, None, 5),
+    (O.MASK_UPDATE_THEN_APPLY, 0.9, False, None, 3),
+    (O.MASK_UPDATE_THEN_APPLY, 0.0, True, None, 5),
+    (O.MASK_STRIDED, 0.9, False, [1, 0, 1, 1], 5),
+    (O.MASK_STRIDED, 0.0, True, [0, 1, 1, 0], 1),
+    (O.MASK_APPLY_THEN_UPDATE, 0.9, False, None, 0),
+]
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("mask,mom,ascent,flags,ns", PARALLEL_MUON_CASES)
+def test_parallel_form_muon_last_layer(mask, mom, ascent, flags, ns, bf16):
+    # Variant 2 (only W2 learns; momentum, per-token eta and Muon kept, no weight norm) in its parallel
+    # form -- momentum scanned over chunks, Newton-Schulz on every chunk's momentum at once, W2 as a
+    # prefix sum -- against the oracle's chunk recurrence; N = 308 leaves a ragged chunk of 20 tokens
+    run_small(60, 1, 2, 308, 64, 160, 96, mask, O.UPD_MUON, bf16, mom, last=True, flags=flags, ns=ns,
+              ascent=ascent, parallel=True)
+
+
+def test_parallel_form_muon_matches_recurrence():
+    # several feature tiles, 128-wide state tiles and Newton-Schulz step tiles per chunk: the parallel
+    # form with Muon against the library's own chunk recurrence, momentum carried in and out of M
+    B, H, N, d, m, chunk = 2, 2, 1100, 128, 384, 256
+    say(f"parallel Muon form vs recurrence B{B} H{H} N{N} d{d} m{m} b{chunk}")
+    (q, k, v, eta, W0), _ = full_ttt_inputs(61, B, H, N, d, m, True)
+    M0 = 0.01 * torch.randn((B, H, 3 * d * m), dtype=torch.float32, device="cuda")
+    Mr, Mp = M0.clone(), M0.clone()
+    kw = dict(m_h=m, momentum=0.9, last_layer_only=True)
+    o_r, W_r = T.ttt_forward(q, k, v, eta, W0, chunk, O.MASK_APPLY_THEN_UPDATE, O.UPD_MUON, M=Mr, **kw)
+    o_p, W_p = T.ttt_forward(q, k, v, eta, W0, chunk, O.MASK_APPLY_THEN_UPDATE, O.UPD_MUON, M=Mp,
+                             parallel_form=True, **kw)
+    torch.cuda.synchronize()
+    assert_close(host(o_p), host(o_r), 2e-2, "o (parallel vs recurrence)", chunk)
+    dm = d * m
+    for name, a, b in zip(("W2", "M2"), (W_p[..., 2 * dm:], Mp[..., 2 * dm:]), (W_r[..., 2 * dm:], Mr[..., 2 * dm:])):
+        assert_close(host(a).reshape(B, H, d, m), host(b).reshape(B, H, d, m), 2e-2, name)
+    assert torch.equal(W_p[..., :2 * dm], W0[None].expand(B, H, -1)[..., :2 * dm])
+    assert torch.equal(Mp[..., :2 * dm], M0[..., :2 * dm])
+
+
 def test_parallel_form_many_strided_chunks_fp32():
     # 40 chunks of 32 tokens: the strided update flags span two 32-bit words
     flags = [(j * 7) % 3 != 0 for j in range(40)]

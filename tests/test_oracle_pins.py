@@ -569,3 +569,49 @@ def test_forward_ref_per_batch_weights_and_momentum(rule, beta, mask):
     o1, W1s, _ = O.ttt_forward_ref(Q, K, V, E, *Ws, chunk, mask, rule, 5, beta, M=M, slices=[(1, 0)])
     assert rel(o1[1, 0], o[1, 0]) == 0.0 and rel(W1s[2][1, 0], W[2][1, 0]) == 0.0
     assert not o1[0].any() and not o1[1, 1].any() and not W1s[0][0].any()
+
+
+@pytest.mark.parametrize("mask,beta,upd", [(O.MASK_APPLY_THEN_UPDATE, 0.9, None), (O.MASK_UPDATE_THEN_APPLY, 0.0, None),
+                                           (O.MASK_STRIDED, 0.9, [1, 0, 1, 1])])
+def test_last_layer_muon_parallel_form(mask, beta, upd):
+    """Variant 2 of the paper's ablation (Sec. 6.1 Steps 1-2, Table 2): only W2 learns, Muon and
+    momentum stay, no weight norm.  The chunk gradient of W2 is -phi(K)^T (eta V) (App. E.2): it
+    depends on the frozen features and on v, never on W2, so the recurrence is a parallel prefix over
+    chunks (Sec. 6.2): every chunk's gradient up front, the momentum as a linear scan, Muon on each
+    chunk's momentum, W2 as W2_0 minus the prefix sum of those.  Built here from the finite-difference
+    gradient, a loop momentum and the SVD form of Newton-Schulz, it must equal the oracle's recurrence;
+    Muon applied to each chunk's outer product before the sum (App. E.3 read literally) must not,
+    because Muon is not additive."""
+    N, chunk = 12, 4
+    q, k, v, eta, W1, W3, W2 = tiny_problem(42, N=N)
+    o, W, _ = O.ttt_scan_ref(q, k, v, eta, W1, W3, W2, chunk, mask, O.UPD_MUON, 5, beta, True, upd)
+    nch = N // chunk
+    updates = [mask != O.MASK_STRIDED or upd[j] for j in range(nch)]
+    G = [fd_gradients(W1, W3, W2, k[j * chunk:(j + 1) * chunk], v[j * chunk:(j + 1) * chunk],
+                      eta[j * chunk:(j + 1) * chunk])[2] for j in range(nch)]
+    # the gradient does not depend on W2 (so the chunk gradients can all be taken up front)
+    G_other = fd_gradients(W1, W3, 3.0 * W2 + 1.0, k[:chunk], v[:chunk], eta[:chunk])[2]
+    assert rel(G_other, G[0]) < 1e-7
+    Mx, U = np.zeros_like(W2), []
+    for j in range(nch):
+        if updates[j]:
+            Mx = beta * Mx + G[j]
+            U.append(ns_via_svd(Mx, 5))
+        else:
+            U.append(np.zeros_like(W2))
+    PQ = phi_rows(W1, W3, q)
+    want = np.zeros_like(o)
+    for t in range(N):
+        j = t // chunk
+        seen = j + (1 if mask == O.MASK_UPDATE_THEN_APPLY else 0)   # chunks whose update t sees
+        W2_t = W2 - sum((U[i] for i in range(seen)), np.zeros_like(W2))
+        want[t] = W2_t @ PQ[t]
+    assert rel(o, want) < 1e-6
+    assert rel(W[2], W2 - sum(U, np.zeros_like(W2))) < 1e-6
+    # negative control: Muon of each chunk's own outer product, summed (E.3 taken literally)
+    lit = W2.copy()
+    for j in range(nch):
+        if updates[j]:
+            lit = lit - ns_via_svd(G[j], 5)
+    if beta:
+        assert rel(lit, W[2]) > 1e-3
