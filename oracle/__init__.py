@@ -1,9 +1,10 @@
-"""fp64 CPU oracle for the TTT-KVB layer and chunked linear attention.
+"""fp64 CPU oracle for the TTT-KVB layer, chunked linear attention and LaCT's sliding-window attention.
 
 TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the benchmark's CPU-baseline
 leg, never by the product path.  It imports nothing from the HIP library.
 """
 from .ttt_ref import *  # noqa: F401,F403
+from .swa_ref import swa_scan_ref, swa_forward_ref  # noqa: F401
 from .ttt_ref import (  # noqa: F401
     MASK_FULL, MASK_UPDATE_THEN_APPLY, MASK_APPLY_THEN_UPDATE, MASK_STRIDED, MASK_TOKEN_CAUSAL,
     UPD_GD, UPD_GD_L2, UPD_MUON_L2, UPD_MUON,
