@@ -305,6 +305,9 @@ def main():
         "k_lin_scan": ("hbm", 8 * dm * S * nchunks),
         # W1 | W3 of the H weight blocks read in fp32 and written in bf16
         "k_w13_cvt": ("hbm", (4 + es) * 2 * dm * H),
+        # sliding-window attention: 4d FLOP per (query, key) pair inside the windows (algorithmic)
+        "k_swa": ("mfma", 4 * d * B * H * (chunk * (chunk + 1) // 2 + (N - chunk) * chunk)),
+        "k_swa_qprep": ("hbm", 2 * 2 * B * H * N * d),
         # parallel form with Muon: every chunk's W2 update read and its momentum written (fp32)
         "k_par_momentum": ("hbm", 8 * dm * S * nchunks),
     }
@@ -486,6 +489,27 @@ def main():
                                                               last_layer_only=True, parallel_form=pf, out=o,
                                                               workspace=wsv), st, 1)
             del wsv, Mv
+        # LaCT's sliding-window attention beside the layer: window = chunk, on the headline q, k, v
+        print("[bench] extras: sliding-window attention", file=sys.stderr, flush=True)
+        Dw = C.SwaDesc(B, H, N, d, chunk, C.TTT_BF16)
+        wsw = torch.empty(T.swa_workspace_bytes(Dw), dtype=torch.uint8, device="cuda")
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(4000 + args.seed)
+        qs_ = 0.5 + torch.rand((H, d), generator=gen, device="cuda")
+        qb_ = 0.3 * torch.randn((H, d), generator=gen, device="cuda")
+        ks_ = 0.5 + torch.rand((H, d), generator=gen, device="cuda")
+        msw = time_calls(torch, lambda: T.swa_forward(q, k, v, chunk, q_scale=qs_, q_shift=qb_, k_scale=ks_, out=o,
+                                                      workspace=wsw), st, 1)
+        pairs = B * H * (chunk * (chunk + 1) // 2 + (N - chunk) * chunk)  # (query, key) pairs in windows
+        fsw = 4 * d * pairs  # q'' . k and p v: 2d each per pair
+        extras["sliding_window_attention"] = {
+            "workload": f"B{B} H{H} N{N} d{d}, causal window {chunk} (= the chunk), bf16, per-channel scale/shift",
+            "ms_per_call": round(msw, 3), "tokens_per_s": round(tokens / (msw * 1e-3)),
+            "algorithmic_tflop": round(fsw / 1e12, 3),
+            "mfma_frac": round(fsw / (msw * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "note": "d = 384 runs as two 192-column workgroups per query block, each computing the scores: "
+                    "1.5x the algorithmic FLOPs are executed"}
+        del wsw
         extras["lact_lm_variant2_muon"] = {
             "workload": f"B{B} H{H} N{N} d{d} m{m} chunk {chunk} bf16, apply-then-update, only W2 learns, "
                         "momentum 0.9 + Muon (5 steps), no weight norm",

@@ -200,6 +200,35 @@ ttt_status linattn_forward(const linattn_desc* desc, const void* q, const void* 
 
 
 /*
+ * LaCT's sliding-window attention, the local branch beside the TTT layer (PaperTrace "5.2.1 LaCT and
+ * TTT-E2E", section 1.1, the window-attention paragraphs, and the remark after Eq. (10)): causal
+ * softmax attention over a window as wide as the chunk, on the same q, k, v as the fast-weight
+ * branch, with a per-channel scale and shift on q and k.  Per (batch, head), token t attends to the
+ * tokens s with t - window < s <= t:
+ *     o_t = sum_s softmax_s(q'_t . k'_s / sqrt(d)) v_s,  q' = q * q_scale + q_shift,
+ *                                                        k' = k * k_scale + k_shift (per channel).
+ *   q, k, v, o  [B][H][N][d] of io_dtype, 16-byte aligned; d a multiple of 32, at most 384
+ *   q_scale, q_shift, k_scale, k_shift   [H][d] fp32 per-head, per-channel parameters, 16-byte
+ *               aligned; NULL means scale 1 or shift 0.  k_shift adds the same amount to every score
+ *               of a query, which softmax removes: it does not change o and is not read.
+ *   workspace   device buffer of at least swa_workspace_bytes(desc) bytes (it holds q * q_scale +
+ *               q_shift, times k_scale), 256-byte aligned; it must not overlap q, k, v or o
+ * Scores, the softmax and the output accumulation are fp32; in bf16 mode the softmax weights are
+ * rounded to bf16 before they multiply v.
+ */
+typedef struct swa_desc {
+    int32_t B, H, N, d;
+    int32_t window;           /* >= 1 tokens, the query included                                 */
+    int32_t io_dtype;         /* ttt_dtype of q, k, v, o                                        */
+} swa_desc;
+
+ttt_status swa_workspace_bytes(const swa_desc* desc, size_t* bytes);
+ttt_status swa_forward(const swa_desc* desc, const void* q, const void* k, const void* v,
+                       const float* q_scale, const float* q_shift, const float* k_scale,
+                       const float* k_shift, void* o, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/*
  * Optional per-kernel timing for measurement tools (not needed for normal use).  While enabled,
  * every kernel launch this library makes is bracketed by two HIP events recorded on the stream
  * it is launched on.  ttt_profile_read waits for the recorded events, writes for each kernel
@@ -207,7 +236,7 @@ ttt_status linattn_forward(const linattn_desc* desc, const void* q, const void* 
  * read, and forgets them.  Kernel classes are numbered 0 .. TTT_PROF_KERNELS-1 and named by
  * ttt_profile_kernel_name.  Enabling or reading while another thread launches is allowed.
  */
-#define TTT_PROF_KERNELS 15
+#define TTT_PROF_KERNELS 17
 ttt_status ttt_profile_enable(int32_t on);
 /* Restricts the bracketing to the kernel classes i whose bit (1u << i) is set in mask; the
  * default is every class.  Each bracket records two events on the launch's stream, which costs

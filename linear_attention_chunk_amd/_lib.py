@@ -21,10 +21,11 @@ EXPORTS = (
     "ttt_abi_version", "ttt_status_string", "ttt_last_error",
     "ttt_workspace_bytes", "ttt_forward", "ttt_forward_noalloc",
     "linattn_workspace_bytes", "linattn_forward",
+    "swa_workspace_bytes", "swa_forward",
     "ttt_profile_enable", "ttt_profile_select", "ttt_profile_read", "ttt_profile_kernel_name",
     "ttt_probe_mfma_bf16",
 )
-PROF_KERNELS = 15
+PROF_KERNELS = 17
 NOALLOC_SCRATCH_BYTES = 64 << 20   # TTT_NOALLOC_SCRATCH_BYTES of include/ttt.h
 
 
@@ -45,6 +46,11 @@ class LinattnDesc(ctypes.Structure):
         ("d_k", c_int32), ("d_v", c_int32), ("chunk", c_int32),
         ("io_dtype", c_int32), ("mask", c_int32), ("update_chunks", c_void_p),
     ]
+
+
+class SwaDesc(ctypes.Structure):
+    _fields_ = [("B", c_int32), ("H", c_int32), ("N", c_int32), ("d", c_int32), ("window", c_int32),
+                ("io_dtype", c_int32)]
 
 
 class TttError(RuntimeError):
@@ -83,6 +89,11 @@ def lib() -> ctypes.CDLL:
     L.linattn_forward.restype = c_int32
     L.linattn_forward.argtypes = [POINTER(LinattnDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                   c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+    L.swa_workspace_bytes.restype = c_int32
+    L.swa_workspace_bytes.argtypes = [POINTER(SwaDesc), POINTER(c_size_t)]
+    L.swa_forward.restype = c_int32
+    L.swa_forward.argtypes = [POINTER(SwaDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                              c_void_p, c_void_p, c_size_t, c_void_p]
     L.ttt_profile_enable.restype = c_int32
     L.ttt_profile_enable.argtypes = [c_int32]
     L.ttt_profile_select.restype = c_int32

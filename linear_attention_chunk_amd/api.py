@@ -225,3 +225,40 @@ def linattn_forward(q, k, v, eta, chunk: int, mask_mode: int = C.MASK_APPLY_THEN
     del keep
     C.check(st)
     return o, S_out
+
+
+def swa_workspace_bytes(desc: C.SwaDesc) -> int:
+    n = ctypes.c_size_t(0)
+    C.check(C.lib().swa_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def swa_forward(q, k, v, window: int, *, q_scale: Optional[torch.Tensor] = None, q_shift: Optional[torch.Tensor] = None,
+                k_scale: Optional[torch.Tensor] = None, k_shift: Optional[torch.Tensor] = None,
+                out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None):
+    """LaCT's causal sliding-window attention through swa_forward of libttt.so: q, k, v [B, H, N, d]
+    (bf16 or fp32); the per-head, per-channel scale / shift parameters are [H, d] fp32 or None.
+    Returns o [B, H, N, d]."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q must be a [B, H, N, d] tensor")
+    B, H, N, d = q.shape
+    dev = q.device
+    if q.dtype not in _DT:
+        raise ValueError(f"unsupported io dtype {q.dtype}")
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype, dev, q.shape)
+    for t, n in ((q_scale, "q_scale"), (q_shift, "q_shift"), (k_scale, "k_scale"), (k_shift, "k_shift")):
+        if t is not None:
+            _need(t, n, torch.float32, dev, (H, d))
+    if out is not None:
+        _need(out, "out", q.dtype, dev, q.shape)
+    if window < 1:
+        raise ValueError("window must be >= 1")
+    D = C.SwaDesc(B, H, N, d, int(window), _DT[q.dtype])
+    workspace = _workspace(workspace, swa_workspace_bytes(D), dev)
+    o = torch.empty_like(q) if out is None else out
+    st = C.lib().swa_forward(ctypes.byref(D), _ptr(q), _ptr(k), _ptr(v), _ptr(q_scale), _ptr(q_shift), _ptr(k_scale),
+                             _ptr(k_shift), _ptr(o), _ptr(workspace),
+                             ctypes.c_size_t(0 if workspace is None else workspace.numel()), _stream_handle(stream))
+    C.check(st)
+    return o

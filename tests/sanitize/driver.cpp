@@ -165,6 +165,29 @@ int main() {
                         run_lin(D);
                     }
     }
+    // sliding-window attention: valid and invalid descriptors, every call stopping at the buffer check
+    {
+        const int ds[] = {-32, 0, 31, 32, 96, 128, 192, 256, 320, 384, 416}, ws[] = {-1, 0, 1, 7, 2048, 1 << 30};
+        const int Ns[] = {-1, 0, 1, 127, 128, 129, 1000}, ios[] = {-1, 0, 1, 2};
+        for (int it = 0; it < 4000; ++it) {
+            swa_desc D;
+            memset(&D, 0, sizeof D);
+            D.B = (int)(next_u64() % 4) - 1; D.H = (int)(next_u64() % 4); D.N = pick(Ns, 7); D.d = pick(ds, 11);
+            D.window = pick(ws, 6); D.io_dtype = pick(ios, 4);
+            size_t need = 0;
+            ttt_status s = swa_workspace_bytes(&D, &need);
+            check_message(s);
+            ttt_status f = swa_forward(&D, (const void*)P, (const void*)(P + (1ull << 36)), (const void*)(P + (2ull << 36)),
+                                       (const float*)(P + (3ull << 36)), nullptr, (const float*)(P + (4ull << 36)), nullptr,
+                                       (void*)(P + (5ull << 36)), (void*)(P + (8ull << 36)), need, nullptr);
+            check_message(f);
+            if (s == TTT_OK && (int64_t)D.B * D.H > 0 && D.N > 0) EXPECT(f == TTT_ERR_DEVICE || f == TTT_ERR_INVALID_ARGUMENT);
+            if (s == TTT_OK && (int64_t)D.B * D.H > 0 && D.N > 0)
+                EXPECT(swa_forward(&D, (const void*)P, (const void*)P, (const void*)P, nullptr, nullptr, nullptr, nullptr,
+                                   (void*)(P + (5ull << 36)), (void*)(P + (8ull << 36)), need - 1, nullptr) == TTT_ERR_WORKSPACE);
+        }
+        EXPECT(swa_workspace_bytes(nullptr, nullptr) == TTT_ERR_INVALID_ARGUMENT);
+    }
     // seeded fuzz: each field from a list of valid values and out-of-range ones
     {
         const int Bs[] = {-1, 0, 1, 2, 3, 8}, Hs[] = {0, 1, 4, 16}, Ns[] = {-5, 0, 1, 63, 64, 300, 2049, 65536};

@@ -20,7 +20,7 @@ P16B = 0x7F0100000000
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ttt_\w+|linattn_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(ttt_\w+|linattn_\w+|swa_\w+)\s*\(", text)))
 
 
 def test_header_declares_the_exports():
@@ -265,3 +265,44 @@ def test_valid_calls_without_a_device_report_device_error():
     # the status table answers for any non-negative value
     assert L.ttt_status_string(C.TTT_ERR_DEVICE) == b"HIP device or launch error"
     assert L.ttt_status_string(0x7FFFFFFF) == b"unknown status"
+
+
+
+def swa_desc(**kw):
+    base = dict(B=2, H=4, N=1000, d=384, window=256, io_dtype=C.TTT_BF16)
+    base.update(kw)
+    return C.SwaDesc(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=48), C.TTT_ERR_INVALID_ARGUMENT), (dict(d=416), C.TTT_ERR_INVALID_ARGUMENT),
+    (dict(window=0), C.TTT_ERR_INVALID_ARGUMENT), (dict(N=-1), C.TTT_ERR_INVALID_ARGUMENT),
+    (dict(io_dtype=3), C.TTT_ERR_INVALID_ARGUMENT), (dict(), C.TTT_OK), (dict(d=32, window=1), C.TTT_OK),
+])
+def test_swa_validation_and_workspace(kw, status):
+    L = C.lib()
+    n = ctypes.c_size_t(0)
+    D = swa_desc(**kw)
+    assert L.swa_workspace_bytes(ctypes.byref(D), ctypes.byref(n)) == status
+    if status == C.TTT_OK:
+        assert n.value == D.B * D.H * D.N * D.d * 2   # the transformed queries, in the io dtype
+
+
+def test_swa_forward_rejects_before_enqueueing():
+    L = C.lib()
+    D = swa_desc()
+    n = ctypes.c_size_t(0)
+    L.swa_workspace_bytes(ctypes.byref(D), ctypes.byref(n))
+    args = (P16, P16 + (1 << 30), P16 + (2 << 30))
+    assert L.swa_forward(ctypes.byref(D), None, *args[1:], None, None, None, None, P16B, P16 + (1 << 34), n.value,
+                         None) == C.TTT_ERR_INVALID_ARGUMENT
+    assert L.swa_forward(ctypes.byref(D), *args, None, None, None, None, P16B, None, 0, None) == C.TTT_ERR_WORKSPACE
+    assert L.swa_forward(ctypes.byref(D), *args, None, None, None, None, P16B, P16 + (1 << 34), n.value - 1,
+                         None) == C.TTT_ERR_WORKSPACE
+    assert L.swa_forward(ctypes.byref(D), *args, None, None, None, None, P16 + 64, P16 + (1 << 34), n.value,
+                         None) == C.TTT_ERR_INVALID_ARGUMENT   # o overlaps q
+    assert L.swa_forward(ctypes.byref(D), *args, P16 + 4, None, None, None, P16B, P16 + (1 << 34), n.value,
+                         None) == C.TTT_ERR_INVALID_ARGUMENT   # misaligned scale vector
+    # nothing to do: no pointer is touched
+    assert L.swa_forward(ctypes.byref(swa_desc(N=0)), None, None, None, None, None, None, None, None, None, 0,
+                         None) == C.TTT_OK

@@ -14,7 +14,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "linear_attention_chunk_amd", "csrc")
-SOURCES = ["errors.hip", "profile.hip", "ttt_layer.hip", "linattn.hip"]
+SOURCES = ["errors.hip", "profile.hip", "ttt_layer.hip", "linattn.hip", "swa.hip"]
 
 
 def _hipcc():
