@@ -24,6 +24,10 @@ Training"):
                                                                    "Causal Linear Attention"
 * several inner-loop gradient steps per chunk (inference time) ... TTT-as-LA, Sec. 4.1
 * gradient ascent in the inner loop: the step's sign flips ....... TTT-as-LA, Sec. 4.2 and 5.2
+* per-chunk rates outside the optimizer step: momentum dW_j = g_j + alpha_j dW_{j-1} over the
+  chunk gradient g_j (unit token weights), W <- W - eta_j Opt(dW_j) .. TTT-as-LA, App. E.1 (per token)
+                                                                   and App. H.1-H.2 (per chunk),
+                                                                   App. E.3 (with Muon)
 
 Readings taken where the pages are silent or garbled (each is also listed in the design notes):
 
@@ -41,7 +45,11 @@ Readings taken where the pages are silent or garbled (each is also listed in the
 * a partial last chunk (N not a multiple of the chunk) simply holds fewer tokens;
 * n inner steps on a chunk repeat the whole update n times, each from the gradient at the current
   W (momentum and Muon included, one momentum step per inner step); ascent adds the gradient
-  instead of subtracting it, everything else unchanged.
+  instead of subtracting it, everything else unchanged;
+* per-chunk rates (App. E.1 written per chunk as in H.1): eta_j and alpha_j belong to each (batch,
+  head) and chunk; the chunk gradient weighs every token by 1; the momentum step is taken on every
+  updating chunk (alpha_j = 0 restarts it from g_j); Muon, when the rule has it, acts on dW_j before
+  eta_j scales it; the weight norm, when the rule has it, follows W - eta_j Opt(dW_j).
 
 Parity status: every function here is pinned by the CPU tests (finite differences, closed forms
 of the linear and last-layer reductions, the SVD polar factor, invariants).  The full SwiGLU
@@ -137,28 +145,38 @@ def chunk_bounds(N, chunk):
     return [(lo, min(lo + chunk, N)) for lo in range(0, N, chunk)]
 
 
-def _weight_update(W, G, Mx, rule, ns_iters, momentum):
-    """One fast-weight update of one matrix: optional momentum, optional Muon, W - U, optional norm."""
+def _weight_update(W, G, Mx, rule, ns_iters, momentum, lr=None, alpha=None):
+    """One fast-weight update of one matrix: optional momentum, optional Muon, W - U, optional norm.
+    With per-chunk rates (lr is not None): the momentum step dW = G + alpha dW is always taken when
+    alpha is given (alpha None: dW = G), and the step is W - lr Opt(dW)."""
     U = G
-    if momentum != 0.0:
+    if lr is not None:
+        if alpha is not None:
+            Mx = alpha * Mx + G
+            U = Mx
+    elif momentum != 0.0:
         Mx = momentum * Mx + G
         U = Mx
     if rule in (UPD_MUON_L2, UPD_MUON):
         U = newton_schulz(U, ns_iters)
-    W = W - U
+    W = W - (U if lr is None else lr * U)
     if rule in (UPD_GD_L2, UPD_MUON_L2):
         W = l2_normalize_rows(W)
     return W, Mx
 
 
 def ttt_scan_ref(q, k, v, eta, W1, W3, W2, chunk, mask, rule, ns_iters=5, momentum=0.0,
-                 last_layer_only=False, update_chunks=None, M=None, inner_steps=1, ascent=False):
+                 last_layer_only=False, update_chunks=None, M=None, inner_steps=1, ascent=False,
+                 chunk_rates=False, chunk_alpha=None):
     """One (batch, head) scan of the TTT-KVB layer.
 
     q, k, v [N, d]; eta [N]; W1, W3 [m, d]; W2 [d, m]; M optional (M1, M3, M2) momentum state.
     Returns (o [N, d], (W1, W3, W2), (M1, M3, M2)).  The apply/update order per chunk follows
     LaCT notes section 1.1 and Eq. (10).  An updating chunk takes ``inner_steps`` gradient steps
     (TTT-as-LA Sec. 4.1); ``ascent`` steps along +g instead of -g (TTT-as-LA Sec. 4.2).
+    chunk_rates: eta is [number of chunks], one rate per chunk applied outside the optimizer step,
+    the chunk gradient weighs its tokens by 1, and chunk_alpha ([number of chunks] or None) holds
+    the per-chunk momentum factors (TTT-as-LA App. E.1, H.1-H.2, E.3); ``momentum`` is then unused.
     """
     q, k, v, eta = _f64(q), _f64(k), _f64(v), _f64(eta)
     W = [_f64(W1).copy(), _f64(W3).copy(), _f64(W2).copy()]
@@ -182,12 +200,17 @@ def ttt_scan_ref(q, k, v, eta, W1, W3, W2, chunk, mask, rule, ns_iters=5, moment
             o[lo:hi] = swiglu_apply(W[0], W[1], W[2], q[lo:hi])
         if update:
             for _ in range(inner_steps):
-                G = chunk_gradients(W[0], W[1], W[2], k[lo:hi], v[lo:hi], eta[lo:hi])
+                w_tok = np.ones(hi - lo) if chunk_rates else eta[lo:hi]
+                G = chunk_gradients(W[0], W[1], W[2], k[lo:hi], v[lo:hi], w_tok)
                 if ascent:
                     G = tuple(-g for g in G)
                 which = (2,) if last_layer_only else (0, 1, 2)
                 for i in which:
-                    W[i], Ms[i] = _weight_update(W[i], G[i], Ms[i], rule, ns_iters, momentum)
+                    if chunk_rates:
+                        a_j = None if chunk_alpha is None else float(chunk_alpha[j])
+                        W[i], Ms[i] = _weight_update(W[i], G[i], Ms[i], rule, ns_iters, 0.0, float(eta[j]), a_j)
+                    else:
+                        W[i], Ms[i] = _weight_update(W[i], G[i], Ms[i], rule, ns_iters, momentum)
         if not apply_first:
             o[lo:hi] = swiglu_apply(W[0], W[1], W[2], q[lo:hi])
     return o, tuple(W), tuple(Ms)
@@ -195,13 +218,14 @@ def ttt_scan_ref(q, k, v, eta, W1, W3, W2, chunk, mask, rule, ns_iters=5, moment
 
 def ttt_forward_ref(q, k, v, eta, W1, W3, W2, chunk, mask, rule, ns_iters=5, momentum=0.0,
                     last_layer_only=False, update_chunks=None, M=None, slices=None, inner_steps=1,
-                    ascent=False):
+                    ascent=False, chunk_rates=False, chunk_alpha=None):
     """The TTT-KVB layer over [B, H, N, d] inputs; every (batch, head) scan is independent.
 
     W1, W3, W2 are per head ([H, ...]) or per (batch, head) ([B, H, ...]).  M, if given, is a
     tuple of three [B, H, ...] momentum arrays.  ``slices`` restricts the work to a list of
     (b, h) pairs (the other outputs stay zero).  Returns (o, (W1, W3, W2), (M1, M3, M2)) with
-    [B, H, ...] weight and momentum stacks.
+    [B, H, ...] weight and momentum stacks.  With chunk_rates, eta and chunk_alpha are
+    [B, H, number of chunks].
     """
     B, H, N, d = q.shape
     m = W1.shape[-2]
@@ -214,7 +238,7 @@ def ttt_forward_ref(q, k, v, eta, W1, W3, W2, chunk, mask, rule, ns_iters=5, mom
         Mi = None if M is None else tuple(x[b, h] for x in M)
         ob, Wb, Mb = ttt_scan_ref(q[b, h], k[b, h], v[b, h], eta[b, h], *ws, chunk, mask, rule,
                                   ns_iters, momentum, last_layer_only, update_chunks, Mi, inner_steps,
-                                  ascent)
+                                  ascent, chunk_rates, None if chunk_alpha is None else chunk_alpha[b, h])
         o[b, h] = ob
         for i in range(3):
             Wo[i][b, h] = Wb[i]

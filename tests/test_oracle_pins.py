@@ -615,3 +615,103 @@ def test_last_layer_muon_parallel_form(mask, beta, upd):
             lit = lit - ns_via_svd(G[j], 5)
     if beta:
         assert rel(lit, W[2]) > 1e-3
+
+
+# ----------------------------------------------------------------------------------------------
+# per-chunk rates outside the optimizer step (TTT-as-LA App. E.1, written per chunk in App. H)
+
+def stepper_chunk_rates(q, k, v, lr, alpha, W1, W3, W2, chunk, mask, rule, last_only=False, upd=None, ns=5):
+    """The chunk recurrence of App. H.2 (with Muon per App. E.3) from independent pieces: finite-
+    difference gradients with every token weighted 1, the momentum step dW = g + alpha_j dW, the SVD
+    form of Newton-Schulz, W - lr_j Opt(dW), loop row norms."""
+    W = [W1.copy(), W3.copy(), W2.copy()]
+    M = [np.zeros_like(x) for x in W]
+    N = q.shape[0]
+    o = np.zeros((N, W2.shape[0]))
+    for j, lo in enumerate(range(0, N, chunk)):
+        hi = min(lo + chunk, N)
+        first = mask in (O.MASK_APPLY_THEN_UPDATE, O.MASK_STRIDED)
+        if first:
+            o[lo:hi] = np.stack([f_token(*W, x) for x in q[lo:hi]])
+        if mask != O.MASK_STRIDED or upd[j]:
+            G = fd_gradients(*W, k[lo:hi], v[lo:hi], np.ones(hi - lo))
+            for i in ([2] if last_only else [0, 1, 2]):
+                M[i] = G[i] if alpha is None else alpha[j] * M[i] + G[i]
+                U = ns_via_svd(M[i], ns) if rule in (O.UPD_MUON_L2, O.UPD_MUON) else M[i]
+                W[i] = W[i] - lr[j] * U
+                if rule in (O.UPD_GD_L2, O.UPD_MUON_L2):
+                    W[i] = rownorm_loops(W[i])
+        if not first:
+            o[lo:hi] = np.stack([f_token(*W, x) for x in q[lo:hi]])
+    return o, W, M
+
+
+@pytest.mark.parametrize("mask,rule,with_alpha,last_only", [
+    (O.MASK_APPLY_THEN_UPDATE, O.UPD_GD_L2, True, False), (O.MASK_UPDATE_THEN_APPLY, O.UPD_MUON_L2, True, False),
+    (O.MASK_STRIDED, O.UPD_MUON, True, True), (O.MASK_APPLY_THEN_UPDATE, O.UPD_GD, False, False),
+])
+def test_chunk_rates_match_independent_stepper(mask, rule, with_alpha, last_only):
+    q, k, v, _, W1, W3, W2 = tiny_problem(50, N=9)
+    rng = np.random.default_rng(51)
+    lr = 0.1 + 0.3 * rng.random(3)
+    alpha = np.array([0.7, 0.0, 0.9]) if with_alpha else None   # alpha_j = 0 restarts the momentum
+    upd = [1, 0, 1] if mask == O.MASK_STRIDED else None
+    o, W, M = O.ttt_scan_ref(q, k, v, lr, W1, W3, W2, 3, mask, rule, 5, 0.0, last_only, upd, chunk_rates=True,
+                             chunk_alpha=alpha)
+    o2, W2s, M2 = stepper_chunk_rates(q, k, v, lr, alpha, W1, W3, W2, 3, mask, rule, last_only, upd)
+    assert rel(o, o2) < 1e-6
+    for a, b in zip(W, W2s):
+        assert rel(a, b) < 1e-6
+
+
+@pytest.mark.parametrize("mask", [O.MASK_UPDATE_THEN_APPLY, O.MASK_APPLY_THEN_UPDATE])
+def test_chunk_rates_parallel_form_mask_c(mask):
+    """App. H.1: with only the last layer learning by GD, per-chunk rates eta_j and momentum alpha_j,
+    O = Phi(Q) W_0 + sum over chunks i <= t of C_ti Phi(Q_t) Phi(K_i)^T V_i with
+    C_ti = sum_{j=i..t} eta_j prod_{s=i+1..j} alpha_s (update-then-apply: chunk t sees its own update;
+    apply-then-update: the mask shifted by one chunk)."""
+    N, chunk = 12, 3
+    q, k, v, _, W1, W3, W2 = tiny_problem(52, N=N)
+    rng = np.random.default_rng(53)
+    nch = N // chunk
+    lr = 0.1 + rng.random(nch)
+    alpha = 0.2 + 0.7 * rng.random(nch)
+    o, W, _ = O.ttt_scan_ref(q, k, v, lr, W1, W3, W2, chunk, mask, O.UPD_GD, 5, 0.0, True, chunk_rates=True,
+                             chunk_alpha=alpha)
+    PQ, PK = phi_rows(W1, W3, q), phi_rows(W1, W3, k)
+
+    def C(t, i):
+        return sum(lr[j] * np.prod([alpha[s] for s in range(i + 1, j + 1)]) for j in range(i, t + 1))
+
+    want = PQ @ W2.T
+    for p in range(N):
+        t = p // chunk - (1 if mask == O.MASK_APPLY_THEN_UPDATE else 0)
+        for s in range(N):
+            i = s // chunk
+            if i <= t:
+                want[p] += C(t, i) * np.dot(PQ[p], PK[s]) * v[s]
+    assert rel(o, want) < 1e-12
+
+
+def test_chunk_rates_equal_token_rates_for_gd_at_constant_rates_but_not_for_muon():
+    """With GD (and the weight norm), a constant per-chunk rate c and momentum beta equal the
+    per-token form with every eta_i = c and momentum beta: c G inside the momentum or c outside it
+    give the same step.  With Muon they differ: Newton-Schulz removes the scale of its input, so the
+    per-token rates only weigh tokens against each other while eta_j outside sets the step size."""
+    q, k, v, _, W1, W3, W2 = tiny_problem(54, N=8)
+    c, beta = 0.37, 0.8
+    for rule in (O.UPD_GD, O.UPD_GD_L2):
+        a = O.ttt_scan_ref(q, k, v, np.full(8, c), W1, W3, W2, 4, O.MASK_APPLY_THEN_UPDATE, rule, 5, beta)
+        b = O.ttt_scan_ref(q, k, v, np.full(2, c), W1, W3, W2, 4, O.MASK_APPLY_THEN_UPDATE, rule, 5, 0.0,
+                           chunk_rates=True, chunk_alpha=np.full(2, beta))
+        assert rel(a[0], b[0]) < 1e-12
+    a = O.ttt_scan_ref(q, k, v, np.full(8, c), W1, W3, W2, 4, O.MASK_APPLY_THEN_UPDATE, O.UPD_MUON, 5, beta)
+    b = O.ttt_scan_ref(q, k, v, np.full(2, c), W1, W3, W2, 4, O.MASK_APPLY_THEN_UPDATE, O.UPD_MUON, 5, 0.0,
+                       chunk_rates=True, chunk_alpha=np.full(2, beta))
+    assert rel(a[1][2], b[1][2]) > 1e-2
+    # the per-chunk Muon step is eta_j times a scale-free update: doubling eta doubles W - W0
+    b2 = O.ttt_scan_ref(q, k, v, np.full(2, 2 * c), W1, W3, W2, 8, O.MASK_APPLY_THEN_UPDATE, O.UPD_MUON, 5, 0.0,
+                        True, chunk_rates=True)
+    b1 = O.ttt_scan_ref(q, k, v, np.full(2, c), W1, W3, W2, 8, O.MASK_APPLY_THEN_UPDATE, O.UPD_MUON, 5, 0.0,
+                        True, chunk_rates=True)
+    assert rel(b2[1][2] - W2, 2 * (b1[1][2] - W2)) < 1e-12
