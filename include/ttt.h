@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define TTT_ABI_VERSION 2
+#define TTT_ABI_VERSION 3
 
 typedef enum {
     TTT_OK = 0,
@@ -114,6 +114,18 @@ typedef struct ttt_desc {
                                  gradient step per chunk (inner_steps > 1: UNSUPPORTED).  Same
                                  results as 0 (the chunk recurrence) up to rounding.  Other rules:
                                  INVALID_ARGUMENT */
+    int32_t chunk_rates;      /* 1: per-chunk rates outside the optimizer step ("TTT with KV
+                                 Binding Is Secretly Linear Attention", App. E.1 written per chunk
+                                 as in App. H.1-H.2; App. E.3 with Muon).  eta is then
+                                 [B][H][ceil(N/chunk)] fp32, one rate eta_j per chunk; the chunk
+                                 gradient g_j weighs every token by 1; the momentum step is
+                                 dW <- g_j + alpha_j dW with alpha_j from chunk_momentum (NULL:
+                                 dW = g_j); the update is W <- [L2-Normalize](W - eta_j Opt(dW)),
+                                 Opt = Muon for the Muon rules, the identity otherwise.  momentum
+                                 must be 0 and parallel_form 0.  0: eta is per token, inside the
+                                 gradient sum (the notes' Eq. (2)).                             */
+    const float* chunk_momentum; /* device, [B][H][ceil(N/chunk)] fp32 alpha_j, 4-byte aligned;
+                                 NULL (no momentum) or used with chunk_rates = 1 only             */
 } ttt_desc;
 
 typedef struct linattn_desc {
@@ -141,7 +153,8 @@ ttt_status ttt_workspace_bytes(const ttt_desc* desc, size_t* bytes);
 /*
  * The TTT-KVB layer (notes Eqs. (2)-(6), (10); paper App. E).
  *   q, k, v   [B][H][N][d_h] of io_dtype, 16-byte aligned
- *   eta       [B][H][N] fp32 per-token learning rates (any sign; negative = gradient ascent)
+ *   eta       [B][H][N] fp32 per-token learning rates (any sign; negative = gradient ascent), or
+ *             with chunk_rates [B][H][ceil(N/chunk)] per-chunk rates
  *   W0        initial fast weights, fp32, [H] or [B][H] blocks of [W1 | W3 | W2], 16-byte aligned
  *   o         [B][H][N][d_h] of io_dtype, output
  *   W_out     nullable; [B][H][3*d_h*m_h] fp32 fast weights after the last chunk

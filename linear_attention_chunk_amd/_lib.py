@@ -37,6 +37,7 @@ class TttDesc(ctypes.Structure):
         ("ns_iters", c_int32), ("momentum", c_float), ("last_layer_only", c_int32),
         ("w0_per_batch", c_int32), ("update_chunks", c_void_p),
         ("inner_steps", c_int32), ("ascent", c_int32), ("parallel_form", c_int32),
+        ("chunk_rates", c_int32), ("chunk_momentum", c_void_p),
     ]
 
 

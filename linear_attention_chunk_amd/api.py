@@ -79,14 +79,15 @@ def unpack_weights(W: torch.Tensor, d: int, m: int):
 
 def ttt_desc(B, H, N, d_h, m_h, chunk, io_dtype, mask, rule, ns_iters=5, momentum=0.0, last_layer_only=False,
              w0_per_batch=False, update_chunks: Optional[Sequence[int]] = None, inner_steps: int = 1,
-             ascent: bool = False, parallel_form: bool = False):
+             ascent: bool = False, parallel_form: bool = False, chunk_rates: bool = False,
+             chunk_momentum: Optional[torch.Tensor] = None):
     """A filled TttDesc plus the host buffer that keeps update_chunks alive."""
     flags = None
     if update_chunks is not None:
         flags = (ctypes.c_uint8 * len(update_chunks))(*[1 if f else 0 for f in update_chunks])
     D = C.TttDesc(B, H, N, d_h, m_h, chunk, io_dtype, mask, rule, ns_iters, float(momentum), int(last_layer_only),
                   int(w0_per_batch), ctypes.cast(flags, ctypes.c_void_p) if flags is not None else None,
-                  int(inner_steps), int(ascent), int(parallel_form))
+                  int(inner_steps), int(ascent), int(parallel_form), int(chunk_rates), _ptr(chunk_momentum))
     return D, flags
 
 
@@ -97,7 +98,8 @@ def ttt_workspace_bytes(desc: C.TttDesc) -> int:
 
 
 def _ttt_prepare(q, k, v, eta, W0, chunk, mask_mode, update_rule, m_h, ns_iters, momentum, last_layer_only,
-                 update_chunks, M, want_W, out, inner_steps, ascent, parallel_form):
+                 update_chunks, M, want_W, out, inner_steps, ascent, parallel_form, chunk_rates=False,
+                 chunk_momentum=None):
     """Argument checks shared by ttt_forward and ttt_forward_noalloc; returns the descriptor, the
     host buffer keeping update_chunks alive, the output and W_out tensors."""
     if not isinstance(q, torch.Tensor) or q.dim() != 4:
@@ -108,15 +110,20 @@ def _ttt_prepare(q, k, v, eta, W0, chunk, mask_mode, update_rule, m_h, ns_iters,
         raise ValueError(f"unsupported io dtype {q.dtype}")
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n, q.dtype, dev, q.shape)
-    _need(eta, "eta", torch.float32, dev, (B, H, N))
+    if chunk < 1:
+        raise ValueError("chunk must be >= 1")
+    nc = -(-N // chunk)
+    _need(eta, "eta", torch.float32, dev, (B, H, nc) if chunk_rates else (B, H, N))
+    if chunk_momentum is not None:
+        if not chunk_rates:
+            raise ValueError("chunk_momentum needs chunk_rates")
+        _need(chunk_momentum, "chunk_momentum", torch.float32, dev, (B, H, nc))
     if not isinstance(W0, torch.Tensor) or W0.dim() not in (2, 3):
         raise ValueError("W0 must be [H, 3*d*m] or [B, H, 3*d*m]")
     per_batch = W0.dim() == 3
     if m_h is None:
         m_h = W0.shape[-1] // (3 * d)
     _need(W0, "W0", torch.float32, dev, ((B, H) if per_batch else (H,)) + (3 * d * m_h,))
-    if chunk < 1:
-        raise ValueError("chunk must be >= 1")
     _flags(update_chunks, N, chunk, mask_mode == C.MASK_STRIDED)
     wshape = (B, H, 3 * d * m_h)
     if out is not None:
@@ -124,7 +131,8 @@ def _ttt_prepare(q, k, v, eta, W0, chunk, mask_mode, update_rule, m_h, ns_iters,
     if M is not None:
         _need(M, "M", torch.float32, dev, wshape)
     D, keep = ttt_desc(B, H, N, d, m_h, chunk, _DT[q.dtype], mask_mode, update_rule, ns_iters, momentum,
-                       last_layer_only, per_batch, update_chunks, inner_steps, ascent, parallel_form)
+                       last_layer_only, per_batch, update_chunks, inner_steps, ascent, parallel_form, chunk_rates,
+                       chunk_momentum)
     o = torch.empty_like(q) if out is None else out
     W_out = torch.empty(wshape, dtype=torch.float32, device=dev) if want_W else None
     return D, keep, o, W_out
@@ -135,17 +143,20 @@ def ttt_forward(q, k, v, eta, W0, chunk: int, mask_mode: int = C.MASK_APPLY_THEN
                 momentum: float = 0.0, last_layer_only: bool = False, update_chunks=None,
                 M: Optional[torch.Tensor] = None, want_W: bool = True, out: Optional[torch.Tensor] = None,
                 workspace: Optional[torch.Tensor] = None, stream=None, inner_steps: int = 1,
-                ascent: bool = False, parallel_form: bool = False):
+                ascent: bool = False, parallel_form: bool = False, chunk_rates: bool = False,
+                chunk_momentum: Optional[torch.Tensor] = None):
     """The TTT-KVB layer through ttt_forward of libttt.so.
 
     q, k, v [B, H, N, d] (bf16 or fp32, same dtype); eta [B, H, N] fp32; W0 fp32 [H, 3*d*m] or
     [B, H, 3*d*m] (see pack_weights).  M, if given, is the [B, H, 3*d*m] fp32 momentum, updated
     in place.  parallel_form (last_layer_only with plain GD only) computes the same layer as
-    chunked linear attention over the frozen SwiGLU features.  Returns (o, W_out or None).
+    chunked linear attention over the frozen SwiGLU features.  chunk_rates: eta is [B, H, chunks], one
+    rate per chunk outside the optimizer step, with per-chunk momentum factors chunk_momentum
+    [B, H, chunks] (or None).  Returns (o, W_out or None).
     """
     D, keep, o, W_out = _ttt_prepare(q, k, v, eta, W0, chunk, mask_mode, update_rule, m_h, ns_iters, momentum,
                                      last_layer_only, update_chunks, M, want_W, out, inner_steps, ascent,
-                                     parallel_form)
+                                     parallel_form, chunk_rates, chunk_momentum)
     nbytes = ttt_workspace_bytes(D)
     workspace = _workspace(workspace, nbytes, q.device)
     st = C.lib().ttt_forward(ctypes.byref(D), _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(W0), _ptr(o), _ptr(W_out),
@@ -161,12 +172,14 @@ def ttt_forward_noalloc(q, k, v, eta, W0, chunk: int, mask_mode: int = C.MASK_AP
                         momentum: float = 0.0, last_layer_only: bool = False, update_chunks=None,
                         M: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                         W_out: Optional[torch.Tensor] = None, stream=None, inner_steps: int = 1,
-                        ascent: bool = False, parallel_form: bool = False):
+                        ascent: bool = False, parallel_form: bool = False, chunk_rates: bool = False,
+                        chunk_momentum: Optional[torch.Tensor] = None):
     """ttt_forward through ttt_forward_noalloc: the library's static device scratch replaces the
     workspace, and the library allocates nothing.  Pass `out` (and `W_out`, [B, H, 3*d*m] fp32, or
     None to skip the final weights) to keep this wrapper from allocating too.  Returns (o, W_out)."""
     D, keep, o, _ = _ttt_prepare(q, k, v, eta, W0, chunk, mask_mode, update_rule, m_h, ns_iters, momentum,
-                                 last_layer_only, update_chunks, M, False, out, inner_steps, ascent, parallel_form)
+                                 last_layer_only, update_chunks, M, False, out, inner_steps, ascent, parallel_form,
+                                 chunk_rates, chunk_momentum)
     if W_out is not None:
         _need(W_out, "W_out", torch.float32, q.device, (D.B, D.H, 3 * D.d_h * D.m_h))
     st = C.lib().ttt_forward_noalloc(ctypes.byref(D), _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(W0), _ptr(o),

@@ -129,7 +129,7 @@ __global__ __launch_bounds__(64 * kUpWaves, 1) void k_up(StepArgs<T> a) {
         tl.template run<PMG>(A1, B1, a.d, smem);
         if (f2) tp.template run_issued<PM1, true>(g2, A2, B2, a.d, smem);
         else tp.template run<PM1>(A2, B2, a.d, smem);
-        const float* eta = a.eta + tok;
+        const float* eta = a.eta ? a.eta + tok : nullptr;  // null: every token weighs 1
         // the tile's hidden units lie in one block (c0 % kHB is 0 or 128) and its tokens start a
         // token block (r0 % kTB == 0)
         static_assert(kHB % kUpCols == 0 && kUpKRows % kTB == 0, "key tiles must align with the blocks");
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(64 * kUpWaves, 1) void k_up(StepArgs<T> a) {
                 const int i = idx / (TK1::FN * 16), j = (idx / 16) % TK1::FN, r = idx % 16;
                 if (!decltype(check)::value || (r0 + col < a.lu && c0 + row < a.m)) {
                     float hk, da, dc;
-                    bwd(tl.acc[0][i][j][r], tl.acc[1][i][j][r], tp.acc[0][i][j][r], a.eta_sign * eta[col], hk, da, dc);
+                    bwd(tl.acc[0][i][j][r], tl.acc[1][i][j][r], tp.acc[0][i][j][r], a.eta_sign * (eta ? eta[col] : 1.0f), hk, da, dc);
                     const uint32_t off = (uint32_t)(col >> kTBShift) * kBlk + (uint32_t)row * kTB + (uint32_t)(col & (kTB - 1));
                     HkE[off] = Elt<T>::st(hk);
                     DA[off] = Elt<T>::st(da);
@@ -295,6 +295,8 @@ template <typename T> struct UpdArgs {
     float* dst; int64_t dst_stride;
     T* sh; int64_t sh_stride;
     int d, m, norm, last_only, shadows;
+    const float* u_scale;                 // per-chunk rates [scan][nchunk]: W - u_scale[s nchunk + jchunk] U,
+    int nchunk, jchunk;                   // or null: W - U
 };
 
 constexpr int kUpdRows = 16;
@@ -317,7 +319,7 @@ template <> struct Vec4<float> {
 // vector and drops the value, so no load waits behind a per-lane branch.  W2's rows are also written
 // to LDS so that W2^T can be stored 16 consecutive elements at a time.
 template <int NV, typename T>
-__device__ __forceinline__ void update_rows(const float* src, const float* U, float* dst, T* shm, T* tileT,
+__device__ __forceinline__ void update_rows(const float* src, const float* U, float us, float* dst, T* shm, T* tileT,
                                             int row0, int L, bool norm, bool to_lds, bool shadows) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int L4 = L / 4;
@@ -335,7 +337,9 @@ __device__ __forceinline__ void update_rows(const float* src, const float* U, fl
 #pragma unroll
             for (int i = 0; i < NV; ++i) uv[i] = u4[min(lane + 64 * i, L4 - 1)];
 #pragma unroll
-            for (int i = 0; i < NV; ++i) { x[i].x -= uv[i].x; x[i].y -= uv[i].y; x[i].z -= uv[i].z; x[i].w -= uv[i].w; }
+            for (int i = 0; i < NV; ++i) {
+                x[i].x -= us * uv[i].x; x[i].y -= us * uv[i].y; x[i].z -= us * uv[i].z; x[i].w -= us * uv[i].w;
+            }
         }
         float ss = 0.f;
 #pragma unroll
@@ -379,15 +383,16 @@ __global__ __launch_bounds__(kThreads) void k_update(UpdArgs<T> a) {
     float* dst = a.dst ? a.dst + s * a.dst_stride + moff : nullptr;
     T* shm = a.sh + s * a.sh_stride + moff;
     static_assert(kMaxDim <= 8 * 256, "update rows hold at most 8 float4 per lane");
+    const float us = a.u_scale ? a.u_scale[(int64_t)s * a.nchunk + a.jchunk] : 1.0f;
     switch ((L / 4 + 63) / 64) {  // uniform per workgroup
-        case 1: update_rows<1>(src, U, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows); break;
-        case 2: update_rows<2>(src, U, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows); break;
-        case 3: update_rows<3>(src, U, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows); break;
-        case 4: update_rows<4>(src, U, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows); break;
-        case 5: update_rows<5>(src, U, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows); break;
-        case 6: update_rows<6>(src, U, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows); break;
-        case 7: update_rows<7>(src, U, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows); break;
-        default: update_rows<8>(src, U, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows); break;
+        case 1: update_rows<1>(src, U, us, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows); break;
+        case 2: update_rows<2>(src, U, us, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows); break;
+        case 3: update_rows<3>(src, U, us, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows); break;
+        case 4: update_rows<4>(src, U, us, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows); break;
+        case 5: update_rows<5>(src, U, us, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows); break;
+        case 6: update_rows<6>(src, U, us, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows); break;
+        case 7: update_rows<7>(src, U, us, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows); break;
+        default: update_rows<8>(src, U, us, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows); break;
     }
     if (mat == 2 && a.shadows) {  // W2^T [m][d]: column c of this 16-row block is 16 consecutive elements
         __syncthreads();
@@ -443,6 +448,8 @@ template <typename T> struct PrepArgs {
     int64_t dm; int mat0, nmat;
     int mbase;                            // matrix index of a scan's first stored matrix (offsets are
                                           // (mat - mbase) d m): 0 for [W1 | W3 | W2], 2 for W2 alone
+    const float* beta_chunk;              // per-chunk momentum factors [scan][nchunk] (beta_chunk[s nchunk +
+    int nchunk, jchunk;                   // jchunk] replaces beta), or null
 };
 
 __device__ __forceinline__ float block_sum(float x, float* red) {
@@ -467,6 +474,7 @@ __global__ __launch_bounds__(kThreads) void k_muon_prep(PrepArgs<T> a) {
     T* Xh = a.Xhi ? a.Xhi + s * a.x_stride + mo : nullptr;
     T* Xl = a.Xhi ? a.Xlo + s * a.x_stride + mo : nullptr;
     float ss = 0.f;
+    const float beta = a.beta_chunk ? a.beta_chunk[(int64_t)s * a.nchunk + a.jchunk] : a.beta;
     const int64_t e0 = (int64_t)blk * kPrepElems;
     // all loads first (an index past the matrix reads its last element and is not used), then the
     // arithmetic and stores, so the loads are in flight together
@@ -492,7 +500,7 @@ __global__ __launch_bounds__(kThreads) void k_muon_prep(PrepArgs<T> a) {
             float u = g[j];
             if (Gs) Gs[e] = u;
             if (M) {
-                u = a.beta * mv[j] + u;
+                u = beta * mv[j] + u;
                 M[e] = u;
             }
             if constexpr (sizeof(T) == 2) {
@@ -1153,6 +1161,13 @@ static ttt_status validate(const ttt_desc* D) {
     if (D->ascent != 0 && D->ascent != 1) return fail(TTT_ERR_INVALID_ARGUMENT, "ascent must be 0/1");
     if (D->parallel_form != 0 && D->parallel_form != 1)
         return fail(TTT_ERR_INVALID_ARGUMENT, "parallel_form must be 0/1");
+    if (D->chunk_rates != 0 && D->chunk_rates != 1) return fail(TTT_ERR_INVALID_ARGUMENT, "chunk_rates must be 0/1");
+    if (D->chunk_rates && D->momentum != 0.0f)
+        return fail(TTT_ERR_INVALID_ARGUMENT, "with chunk_rates the momentum comes from chunk_momentum; momentum must be 0");
+    if (!D->chunk_rates && D->chunk_momentum)
+        return fail(TTT_ERR_INVALID_ARGUMENT, "chunk_momentum is read only with chunk_rates = 1");
+    if (D->chunk_rates && D->parallel_form)
+        return fail(TTT_ERR_UNSUPPORTED, "parallel_form takes per-token rates only");
     if (D->parallel_form) {
         if (!D->last_layer_only || (D->rule != TTT_UPD_GD && D->rule != TTT_UPD_MUON))
             return fail(TTT_ERR_INVALID_ARGUMENT,
@@ -1179,6 +1194,8 @@ static ttt_status validate(const ttt_desc* D) {
 }
 
 static bool is_muon(const ttt_desc& D) { return D.rule == TTT_UPD_MUON_L2 || D.rule == TTT_UPD_MUON; }
+// whether the update keeps a momentum: the chunk momentum beta, or per-chunk factors alpha_j
+static bool has_mom(const ttt_desc& D) { return D.chunk_rates ? D.chunk_momentum != nullptr : D.momentum != 0.0f; }
 
 template <typename T>
 static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const T* k, const T* v,
@@ -1187,7 +1204,8 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
     const int S = D.B * D.H, d = D.d_h, m = D.m_h;
     const int64_t dm = (int64_t)d * m;
     const bool muon = is_muon(D);
-    const bool mom = D.momentum != 0.0f;
+    const bool mom = has_mom(D);
+    const int nchunks = (int)cdiv(D.N, D.chunk);
     float* Wf[2] = {(float*)(ws + L.wf[0]), (float*)(ws + L.wf[1])};
     T* sh[2] = {(T*)(ws + L.sh[0]), (T*)(ws + L.sh[1])};
     float* G = (float*)(ws + L.g);
@@ -1231,7 +1249,7 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
         for (int it = 0; it < nin; ++it) {
             if (it > 0) ja = -1;
             StepArgs<T> a{};
-            a.q = q; a.k = k; a.v = v; a.eta = eta; a.o = o;
+            a.q = q; a.k = k; a.v = v; a.eta = D.chunk_rates ? nullptr : eta; a.o = o;
             a.N = D.N; a.d = d; a.m = m;
             a.Hq = (T*)(ws + L.hq); a.HkE = (T*)(ws + L.hke); a.DA = (T*)(ws + L.da); a.DC = (T*)(ws + L.dc);
             a.inter_stride = L.inter_stride;
@@ -1289,7 +1307,8 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
                 // Newton-Schulz, or zero steps)
                 const bool keep_g = a.ksplit > 1 && !mom && (sizeof(T) == 4 || D.ns_iters == 0);
                 PrepArgs<T> pa{G, L.g_stride, a.ksplit, a.gpart_stride, keep_g ? G : nullptr, M, 3 * dm, D.momentum, part,
-                               L.nblk, split ? Xb[1] : nullptr, split ? Xlo : nullptr, L.x_stride, dm, mat0, nmat};
+                               L.nblk, split ? Xb[1] : nullptr, split ? Xlo : nullptr, L.x_stride, dm, mat0, nmat, 0,
+                               D.chunk_rates ? D.chunk_momentum : nullptr, nchunks, ju};
                 {
                     ProfScope ps(PK_MUON_PREP, st);
                     hipLaunchKernelGGL(k_muon_prep<T>, dim3(S * nmat * L.nblk), dim3(kThreads), 0, st, pa);
@@ -1345,7 +1364,7 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
             const int norm = (D.rule == TTT_UPD_GD_L2 || D.rule == TTT_UPD_MUON_L2) ? 1 : 0;
             const bool final_upd = step == last_upd && it == nin - 1;
             UpdArgs<T> u{Wf[cur], L.wf_stride, 0, D.H, U, 3 * dm, Wf[cur ^ 1], L.wf_stride, sh[cur ^ 1], L.sh_stride,
-                         d, m, norm, D.last_layer_only, 1};
+                         d, m, norm, D.last_layer_only, 1, D.chunk_rates ? eta : nullptr, nchunks, ju};
             if (!w_in_master) {  // the first update reads W0 (per head or per scan)
                 u.src = W0;
                 u.src_stride = 3 * dm;
@@ -1377,7 +1396,7 @@ extern "C" ttt_status ttt_workspace_bytes(const ttt_desc* desc, size_t* bytes) {
     if (rc != TTT_OK) return rc;
     if (!bytes) return fail(TTT_ERR_INVALID_ARGUMENT, "bytes is NULL");
     *bytes = desc->parallel_form ? make_playout(*desc).total
-                                 : make_layout(*desc, is_muon(*desc), desc->momentum != 0.0f).total;
+                                 : make_layout(*desc, is_muon(*desc), has_mom(*desc)).total;
     return TTT_OK;
 }
 
@@ -1403,8 +1422,9 @@ static ttt_status forward_impl(const ttt_desc* desc, const void* q, const void* 
     for (const void* p : p16)
         if (p && !aligned(p, 16)) return fail(TTT_ERR_INVALID_ARGUMENT, "q, k, v, o, W0, W_out, M must be 16-byte aligned");
     if (eta && !aligned(eta, 4)) return fail(TTT_ERR_INVALID_ARGUMENT, "eta must be 4-byte aligned");
+    const size_t eta_bytes = (size_t)S * (D.chunk_rates ? cdiv(D.N, D.chunk) : D.N) * 4;
     if (overlaps(o, io_bytes, q, io_bytes) || overlaps(o, io_bytes, k, io_bytes) || overlaps(o, io_bytes, v, io_bytes) ||
-        overlaps(o, io_bytes, eta, (size_t)S * D.N * 4))
+        overlaps(o, io_bytes, eta, eta_bytes))
         return fail(TTT_ERR_INVALID_ARGUMENT, "o overlaps an input");
     if (overlaps(W_out, w_bytes, W0, w0_bytes)) return fail(TTT_ERR_INVALID_ARGUMENT, "W_out overlaps W0");
     hipStream_t st = (hipStream_t)stream;
@@ -1412,8 +1432,9 @@ static ttt_status forward_impl(const ttt_desc* desc, const void* q, const void* 
     auto buffers = [&](size_t ws_need) -> ttt_status {
         const size_t eb = D.N > 0 ? io_bytes : 0;
         const struct { const void* p; size_t n; const char* name; } bufs[] = {
-            {q, eb, "q"}, {k, eb, "k"}, {v, eb, "v"}, {o, eb, "o"}, {eta, D.N > 0 ? (size_t)S * D.N * 4 : 0, "eta"},
-            {W0, w0_bytes, "W0"}, {W_out, w_bytes, "W_out"}, {M_inout, D.momentum != 0.0f ? w_bytes : 0, "M_inout"},
+            {q, eb, "q"}, {k, eb, "k"}, {v, eb, "v"}, {o, eb, "o"}, {eta, D.N > 0 ? eta_bytes : 0, "eta"},
+            {D.chunk_rates ? D.chunk_momentum : nullptr, D.N > 0 ? (size_t)S * cdiv(D.N, D.chunk) * 4 : 0, "chunk_momentum"},
+            {W0, w0_bytes, "W0"}, {W_out, w_bytes, "W_out"}, {M_inout, has_mom(D) ? w_bytes : 0, "M_inout"},
             {scratch ? nullptr : workspace, ws_need, "workspace"}};
         for (const auto& b : bufs) {
             const ttt_status r = check_buffer(b.p, b.n, b.name);
@@ -1434,7 +1455,7 @@ static ttt_status forward_impl(const ttt_desc* desc, const void* q, const void* 
         return run_parallel_form<float>(D, PL, (const float*)q, (const float*)k, (const float*)v, eta, W0, (float*)o,
                                         W_out, M_inout, (char*)workspace, st);
     }
-    const Layout L = make_layout(D, is_muon(D), D.momentum != 0.0f && !M_inout);
+    const Layout L = make_layout(D, is_muon(D), has_mom(D) && !M_inout);
     if (L.total > 0 && (!workspace || workspace_bytes < L.total))
         return fail(TTT_ERR_WORKSPACE, scratch ? "the call needs %zu bytes of scratch, the library's array holds %zu"
                                                : "workspace needs %zu bytes, got %zu", L.total, workspace_bytes);

@@ -205,6 +205,8 @@ int main() {
             D.last_layer_only = pick(bits, 4); D.w0_per_batch = pick(bits, 4);
             D.update_chunks = (next_u64() & 7) ? flags : nullptr;
             D.inner_steps = pick(inner, 6); D.ascent = pick(bits, 4); D.parallel_form = pick(bits, 4);
+            D.chunk_rates = pick(bits, 4);
+            D.chunk_momentum = (next_u64() & 1) ? (const float*)(P + (9ull << 36)) : nullptr;
             // flags cover at most 4096 chunks: keep strided fuzz cases within them
             if (D.mask == TTT_MASK_STRIDED && D.chunk > 0 && D.N > 0 && (D.N + (int64_t)D.chunk - 1) / D.chunk > 4096)
                 D.chunk = D.N;

@@ -39,7 +39,7 @@ def test_library_loads_and_exports_every_symbol():
 
 def test_version_and_status_strings():
     L = C.lib()
-    assert L.ttt_abi_version() == 2
+    assert L.ttt_abi_version() == 3
     for s in range(5):
         assert L.ttt_status_string(s)
     assert L.ttt_status_string(99) == b"unknown status"
@@ -104,6 +104,11 @@ def ws_bytes(D):
     (dict(parallel_form=1, last_layer_only=1, rule=C.UPD_MUON_L2), C.TTT_ERR_INVALID_ARGUMENT),
     # Variant 2 with Muon has a parallel form, with one gradient step per chunk
     (dict(parallel_form=1, last_layer_only=1, rule=C.UPD_MUON, inner_steps=2), C.TTT_ERR_UNSUPPORTED),
+    # per-chunk rates: the momentum comes from chunk_momentum, not from momentum; no parallel form
+    (dict(chunk_rates=2), C.TTT_ERR_INVALID_ARGUMENT),
+    (dict(chunk_rates=1, momentum=0.9), C.TTT_ERR_INVALID_ARGUMENT),
+    (dict(chunk_momentum=P16), C.TTT_ERR_INVALID_ARGUMENT),
+    (dict(chunk_rates=1, parallel_form=1, last_layer_only=1, rule=C.UPD_GD), C.TTT_ERR_UNSUPPORTED),
     (dict(parallel_form=1, last_layer_only=1, rule=C.UPD_GD, mask=C.MASK_STRIDED, N=1025 * 64,
           update_chunks=ctypes.cast((ctypes.c_uint8 * 1025)(), ctypes.c_void_p)), C.TTT_ERR_UNSUPPORTED),
 ])

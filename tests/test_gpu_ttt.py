@@ -249,6 +249,39 @@ def test_host_and_short_buffers_are_refused_before_enqueueing():
                       M=torch.zeros((B, H, 3 * d * m - 4), device="cuda"))
 
 
+CHUNK_RATE_CASES = [
+    # mask, rule, per-chunk momentum, last layer only
+    (O.MASK_APPLY_THEN_UPDATE, O.UPD_GD_L2, True, False),
+    (O.MASK_UPDATE_THEN_APPLY, O.UPD_MUON_L2, True, False),
+    (O.MASK_STRIDED, O.UPD_MUON, True, True),
+    (O.MASK_APPLY_THEN_UPDATE, O.UPD_GD, False, False),
+]
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("mask,rule,with_alpha,last", CHUNK_RATE_CASES)
+def test_chunk_rates(mask, rule, with_alpha, last, bf16):
+    """Per-chunk rates eta_j outside the optimizer step and per-chunk momentum factors alpha_j (the
+    paper's App. E.1 in App. H's chunk form; E.3 with Muon) against the oracle; N = 308 leaves a
+    ragged chunk, one alpha_j is 0 (the momentum restarts there)."""
+    B, H, N, d, m, chunk = 1, 2, 308, 64, 160, 96
+    nc = -(-N // chunk)
+    say(f"chunk rates B{B} H{H} N{N} d{d} m{m} b{chunk} mask{mask} rule{rule} alpha{with_alpha} last{last} bf16={bf16}")
+    (q, k, v, _, W0), (hq, hk, hv, _, W1, W3, W2) = full_ttt_inputs(70, B, H, N, d, m, bf16)
+    rng = np.random.default_rng(71)
+    lr = (0.05 + 0.25 * rng.random((B, H, nc))).astype(np.float32)
+    alpha = (0.9 * rng.random((B, H, nc))).astype(np.float32) if with_alpha else None
+    if alpha is not None:
+        alpha[0, 1, 2] = 0.0
+    flags = [1, 0, 1, 1] if mask == O.MASK_STRIDED else None
+    o, Wout = T.ttt_forward(q, k, v, dev(lr), W0, chunk, mask, rule, m_h=m, last_layer_only=last, update_chunks=flags,
+                            chunk_rates=True, chunk_momentum=None if alpha is None else dev(alpha))
+    torch.cuda.synchronize()
+    o_ref, W_ref, _ = O.ttt_forward_ref(hq, hk, hv, lr, W1, W3, W2, chunk, mask, rule, 5, 0.0, last, flags,
+                                        chunk_rates=True, chunk_alpha=alpha)
+    check(o, Wout, o_ref, W_ref, d, m, TOL[bf16], chunk, label="per-chunk rates")
+
+
 def test_ascent_is_descent_with_negated_eta():
     """The pages reduce gradient ascent to a sign flip of the step: the library's ascent must give
     the bits that descent gives with -eta."""
