@@ -23,6 +23,8 @@ Training"):
                                                                    Sec. 6.1 Step 6; LA-to-TTT,
                                                                    "Causal Linear Attention"
 * several inner-loop gradient steps per chunk (inference time) ... TTT-as-LA, Sec. 4.1
+* the backward of the linear reduction (outer-loop gradients) ..... TTT-as-LA, Sec. 6.2 and Fig. 4
+                                                                   (training with the parallel form)
 * gradient ascent in the inner loop: the step's sign flips ....... TTT-as-LA, Sec. 4.2 and 5.2
 * per-chunk rates outside the optimizer step: momentum dW_j = g_j + alpha_j dW_{j-1} over the
   chunk gradient g_j (unit token weights), W <- W - eta_j Opt(dW_j) .. TTT-as-LA, App. E.1 (per token)
@@ -293,3 +295,71 @@ def linattn_forward_ref(q, k, v, eta, chunk, mask, S0=None, update_chunks=None, 
 def gemm_intensity(h, b):
     """LaCT notes Eq. (1): FLOP per byte of an h x h bf16 weight times a b x h chunk."""
     return (2.0 * h * h * b) / (2.0 * h * h + 4.0 * h * b)
+
+
+def linattn_backward_scan_ref(q, k, v, eta, S0, chunk, mask, dO, dS_out=None, update_chunks=None):
+    """Gradients of one (batch, head) scan of chunked linear attention (linattn_scan_ref) under the
+    chunked masks, for the loss L = sum_t dO_t . o_t + <dS_out, S_out>.
+
+    Written from the forward's structure: chunk c's queries see the state S_c (S0 plus the updates
+    of the chunks before it, or up to it under update-then-apply and the one-chunk FULL mask), so
+    dq_t = S_c^T dO_t and D_c = sum_{t in c} dO_t q_t^T is the gradient of S_c.  The update of
+    chunk j, dS_j = sum_s eta_s v_s k_s^T, reaches every S_c that includes it and S_out, so its
+    gradient is R_j = sum of those D_c plus dS_out, and dv_s = eta_s R_j k_s, dk_s = eta_s R_j^T v_s,
+    deta_s = v_s . (R_j k_s); chunks that do not update give zero.  dS0 = sum_c D_c + dS_out.
+    Returns (dq, dk, dv, deta, dS0).
+    """
+    q, k, v, eta, dO = (_f64(x) for x in (q, k, v, eta, dO))
+    if mask == MASK_TOKEN_CAUSAL:
+        raise ValueError("the backward covers the chunked masks")
+    S = _f64(S0).copy()
+    N = q.shape[0]
+    bounds = chunk_bounds(N, chunk)
+    if mask == MASK_FULL and len(bounds) > 1:
+        raise ValueError("MASK_FULL needs chunk >= N")
+    post = mask in (MASK_UPDATE_THEN_APPLY, MASK_FULL)
+    upd = [mask != MASK_STRIDED or bool(update_chunks[j]) for j in range(len(bounds))]
+    # forward states each chunk's queries see
+    Sc = []
+    for j, (lo, hi) in enumerate(bounds):
+        dS = (eta[lo:hi, None] * v[lo:hi]).T @ k[lo:hi] if upd[j] else 0.0
+        if post:
+            S = S + dS
+        Sc.append(S.copy())
+        if not post:
+            S = S + dS
+    dq = np.zeros_like(q)
+    D = []
+    for j, (lo, hi) in enumerate(bounds):
+        dq[lo:hi] = dO[lo:hi] @ Sc[j]
+        D.append(dO[lo:hi].T @ q[lo:hi])
+    dSo = np.zeros_like(Sc[0]) if dS_out is None else _f64(dS_out)
+    dk, dv, deta = np.zeros_like(k), np.zeros_like(v), np.zeros_like(eta)
+    for j, (lo, hi) in enumerate(bounds):
+        if not upd[j]:
+            continue
+        seen_by = range(j, len(bounds)) if post else range(j + 1, len(bounds))
+        R = dSo + sum((D[c] for c in seen_by), np.zeros_like(dSo))
+        u = k[lo:hi] @ R.T                       # R_j k_s, one row per token
+        dv[lo:hi] = eta[lo:hi, None] * u
+        dk[lo:hi] = eta[lo:hi, None] * (v[lo:hi] @ R)
+        deta[lo:hi] = np.sum(v[lo:hi] * u, axis=1)
+    dS0 = dSo + sum(D, np.zeros_like(dSo))
+    return dq, dk, dv, deta, dS0
+
+
+def linattn_backward_ref(q, k, v, eta, chunk, mask, dO, S0=None, dS_out=None, update_chunks=None, slices=None):
+    """linattn_backward_scan_ref over [B, H, N, d] inputs; S0 and dS_out are [B, H, d_v, d_k] or None."""
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    out = [np.zeros((B, H, N, dk)), np.zeros((B, H, N, dk)), np.zeros((B, H, N, dv)), np.zeros((B, H, N)),
+           np.zeros((B, H, dv, dk))]
+    todo = [(b, h) for b in range(B) for h in range(H)] if slices is None else list(slices)
+    for b, h in todo:
+        s0 = np.zeros((dv, dk)) if S0 is None else S0[b, h]
+        dso = None if dS_out is None else dS_out[b, h]
+        res = linattn_backward_scan_ref(q[b, h], k[b, h], v[b, h], eta[b, h], s0, chunk, mask, dO[b, h], dso,
+                                        update_chunks)
+        for o_, r in zip(out, res):
+            o_[b, h] = r
+    return tuple(out)
