@@ -333,7 +333,7 @@ def linattn_backward_scan_ref(q, k, v, eta, S0, chunk, mask, dO, dS_out=None, up
     for j, (lo, hi) in enumerate(bounds):
         dq[lo:hi] = dO[lo:hi] @ Sc[j]
         D.append(dO[lo:hi].T @ q[lo:hi])
-    dSo = np.zeros_like(Sc[0]) if dS_out is None else _f64(dS_out)
+    dSo = np.zeros_like(S) if dS_out is None else _f64(dS_out)   # (no tokens: S_out = S0)
     dk, dv, deta = np.zeros_like(k), np.zeros_like(v), np.zeros_like(eta)
     for j, (lo, hi) in enumerate(bounds):
         if not upd[j]:

@@ -101,3 +101,17 @@ def test_backward_batched_wrapper_and_defaults():
     r1 = O.linattn_backward_ref(q, k, v, eta, 4, O.MASK_APPLY_THEN_UPDATE, dO, np.zeros_like(S0), np.zeros_like(dSo))
     for a, bb in zip(r0, r1):
         assert rel(a, bb) == 0.0
+
+
+def test_backward_empty_sequence():
+    # no tokens: S_out = S0, so dS0 = dS_out (zero without it) and every token gradient is empty
+    rng = np.random.default_rng(81)
+    q, k = np.zeros((2, 0, 3))
+    v = dO = np.zeros((0, 4))
+    eta = np.zeros(0)
+    S0, dSo = rng.standard_normal((2, 4, 3))
+    for mask in (O.MASK_APPLY_THEN_UPDATE, O.MASK_UPDATE_THEN_APPLY):
+        dq, dk, dv, de, dS0 = O.linattn_backward_scan_ref(q, k, v, eta, S0, 5, mask, dO, dSo)
+        assert dq.shape == (0, 3) and dk.shape == (0, 3) and dv.shape == (0, 4) and de.shape == (0,)
+        assert np.array_equal(dS0, dSo)
+        assert np.array_equal(O.linattn_backward_scan_ref(q, k, v, eta, S0, 5, mask, dO)[4], np.zeros((4, 3)))
