@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define TTT_ABI_VERSION 3
+#define TTT_ABI_VERSION 4
 
 typedef enum {
     TTT_OK = 0,
@@ -211,6 +211,38 @@ ttt_status linattn_forward(const linattn_desc* desc, const void* q, const void* 
                            const float* eta, const float* S0, void* o, float* S_out,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Device workspace that linattn_backward needs, in bytes: the update, the state and the state
+ * gradient of every chunk and scan (12 bytes per state element per chunk), plus B*H*N*4 bytes per
+ * 128 columns of d_v when d_v > 128; zero when N is 0.
+ */
+ttt_status linattn_backward_workspace_bytes(const linattn_desc* desc, size_t* bytes);
+
+/*
+ * Backward of linattn_forward under the chunked masks (FULL, UPDATE_THEN_APPLY, APPLY_THEN_UPDATE,
+ * STRIDED): the gradients that training through the parallel form needs (paper Sec. 6.2, Fig. 4),
+ * for the loss L = sum over tokens of dO . o + <dS_out, S_out>.  With S_c the state chunk c's queries
+ * see and R_j the sum of dS_out and of sum_{t in c} dO_t q_t^T over the chunks c whose S_c holds
+ * chunk j's update:  dq_t = S_c^T dO_t,  dv_s = eta_s R_j k_s,  dk_s = eta_s R_j^T v_s,
+ * deta_s = v_s . (R_j k_s),  dS0 = dS_out + sum over all chunks of sum_t dO_t q_t^T.  Chunks a
+ * strided mask does not update get zero dk, dv and deta.  TOKEN_CAUSAL is TTT_ERR_UNSUPPORTED.
+ *   q, k, v, eta, S0  as for linattn_forward (the forward's inputs; S0 nullable = zeros)
+ *   dO        [B][H][N][d_v] of io_dtype: the gradient of o
+ *   dS_out    nullable; [B][H][d_v][d_k] fp32 gradient of S_out (NULL = zeros)
+ *   dq, dk    [B][H][N][d_k] of io_dtype; dv [B][H][N][d_v] of io_dtype; deta [B][H][N] fp32
+ *   dS0       nullable; [B][H][d_v][d_k] fp32 gradient of S0 (not written if NULL)
+ *   workspace device buffer of at least linattn_backward_workspace_bytes(desc) bytes, 256-byte
+ *             aligned (may be NULL when that is 0); TTT_ERR_WORKSPACE if it is too small
+ * Pointer alignment: q, k, v, dO, dq, dk, dv 16 bytes; the fp32 buffers 4 bytes.  No output may
+ * overlap an input or another output (TTT_ERR_INVALID_ARGUMENT).  The gradients are computed as
+ * the forward computes o: bf16 products with fp32 accumulation, the chunk states and state
+ * gradients held as bf16 hi + lo pairs (fp32 in fp32 mode).
+ */
+ttt_status linattn_backward(const linattn_desc* desc, const void* q, const void* k, const void* v,
+                            const float* eta, const float* S0, const void* dO, const float* dS_out,
+                            void* dq, void* dk, void* dv, float* deta, float* dS0,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 
 /*
  * LaCT's sliding-window attention, the local branch beside the TTT layer (PaperTrace "5.2.1 LaCT and
@@ -249,7 +281,7 @@ ttt_status swa_forward(const swa_desc* desc, const void* q, const void* k, const
  * read, and forgets them.  Kernel classes are numbered 0 .. TTT_PROF_KERNELS-1 and named by
  * ttt_profile_kernel_name.  Enabling or reading while another thread launches is allowed.
  */
-#define TTT_PROF_KERNELS 17
+#define TTT_PROF_KERNELS 20
 ttt_status ttt_profile_enable(int32_t on);
 /* Restricts the bracketing to the kernel classes i whose bit (1u << i) is set in mask; the
  * default is every class.  Each bracket records two events on the launch's stream, which costs

@@ -20,12 +20,12 @@ UPD_GD, UPD_GD_L2, UPD_MUON_L2, UPD_MUON = range(4)
 EXPORTS = (
     "ttt_abi_version", "ttt_status_string", "ttt_last_error",
     "ttt_workspace_bytes", "ttt_forward", "ttt_forward_noalloc",
-    "linattn_workspace_bytes", "linattn_forward",
+    "linattn_workspace_bytes", "linattn_forward", "linattn_backward_workspace_bytes", "linattn_backward",
     "swa_workspace_bytes", "swa_forward",
     "ttt_profile_enable", "ttt_profile_select", "ttt_profile_read", "ttt_profile_kernel_name",
     "ttt_probe_mfma_bf16",
 )
-PROF_KERNELS = 17
+PROF_KERNELS = 20
 NOALLOC_SCRATCH_BYTES = 64 << 20   # TTT_NOALLOC_SCRATCH_BYTES of include/ttt.h
 
 
@@ -90,6 +90,10 @@ def lib() -> ctypes.CDLL:
     L.linattn_forward.restype = c_int32
     L.linattn_forward.argtypes = [POINTER(LinattnDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                   c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+    L.linattn_backward_workspace_bytes.restype = c_int32
+    L.linattn_backward_workspace_bytes.argtypes = [POINTER(LinattnDesc), POINTER(c_size_t)]
+    L.linattn_backward.restype = c_int32
+    L.linattn_backward.argtypes = [POINTER(LinattnDesc)] + [c_void_p] * 13 + [c_size_t, c_void_p]
     L.swa_workspace_bytes.restype = c_int32
     L.swa_workspace_bytes.argtypes = [POINTER(SwaDesc), POINTER(c_size_t)]
     L.swa_forward.restype = c_int32

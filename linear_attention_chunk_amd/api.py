@@ -240,6 +240,55 @@ def linattn_forward(q, k, v, eta, chunk: int, mask_mode: int = C.MASK_APPLY_THEN
     return o, S_out
 
 
+def linattn_backward_workspace_bytes(desc: C.LinattnDesc) -> int:
+    n = ctypes.c_size_t(0)
+    C.check(C.lib().linattn_backward_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def linattn_backward(q, k, v, eta, dO, chunk: int, mask_mode: int = C.MASK_APPLY_THEN_UPDATE, *,
+                     S0: Optional[torch.Tensor] = None, dS_out: Optional[torch.Tensor] = None, update_chunks=None,
+                     want_dS0: bool = True, workspace: Optional[torch.Tensor] = None, stream=None):
+    """Backward of linattn_forward under a chunked mask through linattn_backward of libttt.so, for the
+    output gradient dO [B, H, N, d_v] and the final-state gradient dS_out ([B, H, d_v, d_k] fp32 or
+    None).  Returns (dq, dk, dv, deta, dS0 or None)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (dO, "dO")):
+        if not isinstance(t, torch.Tensor) or t.dim() != 4:
+            raise ValueError(f"{n} must be a 4-D [B, H, N, d] tensor")
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if q.dtype not in _DT:
+        raise ValueError(f"unsupported io dtype {q.dtype}")
+    _need(q, "q", None, dev)
+    _need(k, "k", q.dtype, dev, q.shape)
+    _need(v, "v", q.dtype, dev, (B, H, N, dv))
+    _need(dO, "dO", q.dtype, dev, (B, H, N, dv))
+    _need(eta, "eta", torch.float32, dev, (B, H, N))
+    if S0 is not None:
+        _need(S0, "S0", torch.float32, dev, (B, H, dv, dk))
+    if dS_out is not None:
+        _need(dS_out, "dS_out", torch.float32, dev, (B, H, dv, dk))
+    if chunk < 1:
+        raise ValueError("chunk must be >= 1")
+    _flags(update_chunks, N, chunk, mask_mode == C.MASK_STRIDED)
+    D, keep = linattn_desc(B, H, N, dk, dv, chunk, _DT[q.dtype], mask_mode, update_chunks)
+    nbytes = linattn_backward_workspace_bytes(D)
+    workspace = _workspace(workspace, nbytes, dev)
+    dq = torch.empty_like(q)
+    dkt = torch.empty_like(k)
+    dvt = torch.empty_like(v)
+    deta = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dS0 = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev) if want_dS0 else None
+    st = C.lib().linattn_backward(ctypes.byref(D), _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(S0), _ptr(dO),
+                                  _ptr(dS_out), _ptr(dq), _ptr(dkt), _ptr(dvt), _ptr(deta), _ptr(dS0), _ptr(workspace),
+                                  ctypes.c_size_t(0 if workspace is None else workspace.numel()),
+                                  _stream_handle(stream))
+    del keep
+    C.check(st)
+    return dq, dkt, dvt, deta, dS0
+
+
 def swa_workspace_bytes(desc: C.SwaDesc) -> int:
     n = ctypes.c_size_t(0)
     C.check(C.lib().swa_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)))

@@ -403,7 +403,8 @@ __global__ __launch_bounds__(kThreads) void k_linattn(LinArgs<T> a) {
 
 // dS_c = sum over chunk c's tokens of eta_i v_i k_i^T (d_v x d_k, fp32), contracting over tokens:
 // both operands are token-major, so both go through the transposing stager, which also applies
-// eta to v.  Chunks a strided mask does not update are skipped (and never read).
+// eta to v (without SCALE the weights are 1 and eta is not read: the backward's sum of dO q^T).
+// Chunks a strided mask does not update are skipped (and never read).
 template <typename T> struct DeltaArgs {
     const T* k; const T* v; const float* eta; float* dS;
     int64_t N; int dk, dv, chunk, nc, ntv, ntk, mode;
@@ -412,9 +413,9 @@ template <typename T> struct DeltaArgs {
 
 constexpr int kDeltaRows = 128, kDeltaCols = 128;
 
-template <typename T>
+template <typename T, bool SCALE = true>
 __global__ __launch_bounds__(kThreads, 2) void k_lin_delta(DeltaArgs<T> a) {
-    using TD = Tile<T, kDeltaRows, kDeltaCols, 2, 2, 1, 1, 1, true, true, true>;
+    using TD = Tile<T, kDeltaRows, kDeltaCols, 2, 2, 1, 1, 1, true, true, SCALE>;
     __shared__ __attribute__((aligned(16))) char smem[TD::LDS];
     const int lb = xcd_block(gridDim.x);
     const int per = a.ntv * a.ntk;
@@ -425,7 +426,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_lin_delta(DeltaArgs<T> a) {
     const int64_t tok = (int64_t)scan * a.N + (int64_t)c * a.chunk;
     const int nl = (int)std::min<int64_t>(a.chunk, a.N - (int64_t)c * a.chunk);
     Opnd<T> A[1] = {{a.v + tok * a.dv + r0, a.dv, a.dv - r0, nl}};
-    A[0].kscale = a.eta + tok;
+    if constexpr (SCALE) A[0].kscale = a.eta + tok;
     const Opnd<T> B[1] = {{a.k + tok * a.dk + c0, a.dk, a.dk - c0, nl}};
     TD tl;
     tl.template run<PM1>(A, B, nl, smem);
@@ -449,12 +450,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_lin_delta(DeltaArgs<T> a) {
 // update (apply-then-update, strided) or after it (update-then-apply, full).  One thread owns 4
 // consecutive elements of one scan's state and walks the chunks.  bf16 io keeps the state as a
 // hi + lo pair of bf16 planes (about 16 bits), fp32 io as one fp32 plane.  The entry/exit strides,
-// the momentum term, the repeats and the sign are those of LinStateIO.
+// the momentum term, the repeats and the sign are those of LinStateIO.  With rev the chunks are
+// walked from the last to the first (the backward's suffix sums of the chunks' query gradients:
+// there "before its own update" means without the chunk's own term).
 template <typename T> struct ScanArgs {
     const float* dS; T* Sc;
     LinStateIO io;
     int64_t dvk;   // d_v * d_k
-    int nc, mode, nscan;
+    int nc, mode, nscan, rev;
     uint32_t flags[32];
 };
 
@@ -488,7 +491,8 @@ __global__ __launch_bounds__(kThreads) void k_lin_scan(ScanArgs<T> a) {
             Pack4<T>::store(dst, st[0], st[1], st[2], st[3]);
         }
     };
-    for (int c = 0; c < a.nc; ++c) {
+    for (int i = 0; i < a.nc; ++i) {
+        const int c = a.rev ? a.nc - 1 - i : i;
         const bool upd = a.mode != TTT_MASK_STRIDED || ((a.flags[c >> 5] >> (c & 31)) & 1u);
         if (!post) put(c);
         if (upd) {
@@ -746,6 +750,56 @@ static size_t lin_ws_bytes(const linattn_desc& D) {
     return lin_chunked_ws_bytes((int64_t)D.B * D.H, cdiv(D.N, lin_block(D)), D.d_k, D.d_v);
 }
 
+// Launch of the delta kernel over every (scan, chunk) of D's sequence: dS_c = sum over the chunk of
+// w_i v_i k_i^T with w = eta (SCALE) or 1; a strided mode skips the chunks flags do not set.
+template <typename T, bool SCALE>
+static ttt_status launch_delta(const linattn_desc& D, int64_t chunk, int64_t nc, int mode, const uint32_t (&flags)[32],
+                               const T* k, const T* v, const float* eta, float* dS, hipStream_t st) {
+    DeltaArgs<T> da{};
+    da.k = k;
+    da.v = v;
+    da.eta = eta;
+    da.dS = dS;
+    da.N = D.N;
+    da.dk = D.d_k;
+    da.dv = D.d_v;
+    da.chunk = (int)chunk;
+    da.nc = (int)nc;
+    da.ntv = (int)cdiv(D.d_v, kDeltaRows);
+    da.ntk = (int)cdiv(D.d_k, kDeltaCols);
+    da.mode = mode;
+    for (int w = 0; w < 32; ++w) da.flags[w] = flags[w];
+    const int64_t S = (int64_t)D.B * D.H;
+    {
+        ProfScope ps(PK_LIN_DELTA, st);
+        hipLaunchKernelGGL((k_lin_delta<T, SCALE>), dim3((unsigned)(S * nc * da.ntv * da.ntk)), dim3(kThreads), 0, st,
+                           da);
+    }
+    return check_launch("k_lin_delta", st);
+}
+
+// Launch of the scan over the chunks of every scan (forward, or backward with rev)
+template <typename T>
+static ttt_status launch_scan(const linattn_desc& D, int64_t nc, int mode, const uint32_t (&flags)[32], const float* src,
+                              T* Sc, const LinStateIO& io, int rev, hipStream_t st) {
+    const int64_t S = (int64_t)D.B * D.H, dvk = (int64_t)D.d_v * D.d_k;
+    ScanArgs<T> sa{};
+    sa.dS = src;
+    sa.Sc = Sc;
+    sa.io = io;
+    sa.dvk = dvk;
+    sa.nc = (int)nc;
+    sa.mode = mode;
+    sa.nscan = (int)S;
+    sa.rev = rev;
+    for (int w = 0; w < 32; ++w) sa.flags[w] = flags[w];
+    {
+        ProfScope ps(PK_LIN_SCAN, st);
+        hipLaunchKernelGGL(k_lin_scan<T>, dim3((unsigned)cdiv(S * dvk / 4, kThreads)), dim3(kThreads), 0, st, sa);
+    }
+    return check_launch("k_lin_scan", st);
+}
+
 template <typename T>
 static ttt_status run_lin_parallel(const linattn_desc& D, LinArgs<T> a, char* ws, hipStream_t st,
                                    const LinStateIO& io) {
@@ -755,44 +809,14 @@ static ttt_status run_lin_parallel(const linattn_desc& D, LinArgs<T> a, char* ws
     float* dS = (float*)ws;
     T* Sc = (T*)(ws + align256((size_t)(S * nc * dvk * 4)));
     // 1. per-chunk updates
-    DeltaArgs<T> da{};
-    da.k = a.k;
-    da.v = a.v;
-    da.eta = a.eta;
-    da.dS = dS;
-    da.N = D.N;
-    da.dk = D.d_k;
-    da.dv = D.d_v;
-    da.chunk = (int)chunk;
-    da.nc = (int)nc;
-    da.ntv = (int)cdiv(D.d_v, kDeltaRows);
-    da.ntk = (int)cdiv(D.d_k, kDeltaCols);
-    da.mode = D.mask;
-    for (int w = 0; w < 32; ++w) da.flags[w] = a.flags[w];
-    {
-        ProfScope ps(PK_LIN_DELTA, st);
-        hipLaunchKernelGGL(k_lin_delta<T>, dim3((unsigned)(S * nc * da.ntv * da.ntk)), dim3(kThreads), 0, st, da);
-    }
-    ttt_status rc = check_launch("k_lin_delta", st);
+    ttt_status rc = launch_delta<T, true>(D, chunk, nc, D.mask, a.flags, a.k, a.v, a.eta, dS, st);
     if (rc != TTT_OK) return rc;
     // (the caller's step between the updates and the scan, which may hand the scan another buffer)
     const float* scan_src = dS;
     if (io.between && (rc = io.between(io.between_ctx, dS, &scan_src, st)) != TTT_OK) return rc;
-    // 2. states seen by each chunk, and S_out
-    ScanArgs<T> sa{};
-    sa.dS = scan_src;
-    sa.Sc = Sc;
-    sa.io = io;
-    sa.dvk = dvk;
-    sa.nc = (int)nc;
-    sa.mode = causal ? TTT_MASK_APPLY_THEN_UPDATE : D.mask;  // a causal block sees the state before it
-    sa.nscan = (int)S;
-    for (int w = 0; w < 32; ++w) sa.flags[w] = a.flags[w];
-    {
-        ProfScope ps(PK_LIN_SCAN, st);
-        hipLaunchKernelGGL(k_lin_scan<T>, dim3((unsigned)cdiv(S * dvk / 4, kThreads)), dim3(kThreads), 0, st, sa);
-    }
-    if ((rc = check_launch("k_lin_scan", st)) != TTT_OK) return rc;
+    // 2. states seen by each chunk, and S_out (a causal block sees the state before it)
+    rc = launch_scan<T>(D, nc, causal ? TTT_MASK_APPLY_THEN_UPDATE : D.mask, a.flags, scan_src, Sc, io, 0, st);
+    if (rc != TTT_OK) return rc;
     // 3. apply
     ApplyArgs<T> aa{};
     aa.q = a.q;
@@ -831,6 +855,296 @@ template ttt_status lin_chunked_run<uint16_t>(const linattn_desc&, const uint32_
                                               const LinStateIO&, char*, hipStream_t);
 template ttt_status lin_chunked_run<float>(const linattn_desc&, const uint32_t (&)[32], const float*, const float*,
                                            const float*, const float*, float*, const LinStateIO&, char*, hipStream_t);
+
+// ---------------------------------------------------------------------------------------------
+// Backward of the chunked masks: the outer-loop gradients for training through the parallel form
+// ("Test-Time Training with KV Binding Is Secretly Linear Attention", Sec. 6.2 and Fig. 4).
+//
+// For L = sum_t dO_t . o_t + <dS_out, S_out>: chunk c's queries see S_c, so dq_t = S_c^T dO_t and
+// D_c = sum over the chunk of dO_t q_t^T is the gradient of S_c.  Chunk j's update reaches the S_c
+// of the chunks after it (and its own under update-then-apply and the full mask) and S_out, so its
+// gradient is R_j = dS_out + the suffix sum of those D_c; then dv_s = eta_s R_j k_s,
+// dk_s = eta_s R_j^T v_s, deta_s = v_s . (R_j k_s), and dS0 = dS_out + sum_c D_c.  A chunk that a
+// strided mask does not update gets zero dk, dv and deta.  Launches: the forward's delta and scan
+// (S_c), the delta kernel with unit weights over (q, dO) into the same dS buffer (D_c), the scan
+// walked backwards (R_j as bf16 hi + lo planes or fp32, and dS0), then the two product kernels.
+
+// dq = dO S_c and dk = diag(eta) v R_c for one chunk: tokens x d_k, contracting over d_v.  The
+// d_v x d_k matrix goes through the transposing stager (its d_k index is the tile column); bf16
+// keeps it as hi + lo planes whose two accumulators are added before the epilogue.  One launch
+// covers both jobs: the first per_job workgroups do dq, the others dk.  The tile leaves row by row
+// through LDS, since the transposed operand permutes the accumulator columns.
+template <typename T> struct BwdTJob {
+    const T* y; const T* M; T* out;
+    const float* eta;  // row factors (dk), or null (dq)
+    int skip;          // strided mask: rows of chunks that do not update are zero
+};
+template <typename T> struct BwdTArgs {
+    BwdTJob<T> job[2];
+    int64_t N; int dk, dv, chunk, nc, ntt, ntn, per_job, mode;
+    uint32_t flags[32];
+};
+
+template <typename T>
+__global__ __launch_bounds__(kThreads, 2) void k_lin_bwd_t(BwdTArgs<T> a) {
+    constexpr int PLANES = sizeof(T) == 2 ? 2 : 1;
+    using TB = Tile<T, kApplyRows, kApplyCols, 1, 2, 1, PLANES, PLANES, false, true>;
+    using PM = typename std::conditional<PLANES == 2, PMQ, PM1>::type;
+    static_assert(TB::RV_LDS <= TB::LDS, "row bands fit the tile's LDS");
+    __shared__ __attribute__((aligned(16))) char smem[TB::LDS];
+    const int lb = xcd_block(gridDim.x);
+    const bool second = lb >= a.per_job;
+    const BwdTJob<T> jb = second ? a.job[1] : a.job[0];
+    const int l = second ? lb - a.per_job : lb;
+    const int per_chunk = a.ntt * a.ntn;
+    const int unit = l / per_chunk, t = l % per_chunk;
+    const int scan = unit / a.nc, c = unit % a.nc;
+    const int r0 = (t / a.ntn) * kApplyRows, c0 = (t % a.ntn) * kApplyCols;
+    const int64_t tok = (int64_t)scan * a.N + (int64_t)c * a.chunk;
+    const int nl = (int)std::min<int64_t>(a.chunk, a.N - (int64_t)c * a.chunk);
+    if (r0 >= nl) return;  // uniform per workgroup
+    const int rows = std::min(kApplyRows, nl - r0), cols = std::min(kApplyCols, a.dk - c0);
+    T* O = jb.out + (tok + r0) * a.dk + c0;
+    if (jb.skip && a.mode == TTT_MASK_STRIDED && !((a.flags[c >> 5] >> (c & 31)) & 1u)) {
+        for (int e = threadIdx.x; e < rows * cols; e += kThreads)
+            O[(uint32_t)(e / cols) * (uint32_t)a.dk + (uint32_t)(e % cols)] = Elt<T>::st(0.f);
+        return;
+    }
+    const int64_t dvk = (int64_t)a.dv * a.dk;
+    const T* M = jb.M + (int64_t)unit * PLANES * dvk + c0;
+    const Opnd<T> A[1] = {{jb.y + (tok + r0) * a.dv, a.dv, nl - r0, a.dv}};
+    Opnd<T> B[PLANES];
+#pragma unroll
+    for (int p = 0; p < PLANES; ++p) B[p] = Opnd<T>{M + p * dvk, a.dk, a.dk - c0, a.dv};
+    TB tl;
+    tl.template run<PM>(A, B, a.dv, smem);
+    if constexpr (PLANES == 2) {
+#pragma unroll
+        for (int i = 0; i < TB::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < TB::FN; ++j) tl.acc[0][i][j] += tl.acc[1][i][j];
+    }
+    const float* eta = jb.eta ? jb.eta + tok + r0 : nullptr;
+    tl.template rows_via_lds<1>(smem, [&](int, int, int row, int col, const float4& v) {
+        if (row < rows && col < cols) {
+            const float f = eta ? eta[row] : 1.f;
+            Pack4<T>::store(O + (uint32_t)row * (uint32_t)a.dk + (uint32_t)col, v.x * f, v.y * f, v.z * f, v.w * f);
+        }
+    });
+}
+
+// dv = diag(eta) k R_c^T for one chunk (tokens x d_v, contracting over d_k; R_c row-major, as the
+// forward's apply reads S_c) and, from the same accumulators, deta_s = v_s . (R_c k_s) over the
+// tile's d_v columns: a thread sums its products per row, a butterfly over the 32 lanes that share
+// rows leaves each lane the whole sum of one row, and the waves of a tile row add theirs in LDS.
+// With more than one column tile the sums go to per-tile partials (deta then points at them).
+template <typename T> struct BwdNArgs {
+    const T* k; const T* R; const T* v; const float* eta; T* dv; float* deta;
+    int64_t N, ntok;  // ntok: B*H*N, the distance between the partials of two column tiles
+    int dk, dvn, chunk, nc, ntt, ntn, mode;
+    uint32_t flags[32];
+};
+
+template <typename T>
+__global__ __launch_bounds__(kThreads, 2) void k_lin_bwd_n(BwdNArgs<T> a) {
+    constexpr int PLANES = sizeof(T) == 2 ? 2 : 1;
+    using TA = Tile<T, kApplyRows, kApplyCols, 1, 2, 1, PLANES, PLANES, false, false>;
+    using PM = typename std::conditional<PLANES == 2, PMQ, PM1>::type;
+    constexpr int NR = TA::FM * 16;  // accumulator rows of a thread
+    static_assert(NR == 32, "one row per lane of a 32-lane half after the butterfly");
+    __shared__ __attribute__((aligned(16))) char smem[TA::LDS];
+    __shared__ float rsum[kApplyRows];
+    const int lb = xcd_block(gridDim.x);
+    const int per_chunk = a.ntt * a.ntn;
+    const int unit = lb / per_chunk, t = lb % per_chunk;
+    const int scan = unit / a.nc, c = unit % a.nc, tc = t % a.ntn;
+    const int r0 = (t / a.ntn) * kApplyRows, c0 = tc * kApplyCols;
+    const int64_t tok = (int64_t)scan * a.N + (int64_t)c * a.chunk;
+    const int nl = (int)std::min<int64_t>(a.chunk, a.N - (int64_t)c * a.chunk);
+    if (r0 >= nl) return;  // uniform per workgroup
+    const int rows = std::min(kApplyRows, nl - r0), cols = std::min(kApplyCols, a.dvn - c0);
+    T* O = a.dv + (tok + r0) * a.dvn + c0;
+    float* de = a.deta + (int64_t)tc * a.ntok + tok + r0;
+    if (a.mode == TTT_MASK_STRIDED && !((a.flags[c >> 5] >> (c & 31)) & 1u)) {
+        for (int e = threadIdx.x; e < rows * cols; e += kThreads)
+            O[(uint32_t)(e / cols) * (uint32_t)a.dvn + (uint32_t)(e % cols)] = Elt<T>::st(0.f);
+        for (int e = threadIdx.x; e < rows; e += kThreads) de[e] = 0.f;
+        return;
+    }
+    if (threadIdx.x < kApplyRows) rsum[threadIdx.x] = 0.f;  // ordered before the adds by run()'s barriers
+    const int64_t dvk = (int64_t)a.dvn * a.dk;
+    const T* R = a.R + (int64_t)unit * PLANES * dvk + (int64_t)c0 * a.dk;
+    const Opnd<T> A[1] = {{a.k + (tok + r0) * a.dk, a.dk, nl - r0, a.dk}};
+    Opnd<T> B[PLANES];
+#pragma unroll
+    for (int p = 0; p < PLANES; ++p) B[p] = Opnd<T>{R + p * dvk, a.dk, a.dvn - c0, a.dk};
+    TA tl;
+    tl.template run<PM>(A, B, a.dk, smem);
+    const float* eta = a.eta + tok + r0;
+    const T* V = a.v + (tok + r0) * a.dvn + c0;
+    // element r of block (i, j) of a thread lies at row wm*WM + i*32 + 8*(r>>2) + 4*(lane>>5) + (r&3)
+    // and column wn*WN + j*32 + (lane&31) of the tile
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / TA::WGN, wn = wave % TA::WGN;
+    float ps[NR];
+#pragma unroll
+    for (int x = 0; x < NR; ++x) ps[x] = 0.f;
+#pragma unroll
+    for (int i = 0; i < TA::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < TA::FN; ++j) {
+            const int col = wn * TA::WN + j * 32 + (lane & 31);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = wm * TA::WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                float u = tl.acc[0][i][j][r];
+                if constexpr (PLANES == 2) u += tl.acc[1][i][j][r];
+                if (row < rows && col < cols) {
+                    const uint32_t off = (uint32_t)row * (uint32_t)a.dvn + (uint32_t)col;
+                    ps[i * 16 + r] += u * Elt<T>::ld(V[off]);
+                    O[off] = Elt<T>::st(u * eta[row]);
+                }
+            }
+        }
+    // butterfly reduce-scatter over the lanes of a 32-lane half: at step s a lane keeps the half of
+    // its list selected by bit s of its lane index and adds the partner's copy of it, so that in the
+    // end ps[0] holds the half's sum for list entry (lane & 31)
+#pragma unroll
+    for (int s = 16; s >= 1; s >>= 1) {
+        const bool up = (lane & s) != 0;
+#pragma unroll
+        for (int x = 0; x < s; ++x) {
+            const float keep = up ? ps[x + s] : ps[x];
+            const float give = up ? ps[x] : ps[x + s];
+            ps[x] = keep + __shfl_xor(give, s);
+        }
+    }
+    {
+        const int x = lane & 31, i = x >> 4, r = x & 15;
+        atomicAdd(&rsum[wm * TA::WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)], ps[0]);
+    }
+    __syncthreads();
+    if (threadIdx.x < rows) de[threadIdx.x] = rsum[threadIdx.x];
+}
+
+// deta = the sum of the column tiles' partials
+__global__ __launch_bounds__(kThreads) void k_lin_deta_sum(const float* part, float* deta, int64_t ntok, int ntn) {
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= ntok) return;
+    float s = 0.f;
+    for (int t = 0; t < ntn; ++t) s += part[(int64_t)t * ntok + i];
+    deta[i] = s;
+}
+
+static ttt_status validate_lin_bwd(const linattn_desc* D) {
+    ttt_status rc = validate_lin(D);
+    if (rc != TTT_OK) return rc;
+    if (D->mask == TTT_MASK_TOKEN_CAUSAL)
+        return fail(TTT_ERR_UNSUPPORTED, "the backward covers the chunked masks (not TOKEN_CAUSAL)");
+    const int64_t S = (int64_t)D->B * D->H, nc = D->N ? cdiv(D->N, D->chunk) : 0;
+    const int64_t ntt = D->N ? cdiv(std::min<int64_t>(D->chunk, D->N), kApplyRows) : 0;
+    const int64_t tiles = S * nc * ntt * std::max(cdiv(D->d_k, kApplyCols), cdiv(D->d_v, kApplyCols));
+    const int64_t dtiles = S * nc * cdiv(D->d_v, kDeltaRows) * cdiv(D->d_k, kDeltaCols);
+    if (2 * tiles > INT32_MAX || dtiles > INT32_MAX || S * D->d_v * (int64_t)D->d_k / 4 > INT32_MAX * (int64_t)kThreads)
+        return fail(TTT_ERR_UNSUPPORTED, "too many tiles for one launch");
+    return TTT_OK;
+}
+
+static size_t lin_bwd_ws_bytes(const linattn_desc& D) {
+    if (D.N == 0) return 0;
+    const int64_t S = (int64_t)D.B * D.H, nc = cdiv(D.N, D.chunk), ntn = cdiv(D.d_v, kApplyCols);
+    const size_t sb = align256((size_t)(S * nc * (int64_t)D.d_v * D.d_k * 4));
+    return 3 * sb + (ntn > 1 ? align256((size_t)(ntn * S * D.N * 4)) : 0);
+}
+
+template <typename T>
+static ttt_status run_lin_bwd(const linattn_desc& D, const uint32_t (&flags)[32], const T* q, const T* k, const T* v,
+                              const float* eta, const float* S0, const T* dO, const float* dS_out, T* dq, T* dk, T* dv,
+                              float* deta, float* dS0, char* ws, hipStream_t st) {
+    const int64_t S = (int64_t)D.B * D.H, dvk = (int64_t)D.d_v * D.d_k;
+    const int64_t chunk = D.chunk, nc = D.N ? cdiv(D.N, chunk) : 0;
+    const size_t sb = align256((size_t)(S * nc * dvk * 4));
+    float* dS = (float*)ws;
+    T* Sc = (T*)(ws + sb);
+    T* R = (T*)(ws + 2 * sb);
+    float* part = (float*)(ws + 3 * sb);
+    uint32_t all[32];
+    for (int w = 0; w < 32; ++w) all[w] = ~0u;
+    ttt_status rc;
+    if (D.N > 0) {
+        // the states the chunks' queries saw
+        if ((rc = launch_delta<T, true>(D, chunk, nc, D.mask, flags, k, v, eta, dS, st)) != TTT_OK) return rc;
+        LinStateIO fio;
+        fio.S0 = S0;
+        fio.s0_stride = dvk;
+        if ((rc = launch_scan<T>(D, nc, D.mask, flags, dS, Sc, fio, 0, st)) != TTT_OK) return rc;
+        // D_c = sum over the chunk of dO q^T, every chunk
+        if ((rc = launch_delta<T, false>(D, chunk, nc, TTT_MASK_APPLY_THEN_UPDATE, all, q, dO, nullptr, dS, st)) !=
+            TTT_OK)
+            return rc;
+    }
+    // R_j (backwards over the chunks, every D_c added; the mask decides whether chunk j's own term is
+    // in R_j) and dS0 = dS_out + sum_c D_c
+    LinStateIO rio;
+    rio.S0 = dS_out;
+    rio.s0_stride = dvk;
+    rio.Sout = dS0;
+    rio.sout_stride = dvk;
+    if (D.N > 0 || dS0)
+        if ((rc = launch_scan<T>(D, nc, D.mask, all, dS, R, rio, 1, st)) != TTT_OK) return rc;
+    if (D.N == 0) return TTT_OK;
+    const int ntt = (int)cdiv(std::min<int64_t>(chunk, D.N), kApplyRows);
+    BwdTArgs<T> ta{};
+    ta.job[0] = BwdTJob<T>{dO, Sc, dq, nullptr, 0};
+    ta.job[1] = BwdTJob<T>{v, R, dk, eta, 1};
+    ta.N = D.N;
+    ta.dk = D.d_k;
+    ta.dv = D.d_v;
+    ta.chunk = (int)chunk;
+    ta.nc = (int)nc;
+    ta.ntt = ntt;
+    ta.ntn = (int)cdiv(D.d_k, kApplyCols);
+    ta.per_job = (int)(S * nc * ntt * ta.ntn);
+    ta.mode = D.mask;
+    for (int w = 0; w < 32; ++w) ta.flags[w] = flags[w];
+    {
+        ProfScope ps(PK_LIN_BWD_T, st);
+        hipLaunchKernelGGL(k_lin_bwd_t<T>, dim3((unsigned)(2 * ta.per_job)), dim3(kThreads), 0, st, ta);
+    }
+    if ((rc = check_launch("k_lin_bwd_t", st)) != TTT_OK) return rc;
+    BwdNArgs<T> na{};
+    const int ntn = (int)cdiv(D.d_v, kApplyCols);
+    na.k = k;
+    na.R = R;
+    na.v = v;
+    na.eta = eta;
+    na.dv = dv;
+    na.deta = ntn > 1 ? part : deta;
+    na.N = D.N;
+    na.ntok = S * D.N;
+    na.dk = D.d_k;
+    na.dvn = D.d_v;
+    na.chunk = (int)chunk;
+    na.nc = (int)nc;
+    na.ntt = ntt;
+    na.ntn = ntn;
+    na.mode = D.mask;
+    for (int w = 0; w < 32; ++w) na.flags[w] = flags[w];
+    {
+        ProfScope ps(PK_LIN_BWD_N, st);
+        hipLaunchKernelGGL(k_lin_bwd_n<T>, dim3((unsigned)(S * nc * ntt * ntn)), dim3(kThreads), 0, st, na);
+    }
+    if ((rc = check_launch("k_lin_bwd_n", st)) != TTT_OK) return rc;
+    if (ntn > 1) {
+        {
+            ProfScope ps(PK_LIN_DETA, st);
+            hipLaunchKernelGGL(k_lin_deta_sum, dim3((unsigned)cdiv(S * D.N, kThreads)), dim3(kThreads), 0, st,
+                               (const float*)part, deta, S * D.N, ntn);
+        }
+        if ((rc = check_launch("k_lin_deta_sum", st)) != TTT_OK) return rc;
+    }
+    return TTT_OK;
+}
 
 }  // namespace ttt
 
@@ -905,4 +1219,70 @@ extern "C" ttt_status linattn_forward(const linattn_desc* desc, const void* q, c
     };
     if (D.io_dtype == TTT_BF16) return go((uint16_t*)nullptr);
     return go((float*)nullptr);
+}
+
+extern "C" ttt_status linattn_backward_workspace_bytes(const linattn_desc* desc, size_t* bytes) {
+    clear_error();
+    ttt_status rc = validate_lin_bwd(desc);
+    if (rc != TTT_OK) return rc;
+    if (!bytes) return fail(TTT_ERR_INVALID_ARGUMENT, "bytes is NULL");
+    *bytes = lin_bwd_ws_bytes(*desc);
+    return TTT_OK;
+}
+
+extern "C" ttt_status linattn_backward(const linattn_desc* desc, const void* q, const void* k, const void* v,
+                                       const float* eta, const float* S0, const void* dO, const float* dS_out,
+                                       void* dq, void* dk, void* dv, float* deta, float* dS0, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+    clear_error();
+    ttt_status rc = validate_lin_bwd(desc);
+    if (rc != TTT_OK) return rc;
+    const linattn_desc& D = *desc;
+    const int64_t S = (int64_t)D.B * D.H;
+    if (S == 0) return TTT_OK;
+    const bool t = D.N > 0;
+    if (t && (!q || !k || !v || !eta || !dO || !dq || !dk || !dv || !deta))
+        return fail(TTT_ERR_INVALID_ARGUMENT, "q, k, v, eta, dO, dq, dk, dv and deta are required");
+    const void* p16[] = {q, k, v, dO, dq, dk, dv};
+    for (const void* p : p16)
+        if (p && !aligned(p, 16)) return fail(TTT_ERR_INVALID_ARGUMENT, "q, k, v, dO, dq, dk, dv must be 16-byte aligned");
+    const void* p4[] = {eta, S0, dS_out, deta, dS0};
+    for (const void* p : p4)
+        if (p && !aligned(p, 4)) return fail(TTT_ERR_INVALID_ARGUMENT, "eta, S0, dS_out, deta, dS0 must be 4-byte aligned");
+    const size_t es = D.io_dtype == TTT_BF16 ? 2 : 4;
+    const size_t qb = t ? (size_t)S * D.N * D.d_k * es : 0, vb = t ? (size_t)S * D.N * D.d_v * es : 0;
+    const size_t eb = t ? (size_t)S * D.N * 4 : 0, sb = (size_t)S * D.d_v * D.d_k * 4;
+    const struct { const void* p; size_t n; const char* name; } ins[] = {
+        {q, qb, "q"}, {k, qb, "k"}, {v, vb, "v"}, {eta, eb, "eta"}, {S0, sb, "S0"}, {dO, vb, "dO"},
+        {dS_out, sb, "dS_out"}};
+    const struct { const void* p; size_t n; const char* name; } outs[] = {
+        {dq, qb, "dq"}, {dk, qb, "dk"}, {dv, vb, "dv"}, {deta, eb, "deta"}, {dS0, sb, "dS0"}};
+    for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+        for (const auto& in : ins)
+            if (overlaps(outs[i].p, outs[i].n, in.p, in.n))
+                return fail(TTT_ERR_INVALID_ARGUMENT, "%s overlaps the input %s", outs[i].name, in.name);
+        for (size_t j = 0; j < i; ++j)
+            if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n))
+                return fail(TTT_ERR_INVALID_ARGUMENT, "%s overlaps %s", outs[i].name, outs[j].name);
+    }
+    const size_t need = lin_bwd_ws_bytes(D);
+    if (need && (!workspace || workspace_bytes < need))
+        return fail(TTT_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+    if (need && !aligned(workspace, 256)) return fail(TTT_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    for (const auto& b : ins)
+        if ((rc = check_buffer(b.p, b.n, b.name)) != TTT_OK) return rc;
+    for (const auto& b : outs)
+        if ((rc = check_buffer(b.p, b.n, b.name)) != TTT_OK) return rc;
+    if ((rc = check_buffer(workspace, need, "workspace")) != TTT_OK) return rc;
+    uint32_t flags[32] = {};
+    if (D.mask == TTT_MASK_STRIDED)
+        for (int64_t j = 0; j < cdiv(D.N, D.chunk); ++j)
+            if (D.update_chunks[j]) flags[j >> 5] |= 1u << (j & 31);
+    hipStream_t st = (hipStream_t)stream;
+    if (D.io_dtype == TTT_BF16)
+        return run_lin_bwd<uint16_t>(D, flags, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, eta, S0,
+                                     (const uint16_t*)dO, dS_out, (uint16_t*)dq, (uint16_t*)dk, (uint16_t*)dv, deta,
+                                     dS0, (char*)workspace, st);
+    return run_lin_bwd<float>(D, flags, (const float*)q, (const float*)k, (const float*)v, eta, S0, (const float*)dO,
+                              dS_out, (float*)dq, (float*)dk, (float*)dv, deta, dS0, (char*)workspace, st);
 }

@@ -562,13 +562,15 @@ struct Tile {
                 }
     }
 
-    template <class F>
+    // (NPU: only the first NPU accumulators are written out)
+    template <int NPU = NP, class F>
     __device__ __forceinline__ void rows_via_lds(char* lds, F&& f) const {
+        static_assert(NPU >= 1 && NPU <= NP, "bad accumulator count");
         float* band = reinterpret_cast<float*>(lds);
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
         const int wm = wave / WGN, wn = wave % WGN;
 #pragma unroll
-        for (int p = 0; p < NP; ++p)
+        for (int p = 0; p < NPU; ++p)
 #pragma unroll
             for (int h = 0; h < WGM; ++h) {
                 lds_barrier();

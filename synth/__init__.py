@@ -12,7 +12,10 @@ Recipe (per (batch, head) slice, so any slice can be regenerated on its own):
   * the initial fast weights of head h come from ``default_rng([seed, 10**6 + h])``, drawing
     W1 (m x d), W3 (m x d), W2 (d x m) with entries N(0, 1/d), stored fp32;
   * q, k, v are rounded once, round-to-nearest-even, to bfloat16 when the workload runs in bf16;
-    the rounded values (held in float32 arrays) are what every consumer sees.
+    the rounded values (held in float32 arrays) are what every consumer sees;
+  * the backward's upstream gradients of slice (b, h) come from ``default_rng([seed, b, h, 7])``:
+    dO [N, d_v] with entries N(0, 1) / sqrt(d_v) (rounded to bfloat16 for bf16 workloads), then
+    dS_out [d_v, d_k] with entries N(0, 1) / sqrt(d_k), kept in fp32.
 """
 from __future__ import annotations
 
@@ -25,6 +28,8 @@ __all__ = [
     "head_weights",
     "make_ttt_inputs",
     "make_linattn_inputs",
+    "grad_slice",
+    "make_linattn_grads",
 ]
 
 
@@ -125,3 +130,23 @@ def make_linattn_inputs(seed: int, B: int, H: int, N: int, d_k: int, d_v: int, b
     for b, h in todo:
         q[b, h], k[b, h], v[b, h], eta[b, h] = slice_inputs(seed, b, h, N, d_k, d_v, eta_kind, eta_scale, bf16)
     return q, k, v, eta
+
+
+def grad_slice(seed: int, b: int, h: int, N: int, d_k: int, d_v: int, bf16: bool = True):
+    """Upstream gradients of one (batch, head) slice: dO [N, d_v] and dS_out [d_v, d_k] (fp32)."""
+    rng = np.random.default_rng([seed, b, h, 7])
+    dO = np.divide(rng.standard_normal((N, d_v), dtype=np.float32), np.float32(np.sqrt(d_v)), dtype=np.float32)
+    dS = np.divide(rng.standard_normal((d_v, d_k), dtype=np.float32), np.float32(np.sqrt(d_k)), dtype=np.float32)
+    if bf16:
+        dO = round_to_bf16(dO)
+    return dO, dS
+
+
+def make_linattn_grads(seed: int, B: int, H: int, N: int, d_k: int, d_v: int, bf16: bool = True, slices=None):
+    """dO [B, H, N, d_v] and dS_out [B, H, d_v, d_k] (slices not listed stay zero)."""
+    dO = np.zeros((B, H, N, d_v), np.float32)
+    dS = np.zeros((B, H, d_v, d_k), np.float32)
+    todo = [(b, h) for b in range(B) for h in range(H)] if slices is None else list(slices)
+    for b, h in todo:
+        dO[b, h], dS[b, h] = grad_slice(seed, b, h, N, d_k, d_v, bf16)
+    return dO, dS

@@ -39,7 +39,7 @@ def test_library_loads_and_exports_every_symbol():
 
 def test_version_and_status_strings():
     L = C.lib()
-    assert L.ttt_abi_version() == 3
+    assert L.ttt_abi_version() == 4
     for s in range(5):
         assert L.ttt_status_string(s)
     assert L.ttt_status_string(99) == b"unknown status"
