@@ -430,6 +430,38 @@ def main():
                             "hbm_GBps": round(lin_bytes / (msl * 1e-3) / 1e9, 1),
                             "hbm_frac": round(lin_bytes / (msl * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                             "workload": f"B{B2} H{H2} N{N2} d_k=d_v={d2} chunk {c2} bf16"}
+        # the backward of the chunked mask at the same shape (the gradients that training through the
+        # parallel form needs), with its kernels' times from one bracketed pass after the timed calls
+        print("[bench] extras: linear-attention backward", file=sys.stderr, flush=True)
+        gb = torch.Generator(device="cuda")
+        gb.manual_seed(3500 + args.seed)
+        dO2 = (torch.randn((B2, H2, N2, d2), generator=gb, device="cuda") / d2 ** 0.5).to(torch.bfloat16)
+        Db, _ = T.linattn_desc(B2, H2, N2, d2, d2, c2, C.TTT_BF16, C.MASK_APPLY_THEN_UPDATE)
+        wsb = torch.empty(max(1, T.linattn_backward_workspace_bytes(Db)), dtype=torch.uint8, device="cuda")
+        bwd = lambda: T.linattn_backward(q2, k2, v2, e2, dO2, c2, C.MASK_APPLY_THEN_UPDATE, want_dS0=False,  # noqa: E731
+                                         workspace=wsb)
+        msb = time_calls(torch, bwd, max(st, 10), 2)
+        C.profile_select(None)
+        C.profile_enable(True)
+        C.profile_read()
+        for _ in range(3):
+            bwd()
+        torch.cuda.synchronize()
+        bk = {kn: round(t / 3, 4) for kn, (t, n) in C.profile_read().items() if n}
+        C.profile_enable(False)
+        # algorithmic bytes: q, k, v, dO and eta in, dq, dk, dv and deta out; algorithmic flops: the two
+        # chunk-update sums (eta v k^T, dO q^T) and the three gradient products, 2 d_k d_v each per token
+        bwd_bytes = B2 * H2 * N2 * (7 * d2 * 2 + 8)
+        bwd_flops = B2 * H2 * N2 * 10 * d2 * d2
+        extras["linattn_backward"] = {
+            "tokens_per_s": round(B2 * N2 / (msb * 1e-3)), "ms_per_call": round(msb, 4),
+            "hbm_GBps": round(bwd_bytes / (msb * 1e-3) / 1e9, 1),
+            "hbm_frac": round(bwd_bytes / (msb * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "mfma_frac": round(bwd_flops / (msb * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "over_forward": round(msb / extras["linattn_chunked"]["ms_per_call"], 2),
+            "kernels_ms": bk,
+            "workload": f"B{B2} H{H2} N{N2} d_k=d_v={d2} chunk {c2} bf16, apply-then-update, dO given"}
+        del dO2, wsb
         # the SwiGLU layer at the same shape (m = 2d), for the linear-vs-SwiGLU comparison
         m2 = 2 * d2
         W02 = torch.randn((H2, 3 * d2 * m2), device="cuda") / d2 ** 0.5

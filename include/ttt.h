@@ -214,7 +214,7 @@ ttt_status linattn_forward(const linattn_desc* desc, const void* q, const void* 
 /*
  * Device workspace that linattn_backward needs, in bytes: the update, the state and the state
  * gradient of every chunk and scan (12 bytes per state element per chunk), plus B*H*N*4 bytes per
- * 128 columns of d_v when d_v > 128; zero when N is 0.
+ * 128 columns of d_k when d_k > 128; zero when N is 0.
  */
 ttt_status linattn_backward_workspace_bytes(const linattn_desc* desc, size_t* bytes);
 

@@ -873,15 +873,20 @@ template ttt_status lin_chunked_run<float>(const linattn_desc&, const uint32_t (
 // d_v x d_k matrix goes through the transposing stager (its d_k index is the tile column); bf16
 // keeps it as hi + lo planes whose two accumulators are added before the epilogue.  One launch
 // covers both jobs: the first per_job workgroups do dq, the others dk.  The tile leaves row by row
-// through LDS, since the transposed operand permutes the accumulator columns.
+// through LDS, since the transposed operand permutes the accumulator columns.  The dk job also forms
+// deta_s = k_s . w_s with w_s = R^T v_s (its rows before the eta factor) over the tile's d_k columns:
+// each thread takes 4 columns of 16 rows; a butterfly over the 32 lanes that share each row leaves
+// the row sums on the even lanes.
 template <typename T> struct BwdTJob {
     const T* y; const T* M; T* out;
     const float* eta;  // row factors (dk), or null (dq)
     int skip;          // strided mask: rows of chunks that do not update are zero
+    const T* kk;       // dk job: the keys, for deta_s = k_s . (R^T v_s) from the unscaled rows
+    float* deta;       // dk job: deta, or its per-column-tile partials (ntok apart); null for dq
 };
 template <typename T> struct BwdTArgs {
     BwdTJob<T> job[2];
-    int64_t N; int dk, dv, chunk, nc, ntt, ntn, per_job, mode;
+    int64_t N, ntok; int dk, dv, chunk, nc, ntt, ntn, per_job, mode;
     uint32_t flags[32];
 };
 
@@ -905,9 +910,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_lin_bwd_t(BwdTArgs<T> a) {
     if (r0 >= nl) return;  // uniform per workgroup
     const int rows = std::min(kApplyRows, nl - r0), cols = std::min(kApplyCols, a.dk - c0);
     T* O = jb.out + (tok + r0) * a.dk + c0;
+    float* de = jb.deta ? jb.deta + (int64_t)(t % a.ntn) * a.ntok + tok + r0 : nullptr;
     if (jb.skip && a.mode == TTT_MASK_STRIDED && !((a.flags[c >> 5] >> (c & 31)) & 1u)) {
         for (int e = threadIdx.x; e < rows * cols; e += kThreads)
             O[(uint32_t)(e / cols) * (uint32_t)a.dk + (uint32_t)(e % cols)] = Elt<T>::st(0.f);
+        if (de)
+            for (int e = threadIdx.x; e < rows; e += kThreads) de[e] = 0.f;
         return;
     }
     const int64_t dvk = (int64_t)a.dv * a.dk;
@@ -925,23 +933,65 @@ __global__ __launch_bounds__(kThreads, 2) void k_lin_bwd_t(BwdTArgs<T> a) {
             for (int j = 0; j < TB::FN; ++j) tl.acc[0][i][j] += tl.acc[1][i][j];
     }
     const float* eta = jb.eta ? jb.eta + tok + r0 : nullptr;
-    tl.template rows_via_lds<1>(smem, [&](int, int, int row, int col, const float4& v) {
+    const T* K = jb.kk ? jb.kk + (tok + r0) * a.dk + c0 : nullptr;
+    constexpr int NV = TB::RV_N / PLANES;  // row pieces of a thread (one accumulator)
+    static_assert(NV == 16 && TB::BN / 4 == 32, "32 lanes per tile row, 16 rows per lane");
+    // the dk job's keys and row factors for the epilogue's positions, all loads issued at once (the
+    // staging registers are free by now)
+    typename Pack4<T>::raw kr[NV];
+    float ef[NV];
+    if (K) {  // uniform: the job
+        TB::rows_via_lds_pos([&](int idx, int p, int row, int col) {
+            if (p == 0) {
+                const bool in = row < rows && col < cols;
+                kr[idx] = Pack4<T>::load_raw(K + (in ? (uint32_t)row * (uint32_t)a.dk + (uint32_t)col : 0u));
+                ef[idx] = eta[in ? row : 0];
+            }
+        });
+    }
+    float pd[NV];
+    tl.template rows_via_lds<1>(smem, [&](int idx, int, int row, int col, const float4& v) {
+        pd[idx] = 0.f;
         if (row < rows && col < cols) {
-            const float f = eta ? eta[row] : 1.f;
-            Pack4<T>::store(O + (uint32_t)row * (uint32_t)a.dk + (uint32_t)col, v.x * f, v.y * f, v.z * f, v.w * f);
+            const uint32_t off = (uint32_t)row * (uint32_t)a.dk + (uint32_t)col;
+            const float f = K ? ef[idx] : 1.f;
+            Pack4<T>::store(O + off, v.x * f, v.y * f, v.z * f, v.w * f);
+            if (K) {
+                float kv[4];
+                Pack4<T>::unpack(kr[idx], kv);
+                pd[idx] = v.x * kv[0] + v.y * kv[1] + v.z * kv[2] + v.w * kv[3];
+            }
         }
     });
+    if (!de) return;  // uniform: the job
+    // reduce-scatter: at step s a lane keeps the half of its list picked by bit s of its lane index
+    // and adds the partner's copy of that half; then lanes l and l ^ 1 add their last entry, so lane l
+    // holds the 32 lanes' sum for entry (l >> 1) & 15
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int sh = 16, n = NV / 2; sh >= 2; sh >>= 1, n >>= 1) {
+        const bool up = (lane & sh) != 0;
+#pragma unroll
+        for (int x = 0; x < n; ++x) {
+            const float keep = up ? pd[x + n] : pd[x];
+            const float give = up ? pd[x] : pd[x + n];
+            pd[x] = keep + __shfl_xor(give, sh);
+        }
+    }
+    pd[0] += __shfl_xor(pd[0], 1);
+    if ((lane & 1) == 0) {
+        // entry idx = h * RV_K + k covers tile row h * WM + (k * NT + tid) / 32
+        const int idx = (lane >> 1) & 15, h = idx / TB::RV_K, k = idx % TB::RV_K;
+        const int row = h * TB::WM + (k * TB::NT + wave * 64 + (lane & 32)) / 32;
+        if (row < rows) de[row] = pd[0];
+    }
 }
 
-// dv = diag(eta) k R_c^T for one chunk (tokens x d_v, contracting over d_k; R_c row-major, as the
-// forward's apply reads S_c) and, from the same accumulators, deta_s = v_s . (R_c k_s) over the
-// tile's d_v columns: a thread sums its products per row, a butterfly over the 32 lanes that share
-// rows leaves each lane the whole sum of one row, and the waves of a tile row add theirs in LDS.
-// With more than one column tile the sums go to per-tile partials (deta then points at them).
+// dv = diag(eta) k R_c^T for one chunk: tokens x d_v, contracting over d_k, R_c row-major (as the
+// forward's apply reads S_c).  The rows' eta factors are staged in LDS before the product.
 template <typename T> struct BwdNArgs {
-    const T* k; const T* R; const T* v; const float* eta; T* dv; float* deta;
-    int64_t N, ntok;  // ntok: B*H*N, the distance between the partials of two column tiles
-    int dk, dvn, chunk, nc, ntt, ntn, mode;
+    const T* k; const T* R; const float* eta; T* dv;
+    int64_t N; int dk, dvn, chunk, nc, ntt, ntn, mode;
     uint32_t flags[32];
 };
 
@@ -950,28 +1000,24 @@ __global__ __launch_bounds__(kThreads, 2) void k_lin_bwd_n(BwdNArgs<T> a) {
     constexpr int PLANES = sizeof(T) == 2 ? 2 : 1;
     using TA = Tile<T, kApplyRows, kApplyCols, 1, 2, 1, PLANES, PLANES, false, false>;
     using PM = typename std::conditional<PLANES == 2, PMQ, PM1>::type;
-    constexpr int NR = TA::FM * 16;  // accumulator rows of a thread
-    static_assert(NR == 32, "one row per lane of a 32-lane half after the butterfly");
     __shared__ __attribute__((aligned(16))) char smem[TA::LDS];
-    __shared__ float rsum[kApplyRows];
     const int lb = xcd_block(gridDim.x);
     const int per_chunk = a.ntt * a.ntn;
     const int unit = lb / per_chunk, t = lb % per_chunk;
-    const int scan = unit / a.nc, c = unit % a.nc, tc = t % a.ntn;
-    const int r0 = (t / a.ntn) * kApplyRows, c0 = tc * kApplyCols;
+    const int scan = unit / a.nc, c = unit % a.nc;
+    const int r0 = (t / a.ntn) * kApplyRows, c0 = (t % a.ntn) * kApplyCols;
     const int64_t tok = (int64_t)scan * a.N + (int64_t)c * a.chunk;
     const int nl = (int)std::min<int64_t>(a.chunk, a.N - (int64_t)c * a.chunk);
     if (r0 >= nl) return;  // uniform per workgroup
     const int rows = std::min(kApplyRows, nl - r0), cols = std::min(kApplyCols, a.dvn - c0);
     T* O = a.dv + (tok + r0) * a.dvn + c0;
-    float* de = a.deta + (int64_t)tc * a.ntok + tok + r0;
     if (a.mode == TTT_MASK_STRIDED && !((a.flags[c >> 5] >> (c & 31)) & 1u)) {
         for (int e = threadIdx.x; e < rows * cols; e += kThreads)
             O[(uint32_t)(e / cols) * (uint32_t)a.dvn + (uint32_t)(e % cols)] = Elt<T>::st(0.f);
-        for (int e = threadIdx.x; e < rows; e += kThreads) de[e] = 0.f;
         return;
     }
-    if (threadIdx.x < kApplyRows) rsum[threadIdx.x] = 0.f;  // ordered before the adds by run()'s barriers
+    __shared__ float er[kApplyRows];  // the rows' eta, ordered before the epilogue by run()'s barriers
+    if (threadIdx.x < rows) er[threadIdx.x] = a.eta[tok + r0 + threadIdx.x];
     const int64_t dvk = (int64_t)a.dvn * a.dk;
     const T* R = a.R + (int64_t)unit * PLANES * dvk + (int64_t)c0 * a.dk;
     const Opnd<T> A[1] = {{a.k + (tok + r0) * a.dk, a.dk, nl - r0, a.dk}};
@@ -980,15 +1026,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_lin_bwd_n(BwdNArgs<T> a) {
     for (int p = 0; p < PLANES; ++p) B[p] = Opnd<T>{R + p * dvk, a.dk, a.dvn - c0, a.dk};
     TA tl;
     tl.template run<PM>(A, B, a.dk, smem);
-    const float* eta = a.eta + tok + r0;
-    const T* V = a.v + (tok + r0) * a.dvn + c0;
-    // element r of block (i, j) of a thread lies at row wm*WM + i*32 + 8*(r>>2) + 4*(lane>>5) + (r&3)
-    // and column wn*WN + j*32 + (lane&31) of the tile
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave / TA::WGN, wn = wave % TA::WGN;
-    float ps[NR];
-#pragma unroll
-    for (int x = 0; x < NR; ++x) ps[x] = 0.f;
+    // element r of a thread's block (i, j) lies on tile row wm*WM + i*32 + 8*(r>>2) + 4*(lane>>5) + (r&3)
+    // and column wn*WN + j*32 + (lane&31)
+    const int lane = threadIdx.x & 63, wm = (threadIdx.x >> 6) / TA::WGN, wn = (threadIdx.x >> 6) % TA::WGN;
 #pragma unroll
     for (int i = 0; i < TA::FM; ++i)
 #pragma unroll
@@ -999,32 +1039,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_lin_bwd_n(BwdNArgs<T> a) {
                 const int row = wm * TA::WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
                 float u = tl.acc[0][i][j][r];
                 if constexpr (PLANES == 2) u += tl.acc[1][i][j][r];
-                if (row < rows && col < cols) {
-                    const uint32_t off = (uint32_t)row * (uint32_t)a.dvn + (uint32_t)col;
-                    ps[i * 16 + r] += u * Elt<T>::ld(V[off]);
-                    O[off] = Elt<T>::st(u * eta[row]);
-                }
+                if (row < rows && col < cols)
+                    O[(uint32_t)row * (uint32_t)a.dvn + (uint32_t)col] = Elt<T>::st(u * er[row]);
             }
         }
-    // butterfly reduce-scatter over the lanes of a 32-lane half: at step s a lane keeps the half of
-    // its list selected by bit s of its lane index and adds the partner's copy of it, so that in the
-    // end ps[0] holds the half's sum for list entry (lane & 31)
-#pragma unroll
-    for (int s = 16; s >= 1; s >>= 1) {
-        const bool up = (lane & s) != 0;
-#pragma unroll
-        for (int x = 0; x < s; ++x) {
-            const float keep = up ? ps[x + s] : ps[x];
-            const float give = up ? ps[x] : ps[x + s];
-            ps[x] = keep + __shfl_xor(give, s);
-        }
-    }
-    {
-        const int x = lane & 31, i = x >> 4, r = x & 15;
-        atomicAdd(&rsum[wm * TA::WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)], ps[0]);
-    }
-    __syncthreads();
-    if (threadIdx.x < rows) de[threadIdx.x] = rsum[threadIdx.x];
 }
 
 // deta = the sum of the column tiles' partials
@@ -1052,7 +1070,7 @@ static ttt_status validate_lin_bwd(const linattn_desc* D) {
 
 static size_t lin_bwd_ws_bytes(const linattn_desc& D) {
     if (D.N == 0) return 0;
-    const int64_t S = (int64_t)D.B * D.H, nc = cdiv(D.N, D.chunk), ntn = cdiv(D.d_v, kApplyCols);
+    const int64_t S = (int64_t)D.B * D.H, nc = cdiv(D.N, D.chunk), ntn = cdiv(D.d_k, kApplyCols);
     const size_t sb = align256((size_t)(S * nc * (int64_t)D.d_v * D.d_k * 4));
     return 3 * sb + (ntn > 1 ? align256((size_t)(ntn * S * D.N * 4)) : 0);
 }
@@ -1094,17 +1112,20 @@ static ttt_status run_lin_bwd(const linattn_desc& D, const uint32_t (&flags)[32]
         if ((rc = launch_scan<T>(D, nc, D.mask, all, dS, R, rio, 1, st)) != TTT_OK) return rc;
     if (D.N == 0) return TTT_OK;
     const int ntt = (int)cdiv(std::min<int64_t>(chunk, D.N), kApplyRows);
+    const int ntk = (int)cdiv(D.d_k, kApplyCols);  // column tiles of dq, dk (and deta partials)
+    float* de = ntk > 1 ? part : deta;
     BwdTArgs<T> ta{};
-    ta.job[0] = BwdTJob<T>{dO, Sc, dq, nullptr, 0};
-    ta.job[1] = BwdTJob<T>{v, R, dk, eta, 1};
+    ta.job[0] = BwdTJob<T>{dO, Sc, dq, nullptr, 0, nullptr, nullptr};
+    ta.job[1] = BwdTJob<T>{v, R, dk, eta, 1, k, de};
     ta.N = D.N;
+    ta.ntok = S * D.N;
     ta.dk = D.d_k;
     ta.dv = D.d_v;
     ta.chunk = (int)chunk;
     ta.nc = (int)nc;
     ta.ntt = ntt;
-    ta.ntn = (int)cdiv(D.d_k, kApplyCols);
-    ta.per_job = (int)(S * nc * ntt * ta.ntn);
+    ta.ntn = ntk;
+    ta.per_job = (int)(S * nc * ntt * ntk);
     ta.mode = D.mask;
     for (int w = 0; w < 32; ++w) ta.flags[w] = flags[w];
     {
@@ -1113,33 +1134,29 @@ static ttt_status run_lin_bwd(const linattn_desc& D, const uint32_t (&flags)[32]
     }
     if ((rc = check_launch("k_lin_bwd_t", st)) != TTT_OK) return rc;
     BwdNArgs<T> na{};
-    const int ntn = (int)cdiv(D.d_v, kApplyCols);
     na.k = k;
     na.R = R;
-    na.v = v;
     na.eta = eta;
     na.dv = dv;
-    na.deta = ntn > 1 ? part : deta;
     na.N = D.N;
-    na.ntok = S * D.N;
     na.dk = D.d_k;
     na.dvn = D.d_v;
     na.chunk = (int)chunk;
     na.nc = (int)nc;
     na.ntt = ntt;
-    na.ntn = ntn;
+    na.ntn = (int)cdiv(D.d_v, kApplyCols);
     na.mode = D.mask;
     for (int w = 0; w < 32; ++w) na.flags[w] = flags[w];
     {
         ProfScope ps(PK_LIN_BWD_N, st);
-        hipLaunchKernelGGL(k_lin_bwd_n<T>, dim3((unsigned)(S * nc * ntt * ntn)), dim3(kThreads), 0, st, na);
+        hipLaunchKernelGGL(k_lin_bwd_n<T>, dim3((unsigned)(S * nc * ntt * na.ntn)), dim3(kThreads), 0, st, na);
     }
     if ((rc = check_launch("k_lin_bwd_n", st)) != TTT_OK) return rc;
-    if (ntn > 1) {
+    if (ntk > 1) {
         {
             ProfScope ps(PK_LIN_DETA, st);
             hipLaunchKernelGGL(k_lin_deta_sum, dim3((unsigned)cdiv(S * D.N, kThreads)), dim3(kThreads), 0, st,
-                               (const float*)part, deta, S * D.N, ntn);
+                               (const float*)part, deta, S * D.N, ntk);
         }
         if ((rc = check_launch("k_lin_deta_sum", st)) != TTT_OK) return rc;
     }

@@ -85,10 +85,26 @@ template <> struct Pack4<uint16_t> {
         *reinterpret_cast<raw*>(p) = raw{(uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16),
                                          (uint32_t)f2bf(c) | ((uint32_t)f2bf(d) << 16)};
     }
+    // four elements as stored (load_raw), and as floats (unpack)
+    __device__ static raw load_raw(const uint16_t* p) { return *reinterpret_cast<const raw*>(p); }
+    __device__ static void unpack(const raw& r, float (&x)[4]) {
+        x[0] = bf2f((uint16_t)(r[0] & 0xFFFFu));
+        x[1] = bf2f((uint16_t)(r[0] >> 16));
+        x[2] = bf2f((uint16_t)(r[1] & 0xFFFFu));
+        x[3] = bf2f((uint16_t)(r[1] >> 16));
+    }
 };
 template <> struct Pack4<float> {
     __device__ static void store(float* p, float a, float b, float c, float d) {
         *reinterpret_cast<f32x4_t*>(p) = f32x4_t{a, b, c, d};
+    }
+    typedef f32x4_t raw;
+    __device__ static raw load_raw(const float* p) { return *reinterpret_cast<const raw*>(p); }
+    __device__ static void unpack(const raw& r, float (&x)[4]) {
+        x[0] = r[0];
+        x[1] = r[1];
+        x[2] = r[2];
+        x[3] = r[3];
     }
 };
 
