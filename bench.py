@@ -308,6 +308,7 @@ def main():
         # sliding-window attention: 4d FLOP per (query, key) pair inside the windows (algorithmic)
         "k_swa": ("mfma", 4 * d * B * H * (chunk * (chunk + 1) // 2 + (N - chunk) * chunk)),
         "k_swa_qprep": ("hbm", 2 * 2 * B * H * N * d),
+        "k_swa_vprep": ("hbm", 2 * 2 * B * H * N * d),
         # parallel form with Muon: every chunk's W2 update read and its momentum written (fp32)
         "k_par_momentum": ("hbm", 8 * dm * S * nchunks),
     }

@@ -257,7 +257,9 @@ ttt_status linattn_backward(const linattn_desc* desc, const void* q, const void*
  *               aligned; NULL means scale 1 or shift 0.  k_shift adds the same amount to every score
  *               of a query, which softmax removes: it does not change o and is not read.
  *   workspace   device buffer of at least swa_workspace_bytes(desc) bytes (it holds q * q_scale +
- *               q_shift, times k_scale), 256-byte aligned; it must not overlap q, k, v or o
+ *               q_shift, times k_scale, and for bf16 heads whose d is a multiple of 64 other than
+ *               320 also v rearranged in blocks of 32 keys), 256-byte aligned; it must not overlap
+ *               q, k, v or o
  * Scores, the softmax and the output accumulation are fp32; in bf16 mode the softmax weights are
  * rounded to bf16 before they multiply v.
  */
@@ -281,7 +283,7 @@ ttt_status swa_forward(const swa_desc* desc, const void* q, const void* k, const
  * read, and forgets them.  Kernel classes are numbered 0 .. TTT_PROF_KERNELS-1 and named by
  * ttt_profile_kernel_name.  Enabling or reading while another thread launches is allowed.
  */
-#define TTT_PROF_KERNELS 20
+#define TTT_PROF_KERNELS 21
 ttt_status ttt_profile_enable(int32_t on);
 /* Restricts the bracketing to the kernel classes i whose bit (1u << i) is set in mask; the
  * default is every class.  Each bracket records two events on the launch's stream, which costs

@@ -31,20 +31,45 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    """Compiles every HIP source into libttt.so (always rebuilds); returns the library path."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+# Extra flags per source.  The sliding-window kernel applies the softmax and its rescale to the
+# accumulators of its second product, so they belong in VGPRs: with the compiler's default placement
+# in AGPRs every key block moved hundreds of values between the two register files.
+EXTRA_FLAGS = {"swa.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form=1"]}
+
+
+def _run(cmd):
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
+    return r.returncode, err
+
+
+def build(verbose: bool = False) -> str:
+    """Compiles every HIP source (in parallel, each to an object) and links libttt.so (always
+    rebuilds); returns the library path."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    objdir = os.path.join(PKG, "_obj")
+    os.makedirs(objdir, exist_ok=True)
+    flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    jobs = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, src.replace(".hip", ".o"))
+        jobs.append((obj, [hipcc(), *flags, *EXTRA_FLAGS.get(src, []), "-I", INCLUDE, "-I", CSRC, "-c",
+                           os.path.join(CSRC, src), "-o", obj]))
+    with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1)) as ex:
+        results = list(ex.map(lambda j: _run(j[1]), jobs))
+    for (obj, cmd), (rc, err) in zip(jobs, results):
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        if rc != 0:
+            raise RuntimeError(f"hipcc failed ({rc}) on {os.path.basename(obj)}:\n{err}")
+        if verbose and err.strip():
+            print(err, file=sys.stderr)
+    tmp = LIB + ".tmp"
+    rc, err = _run([hipcc(), *HIPCC_FLAGS, *[o for o, _ in jobs], "-o", tmp])
+    if rc != 0:
+        raise RuntimeError(f"link failed ({rc}):\n{err}")
     os.replace(tmp, LIB)
     return LIB
 

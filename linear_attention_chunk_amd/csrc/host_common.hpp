@@ -25,7 +25,7 @@ inline ttt_status fail(ttt_status s, const char* fmt, ...) {
 // kernel classes of the optional launch profiler (ttt_profile_*)
 enum ProfKernel { PK_UP = 0, PK_DOWN, PK_UPDATE, PK_MUON_PREP, PK_NS_INIT, PK_NS_GRAM, PK_NS_STEP, PK_LINATTN,
                   PK_LIN_DELTA, PK_LIN_SCAN, PK_LIN_APPLY, PK_PHI, PK_W13, PK_ZERO, PK_PAR_MOM, PK_SWA,
-                  PK_SWA_PREP, PK_LIN_BWD_T, PK_LIN_BWD_N, PK_LIN_DETA };
+                  PK_SWA_PREP, PK_LIN_BWD_T, PK_LIN_BWD_N, PK_LIN_DETA, PK_SWA_VPREP };
 
 // Brackets one launch with events on its stream while profiling is enabled; no-op otherwise.
 struct ProfScope {

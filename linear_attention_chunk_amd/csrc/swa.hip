@@ -169,6 +169,276 @@ __global__ __launch_bounds__(64 * kSwaWaves, 1) void k_swa(SwaArgs<T> a) {
     }
 }
 
+// bf16 heads whose d is a multiple of 64: a walk with the queries resident in registers.  One
+// workgroup of 4 waves (one per SIMD, one workgroup per CU) takes 128 queries of one scan; wave w owns
+// queries 32w .. 32w+31 as two groups of 16 and keeps their q'' over all of d as 16 x 16 x 32 MFMA
+// fragments for the whole walk.  Per block of 32 keys:
+//   - the block's k rows are staged in LDS as they are, and its v block as prepared by k_swa_vprep
+//     (d-major, keys in the order below), in two alternating LDS buffers, so one workgroup barrier
+//     per block suffices;
+//   - each wave forms the transposed scores k q''^T of its 32 queries (keys on the accumulator
+//     rows), so a lane holds 8 keys of one query: the window mask (only on blocks at the window's
+//     edges), the query's maximum over the 4 lanes that hold it (lane swaps across rows and halves),
+//     and the online-softmax step, against a reference maximum that moves only when exceeded by more
+//     than kSwqTau (so the output rows are rarely rescaled; the row sums are kept per lane and
+//     reduced once at the end);
+//   - the lane's 8 weights, rounded to bf16, are its part of the B operand of O^T += v^T P^T.  That
+//     product contracts over the keys in the order the lane holds them: keys 4g .. 4g+3 and
+//     16+4g .. 16+4g+3 for lane group g, the order in which the prepared v block stores them, so a
+//     v fragment is one 16-byte LDS read and P never leaves the registers;
+//   - O^T's accumulators put each lane on its own query and 4 consecutive output columns, over the
+//     workgroup's DO columns: all of d, or for d = 384 one half (two workgroups per query block,
+//     each forming the scores: the accumulators of all 384 columns do not fit the registers).
+// The next block's k and v are loaded into registers while the current block is computed; the MFMA
+// accumulators are kept in VGPRs (build flag), since the softmax works on them with VALU code.
+constexpr int kSwqQ = 128, kSwqK = 32;
+constexpr float kSwqTau = 8.f;  // how far (in e-folds) a block's maximum may exceed the reference
+constexpr float kLog2e = 1.44269504088896341f;
+
+// two floats to a packed bf16 pair, round to nearest even (one instruction on gfx950)
+__device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){x, y}, b2));
+}
+// max / sum of x over lanes l, l ^ 16, l ^ 32, l ^ 48 (the 4 lanes that hold one query): swaps of
+// 16-lane rows and of 32-lane halves
+__device__ __forceinline__ float max4rows(float x) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum4rows(float x) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// The v blocks of every scan for the walk: block kb of scan s is d rows (columns of v) of 32 keys,
+// 64 bytes a row, the keys in the order 0-3, 16-19, 4-7, 20-23, 8-11, 24-27, 12-15, 28-31 (so the 16
+// bytes at 16 g hold keys 4g .. 4g+3 and 16+4g .. 16+4g+3); keys at or beyond N are zero.  One thread
+// takes 8 columns of one block: 32 loads of 16 bytes (one per key), 32 stores of 16 bytes.
+struct VPrepArgs {
+    const uint16_t* v; uint16_t* vp;
+    int64_t N, nkb, nthreads; int d;
+};
+
+__global__ __launch_bounds__(kThreads) void k_swa_vprep(VPrepArgs a) {
+    const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (t >= a.nthreads) return;
+    const int ncg = a.d / 8;
+    const int cg = (int)(t % ncg);
+    const int64_t blk = t / ncg, scan = blk / a.nkb, kb = blk % a.nkb;
+    const int64_t k0 = kb * kSwqK;
+    const uint16_t* src = a.v + (scan * a.N + k0) * a.d + cg * 8;
+    u32x4_t r[kSwqK];
+#pragma unroll
+    for (int k = 0; k < kSwqK; ++k) {
+        const bool in = k0 + k < a.N;  // rows past N read row k0 (in range) and are zeroed
+        r[k] = *reinterpret_cast<const u32x4_t*>(src + (int64_t)(in ? k : 0) * a.d);
+        if (!in) r[k] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+    uint16_t* dst = a.vp + (blk * a.d + cg * 8) * kSwqK;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        // element c of key k: half (c & 1) of word c >> 1
+        auto el = [&](int k) -> uint32_t { return (r[k][c >> 1] >> (16 * (c & 1))) & 0xFFFFu; };
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const u32x4_t w = {el(4 * g) | (el(4 * g + 1) << 16), el(4 * g + 2) | (el(4 * g + 3) << 16),
+                               el(16 + 4 * g) | (el(16 + 4 * g + 1) << 16), el(16 + 4 * g + 2) | (el(16 + 4 * g + 3) << 16)};
+            *reinterpret_cast<u32x4_t*>(dst + c * kSwqK + 8 * g) = w;
+        }
+    }
+}
+
+template <int D, int DO>
+__global__ __launch_bounds__(256, 1) void k_swa_qres(SwaArgs<uint16_t> a, const uint16_t* vp) {
+    using T = uint16_t;
+    constexpr int KP = 2 * D + 16;              // bytes per staged k row
+    constexpr int VP = 2 * kSwqK + 16;          // bytes per staged v row (one column of v)
+    constexpr int NQF = D / 32, NOB = DO / 16;  // q'' fragments per query group, 16-column output blocks
+    constexpr int KPER = kSwqK * D / 8 / 256, VPR = D / 8;
+    constexpr int VPER = DO * 4 / 256;          // 16-byte vectors of the v block per thread
+    static_assert(kSwqK * D / 8 % 256 == 0 && DO * 4 % 256 == 0, "whole rounds");
+    constexpr int K_BYTES = kSwqK * KP, V_BYTES = DO * VP, BUF = K_BYTES + V_BYTES;
+    __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
+
+    const int lb = xcd_block(gridDim.x);
+    const int cb = lb % a.ncb, scan = lb / a.ncb / a.nqb, qb = lb / a.ncb % a.nqb;
+    const int c0 = cb * DO;  // this workgroup's output columns [c0, c0 + DO)
+    const int64_t q0 = (int64_t)qb * kSwqQ;
+    const int nq = (int)std::min<int64_t>(kSwqQ, a.N - q0);
+    const int64_t base = (int64_t)scan * a.N;
+    const int64_t nkb = (a.N + kSwqK - 1) / kSwqK;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    // the lane's query in group g is 32 wave + 16 g + lr; element i of its 16 x 16 score block j
+    // is key 16 j + 4 lg + i of the block
+
+    u32x4_t qf[2][NQF];  // B fragments: query 32 wave + 16 g + lr, d = 32 s + 8 lg .. + 7
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+        const int row = 32 * wave + 16 * g + lr;
+        const T* src = a.q2 + (base + q0 + (row < nq ? row : 0)) * D + lg * 8;
+#pragma unroll
+        for (int s = 0; s < NQF; ++s) {
+            qf[g][s] = *reinterpret_cast<const u32x4_t*>(src + s * 32);
+            if (row >= nq) qf[g][s] = u32x4_t{0u, 0u, 0u, 0u};
+        }
+    }
+    // key blocks that meet the window of some query of this block
+    const int64_t kfirst = std::max<int64_t>(0, q0 - a.window + 1), klast = q0 + nq - 1;
+    const int64_t kstart = (kfirst / kSwqK) * kSwqK;
+    const int nblk = (int)((klast - kstart) / kSwqK) + 1;
+    const float sc = a.inv_sqrt_d * kLog2e;  // base-2 units
+    const float tau = kSwqTau / a.inv_sqrt_d;  // the threshold in raw score units
+
+    u32x4_t kr[KPER], vr[VPER];
+    uint32_t kok = 0;
+    auto load_kv = [&](int64_t k0) {
+        const int nk = (int)std::min<int64_t>(kSwqK, a.N - k0);
+        kok = 0;
+#pragma unroll
+        for (int i = 0; i < KPER; ++i) {
+            const int v = threadIdx.x + i * 256, row = v / VPR, c = v % VPR;
+            const bool in = row < nk;
+            kr[i] = *reinterpret_cast<const u32x4_t*>(a.k + (base + k0 + (in ? row : 0)) * D + c * 8);
+            kok |= (uint32_t)in << i;
+        }
+        const T* vb = vp + ((scan * nkb + k0 / kSwqK) * D + c0) * kSwqK;
+#pragma unroll
+        for (int i = 0; i < VPER; ++i) vr[i] = *reinterpret_cast<const u32x4_t*>(vb + (threadIdx.x + i * 256) * 8);
+    };
+
+    float m[2], lp[2];   // per query: reference maximum (raw score units) and this lane's row-sum part
+    f32x4_t o[2][NOB];   // O^T: element i of block jd is column 16 jd + 4 lg + i of the lane's query
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+        m[g] = -INFINITY;
+        lp[g] = 0.f;
+#pragma unroll
+        for (int j = 0; j < NOB; ++j) o[g][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+    load_kv(kstart);
+    for (int b = 0; b < nblk; ++b) {
+        const int64_t k0 = kstart + (int64_t)b * kSwqK;
+        const int nk = (int)std::min<int64_t>(kSwqK, a.N - k0);
+        char* Ks = smem + (b & 1) * BUF;
+        char* Vs = Ks + K_BYTES;
+        // this buffer was last read two blocks ago, before every wave passed the previous barrier
+#pragma unroll
+        for (int i = 0; i < KPER; ++i) {
+            const int v = threadIdx.x + i * 256, row = v / VPR, c = v % VPR;
+            *reinterpret_cast<u32x4_t*>(Ks + row * KP + c * 16) = ((kok >> i) & 1u) ? kr[i] : u32x4_t{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int i = 0; i < VPER; ++i) {
+            const int v = threadIdx.x + i * 256;
+            *reinterpret_cast<u32x4_t*>(Vs + (v >> 2) * VP + (v & 3) * 16) = vr[i];
+        }
+        if (b + 1 < nblk) load_kv(k0 + kSwqK);
+        lds_barrier();  // the block is staged
+        // transposed scores: A = the block's k rows, B = the queries' q''
+        f32x4_t sacc[2][2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int g = 0; g < 2; ++g) sacc[j][g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int s = 0; s < NQF; ++s)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(Ks + (j * 16 + lr) * KP + s * 64 + lg * 16);
+                Elt<T>::mma(sacc[j][0], kf, qf[0][s]);
+                Elt<T>::mma(sacc[j][1], kf, qf[1][s]);
+            }
+        __builtin_amdgcn_s_setprio(0);
+        // a block inside every query's window (and before N) needs no mask; the test is uniform
+        const bool inside = k0 + kSwqK - 1 <= q0 && q0 + nq - 1 - k0 < a.window && nk == kSwqK;
+        if (!inside) {
+            const int dq = (int)(q0 - k0);
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                const int qr = dq + 32 * wave + 16 * g + lr;  // the lane's query, relative to k0
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int kc = 16 * j + 4 * lg + i;
+                        if (!(kc <= qr && qr - kc < a.window && kc < nk)) sacc[j][g][i] = -INFINITY;
+                    }
+            }
+        }
+        float alpha[2];
+        bool resc = false;
+        u32x4_t pk[2];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            float mx = fmaxf(fmaxf(fmaxf(sacc[0][g][0], sacc[0][g][1]), fmaxf(sacc[0][g][2], sacc[0][g][3])),
+                             fmaxf(fmaxf(sacc[1][g][0], sacc[1][g][1]), fmaxf(sacc[1][g][2], sacc[1][g][3])));
+            mx = max4rows(mx);
+            // a query that has seen no key yet (reference -inf) has nothing to rescale; one with no key
+            // in this block keeps its reference, and its weights stay 0
+            const float mref = m[g];
+            const float mn = mref == -INFINITY || mx > mref + tau ? mx : mref;
+            alpha[g] = mref == -INFINITY || mn == mref ? 1.f : __builtin_amdgcn_exp2f((mref - mn) * sc);
+            resc = resc || alpha[g] != 1.f;
+            m[g] = mn;
+            // p = 2^((s - m) sc); masked scores are -inf and give 0 (a reference still at -inf means
+            // every score of the query is -inf so far: subtracting 0 keeps them -inf)
+            const float off = mn == -INFINITY ? 0.f : -mn * sc;
+            float pw[8];
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pw[4 * j + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j][g][i], sc, off));
+            float ps = 0.f;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const uint32_t w2 = pack_bf16x2(pw[2 * x], pw[2 * x + 1]);
+                pk[g][x] = w2;
+                ps += __uint_as_float(w2 << 16) + __uint_as_float(w2 & 0xFFFF0000u);  // the rounded weights
+            }
+            lp[g] = lp[g] * alpha[g] + ps;
+        }
+        if (__any(resc)) {
+#pragma unroll
+            for (int g = 0; g < 2; ++g)
+#pragma unroll
+                for (int j = 0; j < NOB; ++j)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) o[g][j][i] *= alpha[g];
+        }
+        // O^T += v^T P^T
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int jd = 0; jd < NOB; ++jd) {
+            const u32x4_t vf = *reinterpret_cast<const u32x4_t*>(Vs + (16 * jd + lr) * VP + 16 * lg);
+            Elt<T>::mma(o[0][jd], vf, pk[0]);
+            Elt<T>::mma(o[1][jd], vf, pk[1]);
+        }
+        __builtin_amdgcn_s_setprio(0);
+    }
+    // O = acc / (row sum) for the lane's query if below nq: 4 consecutive columns per store
+    T* O = a.o + (base + q0) * D + c0;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+        const float inv = 1.f / sum4rows(lp[g]);
+        const int row = 32 * wave + 16 * g + lr;
+        if (row < nq) {
+#pragma unroll
+            for (int jd = 0; jd < NOB; ++jd)
+                Pack4<T>::store(O + (uint32_t)row * (uint32_t)D + (uint32_t)(16 * jd + 4 * lg), o[g][jd][0] * inv,
+                                o[g][jd][1] * inv, o[g][jd][2] * inv, o[g][jd][3] * inv);
+        }
+    }
+}
+
 // q'' = (q * gamma_q + beta_q) * gamma_k per channel, four elements per thread; the parameters are
 // per head [H][d] (null: scale 1, shift 0)
 template <typename T> struct QPrepArgs {
@@ -208,9 +478,14 @@ static ttt_status validate_swa(const swa_desc* D) {
     return TTT_OK;
 }
 
+// bf16 heads on the query-resident walk (d a multiple of 64 other than 320)
+static bool swa_qres(const swa_desc& D) { return D.io_dtype == TTT_BF16 && D.d % 64 == 0 && D.d != 320; }
+
 static size_t swa_ws_bytes(const swa_desc& D) {
     const size_t es = D.io_dtype == TTT_BF16 ? 2 : 4;
-    return (size_t)D.B * D.H * D.N * D.d * es;  // q''
+    size_t n = align256((size_t)D.B * D.H * D.N * D.d * es);  // q''
+    if (swa_qres(D)) n += (size_t)D.B * D.H * cdiv(D.N, kSwqK) * kSwqK * D.d * 2;  // prepared v blocks
+    return n;
 }
 
 template <typename T, int DV>
@@ -238,6 +513,30 @@ static ttt_status run_swa(const swa_desc& D, const T* q, const T* k, const T* v,
     // output columns per workgroup: as many as fit the registers beside the scores (bf16: 256, or
     // 192 in two workgroups for wider heads; fp32: 128)
     if constexpr (sizeof(T) == 2) {
+        if (swa_qres(D)) {  // queries resident in registers
+            T* vp = (T*)(ws + align256((size_t)S * D.N * D.d * 2));
+            VPrepArgs va{v, vp, D.N, cdiv(D.N, kSwqK), 0, D.d};
+            va.nthreads = S * va.nkb * (D.d / 8);
+            {
+                ProfScope ps(PK_SWA_VPREP, st);
+                hipLaunchKernelGGL(k_swa_vprep, dim3((unsigned)cdiv(va.nthreads, kThreads)), dim3(kThreads), 0, st, va);
+            }
+            if ((rc = check_launch("k_swa_vprep", st)) != TTT_OK) return rc;
+            a.nqb = (int)cdiv(D.N, kSwqQ);
+            a.ncb = D.d == 384 ? 2 : 1;
+            const unsigned grid = (unsigned)(S * a.nqb * a.ncb);
+            {
+                ProfScope ps(PK_SWA, st);
+                switch (D.d) {
+                    case 64: hipLaunchKernelGGL((k_swa_qres<64, 64>), dim3(grid), dim3(256), 0, st, a, vp); break;
+                    case 128: hipLaunchKernelGGL((k_swa_qres<128, 128>), dim3(grid), dim3(256), 0, st, a, vp); break;
+                    case 192: hipLaunchKernelGGL((k_swa_qres<192, 192>), dim3(grid), dim3(256), 0, st, a, vp); break;
+                    case 256: hipLaunchKernelGGL((k_swa_qres<256, 256>), dim3(grid), dim3(256), 0, st, a, vp); break;
+                    default: hipLaunchKernelGGL((k_swa_qres<384, 192>), dim3(grid), dim3(256), 0, st, a, vp); break;
+                }
+            }
+            return check_launch("k_swa_qres", st);
+        }
         if (D.d <= 128) return launch_swa<T, 128>(a, S * a.nqb, st);
         if (D.d <= 256) return launch_swa<T, 256>(a, S * a.nqb, st);
         a.ncb = (int)cdiv(D.d, 192);

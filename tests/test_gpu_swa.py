@@ -62,6 +62,32 @@ def test_wide_heads_fp32(d):
     run(6, 1, 1, 260, d, 130, False)
 
 
+@pytest.mark.parametrize("d", [64, 128, 192])
+def test_mid_widths_bf16(d):
+    # several 128-query blocks (the last ragged) and windows over many 32-key blocks
+    run(10, 1, 2, 500, d, 300, True)
+
+
+@pytest.mark.parametrize("d", [128, 384])
+def test_growing_scores_bf16(d):
+    """Scores that rise along the sequence (keys along one direction with a growing length), so a
+    query's running maximum keeps jumping by several units from one key block to the next: the
+    kernel's rescale of the output rows runs many times."""
+    N, w = 600, 400
+    say(f"swa growing scores N{N} d{d} window {w}")
+    rng = np.random.default_rng(11 + d)
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    q = np.sqrt(d) * u[None, :] + 0.1 * rng.standard_normal((N, d))
+    k = (np.arange(N) / 8.0)[:, None] * u[None, :] + 0.1 * rng.standard_normal((N, d))
+    v = rng.standard_normal((N, d)) / np.sqrt(d)
+    q, k, v = (synth.round_to_bf16(x.astype(np.float32))[None, None] for x in (q, k, v))
+    o = T.swa_forward(dev(q, torch.bfloat16), dev(k, torch.bfloat16), dev(v, torch.bfloat16), w)
+    torch.cuda.synchronize()
+    o_ref = O.swa_forward_ref(q, k, v, w)
+    assert_close(host(o), o_ref, TOL[True], "o", 256)
+
+
 def test_lact_lm_shape_sampled():
     """B8 H4 N32768 d384, window = chunk = 2048 (the LaCT language-model layer's local branch); two
     (batch, head) slices from the seeded generator, the rest from torch's seeded device generator."""
