@@ -256,10 +256,10 @@ ttt_status linattn_backward(const linattn_desc* desc, const void* q, const void*
  *   q_scale, q_shift, k_scale, k_shift   [H][d] fp32 per-head, per-channel parameters, 16-byte
  *               aligned; NULL means scale 1 or shift 0.  k_shift adds the same amount to every score
  *               of a query, which softmax removes: it does not change o and is not read.
- *   workspace   device buffer of at least swa_workspace_bytes(desc) bytes (it holds q * q_scale +
- *               q_shift, times k_scale, and for bf16 heads whose d is a multiple of 64 other than
- *               320 also v rearranged in blocks of 32 keys), 256-byte aligned; it must not overlap
- *               q, k, v or o
+ *   workspace   device buffer of at least swa_workspace_bytes(desc) bytes, 256-byte aligned, not
+ *               overlapping q, k, v or o: for bf16 heads whose d is a multiple of 64 other than 320
+ *               it holds v rearranged in blocks of 32 keys, otherwise q * q_scale + q_shift, times
+ *               k_scale
  * Scores, the softmax and the output accumulation are fp32; in bf16 mode the softmax weights are
  * rounded to bf16 before they multiply v.
  */

@@ -186,11 +186,11 @@ __global__ __launch_bounds__(64 * kSwaWaves, 1) void k_swa(SwaArgs<T> a) {
 //     product contracts over the keys in the order the lane holds them: keys 4g .. 4g+3 and
 //     16+4g .. 16+4g+3 for lane group g, the order in which the prepared v block stores them, so a
 //     v fragment is one 16-byte LDS read and P never leaves the registers;
-//   - O^T's accumulators put each lane on its own query and 4 consecutive output columns, over the
-//     workgroup's DO columns: all of d, or for d = 384 one half (two workgroups per query block,
-//     each forming the scores: the accumulators of all 384 columns do not fit the registers).
-// The next block's k and v are loaded into registers while the current block is computed; the MFMA
-// accumulators are kept in VGPRs (build flag), since the softmax works on them with VALU code.
+//   - O^T's accumulators put each lane on its own query and 4 consecutive output columns of d.
+// q'' is formed from q and the per-channel parameters as the fragments are loaded (fp32, rounded to
+// bf16 once).  The next block's k and v are loaded into registers while the current block is
+// computed; the MFMA accumulators are kept in VGPRs (build flag), since the softmax works on them
+// with VALU code.
 constexpr int kSwqQ = 128, kSwqK = 32;
 constexpr float kSwqTau = 8.f;  // how far (in e-folds) a block's maximum may exceed the reference
 constexpr float kLog2e = 1.44269504088896341f;
@@ -254,21 +254,27 @@ __global__ __launch_bounds__(kThreads) void k_swa_vprep(VPrepArgs a) {
     }
 }
 
-template <int D, int DO>
-__global__ __launch_bounds__(256, 1) void k_swa_qres(SwaArgs<uint16_t> a, const uint16_t* vp) {
+struct QresArgs {
+    const uint16_t* q; const uint16_t* k; const uint16_t* vp; uint16_t* o;
+    const float* qs; const float* qb; const float* ks;  // [H][d] or null
+    int64_t N; int H, window, nqb;
+    float inv_sqrt_d;
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void k_swa_qres(QresArgs a) {
     using T = uint16_t;
-    constexpr int KP = 2 * D + 16;              // bytes per staged k row
-    constexpr int VP = 2 * kSwqK + 16;          // bytes per staged v row (one column of v)
-    constexpr int NQF = D / 32, NOB = DO / 16;  // q'' fragments per query group, 16-column output blocks
+    constexpr int KP = 2 * D + 16;             // bytes per staged k row
+    constexpr int VP = 2 * kSwqK + 16;         // bytes per staged v row (one column of v)
+    constexpr int NQF = D / 32, NOB = D / 16;  // q'' fragments per query group, 16-column output blocks
     constexpr int KPER = kSwqK * D / 8 / 256, VPR = D / 8;
-    constexpr int VPER = DO * 4 / 256;          // 16-byte vectors of the v block per thread
-    static_assert(kSwqK * D / 8 % 256 == 0 && DO * 4 % 256 == 0, "whole rounds");
-    constexpr int K_BYTES = kSwqK * KP, V_BYTES = DO * VP, BUF = K_BYTES + V_BYTES;
+    constexpr int VPER = D * 4 / 256;          // 16-byte vectors of the v block per thread
+    static_assert(kSwqK * D / 8 % 256 == 0 && D * 4 % 256 == 0, "whole rounds");
+    constexpr int K_BYTES = kSwqK * KP, V_BYTES = D * VP, BUF = K_BYTES + V_BYTES;
     __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
 
     const int lb = xcd_block(gridDim.x);
-    const int cb = lb % a.ncb, scan = lb / a.ncb / a.nqb, qb = lb / a.ncb % a.nqb;
-    const int c0 = cb * DO;  // this workgroup's output columns [c0, c0 + DO)
+    const int scan = lb / a.nqb, qb = lb % a.nqb;
     const int64_t q0 = (int64_t)qb * kSwqQ;
     const int nq = (int)std::min<int64_t>(kSwqQ, a.N - q0);
     const int64_t base = (int64_t)scan * a.N;
@@ -278,15 +284,37 @@ __global__ __launch_bounds__(256, 1) void k_swa_qres(SwaArgs<uint16_t> a, const 
     // the lane's query in group g is 32 wave + 16 g + lr; element i of its 16 x 16 score block j
     // is key 16 j + 4 lg + i of the block
 
-    u32x4_t qf[2][NQF];  // B fragments: query 32 wave + 16 g + lr, d = 32 s + 8 lg .. + 7
+    // B fragments: query 32 wave + 16 g + lr, d = 32 s + 8 lg .. + 7 of q'' = (q * q_scale + q_shift)
+    // * k_scale, formed in fp32 and rounded to bf16 once
+    u32x4_t qf[2][NQF];
+    {
+        const int h = scan % a.H;
+        const float* qs = a.qs ? a.qs + h * D + lg * 8 : nullptr;
+        const float* qbs = a.qb ? a.qb + h * D + lg * 8 : nullptr;
+        const float* ks = a.ks ? a.ks + h * D + lg * 8 : nullptr;
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-        const int row = 32 * wave + 16 * g + lr;
-        const T* src = a.q2 + (base + q0 + (row < nq ? row : 0)) * D + lg * 8;
+        for (int g = 0; g < 2; ++g) {
+            const int row = 32 * wave + 16 * g + lr;
+            const T* src = a.q + (base + q0 + (row < nq ? row : 0)) * D + lg * 8;
 #pragma unroll
-        for (int s = 0; s < NQF; ++s) {
-            qf[g][s] = *reinterpret_cast<const u32x4_t*>(src + s * 32);
-            if (row >= nq) qf[g][s] = u32x4_t{0u, 0u, 0u, 0u};
+            for (int s = 0; s < NQF; ++s) {
+                const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(src + s * 32);
+                float y[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[e] = __uint_as_float(e & 1 ? raw[e >> 1] & 0xFFFF0000u : raw[e >> 1] << 16);
+                if (qs)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) y[e] *= qs[s * 32 + e];
+                if (qbs)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) y[e] += qbs[s * 32 + e];
+                if (ks)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) y[e] *= ks[s * 32 + e];
+                qf[g][s] = row < nq ? u32x4_t{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
+                                              pack_bf16x2(y[6], y[7])}
+                                    : u32x4_t{0u, 0u, 0u, 0u};
+            }
         }
     }
     // key blocks that meet the window of some query of this block
@@ -308,7 +336,7 @@ __global__ __launch_bounds__(256, 1) void k_swa_qres(SwaArgs<uint16_t> a, const 
             kr[i] = *reinterpret_cast<const u32x4_t*>(a.k + (base + k0 + (in ? row : 0)) * D + c * 8);
             kok |= (uint32_t)in << i;
         }
-        const T* vb = vp + ((scan * nkb + k0 / kSwqK) * D + c0) * kSwqK;
+        const T* vb = a.vp + (scan * nkb + k0 / kSwqK) * D * kSwqK;
 #pragma unroll
         for (int i = 0; i < VPER; ++i) vr[i] = *reinterpret_cast<const u32x4_t*>(vb + (threadIdx.x + i * 256) * 8);
     };
@@ -425,7 +453,7 @@ __global__ __launch_bounds__(256, 1) void k_swa_qres(SwaArgs<uint16_t> a, const 
         __builtin_amdgcn_s_setprio(0);
     }
     // O = acc / (row sum) for the lane's query if below nq: 4 consecutive columns per store
-    T* O = a.o + (base + q0) * D + c0;
+    T* O = a.o + (base + q0) * D;
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
         const float inv = 1.f / sum4rows(lp[g]);
@@ -482,10 +510,9 @@ static ttt_status validate_swa(const swa_desc* D) {
 static bool swa_qres(const swa_desc& D) { return D.io_dtype == TTT_BF16 && D.d % 64 == 0 && D.d != 320; }
 
 static size_t swa_ws_bytes(const swa_desc& D) {
+    if (swa_qres(D)) return (size_t)D.B * D.H * cdiv(D.N, kSwqK) * kSwqK * D.d * 2;  // prepared v blocks
     const size_t es = D.io_dtype == TTT_BF16 ? 2 : 4;
-    size_t n = align256((size_t)D.B * D.H * D.N * D.d * es);  // q''
-    if (swa_qres(D)) n += (size_t)D.B * D.H * cdiv(D.N, kSwqK) * kSwqK * D.d * 2;  // prepared v blocks
-    return n;
+    return (size_t)D.B * D.H * D.N * D.d * es;  // q''
 }
 
 template <typename T, int DV>
@@ -501,20 +528,10 @@ template <typename T>
 static ttt_status run_swa(const swa_desc& D, const T* q, const T* k, const T* v, const float* qs, const float* qb,
                           const float* ks, T* o, char* ws, hipStream_t st) {
     const int64_t S = (int64_t)D.B * D.H;
-    T* q2 = (T*)ws;
-    QPrepArgs<T> pa{q, q2, qs, qb, ks, S * D.N * D.d / 4, D.d, D.H, D.N};
-    {
-        ProfScope ps(PK_SWA_PREP, st);
-        hipLaunchKernelGGL(k_swa_qprep<T>, dim3((unsigned)cdiv(pa.n4, kThreads)), dim3(kThreads), 0, st, pa);
-    }
-    ttt_status rc = check_launch("k_swa_qprep", st);
-    if (rc != TTT_OK) return rc;
-    SwaArgs<T> a{q2, k, v, o, D.N, D.d, D.window, (int)cdiv(D.N, kSwaRows), 1, 1.0f / sqrtf((float)D.d)};
-    // output columns per workgroup: as many as fit the registers beside the scores (bf16: 256, or
-    // 192 in two workgroups for wider heads; fp32: 128)
+    ttt_status rc;
     if constexpr (sizeof(T) == 2) {
-        if (swa_qres(D)) {  // queries resident in registers
-            T* vp = (T*)(ws + align256((size_t)S * D.N * D.d * 2));
+        if (swa_qres(D)) {  // queries resident in registers, v prepared in blocks of 32 keys
+            T* vp = (T*)ws;
             VPrepArgs va{v, vp, D.N, cdiv(D.N, kSwqK), 0, D.d};
             va.nthreads = S * va.nkb * (D.d / 8);
             {
@@ -522,21 +539,32 @@ static ttt_status run_swa(const swa_desc& D, const T* q, const T* k, const T* v,
                 hipLaunchKernelGGL(k_swa_vprep, dim3((unsigned)cdiv(va.nthreads, kThreads)), dim3(kThreads), 0, st, va);
             }
             if ((rc = check_launch("k_swa_vprep", st)) != TTT_OK) return rc;
-            a.nqb = (int)cdiv(D.N, kSwqQ);
-            a.ncb = D.d == 384 ? 2 : 1;
-            const unsigned grid = (unsigned)(S * a.nqb * a.ncb);
+            QresArgs a{q, k, vp, o, qs, qb, ks, D.N, D.H, D.window, (int)cdiv(D.N, kSwqQ), 1.0f / sqrtf((float)D.d)};
+            const unsigned grid = (unsigned)(S * a.nqb);
             {
                 ProfScope ps(PK_SWA, st);
                 switch (D.d) {
-                    case 64: hipLaunchKernelGGL((k_swa_qres<64, 64>), dim3(grid), dim3(256), 0, st, a, vp); break;
-                    case 128: hipLaunchKernelGGL((k_swa_qres<128, 128>), dim3(grid), dim3(256), 0, st, a, vp); break;
-                    case 192: hipLaunchKernelGGL((k_swa_qres<192, 192>), dim3(grid), dim3(256), 0, st, a, vp); break;
-                    case 256: hipLaunchKernelGGL((k_swa_qres<256, 256>), dim3(grid), dim3(256), 0, st, a, vp); break;
-                    default: hipLaunchKernelGGL((k_swa_qres<384, 192>), dim3(grid), dim3(256), 0, st, a, vp); break;
+                    case 64: hipLaunchKernelGGL(k_swa_qres<64>, dim3(grid), dim3(256), 0, st, a); break;
+                    case 128: hipLaunchKernelGGL(k_swa_qres<128>, dim3(grid), dim3(256), 0, st, a); break;
+                    case 192: hipLaunchKernelGGL(k_swa_qres<192>, dim3(grid), dim3(256), 0, st, a); break;
+                    case 256: hipLaunchKernelGGL(k_swa_qres<256>, dim3(grid), dim3(256), 0, st, a); break;
+                    default: hipLaunchKernelGGL(k_swa_qres<384>, dim3(grid), dim3(256), 0, st, a); break;
                 }
             }
             return check_launch("k_swa_qres", st);
         }
+    }
+    T* q2 = (T*)ws;
+    QPrepArgs<T> pa{q, q2, qs, qb, ks, S * D.N * D.d / 4, D.d, D.H, D.N};
+    {
+        ProfScope ps(PK_SWA_PREP, st);
+        hipLaunchKernelGGL(k_swa_qprep<T>, dim3((unsigned)cdiv(pa.n4, kThreads)), dim3(kThreads), 0, st, pa);
+    }
+    if ((rc = check_launch("k_swa_qprep", st)) != TTT_OK) return rc;
+    SwaArgs<T> a{q2, k, v, o, D.N, D.d, D.window, (int)cdiv(D.N, kSwaRows), 1, 1.0f / sqrtf((float)D.d)};
+    // output columns per workgroup: as many as fit the registers beside the scores (bf16: 256, or
+    // 192 in two workgroups for wider heads; fp32: 128)
+    if constexpr (sizeof(T) == 2) {
         if (D.d <= 128) return launch_swa<T, 128>(a, S * a.nqb, st);
         if (D.d <= 256) return launch_swa<T, 256>(a, S * a.nqb, st);
         a.ncb = (int)cdiv(D.d, 192);

@@ -290,11 +290,13 @@ def test_swa_validation_and_workspace(kw, status):
     D = swa_desc(**kw)
     assert L.swa_workspace_bytes(ctypes.byref(D), ctypes.byref(n)) == status
     if status == C.TTT_OK:
-        # the transformed queries in the io dtype (256-byte rounded), and for bf16 heads with d a
-        # multiple of 64 (not 320) the v blocks of 32 keys that the query-resident walk reads
-        q2 = -(-D.B * D.H * D.N * D.d * 2 // 256) * 256
-        vp = D.B * D.H * -(-D.N // 32) * 32 * D.d * 2 if D.io_dtype == C.TTT_BF16 and D.d % 64 == 0 and D.d != 320 else 0
-        assert n.value == q2 + vp
+        # bf16 heads with d a multiple of 64 (not 320): the v blocks of 32 keys that the query-resident
+        # walk reads; otherwise the transformed queries in the io dtype
+        es = 2 if D.io_dtype == C.TTT_BF16 else 4
+        if D.io_dtype == C.TTT_BF16 and D.d % 64 == 0 and D.d != 320:
+            assert n.value == D.B * D.H * -(-D.N // 32) * 32 * D.d * 2
+        else:
+            assert n.value == D.B * D.H * D.N * D.d * es
 
 
 def test_swa_forward_rejects_before_enqueueing():
