@@ -33,10 +33,10 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 # taken on.  They are reported only while those sources are unchanged.
 TRAFFIC_SOURCES = ("linear_attention_chunk_amd/csrc/ttt_layer.hip", "linear_attention_chunk_amd/csrc/tile.hpp")
 MEASURED_TRAFFIC = {
-    "source_sha": "81c250e6844b1fe6",
-    "k_up": {"read": 293.6e6, "write": 428.7e6},
-    "k_down": {"read": 570.4e6, "write": 164.0e6},
-    "k_update": {"read": 214.6e6, "write": 177.7e6},
+    "source_sha": "a5ab7c3f7247e400",
+    "k_up": {"read": 337.0e6, "write": 497.8e6},
+    "k_down": {"read": 572.7e6, "write": 163.9e6},
+    "k_update": {"read": 214.5e6, "write": 177.7e6},
 }
 
 
@@ -540,8 +540,8 @@ def main():
             "ms_per_call": round(msw, 3), "tokens_per_s": round(tokens / (msw * 1e-3)),
             "algorithmic_tflop": round(fsw / 1e12, 3),
             "mfma_frac": round(fsw / (msw * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-            "note": "d = 384 runs as two 192-column workgroups per query block, each computing the scores: "
-                    "1.5x the algorithmic FLOPs are executed"}
+            "note": "query-resident walk (one workgroup of 128 queries per CU, keys in blocks of 32) after "
+                    "a pass that rearranges v; the executed FLOPs are the algorithmic ones"}
         del wsw
         extras["lact_lm_variant2_muon"] = {
             "workload": f"B{B} H{H} N{N} d{d} m{m} chunk {chunk} bf16, apply-then-update, only W2 learns, "
