@@ -76,6 +76,26 @@ static void run_lin(linattn_desc D) {
                                    need, nullptr);
     check_message(f);
     if (s == TTT_OK && (int64_t)D.B * D.H > 0) EXPECT(f == TTT_ERR_DEVICE || f == TTT_ERR_INVALID_ARGUMENT);
+    // the backward: its own validation (chunked masks only), then the same buffer check
+    size_t bneed = 0;
+    ttt_status bs = linattn_backward_workspace_bytes(&D, &bneed);
+    check_message(bs);
+    if (s != TTT_OK) EXPECT(bs != TTT_OK);
+    if (D.mask == TTT_MASK_TOKEN_CAUSAL && s == TTT_OK) EXPECT(bs == TTT_ERR_UNSUPPORTED);
+    ttt_status bf = linattn_backward(&D, (const void*)P, (const void*)(P + (1ull << 36)), (const void*)(P + (2ull << 36)),
+                                     (const float*)(P + (3ull << 36)), nullptr, (const void*)(P + (4ull << 36)), nullptr,
+                                     (void*)(P + (5ull << 36)), (void*)(P + (6ull << 36)), (void*)(P + (7ull << 36)),
+                                     (float*)(P + (9ull << 36)), nullptr, (void*)(P + (10ull << 36)), bneed, nullptr);
+    check_message(bf);
+    // (N = 0 with no dS0 asked for has nothing to do)
+    if (bs == TTT_OK && (int64_t)D.B * D.H > 0)
+        EXPECT(D.N == 0 ? bf == TTT_OK : (bf == TTT_ERR_DEVICE || bf == TTT_ERR_INVALID_ARGUMENT));
+    if (bs == TTT_OK && (int64_t)D.B * D.H > 0 && bneed > 0)
+        EXPECT(linattn_backward(&D, (const void*)P, (const void*)(P + (1ull << 36)), (const void*)(P + (2ull << 36)),
+                                (const float*)(P + (3ull << 36)), nullptr, (const void*)(P + (4ull << 36)), nullptr,
+                                (void*)(P + (5ull << 36)), (void*)(P + (6ull << 36)), (void*)(P + (7ull << 36)),
+                                (float*)(P + (9ull << 36)), nullptr, (void*)(P + (10ull << 36)), bneed - 1,
+                                nullptr) == TTT_ERR_WORKSPACE);
 }
 
 static ttt_desc base_desc() {
@@ -102,6 +122,8 @@ int main() {
     EXPECT(linattn_workspace_bytes(nullptr, nullptr) == TTT_ERR_INVALID_ARGUMENT);
     EXPECT(ttt_forward(nullptr, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, nullptr) == TTT_ERR_INVALID_ARGUMENT);
     EXPECT(linattn_forward(nullptr, 0, 0, 0, 0, 0, 0, 0, 0, 0, nullptr) == TTT_ERR_INVALID_ARGUMENT);
+    EXPECT(linattn_backward_workspace_bytes(nullptr, nullptr) == TTT_ERR_INVALID_ARGUMENT);
+    EXPECT(linattn_backward(nullptr, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, nullptr) == TTT_ERR_INVALID_ARGUMENT);
 
     // the profiler's host side: names, selection, a read with nothing recorded, bad sizes
     for (int i = -2; i < TTT_PROF_KERNELS + 2; ++i) EXPECT(ttt_profile_kernel_name(i) != nullptr);

@@ -222,6 +222,54 @@ def test_linattn_workspace_choice_and_rejects():
     assert L.linattn_forward(ctypes.byref(D), *args, P16 + (1 << 34) + 16, need, None) == C.TTT_ERR_INVALID_ARGUMENT
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(), C.TTT_OK), (dict(mask=C.MASK_UPDATE_THEN_APPLY, chunk=1), C.TTT_OK), (dict(mask=C.MASK_FULL, chunk=128), C.TTT_OK),
+    (dict(mask=C.MASK_TOKEN_CAUSAL), C.TTT_ERR_UNSUPPORTED), (dict(d_k=48), C.TTT_ERR_INVALID_ARGUMENT),
+    (dict(d_v=8192), C.TTT_ERR_INVALID_ARGUMENT), (dict(chunk=0), C.TTT_ERR_INVALID_ARGUMENT),
+    (dict(mask=C.MASK_STRIDED), C.TTT_ERR_INVALID_ARGUMENT),
+])
+def test_linattn_backward_validation(kw, status):
+    n = ctypes.c_size_t(1)
+    assert C.lib().linattn_backward_workspace_bytes(ctypes.byref(lin_desc(**kw)), ctypes.byref(n)) == status
+
+
+def test_linattn_backward_workspace_and_rejects():
+    """Workspace: the chunk update, state and state gradient per chunk (12 bytes per state element),
+    plus dη partials per 128 columns of d_k beyond the first; nothing when N is 0.  Missing,
+    misaligned or overlapping buffers and a short workspace are refused before anything is enqueued."""
+    L = C.lib()
+    n = ctypes.c_size_t(0)
+    D = lin_desc(B=2, H=3, N=1000, d_k=320, d_v=64, chunk=256)   # 4 chunks, 3 column tiles of d_k
+    assert L.linattn_backward_workspace_bytes(ctypes.byref(D), ctypes.byref(n)) == C.TTT_OK
+    al = lambda x: (x + 255) // 256 * 256
+    assert n.value == 3 * al(2 * 3 * 4 * 320 * 64 * 4) + al(3 * 2 * 3 * 1000 * 4)
+    need = n.value
+    assert L.linattn_backward_workspace_bytes(ctypes.byref(lin_desc(N=0)), ctypes.byref(n)) == C.TTT_OK and n.value == 0
+    G = 1 << 30
+    ins = [P16, P16 + G, P16 + 2 * G, P16 + 3 * G, None, P16 + 4 * G, None]   # q k v eta S0 dO dS_out
+    OB = P16 + (1 << 34)
+    outs = [OB, OB + G, OB + 2 * G, OB + 3 * G, None]                           # dq dk dv deta dS0
+    ws = P16 + (1 << 36)
+
+    def call(i=None, o=None, w=ws, nw=need):
+        a = list(ins if i is None else i)
+        b = list(outs if o is None else o)
+        return L.linattn_backward(ctypes.byref(D), *a, *b, w, nw, None)
+
+    assert call(i=[None] + ins[1:]) == C.TTT_ERR_INVALID_ARGUMENT                    # q missing
+    assert call(o=outs[:3] + [None, None]) == C.TTT_ERR_INVALID_ARGUMENT             # deta missing
+    assert call(i=[P16 + 2] + ins[1:]) == C.TTT_ERR_INVALID_ARGUMENT                 # misaligned q
+    assert call(o=[P16 + 64] + outs[1:]) == C.TTT_ERR_INVALID_ARGUMENT               # dq overlaps q
+    assert b"overlaps" in L.ttt_last_error()
+    assert call(o=[OB, OB + 64] + outs[2:]) == C.TTT_ERR_INVALID_ARGUMENT            # dk overlaps dq
+    assert call(w=None, nw=0) == C.TTT_ERR_WORKSPACE
+    assert call(nw=need - 1) == C.TTT_ERR_WORKSPACE
+    assert call(w=ws + 16) == C.TTT_ERR_INVALID_ARGUMENT                             # not 256-aligned
+    # no (batch, head): nothing to do, no pointer is touched
+    E = lin_desc(B=0)
+    assert L.linattn_backward(ctypes.byref(E), *([None] * 13), 0, None) == C.TTT_OK
+
+
 def test_linattn_wide_keys_need_the_chunk_parallel_path():
     """d_k above 256 is accepted where the chunk-parallel kernels run (they loop over d_k tiles) and
     refused with TTT_ERR_UNSUPPORTED where only the sequential kernel could run; d_k must stay a
@@ -267,6 +315,13 @@ def test_valid_calls_without_a_device_report_device_error():
     Dl = lin_desc()
     assert L.linattn_forward(ctypes.byref(Dl), P16, P16 + (1 << 30), P16 + (2 << 30), P16 + (3 << 30), None, P16B,
                              None, None, 0, None) == C.TTT_ERR_DEVICE
+    n = ctypes.c_size_t(0)
+    L.linattn_backward_workspace_bytes(ctypes.byref(Dl), ctypes.byref(n))
+    G = 1 << 30
+    OB = P16 + (1 << 34)
+    assert L.linattn_backward(ctypes.byref(Dl), P16, P16 + G, P16 + 2 * G, P16 + 3 * G, None, P16 + 4 * G, None,
+                              OB, OB + G, OB + 2 * G, OB + 3 * G, None, P16 + (1 << 36), n.value,
+                              None) == C.TTT_ERR_DEVICE
     # the status table answers for any non-negative value
     assert L.ttt_status_string(C.TTT_ERR_DEVICE) == b"HIP device or launch error"
     assert L.ttt_status_string(0x7FFFFFFF) == b"unknown status"
