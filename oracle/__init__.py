@@ -11,4 +11,5 @@ from .ttt_ref import (  # noqa: F401
     swiglu_apply, chunk_gradients, l2_normalize_rows, newton_schulz, chunk_bounds,
     ttt_scan_ref, ttt_forward_ref, linattn_scan_ref, linattn_forward_ref, gemm_intensity,
     linattn_backward_scan_ref, linattn_backward_ref,
+    ttt_lastlayer_backward_scan_ref, ttt_lastlayer_backward_ref,
 )

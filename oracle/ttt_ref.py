@@ -25,6 +25,8 @@ Training"):
 * several inner-loop gradient steps per chunk (inference time) ... TTT-as-LA, Sec. 4.1
 * the backward of the linear reduction (outer-loop gradients) ..... TTT-as-LA, Sec. 6.2 and Fig. 4
                                                                    (training with the parallel form)
+* the backward of the layer with frozen W1, W3 (last layer only, GD):
+  the linear reduction's over phi(q), phi(k), then phi's chain rule  TTT-as-LA, Thm. 5.2-5.3, Sec. 6.1-6.2
 * gradient ascent in the inner loop: the step's sign flips ....... TTT-as-LA, Sec. 4.2 and 5.2
 * per-chunk rates outside the optimizer step: momentum dW_j = g_j + alpha_j dW_{j-1} over the
   chunk gradient g_j (unit token weights), W <- W - eta_j Opt(dW_j) .. TTT-as-LA, App. E.1 (per token)
@@ -363,3 +365,66 @@ def linattn_backward_ref(q, k, v, eta, chunk, mask, dO, S0=None, dS_out=None, up
         for o_, r in zip(out, res):
             o_[b, h] = r
     return tuple(out)
+
+
+def ttt_lastlayer_backward_scan_ref(q, k, v, eta, W1, W3, W2, chunk, mask, dO, dW_out=None, update_chunks=None,
+                                    inner_steps=1, ascent=False):
+    """Gradients of one (batch, head) scan of the TTT-KVB layer whose inner loop trains W2 alone by
+    plain GD (ttt_scan_ref with last_layer_only, rule UPD_GD, no momentum), for the loss
+    L = sum_t dO_t . o_t + <dW1_out, W1> + <dW3_out, W3> + <dW2_out, W2_out>.
+
+    With W1 and W3 frozen, phi(x) = SiLU(W1 x) o (W3 x) is fixed, the chunk gradient of W2 is
+    -sum eta v phi(k)^T, and the layer is chunked linear attention with queries phi(q), keys
+    phi(k), values v and state W2 (TTT-as-LA, Thm. 5.2-5.3 and Sec. 6.1 Steps 1-6); its outer-loop
+    gradients (TTT-as-LA, Sec. 6.2) are those of linear attention (linattn_backward_scan_ref),
+    followed by the chain rule through phi.  inner_steps repeats an update that does not depend on
+    W2, and ascent flips its sign: both scale eta.  dW_out is None or (dW1, dW3, dW2) of the
+    shapes of (W1, W3, W2).  Returns (dq, dk, dv, deta, (dW1, dW3, dW2)).
+    """
+    q, k, v, eta, dO = (_f64(x) for x in (q, k, v, eta, dO))
+    W1, W3, W2 = _f64(W1), _f64(W3), _f64(W2)
+    f = (-1.0 if ascent else 1.0) * max(int(inner_steps), 1)
+    A = {"q": q @ W1.T, "k": k @ W1.T}
+    C = {"q": q @ W3.T, "k": k @ W3.T}
+    phi = {s: silu(A[s]) * C[s] for s in ("q", "k")}
+    dW2o = None if dW_out is None else dW_out[2]
+    dphq, dphk, dv, deta, dW2 = linattn_backward_scan_ref(phi["q"], phi["k"], v, f * eta, W2, chunk, mask, dO,
+                                                          dW2o, update_chunks)
+    deta = f * deta
+    dW1 = np.zeros_like(W1) if dW_out is None else _f64(dW_out[0]).copy()
+    dW3 = np.zeros_like(W3) if dW_out is None else _f64(dW_out[1]).copy()
+    dx = {}
+    for s, x, dphi in (("q", q, dphq), ("k", k, dphk)):
+        sg = sigmoid(A[s])
+        dA = dphi * C[s] * sg * (1.0 + A[s] * (1.0 - sg))   # d SiLU(a)/da = s (1 + a (1 - s))
+        dC = dphi * A[s] * sg
+        dx[s] = dA @ W1 + dC @ W3
+        dW1 += dA.T @ x
+        dW3 += dC.T @ x
+    return dx["q"], dx["k"], dv, deta, (dW1, dW3, dW2)
+
+
+def ttt_lastlayer_backward_ref(q, k, v, eta, W1, W3, W2, chunk, mask, dO, dW_out=None, update_chunks=None,
+                               inner_steps=1, ascent=False, slices=None):
+    """ttt_lastlayer_backward_scan_ref over [B, H, N, d] inputs.  W1, W3, W2 are per head ([H, ...])
+    or per (batch, head) ([B, H, ...]); the weight gradients take the same shape (per-head weights
+    sum over the batch).  dW_out is None or three [B, H, ...] arrays (the W_out the layer returns
+    is per (batch, head)).  Returns (dq, dk, dv, deta, (dW1, dW3, dW2))."""
+    B, H, N, d = q.shape
+    per_head = W1.ndim == 3
+    dq, dk, dv = np.zeros((B, H, N, d)), np.zeros((B, H, N, d)), np.zeros((B, H, N, d))
+    deta = np.zeros((B, H, N))
+    dW = [np.zeros(x.shape) for x in (W1, W3, W2)]
+    todo = [(b, h) for b in range(B) for h in range(H)] if slices is None else list(slices)
+    for b, h in todo:
+        ws = [x[h] if per_head else x[b, h] for x in (W1, W3, W2)]
+        dwo = None if dW_out is None else tuple(x[b, h] for x in dW_out)
+        r = ttt_lastlayer_backward_scan_ref(q[b, h], k[b, h], v[b, h], eta[b, h], *ws, chunk, mask, dO[b, h], dwo,
+                                            update_chunks, inner_steps, ascent)
+        dq[b, h], dk[b, h], dv[b, h], deta[b, h] = r[:4]
+        for i in range(3):
+            if per_head:
+                dW[i][h] += r[4][i]
+            else:
+                dW[i][b, h] = r[4][i]
+    return dq, dk, dv, deta, tuple(dW)
