@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define TTT_ABI_VERSION 4
+#define TTT_ABI_VERSION 5
 
 typedef enum {
     TTT_OK = 0,
@@ -188,6 +188,46 @@ ttt_status ttt_forward_noalloc(const ttt_desc* desc, const void* q, const void* 
                                void* stream);
 
 /*
+ * Device workspace that ttt_backward needs, in bytes (the size with dW0 requested, which covers a
+ * call without it): the io-dtype copies of W1 | W3 and their transposes, phi(q), phi(k), their
+ * gradients, dA | dC of both sides (16 m_h bytes per token and scan in bf16, twice in fp32), the
+ * scans' dW2, the partial sums of dW1 | dW3, and the linear-attention backward's workspace over
+ * d_k = m_h, d_v = d_h (linattn_backward_workspace_bytes).
+ */
+ttt_status ttt_backward_workspace_bytes(const ttt_desc* desc, size_t* bytes);
+
+/*
+ * Backward of ttt_forward for the layer whose inner loop trains W2 alone by plain GD: desc must
+ * have last_layer_only = 1, rule TTT_UPD_GD, momentum 0 and chunk_rates 0 (else
+ * TTT_ERR_UNSUPPORTED); inner_steps, ascent, the chunked masks and w0_per_batch are as for the
+ * forward, and parallel_form is ignored (both forms compute the same layer).  With W1 and W3 frozen,
+ * phi(x) = SiLU(W1 x) * (W3 x) is fixed and the layer is chunked linear attention with queries
+ * phi(q), keys phi(k), values v and state W2, updated by escale * sum eta v phi(k)^T, escale =
+ * (ascent ? -1 : 1) * max(inner_steps, 1) ("TTT with KV Binding Is Secretly Linear Attention",
+ * Thm. 5.2-5.3, Sec. 6.1-6.2 and Fig. 4: the outer-loop gradients of training through the parallel
+ * form).  The gradients are those of
+ *     L = sum over tokens of dO . o + <dW_out, W_out>
+ * (W_out as ttt_forward writes it: W1 and W3 as given, W2 after the last chunk), for every input:
+ *   q, k, v, eta, W0   the forward's inputs, as for ttt_forward
+ *   dO        [B][H][N][d_h] of io_dtype, 16-byte aligned: the gradient of o
+ *   dW_out    nullable; [B][H][3*d_h*m_h] fp32, 16-byte aligned: the gradient of W_out (NULL = 0)
+ *   dq, dk, dv [B][H][N][d_h] of io_dtype, 16-byte aligned; deta [B][H][N] fp32, 4-byte aligned
+ *   dW0       nullable; fp32 with W0's shape ([H] or [B][H] blocks of [dW1 | dW3 | dW2]), 16-byte
+ *             aligned; per-head weights sum their scans' gradients over the batch.  NULL: not
+ *             computed (the weight-gradient contraction is skipped)
+ *   workspace device buffer of at least ttt_backward_workspace_bytes(desc) bytes, 256-byte aligned
+ *             (may be NULL when that is 0); TTT_ERR_WORKSPACE if it is too small
+ * No output may overlap an input or another output (TTT_ERR_INVALID_ARGUMENT).  Products run in the
+ * io dtype with fp32 accumulation (bf16: phi, its gradient, dA | dC and W1 | W3 are rounded to bf16
+ * as contraction operands; the linear-attention states are bf16 hi + lo pairs), and every sum is
+ * taken in a fixed order, so results do not depend on scheduling.
+ */
+ttt_status ttt_backward(const ttt_desc* desc, const void* q, const void* k, const void* v,
+                        const float* eta, const float* W0, const void* dO, const float* dW_out,
+                        void* dq, void* dk, void* dv, float* deta, float* dW0,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Device workspace that linattn_forward needs, in bytes.  Zero when the call runs the sequential
  * kernel (chunks so small that 4 d_k d_v > 2 chunk (d_k + d_v), or token-causal mode with N < 256);
  * otherwise room for every chunk's own update and the state each chunk's queries see, 8 bytes per
@@ -283,7 +323,7 @@ ttt_status swa_forward(const swa_desc* desc, const void* q, const void* k, const
  * read, and forgets them.  Kernel classes are numbered 0 .. TTT_PROF_KERNELS-1 and named by
  * ttt_profile_kernel_name.  Enabling or reading while another thread launches is allowed.
  */
-#define TTT_PROF_KERNELS 21
+#define TTT_PROF_KERNELS 26
 ttt_status ttt_profile_enable(int32_t on);
 /* Restricts the bracketing to the kernel classes i whose bit (1u << i) is set in mask; the
  * default is every class.  Each bracket records two events on the launch's stream, which costs

@@ -14,7 +14,8 @@ def __getattr__(name):
     # the torch-based binding is imported on first use, so the ctypes layer loads without torch
     if name in ("ttt_forward", "ttt_forward_noalloc", "linattn_forward", "pack_weights", "unpack_weights", "ttt_desc", "linattn_desc",
                 "ttt_workspace_bytes", "linattn_workspace_bytes", "swa_forward", "swa_workspace_bytes",
-                "linattn_backward", "linattn_backward_workspace_bytes"):
+                "linattn_backward", "linattn_backward_workspace_bytes", "ttt_backward",
+                "ttt_backward_workspace_bytes"):
         from . import api
         return getattr(api, name)
     raise AttributeError(name)

@@ -19,13 +19,13 @@ UPD_GD, UPD_GD_L2, UPD_MUON_L2, UPD_MUON = range(4)
 # every function include/ttt.h declares
 EXPORTS = (
     "ttt_abi_version", "ttt_status_string", "ttt_last_error",
-    "ttt_workspace_bytes", "ttt_forward", "ttt_forward_noalloc",
+    "ttt_workspace_bytes", "ttt_forward", "ttt_forward_noalloc", "ttt_backward_workspace_bytes", "ttt_backward",
     "linattn_workspace_bytes", "linattn_forward", "linattn_backward_workspace_bytes", "linattn_backward",
     "swa_workspace_bytes", "swa_forward",
     "ttt_profile_enable", "ttt_profile_select", "ttt_profile_read", "ttt_profile_kernel_name",
     "ttt_probe_mfma_bf16",
 )
-PROF_KERNELS = 21
+PROF_KERNELS = 26
 NOALLOC_SCRATCH_BYTES = 64 << 20   # TTT_NOALLOC_SCRATCH_BYTES of include/ttt.h
 
 
@@ -85,6 +85,10 @@ def lib() -> ctypes.CDLL:
     L.ttt_forward_noalloc.restype = c_int32
     L.ttt_forward_noalloc.argtypes = [POINTER(TttDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                       c_void_p, c_void_p, c_void_p]
+    L.ttt_backward_workspace_bytes.restype = c_int32
+    L.ttt_backward_workspace_bytes.argtypes = [POINTER(TttDesc), POINTER(c_size_t)]
+    L.ttt_backward.restype = c_int32
+    L.ttt_backward.argtypes = [POINTER(TttDesc)] + [c_void_p] * 13 + [c_size_t, c_void_p]
     L.linattn_workspace_bytes.restype = c_int32
     L.linattn_workspace_bytes.argtypes = [POINTER(LinattnDesc), POINTER(c_size_t)]
     L.linattn_forward.restype = c_int32

@@ -189,6 +189,57 @@ def ttt_forward_noalloc(q, k, v, eta, W0, chunk: int, mask_mode: int = C.MASK_AP
     return o, W_out
 
 
+def ttt_backward_workspace_bytes(desc: C.TttDesc) -> int:
+    n = ctypes.c_size_t(0)
+    C.check(C.lib().ttt_backward_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def ttt_backward(q, k, v, eta, W0, dO, chunk: int, mask_mode: int = C.MASK_APPLY_THEN_UPDATE, *,
+                 m_h: Optional[int] = None, dW_out: Optional[torch.Tensor] = None, want_dW0: bool = True,
+                 update_chunks=None, inner_steps: int = 1, ascent: bool = False,
+                 workspace: Optional[torch.Tensor] = None, stream=None):
+    """Backward of ttt_forward for the layer whose inner loop trains W2 alone by plain GD
+    (last_layer_only, UPD_GD, no momentum), through ttt_backward of libttt.so.
+
+    dO [B, H, N, d] is the gradient of o, dW_out ([B, H, 3*d*m] fp32 or None) that of W_out.
+    Returns (dq, dk, dv, deta, dW0 or None); dW0 has W0's shape (per-head weights sum over the
+    batch)."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q must be a [B, H, N, d] tensor")
+    B, H, N, d = q.shape
+    dev = q.device
+    if q.dtype not in _DT:
+        raise ValueError(f"unsupported io dtype {q.dtype}")
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (dO, "dO")):
+        _need(t, n, q.dtype, dev, q.shape)
+    _need(eta, "eta", torch.float32, dev, (B, H, N))
+    if chunk < 1:
+        raise ValueError("chunk must be >= 1")
+    if not isinstance(W0, torch.Tensor) or W0.dim() not in (2, 3):
+        raise ValueError("W0 must be [H, 3*d*m] or [B, H, 3*d*m]")
+    per_batch = W0.dim() == 3
+    if m_h is None:
+        m_h = W0.shape[-1] // (3 * d)
+    _need(W0, "W0", torch.float32, dev, ((B, H) if per_batch else (H,)) + (3 * d * m_h,))
+    if dW_out is not None:
+        _need(dW_out, "dW_out", torch.float32, dev, (B, H, 3 * d * m_h))
+    _flags(update_chunks, N, chunk, mask_mode == C.MASK_STRIDED)
+    D, keep = ttt_desc(B, H, N, d, m_h, chunk, _DT[q.dtype], mask_mode, C.UPD_GD, 0, 0.0, True, per_batch,
+                       update_chunks, inner_steps, ascent)
+    nbytes = ttt_backward_workspace_bytes(D)
+    workspace = _workspace(workspace, nbytes, dev)
+    dq, dkt, dvt = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    deta = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dW0 = torch.empty_like(W0) if want_dW0 else None
+    st = C.lib().ttt_backward(ctypes.byref(D), _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(W0), _ptr(dO),
+                              _ptr(dW_out), _ptr(dq), _ptr(dkt), _ptr(dvt), _ptr(deta), _ptr(dW0), _ptr(workspace),
+                              ctypes.c_size_t(0 if workspace is None else workspace.numel()), _stream_handle(stream))
+    del keep
+    C.check(st)
+    return dq, dkt, dvt, deta, dW0
+
+
 def linattn_desc(B, H, N, d_k, d_v, chunk, io_dtype, mask, update_chunks=None):
     flags = None
     if update_chunks is not None:

@@ -25,7 +25,8 @@ inline ttt_status fail(ttt_status s, const char* fmt, ...) {
 // kernel classes of the optional launch profiler (ttt_profile_*)
 enum ProfKernel { PK_UP = 0, PK_DOWN, PK_UPDATE, PK_MUON_PREP, PK_NS_INIT, PK_NS_GRAM, PK_NS_STEP, PK_LINATTN,
                   PK_LIN_DELTA, PK_LIN_SCAN, PK_LIN_APPLY, PK_PHI, PK_W13, PK_ZERO, PK_PAR_MOM, PK_SWA,
-                  PK_SWA_PREP, PK_LIN_BWD_T, PK_LIN_BWD_N, PK_LIN_DETA, PK_SWA_VPREP };
+                  PK_SWA_PREP, PK_LIN_BWD_T, PK_LIN_BWD_N, PK_LIN_DETA, PK_SWA_VPREP, PK_W13T, PK_PHI_BWD,
+                  PK_PHI_DX, PK_DW13, PK_DW_SUM };
 
 // Brackets one launch with events on its stream while profiling is enabled; no-op otherwise.
 struct ProfScope {
@@ -110,5 +111,33 @@ size_t lin_chunked_ws_bytes(int64_t nscan, int64_t nchunks, int d_k, int d_v);
 template <typename T>
 ttt_status lin_chunked_run(const linattn_desc& D, const uint32_t (&flags)[32], const T* q, const T* k, const T* v,
                            const float* eta, T* o, const LinStateIO& io, char* ws, hipStream_t st);
+
+// The checks of a TTT layer descriptor shared by the forward and the backward entry points
+ttt_status validate_ttt_desc(const ttt_desc* D);
+
+// The backward of the chunked path as a building block (also driven by the TTT layer's backward).
+// S0 of scan s at S0 + (s0_heads ? s % s0_heads : s) * s0_stride (null: zeros); dS_out of scan s at
+// dS_out + s * dso_stride (null: zeros); dS0 of scan s to dS0 + s * ds0_stride (null: not written).
+// The forward's chunk updates were escale * sum eta v k^T (the sign of ascent, repeated steps).
+struct LinBwdIO {
+    const float* S0 = nullptr;
+    int64_t s0_stride = 0;
+    int s0_heads = 0;
+    const float* dS_out = nullptr;
+    int64_t dso_stride = 0;
+    float* dS0 = nullptr;
+    int64_t ds0_stride = 0;
+    float escale = 1.f;
+};
+// the backward's checks of a linear-attention descriptor
+ttt_status validate_lin_desc_bwd(const linattn_desc* D);
+// workspace of lin_chunked_bwd
+size_t lin_chunked_bwd_ws_bytes(const linattn_desc& D);
+// D.mask is a chunked mask (not TOKEN_CAUSAL); flags as for lin_chunked_run.  dq, dk [S][N][d_k],
+// dv [S][N][d_v], deta [S][N] as for linattn_backward.
+template <typename T>
+ttt_status lin_chunked_bwd(const linattn_desc& D, const uint32_t (&flags)[32], const T* q, const T* k, const T* v,
+                           const float* eta, const T* dO, const LinBwdIO& io, T* dq, T* dk, T* dv, float* deta,
+                           char* ws, hipStream_t st);
 
 }  // namespace ttt

@@ -887,6 +887,7 @@ template <typename T> struct BwdTJob {
 template <typename T> struct BwdTArgs {
     BwdTJob<T> job[2];
     int64_t N, ntok; int dk, dv, chunk, nc, ntt, ntn, per_job, mode;
+    float es;  // dk job: the forward's update scale (eta's factor)
     uint32_t flags[32];
 };
 
@@ -954,7 +955,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_lin_bwd_t(BwdTArgs<T> a) {
         pd[idx] = 0.f;
         if (row < rows && col < cols) {
             const uint32_t off = (uint32_t)row * (uint32_t)a.dk + (uint32_t)col;
-            const float f = K ? ef[idx] : 1.f;
+            const float f = K ? ef[idx] * a.es : 1.f;
             Pack4<T>::store(O + off, v.x * f, v.y * f, v.z * f, v.w * f);
             if (K) {
                 float kv[4];
@@ -983,7 +984,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_lin_bwd_t(BwdTArgs<T> a) {
         // entry idx = h * RV_K + k covers tile row h * WM + (k * NT + tid) / 32
         const int idx = (lane >> 1) & 15, h = idx / TB::RV_K, k = idx % TB::RV_K;
         const int row = h * TB::WM + (k * TB::NT + wave * 64 + (lane & 32)) / 32;
-        if (row < rows) de[row] = pd[0];
+        if (row < rows) de[row] = pd[0] * a.es;
     }
 }
 
@@ -992,6 +993,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_lin_bwd_t(BwdTArgs<T> a) {
 template <typename T> struct BwdNArgs {
     const T* k; const T* R; const float* eta; T* dv;
     int64_t N; int dk, dvn, chunk, nc, ntt, ntn, mode;
+    float es;  // the forward's update scale (eta's factor)
     uint32_t flags[32];
 };
 
@@ -1017,7 +1019,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_lin_bwd_n(BwdNArgs<T> a) {
         return;
     }
     __shared__ float er[kApplyRows];  // the rows' eta, ordered before the epilogue by run()'s barriers
-    if (threadIdx.x < rows) er[threadIdx.x] = a.eta[tok + r0 + threadIdx.x];
+    if (threadIdx.x < rows) er[threadIdx.x] = a.es * a.eta[tok + r0 + threadIdx.x];
     const int64_t dvk = (int64_t)a.dvn * a.dk;
     const T* R = a.R + (int64_t)unit * PLANES * dvk + (int64_t)c0 * a.dk;
     const Opnd<T> A[1] = {{a.k + (tok + r0) * a.dk, a.dk, nl - r0, a.dk}};
@@ -1054,7 +1056,7 @@ __global__ __launch_bounds__(kThreads) void k_lin_deta_sum(const float* part, fl
     deta[i] = s;
 }
 
-static ttt_status validate_lin_bwd(const linattn_desc* D) {
+ttt_status validate_lin_desc_bwd(const linattn_desc* D) {
     ttt_status rc = validate_lin(D);
     if (rc != TTT_OK) return rc;
     if (D->mask == TTT_MASK_TOKEN_CAUSAL)
@@ -1068,7 +1070,7 @@ static ttt_status validate_lin_bwd(const linattn_desc* D) {
     return TTT_OK;
 }
 
-static size_t lin_bwd_ws_bytes(const linattn_desc& D) {
+size_t lin_chunked_bwd_ws_bytes(const linattn_desc& D) {
     if (D.N == 0) return 0;
     const int64_t S = (int64_t)D.B * D.H, nc = cdiv(D.N, D.chunk), ntn = cdiv(D.d_k, kApplyCols);
     const size_t sb = align256((size_t)(S * nc * (int64_t)D.d_v * D.d_k * 4));
@@ -1076,9 +1078,9 @@ static size_t lin_bwd_ws_bytes(const linattn_desc& D) {
 }
 
 template <typename T>
-static ttt_status run_lin_bwd(const linattn_desc& D, const uint32_t (&flags)[32], const T* q, const T* k, const T* v,
-                              const float* eta, const float* S0, const T* dO, const float* dS_out, T* dq, T* dk, T* dv,
-                              float* deta, float* dS0, char* ws, hipStream_t st) {
+ttt_status lin_chunked_bwd(const linattn_desc& D, const uint32_t (&flags)[32], const T* q, const T* k, const T* v,
+                           const float* eta, const T* dO, const LinBwdIO& io, T* dq, T* dk, T* dv, float* deta,
+                           char* ws, hipStream_t st) {
     const int64_t S = (int64_t)D.B * D.H, dvk = (int64_t)D.d_v * D.d_k;
     const int64_t chunk = D.chunk, nc = D.N ? cdiv(D.N, chunk) : 0;
     const size_t sb = align256((size_t)(S * nc * dvk * 4));
@@ -1093,8 +1095,10 @@ static ttt_status run_lin_bwd(const linattn_desc& D, const uint32_t (&flags)[32]
         // the states the chunks' queries saw
         if ((rc = launch_delta<T, true>(D, chunk, nc, D.mask, flags, k, v, eta, dS, st)) != TTT_OK) return rc;
         LinStateIO fio;
-        fio.S0 = S0;
-        fio.s0_stride = dvk;
+        fio.S0 = io.S0;
+        fio.s0_stride = io.s0_stride;
+        fio.s0_heads = io.s0_heads;
+        fio.dsign = io.escale;
         if ((rc = launch_scan<T>(D, nc, D.mask, flags, dS, Sc, fio, 0, st)) != TTT_OK) return rc;
         // D_c = sum over the chunk of dO q^T, every chunk
         if ((rc = launch_delta<T, false>(D, chunk, nc, TTT_MASK_APPLY_THEN_UPDATE, all, q, dO, nullptr, dS, st)) !=
@@ -1104,11 +1108,11 @@ static ttt_status run_lin_bwd(const linattn_desc& D, const uint32_t (&flags)[32]
     // R_j (backwards over the chunks, every D_c added; the mask decides whether chunk j's own term is
     // in R_j) and dS0 = dS_out + sum_c D_c
     LinStateIO rio;
-    rio.S0 = dS_out;
-    rio.s0_stride = dvk;
-    rio.Sout = dS0;
-    rio.sout_stride = dvk;
-    if (D.N > 0 || dS0)
+    rio.S0 = io.dS_out;
+    rio.s0_stride = io.dso_stride;
+    rio.Sout = io.dS0;
+    rio.sout_stride = io.ds0_stride;
+    if (D.N > 0 || io.dS0)
         if ((rc = launch_scan<T>(D, nc, D.mask, all, dS, R, rio, 1, st)) != TTT_OK) return rc;
     if (D.N == 0) return TTT_OK;
     const int ntt = (int)cdiv(std::min<int64_t>(chunk, D.N), kApplyRows);
@@ -1127,6 +1131,7 @@ static ttt_status run_lin_bwd(const linattn_desc& D, const uint32_t (&flags)[32]
     ta.ntn = ntk;
     ta.per_job = (int)(S * nc * ntt * ntk);
     ta.mode = D.mask;
+    ta.es = io.escale;
     for (int w = 0; w < 32; ++w) ta.flags[w] = flags[w];
     {
         ProfScope ps(PK_LIN_BWD_T, st);
@@ -1146,6 +1151,7 @@ static ttt_status run_lin_bwd(const linattn_desc& D, const uint32_t (&flags)[32]
     na.ntt = ntt;
     na.ntn = (int)cdiv(D.d_v, kApplyCols);
     na.mode = D.mask;
+    na.es = io.escale;
     for (int w = 0; w < 32; ++w) na.flags[w] = flags[w];
     {
         ProfScope ps(PK_LIN_BWD_N, st);
@@ -1162,6 +1168,14 @@ static ttt_status run_lin_bwd(const linattn_desc& D, const uint32_t (&flags)[32]
     }
     return TTT_OK;
 }
+
+template ttt_status lin_chunked_bwd<uint16_t>(const linattn_desc&, const uint32_t (&)[32], const uint16_t*,
+                                              const uint16_t*, const uint16_t*, const float*, const uint16_t*,
+                                              const LinBwdIO&, uint16_t*, uint16_t*, uint16_t*, float*, char*,
+                                              hipStream_t);
+template ttt_status lin_chunked_bwd<float>(const linattn_desc&, const uint32_t (&)[32], const float*, const float*,
+                                           const float*, const float*, const float*, const LinBwdIO&, float*, float*,
+                                           float*, float*, char*, hipStream_t);
 
 }  // namespace ttt
 
@@ -1240,10 +1254,10 @@ extern "C" ttt_status linattn_forward(const linattn_desc* desc, const void* q, c
 
 extern "C" ttt_status linattn_backward_workspace_bytes(const linattn_desc* desc, size_t* bytes) {
     clear_error();
-    ttt_status rc = validate_lin_bwd(desc);
+    ttt_status rc = validate_lin_desc_bwd(desc);
     if (rc != TTT_OK) return rc;
     if (!bytes) return fail(TTT_ERR_INVALID_ARGUMENT, "bytes is NULL");
-    *bytes = lin_bwd_ws_bytes(*desc);
+    *bytes = lin_chunked_bwd_ws_bytes(*desc);
     return TTT_OK;
 }
 
@@ -1252,7 +1266,7 @@ extern "C" ttt_status linattn_backward(const linattn_desc* desc, const void* q, 
                                        void* dq, void* dk, void* dv, float* deta, float* dS0, void* workspace,
                                        size_t workspace_bytes, void* stream) {
     clear_error();
-    ttt_status rc = validate_lin_bwd(desc);
+    ttt_status rc = validate_lin_desc_bwd(desc);
     if (rc != TTT_OK) return rc;
     const linattn_desc& D = *desc;
     const int64_t S = (int64_t)D.B * D.H;
@@ -1282,7 +1296,7 @@ extern "C" ttt_status linattn_backward(const linattn_desc* desc, const void* q, 
             if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n))
                 return fail(TTT_ERR_INVALID_ARGUMENT, "%s overlaps %s", outs[i].name, outs[j].name);
     }
-    const size_t need = lin_bwd_ws_bytes(D);
+    const size_t need = lin_chunked_bwd_ws_bytes(D);
     if (need && (!workspace || workspace_bytes < need))
         return fail(TTT_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
     if (need && !aligned(workspace, 256)) return fail(TTT_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
@@ -1296,10 +1310,18 @@ extern "C" ttt_status linattn_backward(const linattn_desc* desc, const void* q, 
         for (int64_t j = 0; j < cdiv(D.N, D.chunk); ++j)
             if (D.update_chunks[j]) flags[j >> 5] |= 1u << (j & 31);
     hipStream_t st = (hipStream_t)stream;
+    const int64_t dvk = (int64_t)D.d_v * D.d_k;
+    LinBwdIO io;
+    io.S0 = S0;
+    io.s0_stride = dvk;
+    io.dS_out = dS_out;
+    io.dso_stride = dvk;
+    io.dS0 = dS0;
+    io.ds0_stride = dvk;
     if (D.io_dtype == TTT_BF16)
-        return run_lin_bwd<uint16_t>(D, flags, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, eta, S0,
-                                     (const uint16_t*)dO, dS_out, (uint16_t*)dq, (uint16_t*)dk, (uint16_t*)dv, deta,
-                                     dS0, (char*)workspace, st);
-    return run_lin_bwd<float>(D, flags, (const float*)q, (const float*)k, (const float*)v, eta, S0, (const float*)dO,
-                              dS_out, (float*)dq, (float*)dk, (float*)dv, deta, dS0, (char*)workspace, st);
+        return lin_chunked_bwd<uint16_t>(D, flags, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, eta,
+                                         (const uint16_t*)dO, io, (uint16_t*)dq, (uint16_t*)dk, (uint16_t*)dv, deta,
+                                         (char*)workspace, st);
+    return lin_chunked_bwd<float>(D, flags, (const float*)q, (const float*)k, (const float*)v, eta, (const float*)dO,
+                                  io, (float*)dq, (float*)dk, (float*)dv, deta, (char*)workspace, st);
 }

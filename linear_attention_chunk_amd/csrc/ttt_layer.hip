@@ -18,6 +18,7 @@
 #include <type_traits>
 
 #include "host_common.hpp"
+#include "phi.hpp"
 #include "tile.hpp"
 
 namespace ttt {
@@ -754,55 +755,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_ns_step(NSArgs<T> a) {
 // chunk-parallel linear-attention kernels do the rest, with the recurrence's momentum, inner steps
 // and ascent folded into their state scan.
 
-// W1 | W3 (the first 2 d m floats of each fast-weight block) in bf16, as contraction operands
-template <typename T>
-__global__ __launch_bounds__(kThreads) void k_w13_cvt(const float* W0, int64_t w_stride, T* out, int64_t n4,
-                                                      int64_t per4) {
-    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (i >= n4) return;
-    const int64_t h = i / per4, j = i % per4;
-    const float4 w = *reinterpret_cast<const float4*>(W0 + h * w_stride + 4 * j);
-    Pack4<T>::store(out + 4 * i, w.x, w.y, w.z, w.w);
-}
-
-template <typename T> struct PhiArgs {
-    const T* x[2]; T* phi[2];        // q and k [S][N][d], their features [S][N][m]
-    const T* W; int64_t w_stride;    // W1 of weight block hw at W + hw * w_stride, W3 d m after it
-    int w_heads;                     // hw = s % w_heads, or s when 0 (one block per scan)
-    int64_t N; int d, m, nscan, ntt, nct;  // token and hidden tiles per scan
-};
-
-// Tiles of 256 tokens x 128 hidden units on 8 waves, products x W1^T and x W3^T, as the query
-// tiles of k_up; the epilogue writes phi row-major (hidden units contiguous).
-template <typename T>
-__global__ __launch_bounds__(64 * kUpWaves, 1) void k_phi(PhiArgs<T> a) {
-    using TQ = Tile<T, kUpQRows, kUpCols, 2, 4, 1, 2, 2, false, false, false, kUpWaves>;
-    __shared__ __attribute__((aligned(16))) char smem[TQ::LDS];
-    const int per = a.ntt * a.nct;
-    const int lb = xcd_block(gridDim.x);
-    const int u = lb / per, t = lb % per;
-    const int which = u / a.nscan, s = u % a.nscan;
-    const int hw = a.w_heads ? s % a.w_heads : s;
-    const int r0 = (t / a.nct) * kUpQRows, c0 = (t % a.nct) * kUpCols;
-    const int64_t dm = (int64_t)a.d * a.m;
-    const T* W1 = a.W + (int64_t)hw * a.w_stride;
-    const T* W3 = W1 + dm;
-    const int rows = (int)(a.N - r0);
-    const Opnd<T> A[1] = {{a.x[which] + ((int64_t)s * a.N + r0) * a.d, a.d, rows, a.d}};
-    const Opnd<T> B[2] = {{W1 + (int64_t)c0 * a.d, a.d, a.m - c0, a.d}, {W3 + (int64_t)c0 * a.d, a.d, a.m - c0, a.d}};
-    TQ tl;
-    tl.template run<PMQ>(A, B, a.d, smem);
-    T* P = a.phi[which] + ((int64_t)s * a.N + r0) * a.m + c0;
-    auto epi = [&](auto check) {
-        tl.for_each([&](const float (&v)[2], int row, int col) {
-            if (!decltype(check)::value || (row < rows && c0 + col < a.m))
-                P[(int64_t)row * a.m + col] = Elt<T>::st(v[0] * sigmoidf_(v[0]) * v[1]);
-        });
-    };
-    if (kUpQRows <= rows && c0 + kUpCols <= a.m) epi(std::false_type{});
-    else epi(std::true_type{});
-}
-
 // ---------------------------------------------------------------------------------------------
 // host driver
 
@@ -1091,11 +1043,11 @@ static ttt_status run_parallel_form(const ttt_desc& D, const PLayout& L, const T
     // 2. the features of every query and key
     T* phq = (T*)(ws + L.phq);
     T* phk = (T*)(ws + L.phk);
-    PhiArgs<T> pa{{q, k}, {phq, phk}, W13, w13_stride, D.w0_per_batch ? 0 : D.H, D.N, D.d_h, D.m_h, (int)S,
-                  (int)cdiv(D.N, kUpQRows), (int)cdiv(D.m_h, kUpCols)};
+    PhiArgs<T> pa{{q, k}, {phq, phk}, {nullptr, nullptr}, W13, w13_stride, D.w0_per_batch ? 0 : D.H, D.N, D.d_h,
+                  D.m_h, (int)S, (int)cdiv(D.N, kPhiRows), (int)cdiv(D.m_h, kPhiCols)};
     {
         ProfScope ps(PK_PHI, st);
-        hipLaunchKernelGGL(k_phi<T>, dim3((unsigned)(2 * S * pa.ntt * pa.nct)), dim3(64 * kUpWaves), 0, st, pa);
+        hipLaunchKernelGGL((k_phi<T, false>), dim3((unsigned)(2 * S * pa.ntt * pa.nct)), dim3(64 * kPhiWaves), 0, st, pa);
     }
     if ((rc = check_launch("k_phi", st)) != TTT_OK) return rc;
     // 3. chunked linear attention over the features, with W2 [d][m] as the state S [d_v][d_k]
@@ -1135,7 +1087,7 @@ static ttt_status run_parallel_form(const ttt_desc& D, const PLayout& L, const T
     return copy_w0(2 * dm);
 }
 
-static ttt_status validate(const ttt_desc* D) {
+ttt_status validate_ttt_desc(const ttt_desc* D) {
     if (!D) return fail(TTT_ERR_INVALID_ARGUMENT, "desc is NULL");
     if (D->B < 0 || D->H < 0 || D->N < 0) return fail(TTT_ERR_INVALID_ARGUMENT, "B, H, N must be >= 0");
     if (D->d_h < 32 || D->d_h > kMaxDim || D->d_h % 32)
@@ -1181,7 +1133,7 @@ static ttt_status validate(const ttt_desc* D) {
         // launch sizes: the feature tiles, and the linear-attention tiles over chunks and state
         const int64_t nd = cdiv(D->d_h, 128), nm = cdiv(D->m_h, 128);
         const int64_t lim = 1LL << 31;
-        if (2 * S * cdiv(D->N, kUpQRows) * cdiv(D->m_h, kUpCols) >= lim || S * nc * nd * nm >= lim ||
+        if (2 * S * cdiv(D->N, kPhiRows) * cdiv(D->m_h, kPhiCols) >= lim || S * nc * nd * nm >= lim ||
             S * nc * cdiv(std::min<int64_t>(D->chunk, D->N), 128) * nd >= lim)
             return fail(TTT_ERR_UNSUPPORTED, "parallel_form: B*H, N, d_h, m_h too large for one launch");
     }
@@ -1392,7 +1344,7 @@ using namespace ttt;
 
 extern "C" ttt_status ttt_workspace_bytes(const ttt_desc* desc, size_t* bytes) {
     clear_error();
-    ttt_status rc = validate(desc);
+    ttt_status rc = validate_ttt_desc(desc);
     if (rc != TTT_OK) return rc;
     if (!bytes) return fail(TTT_ERR_INVALID_ARGUMENT, "bytes is NULL");
     *bytes = desc->parallel_form ? make_playout(*desc).total
@@ -1407,7 +1359,7 @@ namespace ttt {
 static ttt_status forward_impl(const ttt_desc* desc, const void* q, const void* k, const void* v, const float* eta,
                                const float* W0, void* o, float* W_out, float* M_inout, void* workspace,
                                size_t workspace_bytes, void* stream, bool scratch) {
-    ttt_status rc = validate(desc);
+    ttt_status rc = validate_ttt_desc(desc);
     if (rc != TTT_OK) return rc;
     const ttt_desc& D = *desc;
     const int64_t S = (int64_t)D.B * D.H;
@@ -1513,7 +1465,7 @@ extern "C" ttt_status ttt_forward_noalloc(const ttt_desc* desc, const void* q, c
                                           const float* eta, const float* W0, void* o, float* W_out, float* M_inout,
                                           void* stream) {
     clear_error();
-    ttt_status rc = validate(desc);
+    ttt_status rc = validate_ttt_desc(desc);
     if (rc != TTT_OK) return rc;
     void* ws = nullptr;
     if ((rc = scratch_address(&ws)) != TTT_OK) return rc;

@@ -15,7 +15,11 @@ Recipe (per (batch, head) slice, so any slice can be regenerated on its own):
     the rounded values (held in float32 arrays) are what every consumer sees;
   * the backward's upstream gradients of slice (b, h) come from ``default_rng([seed, b, h, 7])``:
     dO [N, d_v] with entries N(0, 1) / sqrt(d_v) (rounded to bfloat16 for bf16 workloads), then
-    dS_out [d_v, d_k] with entries N(0, 1) / sqrt(d_k), kept in fp32.
+    dS_out [d_v, d_k] with entries N(0, 1) / sqrt(d_k), kept in fp32;
+  * the TTT layer's upstream gradients of slice (b, h) come from ``default_rng([seed, b, h, 8])``:
+    dO [N, d] with entries N(0, 1) / sqrt(d) (rounded to bfloat16 for bf16 workloads), then the
+    gradients of the returned fast weights dW1 (m x d), dW3 (m x d), dW2 (d x m) with entries
+    N(0, 1) / sqrt(d), kept in fp32.
 """
 from __future__ import annotations
 
@@ -30,6 +34,8 @@ __all__ = [
     "make_linattn_inputs",
     "grad_slice",
     "make_linattn_grads",
+    "layer_grad_slice",
+    "make_ttt_grads",
 ]
 
 
@@ -150,3 +156,29 @@ def make_linattn_grads(seed: int, B: int, H: int, N: int, d_k: int, d_v: int, bf
     for b, h in todo:
         dO[b, h], dS[b, h] = grad_slice(seed, b, h, N, d_k, d_v, bf16)
     return dO, dS
+
+
+def layer_grad_slice(seed: int, b: int, h: int, N: int, d: int, m: int, bf16: bool = True):
+    """Upstream gradients of one (batch, head) slice of the TTT layer: dO [N, d] and the gradients
+    of the returned fast weights (dW1 [m, d], dW3 [m, d], dW2 [d, m], fp32)."""
+    rng = np.random.default_rng([seed, b, h, 8])
+    s = np.float32(np.sqrt(d))
+    dO = np.divide(rng.standard_normal((N, d), dtype=np.float32), s, dtype=np.float32)
+    dW = tuple(np.divide(rng.standard_normal(shape, dtype=np.float32), s, dtype=np.float32)
+               for shape in ((m, d), (m, d), (d, m)))
+    if bf16:
+        dO = round_to_bf16(dO)
+    return dO, dW
+
+
+def make_ttt_grads(seed: int, B: int, H: int, N: int, d: int, m: int, bf16: bool = True, slices=None):
+    """dO [B, H, N, d] and (dW1 [B, H, m, d], dW3 [B, H, m, d], dW2 [B, H, d, m]) (slices not listed
+    stay zero)."""
+    dO = np.zeros((B, H, N, d), np.float32)
+    dW = (np.zeros((B, H, m, d), np.float32), np.zeros((B, H, m, d), np.float32), np.zeros((B, H, d, m), np.float32))
+    todo = [(b, h) for b in range(B) for h in range(H)] if slices is None else list(slices)
+    for b, h in todo:
+        dO[b, h], ws = layer_grad_slice(seed, b, h, N, d, m, bf16)
+        for i in range(3):
+            dW[i][b, h] = ws[i]
+    return dO, dW

@@ -64,6 +64,27 @@ static void run_ttt(ttt_desc D) {
     // a workspace one byte short is refused before any buffer is looked at
     if (s == TTT_OK && need > 0 && (int64_t)D.B * D.H > 0)
         EXPECT(ttt_forward(&D, q, k, v, eta, W0, o, Wout, nullptr, ws, need - 1, nullptr) == TTT_ERR_WORKSPACE);
+    // the backward: the forward's checks, then the layer it covers (W2 alone, plain GD, no momentum)
+    size_t bneed = 0;
+    ttt_status bs = ttt_backward_workspace_bytes(&D, &bneed);
+    check_message(bs);
+    if (s != TTT_OK) EXPECT(bs == s);
+    const bool covered = D.last_layer_only == 1 && D.rule == TTT_UPD_GD && D.momentum == 0.f && D.chunk_rates == 0;
+    if (s == TTT_OK && !covered) EXPECT(bs == TTT_ERR_UNSUPPORTED);
+    const void* dO = (const void*)(P + (9ull << 36));
+    void* dq = (void*)(P + (10ull << 36));
+    void* dk = (void*)(P + (11ull << 36));
+    void* dv = (void*)(P + (12ull << 36));
+    float* deta = (float*)(P + (13ull << 36));
+    float* dW0 = (float*)(P + (14ull << 36));
+    void* bws = (void*)(P + (15ull << 36));
+    ttt_status bf = ttt_backward(&D, q, k, v, eta, W0, dO, nullptr, dq, dk, dv, deta, dW0, bws, bneed, nullptr);
+    check_message(bf);
+    if (bs != TTT_OK) EXPECT(bf == bs || bf == TTT_ERR_INVALID_ARGUMENT);
+    else if ((int64_t)D.B * D.H > 0) EXPECT(bf == TTT_ERR_DEVICE || bf == TTT_ERR_INVALID_ARGUMENT);
+    if (bs == TTT_OK && bneed > 0 && (int64_t)D.B * D.H > 0)
+        EXPECT(ttt_backward(&D, q, k, v, eta, W0, dO, nullptr, dq, dk, dv, deta, dW0, bws, bneed - 1, nullptr) ==
+               TTT_ERR_WORKSPACE);
 }
 
 static void run_lin(linattn_desc D) {
@@ -123,6 +144,8 @@ int main() {
     EXPECT(ttt_forward(nullptr, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, nullptr) == TTT_ERR_INVALID_ARGUMENT);
     EXPECT(linattn_forward(nullptr, 0, 0, 0, 0, 0, 0, 0, 0, 0, nullptr) == TTT_ERR_INVALID_ARGUMENT);
     EXPECT(linattn_backward_workspace_bytes(nullptr, nullptr) == TTT_ERR_INVALID_ARGUMENT);
+    EXPECT(ttt_backward_workspace_bytes(nullptr, nullptr) == TTT_ERR_INVALID_ARGUMENT);
+    EXPECT(ttt_backward(nullptr, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, nullptr) == TTT_ERR_INVALID_ARGUMENT);
     EXPECT(linattn_backward(nullptr, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, nullptr) == TTT_ERR_INVALID_ARGUMENT);
 
     // the profiler's host side: names, selection, a read with nothing recorded, bad sizes
@@ -166,6 +189,9 @@ int main() {
         D = base_desc(); D.N = 1; D.chunk = 4096; run_ttt(D);
         D = base_desc(); D.B = 8; D.H = 4; D.N = 32768; D.d_h = 384; D.m_h = 768; D.chunk = 2048; run_ttt(D);
         D.rule = TTT_UPD_MUON_L2; D.momentum = 0.9f; run_ttt(D);
+        D = base_desc(); D.B = 8; D.H = 4; D.N = 32768; D.d_h = 384; D.m_h = 768; D.chunk = 2048;
+        D.rule = TTT_UPD_GD; D.last_layer_only = 1; run_ttt(D);            // the backward's workload
+        D.w0_per_batch = 1; D.ascent = 1; D.inner_steps = 4; run_ttt(D);
         D = base_desc(); D.B = 1 << 20; D.H = 2; run_ttt(D);            // B*H beyond the limit
         D = base_desc(); D.N = 0x7FFFFFFF; D.chunk = 0x7FFFFFFF; run_ttt(D);
         D = base_desc(); D.m_h = 2048; D.chunk = 1 << 20; D.N = 1 << 20; run_ttt(D);

@@ -39,7 +39,7 @@ def test_library_loads_and_exports_every_symbol():
 
 def test_version_and_status_strings():
     L = C.lib()
-    assert L.ttt_abi_version() == 4
+    assert L.ttt_abi_version() == 5
     for s in range(5):
         assert L.ttt_status_string(s)
     assert L.ttt_status_string(99) == b"unknown status"
@@ -288,6 +288,71 @@ def test_linattn_wide_keys_need_the_chunk_parallel_path():
         assert L.linattn_workspace_bytes(ctypes.byref(D), ctypes.byref(n)) == C.TTT_ERR_INVALID_ARGUMENT
 
 
+def bwd_desc(**kw):
+    return desc(**dict(dict(last_layer_only=1, rule=C.UPD_GD), **kw))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), C.TTT_OK), (dict(mask=C.MASK_UPDATE_THEN_APPLY, inner_steps=3, ascent=1), C.TTT_OK),
+    (dict(parallel_form=1, w0_per_batch=1), C.TTT_OK), (dict(N=0), C.TTT_OK),
+    # only the layer whose inner loop trains W2 alone by plain GD, without momentum
+    (dict(last_layer_only=0), C.TTT_ERR_UNSUPPORTED), (dict(rule=C.UPD_GD_L2), C.TTT_ERR_UNSUPPORTED),
+    (dict(rule=C.UPD_MUON), C.TTT_ERR_UNSUPPORTED), (dict(momentum=0.9), C.TTT_ERR_UNSUPPORTED),
+    (dict(chunk_rates=1), C.TTT_ERR_UNSUPPORTED), (dict(mask=C.MASK_TOKEN_CAUSAL), C.TTT_ERR_UNSUPPORTED),
+    (dict(d_h=48), C.TTT_ERR_INVALID_ARGUMENT), (dict(mask=C.MASK_STRIDED), C.TTT_ERR_INVALID_ARGUMENT),
+])
+def test_ttt_backward_validation(kw, status):
+    n = ctypes.c_size_t(0)
+    assert C.lib().ttt_backward_workspace_bytes(ctypes.byref(bwd_desc(**kw)), ctypes.byref(n)) == status
+
+
+def test_ttt_backward_workspace_and_rejects():
+    """Workspace: W1 | W3 and their transposes in bf16, phi(q), phi(k), their gradients, dA | dC of
+    both sides, the scans' dW2 and the dW1 | dW3 partials, then the linear-attention backward's
+    workspace over d_k = m, d_v = d.  Missing, misaligned or overlapping buffers and a short
+    workspace are refused before anything is enqueued."""
+    L = C.lib()
+    n = ctypes.c_size_t(0)
+    B, H, N, d, m, chunk = 2, 4, 256, 64, 128, 64
+    D = bwd_desc()
+    assert L.ttt_backward_workspace_bytes(ctypes.byref(D), ctypes.byref(n)) == C.TTT_OK
+    al = lambda x: (x + 255) // 256 * 256
+    S, dm, nc = B * H, d * m, N // chunk
+    # one token part: 4 weight tiles, and two parts of 2 * 2 * 256 / 2 positions would be under 1024
+    expect = 2 * al(H * 2 * dm * 2) + 4 * al(S * N * m * 2) + 2 * al(S * N * 2 * m * 2) + al(S * dm * 4) \
+        + al(1 * H * 2 * dm * 4) + 3 * al(S * nc * dm * 4)
+    assert n.value == expect
+    need = n.value
+    # no tokens: only the scans' dW2
+    assert L.ttt_backward_workspace_bytes(ctypes.byref(bwd_desc(N=0)), ctypes.byref(n)) == C.TTT_OK
+    assert n.value == al(S * dm * 4)
+    G = 1 << 30
+    ins = [P16, P16 + G, P16 + 2 * G, P16 + 3 * G, P16 + 4 * G, P16 + 5 * G, None]  # q k v eta W0 dO dW_out
+    OB = P16 + (1 << 34)
+    outs = [OB, OB + G, OB + 2 * G, OB + 3 * G, OB + 4 * G]                     # dq dk dv deta dW0
+    ws = P16 + (1 << 36)
+
+    def call(i=None, o=None, w=ws, nw=need):
+        a = list(ins if i is None else i)
+        b = list(outs if o is None else o)
+        return L.ttt_backward(ctypes.byref(D), *a, *b, w, nw, None)
+
+    assert call(i=[None] + ins[1:]) == C.TTT_ERR_INVALID_ARGUMENT                   # q missing
+    assert call(i=ins[:4] + [None] + ins[5:]) == C.TTT_ERR_INVALID_ARGUMENT         # W0 missing
+    assert call(o=outs[:3] + [None, outs[4]]) == C.TTT_ERR_INVALID_ARGUMENT         # deta missing
+    assert call(i=ins[:5] + [P16 + 5 * G + 8, None]) == C.TTT_ERR_INVALID_ARGUMENT  # misaligned dO
+    assert call(o=outs[:4] + [OB + 4 * G + 4]) == C.TTT_ERR_INVALID_ARGUMENT        # misaligned dW0
+    assert call(o=[P16 + 64] + outs[1:]) == C.TTT_ERR_INVALID_ARGUMENT              # dq overlaps q
+    assert b"overlaps" in L.ttt_last_error()
+    assert call(o=outs[:4] + [P16 + 4 * G + 16]) == C.TTT_ERR_INVALID_ARGUMENT      # dW0 overlaps W0
+    assert call(o=[OB, OB + 64] + outs[2:]) == C.TTT_ERR_INVALID_ARGUMENT           # dk overlaps dq
+    assert call(w=None, nw=0) == C.TTT_ERR_WORKSPACE
+    assert call(nw=need - 1) == C.TTT_ERR_WORKSPACE
+    assert call(w=ws + 16) == C.TTT_ERR_INVALID_ARGUMENT                            # not 256-aligned
+    # no (batch, head): nothing to do, no pointer is touched
+    assert L.ttt_backward(ctypes.byref(bwd_desc(B=0)), *([None] * 13), 0, None) == C.TTT_OK
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(C, "_lib", None)
     monkeypatch.setattr(C, "LIB_PATH", str(tmp_path / "missing.so"))
@@ -322,6 +387,11 @@ def test_valid_calls_without_a_device_report_device_error():
     assert L.linattn_backward(ctypes.byref(Dl), P16, P16 + G, P16 + 2 * G, P16 + 3 * G, None, P16 + 4 * G, None,
                               OB, OB + G, OB + 2 * G, OB + 3 * G, None, P16 + (1 << 36), n.value,
                               None) == C.TTT_ERR_DEVICE
+    Db = bwd_desc()
+    L.ttt_backward_workspace_bytes(ctypes.byref(Db), ctypes.byref(n))
+    assert L.ttt_backward(ctypes.byref(Db), P16, P16 + G, P16 + 2 * G, P16 + 3 * G, P16 + 4 * G, P16 + 5 * G, None,
+                          OB, OB + G, OB + 2 * G, OB + 3 * G, OB + 4 * G, P16 + (1 << 36), n.value,
+                          None) == C.TTT_ERR_DEVICE
     # the status table answers for any non-negative value
     assert L.ttt_status_string(C.TTT_ERR_DEVICE) == b"HIP device or launch error"
     assert L.ttt_status_string(0x7FFFFFFF) == b"unknown status"

@@ -14,7 +14,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "linear_attention_chunk_amd", "csrc")
-SOURCES = ["errors.hip", "profile.hip", "ttt_layer.hip", "linattn.hip", "swa.hip"]
+SOURCES = ["errors.hip", "profile.hip", "ttt_layer.hip", "ttt_backward.hip", "linattn.hip", "swa.hip"]
 
 
 def _hipcc():
@@ -31,7 +31,7 @@ def test_host_code_under_asan_and_ubsan(tmp_path):
     san = ["-Xarch_host", "-fsanitize=address,undefined", "-Xarch_host", "-fno-sanitize-recover=all"]
     common = ["--offload-arch=gfx950", "-O1", "-g", "-std=c++17", "-fno-omit-frame-pointer",
               "-Wno-unused-command-line-argument", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
-    # the four sources compile in parallel
+    # the sources compile in parallel
     procs = [subprocess.Popen([hipcc, *common, *san, "-fPIC", "-c", os.path.join(CSRC, s), "-o",
                                str(tmp_path / (s + ".o"))], stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
              for s in SOURCES]
