@@ -189,10 +189,10 @@ ttt_status ttt_forward_noalloc(const ttt_desc* desc, const void* q, const void* 
 
 /*
  * Device workspace that ttt_backward needs, in bytes (the size with dW0 requested, which covers a
- * call without it): the io-dtype copies of W1 | W3 and their transposes, phi(q), phi(k), their
- * gradients, dA | dC of both sides (16 m_h bytes per token and scan in bf16, twice in fp32), the
- * scans' dW2, the partial sums of dW1 | dW3, and the linear-attention backward's workspace over
- * d_k = m_h, d_v = d_h (linattn_backward_workspace_bytes).
+ * call without it): the io-dtype copies of W1 | W3 and their transposes, phi(q), phi(k), and the
+ * factors of phi's backward for both sides, later dA | dC (12 m_h bytes per token and scan in bf16,
+ * twice in fp32), the scans' dW2, the partial sums of dW1 | dW3, and the linear-attention
+ * backward's workspace over d_k = m_h, d_v = d_h (linattn_backward_workspace_bytes).
  */
 ttt_status ttt_backward_workspace_bytes(const ttt_desc* desc, size_t* bytes);
 
@@ -323,7 +323,7 @@ ttt_status swa_forward(const swa_desc* desc, const void* q, const void* k, const
  * read, and forgets them.  Kernel classes are numbered 0 .. TTT_PROF_KERNELS-1 and named by
  * ttt_profile_kernel_name.  Enabling or reading while another thread launches is allowed.
  */
-#define TTT_PROF_KERNELS 26
+#define TTT_PROF_KERNELS 25
 ttt_status ttt_profile_enable(int32_t on);
 /* Restricts the bracketing to the kernel classes i whose bit (1u << i) is set in mask; the
  * default is every class.  Each bracket records two events on the launch's stream, which costs

@@ -25,8 +25,8 @@ inline ttt_status fail(ttt_status s, const char* fmt, ...) {
 // kernel classes of the optional launch profiler (ttt_profile_*)
 enum ProfKernel { PK_UP = 0, PK_DOWN, PK_UPDATE, PK_MUON_PREP, PK_NS_INIT, PK_NS_GRAM, PK_NS_STEP, PK_LINATTN,
                   PK_LIN_DELTA, PK_LIN_SCAN, PK_LIN_APPLY, PK_PHI, PK_W13, PK_ZERO, PK_PAR_MOM, PK_SWA,
-                  PK_SWA_PREP, PK_LIN_BWD_T, PK_LIN_BWD_N, PK_LIN_DETA, PK_SWA_VPREP, PK_W13T, PK_PHI_BWD,
-                  PK_PHI_DX, PK_DW13, PK_DW_SUM };
+                  PK_SWA_PREP, PK_LIN_BWD_T, PK_LIN_BWD_N, PK_LIN_DETA, PK_SWA_VPREP, PK_W13T, PK_PHI_DX,
+                  PK_DW13, PK_DW_SUM };
 
 // Brackets one launch with events on its stream while profiling is enabled; no-op otherwise.
 struct ProfScope {
@@ -119,6 +119,8 @@ ttt_status validate_ttt_desc(const ttt_desc* D);
 // S0 of scan s at S0 + (s0_heads ? s % s0_heads : s) * s0_stride (null: zeros); dS_out of scan s at
 // dS_out + s * dso_stride (null: zeros); dS0 of scan s to dS0 + s * ds0_stride (null: not written).
 // The forward's chunk updates were escale * sum eta v k^T (the sign of ascent, repeated steps).
+// gate[0], gate[1]: both null, or [S][N][2 d_k] buffers of io-dtype factors u | w for dq and dk:
+// then dq and dk are not written; each gate row becomes dq u | dq w (dk u | dk w) in place.
 struct LinBwdIO {
     const float* S0 = nullptr;
     int64_t s0_stride = 0;
@@ -128,6 +130,7 @@ struct LinBwdIO {
     float* dS0 = nullptr;
     int64_t ds0_stride = 0;
     float escale = 1.f;
+    void* gate[2] = {nullptr, nullptr};
 };
 // the backward's checks of a linear-attention descriptor
 ttt_status validate_lin_desc_bwd(const linattn_desc* D);

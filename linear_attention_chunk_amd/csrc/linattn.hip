@@ -883,6 +883,7 @@ template <typename T> struct BwdTJob {
     int skip;          // strided mask: rows of chunks that do not update are zero
     const T* kk;       // dk job: the keys, for deta_s = k_s . (R^T v_s) from the unscaled rows
     float* deta;       // dk job: deta, or its per-column-tile partials (ntok apart); null for dq
+    T* gate;           // GATE: rows of 2 d_k holding factors u | w, overwritten by g u | g w
 };
 template <typename T> struct BwdTArgs {
     BwdTJob<T> job[2];
@@ -891,7 +892,11 @@ template <typename T> struct BwdTArgs {
     uint32_t flags[32];
 };
 
-template <typename T>
+// GATE: a job's result g (dq or dk) is not stored; the row's factors u (columns 0 .. d_k-1) and w
+// (d_k .. 2 d_k-1) of the job's gate buffer are read and replaced by g u and g w, each element by the
+// thread that reads it (the gradient carried on through an elementwise product, e.g. the TTT layer's
+// SwiGLU features).
+template <typename T, bool GATE>
 __global__ __launch_bounds__(kThreads, 2) void k_lin_bwd_t(BwdTArgs<T> a) {
     constexpr int PLANES = sizeof(T) == 2 ? 2 : 1;
     using TB = Tile<T, kApplyRows, kApplyCols, 1, 2, 1, PLANES, PLANES, false, true>;
@@ -910,11 +915,16 @@ __global__ __launch_bounds__(kThreads, 2) void k_lin_bwd_t(BwdTArgs<T> a) {
     const int nl = (int)std::min<int64_t>(a.chunk, a.N - (int64_t)c * a.chunk);
     if (r0 >= nl) return;  // uniform per workgroup
     const int rows = std::min(kApplyRows, nl - r0), cols = std::min(kApplyCols, a.dk - c0);
-    T* O = jb.out + (tok + r0) * a.dk + c0;
+    // output rows: dk elements apart, or 2 dk in the gate buffer (g u here, g w dk further on)
+    const uint32_t ld = GATE ? 2u * (uint32_t)a.dk : (uint32_t)a.dk;
+    T* O = (GATE ? jb.gate : jb.out) + (tok + r0) * ld + c0;
     float* de = jb.deta ? jb.deta + (int64_t)(t % a.ntn) * a.ntok + tok + r0 : nullptr;
     if (jb.skip && a.mode == TTT_MASK_STRIDED && !((a.flags[c >> 5] >> (c & 31)) & 1u)) {
-        for (int e = threadIdx.x; e < rows * cols; e += kThreads)
-            O[(uint32_t)(e / cols) * (uint32_t)a.dk + (uint32_t)(e % cols)] = Elt<T>::st(0.f);
+        for (int e = threadIdx.x; e < rows * cols; e += kThreads) {
+            const uint32_t off = (uint32_t)(e / cols) * ld + (uint32_t)(e % cols);
+            O[off] = Elt<T>::st(0.f);
+            if (GATE) O[off + a.dk] = Elt<T>::st(0.f);
+        }
         if (de)
             for (int e = threadIdx.x; e < rows; e += kThreads) de[e] = 0.f;
         return;
@@ -954,9 +964,19 @@ __global__ __launch_bounds__(kThreads, 2) void k_lin_bwd_t(BwdTArgs<T> a) {
     tl.template rows_via_lds<1>(smem, [&](int idx, int, int row, int col, const float4& v) {
         pd[idx] = 0.f;
         if (row < rows && col < cols) {
-            const uint32_t off = (uint32_t)row * (uint32_t)a.dk + (uint32_t)col;
             const float f = K ? ef[idx] * a.es : 1.f;
-            Pack4<T>::store(O + off, v.x * f, v.y * f, v.z * f, v.w * f);
+            if constexpr (GATE) {
+                const uint32_t off = (uint32_t)row * ld + (uint32_t)col;
+                float u[4], w[4];
+                Pack4<T>::unpack(Pack4<T>::load_raw(O + off), u);
+                Pack4<T>::unpack(Pack4<T>::load_raw(O + off + a.dk), w);
+                const float g[4] = {v.x * f, v.y * f, v.z * f, v.w * f};
+                Pack4<T>::store(O + off, g[0] * u[0], g[1] * u[1], g[2] * u[2], g[3] * u[3]);
+                Pack4<T>::store(O + off + a.dk, g[0] * w[0], g[1] * w[1], g[2] * w[2], g[3] * w[3]);
+            } else {
+                const uint32_t off = (uint32_t)row * (uint32_t)a.dk + (uint32_t)col;
+                Pack4<T>::store(O + off, v.x * f, v.y * f, v.z * f, v.w * f);
+            }
             if (K) {
                 float kv[4];
                 Pack4<T>::unpack(kr[idx], kv);
@@ -1119,8 +1139,9 @@ ttt_status lin_chunked_bwd(const linattn_desc& D, const uint32_t (&flags)[32], c
     const int ntk = (int)cdiv(D.d_k, kApplyCols);  // column tiles of dq, dk (and deta partials)
     float* de = ntk > 1 ? part : deta;
     BwdTArgs<T> ta{};
-    ta.job[0] = BwdTJob<T>{dO, Sc, dq, nullptr, 0, nullptr, nullptr};
-    ta.job[1] = BwdTJob<T>{v, R, dk, eta, 1, k, de};
+    const bool gate = io.gate[0] != nullptr;
+    ta.job[0] = BwdTJob<T>{dO, Sc, dq, nullptr, 0, nullptr, nullptr, (T*)io.gate[0]};
+    ta.job[1] = BwdTJob<T>{v, R, dk, eta, 1, k, de, (T*)io.gate[1]};
     ta.N = D.N;
     ta.ntok = S * D.N;
     ta.dk = D.d_k;
@@ -1135,7 +1156,8 @@ ttt_status lin_chunked_bwd(const linattn_desc& D, const uint32_t (&flags)[32], c
     for (int w = 0; w < 32; ++w) ta.flags[w] = flags[w];
     {
         ProfScope ps(PK_LIN_BWD_T, st);
-        hipLaunchKernelGGL(k_lin_bwd_t<T>, dim3((unsigned)(2 * ta.per_job)), dim3(kThreads), 0, st, ta);
+        if (gate) hipLaunchKernelGGL((k_lin_bwd_t<T, true>), dim3((unsigned)(2 * ta.per_job)), dim3(kThreads), 0, st, ta);
+        else hipLaunchKernelGGL((k_lin_bwd_t<T, false>), dim3((unsigned)(2 * ta.per_job)), dim3(kThreads), 0, st, ta);
     }
     if ((rc = check_launch("k_lin_bwd_t", st)) != TTT_OK) return rc;
     BwdNArgs<T> na{};

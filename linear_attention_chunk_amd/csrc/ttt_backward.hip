@@ -5,11 +5,11 @@
 // W2, phi(x) = SiLU(W1 x) o (W3 x) (PaperTrace "5.2.1 LaCT and TTT-E2E", Eq. (3)), so its gradients
 // are those of linear attention followed by the chain rule through phi:
 //   w13t   W1^T | W3^T as [d][2m] contraction operands (and W1 | W3 in bf16 for phi)
-//   phi    phi(q), phi(k) on MFMA (the forward's feature kernel)
-//   linear the chunked linear-attention backward over (phi(q), phi(k), v) with state W2
-//          -> dphi(q), dphi(k), dv, deta, dW2
-//   dphi   a = x W1^T, c = x W3^T again on MFMA; dA = dphi c SiLU'(a), dC = dphi SiLU(a) in the
-//          epilogue, stored side by side as [N][2m]
+//   phi    a = x W1^T, c = x W3^T on MFMA for q and k; the epilogue writes phi = SiLU(a) c and,
+//          side by side in rows of 2m, the factors u = c SiLU'(a) and w = SiLU(a)
+//   linear the chunked linear-attention backward over (phi(q), phi(k), v) with state W2 -> dv,
+//          deta, dW2; its dq and dk (the gradients g of phi(q), phi(k)) never leave the product
+//          kernel's epilogue, which turns each u | w row into dA = g u | dC = g w in place
 //   dx     dq, dk = [dA | dC] [W1; W3] on MFMA (contraction over 2m)
 //   dw13   dW1 | dW3 = [dA | dC]^T x over the tokens of q and k (and the batch, for per-head
 //          weights), split over token ranges into partial buffers
@@ -207,7 +207,7 @@ static int dw_parts(int64_t tiles, int64_t total) {
 }
 
 struct BLayout {
-    size_t w13, w13t, ph[2], dph[2], dac[2], dw2, part, lin, total;
+    size_t w13, w13t, ph[2], dac[2], dw2, part, lin, total;
     int nparts;
     int64_t lp;
 };
@@ -227,8 +227,7 @@ static BLayout make_blayout(const ttt_desc& D, bool want_dw) {
         if (es == 2) L.w13 = take((size_t)nw * 2 * dm * es);
         L.w13t = take((size_t)nw * 2 * dm * es);
         for (int i = 0; i < 2; ++i) L.ph[i] = take((size_t)S * D.N * m * es);
-        for (int i = 0; i < 2; ++i) L.dph[i] = take((size_t)S * D.N * m * es);
-        for (int i = 0; i < 2; ++i) L.dac[i] = take((size_t)S * D.N * 2 * m * es);
+        for (int i = 0; i < 2; ++i) L.dac[i] = take((size_t)S * D.N * 2 * m * es);  // u | w, then dA | dC
     }
     if (want_dw) {
         L.dw2 = take((size_t)S * dm * 4);
@@ -277,7 +276,6 @@ static ttt_status run_backward(const ttt_desc& D, const BLayout& L, const T* q, 
     const int w_heads = D.w0_per_batch ? 0 : D.H;
     ttt_status rc;
     T* ph[2] = {(T*)(ws + L.ph[0]), (T*)(ws + L.ph[1])};
-    T* dph[2] = {(T*)(ws + L.dph[0]), (T*)(ws + L.dph[1])};
     T* dac[2] = {(T*)(ws + L.dac[0]), (T*)(ws + L.dac[1])};
     T* Wt = (T*)(ws + L.w13t);
     float* dW2 = dW0 ? (float*)(ws + L.dw2) : nullptr;
@@ -306,12 +304,12 @@ static ttt_status run_backward(const ttt_desc& D, const BLayout& L, const T* q, 
                                W0, 3 * dm, Wt, (int)d, (int)m);
         }
         if ((rc = check_launch("k_w13t_cvt", st)) != TTT_OK) return rc;
-        // 2. the features of every query and key
-        PhiArgs<T> pa{{q, k}, {ph[0], ph[1]}, {nullptr, nullptr}, W13, w13_stride, w_heads, D.N, (int)d, (int)m,
+        // 2. the features of every query and key, and the factors u | w of their backward
+        PhiArgs<T> pa{{q, k}, {ph[0], ph[1]}, {dac[0], dac[1]}, W13, w13_stride, w_heads, D.N, (int)d, (int)m,
                       (int)S, (int)cdiv(D.N, kPhiRows), (int)cdiv(m, kPhiCols)};
         {
             ProfScope ps(PK_PHI, st);
-            hipLaunchKernelGGL((k_phi<T, false>), dim3((unsigned)(2 * S * pa.ntt * pa.nct)), dim3(64 * kPhiWaves), 0,
+            hipLaunchKernelGGL((k_phi<T, true>), dim3((unsigned)(2 * S * pa.ntt * pa.nct)), dim3(64 * kPhiWaves), 0,
                                st, pa);
         }
         if ((rc = check_launch("k_phi", st)) != TTT_OK) return rc;
@@ -331,27 +329,15 @@ static ttt_status run_backward(const ttt_desc& D, const BLayout& L, const T* q, 
     io.dS0 = dW2;
     io.ds0_stride = dm;
     io.escale = (D.ascent ? -1.0f : 1.0f) * (float)(D.inner_steps > 1 ? D.inner_steps : 1);
-    if ((rc = lin_chunked_bwd<T>(LD, flags, ph[0], ph[1], v, eta, dO, io, dph[0], dph[1], dv, deta, ws + L.lin, st)) !=
-        TTT_OK)
+    if (D.N > 0) {  // the gradients of phi(q), phi(k) turn u | w into dA | dC
+        io.gate[0] = dac[0];
+        io.gate[1] = dac[1];
+    }
+    if ((rc = lin_chunked_bwd<T>(LD, flags, ph[0], ph[1], v, eta, dO, io, nullptr, nullptr, dv, deta, ws + L.lin,
+                                 st)) != TTT_OK)
         return rc;
     if (D.N > 0) {
-        // 4. dA | dC from dphi, with a and c formed again
-        PhiArgs<T> pb{{q, k}, {dac[0], dac[1]}, {dph[0], dph[1]}, nullptr, 0, w_heads, D.N, (int)d, (int)m, (int)S,
-                      (int)cdiv(D.N, kPhiRows), (int)cdiv(m, kPhiCols)};
-        if constexpr (sizeof(T) == 2) {
-            pb.W = (const T*)(ws + L.w13);
-            pb.w_stride = 2 * dm;
-        } else {
-            pb.W = reinterpret_cast<const T*>(W0);
-            pb.w_stride = 3 * dm;
-        }
-        {
-            ProfScope ps(PK_PHI_BWD, st);
-            hipLaunchKernelGGL((k_phi<T, true>), dim3((unsigned)(2 * S * pb.ntt * pb.nct)), dim3(64 * kPhiWaves), 0,
-                               st, pb);
-        }
-        if ((rc = check_launch("k_phi (backward)", st)) != TTT_OK) return rc;
-        // 5. dq, dk
+        // 4. dq, dk
         DxArgs<T> xa{{dac[0], dac[1]}, {dq, dk}, Wt, w_heads, D.N, (int)d, (int)m, (int)S,
                      (int)cdiv(D.N, kDxRows), (int)cdiv(d, kDxCols)};
         {
@@ -359,7 +345,7 @@ static ttt_status run_backward(const ttt_desc& D, const BLayout& L, const T* q, 
             hipLaunchKernelGGL(k_phi_dx<T>, dim3((unsigned)(2 * S * xa.ntt * xa.ntd)), dim3(kThreads), 0, st, xa);
         }
         if ((rc = check_launch("k_phi_dx", st)) != TTT_OK) return rc;
-        // 6. dW1 | dW3 partials
+        // 5. dW1 | dW3 partials
         if (dW0) {
             DwArgs<T> wa{{dac[0], dac[1]}, {q, k}, (float*)(ws + L.part), (int)nw, D.w0_per_batch ? 1 : D.B, D.H,
                          D.w0_per_batch ? 0 : 1, D.N, L.lp, (int)d, (int)m, (int)cdiv(m, kDwRows),
@@ -372,7 +358,7 @@ static ttt_status run_backward(const ttt_desc& D, const BLayout& L, const T* q, 
             if ((rc = check_launch("k_dw13", st)) != TTT_OK) return rc;
         }
     }
-    // 7. dW0
+    // 6. dW0
     if (dW0) {
         DwSumArgs sa{D.N > 0 ? (const float*)(ws + L.part) : nullptr, L.nparts, dW2, dWo, dW0, (int)nw,
                      D.w0_per_batch ? 1 : D.B, D.H, D.w0_per_batch ? 0 : 1, dm};

@@ -307,9 +307,9 @@ def test_ttt_backward_validation(kw, status):
 
 
 def test_ttt_backward_workspace_and_rejects():
-    """Workspace: W1 | W3 and their transposes in bf16, phi(q), phi(k), their gradients, dA | dC of
-    both sides, the scans' dW2 and the dW1 | dW3 partials, then the linear-attention backward's
-    workspace over d_k = m, d_v = d.  Missing, misaligned or overlapping buffers and a short
+    """Workspace: W1 | W3 and their transposes in bf16, phi(q), phi(k), the factors of phi's backward
+    (later dA | dC) of both sides, the scans' dW2 and the dW1 | dW3 partials, then the
+    linear-attention backward's workspace over d_k = m, d_v = d.  Missing, misaligned or overlapping buffers and a short
     workspace are refused before anything is enqueued."""
     L = C.lib()
     n = ctypes.c_size_t(0)
@@ -319,7 +319,7 @@ def test_ttt_backward_workspace_and_rejects():
     al = lambda x: (x + 255) // 256 * 256
     S, dm, nc = B * H, d * m, N // chunk
     # one token part: 4 weight tiles, and two parts of 2 * 2 * 256 / 2 positions would be under 1024
-    expect = 2 * al(H * 2 * dm * 2) + 4 * al(S * N * m * 2) + 2 * al(S * N * 2 * m * 2) + al(S * dm * 4) \
+    expect = 2 * al(H * 2 * dm * 2) + 2 * al(S * N * m * 2) + 2 * al(S * N * 2 * m * 2) + al(S * dm * 4) \
         + al(1 * H * 2 * dm * 4) + 3 * al(S * nc * dm * 4)
     assert n.value == expect
     need = n.value
