@@ -507,6 +507,38 @@ def main():
             "recurrence_ms_per_call": round(msp[False], 3), "parallel_form_ms_per_call": round(msp[True], 3),
             "parallel_form_tokens_per_s": round(tokens / (msp[True] * 1e-3)),
             "parallel_form_speedup": round(msp[False] / msp[True], 2)}
+        # its backward (the outer-loop gradients of q, k, v, eta and W0 from dO), the training-side twin
+        print("[bench] extras: last-layer GD backward", file=sys.stderr, flush=True)
+        gb = torch.Generator(device="cuda")
+        gb.manual_seed(3600 + args.seed)
+        dOl = (torch.randn((B, H, N, d), generator=gb, device="cuda") / d ** 0.5).to(torch.bfloat16)
+        Dg, _ = T.ttt_desc(B, H, N, d, m, chunk, C.TTT_BF16, C.MASK_APPLY_THEN_UPDATE, C.UPD_GD, 0, 0.0,
+                           last_layer_only=True)
+        wsg = torch.empty(T.ttt_backward_workspace_bytes(Dg), dtype=torch.uint8, device="cuda")
+        lbwd = lambda: T.ttt_backward(q, k, v, eta, W0, dOl, chunk, C.MASK_APPLY_THEN_UPDATE, m_h=m,  # noqa: E731
+                                      workspace=wsg)
+        msg = time_calls(torch, lbwd, st, 1)
+        C.profile_select(None)
+        C.profile_enable(True)
+        C.profile_read()
+        for _ in range(3):
+            lbwd()
+        torch.cuda.synchronize()
+        gk = {kn: round(t / 3, 4) for kn, (t, n) in C.profile_read().items() if n}
+        C.profile_enable(False)
+        # algorithmic flops per token and scan: the features again (a and c of q and k, 8 d m), the
+        # linear-attention backward over d_k = m, d_v = d (the chunk states again, the query-gradient
+        # sums, dphi(q), dphi(k), dv: 10 d m), dq and dk (8 d m), dW1 and dW3 (8 d m)
+        gflops = tokens * H * 34 * d * m
+        extras["lact_lm_last_layer_gd_backward"] = {
+            "workload": f"B{B} H{H} N{N} d{d} m{m} chunk {chunk} bf16, apply-then-update, only W2 learns (plain "
+                        "GD): gradients of q, k, v, eta and the per-head W0 from dO",
+            "ms_per_call": round(msg, 3), "tokens_per_s": round(tokens / (msg * 1e-3)),
+            "algorithmic_tflop": round(gflops / 1e12, 3),
+            "mfma_frac": round(gflops / (msg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "over_parallel_forward": round(msg / msp[True], 2),
+            "training_step_ms": round(msg + msp[True], 3), "kernels_ms": gk}
+        del dOl, wsg
         # Variant 2 of the paper's ablation: only W2 learns, momentum 0.9, per-token eta and Muon (5
         # Newton-Schulz steps) kept, no weight norm; chunk recurrence against the parallel form
         print("[bench] extras: Variant 2 (last layer, Muon + momentum), recurrence and parallel form",

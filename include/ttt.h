@@ -218,9 +218,9 @@ ttt_status ttt_backward_workspace_bytes(const ttt_desc* desc, size_t* bytes);
  *   workspace device buffer of at least ttt_backward_workspace_bytes(desc) bytes, 256-byte aligned
  *             (may be NULL when that is 0); TTT_ERR_WORKSPACE if it is too small
  * No output may overlap an input or another output (TTT_ERR_INVALID_ARGUMENT).  Products run in the
- * io dtype with fp32 accumulation (bf16: phi, its gradient, dA | dC and W1 | W3 are rounded to bf16
- * as contraction operands; the linear-attention states are bf16 hi + lo pairs), and every sum is
- * taken in a fixed order, so results do not depend on scheduling.
+ * io dtype with fp32 accumulation (bf16: phi, dA | dC, W1 | W3 and the linear-attention states and
+ * state gradients are rounded to bf16 as contraction operands; the states are summed in fp32), and
+ * every sum is taken in a fixed order, so results do not depend on scheduling.
  */
 ttt_status ttt_backward(const ttt_desc* desc, const void* q, const void* k, const void* v,
                         const float* eta, const float* W0, const void* dO, const float* dW_out,
@@ -252,9 +252,9 @@ ttt_status linattn_forward(const linattn_desc* desc, const void* q, const void* 
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Device workspace that linattn_backward needs, in bytes: the update, the state and the state
- * gradient of every chunk and scan (12 bytes per state element per chunk), plus B*H*N*4 bytes per
- * 128 columns of d_k when d_k > 128; zero when N is 0.
+ * Device workspace that linattn_backward needs, in bytes: the update (fp32), the state and the
+ * state gradient (io dtype) of every chunk and scan (8 bytes per state element per chunk in bf16,
+ * 12 in fp32), plus B*H*N*4 bytes per 128 columns of d_k when d_k > 128; zero when N is 0.
  */
 ttt_status linattn_backward_workspace_bytes(const linattn_desc* desc, size_t* bytes);
 
@@ -274,9 +274,9 @@ ttt_status linattn_backward_workspace_bytes(const linattn_desc* desc, size_t* by
  *   workspace device buffer of at least linattn_backward_workspace_bytes(desc) bytes, 256-byte
  *             aligned (may be NULL when that is 0); TTT_ERR_WORKSPACE if it is too small
  * Pointer alignment: q, k, v, dO, dq, dk, dv 16 bytes; the fp32 buffers 4 bytes.  No output may
- * overlap an input or another output (TTT_ERR_INVALID_ARGUMENT).  The gradients are computed as
- * the forward computes o: bf16 products with fp32 accumulation, the chunk states and state
- * gradients held as bf16 hi + lo pairs (fp32 in fp32 mode).
+ * overlap an input or another output (TTT_ERR_INVALID_ARGUMENT).  Products run in the io dtype
+ * with fp32 accumulation; the chunk states and state gradients are summed in fp32 and enter the
+ * products rounded once to the io dtype (the forward's apply keeps bf16 states as hi + lo pairs).
  */
 ttt_status linattn_backward(const linattn_desc* desc, const void* q, const void* k, const void* v,
                             const float* eta, const float* S0, const void* dO, const float* dS_out,

@@ -458,6 +458,7 @@ template <typename T> struct ScanArgs {
     LinStateIO io;
     int64_t dvk;   // d_v * d_k
     int nc, mode, nscan, rev;
+    int planes;    // bf16: 2 (hi + lo) or 1 (the state rounded once); fp32: 1
     uint32_t flags[32];
 };
 
@@ -480,8 +481,8 @@ __global__ __launch_bounds__(kThreads) void k_lin_scan(ScanArgs<T> a) {
         for (int u = 0; u < 4; ++u) mom[u] = io.msign * io.M0[scan * io.m_stride + e + u];
     const bool post = a.mode == TTT_MASK_UPDATE_THEN_APPLY || a.mode == TTT_MASK_FULL;
     auto put = [&](int c) {
-        T* dst = a.Sc + ((scan * a.nc + c) * PLANES) * a.dvk + e;
-        if constexpr (PLANES == 2) {
+        T* dst = a.Sc + ((scan * a.nc + c) * a.planes) * a.dvk + e;
+        if (PLANES == 2 && a.planes == 2) {
             float lo[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) lo[u] = st[u] - bf2f(f2bf(st[u]));
@@ -781,7 +782,7 @@ static ttt_status launch_delta(const linattn_desc& D, int64_t chunk, int64_t nc,
 // Launch of the scan over the chunks of every scan (forward, or backward with rev)
 template <typename T>
 static ttt_status launch_scan(const linattn_desc& D, int64_t nc, int mode, const uint32_t (&flags)[32], const float* src,
-                              T* Sc, const LinStateIO& io, int rev, hipStream_t st) {
+                              T* Sc, const LinStateIO& io, int rev, int planes, hipStream_t st) {
     const int64_t S = (int64_t)D.B * D.H, dvk = (int64_t)D.d_v * D.d_k;
     ScanArgs<T> sa{};
     sa.dS = src;
@@ -792,6 +793,7 @@ static ttt_status launch_scan(const linattn_desc& D, int64_t nc, int mode, const
     sa.mode = mode;
     sa.nscan = (int)S;
     sa.rev = rev;
+    sa.planes = planes;
     for (int w = 0; w < 32; ++w) sa.flags[w] = flags[w];
     {
         ProfScope ps(PK_LIN_SCAN, st);
@@ -815,7 +817,8 @@ static ttt_status run_lin_parallel(const linattn_desc& D, LinArgs<T> a, char* ws
     const float* scan_src = dS;
     if (io.between && (rc = io.between(io.between_ctx, dS, &scan_src, st)) != TTT_OK) return rc;
     // 2. states seen by each chunk, and S_out (a causal block sees the state before it)
-    rc = launch_scan<T>(D, nc, causal ? TTT_MASK_APPLY_THEN_UPDATE : D.mask, a.flags, scan_src, Sc, io, 0, st);
+    rc = launch_scan<T>(D, nc, causal ? TTT_MASK_APPLY_THEN_UPDATE : D.mask, a.flags, scan_src, Sc, io, 0,
+                        sizeof(T) == 2 ? 2 : 1, st);
     if (rc != TTT_OK) return rc;
     // 3. apply
     ApplyArgs<T> aa{};
@@ -867,16 +870,19 @@ template ttt_status lin_chunked_run<float>(const linattn_desc&, const uint32_t (
 // dk_s = eta_s R_j^T v_s, deta_s = v_s . (R_j k_s), and dS0 = dS_out + sum_c D_c.  A chunk that a
 // strided mask does not update gets zero dk, dv and deta.  Launches: the forward's delta and scan
 // (S_c), the delta kernel with unit weights over (q, dO) into the same dS buffer (D_c), the scan
-// walked backwards (R_j as bf16 hi + lo planes or fp32, and dS0), then the two product kernels.
+// walked backwards (R_j and dS0), then the two product kernels.  The scans carry fp32; the products
+// read S_c and R_j as one io-dtype plane (bf16: the state rounded once, as the products' other
+// operands are), where the forward's apply reads bf16 states as hi + lo pairs.
+constexpr int kBwdPlanes = 1;
 
 // dq = dO S_c and dk = diag(eta) v R_c for one chunk: tokens x d_k, contracting over d_v.  The
-// d_v x d_k matrix goes through the transposing stager (its d_k index is the tile column); bf16
-// keeps it as hi + lo planes whose two accumulators are added before the epilogue.  One launch
-// covers both jobs: the first per_job workgroups do dq, the others dk.  The tile leaves row by row
-// through LDS, since the transposed operand permutes the accumulator columns.  The dk job also forms
-// deta_s = k_s . w_s with w_s = R^T v_s (its rows before the eta factor) over the tile's d_k columns:
-// each thread takes 4 columns of 16 rows; a butterfly over the 32 lanes that share each row leaves
-// the row sums on the even lanes.
+// d_v x d_k matrix goes through the transposing stager (its d_k index is the tile column).  One
+// launch covers both jobs: the first per_job workgroups do dq, the others dk.  The tile leaves row by
+// row through LDS, since the transposed operand permutes the accumulator columns.  The dk job also
+// forms deta_s = k_s . w_s with w_s = R^T v_s (its rows before the eta factor) over the tile's d_k
+// columns: each thread takes 4 columns of 16 rows; a butterfly over the 32 lanes that share each row
+// leaves the row sums on the even lanes.
+
 template <typename T> struct BwdTJob {
     const T* y; const T* M; T* out;
     const float* eta;  // row factors (dk), or null (dq)
@@ -898,7 +904,7 @@ template <typename T> struct BwdTArgs {
 // SwiGLU features).
 template <typename T, bool GATE>
 __global__ __launch_bounds__(kThreads, 2) void k_lin_bwd_t(BwdTArgs<T> a) {
-    constexpr int PLANES = sizeof(T) == 2 ? 2 : 1;
+    constexpr int PLANES = kBwdPlanes;
     using TB = Tile<T, kApplyRows, kApplyCols, 1, 2, 1, PLANES, PLANES, false, true>;
     using PM = typename std::conditional<PLANES == 2, PMQ, PM1>::type;
     static_assert(TB::RV_LDS <= TB::LDS, "row bands fit the tile's LDS");
@@ -1019,7 +1025,7 @@ template <typename T> struct BwdNArgs {
 
 template <typename T>
 __global__ __launch_bounds__(kThreads, 2) void k_lin_bwd_n(BwdNArgs<T> a) {
-    constexpr int PLANES = sizeof(T) == 2 ? 2 : 1;
+    constexpr int PLANES = kBwdPlanes;
     using TA = Tile<T, kApplyRows, kApplyCols, 1, 2, 1, PLANES, PLANES, false, false>;
     using PM = typename std::conditional<PLANES == 2, PMQ, PM1>::type;
     __shared__ __attribute__((aligned(16))) char smem[TA::LDS];
@@ -1090,11 +1096,12 @@ ttt_status validate_lin_desc_bwd(const linattn_desc* D) {
     return TTT_OK;
 }
 
+// dS_c (fp32), then S_c and R_c (one io-dtype plane each), then the deta partials
 size_t lin_chunked_bwd_ws_bytes(const linattn_desc& D) {
     if (D.N == 0) return 0;
     const int64_t S = (int64_t)D.B * D.H, nc = cdiv(D.N, D.chunk), ntn = cdiv(D.d_k, kApplyCols);
-    const size_t sb = align256((size_t)(S * nc * (int64_t)D.d_v * D.d_k * 4));
-    return 3 * sb + (ntn > 1 ? align256((size_t)(ntn * S * D.N * 4)) : 0);
+    const size_t es = D.io_dtype == TTT_BF16 ? 2 : 4, n = (size_t)(S * nc * (int64_t)D.d_v * D.d_k);
+    return align256(n * 4) + 2 * align256(n * es) + (ntn > 1 ? align256((size_t)(ntn * S * D.N * 4)) : 0);
 }
 
 template <typename T>
@@ -1103,11 +1110,11 @@ ttt_status lin_chunked_bwd(const linattn_desc& D, const uint32_t (&flags)[32], c
                            char* ws, hipStream_t st) {
     const int64_t S = (int64_t)D.B * D.H, dvk = (int64_t)D.d_v * D.d_k;
     const int64_t chunk = D.chunk, nc = D.N ? cdiv(D.N, chunk) : 0;
-    const size_t sb = align256((size_t)(S * nc * dvk * 4));
+    const size_t sb = align256((size_t)(S * nc * dvk * 4)), tb = align256((size_t)(S * nc * dvk) * sizeof(T));
     float* dS = (float*)ws;
     T* Sc = (T*)(ws + sb);
-    T* R = (T*)(ws + 2 * sb);
-    float* part = (float*)(ws + 3 * sb);
+    T* R = (T*)(ws + sb + tb);
+    float* part = (float*)(ws + sb + 2 * tb);
     uint32_t all[32];
     for (int w = 0; w < 32; ++w) all[w] = ~0u;
     ttt_status rc;
@@ -1119,7 +1126,7 @@ ttt_status lin_chunked_bwd(const linattn_desc& D, const uint32_t (&flags)[32], c
         fio.s0_stride = io.s0_stride;
         fio.s0_heads = io.s0_heads;
         fio.dsign = io.escale;
-        if ((rc = launch_scan<T>(D, nc, D.mask, flags, dS, Sc, fio, 0, st)) != TTT_OK) return rc;
+        if ((rc = launch_scan<T>(D, nc, D.mask, flags, dS, Sc, fio, 0, kBwdPlanes, st)) != TTT_OK) return rc;
         // D_c = sum over the chunk of dO q^T, every chunk
         if ((rc = launch_delta<T, false>(D, chunk, nc, TTT_MASK_APPLY_THEN_UPDATE, all, q, dO, nullptr, dS, st)) !=
             TTT_OK)
@@ -1133,7 +1140,7 @@ ttt_status lin_chunked_bwd(const linattn_desc& D, const uint32_t (&flags)[32], c
     rio.Sout = io.dS0;
     rio.sout_stride = io.ds0_stride;
     if (D.N > 0 || io.dS0)
-        if ((rc = launch_scan<T>(D, nc, D.mask, all, dS, R, rio, 1, st)) != TTT_OK) return rc;
+        if ((rc = launch_scan<T>(D, nc, D.mask, all, dS, R, rio, 1, kBwdPlanes, st)) != TTT_OK) return rc;
     if (D.N == 0) return TTT_OK;
     const int ntt = (int)cdiv(std::min<int64_t>(chunk, D.N), kApplyRows);
     const int ntk = (int)cdiv(D.d_k, kApplyCols);  // column tiles of dq, dk (and deta partials)
