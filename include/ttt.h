@@ -230,9 +230,9 @@ ttt_status ttt_backward(const ttt_desc* desc, const void* q, const void* k, cons
 /*
  * Device workspace that linattn_forward needs, in bytes.  Zero when the call runs the sequential
  * kernel (chunks so small that 4 d_k d_v > 2 chunk (d_k + d_v), or token-causal mode with N < 256);
- * otherwise room for every chunk's own update and the state each chunk's queries see, 8 bytes per
- * state element per chunk and scan (the chunk-parallel path; token-causal mode counts chunks of
- * 128 tokens).
+ * otherwise room for every chunk's own update (fp32) and the state each chunk's queries see (io
+ * dtype), 6 bytes per state element per chunk and scan in bf16, 8 in fp32 (the chunk-parallel path;
+ * token-causal mode counts chunks of 128 tokens).
  */
 ttt_status linattn_workspace_bytes(const linattn_desc* desc, size_t* bytes);
 
@@ -246,6 +246,9 @@ ttt_status linattn_workspace_bytes(const linattn_desc* desc, size_t* bytes);
  *   S_out     nullable; [B][H][d_v][d_k] fp32 state after the last chunk
  *   workspace device buffer of at least linattn_workspace_bytes(desc) bytes, 256-byte aligned
  *             (may be NULL when that is 0); TTT_ERR_WORKSPACE if it is too small
+ * The state is carried in fp32.  Products run in the io dtype with fp32 accumulation: the
+ * chunk-parallel path hands each chunk's state to the apply rounded once to the io dtype, the
+ * sequential kernel keeps a bf16 hi + lo copy of it (about 16 bits).
  */
 ttt_status linattn_forward(const linattn_desc* desc, const void* q, const void* k, const void* v,
                            const float* eta, const float* S0, void* o, float* S_out,
@@ -276,7 +279,7 @@ ttt_status linattn_backward_workspace_bytes(const linattn_desc* desc, size_t* by
  * Pointer alignment: q, k, v, dO, dq, dk, dv 16 bytes; the fp32 buffers 4 bytes.  No output may
  * overlap an input or another output (TTT_ERR_INVALID_ARGUMENT).  Products run in the io dtype
  * with fp32 accumulation; the chunk states and state gradients are summed in fp32 and enter the
- * products rounded once to the io dtype (the forward's apply keeps bf16 states as hi + lo pairs).
+ * products rounded once to the io dtype, as in the forward.
  */
 ttt_status linattn_backward(const linattn_desc* desc, const void* q, const void* k, const void* v,
                             const float* eta, const float* S0, const void* dO, const float* dS_out,

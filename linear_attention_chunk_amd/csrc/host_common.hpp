@@ -105,8 +105,8 @@ struct LinStateIO {
     ttt_status (*between)(void* ctx, float* dS, const float** src, hipStream_t st) = nullptr;
     void* between_ctx = nullptr;
 };
-// workspace of lin_chunked_run: dS_c (fp32) and S_c (bf16 hi + lo, or fp32) per chunk
-size_t lin_chunked_ws_bytes(int64_t nscan, int64_t nchunks, int d_k, int d_v);
+// workspace of lin_chunked_run: dS_c (fp32) and S_c (one plane of es-byte elements) per chunk
+size_t lin_chunked_ws_bytes(int64_t nscan, int64_t nchunks, int d_k, int d_v, size_t es);
 // D.mask is a chunked mask (not TOKEN_CAUSAL); flags holds the strided update bits (bit j = chunk j)
 template <typename T>
 ttt_status lin_chunked_run(const linattn_desc& D, const uint32_t (&flags)[32], const T* q, const T* k, const T* v,

@@ -448,8 +448,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_lin_delta(DeltaArgs<T> a) {
 
 // The state each chunk's queries see, from S0 and the chunk updates dS_c: before chunk c's own
 // update (apply-then-update, strided) or after it (update-then-apply, full).  One thread owns 4
-// consecutive elements of one scan's state and walks the chunks.  bf16 io keeps the state as a
-// hi + lo pair of bf16 planes (about 16 bits), fp32 io as one fp32 plane.  The entry/exit strides,
+// consecutive elements of one scan's state and walks the chunks in fp32, writing each chunk's state
+// as `planes` io-dtype planes (bf16: hi, or hi and lo = bf16(x - hi)).  The entry/exit strides,
 // the momentum term, the repeats and the sign are those of LinStateIO.  With rev the chunks are
 // walked from the last to the first (the backward's suffix sums of the chunks' query gradients:
 // there "before its own update" means without the chunk's own term).
@@ -517,7 +517,11 @@ __global__ __launch_bounds__(kThreads) void k_lin_scan(ScanArgs<T> a) {
         for (int u = 0; u < 4; ++u) io.Mout[scan * io.m_stride + e + u] = io.msign * mom[u];
 }
 
-// o (chunk c's tokens x d_v) = q_c S_c^T, contracting over d_k: bf16 as hi and lo products summed
+// The chunk-parallel path keeps the states in fp32 through the scans and hands them to the products
+// as one io-dtype plane (bf16: the state rounded once, as the products' other operands are).
+constexpr int kStatePlanes = 1;
+
+// o (chunk c's tokens x d_v) = q_c S_c^T, contracting over d_k
 template <typename T> struct ApplyArgs {
     const T* q; const T* Sc; T* o;
     const T* k; const T* v; const float* eta;  // token-causal apply only
@@ -528,7 +532,7 @@ constexpr int kApplyRows = 128, kApplyCols = 128;
 
 template <typename T>
 __global__ __launch_bounds__(kThreads, 2) void k_lin_apply(ApplyArgs<T> a) {
-    constexpr int PLANES = sizeof(T) == 2 ? 2 : 1;
+    constexpr int PLANES = kStatePlanes;
     using TA = Tile<T, kApplyRows, kApplyCols, 1, 2, 1, PLANES, PLANES, false, false>;
     using PM = typename std::conditional<PLANES == 2, PMQ, PM1>::type;
     __shared__ __attribute__((aligned(16))) char smem[TA::LDS];
@@ -569,15 +573,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_lin_apply(ApplyArgs<T> a) {
 // that is o = q S_c^T + tril(q k^T) diag(eta) v.  One workgroup takes a block and 128 columns of
 // d_v.  The masked, eta-scaled q k^T block is rounded to the io dtype straight into the A regions
 // of the LDS stages of the P v product (v through the transposing stager), as the sequential
-// kernel rounds it.  q S_c^T sums the bf16 hi and lo state planes in one accumulator; it is added
-// through an fp32 LDS buffer, because the transposing stager leaves P v in another column order.
+// kernel rounds it.  q S_c^T is added through an fp32 LDS buffer, because the transposing stager
+// leaves P v in another column order.
 constexpr int kCausalBlock = 128;
 
 // One workgroup per CU: its three accumulators and v's early-loaded stages need about 390 VGPRs,
 // which two workgroups per CU could only hold by spilling (measured: 1.4% slower with spills).
 template <typename T>
 __global__ __launch_bounds__(kThreads, 1) void k_lin_apply_causal(ApplyArgs<T> a) {  // fp32: 147 KB LDS
-    constexpr int PLANES = sizeof(T) == 2 ? 2 : 1;
+    constexpr int PLANES = kStatePlanes;
     using TP = Tile<T, kCausalBlock, kCausalBlock, 1, 2, 1, 1, 1, false, false>;  // q k^T
     using TD = Tile<T, kCausalBlock, kApplyCols, 2, 2, 1, 1, 1, false, true>;     // P v, P in LDS
     using TA = Tile<T, kCausalBlock, kApplyCols, 1, 2, 1, 1, 1, false, false>;    // q S_c^T per plane
@@ -635,7 +639,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_lin_apply_causal(ApplyArgs<T> a
     for (int st = 0; st < NST; ++st) td.template compute<PM1>(smem + st * TD::STAGE);
     lds_barrier();  // every wave is done with P v's stages
 
-    // q S_c^T, hi then lo plane into one accumulator
+    // q S_c^T (each state plane into one accumulator)
     const int64_t dvk = (int64_t)a.dv * a.dk;
     const T* Sp = a.Sc + (int64_t)unit * PLANES * dvk + (int64_t)c0 * a.dk;
     TA ta;
@@ -742,13 +746,15 @@ static int64_t lin_block(const linattn_desc& D) {
     return D.mask == TTT_MASK_TOKEN_CAUSAL ? kCausalBlock : D.chunk;
 }
 
-size_t lin_chunked_ws_bytes(int64_t nscan, int64_t nchunks, int d_k, int d_v) {
-    return align256((size_t)(nscan * nchunks * (int64_t)d_v * d_k * 4)) * 2;  // dS_c (fp32), then S_c
+size_t lin_chunked_ws_bytes(int64_t nscan, int64_t nchunks, int d_k, int d_v, size_t es) {
+    const size_t n = (size_t)(nscan * nchunks * (int64_t)d_v * d_k);
+    return align256(n * 4) + align256(n * es * kStatePlanes);  // dS_c (fp32), then S_c
 }
 
 static size_t lin_ws_bytes(const linattn_desc& D) {
     if (!lin_parallel(D)) return 0;
-    return lin_chunked_ws_bytes((int64_t)D.B * D.H, cdiv(D.N, lin_block(D)), D.d_k, D.d_v);
+    return lin_chunked_ws_bytes((int64_t)D.B * D.H, cdiv(D.N, lin_block(D)), D.d_k, D.d_v,
+                                D.io_dtype == TTT_BF16 ? 2 : 4);
 }
 
 // Launch of the delta kernel over every (scan, chunk) of D's sequence: dS_c = sum over the chunk of
@@ -809,7 +815,7 @@ static ttt_status run_lin_parallel(const linattn_desc& D, LinArgs<T> a, char* ws
     const int64_t chunk = lin_block(D);
     const int64_t S = (int64_t)D.B * D.H, nc = cdiv(D.N, chunk), dvk = (int64_t)D.d_v * D.d_k;
     float* dS = (float*)ws;
-    T* Sc = (T*)(ws + align256((size_t)(S * nc * dvk * 4)));
+    T* Sc = (T*)(ws + align256((size_t)(S * nc * dvk * 4)));  // kStatePlanes io-dtype planes per chunk
     // 1. per-chunk updates
     ttt_status rc = launch_delta<T, true>(D, chunk, nc, D.mask, a.flags, a.k, a.v, a.eta, dS, st);
     if (rc != TTT_OK) return rc;
@@ -818,7 +824,7 @@ static ttt_status run_lin_parallel(const linattn_desc& D, LinArgs<T> a, char* ws
     if (io.between && (rc = io.between(io.between_ctx, dS, &scan_src, st)) != TTT_OK) return rc;
     // 2. states seen by each chunk, and S_out (a causal block sees the state before it)
     rc = launch_scan<T>(D, nc, causal ? TTT_MASK_APPLY_THEN_UPDATE : D.mask, a.flags, scan_src, Sc, io, 0,
-                        sizeof(T) == 2 ? 2 : 1, st);
+                        kStatePlanes, st);
     if (rc != TTT_OK) return rc;
     // 3. apply
     ApplyArgs<T> aa{};
@@ -871,9 +877,8 @@ template ttt_status lin_chunked_run<float>(const linattn_desc&, const uint32_t (
 // strided mask does not update gets zero dk, dv and deta.  Launches: the forward's delta and scan
 // (S_c), the delta kernel with unit weights over (q, dO) into the same dS buffer (D_c), the scan
 // walked backwards (R_j and dS0), then the two product kernels.  The scans carry fp32; the products
-// read S_c and R_j as one io-dtype plane (bf16: the state rounded once, as the products' other
-// operands are), where the forward's apply reads bf16 states as hi + lo pairs.
-constexpr int kBwdPlanes = 1;
+// read S_c and R_j as one io-dtype plane, as the forward's apply reads S_c.
+constexpr int kBwdPlanes = kStatePlanes;
 
 // dq = dO S_c and dk = diag(eta) v R_c for one chunk: tokens x d_k, contracting over d_v.  The
 // d_v x d_k matrix goes through the transposing stager (its d_k index is the tile column).  One

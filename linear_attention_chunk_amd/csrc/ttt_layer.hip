@@ -857,7 +857,7 @@ static PLayout make_playout(const ttt_desc& D) {
     if (es == 2) L.w13 = take((size_t)(D.w0_per_batch ? S : D.H) * 2 * dm * es);
     L.phq = take((size_t)S * D.N * D.m_h * es);
     L.phk = take((size_t)S * D.N * D.m_h * es);
-    L.lin = take(lin_chunked_ws_bytes(S, L.nc, D.m_h, D.d_h));
+    L.lin = take(lin_chunked_ws_bytes(S, L.nc, D.m_h, D.d_h, es));
     L.nblk = (int)cdiv(dm, kPrepElems);
     if (D.rule == TTT_UPD_MUON) {
         const int64_t nmx = S * L.nc, p = std::min(D.d_h, D.m_h);

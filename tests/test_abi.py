@@ -132,10 +132,10 @@ def test_workspace_sizes():
     # a FULL mask needs one chunk covering the sequence
     assert ws_bytes(desc(mask=C.MASK_FULL, chunk=256))[0] == C.TTT_OK
     # the parallel form holds phi(q), phi(k) ([B H N m] each) and the per-chunk linear-attention
-    # states (dS and S_c, 8 bytes per element of the d x m state per chunk)
+    # states (dS in fp32 and S_c in bf16, 6 bytes per element of the d x m state per chunk)
     st, par = ws_bytes(desc(parallel_form=1, last_layer_only=1, rule=C.UPD_GD))
     assert st == C.TTT_OK
-    assert par >= 2 * 2 * 4 * 256 * 128 * 2 + 8 * 4 * 64 * 128 * 8
+    assert par >= 2 * 2 * 4 * 256 * 128 * 2 + 8 * 4 * 64 * 128 * 6
     st, par0 = ws_bytes(desc(parallel_form=1, last_layer_only=1, rule=C.UPD_GD, N=0))
     assert st == C.TTT_OK and par0 < par
     # with Muon it also holds every (scan, chunk) matrix's Newton-Schulz buffers: at least the fp32
@@ -198,15 +198,15 @@ def test_linattn_forward_rejects():
 
 
 def test_linattn_workspace_choice_and_rejects():
-    """Large chunks take the chunk-parallel path, which needs 8 bytes per state element per chunk and
-    scan; token-causal mode and small chunks need none.  A short or misaligned workspace is refused
+    """Large chunks take the chunk-parallel path, which needs 6 bytes per state element per chunk and
+    scan in bf16; token-causal mode and small chunks need none.  A short or misaligned workspace is refused
     before anything is enqueued."""
     L = C.lib()
     n = ctypes.c_size_t(1)
     D = lin_desc(B=2, H=3, N=1000, d_k=128, d_v=64, chunk=256)   # 4 chunks, 4*128*64 <= 2*256*192
     assert L.linattn_workspace_bytes(ctypes.byref(D), ctypes.byref(n)) == C.TTT_OK
-    per = 2 * 3 * 4 * 128 * 64 * 4
-    assert n.value == 2 * ((per + 255) // 256 * 256)
+    per = 2 * 3 * 4 * 128 * 64 * 4                               # fp32 updates; bf16 states take half
+    assert n.value == (per + 255) // 256 * 256 + (per // 2 + 255) // 256 * 256
     need = n.value
     for kw in (dict(mask=C.MASK_TOKEN_CAUSAL, N=200), dict(chunk=32)):
         kw = dict(dict(B=2, H=3, N=1000, d_k=128, d_v=64), **kw)
@@ -215,7 +215,7 @@ def test_linattn_workspace_choice_and_rejects():
     D2 = lin_desc(B=2, H=3, N=1000, d_k=128, d_v=64, mask=C.MASK_TOKEN_CAUSAL)
     assert L.linattn_workspace_bytes(ctypes.byref(D2), ctypes.byref(n)) == C.TTT_OK
     per2 = 2 * 3 * 8 * 128 * 64 * 4
-    assert n.value == 2 * ((per2 + 255) // 256 * 256)
+    assert n.value == (per2 + 255) // 256 * 256 + (per2 // 2 + 255) // 256 * 256
     args = (P16, P16 + (1 << 30), P16 + (2 << 30), P16 + (3 << 30), None, P16B, None)
     assert L.linattn_forward(ctypes.byref(D), *args, None, 0, None) == C.TTT_ERR_WORKSPACE
     assert L.linattn_forward(ctypes.byref(D), *args, P16 + (1 << 34), need - 1, None) == C.TTT_ERR_WORKSPACE
