@@ -107,6 +107,19 @@ def time_calls(torch, fn, steps, warmup):
     return a.elapsed_time(b) / steps
 
 
+def graph_replay_ms(torch, fn, steps):
+    """The call captured once into a HIP graph (after an eager call), then timed as graph replays."""
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, capture_error_mode="thread_local"):
+        fn()
+    torch.cuda.synchronize()
+    ms = time_calls(torch, g.replay, steps, 2)
+    del g
+    return ms
+
+
 def measured_peaks(torch, C):
     """Rates this device sustains, timed outside the timed region: the library's MFMA-loop probe
     (bf16 32x32x16 MFMAs on register operands, 1024 workgroups x 512 rounds) and a 1 GiB
@@ -415,7 +428,30 @@ def main():
         f5 = lact_flops(B5, H5, N5, d5, m5, upd_tokens=12 * c5, ns_iters=5, n_updates=12)
         extras["nvs_strided_muon"] = {"tokens_per_s": round(B5 * N5 / (ms5 * 1e-3)), "ms_per_call": round(ms5, 3),
                                       "mfma_frac": round(f5 / (ms5 * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
-        del q5, k5, v5, e5, W05, ws5, o5
+        # the same two launch-bound calls captured once into a HIP graph and replayed: the tiny layer
+        # (4 chunks, a few microseconds of work per launch) and the strided mask (12 Muon updates,
+        # about 140 launches)
+        print("[bench] extras: graph replay", file=sys.stderr, flush=True)
+        q1, k1, v1, e1, W01 = gpu_inputs(torch, 1, 1, 256, 32, 32, 2500 + args.seed)
+        q1, k1, v1 = q1.float(), k1.float(), v1.float()
+        D1, _ = T.ttt_desc(1, 1, 256, 32, 32, 64, C.TTT_F32, C.MASK_APPLY_THEN_UPDATE, C.UPD_GD_L2)
+        ws1 = torch.empty(max(1, T.ttt_workspace_bytes(D1)), dtype=torch.uint8, device="cuda")
+        o1 = torch.empty_like(q1)
+        tiny = lambda: T.ttt_forward(q1, k1, v1, e1, W01, 64, C.MASK_APPLY_THEN_UPDATE, C.UPD_GD_L2,  # noqa: E731
+                                     m_h=32, out=o1, want_W=False, workspace=ws1)
+        st_g = max(20, args.steps)
+        ms1e, ms1g = time_calls(torch, tiny, st_g, 3), graph_replay_ms(torch, tiny, st_g)
+        q5, k5, v5, e5, W05 = gpu_inputs(torch, B5, H5, N5, d5, m5, 2000 + args.seed)
+        ws5 = torch.empty(T.ttt_workspace_bytes(D5), dtype=torch.uint8, device="cuda")
+        o5 = torch.empty_like(q5)
+        nvs = lambda: T.ttt_forward(q5, k5, v5, e5, W05, c5, C.MASK_STRIDED, C.UPD_MUON_L2, m_h=m5,  # noqa: E731
+                                    update_chunks=flags, out=o5, want_W=False, workspace=ws5)
+        ms5e, ms5g = time_calls(torch, nvs, st, 1), graph_replay_ms(torch, nvs, st)
+        extras["graph_replay"] = {
+            "tiny_layer": {"workload": "B1 H1 N256 d32 m32 chunk 64 fp32, L2-Normalize(W - g)",
+                           "eager_ms_per_call": round(ms1e, 4), "graph_ms_per_call": round(ms1g, 4)},
+            "nvs_strided_muon": {"eager_ms_per_call": round(ms5e, 3), "graph_ms_per_call": round(ms5g, 3)}}
+        del q1, k1, v1, e1, W01, ws1, o1, q5, k5, v5, e5, W05, ws5, o5
         print("[bench] extras: linear attention", file=sys.stderr, flush=True)
         B2, H2, N2, d2, c2 = 4, 16, 8192, 128, 256
         q2, k2, v2, e2, _ = gpu_inputs(torch, B2, H2, N2, d2, 0, 3000 + args.seed, "sigmoid", 0.05)
