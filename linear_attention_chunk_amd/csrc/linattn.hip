@@ -571,24 +571,25 @@ __global__ __launch_bounds__(kThreads, 2) void k_lin_apply(ApplyArgs<T> a) {
 // order), and this kernel adds the block's own causal term.  For query token i of the block
 //   o_i = S_c q_i + sum over the block's tokens j <= i of eta_j (k_j . q_i) v_j,
 // that is o = q S_c^T + tril(q k^T) diag(eta) v.  One workgroup takes a block and 128 columns of
-// d_v.  The masked, eta-scaled q k^T block is rounded to the io dtype straight into the A regions
-// of the LDS stages of the P v product (v through the transposing stager), as the sequential
-// kernel rounds it.  q S_c^T is added through an fp32 LDS buffer, because the transposing stager
-// leaves P v in another column order.
+// d_v.  q k^T and q S_c^T are one contraction over d_k with two accumulators (q staged once).  The
+// masked, eta-scaled q k^T block is rounded to the io dtype straight into the A regions of the LDS
+// stages of the P v product (v through the transposing stager), as the sequential kernel rounds it.
+// P v is added to q S_c^T through an fp32 LDS buffer, because the transposing stager leaves P v in
+// another column order.
 constexpr int kCausalBlock = 128;
 
-// One workgroup per CU: its three accumulators and v's early-loaded stages need about 390 VGPRs,
-// which two workgroups per CU could only hold by spilling (measured: 1.4% slower with spills).
+// One workgroup per CU: its three accumulators and v's early-loaded stages need more than the 256
+// VGPRs that two workgroups per CU would leave each wave.
 template <typename T>
 __global__ __launch_bounds__(kThreads, 1) void k_lin_apply_causal(ApplyArgs<T> a) {  // fp32: 147 KB LDS
-    constexpr int PLANES = kStatePlanes;
-    using TP = Tile<T, kCausalBlock, kCausalBlock, 1, 2, 1, 1, 1, false, false>;  // q k^T
+    static_assert(kStatePlanes == 1, "q S_c^T is one accumulator");
+    using TQ = Tile<T, kCausalBlock, kCausalBlock, 1, 2, 1, 2, 2, false, false>;  // q k^T and q S_c^T
     using TD = Tile<T, kCausalBlock, kApplyCols, 2, 2, 1, 1, 1, false, true>;     // P v, P in LDS
-    using TA = Tile<T, kCausalBlock, kApplyCols, 1, 2, 1, 1, 1, false, false>;    // q S_c^T per plane
     constexpr int NST = kCausalBlock / TD::KSTEP;  // key-token stages of P v, all resident
     constexpr int OP = kApplyCols + 4;             // fp32 combine-buffer pitch (floats)
-    constexpr int LDSB = std::max(std::max(TP::LDS, NST * TD::STAGE), std::max(TA::LDS, kCausalBlock * OP * 4));
-    static_assert(kCausalBlock % TD::KSTEP == 0 && kApplyRows == kCausalBlock, "block and tile shapes");
+    constexpr int LDSB = std::max(std::max(TQ::LDS, NST * TD::STAGE), kCausalBlock * OP * 4);
+    static_assert(kCausalBlock % TD::KSTEP == 0 && kApplyRows == kCausalBlock && kApplyCols == kCausalBlock,
+                  "block and tile shapes");
     __shared__ __attribute__((aligned(16))) char smem[LDSB];
     const int lb = xcd_block(gridDim.x);
     const int unit = lb / a.ntv, cv = lb % a.ntv;
@@ -597,7 +598,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_lin_apply_causal(ApplyArgs<T> a
     const int64_t tok = (int64_t)scan * a.N + (int64_t)c * kCausalBlock;
     const int nl = (int)std::min<int64_t>(kCausalBlock, a.N - (int64_t)c * kCausalBlock);
 
-    // v's stages are loaded first, so they are in flight during q k^T
+    // v's stages are loaded first, so they are in flight during the first contraction
     const Opnd<T> Bv = {a.v + tok * a.dv + c0, a.dv, a.dv - c0, nl};  // rows: d_v columns; k: tokens
     const bool vfull = a.dv - c0 >= kApplyCols && nl == kCausalBlock;
     typename TD::SB gv[NST];
@@ -607,21 +608,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_lin_apply_causal(ApplyArgs<T> a
         else gv[st].template load<false>(Bv, st * TD::KSTEP);
     }
     // eta of the key tokens this lane's P columns belong to (clamped to the block; masked later)
-    float ek[TP::FN];
-    TP::for_each_pos([&](int idx, int, int col) {
-        if (idx < TP::FN * 16 && idx % 16 == 0) ek[idx / 16] = a.eta[tok + std::min(col, nl - 1)];
+    float ek[TQ::FN];
+    TQ::for_each_pos([&](int idx, int, int col) {
+        if (idx < TQ::FN * 16 && idx % 16 == 0) ek[idx / 16] = a.eta[tok + std::min(col, nl - 1)];
     });
 
-    // P = q k^T over the block (rows: query tokens, columns: key tokens)
+    // P = q k^T over the block (rows: query tokens, columns: key tokens) and q S_c^T (columns: d_v)
+    const int64_t dvk = (int64_t)a.dv * a.dk;
     const Opnd<T> Aq[1] = {{a.q + tok * a.dk, a.dk, nl, a.dk}};
-    const Opnd<T> Bk[1] = {{a.k + tok * a.dk, a.dk, nl, a.dk}};
-    TP tp;
-    tp.template run<PM1>(Aq, Bk, a.dk, smem);
-    lds_barrier();  // every wave is done with q k^T's stages
+    const Opnd<T> Bks[2] = {{a.k + tok * a.dk, a.dk, nl, a.dk},
+                            {a.Sc + (int64_t)unit * dvk + (int64_t)c0 * a.dk, a.dk, a.dv - c0, a.dk}};
+    TQ tq;
+    tq.template run<PMQ>(Aq, Bks, a.dk, smem);
+    lds_barrier();  // every wave is done with the contraction's stages
     {
         int idx = 0;
-        tp.for_each([&](const float (&v)[1], int row, int col) {
-            const float val = (col <= row && col < nl) ? v[0] * ek[(idx / 16) % TP::FN] : 0.f;
+        tq.for_each([&](const float (&v)[2], int row, int col) {
+            const float val = (col <= row && col < nl) ? v[0] * ek[(idx / 16) % TQ::FN] : 0.f;
             ++idx;
             *reinterpret_cast<T*>(smem + (col / TD::KSTEP) * TD::STAGE + row * TD::PITCH +
                                   (col % TD::KSTEP) * (int)sizeof(T)) = Elt<T>::st(val);
@@ -638,25 +641,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_lin_apply_causal(ApplyArgs<T> a
 #pragma unroll
     for (int st = 0; st < NST; ++st) td.template compute<PM1>(smem + st * TD::STAGE);
     lds_barrier();  // every wave is done with P v's stages
-
-    // q S_c^T (each state plane into one accumulator)
-    const int64_t dvk = (int64_t)a.dv * a.dk;
-    const T* Sp = a.Sc + (int64_t)unit * PLANES * dvk + (int64_t)c0 * a.dk;
-    TA ta;
-#pragma unroll
-    for (int pl = 0; pl < PLANES; ++pl) {
-        const Opnd<T> Bs[1] = {{Sp + pl * dvk, a.dk, a.dv - c0, a.dk}};
-        ta.template run<PM1>(Aq, Bs, a.dk, smem, pl > 0);
-    }
-    lds_barrier();
     float* buf = reinterpret_cast<float*>(smem);
     td.for_each([&](const float (&v)[1], int row, int col) { buf[row * OP + col] = v[0]; });
     __syncthreads();
     T* O = a.o + tok * a.dv + c0;
     auto epi = [&](auto check) {
-        ta.for_each([&](const float (&v)[1], int row, int col) {
+        tq.for_each([&](const float (&v)[2], int row, int col) {
             if (!decltype(check)::value || (row < nl && c0 + col < a.dv))
-                O[(uint32_t)row * (uint32_t)a.dv + (uint32_t)col] = Elt<T>::st(v[0] + buf[row * OP + col]);
+                O[(uint32_t)row * (uint32_t)a.dv + (uint32_t)col] = Elt<T>::st(v[1] + buf[row * OP + col]);
         });
     };
     if (nl == kCausalBlock && c0 + kApplyCols <= a.dv) epi(std::false_type{});
