@@ -367,10 +367,68 @@ def linattn_backward_ref(q, k, v, eta, chunk, mask, dO, S0=None, dS_out=None, up
     return tuple(out)
 
 
+def _momentum_state_backward(phq, phk, v, eta, S0, chunk, mask, dO, dS_out, update_chunks, reps, sign, beta):
+    """The linear-attention part of the layer's backward when W2's steps carry momentum.
+
+    Forward, per updating chunk and step (reps steps): m <- beta m + sign dS_c, S <- S + m, with
+    dS_c = sum eta v phi(k)^T and m starting at zero (m is minus the momentum M of M <- beta M + g,
+    W2 <- W2 - M; LaCT notes, text after Eq. (6)).  Backward: the chunks' queries see S_c, so
+    dphi(q)_t = S_c^T dO_t and D_c = sum_t dO_t phi(q)_t^T is S_c's gradient; the same recurrence
+    is then walked transposed from the last chunk: with gS and gm the gradients of S and m after a
+    step, each step of chunk c gives g = gm + gS to sign dS_c, and gm <- beta g before it (gS passes
+    through).  The final momentum is not part of the loss.  Returns (dphi(q), dphi(k), dv, deta, dS0).
+    """
+    N = phq.shape[0]
+    bounds = chunk_bounds(N, chunk)
+    post = mask in (MASK_UPDATE_THEN_APPLY, MASK_FULL)
+    upd = [mask != MASK_STRIDED or bool(update_chunks[j]) for j in range(len(bounds))]
+    S, m = _f64(S0).copy(), np.zeros_like(_f64(S0))
+    Sc = []
+    for j, (lo, hi) in enumerate(bounds):
+        dS = (eta[lo:hi, None] * v[lo:hi]).T @ phk[lo:hi]
+        if post and upd[j]:
+            for _ in range(reps):
+                m = beta * m + sign * dS
+                S = S + m
+        Sc.append(S.copy())
+        if not post and upd[j]:
+            for _ in range(reps):
+                m = beta * m + sign * dS
+                S = S + m
+    dphq = np.zeros_like(phq)
+    D = []
+    for j, (lo, hi) in enumerate(bounds):
+        dphq[lo:hi] = dO[lo:hi] @ Sc[j]
+        D.append(dO[lo:hi].T @ phq[lo:hi])
+    gS = np.zeros_like(S) if dS_out is None else _f64(dS_out).copy()
+    gm = np.zeros_like(S)
+    R = [None] * len(bounds)
+    for j in reversed(range(len(bounds))):
+        if post:
+            gS = gS + D[j]
+        if upd[j]:
+            Rj = np.zeros_like(S)
+            for _ in range(reps):
+                g = gm + gS
+                Rj = Rj + g
+                gm = beta * g
+            R[j] = sign * Rj          # the gradient of dS_j
+        if not post:
+            gS = gS + D[j]
+    dphk, dv, deta = np.zeros_like(phk), np.zeros_like(v), np.zeros_like(eta)
+    for j, (lo, hi) in enumerate(bounds):
+        if upd[j]:
+            u = phk[lo:hi] @ R[j].T
+            dv[lo:hi] = eta[lo:hi, None] * u
+            dphk[lo:hi] = eta[lo:hi, None] * (v[lo:hi] @ R[j])
+            deta[lo:hi] = np.sum(v[lo:hi] * u, axis=1)
+    return dphq, dphk, dv, deta, gS
+
+
 def ttt_lastlayer_backward_scan_ref(q, k, v, eta, W1, W3, W2, chunk, mask, dO, dW_out=None, update_chunks=None,
-                                    inner_steps=1, ascent=False):
+                                    inner_steps=1, ascent=False, momentum=0.0):
     """Gradients of one (batch, head) scan of the TTT-KVB layer whose inner loop trains W2 alone by
-    plain GD (ttt_scan_ref with last_layer_only, rule UPD_GD, no momentum), for the loss
+    plain GD (ttt_scan_ref with last_layer_only, rule UPD_GD), for the loss
     L = sum_t dO_t . o_t + <dW1_out, W1> + <dW3_out, W3> + <dW2_out, W2_out>.
 
     With W1 and W3 frozen, phi(x) = SiLU(W1 x) o (W3 x) is fixed, the chunk gradient of W2 is
@@ -378,19 +436,25 @@ def ttt_lastlayer_backward_scan_ref(q, k, v, eta, W1, W3, W2, chunk, mask, dO, d
     phi(k), values v and state W2 (TTT-as-LA, Thm. 5.2-5.3 and Sec. 6.1 Steps 1-6); its outer-loop
     gradients (TTT-as-LA, Sec. 6.2) are those of linear attention (linattn_backward_scan_ref),
     followed by the chain rule through phi.  inner_steps repeats an update that does not depend on
-    W2, and ascent flips its sign: both scale eta.  dW_out is None or (dW1, dW3, dW2) of the
-    shapes of (W1, W3, W2).  Returns (dq, dk, dv, deta, (dW1, dW3, dW2)).
+    W2, and ascent flips its sign: without momentum both scale eta.  With momentum (starting from
+    zero, its final state outside the loss) the state part is _momentum_state_backward.  dW_out is
+    None or (dW1, dW3, dW2) of the shapes of (W1, W3, W2).  Returns (dq, dk, dv, deta, (dW1, dW3, dW2)).
     """
     q, k, v, eta, dO = (_f64(x) for x in (q, k, v, eta, dO))
     W1, W3, W2 = _f64(W1), _f64(W3), _f64(W2)
-    f = (-1.0 if ascent else 1.0) * max(int(inner_steps), 1)
+    sign, reps = (-1.0 if ascent else 1.0), max(int(inner_steps), 1)
     A = {"q": q @ W1.T, "k": k @ W1.T}
     C = {"q": q @ W3.T, "k": k @ W3.T}
     phi = {s: silu(A[s]) * C[s] for s in ("q", "k")}
     dW2o = None if dW_out is None else dW_out[2]
-    dphq, dphk, dv, deta, dW2 = linattn_backward_scan_ref(phi["q"], phi["k"], v, f * eta, W2, chunk, mask, dO,
-                                                          dW2o, update_chunks)
-    deta = f * deta
+    if momentum == 0.0:
+        f = sign * reps
+        dphq, dphk, dv, deta, dW2 = linattn_backward_scan_ref(phi["q"], phi["k"], v, f * eta, W2, chunk, mask, dO,
+                                                              dW2o, update_chunks)
+        deta = f * deta
+    else:
+        dphq, dphk, dv, deta, dW2 = _momentum_state_backward(phi["q"], phi["k"], v, eta, W2, chunk, mask, dO, dW2o,
+                                                             update_chunks, reps, sign, float(momentum))
     dW1 = np.zeros_like(W1) if dW_out is None else _f64(dW_out[0]).copy()
     dW3 = np.zeros_like(W3) if dW_out is None else _f64(dW_out[1]).copy()
     dx = {}
@@ -405,7 +469,7 @@ def ttt_lastlayer_backward_scan_ref(q, k, v, eta, W1, W3, W2, chunk, mask, dO, d
 
 
 def ttt_lastlayer_backward_ref(q, k, v, eta, W1, W3, W2, chunk, mask, dO, dW_out=None, update_chunks=None,
-                               inner_steps=1, ascent=False, slices=None):
+                               inner_steps=1, ascent=False, slices=None, momentum=0.0):
     """ttt_lastlayer_backward_scan_ref over [B, H, N, d] inputs.  W1, W3, W2 are per head ([H, ...])
     or per (batch, head) ([B, H, ...]); the weight gradients take the same shape (per-head weights
     sum over the batch).  dW_out is None or three [B, H, ...] arrays (the W_out the layer returns
@@ -420,7 +484,7 @@ def ttt_lastlayer_backward_ref(q, k, v, eta, W1, W3, W2, chunk, mask, dO, dW_out
         ws = [x[h] if per_head else x[b, h] for x in (W1, W3, W2)]
         dwo = None if dW_out is None else tuple(x[b, h] for x in dW_out)
         r = ttt_lastlayer_backward_scan_ref(q[b, h], k[b, h], v[b, h], eta[b, h], *ws, chunk, mask, dO[b, h], dwo,
-                                            update_chunks, inner_steps, ascent)
+                                            update_chunks, inner_steps, ascent, momentum)
         dq[b, h], dk[b, h], dv[b, h], deta[b, h] = r[:4]
         for i in range(3):
             if per_head:

@@ -25,23 +25,27 @@ def problem(seed, N=9, d=3, m=4):
     return q, k, v, eta, W1, W3, W2, dO, dWo
 
 
-def loss(q, k, v, eta, W1, W3, W2, chunk, mask, dO, dWo, upd, steps, ascent):
-    o, W, _ = O.ttt_scan_ref(q, k, v, eta, W1, W3, W2, chunk, mask, O.UPD_GD, last_layer_only=True,
+def loss(q, k, v, eta, W1, W3, W2, chunk, mask, dO, dWo, upd, steps, ascent, beta=0.0):
+    # the recurrence with momentum starting from zero; its final momentum is not part of the loss
+    o, W, _ = O.ttt_scan_ref(q, k, v, eta, W1, W3, W2, chunk, mask, O.UPD_GD, momentum=beta, last_layer_only=True,
                              update_chunks=upd, inner_steps=steps, ascent=ascent)
     return float(np.sum(dO * o) + sum(np.sum(g * w) for g, w in zip(dWo, W)))
 
 
-CASES = [(O.MASK_APPLY_THEN_UPDATE, 3, None, 1, False), (O.MASK_UPDATE_THEN_APPLY, 4, None, 1, False),
-         (O.MASK_FULL, 9, None, 1, False), (O.MASK_STRIDED, 2, [1, 0, 1, 1, 0], 1, False),
-         (O.MASK_APPLY_THEN_UPDATE, 4, None, 2, True), (O.MASK_UPDATE_THEN_APPLY, 3, None, 3, False)]
+CASES = [(O.MASK_APPLY_THEN_UPDATE, 3, None, 1, False, 0.0), (O.MASK_UPDATE_THEN_APPLY, 4, None, 1, False, 0.0),
+         (O.MASK_FULL, 9, None, 1, False, 0.0), (O.MASK_STRIDED, 2, [1, 0, 1, 1, 0], 1, False, 0.0),
+         (O.MASK_APPLY_THEN_UPDATE, 4, None, 2, True, 0.0), (O.MASK_UPDATE_THEN_APPLY, 3, None, 3, False, 0.0),
+         # momentum (W2 <- W2 - M, M <- beta M + g): every order, several steps, ascent, skipped chunks
+         (O.MASK_APPLY_THEN_UPDATE, 2, None, 1, False, 0.9), (O.MASK_UPDATE_THEN_APPLY, 3, None, 2, True, 0.5),
+         (O.MASK_FULL, 9, None, 3, False, 0.7), (O.MASK_STRIDED, 2, [0, 1, 1, 0, 1], 2, False, 0.9)]
 
 
-@pytest.mark.parametrize("mask,chunk,upd,steps,ascent", CASES)
-def test_layer_backward_matches_finite_differences(mask, chunk, upd, steps, ascent):
-    args = list(problem(90 + mask + 7 * steps))
+@pytest.mark.parametrize("mask,chunk,upd,steps,ascent,beta", CASES)
+def test_layer_backward_matches_finite_differences(mask, chunk, upd, steps, ascent, beta):
+    args = list(problem(90 + mask + 7 * steps + int(10 * beta)))
     dO, dWo = args[7], args[8]
     args = args[:7]
-    got = O.ttt_lastlayer_backward_scan_ref(*args, chunk, mask, dO, dWo, upd, steps, ascent)
+    got = O.ttt_lastlayer_backward_scan_ref(*args, chunk, mask, dO, dWo, upd, steps, ascent, momentum=beta)
     grads = list(got[:4]) + list(got[4])
     h = 1e-6
     for which, g in enumerate(grads):
@@ -49,16 +53,37 @@ def test_layer_backward_matches_finite_differences(mask, chunk, upd, steps, asce
         for idx in np.ndindex(*args[which].shape):
             a = [x.copy() for x in args]
             a[which][idx] += h
-            lp = loss(*a, chunk, mask, dO, dWo, upd, steps, ascent)
+            lp = loss(*a, chunk, mask, dO, dWo, upd, steps, ascent, beta)
             a[which][idx] -= 2 * h
-            lm = loss(*a, chunk, mask, dO, dWo, upd, steps, ascent)
+            lm = loss(*a, chunk, mask, dO, dWo, upd, steps, ascent, beta)
             fd[idx] = (lp - lm) / (2 * h)
         assert rel(g, fd) < 1e-6, which
 
 
-@pytest.mark.parametrize("mask,chunk,upd", [(O.MASK_APPLY_THEN_UPDATE, 4, None), (O.MASK_UPDATE_THEN_APPLY, 5, None),
-                                            (O.MASK_STRIDED, 3, [0, 1, 1, 0, 1])])
-def test_layer_backward_matches_double_autograd(mask, chunk, upd):
+def test_momentum_zero_matches_the_linear_path():
+    # beta = 0 through the momentum recurrence equals the plain path (which scales eta by the steps)
+    args = list(problem(150))
+    dO, dWo = args[7], args[8]
+    a = O.ttt_lastlayer_backward_scan_ref(*args[:7], 3, O.MASK_APPLY_THEN_UPDATE, dO, dWo, None, 2, True)
+    b = O.ttt_ref._momentum_state_backward  # the momentum path run directly with beta = 0 on the same features
+    W1, W3 = args[4], args[5]
+    phi = lambda x: O.silu(x @ W1.T) * (x @ W3.T)
+    got = b(phi(args[0]), phi(args[1]), args[2], args[3], args[6], 3, O.MASK_APPLY_THEN_UPDATE, dO, dWo[2], None, 2,
+            -1.0, 0.0)
+    ref = O.linattn_backward_scan_ref(phi(args[0]), phi(args[1]), args[2], -2.0 * args[3], args[6], 3,
+                                      O.MASK_APPLY_THEN_UPDATE, dO, dWo[2])
+    for i, (x, y) in enumerate(zip(got, ref)):
+        y = -2.0 * y if i == 3 else y
+        assert rel(x, y) < 1e-12, i
+    assert rel(a[2], got[2]) < 1e-12
+
+
+@pytest.mark.parametrize("mask,chunk,upd,beta", [(O.MASK_APPLY_THEN_UPDATE, 4, None, 0.0),
+                                                 (O.MASK_UPDATE_THEN_APPLY, 5, None, 0.0),
+                                                 (O.MASK_STRIDED, 3, [0, 1, 1, 0, 1], 0.0),
+                                                 (O.MASK_APPLY_THEN_UPDATE, 4, None, 0.9),
+                                                 (O.MASK_STRIDED, 3, [1, 0, 1, 1, 0], 0.6)])
+def test_layer_backward_matches_double_autograd(mask, chunk, upd, beta):
     torch = pytest.importorskip("torch")
     N, d, m = 13, 4, 6
     q, k, v, eta, W1, W3, W2, dO, dWo = problem(110 + mask, N, d, m)
@@ -69,7 +94,7 @@ def test_layer_backward_matches_double_autograd(mask, chunk, upd):
         return (torch.nn.functional.silu(x @ t1.T) * (x @ t3.T)) @ W2_.T
 
     post = mask == O.MASK_UPDATE_THEN_APPLY
-    W, outs = t2, []
+    W, outs, M = t2, [], torch.zeros_like(t2)
     for j, lo in enumerate(range(0, N, chunk)):
         hi = min(lo + chunk, N)
         if not post:
@@ -77,13 +102,14 @@ def test_layer_backward_matches_double_autograd(mask, chunk, upd):
         if upd is None or upd[j]:
             inner = -(te[lo:hi, None] * f(W, tk[lo:hi]) * tv[lo:hi]).sum()  # sum eta_i L(f(k_i), v_i)
             g, = torch.autograd.grad(inner, W, create_graph=True)
-            W = W - g
+            M = beta * M + g
+            W = W - M
         if post:
             outs.append(f(W, tq[lo:hi]))
     L = (torch.cat(outs) * torch.tensor(dO)).sum()
     L = L + (t1 * torch.tensor(dWo[0])).sum() + (t3 * torch.tensor(dWo[1])).sum() + (W * torch.tensor(dWo[2])).sum()
     L.backward()
-    got = O.ttt_lastlayer_backward_scan_ref(q, k, v, eta, W1, W3, W2, chunk, mask, dO, dWo, upd)
+    got = O.ttt_lastlayer_backward_scan_ref(q, k, v, eta, W1, W3, W2, chunk, mask, dO, dWo, upd, momentum=beta)
     for g, x in zip(list(got[:4]) + list(got[4]), t):
         assert rel(g, x.grad.numpy()) < 1e-12
 
