@@ -118,7 +118,9 @@ ttt_status validate_ttt_desc(const ttt_desc* D);
 // The backward of the chunked path as a building block (also driven by the TTT layer's backward).
 // S0 of scan s at S0 + (s0_heads ? s % s0_heads : s) * s0_stride (null: zeros); dS_out of scan s at
 // dS_out + s * dso_stride (null: zeros); dS0 of scan s to dS0 + s * ds0_stride (null: not written).
-// The forward's chunk updates were escale * sum eta v k^T (the sign of ascent, repeated steps).
+// The forward's updating chunks added u = dsign * sum eta v k^T to the state reps times, directly
+// or (mom) through a running term m <- beta m + u, S <- S + m that started at zero and whose final
+// value is not part of the loss.
 // gate[0], gate[1]: both null, or [S][N][2 d_k] buffers of io-dtype factors u | w for dq and dk:
 // then dq and dk are not written; each gate row becomes dq u | dq w (dk u | dk w) in place.
 struct LinBwdIO {
@@ -129,7 +131,10 @@ struct LinBwdIO {
     int64_t dso_stride = 0;
     float* dS0 = nullptr;
     int64_t ds0_stride = 0;
-    float escale = 1.f;
+    float dsign = 1.f;
+    int reps = 1;
+    int mom = 0;
+    float beta = 0.f;
     void* gate[2] = {nullptr, nullptr};
 };
 // the backward's checks of a linear-attention descriptor

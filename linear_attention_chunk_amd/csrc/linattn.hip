@@ -480,22 +480,49 @@ __global__ __launch_bounds__(kThreads) void k_lin_scan(ScanArgs<T> a) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) mom[u] = io.msign * io.M0[scan * io.m_stride + e + u];
     const bool post = a.mode == TTT_MASK_UPDATE_THEN_APPLY || a.mode == TTT_MASK_FULL;
-    auto put = [&](int c) {
+    auto put = [&](int c, const f32x4_t& x) {
         T* dst = a.Sc + ((scan * a.nc + c) * a.planes) * a.dvk + e;
         if (PLANES == 2 && a.planes == 2) {
             float lo[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) lo[u] = st[u] - bf2f(f2bf(st[u]));
-            Pack4<T>::store(dst, st[0], st[1], st[2], st[3]);
+            for (int u = 0; u < 4; ++u) lo[u] = x[u] - bf2f(f2bf(x[u]));
+            Pack4<T>::store(dst, x[0], x[1], x[2], x[3]);
             Pack4<T>::store(dst + a.dvk, lo[0], lo[1], lo[2], lo[3]);
         } else {
-            Pack4<T>::store(dst, st[0], st[1], st[2], st[3]);
+            Pack4<T>::store(dst, x[0], x[1], x[2], x[3]);
         }
     };
+    if (a.rev && io.mom) {
+        // The momentum recurrence transposed, from the last chunk: st is the gradient of the state,
+        // mom that of the running term m (zero at the end: the final momentum is not in the loss).
+        // Every chunk's D_c adds to st (before its own update's transpose where the chunk's queries
+        // see its update, after it otherwise); each step of an updating chunk gives g = mom + st to
+        // the chunk's update and sets mom <- beta g.  The chunk's slot receives the sum of its g.
+        for (int i = 0; i < a.nc; ++i) {
+            const int c = a.nc - 1 - i;
+            const bool upd = a.mode != TTT_MASK_STRIDED || ((a.flags[c >> 5] >> (c & 31)) & 1u);
+            const f32x4_t d = *reinterpret_cast<const f32x4_t*>(a.dS + (scan * a.nc + c) * a.dvk + e);
+            if (post) st += d;
+            if (upd) {
+                f32x4_t r = {0.f, 0.f, 0.f, 0.f};
+                for (int k = 0; k < io.reps; ++k) {
+                    const f32x4_t gsum = mom + st;
+                    r += gsum;
+                    mom = io.beta * gsum;
+                }
+                put(c, r);
+            }
+            if (!post) st += d;
+        }
+        if (io.Sout)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) io.Sout[scan * io.sout_stride + e + u] = st[u];
+        return;
+    }
     for (int i = 0; i < a.nc; ++i) {
         const int c = a.rev ? a.nc - 1 - i : i;
         const bool upd = a.mode != TTT_MASK_STRIDED || ((a.flags[c >> 5] >> (c & 31)) & 1u);
-        if (!post) put(c);
+        if (!post) put(c, st);
         if (upd) {
             const f32x4_t d = io.dsign * *reinterpret_cast<const f32x4_t*>(a.dS + (scan * a.nc + c) * a.dvk + e);
             for (int r = 0; r < io.reps; ++r) {
@@ -507,7 +534,7 @@ __global__ __launch_bounds__(kThreads) void k_lin_scan(ScanArgs<T> a) {
                 }
             }
         }
-        if (post) put(c);
+        if (post) put(c, st);
     }
     if (io.Sout)
 #pragma unroll
@@ -1122,7 +1149,10 @@ ttt_status lin_chunked_bwd(const linattn_desc& D, const uint32_t (&flags)[32], c
         fio.S0 = io.S0;
         fio.s0_stride = io.s0_stride;
         fio.s0_heads = io.s0_heads;
-        fio.dsign = io.escale;
+        fio.dsign = io.dsign;
+        fio.reps = io.reps;
+        fio.mom = io.mom;
+        fio.beta = io.beta;
         if ((rc = launch_scan<T>(D, nc, D.mask, flags, dS, Sc, fio, 0, kBwdPlanes, st)) != TTT_OK) return rc;
         // D_c = sum over the chunk of dO q^T, every chunk
         if ((rc = launch_delta<T, false>(D, chunk, nc, TTT_MASK_APPLY_THEN_UPDATE, all, q, dO, nullptr, dS, st)) !=
@@ -1136,8 +1166,17 @@ ttt_status lin_chunked_bwd(const linattn_desc& D, const uint32_t (&flags)[32], c
     rio.s0_stride = io.dso_stride;
     rio.Sout = io.dS0;
     rio.sout_stride = io.ds0_stride;
+    if (io.mom) {  // the momentum recurrence transposed: every D_c adds, the mask's chunks update
+        rio.mom = 1;
+        rio.beta = io.beta;
+        rio.reps = io.reps;
+    }
     if (D.N > 0 || io.dS0)
-        if ((rc = launch_scan<T>(D, nc, D.mask, all, dS, R, rio, 1, kBwdPlanes, st)) != TTT_OK) return rc;
+        if ((rc = launch_scan<T>(D, nc, D.mask, io.mom ? flags : all, dS, R, rio, 1, kBwdPlanes, st)) != TTT_OK)
+            return rc;
+    // the gradient of a chunk's update sum eta v k^T: R_j times the update's sign, and (without
+    // momentum) times its repeats, which the reverse scan folds in otherwise
+    const float es = io.mom ? io.dsign : io.dsign * (float)io.reps;
     if (D.N == 0) return TTT_OK;
     const int ntt = (int)cdiv(std::min<int64_t>(chunk, D.N), kApplyRows);
     const int ntk = (int)cdiv(D.d_k, kApplyCols);  // column tiles of dq, dk (and deta partials)
@@ -1156,7 +1195,7 @@ ttt_status lin_chunked_bwd(const linattn_desc& D, const uint32_t (&flags)[32], c
     ta.ntn = ntk;
     ta.per_job = (int)(S * nc * ntt * ntk);
     ta.mode = D.mask;
-    ta.es = io.escale;
+    ta.es = es;
     for (int w = 0; w < 32; ++w) ta.flags[w] = flags[w];
     {
         ProfScope ps(PK_LIN_BWD_T, st);
@@ -1177,7 +1216,7 @@ ttt_status lin_chunked_bwd(const linattn_desc& D, const uint32_t (&flags)[32], c
     na.ntt = ntt;
     na.ntn = (int)cdiv(D.d_v, kApplyCols);
     na.mode = D.mask;
-    na.es = io.escale;
+    na.es = es;
     for (int w = 0; w < 32; ++w) na.flags[w] = flags[w];
     {
         ProfScope ps(PK_LIN_BWD_N, st);

@@ -31,9 +31,9 @@ def split(W, d, m):
 
 
 def run(seed, B, H, N, d, m, chunk, mask, bf16, flags=None, inner=1, ascent=False, per_batch=False, dW_out=True,
-        want_dW0=True):
+        want_dW0=True, momentum=0.0):
     say(f"ttt_backward case B{B} H{H} N{N} d{d} m{m} b{chunk} mask{mask} bf16={bf16} flags={flags} inner{inner} "
-        f"ascent{ascent} per_batch={per_batch} dW_out={dW_out} want_dW0={want_dW0}")
+        f"ascent{ascent} per_batch={per_batch} dW_out={dW_out} want_dW0={want_dW0} momentum={momentum}")
     (q, k, v, eta, W0), (hq, hk, hv, he, W1, W3, W2) = full_ttt_inputs(seed, B, H, N, d, m, bf16)
     if per_batch:  # a different weight block for every (batch, head)
         Ws = [np.zeros((B, H) + w.shape[1:], np.float32) for w in (W1, W3, W2)]
@@ -48,9 +48,10 @@ def run(seed, B, H, N, d, m, chunk, mask, bf16, flags=None, inner=1, ascent=Fals
     dt = torch.bfloat16 if bf16 else torch.float32
     got = T.ttt_backward(q, k, v, eta, W0, dev(dO, dt), chunk, mask, m_h=m,
                          dW_out=None if dWo is None else dev(pack(*dWo)), want_dW0=want_dW0, update_chunks=flags,
-                         inner_steps=inner, ascent=ascent)
+                         inner_steps=inner, ascent=ascent, momentum=momentum)
     torch.cuda.synchronize()
-    ref = O.ttt_lastlayer_backward_ref(hq, hk, hv, he, W1, W3, W2, chunk, mask, dO, dWo, flags, inner, ascent)
+    ref = O.ttt_lastlayer_backward_ref(hq, hk, hv, he, W1, W3, W2, chunk, mask, dO, dWo, flags, inner, ascent,
+                                       momentum=momentum)
     tol = TOL[bf16]
     if N == 0:
         for g, r in zip(got[:4], ref[:4]):
@@ -90,6 +91,23 @@ def test_strided_inner_ascent(flags, inner, ascent, bf16):
         if not f:
             assert torch.count_nonzero(got[2][:, :, 96 * c:96 * (c + 1)]).item() == 0
             assert torch.count_nonzero(got[3][:, :, 96 * c:96 * (c + 1)]).item() == 0
+
+
+MOMENTUM_CASES = [
+    # mask, chunk, strided flags, inner steps, ascent, momentum
+    (O.MASK_APPLY_THEN_UPDATE, 96, None, 1, False, 0.9),
+    (O.MASK_UPDATE_THEN_APPLY, 96, None, 2, True, 0.5),
+    (O.MASK_STRIDED, 96, [1, 0, 1, 1], 1, False, 0.9),
+    (O.MASK_STRIDED, 96, [0, 1, 1, 0], 3, True, 0.7),
+]
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("mask,chunk,flags,inner,ascent,mom", MOMENTUM_CASES)
+def test_momentum(mask, chunk, flags, inner, ascent, mom, bf16):
+    # the W2 steps through a momentum that starts from zero (the reverse scan walks the momentum
+    # recurrence transposed); N = 308 leaves a ragged last chunk, m = 160 partial tiles
+    run(11, 1, 2, 308, 64, 160, chunk, mask, bf16, flags=flags, inner=inner, ascent=ascent, momentum=mom)
 
 
 @pytest.mark.parametrize("bf16", [False, True])
