@@ -25,8 +25,9 @@ Training"):
 * several inner-loop gradient steps per chunk (inference time) ... TTT-as-LA, Sec. 4.1
 * the backward of the linear reduction (outer-loop gradients) ..... TTT-as-LA, Sec. 6.2 and Fig. 4
                                                                    (training with the parallel form)
-* the backward of the layer with frozen W1, W3 (last layer only, GD):
-  the linear reduction's over phi(q), phi(k), then phi's chain rule  TTT-as-LA, Thm. 5.2-5.3, Sec. 6.1-6.2
+* the backward of the layer with frozen W1, W3 (last layer only, GD, momentum, the L2 norm):
+  the state's recurrence transposed over phi(q), phi(k), then phi's chain rule  TTT-as-LA, Thm. 5.2-5.3,
+                                                                   Sec. 6.1-6.2
 * gradient ascent in the inner loop: the step's sign flips ....... TTT-as-LA, Sec. 4.2 and 5.2
 * per-chunk rates outside the optimizer step: momentum dW_j = g_j + alpha_j dW_{j-1} over the
   chunk gradient g_j (unit token weights), W <- W - eta_j Opt(dW_j) .. TTT-as-LA, App. E.1 (per token)
@@ -367,34 +368,47 @@ def linattn_backward_ref(q, k, v, eta, chunk, mask, dO, S0=None, dS_out=None, up
     return tuple(out)
 
 
-def _momentum_state_backward(phq, phk, v, eta, S0, chunk, mask, dO, dS_out, update_chunks, reps, sign, beta):
-    """The linear-attention part of the layer's backward when W2's steps carry momentum.
+def _recurrent_state_backward(phq, phk, v, eta, S0, chunk, mask, dO, dS_out, update_chunks, reps, sign, beta, norm):
+    """The linear-attention part of the layer's backward when W2's steps carry momentum or end in
+    the L2 norm (the state walked chunk by chunk).
 
-    Forward, per updating chunk and step (reps steps): m <- beta m + sign dS_c, S <- S + m, with
-    dS_c = sum eta v phi(k)^T and m starting at zero (m is minus the momentum M of M <- beta M + g,
-    W2 <- W2 - M; LaCT notes, text after Eq. (6)).  Backward: the chunks' queries see S_c, so
-    dphi(q)_t = S_c^T dO_t and D_c = sum_t dO_t phi(q)_t^T is S_c's gradient; the same recurrence
-    is then walked transposed from the last chunk: with gS and gm the gradients of S and m after a
-    step, each step of chunk c gives g = gm + gS to sign dS_c, and gm <- beta g before it (gS passes
-    through).  The final momentum is not part of the loss.  Returns (dphi(q), dphi(k), dv, deta, dS0).
+    Forward, per updating chunk and step (reps steps): m <- beta m + sign dS_c, x = S + m, and S <- x,
+    or S <- L2-Normalize(x) row by row (norm; LaCT notes Eq. (5)), with dS_c = sum eta v phi(k)^T and
+    m starting at zero (m is minus the momentum M of M <- beta M + g, W2 <- [norm](W2 - M); LaCT notes,
+    text after Eq. (6)).  Backward: the chunks' queries see S_c, so dphi(q)_t = S_c^T dO_t and
+    D_c = sum_t dO_t phi(q)_t^T is S_c's gradient; the recurrence is then walked transposed from the
+    last chunk: with gS and gm the gradients of S and m after a step, the step's norm sends gS back
+    to gx = (gS - y (y . gS)) / |x| per row (y = S after the step; gS / eps where |x| <= eps), its
+    update receives g = gm + gx, and gm <- beta g, gS <- gx before it.  The final momentum is not part
+    of the loss.  Returns (dphi(q), dphi(k), dv, deta, dS0).
     """
     N = phq.shape[0]
     bounds = chunk_bounds(N, chunk)
     post = mask in (MASK_UPDATE_THEN_APPLY, MASK_FULL)
     upd = [mask != MASK_STRIDED or bool(update_chunks[j]) for j in range(len(bounds))]
     S, m = _f64(S0).copy(), np.zeros_like(_f64(S0))
-    Sc = []
+    Sc, steps = [], {}  # steps[j]: (y, |x| per row) of each of chunk j's steps
+
+    def update(j, dS):
+        nonlocal S, m
+        steps[j] = []
+        for _ in range(reps):
+            m = beta * m + sign * dS
+            x = S + m
+            if norm:
+                n = np.sqrt(np.sum(x * x, axis=1, keepdims=True))
+                S = x / np.maximum(n, ROW_NORM_EPS)
+                steps[j].append((S.copy(), n))
+            else:
+                S = x
+
     for j, (lo, hi) in enumerate(bounds):
         dS = (eta[lo:hi, None] * v[lo:hi]).T @ phk[lo:hi]
         if post and upd[j]:
-            for _ in range(reps):
-                m = beta * m + sign * dS
-                S = S + m
+            update(j, dS)
         Sc.append(S.copy())
         if not post and upd[j]:
-            for _ in range(reps):
-                m = beta * m + sign * dS
-                S = S + m
+            update(j, dS)
     dphq = np.zeros_like(phq)
     D = []
     for j, (lo, hi) in enumerate(bounds):
@@ -408,10 +422,17 @@ def _momentum_state_backward(phq, phk, v, eta, S0, chunk, mask, dO, dS_out, upda
             gS = gS + D[j]
         if upd[j]:
             Rj = np.zeros_like(S)
-            for _ in range(reps):
-                g = gm + gS
+            for r in reversed(range(reps)):
+                if norm:
+                    y, n = steps[j][r]
+                    gx = np.where(n > ROW_NORM_EPS, (gS - y * np.sum(y * gS, axis=1, keepdims=True)) / np.maximum(n, ROW_NORM_EPS),
+                                  gS / ROW_NORM_EPS)
+                else:
+                    gx = gS
+                g = gm + gx
                 Rj = Rj + g
                 gm = beta * g
+                gS = gx
             R[j] = sign * Rj          # the gradient of dS_j
         if not post:
             gS = gS + D[j]
@@ -426,9 +447,9 @@ def _momentum_state_backward(phq, phk, v, eta, S0, chunk, mask, dO, dS_out, upda
 
 
 def ttt_lastlayer_backward_scan_ref(q, k, v, eta, W1, W3, W2, chunk, mask, dO, dW_out=None, update_chunks=None,
-                                    inner_steps=1, ascent=False, momentum=0.0):
+                                    inner_steps=1, ascent=False, momentum=0.0, rule=UPD_GD):
     """Gradients of one (batch, head) scan of the TTT-KVB layer whose inner loop trains W2 alone by
-    plain GD (ttt_scan_ref with last_layer_only, rule UPD_GD), for the loss
+    GD (ttt_scan_ref with last_layer_only, rule UPD_GD or UPD_GD_L2), for the loss
     L = sum_t dO_t . o_t + <dW1_out, W1> + <dW3_out, W3> + <dW2_out, W2_out>.
 
     With W1 and W3 frozen, phi(x) = SiLU(W1 x) o (W3 x) is fixed, the chunk gradient of W2 is
@@ -436,8 +457,9 @@ def ttt_lastlayer_backward_scan_ref(q, k, v, eta, W1, W3, W2, chunk, mask, dO, d
     phi(k), values v and state W2 (TTT-as-LA, Thm. 5.2-5.3 and Sec. 6.1 Steps 1-6); its outer-loop
     gradients (TTT-as-LA, Sec. 6.2) are those of linear attention (linattn_backward_scan_ref),
     followed by the chain rule through phi.  inner_steps repeats an update that does not depend on
-    W2, and ascent flips its sign: without momentum both scale eta.  With momentum (starting from
-    zero, its final state outside the loss) the state part is _momentum_state_backward.  dW_out is
+    W2, and ascent flips its sign: without momentum or norm both scale eta.  With momentum (starting
+    from zero, its final state outside the loss) or the L2 norm (UPD_GD_L2: Variant 1 of TTT-as-LA
+    Sec. 6.1 without Muon) the state part is _recurrent_state_backward.  dW_out is
     None or (dW1, dW3, dW2) of the shapes of (W1, W3, W2).  Returns (dq, dk, dv, deta, (dW1, dW3, dW2)).
     """
     q, k, v, eta, dO = (_f64(x) for x in (q, k, v, eta, dO))
@@ -447,14 +469,17 @@ def ttt_lastlayer_backward_scan_ref(q, k, v, eta, W1, W3, W2, chunk, mask, dO, d
     C = {"q": q @ W3.T, "k": k @ W3.T}
     phi = {s: silu(A[s]) * C[s] for s in ("q", "k")}
     dW2o = None if dW_out is None else dW_out[2]
-    if momentum == 0.0:
+    if rule not in (UPD_GD, UPD_GD_L2):
+        raise ValueError("the backward covers W2 learning alone by GD, with or without the L2 norm")
+    if momentum == 0.0 and rule == UPD_GD:
         f = sign * reps
         dphq, dphk, dv, deta, dW2 = linattn_backward_scan_ref(phi["q"], phi["k"], v, f * eta, W2, chunk, mask, dO,
                                                               dW2o, update_chunks)
         deta = f * deta
     else:
-        dphq, dphk, dv, deta, dW2 = _momentum_state_backward(phi["q"], phi["k"], v, eta, W2, chunk, mask, dO, dW2o,
-                                                             update_chunks, reps, sign, float(momentum))
+        dphq, dphk, dv, deta, dW2 = _recurrent_state_backward(phi["q"], phi["k"], v, eta, W2, chunk, mask, dO, dW2o,
+                                                              update_chunks, reps, sign, float(momentum),
+                                                              rule == UPD_GD_L2)
     dW1 = np.zeros_like(W1) if dW_out is None else _f64(dW_out[0]).copy()
     dW3 = np.zeros_like(W3) if dW_out is None else _f64(dW_out[1]).copy()
     dx = {}
@@ -469,7 +494,7 @@ def ttt_lastlayer_backward_scan_ref(q, k, v, eta, W1, W3, W2, chunk, mask, dO, d
 
 
 def ttt_lastlayer_backward_ref(q, k, v, eta, W1, W3, W2, chunk, mask, dO, dW_out=None, update_chunks=None,
-                               inner_steps=1, ascent=False, slices=None, momentum=0.0):
+                               inner_steps=1, ascent=False, slices=None, momentum=0.0, rule=UPD_GD):
     """ttt_lastlayer_backward_scan_ref over [B, H, N, d] inputs.  W1, W3, W2 are per head ([H, ...])
     or per (batch, head) ([B, H, ...]); the weight gradients take the same shape (per-head weights
     sum over the batch).  dW_out is None or three [B, H, ...] arrays (the W_out the layer returns
@@ -484,7 +509,7 @@ def ttt_lastlayer_backward_ref(q, k, v, eta, W1, W3, W2, chunk, mask, dO, dW_out
         ws = [x[h] if per_head else x[b, h] for x in (W1, W3, W2)]
         dwo = None if dW_out is None else tuple(x[b, h] for x in dW_out)
         r = ttt_lastlayer_backward_scan_ref(q[b, h], k[b, h], v[b, h], eta[b, h], *ws, chunk, mask, dO[b, h], dwo,
-                                            update_chunks, inner_steps, ascent, momentum)
+                                            update_chunks, inner_steps, ascent, momentum, rule)
         dq[b, h], dk[b, h], dv[b, h], deta[b, h] = r[:4]
         for i in range(3):
             if per_head:

@@ -25,9 +25,9 @@ def problem(seed, N=9, d=3, m=4):
     return q, k, v, eta, W1, W3, W2, dO, dWo
 
 
-def loss(q, k, v, eta, W1, W3, W2, chunk, mask, dO, dWo, upd, steps, ascent, beta=0.0):
+def loss(q, k, v, eta, W1, W3, W2, chunk, mask, dO, dWo, upd, steps, ascent, beta=0.0, rule=O.UPD_GD):
     # the recurrence with momentum starting from zero; its final momentum is not part of the loss
-    o, W, _ = O.ttt_scan_ref(q, k, v, eta, W1, W3, W2, chunk, mask, O.UPD_GD, momentum=beta, last_layer_only=True,
+    o, W, _ = O.ttt_scan_ref(q, k, v, eta, W1, W3, W2, chunk, mask, rule, momentum=beta, last_layer_only=True,
                              update_chunks=upd, inner_steps=steps, ascent=ascent)
     return float(np.sum(dO * o) + sum(np.sum(g * w) for g, w in zip(dWo, W)))
 
@@ -38,14 +38,20 @@ CASES = [(O.MASK_APPLY_THEN_UPDATE, 3, None, 1, False, 0.0), (O.MASK_UPDATE_THEN
          # momentum (W2 <- W2 - M, M <- beta M + g): every order, several steps, ascent, skipped chunks
          (O.MASK_APPLY_THEN_UPDATE, 2, None, 1, False, 0.9), (O.MASK_UPDATE_THEN_APPLY, 3, None, 2, True, 0.5),
          (O.MASK_FULL, 9, None, 3, False, 0.7), (O.MASK_STRIDED, 2, [0, 1, 1, 0, 1], 2, False, 0.9)]
+# the L2 norm after each step (Variant 1 without Muon), alone and with momentum
+CASES_L2 = [(O.MASK_APPLY_THEN_UPDATE, 3, None, 1, False, 0.0), (O.MASK_UPDATE_THEN_APPLY, 4, None, 2, True, 0.0),
+            (O.MASK_FULL, 9, None, 1, False, 0.0), (O.MASK_STRIDED, 2, [1, 0, 1, 1, 0], 1, False, 0.0),
+            (O.MASK_APPLY_THEN_UPDATE, 2, None, 1, False, 0.9), (O.MASK_UPDATE_THEN_APPLY, 3, None, 3, True, 0.5),
+            (O.MASK_STRIDED, 2, [0, 1, 1, 0, 1], 2, False, 0.9)]
 
 
-@pytest.mark.parametrize("mask,chunk,upd,steps,ascent,beta", CASES)
-def test_layer_backward_matches_finite_differences(mask, chunk, upd, steps, ascent, beta):
-    args = list(problem(90 + mask + 7 * steps + int(10 * beta)))
+@pytest.mark.parametrize("mask,chunk,upd,steps,ascent,beta,rule",
+                         [c + (O.UPD_GD,) for c in CASES] + [c + (O.UPD_GD_L2,) for c in CASES_L2])
+def test_layer_backward_matches_finite_differences(mask, chunk, upd, steps, ascent, beta, rule):
+    args = list(problem(90 + mask + 7 * steps + int(10 * beta) + 5 * rule))
     dO, dWo = args[7], args[8]
     args = args[:7]
-    got = O.ttt_lastlayer_backward_scan_ref(*args, chunk, mask, dO, dWo, upd, steps, ascent, momentum=beta)
+    got = O.ttt_lastlayer_backward_scan_ref(*args, chunk, mask, dO, dWo, upd, steps, ascent, momentum=beta, rule=rule)
     grads = list(got[:4]) + list(got[4])
     h = 1e-6
     for which, g in enumerate(grads):
@@ -53,9 +59,9 @@ def test_layer_backward_matches_finite_differences(mask, chunk, upd, steps, asce
         for idx in np.ndindex(*args[which].shape):
             a = [x.copy() for x in args]
             a[which][idx] += h
-            lp = loss(*a, chunk, mask, dO, dWo, upd, steps, ascent, beta)
+            lp = loss(*a, chunk, mask, dO, dWo, upd, steps, ascent, beta, rule)
             a[which][idx] -= 2 * h
-            lm = loss(*a, chunk, mask, dO, dWo, upd, steps, ascent, beta)
+            lm = loss(*a, chunk, mask, dO, dWo, upd, steps, ascent, beta, rule)
             fd[idx] = (lp - lm) / (2 * h)
         assert rel(g, fd) < 1e-6, which
 
@@ -65,11 +71,11 @@ def test_momentum_zero_matches_the_linear_path():
     args = list(problem(150))
     dO, dWo = args[7], args[8]
     a = O.ttt_lastlayer_backward_scan_ref(*args[:7], 3, O.MASK_APPLY_THEN_UPDATE, dO, dWo, None, 2, True)
-    b = O.ttt_ref._momentum_state_backward  # the momentum path run directly with beta = 0 on the same features
+    b = O.ttt_ref._recurrent_state_backward  # the recurrent path run directly with beta = 0 on the same features
     W1, W3 = args[4], args[5]
     phi = lambda x: O.silu(x @ W1.T) * (x @ W3.T)
     got = b(phi(args[0]), phi(args[1]), args[2], args[3], args[6], 3, O.MASK_APPLY_THEN_UPDATE, dO, dWo[2], None, 2,
-            -1.0, 0.0)
+            -1.0, 0.0, False)
     ref = O.linattn_backward_scan_ref(phi(args[0]), phi(args[1]), args[2], -2.0 * args[3], args[6], 3,
                                       O.MASK_APPLY_THEN_UPDATE, dO, dWo[2])
     for i, (x, y) in enumerate(zip(got, ref)):
@@ -83,7 +89,8 @@ def test_momentum_zero_matches_the_linear_path():
                                                  (O.MASK_STRIDED, 3, [0, 1, 1, 0, 1], 0.0),
                                                  (O.MASK_APPLY_THEN_UPDATE, 4, None, 0.9),
                                                  (O.MASK_STRIDED, 3, [1, 0, 1, 1, 0], 0.6)])
-def test_layer_backward_matches_double_autograd(mask, chunk, upd, beta):
+@pytest.mark.parametrize("norm", [False, True])
+def test_layer_backward_matches_double_autograd(mask, chunk, upd, beta, norm):
     torch = pytest.importorskip("torch")
     N, d, m = 13, 4, 6
     q, k, v, eta, W1, W3, W2, dO, dWo = problem(110 + mask, N, d, m)
@@ -104,12 +111,15 @@ def test_layer_backward_matches_double_autograd(mask, chunk, upd, beta):
             g, = torch.autograd.grad(inner, W, create_graph=True)
             M = beta * M + g
             W = W - M
+            if norm:  # rows to unit norm over the input dimension (eps never binds here)
+                W = W / torch.clamp(torch.sqrt((W * W).sum(dim=1, keepdim=True)), min=1e-6)
         if post:
             outs.append(f(W, tq[lo:hi]))
     L = (torch.cat(outs) * torch.tensor(dO)).sum()
     L = L + (t1 * torch.tensor(dWo[0])).sum() + (t3 * torch.tensor(dWo[1])).sum() + (W * torch.tensor(dWo[2])).sum()
     L.backward()
-    got = O.ttt_lastlayer_backward_scan_ref(q, k, v, eta, W1, W3, W2, chunk, mask, dO, dWo, upd, momentum=beta)
+    got = O.ttt_lastlayer_backward_scan_ref(q, k, v, eta, W1, W3, W2, chunk, mask, dO, dWo, upd, momentum=beta,
+                                            rule=O.UPD_GD_L2 if norm else O.UPD_GD)
     for g, x in zip(list(got[:4]) + list(got[4]), t):
         assert rel(g, x.grad.numpy()) < 1e-12
 
