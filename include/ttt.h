@@ -192,21 +192,24 @@ ttt_status ttt_forward_noalloc(const ttt_desc* desc, const void* q, const void* 
  * call without it): the io-dtype copies of W1 | W3 and their transposes, phi(q), phi(k), and the
  * factors of phi's backward for both sides, later dA | dC (12 m_h bytes per token and scan in bf16,
  * twice in fp32), the scans' dW2, the partial sums of dW1 | dW3, and the linear-attention
- * backward's workspace over d_k = m_h, d_v = d_h (linattn_backward_workspace_bytes).
+ * backward's workspace over d_k = m_h, d_v = d_h (linattn_backward_workspace_bytes); with
+ * TTT_UPD_GD_L2 also W2 after every step of every chunk in fp32, and its row norms.
  */
 ttt_status ttt_backward_workspace_bytes(const ttt_desc* desc, size_t* bytes);
 
 /*
  * Backward of ttt_forward for the layer whose inner loop trains W2 alone by GD: desc must have
- * last_layer_only = 1, rule TTT_UPD_GD and chunk_rates 0 (else TTT_ERR_UNSUPPORTED); inner_steps,
- * ascent, momentum, the chunked masks and w0_per_batch are as for the forward, and parallel_form is
- * ignored (both forms compute the same layer).  With W1 and W3 frozen, phi(x) = SiLU(W1 x) * (W3 x)
- * is fixed and the layer is chunked linear attention with queries phi(q), keys phi(k), values v and
- * state W2: each of an updating chunk's max(inner_steps, 1) steps adds u = (ascent ? -1 : 1) *
- * sum eta v phi(k)^T to W2, directly or, with momentum, through M <- momentum M - u, W2 <- W2 - M
- * ("TTT with KV Binding Is Secretly Linear Attention", Thm. 5.2-5.3, Sec. 6.1-6.2 and Fig. 4: the
- * outer-loop gradients of training through the parallel form).  The momentum is the one a forward
- * call with M_inout = NULL keeps: it starts from zero and its final state is not part of the loss.
+ * last_layer_only = 1, rule TTT_UPD_GD or TTT_UPD_GD_L2, and chunk_rates 0 (else
+ * TTT_ERR_UNSUPPORTED); inner_steps, ascent, momentum, the chunked masks and w0_per_batch are as for
+ * the forward, and parallel_form is ignored (both forms compute the same layer).  With W1 and W3
+ * frozen, phi(x) = SiLU(W1 x) * (W3 x) is fixed and W2 is the state of chunked linear attention with
+ * queries phi(q), keys phi(k) and values v: each of an updating chunk's max(inner_steps, 1) steps
+ * adds u = (ascent ? -1 : 1) * sum eta v phi(k)^T to W2, directly or, with momentum, through
+ * M <- momentum M - u, W2 <- W2 - M, and TTT_UPD_GD_L2 then L2-normalizes W2's rows (notes Eq. (5);
+ * Variant 1 of "TTT with KV Binding Is Secretly Linear Attention", Sec. 6.1, without Muon)
+ * (the same paper, Thm. 5.2-5.3, Sec. 6.1-6.2 and Fig. 4: the outer-loop gradients of training
+ * through the parallel form).  The momentum is the one a forward call with M_inout = NULL keeps: it
+ * starts from zero and its final state is not part of the loss.
  * The gradients are those of
  *     L = sum over tokens of dO . o + <dW_out, W_out>
  * (W_out as ttt_forward writes it: W1 and W3 as given, W2 after the last chunk), for every input:

@@ -120,7 +120,7 @@ ttt_status validate_ttt_desc(const ttt_desc* D);
 // dS_out + s * dso_stride (null: zeros); dS0 of scan s to dS0 + s * ds0_stride (null: not written).
 // The forward's updating chunks added u = dsign * sum eta v k^T to the state reps times, directly
 // or (mom) through a running term m <- beta m + u, S <- S + m that started at zero and whose final
-// value is not part of the loss.
+// value is not part of the loss; with norm every step's S then had its rows L2-normalized.
 // gate[0], gate[1]: both null, or [S][N][2 d_k] buffers of io-dtype factors u | w for dq and dk:
 // then dq and dk are not written; each gate row becomes dq u | dq w (dk u | dk w) in place.
 struct LinBwdIO {
@@ -135,12 +135,13 @@ struct LinBwdIO {
     int reps = 1;
     int mom = 0;
     float beta = 0.f;
+    int norm = 0;  // each step ends in the L2 norm of the state's rows (over d_k), w / max(|w|, 1e-6)
     void* gate[2] = {nullptr, nullptr};
 };
 // the backward's checks of a linear-attention descriptor
 ttt_status validate_lin_desc_bwd(const linattn_desc* D);
-// workspace of lin_chunked_bwd
-size_t lin_chunked_bwd_ws_bytes(const linattn_desc& D);
+// workspace of lin_chunked_bwd (norm, reps: those of the LinBwdIO the call will take)
+size_t lin_chunked_bwd_ws_bytes(const linattn_desc& D, int norm = 0, int reps = 1);
 // D.mask is a chunked mask (not TOKEN_CAUSAL); flags as for lin_chunked_run.  dq, dk [S][N][d_k],
 // dv [S][N][d_v], deta [S][N] as for linattn_backward.
 template <typename T>

@@ -899,6 +899,138 @@ template ttt_status lin_chunked_run<float>(const linattn_desc&, const uint32_t (
 // read S_c and R_j as one io-dtype plane, as the forward's apply reads S_c.
 constexpr int kBwdPlanes = kStatePlanes;
 
+// The states of a recurrence whose steps end in the L2 norm of the state's rows, forward and
+// transposed: one wave per row of one scan's state (d_k elements, 4 per lane and float4), walking
+// the chunks in fp32.  Forward: per updating chunk and step, m <- beta m + dsign dS_c (beta = 0
+// without momentum), x = S + m, S <- x / max(|x|, 1e-6) row by row; the step's S and |x| are kept
+// for the transpose, and each chunk's state as its queries see it goes out as one io-dtype plane.
+// Reverse, from the last chunk, with st and mom the gradients of S and m: every chunk's D_c adds to
+// st (where its queries saw it), and each step, last first, takes the norm's transpose
+// gx = (st - y (y . st)) / |x| (st / 1e-6 where |x| <= 1e-6; y the step's S), gives g = mom + gx to
+// the chunk's update, and sets mom <- beta g, st <- gx; the chunk's slot receives the sum of its g.
+constexpr int kRowScanVec = 8;  // float4 per lane: rows of up to 2048 elements
+constexpr float kRowNormEps = 1e-6f;
+
+template <typename T> struct RowScanArgs {
+    const float* src;  // [S][nc][d_v][d_k] fp32: the chunk updates (forward) or the D_c (reverse)
+    T* out;            // [S][nc][d_v][d_k]: the states the chunks' queries see (forward) or R_c (reverse)
+    float* y;          // [S][nc * reps][d_v][d_k] fp32: each step's state
+    float* nrm;        // [S][nc * reps][d_v]: each step's |x|
+    LinStateIO io;     // forward: S0; reverse: S0 = dS_out, Sout = dS0; dsign, reps, beta
+    int64_t dvk; int dv, dk, nc, mode, nscan, rev;
+    uint32_t flags[32];
+};
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_lin_row_scan(RowScanArgs<T> a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    if (row >= (int64_t)a.nscan * a.dv) return;  // whole waves; the kernel has no barrier
+    const int64_t scan = row / a.dv;
+    const int r = (int)(row % a.dv), nv = a.dk / 4;
+    const LinStateIO& io = a.io;
+    const int reps = io.reps;
+    const float beta = io.mom ? io.beta : 0.f;
+    const bool post = a.mode == TTT_MASK_UPDATE_THEN_APPLY || a.mode == TTT_MASK_FULL;
+    f32x4_t st[kRowScanVec], mm[kRowScanVec];
+#pragma unroll
+    for (int i = 0; i < kRowScanVec; ++i) {
+        st[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        mm[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const int e = (i * 64 + lane) * 4;
+        if (io.S0 && i * 64 + lane < nv) {  // only 4-byte aligned
+            const float* s0 = io.S0 + (io.s0_heads ? scan % io.s0_heads : scan) * io.s0_stride + (int64_t)r * a.dk + e;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) st[i][u] = s0[u];
+        }
+    }
+    auto slot = [&](int c) { return (scan * a.nc + c) * a.dvk + (int64_t)r * a.dk; };
+    auto step_slot = [&](int c, int k) { return ((scan * a.nc + c) * reps + k); };
+    auto put = [&](int c, const f32x4_t (&x)[kRowScanVec]) {
+        T* dst = a.out + slot(c);
+#pragma unroll
+        for (int i = 0; i < kRowScanVec; ++i)
+            if (i * 64 + lane < nv) Pack4<T>::store(dst + (i * 64 + lane) * 4, x[i][0], x[i][1], x[i][2], x[i][3]);
+    };
+    auto load = [&](const float* p, f32x4_t (&x)[kRowScanVec]) {
+#pragma unroll
+        for (int i = 0; i < kRowScanVec; ++i)
+            x[i] = i * 64 + lane < nv ? *reinterpret_cast<const f32x4_t*>(p + (i * 64 + lane) * 4)
+                                      : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    };
+    auto dot = [&](const f32x4_t (&x)[kRowScanVec], const f32x4_t (&w)[kRowScanVec]) {
+        float t = 0.f;
+#pragma unroll
+        for (int i = 0; i < kRowScanVec; ++i) t += x[i][0] * w[i][0] + x[i][1] * w[i][1] + x[i][2] * w[i][2] + x[i][3] * w[i][3];
+        return wave_sum(t);
+    };
+    f32x4_t d[kRowScanVec];
+    if (!a.rev) {
+        for (int c = 0; c < a.nc; ++c) {
+            const bool upd = a.mode != TTT_MASK_STRIDED || ((a.flags[c >> 5] >> (c & 31)) & 1u);
+            if (!post) put(c, st);
+            if (upd) {
+                load(a.src + slot(c), d);
+                for (int k = 0; k < reps; ++k) {
+#pragma unroll
+                    for (int i = 0; i < kRowScanVec; ++i) {
+                        mm[i] = beta * mm[i] + io.dsign * d[i];
+                        st[i] += mm[i];
+                    }
+                    const float n = sqrtf(dot(st, st)), f = 1.f / fmaxf(n, kRowNormEps);
+                    float* yp = a.y + step_slot(c, k) * a.dvk + (int64_t)r * a.dk;
+#pragma unroll
+                    for (int i = 0; i < kRowScanVec; ++i) {
+                        st[i] *= f;
+                        if (i * 64 + lane < nv) *reinterpret_cast<f32x4_t*>(yp + (i * 64 + lane) * 4) = st[i];
+                    }
+                    if (lane == 0) a.nrm[step_slot(c, k) * a.dv + r] = n;
+                }
+            }
+            if (post) put(c, st);
+        }
+        return;
+    }
+    f32x4_t y[kRowScanVec], rs[kRowScanVec];
+    for (int i = 0; i < a.nc; ++i) {
+        const int c = a.nc - 1 - i;
+        const bool upd = a.mode != TTT_MASK_STRIDED || ((a.flags[c >> 5] >> (c & 31)) & 1u);
+        load(a.src + slot(c), d);
+        if (post)
+#pragma unroll
+            for (int j = 0; j < kRowScanVec; ++j) st[j] += d[j];
+        if (upd) {
+#pragma unroll
+            for (int j = 0; j < kRowScanVec; ++j) rs[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int k = reps - 1; k >= 0; --k) {
+                load(a.y + step_slot(c, k) * a.dvk + (int64_t)r * a.dk, y);
+                const float n = a.nrm[step_slot(c, k) * a.dv + r];
+                const float yg = dot(y, st);
+                const bool big = n > kRowNormEps;
+                const float inv = 1.f / fmaxf(n, kRowNormEps);
+#pragma unroll
+                for (int j = 0; j < kRowScanVec; ++j) {
+                    const f32x4_t gx = big ? (st[j] - yg * y[j]) * inv : st[j] * inv;
+                    const f32x4_t g = mm[j] + gx;
+                    rs[j] += g;
+                    mm[j] = beta * g;
+                    st[j] = gx;
+                }
+            }
+            put(c, rs);
+        }
+        if (!post)
+#pragma unroll
+            for (int j = 0; j < kRowScanVec; ++j) st[j] += d[j];
+    }
+    if (io.Sout)
+#pragma unroll
+        for (int i = 0; i < kRowScanVec; ++i)
+            if (i * 64 + lane < nv)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) io.Sout[scan * io.sout_stride + (int64_t)r * a.dk + (i * 64 + lane) * 4 + u] = st[i][u];
+}
+
 // dq = dO S_c and dk = diag(eta) v R_c for one chunk: tokens x d_k, contracting over d_v.  The
 // d_v x d_k matrix goes through the transposing stager (its d_k index is the tile column).  One
 // launch covers both jobs: the first per_job workgroups do dq, the others dk.  The tile leaves row by
@@ -1120,12 +1252,15 @@ ttt_status validate_lin_desc_bwd(const linattn_desc* D) {
     return TTT_OK;
 }
 
-// dS_c (fp32), then S_c and R_c (one io-dtype plane each), then the deta partials
-size_t lin_chunked_bwd_ws_bytes(const linattn_desc& D) {
+// dS_c (fp32), then S_c and R_c (one io-dtype plane each), then the deta partials; with the row norm
+// also every step's state (fp32) and row norms
+size_t lin_chunked_bwd_ws_bytes(const linattn_desc& D, int norm, int reps) {
     if (D.N == 0) return 0;
     const int64_t S = (int64_t)D.B * D.H, nc = cdiv(D.N, D.chunk), ntn = cdiv(D.d_k, kApplyCols);
     const size_t es = D.io_dtype == TTT_BF16 ? 2 : 4, n = (size_t)(S * nc * (int64_t)D.d_v * D.d_k);
-    return align256(n * 4) + 2 * align256(n * es) + (ntn > 1 ? align256((size_t)(ntn * S * D.N * 4)) : 0);
+    size_t b = align256(n * 4) + 2 * align256(n * es) + (ntn > 1 ? align256((size_t)(ntn * S * D.N * 4)) : 0);
+    if (norm) b += align256(n * reps * 4) + align256((size_t)(S * nc * reps * (int64_t)D.d_v * 4));
+    return b;
 }
 
 template <typename T>
@@ -1135,10 +1270,37 @@ ttt_status lin_chunked_bwd(const linattn_desc& D, const uint32_t (&flags)[32], c
     const int64_t S = (int64_t)D.B * D.H, dvk = (int64_t)D.d_v * D.d_k;
     const int64_t chunk = D.chunk, nc = D.N ? cdiv(D.N, chunk) : 0;
     const size_t sb = align256((size_t)(S * nc * dvk * 4)), tb = align256((size_t)(S * nc * dvk) * sizeof(T));
+    const int64_t ntk_ = cdiv(D.d_k, kApplyCols);
+    const size_t pb = ntk_ > 1 ? align256((size_t)(ntk_ * S * D.N * 4)) : 0;
     float* dS = (float*)ws;
     T* Sc = (T*)(ws + sb);
     T* R = (T*)(ws + sb + tb);
     float* part = (float*)(ws + sb + 2 * tb);
+    float* ybuf = (float*)(ws + sb + 2 * tb + pb);  // norm: each step's state, then the row norms
+    float* nbuf = (float*)(ws + sb + 2 * tb + pb + align256((size_t)(S * nc * dvk) * io.reps * 4));
+    // the row-wise scans of a state whose steps end in the row norm
+    auto row_scan = [&](const float* src, T* out, const LinStateIO& sio, int rev) -> ttt_status {
+        RowScanArgs<T> ra{};
+        ra.src = src;
+        ra.out = out;
+        ra.y = ybuf;
+        ra.nrm = nbuf;
+        ra.io = sio;
+        ra.dvk = dvk;
+        ra.dv = D.d_v;
+        ra.dk = D.d_k;
+        ra.nc = (int)nc;
+        ra.mode = D.mask;
+        ra.nscan = (int)S;
+        ra.rev = rev;
+        for (int w = 0; w < 32; ++w) ra.flags[w] = flags[w];
+        {
+            ProfScope ps(PK_LIN_SCAN, st);
+            hipLaunchKernelGGL(k_lin_row_scan<T>, dim3((unsigned)cdiv(S * D.d_v, kThreads / 64)), dim3(kThreads), 0,
+                               st, ra);
+        }
+        return check_launch("k_lin_row_scan", st);
+    };
     uint32_t all[32];
     for (int w = 0; w < 32; ++w) all[w] = ~0u;
     ttt_status rc;
@@ -1153,7 +1315,9 @@ ttt_status lin_chunked_bwd(const linattn_desc& D, const uint32_t (&flags)[32], c
         fio.reps = io.reps;
         fio.mom = io.mom;
         fio.beta = io.beta;
-        if ((rc = launch_scan<T>(D, nc, D.mask, flags, dS, Sc, fio, 0, kBwdPlanes, st)) != TTT_OK) return rc;
+        if (io.norm) rc = row_scan(dS, Sc, fio, 0);
+        else rc = launch_scan<T>(D, nc, D.mask, flags, dS, Sc, fio, 0, kBwdPlanes, st);
+        if (rc != TTT_OK) return rc;
         // D_c = sum over the chunk of dO q^T, every chunk
         if ((rc = launch_delta<T, false>(D, chunk, nc, TTT_MASK_APPLY_THEN_UPDATE, all, q, dO, nullptr, dS, st)) !=
             TTT_OK)
@@ -1166,17 +1330,19 @@ ttt_status lin_chunked_bwd(const linattn_desc& D, const uint32_t (&flags)[32], c
     rio.s0_stride = io.dso_stride;
     rio.Sout = io.dS0;
     rio.sout_stride = io.ds0_stride;
-    if (io.mom) {  // the momentum recurrence transposed: every D_c adds, the mask's chunks update
-        rio.mom = 1;
+    if (io.mom || io.norm) {  // the recurrence transposed: every D_c adds, the mask's chunks update
+        rio.mom = io.mom;
         rio.beta = io.beta;
         rio.reps = io.reps;
     }
-    if (D.N > 0 || io.dS0)
-        if ((rc = launch_scan<T>(D, nc, D.mask, io.mom ? flags : all, dS, R, rio, 1, kBwdPlanes, st)) != TTT_OK)
-            return rc;
-    // the gradient of a chunk's update sum eta v k^T: R_j times the update's sign, and (without
-    // momentum) times its repeats, which the reverse scan folds in otherwise
-    const float es = io.mom ? io.dsign : io.dsign * (float)io.reps;
+    if (D.N > 0 || io.dS0) {
+        if (io.norm) rc = row_scan(dS, R, rio, 1);
+        else rc = launch_scan<T>(D, nc, D.mask, io.mom ? flags : all, dS, R, rio, 1, kBwdPlanes, st);
+        if (rc != TTT_OK) return rc;
+    }
+    // the gradient of a chunk's update sum eta v k^T: R_j times the update's sign, and (for a plain
+    // sum) times its repeats, which the transposed recurrence folds in otherwise
+    const float es = (io.mom || io.norm) ? io.dsign : io.dsign * (float)io.reps;
     if (D.N == 0) return TTT_OK;
     const int ntt = (int)cdiv(std::min<int64_t>(chunk, D.N), kApplyRows);
     const int ntk = (int)cdiv(D.d_k, kApplyCols);  // column tiles of dq, dk (and deta partials)

@@ -1,5 +1,5 @@
 // Backward of the TTT-KVB layer whose inner loop trains W2 alone by GD (last layer only, with or
-// without momentum): the outer-loop gradients that training through the parallel form needs ("TTT with KV
+// without momentum and the L2 norm): the outer-loop gradients that training through the parallel form needs ("TTT with KV
 // Binding Is Secretly Linear Attention", Thm. 5.2-5.3, Sec. 6.1-6.2 and Fig. 4).  With W1 and W3
 // frozen the layer is chunked linear attention with queries phi(q), keys phi(k), values v and state
 // W2, phi(x) = SiLU(W1 x) o (W3 x) (PaperTrace "5.2.1 LaCT and TTT-E2E", Eq. (3)), so its gradients
@@ -239,7 +239,7 @@ static BLayout make_blayout(const ttt_desc& D, bool want_dw) {
             L.part = take((size_t)L.nparts * nw * 2 * dm * 4);
         }
     }
-    L.lin = take(lin_chunked_bwd_ws_bytes(lin_desc_of(D)));
+    L.lin = take(lin_chunked_bwd_ws_bytes(lin_desc_of(D), D.rule == TTT_UPD_GD_L2, D.inner_steps > 1 ? D.inner_steps : 1));
     L.total = off;
     return L;
 }
@@ -247,10 +247,10 @@ static BLayout make_blayout(const ttt_desc& D, bool want_dw) {
 static ttt_status validate_bwd(const ttt_desc* D) {
     ttt_status rc = validate_ttt_desc(D);
     if (rc != TTT_OK) return rc;
-    if (!D->last_layer_only || D->rule != TTT_UPD_GD || D->chunk_rates)
+    if (!D->last_layer_only || (D->rule != TTT_UPD_GD && D->rule != TTT_UPD_GD_L2) || D->chunk_rates)
         return fail(TTT_ERR_UNSUPPORTED,
-                    "the backward covers the layer whose inner loop trains W2 alone by GD (with or without momentum): "
-                    "last_layer_only = 1, rule TTT_UPD_GD, per-token rates");
+                    "the backward covers the layer whose inner loop trains W2 alone by GD (with or without momentum "
+                    "and the L2 norm): last_layer_only = 1, rule TTT_UPD_GD or TTT_UPD_GD_L2, per-token rates");
     const int64_t S = (int64_t)D->B * D->H, nc = D->N > 0 ? cdiv(D->N, D->chunk) : 0;
     if (D->mask == TTT_MASK_STRIDED && nc > 32 * 32)
         return fail(TTT_ERR_UNSUPPORTED, "the backward with MASK_STRIDED supports at most 1024 chunks");
@@ -334,6 +334,7 @@ static ttt_status run_backward(const ttt_desc& D, const BLayout& L, const T* q, 
         io.mom = 1;
         io.beta = D.momentum;
     }
+    io.norm = D.rule == TTT_UPD_GD_L2;  // W2's rows L2-normalized after every step
     if (D.N > 0) {  // the gradients of phi(q), phi(k) turn u | w into dA | dC
         io.gate[0] = dac[0];
         io.gate[1] = dac[1];

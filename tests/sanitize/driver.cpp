@@ -64,12 +64,12 @@ static void run_ttt(ttt_desc D) {
     // a workspace one byte short is refused before any buffer is looked at
     if (s == TTT_OK && need > 0 && (int64_t)D.B * D.H > 0)
         EXPECT(ttt_forward(&D, q, k, v, eta, W0, o, Wout, nullptr, ws, need - 1, nullptr) == TTT_ERR_WORKSPACE);
-    // the backward: the forward's checks, then the layer it covers (W2 alone by GD, per-token rates)
+    // the backward: the forward's checks, then the layer it covers (W2 alone by GD [+ L2], per-token rates)
     size_t bneed = 0;
     ttt_status bs = ttt_backward_workspace_bytes(&D, &bneed);
     check_message(bs);
     if (s != TTT_OK) EXPECT(bs == s);
-    const bool covered = D.last_layer_only == 1 && D.rule == TTT_UPD_GD && D.chunk_rates == 0;
+    const bool covered = D.last_layer_only == 1 && (D.rule == TTT_UPD_GD || D.rule == TTT_UPD_GD_L2) && D.chunk_rates == 0;
     if (s == TTT_OK && !covered) EXPECT(bs == TTT_ERR_UNSUPPORTED);
     const void* dO = (const void*)(P + (9ull << 36));
     void* dq = (void*)(P + (10ull << 36));

@@ -31,9 +31,9 @@ def split(W, d, m):
 
 
 def run(seed, B, H, N, d, m, chunk, mask, bf16, flags=None, inner=1, ascent=False, per_batch=False, dW_out=True,
-        want_dW0=True, momentum=0.0):
+        want_dW0=True, momentum=0.0, rule=O.UPD_GD):
     say(f"ttt_backward case B{B} H{H} N{N} d{d} m{m} b{chunk} mask{mask} bf16={bf16} flags={flags} inner{inner} "
-        f"ascent{ascent} per_batch={per_batch} dW_out={dW_out} want_dW0={want_dW0} momentum={momentum}")
+        f"ascent{ascent} per_batch={per_batch} dW_out={dW_out} want_dW0={want_dW0} momentum={momentum} rule={rule}")
     (q, k, v, eta, W0), (hq, hk, hv, he, W1, W3, W2) = full_ttt_inputs(seed, B, H, N, d, m, bf16)
     if per_batch:  # a different weight block for every (batch, head)
         Ws = [np.zeros((B, H) + w.shape[1:], np.float32) for w in (W1, W3, W2)]
@@ -48,10 +48,10 @@ def run(seed, B, H, N, d, m, chunk, mask, bf16, flags=None, inner=1, ascent=Fals
     dt = torch.bfloat16 if bf16 else torch.float32
     got = T.ttt_backward(q, k, v, eta, W0, dev(dO, dt), chunk, mask, m_h=m,
                          dW_out=None if dWo is None else dev(pack(*dWo)), want_dW0=want_dW0, update_chunks=flags,
-                         inner_steps=inner, ascent=ascent, momentum=momentum)
+                         inner_steps=inner, ascent=ascent, momentum=momentum, update_rule=rule)
     torch.cuda.synchronize()
     ref = O.ttt_lastlayer_backward_ref(hq, hk, hv, he, W1, W3, W2, chunk, mask, dO, dWo, flags, inner, ascent,
-                                       momentum=momentum)
+                                       momentum=momentum, rule=rule)
     tol = TOL[bf16]
     if N == 0:
         for g, r in zip(got[:4], ref[:4]):
@@ -108,6 +108,29 @@ def test_momentum(mask, chunk, flags, inner, ascent, mom, bf16):
     # the W2 steps through a momentum that starts from zero (the reverse scan walks the momentum
     # recurrence transposed); N = 308 leaves a ragged last chunk, m = 160 partial tiles
     run(11, 1, 2, 308, 64, 160, chunk, mask, bf16, flags=flags, inner=inner, ascent=ascent, momentum=mom)
+
+
+L2_CASES = [
+    # mask, chunk, strided flags, inner steps, ascent, momentum
+    (O.MASK_APPLY_THEN_UPDATE, 96, None, 1, False, 0.0),
+    (O.MASK_UPDATE_THEN_APPLY, 96, None, 2, True, 0.0),
+    (O.MASK_APPLY_THEN_UPDATE, 96, None, 1, False, 0.9),
+    (O.MASK_STRIDED, 96, [0, 1, 1, 0], 3, False, 0.5),
+]
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("mask,chunk,flags,inner,ascent,mom", L2_CASES)
+def test_l2_norm(mask, chunk, flags, inner, ascent, mom, bf16):
+    # Variant 1 without Muon: W2's rows L2-normalized after every step (the row-wise scans, forward
+    # and transposed); m = 160 gives W2 rows that span two 128-wide float4 groups per lane
+    run(12, 1, 2, 308, 64, 160, chunk, mask, bf16, flags=flags, inner=inner, ascent=ascent, momentum=mom,
+        rule=O.UPD_GD_L2)
+
+
+def test_l2_norm_full_mask_per_batch_weights():
+    run(13, 2, 2, 150, 64, 96, 150, O.MASK_FULL, True, per_batch=True, rule=O.UPD_GD_L2)
+    run(13, 2, 2, 150, 64, 96, 150, O.MASK_FULL, False, rule=O.UPD_GD_L2, momentum=0.9)
 
 
 @pytest.mark.parametrize("bf16", [False, True])
