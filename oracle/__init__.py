@@ -12,4 +12,5 @@ from .ttt_ref import (  # noqa: F401
     ttt_scan_ref, ttt_forward_ref, linattn_scan_ref, linattn_forward_ref, gemm_intensity,
     linattn_backward_scan_ref, linattn_backward_ref,
     ttt_lastlayer_backward_scan_ref, ttt_lastlayer_backward_ref,
+    swiglu_apply_backward, chunk_gradients_backward, ttt_backward_scan_ref, ttt_backward_ref,
 )

@@ -28,6 +28,10 @@ Training"):
 * the backward of the layer with frozen W1, W3 (last layer only, GD, momentum, the L2 norm):
   the state's recurrence transposed over phi(q), phi(k), then phi's chain rule  TTT-as-LA, Thm. 5.2-5.3,
                                                                    Sec. 6.1-6.2
+* the backward of the chunk recurrence with all three weights learning (GD, GD + L2, momentum):
+  reverse mode over the steps, each through the norm's transpose, W - U, the momentum and the
+  chunk gradient differentiated once more (SiLU'' included) .... TTT-as-LA, Sec. 6.2; LaCT notes,
+                                                                   Eqs. (2)-(5) and section 1.1
 * gradient ascent in the inner loop: the step's sign flips ....... TTT-as-LA, Sec. 4.2 and 5.2
 * per-chunk rates outside the optimizer step: momentum dW_j = g_j + alpha_j dW_{j-1} over the
   chunk gradient g_j (unit token weights), W <- W - eta_j Opt(dW_j) .. TTT-as-LA, App. E.1 (per token)
@@ -510,6 +514,170 @@ def ttt_lastlayer_backward_ref(q, k, v, eta, W1, W3, W2, chunk, mask, dO, dW_out
         dwo = None if dW_out is None else tuple(x[b, h] for x in dW_out)
         r = ttt_lastlayer_backward_scan_ref(q[b, h], k[b, h], v[b, h], eta[b, h], *ws, chunk, mask, dO[b, h], dwo,
                                             update_chunks, inner_steps, ascent, momentum, rule)
+        dq[b, h], dk[b, h], dv[b, h], deta[b, h] = r[:4]
+        for i in range(3):
+            if per_head:
+                dW[i][h] += r[4][i]
+            else:
+                dW[i][b, h] = r[4][i]
+    return dq, dk, dv, deta, tuple(dW)
+
+
+def _row_norm_transpose(X, g, eps=ROW_NORM_EPS):
+    """The transpose of L2-Normalize's Jacobian at X (rows over the input dimension), applied to a
+    gradient g of its output: (g - y (y . g)) / |x| with y = x / |x| where |x| > eps, g / eps where
+    the floor binds (LaCT notes, Eq. (5))."""
+    n = np.sqrt(np.sum(X * X, axis=1, keepdims=True))
+    y = X / np.maximum(n, eps)
+    big = n > eps
+    return np.where(big, (g - y * np.sum(y * g, axis=1, keepdims=True)) / np.where(big, n, 1.0), g / eps)
+
+
+def swiglu_apply_backward(W1, W3, W2, X, dO):
+    """Gradients of sum dO . f_W(X) (LaCT notes, Eq. (3)): returns (dX, dW1, dW3, dW2)."""
+    A, C = X @ W1.T, X @ W3.T
+    s = sigmoid(A)
+    dH = dO @ W2                                   # [n, m]
+    dA = dH * C * s * (1.0 + A * (1.0 - s))        # SiLU'(a) = s (1 + a (1 - s))
+    dC = dH * A * s
+    return dA @ W1 + dC @ W3, dA.T @ X, dC.T @ X, dO.T @ (A * s * C)
+
+
+def chunk_gradients_backward(W1, W3, W2, K, V, eta, G1b, G3b, G2b):
+    """The transpose of chunk_gradients' derivative: given the gradients (G1b, G3b, G2b) of a loss
+    with respect to its outputs (G1, G3, G2), the gradients with respect to its inputs W1, W3, W2,
+    K, V, eta (LaCT notes, Eqs. (2)-(4), differentiated once more).  Returns
+    (dW1, dW3, dW2, dK, dV, deta).
+
+    With A = K W1^T, C = K W3^T, s = sigmoid(A), H = SiLU(A) C, Df = -eta V and E = Df W2, the
+    forward is G2 = Df^T H, G1 = (E C SiLU'(A))^T K, G3 = (E SiLU(A))^T K; every step below is the
+    chain rule through one of these, SiLU''(a) = s (1 - s) (2 + a (1 - 2 s)) included."""
+    A, C = K @ W1.T, K @ W3.T
+    s = sigmoid(A)
+    S0 = A * s                                      # SiLU(a)
+    S1 = s * (1.0 + A * (1.0 - s))                  # SiLU'(a)
+    S2 = s * (1.0 - s) * (2.0 + A * (1.0 - 2.0 * s))  # SiLU''(a)
+    Df = -eta[:, None] * V
+    H = S0 * C
+    E = Df @ W2
+    # G1 = (E C S1)^T K and G3 = (E S0)^T K
+    dDA, dDC = K @ G1b.T, K @ G3b.T                # gradients of E C S1 and of E S0, [n, m]
+    dK = (E * C * S1) @ G1b + (E * S0) @ G3b
+    # G2 = Df^T H
+    dDf = H @ G2b.T                                 # [n, d]
+    dH = Df @ G2b                                   # [n, m]
+    # the elementwise products, back to E, C and A
+    dE = dDA * C * S1 + dDC * S0
+    dC = dDA * E * S1 + dH * S0
+    dA = dDA * E * C * S2 + dDC * E * S1 + dH * C * S1
+    # E = Df W2, A = K W1^T, C = K W3^T, Df = -eta V
+    dDf += dE @ W2.T
+    dW2 = Df.T @ dE
+    dK += dA @ W1 + dC @ W3
+    dW1, dW3 = dA.T @ K, dC.T @ K
+    dV = -eta[:, None] * dDf
+    deta = -np.sum(V * dDf, axis=1)
+    return dW1, dW3, dW2, dK, dV, deta
+
+
+def ttt_backward_scan_ref(q, k, v, eta, W1, W3, W2, chunk, mask, dO, dW_out=None, update_chunks=None,
+                          inner_steps=1, ascent=False, momentum=0.0, rule=UPD_GD, last_layer_only=False):
+    """Gradients of one (batch, head) scan of the TTT-KVB layer (ttt_scan_ref, rule UPD_GD or
+    UPD_GD_L2, all three weights learning unless last_layer_only) for the loss
+    L = sum_t dO_t . o_t + <dW1_out, W1_out> + <dW3_out, W3_out> + <dW2_out, W2_out>.
+
+    The outer-loop gradient (TTT-as-LA, Sec. 6.2) of the chunk recurrence (LaCT notes, section 1.1
+    and Eqs. (2)-(5)), taken in reverse mode: the forward is run once and keeps every step's weights
+    (and, with the norm, every step's W - U); then, from the last step back, the gradient of the
+    weights a step produced goes through the norm's transpose, the step W - U, the momentum
+    M <- beta M + g (starting from zero; the final momentum is outside the loss) and the chunk
+    gradient g (chunk_gradients_backward), and the queries that read a set of weights add the
+    gradient of their outputs (swiglu_apply_backward).  dW_out is None or (dW1, dW3, dW2).
+    Returns (dq, dk, dv, deta, (dW1, dW3, dW2)) with dW the gradients of W1, W3, W2 on entry.
+    """
+    q, k, v, eta, dO = (_f64(x) for x in (q, k, v, eta, dO))
+    if rule not in (UPD_GD, UPD_GD_L2):
+        raise ValueError("the backward covers GD, with or without the L2 norm")
+    N, d = q.shape
+    bounds = chunk_bounds(N, chunk)
+    if mask == MASK_FULL and len(bounds) > 1:
+        raise ValueError("MASK_FULL needs chunk >= N")
+    if mask == MASK_TOKEN_CAUSAL:
+        raise ValueError("MASK_TOKEN_CAUSAL is defined for the linear model only")
+    sign = -1.0 if ascent else 1.0
+    learn = (2,) if last_layer_only else (0, 1, 2)
+    norm = rule == UPD_GD_L2
+    # forward: Ws[t] are the weights before step t; reads[t] the chunks whose queries see Ws[t]
+    W = [_f64(W1).copy(), _f64(W3).copy(), _f64(W2).copy()]
+    M = [np.zeros_like(x) for x in W]
+    Ws, Xs, steps, reads = [], [], [], {}
+    for j, (lo, hi) in enumerate(bounds):
+        update = mask != MASK_STRIDED or bool(update_chunks[j])
+        apply_first = mask in (MASK_APPLY_THEN_UPDATE, MASK_STRIDED)
+        if apply_first:
+            reads.setdefault(len(Ws), []).append(j)
+        if update:
+            for _ in range(max(int(inner_steps), 1)):
+                G = chunk_gradients(W[0], W[1], W[2], k[lo:hi], v[lo:hi], eta[lo:hi])
+                Ws.append([x.copy() for x in W])
+                X = [None, None, None]
+                for i in learn:
+                    M[i] = momentum * M[i] + sign * G[i]
+                    X[i] = W[i] - M[i]
+                    W[i] = l2_normalize_rows(X[i]) if norm else X[i]
+                Xs.append(X)
+                steps.append(j)
+        if not apply_first:
+            reads.setdefault(len(Ws), []).append(j)
+    T = len(Ws)
+    # reverse
+    dq, dk, dv, deta = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v), np.zeros_like(eta)
+    dW = [np.zeros_like(x) for x in W] if dW_out is None else [_f64(x).copy() for x in dW_out]
+    dM = [np.zeros_like(x) for x in W]
+    Wt = W
+    for t in range(T, -1, -1):
+        if t < T:  # step t took Ws[t] to the weights whose gradient dW now holds
+            Wt = Ws[t]
+            lo, hi = bounds[steps[t]]
+            gG = [np.zeros_like(x) for x in W]  # gradient of the chunk gradient g
+            for i in learn:
+                gx = _row_norm_transpose(Xs[t][i], dW[i]) if norm else dW[i]  # gradient of X = W - M
+                dMi = dM[i] - gx                   # M enters X with a minus sign
+                gG[i] = sign * dMi
+                dM[i] = momentum * dMi
+                dW[i] = gx
+            r = chunk_gradients_backward(Wt[0], Wt[1], Wt[2], k[lo:hi], v[lo:hi], eta[lo:hi], *gG)
+            for i in range(3):
+                dW[i] = dW[i] + r[i]
+            dk[lo:hi] += r[3]
+            dv[lo:hi] += r[4]
+            deta[lo:hi] += r[5]
+        for j in reads.get(t, []):  # the queries that read the weights of this point
+            lo, hi = bounds[j]
+            r = swiglu_apply_backward(Wt[0], Wt[1], Wt[2], q[lo:hi], dO[lo:hi])
+            dq[lo:hi] += r[0]
+            for i in range(3):
+                dW[i] = dW[i] + r[1 + i]
+    return dq, dk, dv, deta, tuple(dW)
+
+
+def ttt_backward_ref(q, k, v, eta, W1, W3, W2, chunk, mask, dO, dW_out=None, update_chunks=None, inner_steps=1,
+                     ascent=False, momentum=0.0, rule=UPD_GD, last_layer_only=False, slices=None):
+    """ttt_backward_scan_ref over [B, H, N, d] inputs.  W1, W3, W2 are per head ([H, ...]) or per
+    (batch, head) ([B, H, ...]); the weight gradients take the same shape (per-head weights sum over
+    the batch).  dW_out is None or three [B, H, ...] arrays.  Returns (dq, dk, dv, deta, (dW1, dW3,
+    dW2))."""
+    B, H, N, d = q.shape
+    per_head = W1.ndim == 3
+    dq, dk, dv = np.zeros((B, H, N, d)), np.zeros((B, H, N, d)), np.zeros((B, H, N, d))
+    deta = np.zeros((B, H, N))
+    dW = [np.zeros(x.shape) for x in (W1, W3, W2)]
+    todo = [(b, h) for b in range(B) for h in range(H)] if slices is None else list(slices)
+    for b, h in todo:
+        ws = [x[h] if per_head else x[b, h] for x in (W1, W3, W2)]
+        dwo = None if dW_out is None else tuple(x[b, h] for x in dW_out)
+        r = ttt_backward_scan_ref(q[b, h], k[b, h], v[b, h], eta[b, h], *ws, chunk, mask, dO[b, h], dwo,
+                                  update_chunks, inner_steps, ascent, momentum, rule, last_layer_only)
         dq[b, h], dk[b, h], dv[b, h], deta[b, h] = r[:4]
         for i in range(3):
             if per_head:
