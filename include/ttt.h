@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define TTT_ABI_VERSION 5
+#define TTT_ABI_VERSION 6
 
 typedef enum {
     TTT_OK = 0,
@@ -189,19 +189,35 @@ ttt_status ttt_forward_noalloc(const ttt_desc* desc, const void* q, const void* 
 
 /*
  * Device workspace that ttt_backward needs, in bytes (the size with dW0 requested, which covers a
- * call without it): the io-dtype copies of W1 | W3 and their transposes, phi(q), phi(k), and the
- * factors of phi's backward for both sides, later dA | dC (12 m_h bytes per token and scan in bf16,
- * twice in fp32), the scans' dW2, the partial sums of dW1 | dW3, and the linear-attention
- * backward's workspace over d_k = m_h, d_v = d_h (linattn_backward_workspace_bytes); with
- * TTT_UPD_GD_L2 also W2 after every step of every chunk in fp32, and its row norms.
+ * call without it).  last_layer_only = 1: the io-dtype copies of W1 | W3 and their transposes,
+ * phi(q), phi(k), and the factors of phi's backward for both sides, later dA | dC (12 m_h bytes per
+ * token and scan in bf16, twice in fp32), the scans' dW2, the partial sums of dW1 | dW3, and the
+ * linear-attention backward's workspace over d_k = m_h, d_v = d_h
+ * (linattn_backward_workspace_bytes); with TTT_UPD_GD_L2 also W2 after every step of every chunk in
+ * fp32, and its row norms.  last_layer_only = 0: the forward's own workspace (ttt_workspace_bytes
+ * without Muon), the weights before every update and after the last (fp32, 12 d_h m_h bytes per
+ * scan and update), with TTT_UPD_GD_L2 every update's row norms, the running weight and momentum
+ * gradients, the contraction operands of one update, and per-chunk intermediates (about
+ * 14 m_h io-dtype elements and 12 m_h fp32 scratch bytes per token of one chunk and scan, plus
+ * 3 m_h elements per token of the longest run of chunks that read one set of weights).
  */
 ttt_status ttt_backward_workspace_bytes(const ttt_desc* desc, size_t* bytes);
 
 /*
- * Backward of ttt_forward for the layer whose inner loop trains W2 alone by GD: desc must have
- * last_layer_only = 1, rule TTT_UPD_GD or TTT_UPD_GD_L2, and chunk_rates 0 (else
+ * Backward of ttt_forward for rule TTT_UPD_GD or TTT_UPD_GD_L2 with chunk_rates 0 (else
  * TTT_ERR_UNSUPPORTED); inner_steps, ascent, momentum, the chunked masks and w0_per_batch are as for
- * the forward, and parallel_form is ignored (both forms compute the same layer).  With W1 and W3
+ * the forward.
+ *
+ * last_layer_only = 0 (all three weights learning, parallel_form 0): the reverse of the chunk
+ * recurrence (notes Eqs. (2)-(5), section 1.1): the forward runs again and records the weights
+ * before every update; then, from the last update back, the gradient of an update's output weights
+ * goes through the row norm's transpose, the step W - U, the momentum (M <- momentum M + g, which
+ * starts from zero) and the chunk gradient g = grad_W sum eta L(f_W(k), v), whose own derivative in
+ * W, k, v and eta (SiLU'' included) carries it on; the queries that read a set of weights add the
+ * gradient of their outputs.
+ *
+ * last_layer_only = 1 (the layer whose inner loop trains W2 alone; parallel_form is ignored, both
+ * forms compute the same layer).  With W1 and W3
  * frozen, phi(x) = SiLU(W1 x) * (W3 x) is fixed and W2 is the state of chunked linear attention with
  * queries phi(q), keys phi(k) and values v: each of an updating chunk's max(inner_steps, 1) steps
  * adds u = (ascent ? -1 : 1) * sum eta v phi(k)^T to W2, directly or, with momentum, through
@@ -224,8 +240,10 @@ ttt_status ttt_backward_workspace_bytes(const ttt_desc* desc, size_t* bytes);
  *             (may be NULL when that is 0); TTT_ERR_WORKSPACE if it is too small
  * No output may overlap an input or another output (TTT_ERR_INVALID_ARGUMENT).  Products run in the
  * io dtype with fp32 accumulation (bf16: phi, dA | dC, W1 | W3 and the linear-attention states and
- * state gradients are rounded to bf16 as contraction operands; the states are summed in fp32), and
- * every sum is taken in a fixed order, so results do not depend on scheduling.
+ * state gradients are rounded to bf16 as contraction operands; the states are summed in fp32; with
+ * all weights learning the weights and their gradients are carried in fp32 and rounded to bf16 as
+ * operands, and so are the per-token intermediates), and every sum is taken in a fixed order, so
+ * results do not depend on scheduling.
  */
 ttt_status ttt_backward(const ttt_desc* desc, const void* q, const void* k, const void* v,
                         const float* eta, const float* W0, const void* dO, const float* dW_out,
@@ -331,7 +349,7 @@ ttt_status swa_forward(const swa_desc* desc, const void* q, const void* k, const
  * read, and forgets them.  Kernel classes are numbered 0 .. TTT_PROF_KERNELS-1 and named by
  * ttt_profile_kernel_name.  Enabling or reading while another thread launches is allowed.
  */
-#define TTT_PROF_KERNELS 25
+#define TTT_PROF_KERNELS 31
 ttt_status ttt_profile_enable(int32_t on);
 /* Restricts the bracketing to the kernel classes i whose bit (1u << i) is set in mask; the
  * default is every class.  Each bracket records two events on the launch's stream, which costs

@@ -14,7 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libttt.so")
-SOURCES = ["errors.hip", "profile.hip", "ttt_layer.hip", "ttt_backward.hip", "linattn.hip", "swa.hip"]
+SOURCES = ["errors.hip", "profile.hip", "ttt_layer.hip", "ttt_backward.hip", "ttt_full_bwd.hip", "linattn.hip",
+           "swa.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",

@@ -247,7 +247,8 @@ static BLayout make_blayout(const ttt_desc& D, bool want_dw) {
 static ttt_status validate_bwd(const ttt_desc* D) {
     ttt_status rc = validate_ttt_desc(D);
     if (rc != TTT_OK) return rc;
-    if (!D->last_layer_only || (D->rule != TTT_UPD_GD && D->rule != TTT_UPD_GD_L2) || D->chunk_rates)
+    if (!D->last_layer_only) return validate_full_bwd(D);  // all three weights learning
+    if ((D->rule != TTT_UPD_GD && D->rule != TTT_UPD_GD_L2) || D->chunk_rates)
         return fail(TTT_ERR_UNSUPPORTED,
                     "the backward covers the layer whose inner loop trains W2 alone by GD (with or without momentum "
                     "and the L2 norm): last_layer_only = 1, rule TTT_UPD_GD or TTT_UPD_GD_L2, per-token rates");
@@ -386,7 +387,7 @@ extern "C" ttt_status ttt_backward_workspace_bytes(const ttt_desc* desc, size_t*
     ttt_status rc = validate_bwd(desc);
     if (rc != TTT_OK) return rc;
     if (!bytes) return fail(TTT_ERR_INVALID_ARGUMENT, "bytes is NULL");
-    *bytes = make_blayout(*desc, true).total;
+    *bytes = desc->last_layer_only ? make_blayout(*desc, true).total : full_bwd_ws_bytes(*desc);
     return TTT_OK;
 }
 
@@ -427,17 +428,27 @@ extern "C" ttt_status ttt_backward(const ttt_desc* desc, const void* q, const vo
             if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n))
                 return fail(TTT_ERR_INVALID_ARGUMENT, "%s overlaps %s", outs[i].name, outs[j].name);
     }
-    const BLayout L = make_blayout(D, dW0 != nullptr);
-    if (L.total && (!workspace || workspace_bytes < L.total))
-        return fail(TTT_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
-                    workspace ? workspace_bytes : 0);
-    if (L.total && !aligned(workspace, 256)) return fail(TTT_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    const bool full = !D.last_layer_only;
+    const BLayout L = full ? BLayout{} : make_blayout(D, dW0 != nullptr);
+    const size_t need = full ? full_bwd_ws_bytes(D) : L.total;
+    if (need && (!workspace || workspace_bytes < need))
+        return fail(TTT_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+    if (need && !aligned(workspace, 256)) return fail(TTT_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
     for (const auto& b : ins)
         if ((rc = check_buffer(b.p, b.n, b.name)) != TTT_OK) return rc;
     for (const auto& b : outs)
         if ((rc = check_buffer(b.p, b.n, b.name)) != TTT_OK) return rc;
-    if ((rc = check_buffer(workspace, L.total, "workspace")) != TTT_OK) return rc;
+    if ((rc = check_buffer(workspace, need, "workspace")) != TTT_OK) return rc;
     hipStream_t st = (hipStream_t)stream;
+    if (full) {
+        if (D.io_dtype == TTT_BF16)
+            return run_full_backward<uint16_t>(D, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, eta, W0,
+                                               (const uint16_t*)dO, dW_out, (uint16_t*)dq, (uint16_t*)dk,
+                                               (uint16_t*)dv, deta, dW0, (char*)workspace, st);
+        return run_full_backward<float>(D, (const float*)q, (const float*)k, (const float*)v, eta, W0,
+                                        (const float*)dO, dW_out, (float*)dq, (float*)dk, (float*)dv, deta, dW0,
+                                        (char*)workspace, st);
+    }
     if (D.io_dtype == TTT_BF16)
         return run_backward<uint16_t>(D, L, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, eta, W0,
                                       (const uint16_t*)dO, dW_out, (uint16_t*)dq, (uint16_t*)dk, (uint16_t*)dv, deta,

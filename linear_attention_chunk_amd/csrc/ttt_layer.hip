@@ -298,6 +298,7 @@ template <typename T> struct UpdArgs {
     int d, m, norm, last_only, shadows;
     const float* u_scale;                 // per-chunk rates [scan][nchunk]: W - u_scale[s nchunk + jchunk] U,
     int nchunk, jchunk;                   // or null: W - U
+    float* nrm; int64_t nrm_stride;       // with norm: each normalized row's |W - U| (rows W1, W3, W2), or null
 };
 
 constexpr int kUpdRows = 16;
@@ -321,7 +322,7 @@ template <> struct Vec4<float> {
 // to LDS so that W2^T can be stored 16 consecutive elements at a time.
 template <int NV, typename T>
 __device__ __forceinline__ void update_rows(const float* src, const float* U, float us, float* dst, T* shm, T* tileT,
-                                            int row0, int L, bool norm, bool to_lds, bool shadows) {
+                                            int row0, int L, bool norm, bool to_lds, bool shadows, float* nrm) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int L4 = L / 4;
 #pragma unroll
@@ -347,7 +348,11 @@ __device__ __forceinline__ void update_rows(const float* src, const float* U, fl
         for (int i = 0; i < NV; ++i)
             if (lane + 64 * i < L4) ss += x[i].x * x[i].x + x[i].y * x[i].y + x[i].z * x[i].z + x[i].w * x[i].w;
         float sc = 1.0f;
-        if (norm) sc = 1.0f / fmaxf(sqrtf(wave_sum(ss)), 1e-6f);
+        if (norm) {
+            const float n = sqrtf(wave_sum(ss));
+            sc = 1.0f / fmaxf(n, 1e-6f);
+            if (nrm && lane == 0) nrm[row0 + row] = n;
+        }
         float4* d4 = dst ? reinterpret_cast<float4*>(dst + ro) : nullptr;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
@@ -385,15 +390,16 @@ __global__ __launch_bounds__(kThreads) void k_update(UpdArgs<T> a) {
     T* shm = a.sh + s * a.sh_stride + moff;
     static_assert(kMaxDim <= 8 * 256, "update rows hold at most 8 float4 per lane");
     const float us = a.u_scale ? a.u_scale[(int64_t)s * a.nchunk + a.jchunk] : 1.0f;
+    float* nrm = (a.nrm && norm) ? a.nrm + s * a.nrm_stride + (mat == 0 ? 0 : mat == 1 ? a.m : 2 * a.m) : nullptr;
     switch ((L / 4 + 63) / 64) {  // uniform per workgroup
-        case 1: update_rows<1>(src, U, us, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows); break;
-        case 2: update_rows<2>(src, U, us, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows); break;
-        case 3: update_rows<3>(src, U, us, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows); break;
-        case 4: update_rows<4>(src, U, us, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows); break;
-        case 5: update_rows<5>(src, U, us, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows); break;
-        case 6: update_rows<6>(src, U, us, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows); break;
-        case 7: update_rows<7>(src, U, us, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows); break;
-        default: update_rows<8>(src, U, us, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows); break;
+        case 1: update_rows<1>(src, U, us, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows, nrm); break;
+        case 2: update_rows<2>(src, U, us, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows, nrm); break;
+        case 3: update_rows<3>(src, U, us, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows, nrm); break;
+        case 4: update_rows<4>(src, U, us, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows, nrm); break;
+        case 5: update_rows<5>(src, U, us, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows, nrm); break;
+        case 6: update_rows<6>(src, U, us, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows, nrm); break;
+        case 7: update_rows<7>(src, U, us, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows, nrm); break;
+        default: update_rows<8>(src, U, us, dst, shm, tileT, row0, L, norm, mat == 2, a.shadows, nrm); break;
     }
     if (mat == 2 && a.shadows) {  // W2^T [m][d]: column c of this 16-row block is 16 consecutive elements
         __syncthreads();
@@ -1152,7 +1158,7 @@ static bool has_mom(const ttt_desc& D) { return D.chunk_rates ? D.chunk_momentum
 template <typename T>
 static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const T* k, const T* v,
                           const float* eta, const float* W0, T* o, float* W_out, float* M_inout,
-                          char* ws, hipStream_t st) {
+                          char* ws, hipStream_t st, float* hist = nullptr, float* nrm = nullptr) {
     const int S = D.B * D.H, d = D.d_h, m = D.m_h;
     const int64_t dm = (int64_t)d * m;
     const bool muon = is_muon(D);
@@ -1185,14 +1191,19 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
     int last_upd = -1;
     for (int step = 0; step < nsteps && step < nc; ++step)
         if (D.mask != TTT_MASK_STRIDED || D.update_chunks[step]) last_upd = step;
+    // hist (the backward's record): the weights before update i go to hist + i S 3 d m, the last
+    // update's result after them, and with the norm each update's row norms to nrm + i S (2m + d);
+    // then there is no output (o is null)
+    const int64_t hstride = (int64_t)S * 3 * dm;
+    int ui = 0;  // updates so far
     {  // W0 -> shadows, and the master copy only if no update follows (the first update reads W0)
-        UpdArgs<T> u{W0, 3 * dm, D.w0_per_batch ? 0 : 1, D.H, nullptr, 0, last_upd < 0 ? Wf[0] : nullptr,
+        UpdArgs<T> u{W0, 3 * dm, D.w0_per_batch ? 0 : 1, D.H, nullptr, 0, hist ? hist : last_upd < 0 ? Wf[0] : nullptr,
                      L.wf_stride, sh[0], L.sh_stride, d, m, 0, 0, 1};
         if ((rc = launch_update<T>(u, S * upd_blocks, st)) != TTT_OK) return rc;
     }
-    bool w_in_master = last_upd < 0;  // whether the current W is in Wf[cur], or still only in W0
+    bool w_in_master = hist || last_upd < 0;  // whether the current W is in Wf[cur], or still only in W0
     for (int step = 0; step < nsteps; ++step) {
-        int ja = uta ? step - 1 : step;
+        int ja = o ? (uta ? step - 1 : step) : -1;
         int ju = step < nc ? step : -1;
         if (D.mask == TTT_MASK_STRIDED && ju >= 0 && !D.update_chunks[ju]) ju = -1;
         // an updating chunk takes inner_steps gradient steps, each from the gradient at the current
@@ -1317,6 +1328,13 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
             const bool final_upd = step == last_upd && it == nin - 1;
             UpdArgs<T> u{Wf[cur], L.wf_stride, 0, D.H, U, 3 * dm, Wf[cur ^ 1], L.wf_stride, sh[cur ^ 1], L.sh_stride,
                          d, m, norm, D.last_layer_only, 1, D.chunk_rates ? eta : nullptr, nchunks, ju};
+            if (hist) {
+                u.src = hist + ui * hstride;
+                u.dst = hist + (ui + 1) * hstride;
+                u.nrm = nrm ? nrm + ui * (int64_t)S * (2 * m + d) : nullptr;
+                u.nrm_stride = 2 * m + d;
+            }
+            ++ui;
             if (!w_in_master) {  // the first update reads W0 (per head or per scan)
                 u.src = W0;
                 u.src_stride = 3 * dm;
@@ -1337,6 +1355,21 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
     }
     return TTT_OK;
 }
+
+// The forward recurrence run for its record alone (no output): every update's input weights and,
+// with the norm, its row norms, as described at run_ttt.
+size_t ttt_history_ws_bytes(const ttt_desc& D) { return make_layout(D, false, has_mom(D)).total; }
+
+template <typename T>
+ttt_status ttt_run_history(const ttt_desc& D, const T* q, const T* k, const T* v, const float* eta, const float* W0,
+                           float* hist, float* nrm, char* ws, hipStream_t st) {
+    const Layout L = make_layout(D, false, has_mom(D));
+    return run_ttt<T>(D, L, q, k, v, eta, W0, nullptr, nullptr, nullptr, ws, st, hist, nrm);
+}
+template ttt_status ttt_run_history<uint16_t>(const ttt_desc&, const uint16_t*, const uint16_t*, const uint16_t*,
+                                              const float*, const float*, float*, float*, char*, hipStream_t);
+template ttt_status ttt_run_history<float>(const ttt_desc&, const float*, const float*, const float*, const float*,
+                                           const float*, float*, float*, char*, hipStream_t);
 
 }  // namespace ttt
 

@@ -39,7 +39,7 @@ def test_library_loads_and_exports_every_symbol():
 
 def test_version_and_status_strings():
     L = C.lib()
-    assert L.ttt_abi_version() == 5
+    assert L.ttt_abi_version() == 6
     for s in range(5):
         assert L.ttt_status_string(s)
     assert L.ttt_status_string(99) == b"unknown status"
@@ -295,8 +295,13 @@ def bwd_desc(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(), C.TTT_OK), (dict(mask=C.MASK_UPDATE_THEN_APPLY, inner_steps=3, ascent=1), C.TTT_OK),
     (dict(parallel_form=1, w0_per_batch=1), C.TTT_OK), (dict(N=0), C.TTT_OK),
-    # only the layer whose inner loop trains W2 alone by GD (momentum and the L2 norm allowed)
-    (dict(last_layer_only=0), C.TTT_ERR_UNSUPPORTED), (dict(rule=C.UPD_GD_L2), C.TTT_OK),
+    # the layer whose inner loop trains W2 alone by GD (momentum and the L2 norm allowed), and the
+    # recurrence with all three weights learning by GD or GD + L2 (momentum allowed)
+    (dict(last_layer_only=0), C.TTT_OK), (dict(rule=C.UPD_GD_L2), C.TTT_OK),
+    (dict(last_layer_only=0, rule=C.UPD_GD_L2, momentum=0.9, inner_steps=2, ascent=1), C.TTT_OK),
+    (dict(last_layer_only=0, rule=C.UPD_MUON_L2), C.TTT_ERR_UNSUPPORTED),
+    (dict(last_layer_only=0, chunk_rates=1), C.TTT_ERR_UNSUPPORTED),
+    (dict(last_layer_only=0, parallel_form=1), C.TTT_ERR_INVALID_ARGUMENT),
     (dict(rule=C.UPD_GD_L2, momentum=0.9, inner_steps=3), C.TTT_OK), (dict(rule=C.UPD_MUON_L2), C.TTT_ERR_UNSUPPORTED),
     (dict(rule=C.UPD_MUON), C.TTT_ERR_UNSUPPORTED), (dict(momentum=0.9), C.TTT_OK),
     (dict(chunk_rates=1), C.TTT_ERR_UNSUPPORTED), (dict(mask=C.MASK_TOKEN_CAUSAL), C.TTT_ERR_UNSUPPORTED),
@@ -352,6 +357,39 @@ def test_ttt_backward_workspace_and_rejects():
     assert call(w=ws + 16) == C.TTT_ERR_INVALID_ARGUMENT                            # not 256-aligned
     # no (batch, head): nothing to do, no pointer is touched
     assert L.ttt_backward(ctypes.byref(bwd_desc(B=0)), *([None] * 13), 0, None) == C.TTT_OK
+
+
+def test_full_backward_workspace():
+    """All three weights learning: the forward's workspace (no Muon), the weights before every update
+    and after the last (fp32), the row norms of every update (GD + L2), the running weight gradient,
+    Gamma, the six [m][d] operand blocks, the key tiles' fp32 scratch (3 x 128 x 128 floats per
+    tile), the key chunk's planes (4m + 2m + m), the deta partials, the query range's planes
+    (2m + m) and the weight-gradient parts; momentum adds its gradient, several inner steps the
+    fp32 dk, dv accumulators."""
+    L = C.lib()
+    n = ctypes.c_size_t(0)
+    al = lambda x: (x + 255) // 256 * 256
+    B, H, N, d, m, chunk = 2, 4, 256, 64, 128, 64
+    S, dm = B * H, d * m
+    for rule, mom, steps, mask, flags in ((C.UPD_GD, 0.0, 1, C.MASK_APPLY_THEN_UPDATE, None),
+                                          (C.UPD_GD_L2, 0.9, 2, C.MASK_STRIDED, [0, 0, 1, 1])):
+        arr = None if flags is None else (ctypes.c_uint8 * 4)(*flags)
+        keep = None if arr is None else ctypes.cast(arr, ctypes.c_void_p)
+        D = desc(rule=rule, momentum=mom, inner_steps=steps, mask=mask, update_chunks=keep)
+        st, fwd = ws_bytes(desc(rule=rule, momentum=mom, inner_steps=steps, mask=mask, update_chunks=keep))
+        assert st == C.TTT_OK
+        assert L.ttt_backward_workspace_bytes(ctypes.byref(D), ctypes.byref(n)) == C.TTT_OK
+        T = steps * (4 if flags is None else sum(flags))
+        qcap = chunk if flags is None else 3 * chunk  # strided: chunks 0-2 read the first weights
+        expect = al(fwd) + al((T + 1) * S * 3 * dm * 4) + (al(T * S * (2 * m + d) * 4) if rule == C.UPD_GD_L2 else 0)
+        expect += al(S * 3 * dm * 4) + (al(S * 3 * dm * 4) if mom else 0) + al(S * 3 * dm * 4) + al(S * 6 * dm * 2)
+        expect += al(S * 1 * 3 * 128 * 128 * 4) + al(S * chunk * 4 * m * 2) + al(S * chunk * 2 * m * 2)
+        expect += al(S * chunk * m * 2)
+        if steps > 1:
+            expect += 2 * al(S * chunk * d * 4)
+        expect += al(1 * S * chunk * 4) + al(S * qcap * 2 * m * 2) + al(S * qcap * m * 2)
+        expect += al(1 * S * 3 * dm * 4)  # one part: 16 tiles, and parts under 1024 positions are not taken
+        assert n.value == expect, (rule, mom, steps)
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

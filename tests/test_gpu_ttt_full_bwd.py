@@ -1,0 +1,125 @@
+"""GPU parity of ttt_backward with all three fast weights learning (last_layer_only = 0; GD or
+GD + L2, with or without momentum), through the C ABI, against the fp64 oracle of the recurrence's
+backward.
+
+Tolerances are the forward's: relative L2 <= 1e-5 for fp32 inputs, <= 2e-2 for bf16 inputs, over
+every gradient as a whole, per (batch, head), per chunk of token rows, and 5x that per row."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle as O
+import synth
+import linear_attention_chunk_amd as T
+from gpu_util import assert_close, bulk_ttt_inputs, dev, full_ttt_inputs, host, say
+
+pytestmark = pytest.mark.gpu
+
+TOL = {False: 1e-5, True: 2e-2}
+
+
+def pack(W1, W3, W2):
+    lead = W1.shape[:-2]
+    return np.concatenate([W1.reshape(*lead, -1), W3.reshape(*lead, -1), W2.reshape(*lead, -1)], axis=-1)
+
+
+def split(W, d, m):
+    dm = d * m
+    return W[..., :dm].reshape(*W.shape[:-1], m, d), W[..., dm:2 * dm].reshape(*W.shape[:-1], m, d), \
+        W[..., 2 * dm:].reshape(*W.shape[:-1], d, m)
+
+
+def run(seed, B, H, N, d, m, chunk, mask, bf16, rule=O.UPD_GD_L2, flags=None, inner=1, ascent=False, momentum=0.0,
+        per_batch=False, dW_out=True, want_dW0=True):
+    say(f"full ttt_backward case B{B} H{H} N{N} d{d} m{m} b{chunk} mask{mask} bf16={bf16} rule={rule} flags={flags} "
+        f"inner{inner} ascent{ascent} momentum={momentum} per_batch={per_batch} dW_out={dW_out} want_dW0={want_dW0}")
+    (q, k, v, eta, W0), (hq, hk, hv, he, W1, W3, W2) = full_ttt_inputs(seed, B, H, N, d, m, bf16)
+    if per_batch:
+        Ws = [np.zeros((B, H) + w.shape[1:], np.float32) for w in (W1, W3, W2)]
+        for b in range(B):
+            for h in range(H):
+                for i, w in enumerate(synth.head_weights(seed * 100 + b, h, d, m)):
+                    Ws[i][b, h] = w
+        W1, W3, W2 = Ws
+        W0 = dev(pack(W1, W3, W2))
+    dO, dWo = synth.make_ttt_grads(seed, B, H, N, d, m, bf16)
+    dWo = dWo if dW_out else None
+    dt = torch.bfloat16 if bf16 else torch.float32
+    got = T.ttt_backward(q, k, v, eta, W0, dev(dO, dt), chunk, mask, m_h=m,
+                         dW_out=None if dWo is None else dev(pack(*dWo)), want_dW0=want_dW0, update_chunks=flags,
+                         inner_steps=inner, ascent=ascent, momentum=momentum, update_rule=rule, last_layer_only=False)
+    torch.cuda.synchronize()
+    ref = O.ttt_backward_ref(hq, hk, hv, he, W1, W3, W2, chunk, mask, dO, dWo, flags, inner, ascent, momentum, rule)
+    tol = TOL[bf16]
+    if N == 0:
+        for g, r in zip(got[:4], ref[:4]):
+            assert tuple(g.shape) == r.shape and g.numel() == 0
+    else:
+        for name, g, r in zip(("dq", "dk", "dv"), got[:3], ref[:3]):
+            assert_close(host(g), r, tol, name, chunk)
+        assert_close(host(got[3]), ref[3], tol, "deta")
+    if want_dW0:
+        assert tuple(got[4].shape) == tuple(W0.shape)
+        for name, g, r in zip(("dW1", "dW3", "dW2"), split(host(got[4]), d, m), ref[4]):
+            assert_close(g, r, tol, name)
+    else:
+        assert got[4] is None
+    return got, ref
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("rule", [O.UPD_GD, O.UPD_GD_L2])
+@pytest.mark.parametrize("mask", [O.MASK_APPLY_THEN_UPDATE, O.MASK_UPDATE_THEN_APPLY])
+def test_masks_rules_ragged(mask, rule, bf16):
+    # 3 chunks of 96 and a tail of 20; m = 160 leaves partial hidden-unit tiles, d = 64 a partial
+    # column tile
+    run(1, 1, 2, 308, 64, 160, 96, mask, bf16, rule=rule)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_full_mask(bf16):
+    run(2, 1, 2, 150, 64, 96, 150, O.MASK_FULL, bf16)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("flags,inner,ascent", [([1, 0, 1, 1], 1, False), ([0, 0, 1, 0], 3, True)])
+def test_strided_inner_ascent(flags, inner, ascent, bf16):
+    # chunks that do not update read the weights of the next update (a query range of several
+    # chunks); several inner steps collect dk, dv and deta over the chunk's steps
+    got, _ = run(3, 1, 2, 308, 64, 160, 96, O.MASK_STRIDED, bf16, flags=flags, inner=inner, ascent=ascent)
+    for c, f in enumerate(flags):
+        if not f:
+            assert torch.count_nonzero(got[1][:, :, 96 * c:96 * (c + 1)]).item() == 0
+            assert torch.count_nonzero(got[3][:, :, 96 * c:96 * (c + 1)]).item() == 0
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("mask,rule,inner,mom", [(O.MASK_APPLY_THEN_UPDATE, O.UPD_GD_L2, 1, 0.9),
+                                                 (O.MASK_UPDATE_THEN_APPLY, O.UPD_GD, 2, 0.5)])
+def test_momentum(mask, rule, inner, mom, bf16):
+    run(4, 1, 2, 308, 64, 160, 96, mask, bf16, rule=rule, inner=inner, momentum=mom)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_weight_layouts(bf16):
+    # per-head weights: the gradient sums the batch's scans; per-(batch, head) weights: one each
+    run(5, 3, 2, 260, 64, 128, 128, O.MASK_APPLY_THEN_UPDATE, bf16)
+    run(6, 2, 2, 260, 64, 128, 128, O.MASK_APPLY_THEN_UPDATE, bf16, per_batch=True)
+
+
+def test_wide_heads():
+    # d = 128, m = 384: three hidden-unit tiles, several token tiles per chunk and weight-gradient
+    # token parts
+    run(7, 2, 1, 1100, 128, 384, 512, O.MASK_APPLY_THEN_UPDATE, True)
+    run(8, 1, 2, 700, 128, 384, 256, O.MASK_UPDATE_THEN_APPLY, False, per_batch=True)
+
+
+def test_defaults_and_optional_outputs():
+    run(9, 1, 2, 200, 64, 96, 64, O.MASK_APPLY_THEN_UPDATE, True, dW_out=False)
+    run(9, 1, 2, 200, 64, 96, 64, O.MASK_APPLY_THEN_UPDATE, True, dW_out=False, want_dW0=False)
+
+
+def test_empty_sequence():
+    for pb in (False, True):
+        run(10, 2, 2, 0, 64, 96, 64, O.MASK_APPLY_THEN_UPDATE, True, per_batch=pb)
