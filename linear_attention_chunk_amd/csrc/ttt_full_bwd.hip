@@ -38,6 +38,7 @@ constexpr int kFxCols = 128;   // columns of d per dx tile
 constexpr int kFwTile = 128;   // weight-gradient tiles
 constexpr int kFbRowVec = 8;   // prep: float4 per lane, rows of up to 2048 elements
 constexpr float kFbEps = 1e-6f;
+constexpr int kFbMaxUpdates = 1 << 16;  // updates whose weights the backward records
 
 template <typename T> using FbTQ = Tile<T, kFbRows, kFbCols, 2, 4, 1, 2, 2, false, false, false, kFbWaves>;
 template <typename T> using FbTP = Tile<T, kFbRows, kFbCols, 2, 4, 1, 1, 1, false, false, false, kFbWaves>;
@@ -684,6 +685,9 @@ ttt_status validate_full_bwd(const ttt_desc* D) {
     const int64_t S = (int64_t)D->B * D->H, d = D->d_h, m = D->m_h;
     const int64_t bmax = D->N < D->chunk ? D->N : D->chunk;
     const int64_t lim = 1LL << 31;
+    // every update keeps a copy of the weights: the count is bounded before anything is planned
+    if ((D->N > 0 ? cdiv(D->N, D->chunk) : 0) * std::max(1, D->inner_steps) > kFbMaxUpdates)
+        return fail(TTT_ERR_UNSUPPORTED, "the backward records at most %d updates (chunks x inner steps)", kFbMaxUpdates);
     // launch sizes (the query range may span every chunk)
     if (S * (cdiv(bmax, kFbRows) + cdiv(D->N, kFbRows)) * cdiv(m, kFbCols) >= lim ||
         S * (2 * cdiv(bmax, kFxRows) + cdiv(D->N, kFxRows)) * cdiv(d, kFxCols) >= lim ||

@@ -14,7 +14,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "linear_attention_chunk_amd", "csrc")
-SOURCES = ["errors.hip", "profile.hip", "ttt_layer.hip", "ttt_backward.hip", "linattn.hip", "swa.hip"]
+SOURCES = ["errors.hip", "profile.hip", "ttt_layer.hip", "ttt_backward.hip", "ttt_full_bwd.hip", "linattn.hip",
+           "swa.hip"]
 
 
 def _hipcc():
