@@ -574,7 +574,36 @@ def main():
             "mfma_frac": round(gflops / (msg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
             "over_parallel_forward": round(msg / msp[True], 2),
             "training_step_ms": round(msg + msp[True], 3), "kernels_ms": gk}
-        del dOl, wsg
+        # the headline layer's backward (all three weights learning, GD + L2): the forward again for its
+        # record, then the reverse of the chunk recurrence
+        print("[bench] extras: GD + L2 backward, all weights learning", file=sys.stderr, flush=True)
+        Df, _ = T.ttt_desc(B, H, N, d, m, chunk, C.TTT_BF16, C.MASK_APPLY_THEN_UPDATE, C.UPD_GD_L2, 0, 0.0)
+        wsf = torch.empty(T.ttt_backward_workspace_bytes(Df), dtype=torch.uint8, device="cuda")
+        fbwd = lambda: T.ttt_backward(q, k, v, eta, W0, dOl, chunk, C.MASK_APPLY_THEN_UPDATE, m_h=m,  # noqa: E731
+                                      update_rule=C.UPD_GD_L2, last_layer_only=False, workspace=wsf)
+        msf = time_calls(torch, fbwd, st, 1)
+        C.profile_select(None)
+        C.profile_enable(True)
+        C.profile_read()
+        for _ in range(3):
+            fbwd()
+        torch.cuda.synchronize()
+        fk = {kn: round(t / 3, 4) for kn, (t, n) in C.profile_read().items() if n}
+        C.profile_enable(False)
+        # algorithmic flops per token and scan: the forward again without outputs (a, c and v W2 of the
+        # keys, the three chunk gradients: 12 d m), then the key tiles' two passes (12 d m), the query
+        # tiles (6 d m), dk (8 d m), dv (4 d m), dq (4 d m) and the weight gradients over keys and
+        # queries (12 d m)
+        fflops = tokens * H * 58 * d * m
+        extras["lact_lm_gd_l2_backward"] = {
+            "workload": f"B{B} H{H} N{N} d{d} m{m} chunk {chunk} bf16, apply-then-update, GD + L2 with all three "
+                        "weights learning: gradients of q, k, v, eta and the per-head W0 from dO",
+            "ms_per_call": round(msf, 3), "tokens_per_s": round(tokens / (msf * 1e-3)),
+            "algorithmic_tflop": round(fflops / 1e12, 3),
+            "mfma_frac": round(fflops / (msf * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "over_forward": round(msf / ms, 2), "training_step_ms": round(msf + ms, 3),
+            "workspace_GB": round(wsf.numel() / 1e9, 2), "kernels_ms": fk}
+        del dOl, wsg, wsf
         # Variant 2 of the paper's ablation: only W2 learns, momentum 0.9, per-token eta and Muon (5
         # Newton-Schulz steps) kept, no weight norm; chunk recurrence against the parallel form
         print("[bench] extras: Variant 2 (last layer, Muon + momentum), recurrence and parallel form",

@@ -158,13 +158,56 @@ __global__ __launch_bounds__(kThreads) void k_fb_ops(FbOpsArgs<T> a) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// A key tile's first-pass values A, C, P, kept for the second pass's epilogue.  bf16 operands: in
+// registers, rounded to bf16 (two values per register; the planes the epilogue writes are bf16
+// too).  fp32 operands: in a per-thread fp32 scratch, element idx's value j at ((idx * 3 + j) * NT +
+// thread), written and read by the same thread.
+template <typename T, int E, int NT> struct KeyKeep;
+template <int E, int NT> struct KeyKeep<uint16_t, E, NT> {
+    uint32_t ac[E], pp[E / 2];
+    __device__ __forceinline__ void begin(float*) {}
+    __device__ __forceinline__ void put(int idx, float x, float c, float p) {
+        ac[idx] = (uint32_t)f2bf(x) | ((uint32_t)f2bf(c) << 16);
+        const uint32_t h = f2bf(p);
+        pp[idx / 2] = (idx & 1) ? (pp[idx / 2] & 0xFFFFu) | (h << 16) : h;
+    }
+    __device__ __forceinline__ void reopen() {}
+    __device__ __forceinline__ void get(int idx, float& x, float& c, float& p) const {
+        x = __uint_as_float(ac[idx] << 16);
+        c = __uint_as_float(ac[idx] & 0xFFFF0000u);
+        p = __uint_as_float((idx & 1) ? (pp[idx / 2] & 0xFFFF0000u) : (pp[idx / 2] << 16));
+    }
+};
+template <int E, int NT> struct KeyKeep<float, E, NT> {
+    float* sc;
+    const float* sr;
+    __device__ __forceinline__ void begin(float* base) { sc = base + threadIdx.x; }
+    __device__ __forceinline__ void put(int idx, float x, float c, float p) {
+        sc[(idx * 3 + 0) * NT] = x;
+        sc[(idx * 3 + 1) * NT] = c;
+        sc[(idx * 3 + 2) * NT] = p;
+    }
+    // the epilogue forms its addresses afresh: the pointer is laundered, so that the first pass's
+    // 3 E store addresses are not kept live through the second pass
+    __device__ __forceinline__ void reopen() {
+        sr = sc;
+        asm volatile("" : "+v"(sr));
+    }
+    __device__ __forceinline__ void get(int idx, float& x, float& c, float& p) const {
+        x = sr[(idx * 3 + 0) * NT];
+        c = sr[(idx * 3 + 1) * NT];
+        p = sr[(idx * 3 + 2) * NT];
+    }
+};
+
+// ---------------------------------------------------------------------------------------------
 // up: query tiles and key tiles of one version (token rows x hidden units).  Planes are token-major
 // rows of the version's query range (qa: dA | dC, qh: H) or key chunk (pk: DA | DC | dA | dC,
 // pv: H | dE, pe: -e dE).
 template <typename T> struct FbUpArgs {
     const T* q; const T* k; const T* v; const T* dO; const float* eta;
     const T* op;          // [S][6dm]
-    float* acp;           // key tiles' pass-1 values, per tile 3 x 256 x 128 floats
+    float* acp;           // fp32 operands: the key tiles' first-pass values, 3 x 128 x 128 floats per tile
     T* qa; T* qh;         // [S][qcap][2m], [S][qcap][m]
     T* pk; T* pv; T* pe;  // [S][bcap][4m], [S][bcap][2m], [S][bcap][m]
     int64_t N, qcap, bcap; int d, m;
@@ -207,14 +250,12 @@ __global__ __launch_bounds__(64 * kFbWaves, 1) void k_fb_up(FbUpArgs<T> a) {
             tl.template run<PMQ>(AK, B1, a.d, smem);
             tp.template run<PM1>(AV, B2, a.d, smem);
         }
-        // A, C, P: element idx, value j at ((idx * 3 + j) * NT + thread), read back by the same thread
-        float* sc = a.acp + ((int64_t)s * a.nK + t) * (3 * TQ::ELEMS * TQ::NT) + threadIdx.x;
+        KeyKeep<T, TQ::ELEMS, TQ::NT> keep;
+        keep.begin(a.acp ? a.acp + ((int64_t)s * a.nK + t) * (3 * TQ::ELEMS * TQ::NT) : nullptr);
         TQ::for_each_pos([&](int idx, int, int) {
             int i, j, r;
             at(idx, i, j, r);
-            sc[(idx * 3 + 0) * TQ::NT] = tl.acc[0][i][j][r];
-            sc[(idx * 3 + 1) * TQ::NT] = tl.acc[1][i][j][r];
-            sc[(idx * 3 + 2) * TQ::NT] = tp.acc[0][i][j][r];
+            keep.put(idx, tl.acc[0][i][j][r], tl.acc[1][i][j][r], tp.acc[0][i][j][r]);
         });
         {
             const Opnd<T> B1[2] = {{blk(0, c0), a.d, m - c0, a.d}, {blk(1, c0), a.d, m - c0, a.d}};
@@ -222,10 +263,7 @@ __global__ __launch_bounds__(64 * kFbWaves, 1) void k_fb_up(FbUpArgs<T> a) {
             tl.template run<PMQ>(AK, B1, a.d, smem);
             tp.template run<PM1>(AV, B2, a.d, smem);
         }
-        // the epilogue forms its scratch addresses afresh: the pointer is laundered, so that the
-        // first pass's 96 store addresses are not kept live through the second pass
-        const float* sr = sc;
-        asm volatile("" : "+v"(sr));
+        keep.reopen();
         const float* eta = a.eta + tok;
         const int64_t prow = (int64_t)s * a.bcap + r0;
         T* PK = a.pk + prow * 4 * m + c0;
@@ -236,8 +274,8 @@ __global__ __launch_bounds__(64 * kFbWaves, 1) void k_fb_up(FbUpArgs<T> a) {
                 if (!decltype(check)::value || (row < rows && c0 + col < m)) {
                     int i, j, r;
                     at(idx, i, j, r);
-                    const float x = sr[(idx * 3 + 0) * TQ::NT], c = sr[(idx * 3 + 1) * TQ::NT];
-                    const float p = sr[(idx * 3 + 2) * TQ::NT];
+                    float x, c, p;
+                    keep.get(idx, x, c, p);
                     const float p1 = tl.acc[0][i][j][r], p3 = tl.acc[1][i][j][r], rr = tp.acc[0][i][j][r];
                     const float e = a.sign * eta[row];
                     const float sg = sigmoidf_(x), s0 = x * sg, s1 = sg * (1.f + x * (1.f - sg));
@@ -655,7 +693,7 @@ static FLayout make_flayout(const ttt_desc& D, const FbPlan& P) {
     L.G = take((size_t)S * 3 * dm * 4);
     L.op = take((size_t)S * 6 * dm * es);
     if (P.T > 0) {
-        L.acp = take((size_t)S * L.nK * 3 * FbTQ<float>::ELEMS * FbTQ<float>::NT * 4);
+        if (es == 4) L.acp = take((size_t)S * L.nK * 3 * FbTQ<float>::ELEMS * FbTQ<float>::NT * 4);
         L.pk = take((size_t)S * L.bcap * 4 * m * es);
         L.pv = take((size_t)S * L.bcap * 2 * m * es);
         L.pe = take((size_t)S * L.bcap * m * es);

@@ -362,10 +362,10 @@ def test_ttt_backward_workspace_and_rejects():
 def test_full_backward_workspace():
     """All three weights learning: the forward's workspace (no Muon), the weights before every update
     and after the last (fp32), the row norms of every update (GD + L2), the running weight gradient,
-    Gamma, the six [m][d] operand blocks, the key tiles' fp32 scratch (3 x 128 x 128 floats per
-    tile), the key chunk's planes (4m + 2m + m), the deta partials, the query range's planes
-    (2m + m) and the weight-gradient parts; momentum adds its gradient, several inner steps the
-    fp32 dk, dv accumulators."""
+    Gamma, the six [m][d] operand blocks, the key chunk's planes (4m + 2m + m), the deta partials,
+    the query range's planes (2m + m) and the weight-gradient parts; momentum adds its gradient,
+    several inner steps the fp32 dk, dv accumulators, fp32 operands a scratch of 3 x 128 x 128
+    floats per key tile."""
     L = C.lib()
     n = ctypes.c_size_t(0)
     al = lambda x: (x + 255) // 256 * 256
@@ -383,7 +383,7 @@ def test_full_backward_workspace():
         qcap = chunk if flags is None else 3 * chunk  # strided: chunks 0-2 read the first weights
         expect = al(fwd) + al((T + 1) * S * 3 * dm * 4) + (al(T * S * (2 * m + d) * 4) if rule == C.UPD_GD_L2 else 0)
         expect += al(S * 3 * dm * 4) + (al(S * 3 * dm * 4) if mom else 0) + al(S * 3 * dm * 4) + al(S * 6 * dm * 2)
-        expect += al(S * 1 * 3 * 128 * 128 * 4) + al(S * chunk * 4 * m * 2) + al(S * chunk * 2 * m * 2)
+        expect += al(S * chunk * 4 * m * 2) + al(S * chunk * 2 * m * 2)  # (bf16: no first-pass scratch)
         expect += al(S * chunk * m * 2)
         if steps > 1:
             expect += 2 * al(S * chunk * d * 4)

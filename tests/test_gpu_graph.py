@@ -119,6 +119,19 @@ def test_linear_attention_and_backwards_replay():
         C.check(st)
 
     replay_matches_eager("ttt_backward", tbwd, touts)
+    # the backward with all three weights learning (GD + L2, momentum), dW_out given
+    Df, _ = T.ttt_desc(1, 2, 308, 64, 160, 96, C.TTT_BF16, O.MASK_APPLY_THEN_UPDATE, C.UPD_GD_L2, 0, 0.9)
+    wsf = torch.empty(max(1, T.ttt_backward_workspace_bytes(Df)), dtype=torch.uint8, device="cuda")
+    dWo = 0.1 * torch.randn((1, 2, W0.shape[-1]), device="cuda")
+    fouts = [torch.empty_like(qt) for _ in range(3)] + [torch.empty_like(et), torch.empty_like(W0)]
+
+    def fbwd():
+        st = C.lib().ttt_backward(A.ctypes.byref(Df), *[A._ptr(x) for x in (qt, kt, vt, et, W0, dOt, dWo)],
+                                  *[A._ptr(x) for x in fouts], A._ptr(wsf), A.ctypes.c_size_t(wsf.numel()),
+                                  A._stream_handle(None))
+        C.check(st)
+
+    replay_matches_eager("ttt_backward, all weights", fbwd, fouts)
     # sliding-window attention
     Ds = C.SwaDesc(1, 2, 308, 64, 96, C.TTT_BF16)
     wss = torch.empty(max(1, T.swa_workspace_bytes(Ds)), dtype=torch.uint8, device="cuda")

@@ -123,3 +123,40 @@ def test_defaults_and_optional_outputs():
 def test_empty_sequence():
     for pb in (False, True):
         run(10, 2, 2, 0, 64, 96, 64, O.MASK_APPLY_THEN_UPDATE, True, per_batch=pb)
+
+
+def test_full_size_sampled():
+    # the LaCT-LLM layer's shape (B=8, H=4, N=32768, d=384, m=768, chunk 2048, bf16, GD + L2) with
+    # per-(batch, head) weights; two slices come from the seeded generator and are compared with the
+    # oracle (their weight-gradient blocks included), the others are filled on the device
+    B, H, N, d, m, chunk = 8, 4, 32768, 384, 768, 2048
+    say(f"full ttt_backward full-size case B{B} H{H} N{N} d{d} m{m} b{chunk}")
+    picks = [(0, 0), (7, 3)]
+    q, k, v, eta, W0h, ex, Wh = bulk_ttt_inputs(12, B, H, N, d, m, True, exact=picks)
+    W0 = W0h[None].expand(B, H, -1).contiguous()
+    g = torch.Generator(device="cuda")
+    g.manual_seed(778)
+    dO = (torch.randn((B, H, N, d), generator=g, device="cuda") / np.sqrt(d)).to(torch.bfloat16)
+    dWo = torch.randn((B, H, 3 * d * m), generator=g, device="cuda") / np.sqrt(d)
+    hg = {}
+    for (b, h) in picks:
+        dos, dws = synth.layer_grad_slice(12, b, h, N, d, m, True)
+        dO[b, h] = dev(dos, torch.bfloat16)
+        dWo[b, h] = dev(pack(*dws))
+        hg[(b, h)] = (dos, dws)
+    got = T.ttt_backward(q, k, v, eta, W0, dO, chunk, O.MASK_APPLY_THEN_UPDATE, m_h=m, dW_out=dWo,
+                         update_rule=O.UPD_GD_L2, last_layer_only=False)
+    torch.cuda.synchronize()
+    for (b, h) in picks:
+        qs, ks, vs, es = ex[(b, h)]
+        dos, dws = hg[(b, h)]
+        say(f"  oracle slice ({b}, {h})")
+        ref = O.ttt_backward_scan_ref(qs, ks, vs, es, Wh[0][h], Wh[1][h], Wh[2][h], chunk, O.MASK_APPLY_THEN_UPDATE,
+                                      dos, dws, rule=O.UPD_GD_L2)
+        for name, gg, r in zip(("dq", "dk", "dv"), got[:3], ref[:3]):
+            assert_close(host(gg[b, h]), r, TOL[True], f"{name}[{b},{h}]", chunk)
+        assert_close(host(got[3][b, h])[None], ref[3][None], TOL[True], f"deta[{b},{h}]")
+        for name, gg, r in zip(("dW1", "dW3", "dW2"), split(host(got[4][b, h]), d, m), ref[4]):
+            assert_close(gg, r, TOL[True], f"{name}[{b},{h}]")
+    for t in got:
+        assert torch.isfinite(t).all()
