@@ -13,4 +13,5 @@ from .ttt_ref import (  # noqa: F401
     linattn_backward_scan_ref, linattn_backward_ref,
     ttt_lastlayer_backward_scan_ref, ttt_lastlayer_backward_ref,
     swiglu_apply_backward, chunk_gradients_backward, ttt_backward_scan_ref, ttt_backward_ref,
+    newton_schulz_backward,
 )

@@ -28,10 +28,11 @@ Training"):
 * the backward of the layer with frozen W1, W3 (last layer only, GD, momentum, the L2 norm):
   the state's recurrence transposed over phi(q), phi(k), then phi's chain rule  TTT-as-LA, Thm. 5.2-5.3,
                                                                    Sec. 6.1-6.2
-* the backward of the chunk recurrence with all three weights learning (GD, GD + L2, momentum):
-  reverse mode over the steps, each through the norm's transpose, W - U, the momentum and the
-  chunk gradient differentiated once more (SiLU'' included) .... TTT-as-LA, Sec. 6.2; LaCT notes,
-                                                                   Eqs. (2)-(5) and section 1.1
+* the backward of the chunk recurrence (every rule, momentum, all three weights learning or W2
+  alone): reverse mode over the steps, each through the norm's transpose, W - U or W - Muon(U)
+  (Newton-Schulz walked back), the momentum and the chunk gradient differentiated once more
+  (SiLU'' included) ................................................ TTT-as-LA, Sec. 6.2; LaCT notes,
+                                                                   Eqs. (2)-(6) and section 1.1
 * gradient ascent in the inner loop: the step's sign flips ....... TTT-as-LA, Sec. 4.2 and 5.2
 * per-chunk rates outside the optimizer step: momentum dW_j = g_j + alpha_j dW_{j-1} over the
   chunk gradient g_j (unit token weights), W <- W - eta_j Opt(dW_j) .. TTT-as-LA, App. E.1 (per token)
@@ -533,6 +534,30 @@ def _row_norm_transpose(X, g, eps=ROW_NORM_EPS):
     return np.where(big, (g - y * np.sum(y * g, axis=1, keepdims=True)) / np.where(big, n, 1.0), g / eps)
 
 
+def newton_schulz_backward(U, iters, G, eps=NS_EPS):
+    """The gradient with respect to U of <G, newton_schulz(U, iters)> (LaCT notes, Eq. (6)): the
+    iteration run again, then walked back.  One cubic step X' = 1.5 X - 0.5 (X X^T) X takes a
+    gradient G of X' to 1.5 G - 0.5 [(G X^T + X G^T) X + (X X^T) G]; the start X0 = U / (|U| + eps)
+    takes G to G / (|U| + eps) - <G, U> U / ((|U| + eps)^2 |U|) (the second term is absent at U = 0).
+    A U with more rows than columns is handled transposed, as the forward does."""
+    U, G = _f64(U), _f64(G)
+    tr = U.shape[0] > U.shape[1]
+    X = U.T if tr else U
+    G = G.T if tr else G
+    n = np.sqrt(np.sum(X * X))
+    Xs = [X / (n + eps)]
+    for _ in range(iters):
+        Xk = Xs[-1]
+        Xs.append(1.5 * Xk - 0.5 * ((Xk @ Xk.T) @ Xk))
+    for k in range(iters - 1, -1, -1):
+        Xk = Xs[k]
+        G = 1.5 * G - 0.5 * ((G @ Xk.T + Xk @ G.T) @ Xk + (Xk @ Xk.T) @ G)
+    dX = G / (n + eps)
+    if n > 0:
+        dX = dX - (np.sum(G * X) / ((n + eps) ** 2 * n)) * X
+    return dX.T if tr else dX
+
+
 def swiglu_apply_backward(W1, W3, W2, X, dO):
     """Gradients of sum dO . f_W(X) (LaCT notes, Eq. (3)): returns (dX, dW1, dW3, dW2)."""
     A, C = X @ W1.T, X @ W3.T
@@ -581,23 +606,24 @@ def chunk_gradients_backward(W1, W3, W2, K, V, eta, G1b, G3b, G2b):
 
 
 def ttt_backward_scan_ref(q, k, v, eta, W1, W3, W2, chunk, mask, dO, dW_out=None, update_chunks=None,
-                          inner_steps=1, ascent=False, momentum=0.0, rule=UPD_GD, last_layer_only=False):
-    """Gradients of one (batch, head) scan of the TTT-KVB layer (ttt_scan_ref, rule UPD_GD or
-    UPD_GD_L2, all three weights learning unless last_layer_only) for the loss
+                          inner_steps=1, ascent=False, momentum=0.0, rule=UPD_GD, last_layer_only=False, ns_iters=5):
+    """Gradients of one (batch, head) scan of the TTT-KVB layer (ttt_scan_ref with any of the four
+    rules, all three weights learning unless last_layer_only) for the loss
     L = sum_t dO_t . o_t + <dW1_out, W1_out> + <dW3_out, W3_out> + <dW2_out, W2_out>.
 
     The outer-loop gradient (TTT-as-LA, Sec. 6.2) of the chunk recurrence (LaCT notes, section 1.1
     and Eqs. (2)-(5)), taken in reverse mode: the forward is run once and keeps every step's weights
     (and, with the norm, every step's W - U); then, from the last step back, the gradient of the
-    weights a step produced goes through the norm's transpose, the step W - U, the momentum
-    M <- beta M + g (starting from zero; the final momentum is outside the loss) and the chunk
-    gradient g (chunk_gradients_backward), and the queries that read a set of weights add the
-    gradient of their outputs (swiglu_apply_backward).  dW_out is None or (dW1, dW3, dW2).
+    weights a step produced goes through the norm's transpose, the step W - U (W - Muon(U) with
+    newton_schulz_backward), the momentum M <- beta M + g (starting from zero; the final momentum is
+    outside the loss) and the chunk gradient g (chunk_gradients_backward), and the queries that read
+    a set of weights add the gradient of their outputs (swiglu_apply_backward).  dW_out is None or
+    (dW1, dW3, dW2).
     Returns (dq, dk, dv, deta, (dW1, dW3, dW2)) with dW the gradients of W1, W3, W2 on entry.
     """
     q, k, v, eta, dO = (_f64(x) for x in (q, k, v, eta, dO))
-    if rule not in (UPD_GD, UPD_GD_L2):
-        raise ValueError("the backward covers GD, with or without the L2 norm")
+    if rule not in (UPD_GD, UPD_GD_L2, UPD_MUON_L2, UPD_MUON):
+        raise ValueError("unknown update rule")
     N, d = q.shape
     bounds = chunk_bounds(N, chunk)
     if mask == MASK_FULL and len(bounds) > 1:
@@ -606,11 +632,12 @@ def ttt_backward_scan_ref(q, k, v, eta, W1, W3, W2, chunk, mask, dO, dW_out=None
         raise ValueError("MASK_TOKEN_CAUSAL is defined for the linear model only")
     sign = -1.0 if ascent else 1.0
     learn = (2,) if last_layer_only else (0, 1, 2)
-    norm = rule == UPD_GD_L2
+    norm = rule in (UPD_GD_L2, UPD_MUON_L2)
+    muon = rule in (UPD_MUON_L2, UPD_MUON)
     # forward: Ws[t] are the weights before step t; reads[t] the chunks whose queries see Ws[t]
     W = [_f64(W1).copy(), _f64(W3).copy(), _f64(W2).copy()]
     M = [np.zeros_like(x) for x in W]
-    Ws, Xs, steps, reads = [], [], [], {}
+    Ws, Xs, Us, steps, reads = [], [], [], [], {}
     for j, (lo, hi) in enumerate(bounds):
         update = mask != MASK_STRIDED or bool(update_chunks[j])
         apply_first = mask in (MASK_APPLY_THEN_UPDATE, MASK_STRIDED)
@@ -620,12 +647,14 @@ def ttt_backward_scan_ref(q, k, v, eta, W1, W3, W2, chunk, mask, dO, dW_out=None
             for _ in range(max(int(inner_steps), 1)):
                 G = chunk_gradients(W[0], W[1], W[2], k[lo:hi], v[lo:hi], eta[lo:hi])
                 Ws.append([x.copy() for x in W])
-                X = [None, None, None]
+                X, Ui = [None, None, None], [None, None, None]
                 for i in learn:
                     M[i] = momentum * M[i] + sign * G[i]
-                    X[i] = W[i] - M[i]
+                    Ui[i] = M[i].copy()
+                    X[i] = W[i] - (newton_schulz(M[i], ns_iters) if muon else M[i])
                     W[i] = l2_normalize_rows(X[i]) if norm else X[i]
                 Xs.append(X)
+                Us.append(Ui)
                 steps.append(j)
         if not apply_first:
             reads.setdefault(len(Ws), []).append(j)
@@ -641,8 +670,9 @@ def ttt_backward_scan_ref(q, k, v, eta, W1, W3, W2, chunk, mask, dO, dW_out=None
             lo, hi = bounds[steps[t]]
             gG = [np.zeros_like(x) for x in W]  # gradient of the chunk gradient g
             for i in learn:
-                gx = _row_norm_transpose(Xs[t][i], dW[i]) if norm else dW[i]  # gradient of X = W - M
-                dMi = dM[i] - gx                   # M enters X with a minus sign
+                gx = _row_norm_transpose(Xs[t][i], dW[i]) if norm else dW[i]  # gradient of X = W - Opt(M)
+                # M enters X with a minus sign, through Muon when the rule has it
+                dMi = dM[i] + (newton_schulz_backward(Us[t][i], ns_iters, -gx) if muon else -gx)
                 gG[i] = sign * dMi
                 dM[i] = momentum * dMi
                 dW[i] = gx
@@ -662,7 +692,7 @@ def ttt_backward_scan_ref(q, k, v, eta, W1, W3, W2, chunk, mask, dO, dW_out=None
 
 
 def ttt_backward_ref(q, k, v, eta, W1, W3, W2, chunk, mask, dO, dW_out=None, update_chunks=None, inner_steps=1,
-                     ascent=False, momentum=0.0, rule=UPD_GD, last_layer_only=False, slices=None):
+                     ascent=False, momentum=0.0, rule=UPD_GD, last_layer_only=False, slices=None, ns_iters=5):
     """ttt_backward_scan_ref over [B, H, N, d] inputs.  W1, W3, W2 are per head ([H, ...]) or per
     (batch, head) ([B, H, ...]); the weight gradients take the same shape (per-head weights sum over
     the batch).  dW_out is None or three [B, H, ...] arrays.  Returns (dq, dk, dv, deta, (dW1, dW3,
@@ -677,7 +707,7 @@ def ttt_backward_ref(q, k, v, eta, W1, W3, W2, chunk, mask, dO, dW_out=None, upd
         ws = [x[h] if per_head else x[b, h] for x in (W1, W3, W2)]
         dwo = None if dW_out is None else tuple(x[b, h] for x in dW_out)
         r = ttt_backward_scan_ref(q[b, h], k[b, h], v[b, h], eta[b, h], *ws, chunk, mask, dO[b, h], dwo,
-                                  update_chunks, inner_steps, ascent, momentum, rule, last_layer_only)
+                                  update_chunks, inner_steps, ascent, momentum, rule, last_layer_only, ns_iters)
         dq[b, h], dk[b, h], dv[b, h], deta[b, h] = r[:4]
         for i in range(3):
             if per_head:

@@ -1,5 +1,5 @@
-"""Pins of the backward of the TTT-KVB chunk recurrence with all three weights learning (GD and
-GD + L2, with and without momentum), CPU only.
+"""Pins of the backward of the TTT-KVB chunk recurrence (GD, GD + L2, Muon with and without the
+norm, with and without momentum; all three weights learning or W2 alone), CPU only.
 
 Each pin takes a route other than the chain rule the oracle writes out: central finite differences
 through the forward recurrence (ttt_scan_ref), torch's float64 autograd through a recurrence written
@@ -65,6 +65,21 @@ def test_chunk_gradients_backward_matches_finite_differences():
         assert rel(g, r) < 1e-8, i
 
 
+@pytest.mark.parametrize("shape", [(3, 5), (6, 4), (4, 4)])
+def test_newton_schulz_backward_matches_finite_differences(shape):
+    # wide, tall (run transposed) and square matrices through five cubic steps and the start's scaling
+    rng = np.random.default_rng(7 + shape[0])
+    U = rng.standard_normal(shape)
+    G = rng.standard_normal(shape)
+    got = O.newton_schulz_backward(U, 5, G)
+    fd = fd_grads([U], lambda a: float(np.sum(G * O.newton_schulz(a[0], 5))))[0]
+    assert rel(got, fd) < 1e-7
+    # zero steps: only the scaling U / (|U| + eps)
+    got0 = O.newton_schulz_backward(U, 0, G)
+    fd0 = fd_grads([U], lambda a: float(np.sum(G * O.newton_schulz(a[0], 0))))[0]
+    assert rel(got0, fd0) < 1e-7
+
+
 def loss(a, chunk, mask, dO, dWo, upd, steps, ascent, beta, rule, last):
     o, W, _ = O.ttt_scan_ref(*a, chunk, mask, rule, momentum=beta, last_layer_only=last, update_chunks=upd,
                              inner_steps=steps, ascent=ascent)
@@ -85,13 +100,30 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("mask,chunk,upd,steps,ascent,beta,rule", CASES)
-def test_backward_matches_finite_differences(mask, chunk, upd, steps, ascent, beta, rule):
+# Muon (five Newton-Schulz steps on the momentum or the gradient), with and without the norm, all
+# three weights learning (last = False) or W2 alone
+CASES_MUON = [
+    (O.MASK_APPLY_THEN_UPDATE, 3, None, 1, False, 0.0, O.UPD_MUON_L2, False),
+    (O.MASK_UPDATE_THEN_APPLY, 4, None, 2, True, 0.9, O.UPD_MUON_L2, False),
+    (O.MASK_STRIDED, 2, [0, 1, 1, 0, 1], 1, False, 0.5, O.UPD_MUON, False),
+    (O.MASK_FULL, 9, None, 1, False, 0.0, O.UPD_MUON, False),
+    (O.MASK_APPLY_THEN_UPDATE, 2, None, 2, False, 0.9, O.UPD_MUON_L2, True),
+    (O.MASK_UPDATE_THEN_APPLY, 3, None, 1, True, 0.0, O.UPD_MUON, True),
+]
+
+
+@pytest.mark.parametrize("mask,chunk,upd,steps,ascent,beta,rule,last",
+                         [c + (False,) for c in CASES] + CASES_MUON)
+def test_backward_matches_finite_differences(mask, chunk, upd, steps, ascent, beta, rule, last):
+    # Muon's output has unit scale whatever the gradient's, so its cases take small eta too
     args, dO, dWo = problem(30 + mask + 7 * steps + rule, scale=0.3 if rule == O.UPD_GD_L2 else 0.03)
-    got = O.ttt_backward_scan_ref(*args, chunk, mask, dO, dWo, upd, steps, ascent, beta, rule)
-    fd = fd_grads(args, lambda a: loss(a, chunk, mask, dO, dWo, upd, steps, ascent, beta, rule, False))
+    got = O.ttt_backward_scan_ref(*args, chunk, mask, dO, dWo, upd, steps, ascent, beta, rule, last)
+    fd = fd_grads(args, lambda a: loss(a, chunk, mask, dO, dWo, upd, steps, ascent, beta, rule, last))
+    # Muon normalizes its input, so a small eta meets large curvature: central differences with
+    # h = 1e-6 are good to about 1e-6 there (the double-autograd pin below is exact)
+    tol = 1e-5 if rule in (O.UPD_MUON, O.UPD_MUON_L2) else 1e-7
     for i, (g, r) in enumerate(zip(list(got[:4]) + list(got[4]), fd)):
-        assert rel(g, r) < 1e-7, i
+        assert rel(g, r) < tol, i
 
 
 @pytest.mark.parametrize("mask,chunk,upd,steps,ascent,beta,rule", CASES[3:7])
@@ -105,11 +137,13 @@ def test_last_layer_only_matches_the_last_layer_backward(mask, chunk, upd, steps
         assert rel(x, y) < 1e-12
 
 
-@pytest.mark.parametrize("mask,chunk,upd,beta,norm", [(O.MASK_APPLY_THEN_UPDATE, 4, None, 0.0, False),
-                                                      (O.MASK_UPDATE_THEN_APPLY, 5, None, 0.0, True),
-                                                      (O.MASK_STRIDED, 3, [0, 1, 1, 0, 1], 0.9, True),
-                                                      (O.MASK_APPLY_THEN_UPDATE, 4, None, 0.6, False)])
-def test_backward_matches_double_autograd(mask, chunk, upd, beta, norm):
+@pytest.mark.parametrize("mask,chunk,upd,beta,norm,muon", [(O.MASK_APPLY_THEN_UPDATE, 4, None, 0.0, False, False),
+                                                           (O.MASK_UPDATE_THEN_APPLY, 5, None, 0.0, True, False),
+                                                           (O.MASK_STRIDED, 3, [0, 1, 1, 0, 1], 0.9, True, False),
+                                                           (O.MASK_APPLY_THEN_UPDATE, 4, None, 0.6, False, False),
+                                                           (O.MASK_APPLY_THEN_UPDATE, 4, None, 0.9, True, True),
+                                                           (O.MASK_UPDATE_THEN_APPLY, 5, None, 0.0, False, True)])
+def test_backward_matches_double_autograd(mask, chunk, upd, beta, norm, muon):
     torch = pytest.importorskip("torch")
     N, d, m = 13, 4, 6
     args, dO, dWo = problem(80 + mask, N, d, m)
@@ -118,6 +152,13 @@ def test_backward_matches_double_autograd(mask, chunk, upd, beta, norm):
 
     def f(W, x):  # rows of the SwiGLU fast weight over rows of x
         return (torch.nn.functional.silu(x @ W[0].T) * (x @ W[1].T)) @ W[2].T
+
+    def ns(U):  # five cubic Newton-Schulz steps on the side with the smaller Gram matrix
+        X = U.T if U.shape[0] > U.shape[1] else U
+        X = X / (torch.sqrt((X * X).sum()) + 1e-7)
+        for _ in range(5):
+            X = 1.5 * X - 0.5 * (X @ X.T) @ X
+        return X.T if U.shape[0] > U.shape[1] else X
 
     post = mask == O.MASK_UPDATE_THEN_APPLY
     W, outs = list(t[4:]), []
@@ -131,15 +172,15 @@ def test_backward_matches_double_autograd(mask, chunk, upd, beta, norm):
             g = torch.autograd.grad(inner, W, create_graph=True)
             for i in range(3):
                 M[i] = beta * M[i] + g[i]
-                W[i] = W[i] - M[i]
+                W[i] = W[i] - (ns(M[i]) if muon else M[i])
                 if norm:  # rows to unit norm over the input dimension (eps never binds here)
                     W[i] = W[i] / torch.clamp(torch.sqrt((W[i] * W[i]).sum(dim=1, keepdim=True)), min=1e-6)
         if post:
             outs.append(f(W, tq[lo:hi]))
     L = (torch.cat(outs) * torch.tensor(dO)).sum() + sum((w * torch.tensor(g)).sum() for w, g in zip(W, dWo))
     L.backward()
-    got = O.ttt_backward_scan_ref(*args, chunk, mask, dO, dWo, upd, 1, False, beta,
-                                  O.UPD_GD_L2 if norm else O.UPD_GD)
+    rule = (O.UPD_MUON_L2 if norm else O.UPD_MUON) if muon else (O.UPD_GD_L2 if norm else O.UPD_GD)
+    got = O.ttt_backward_scan_ref(*args, chunk, mask, dO, dWo, upd, 1, False, beta, rule)
     for g, x in zip(list(got[:4]) + list(got[4]), t):
         assert rel(g, x.grad.numpy()) < 1e-12
 
