@@ -25,7 +25,7 @@ EXPORTS = (
     "ttt_profile_enable", "ttt_profile_select", "ttt_profile_read", "ttt_profile_kernel_name",
     "ttt_probe_mfma_bf16",
 )
-PROF_KERNELS = 31
+PROF_KERNELS = 32
 NOALLOC_SCRATCH_BYTES = 64 << 20   # TTT_NOALLOC_SCRATCH_BYTES of include/ttt.h
 
 

@@ -198,11 +198,11 @@ def ttt_backward_workspace_bytes(desc: C.TttDesc) -> int:
 def ttt_backward(q, k, v, eta, W0, dO, chunk: int, mask_mode: int = C.MASK_APPLY_THEN_UPDATE, *,
                  m_h: Optional[int] = None, dW_out: Optional[torch.Tensor] = None, want_dW0: bool = True,
                  update_chunks=None, inner_steps: int = 1, ascent: bool = False, momentum: float = 0.0,
-                 update_rule: int = C.UPD_GD, last_layer_only: bool = True,
+                 update_rule: int = C.UPD_GD, last_layer_only: bool = True, ns_iters: int = 5,
                  workspace: Optional[torch.Tensor] = None, stream=None):
-    """Backward of ttt_forward for UPD_GD or UPD_GD_L2 (momentum as a forward call without M, i.e.
-    from zero), through ttt_backward of libttt.so: with last_layer_only the layer whose inner loop
-    trains W2 alone, otherwise the recurrence with all three weights learning.
+    """Backward of ttt_forward (momentum as a forward call without M, i.e. from zero), through
+    ttt_backward of libttt.so: with last_layer_only the layer whose inner loop trains W2 alone,
+    otherwise the recurrence with all three weights learning; ns_iters as for ttt_forward (Muon).
 
     dO [B, H, N, d] is the gradient of o, dW_out ([B, H, 3*d*m] fp32 or None) that of W_out.
     Returns (dq, dk, dv, deta, dW0 or None); dW0 has W0's shape (per-head weights sum over the
@@ -227,7 +227,7 @@ def ttt_backward(q, k, v, eta, W0, dO, chunk: int, mask_mode: int = C.MASK_APPLY
     if dW_out is not None:
         _need(dW_out, "dW_out", torch.float32, dev, (B, H, 3 * d * m_h))
     _flags(update_chunks, N, chunk, mask_mode == C.MASK_STRIDED)
-    D, keep = ttt_desc(B, H, N, d, m_h, chunk, _DT[q.dtype], mask_mode, update_rule, 0, momentum,
+    D, keep = ttt_desc(B, H, N, d, m_h, chunk, _DT[q.dtype], mask_mode, update_rule, ns_iters, momentum,
                        bool(last_layer_only), per_batch, update_chunks, inner_steps, ascent)
     nbytes = ttt_backward_workspace_bytes(D)
     workspace = _workspace(workspace, nbytes, dev)

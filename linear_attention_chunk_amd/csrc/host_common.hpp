@@ -26,7 +26,8 @@ inline ttt_status fail(ttt_status s, const char* fmt, ...) {
 enum ProfKernel { PK_UP = 0, PK_DOWN, PK_UPDATE, PK_MUON_PREP, PK_NS_INIT, PK_NS_GRAM, PK_NS_STEP, PK_LINATTN,
                   PK_LIN_DELTA, PK_LIN_SCAN, PK_LIN_APPLY, PK_PHI, PK_W13, PK_ZERO, PK_PAR_MOM, PK_SWA,
                   PK_SWA_PREP, PK_LIN_BWD_T, PK_LIN_BWD_N, PK_LIN_DETA, PK_SWA_VPREP, PK_W13T, PK_PHI_DX,
-                  PK_DW13, PK_DW_SUM, PK_FB_PREP, PK_FB_OPS, PK_FB_UP, PK_FB_DX, PK_FB_DW, PK_FB_MISC };
+                  PK_DW13, PK_DW_SUM, PK_FB_PREP, PK_FB_OPS, PK_FB_UP, PK_FB_DX, PK_FB_DW, PK_FB_MISC,
+                  PK_FB_NSB };
 
 // Brackets one launch with events on its stream while profiling is enabled; no-op otherwise.
 struct ProfScope {
@@ -152,10 +153,15 @@ ttt_status lin_chunked_bwd(const linattn_desc& D, const uint32_t (&flags)[32], c
 // The forward recurrence run for its record: the weights before each update at hist + i S 3 d m
 // (i = 0 .. updates, the last one the final weights) and, with the norm, each update's row norms
 // (|W - U| of the 2m + d rows) at nrm + i S (2m + d); no output.  ws: ttt_history_ws_bytes.
+// With Muon each update's U (the input of Newton-Schulz, fp32) goes to urec + i S 3 d m.
 size_t ttt_history_ws_bytes(const ttt_desc& D);
 template <typename T>
 ttt_status ttt_run_history(const ttt_desc& D, const T* q, const T* k, const T* v, const float* eta, const float* W0,
-                           float* hist, float* nrm, char* ws, hipStream_t st);
+                           float* hist, float* nrm, float* urec, char* ws, hipStream_t st);
+// Newton-Schulz iterates of U for the backward (fp32): X_k at X + k S 3 d m (k < max(ns_iters, 1)),
+// the Gram matrix of X_k at P + k S 3 p^2 (k < ns_iters), the partial sums of U^2 in part
+// (S x 3 x ceil(d m / 4096)); the learned matrices only (W2 alone with last_layer_only).
+ttt_status ns_iterates(const ttt_desc& D, const float* U, float* part, float* X, float* P, hipStream_t st);
 
 // The backward of the recurrence with all three weights learning (GD or GD + L2, momentum): the
 // descriptor checks beyond validate_ttt_desc, the workspace, and the run (arguments as for

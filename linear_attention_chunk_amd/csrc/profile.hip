@@ -19,7 +19,7 @@ const char* kNames[TTT_PROF_KERNELS] = {"k_up", "k_down", "k_update", "k_muon_pr
                                         "k_par_momentum", "k_swa", "k_swa_qprep", "k_lin_bwd_t",
                                         "k_lin_bwd_n", "k_lin_deta_sum", "k_swa_vprep", "k_w13t_cvt",
                                         "k_phi_dx", "k_dw13", "k_dw_sum", "k_fb_prep", "k_fb_ops",
-                                        "k_fb_up", "k_fb_dx", "k_fb_dw", "k_fb_misc"};
+                                        "k_fb_up", "k_fb_dx", "k_fb_dw", "k_fb_misc", "k_nsb"};
 }  // namespace
 
 static thread_local bool t_prof_off = false;

@@ -244,10 +244,17 @@ static BLayout make_blayout(const ttt_desc& D, bool want_dw) {
     return L;
 }
 
+// whether the backward runs as the reverse of the recurrence (all weights learning, or Muon) rather
+// than through linear attention over phi (W2 alone, GD or GD + L2)
+static bool uses_full(const ttt_desc& D) {
+    return !D.last_layer_only || D.rule == TTT_UPD_MUON || D.rule == TTT_UPD_MUON_L2;
+}
+
 static ttt_status validate_bwd(const ttt_desc* D) {
     ttt_status rc = validate_ttt_desc(D);
     if (rc != TTT_OK) return rc;
-    if (!D->last_layer_only) return validate_full_bwd(D);  // all three weights learning
+    // all three weights learning, or Muon: the reverse of the recurrence
+    if (!D->last_layer_only || D->rule == TTT_UPD_MUON || D->rule == TTT_UPD_MUON_L2) return validate_full_bwd(D);
     if ((D->rule != TTT_UPD_GD && D->rule != TTT_UPD_GD_L2) || D->chunk_rates)
         return fail(TTT_ERR_UNSUPPORTED,
                     "the backward covers the layer whose inner loop trains W2 alone by GD (with or without momentum "
@@ -387,7 +394,7 @@ extern "C" ttt_status ttt_backward_workspace_bytes(const ttt_desc* desc, size_t*
     ttt_status rc = validate_bwd(desc);
     if (rc != TTT_OK) return rc;
     if (!bytes) return fail(TTT_ERR_INVALID_ARGUMENT, "bytes is NULL");
-    *bytes = desc->last_layer_only ? make_blayout(*desc, true).total : full_bwd_ws_bytes(*desc);
+    *bytes = uses_full(*desc) ? full_bwd_ws_bytes(*desc) : make_blayout(*desc, true).total;
     return TTT_OK;
 }
 
@@ -428,7 +435,7 @@ extern "C" ttt_status ttt_backward(const ttt_desc* desc, const void* q, const vo
             if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n))
                 return fail(TTT_ERR_INVALID_ARGUMENT, "%s overlaps %s", outs[i].name, outs[j].name);
     }
-    const bool full = !D.last_layer_only;
+    const bool full = uses_full(D);
     const BLayout L = full ? BLayout{} : make_blayout(D, dW0 != nullptr);
     const size_t need = full ? full_bwd_ws_bytes(D) : L.total;
     if (need && (!workspace || workspace_bytes < need))

@@ -52,8 +52,10 @@ struct FbPrepArgs {
     float* dW; const float* part; int nparts; int64_t part_stride;  // [S][3dm]; part p at part + p part_stride
     const float* y; const float* nrm;  // norm: the update's output [S][3dm] and its row norms [S][2m + d]
     float* dM; float beta;             // momentum: the gradient of M [S][3dm], or null
-    float* G;                          // out: Gamma [S][3dm]
+    float* G;                          // out: Gamma [S][3dm], or with Muon the gradient of its output
     int d, m, nscan;
+    int muon;                          // G <- -gx (Newton-Schulz's backward and k_nsb_final follow)
+    int frozen;                        // rows 0 .. frozen-1 (W1, W3 with last_layer_only) do not update
 };
 
 __global__ __launch_bounds__(kThreads) void k_fb_prep(FbPrepArgs a) {
@@ -77,7 +79,8 @@ __global__ __launch_bounds__(kThreads) void k_fb_prep(FbPrepArgs a) {
                 g[i] += *reinterpret_cast<const f32x4_t*>(a.part + p * a.part_stride + off + 4 * c);
         }
     }
-    if (a.y) {  // the norm's transpose at this update's row
+    const bool fz = r < a.frozen;  // uniform per wave
+    if (a.y && !fz) {  // the norm's transpose at this update's row
         f32x4_t y[kFbRowVec];
         float t = 0.f;
 #pragma unroll
@@ -97,7 +100,9 @@ __global__ __launch_bounds__(kThreads) void k_fb_prep(FbPrepArgs a) {
         if (c < nv) {
             const int64_t e = off + 4 * c;
             f32x4_t dmi = -g[i];
-            if (a.dM) {
+            if (fz) {
+                dmi = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            } else if (a.dM && !a.muon) {
                 dmi += *reinterpret_cast<const f32x4_t*>(a.dM + e);
                 *reinterpret_cast<f32x4_t*>(a.dM + e) = a.beta * dmi;
             }
@@ -557,6 +562,169 @@ __global__ __launch_bounds__(kThreads, 2) void k_fb_dw(FbDwArgs<T> a) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// Newton-Schulz walked back (Muon), in fp32, for every scan's learned matrices at once.  With X the
+// iterate of a step and G the gradient of its output, the gradient of its input is
+//   wide X (rows <= columns):  1.5 G - 0.5 [(Q + Q^T) X + (X X^T) G],  Q = G X^T
+//   tall X:                    1.5 G - 0.5 [G (X^T X) + X (Q + Q^T)],  Q = G^T X
+// (the forward steps on the side with the smaller Gram matrix, as the tall form does transposed).
+// k_nsb_q writes Q + Q^T, k_nsb_step the new gradient (to the other buffer: every tile reads G), and
+// the start X_0 = U / (|U| + 1e-7) is taken back by k_nsb_dot and k_nsb_final.
+struct PMD { static constexpr int a[2] = {0, 1}; static constexpr int b[2] = {0, 1}; };
+constexpr int kNsbQ = 64;                      // Q tiles
+constexpr int kNsbRows = 128, kNsbCols = 64;   // step tiles
+constexpr int kNsbElems = 4096;                // elements per block of the dot and final kernels
+
+struct NsbArgs {
+    const float* G; float* Gout;     // [S][3dm]
+    const float* X;                  // the step's iterate [S][3dm]
+    const float* P;                  // its Gram matrix [S][3 p^2]
+    float* Q;                        // Q + Q^T [S][3 p^2]
+    int d, m, mat0, nmat, tiles;     // tiles per matrix
+};
+
+__global__ __launch_bounds__(kThreads, 2) void k_nsb_q(NsbArgs a) {
+    using TW = Tile<float, kNsbQ, kNsbQ, 2, 2, 2, 2, 2, false, false, false, 4, 2>;
+    using TT = Tile<float, kNsbQ, kNsbQ, 2, 2, 2, 2, 2, true, true, false, 4, 2>;
+    constexpr int LDSB = std::max(TW::LDS, TT::LDS);
+    __shared__ __attribute__((aligned(16))) char smem[LDSB];
+    const int per = a.nmat * a.tiles;
+    const int lb = xcd_block(gridDim.x);
+    const int s = lb / per;
+    int t = lb % per;
+    const int mat = a.mat0 + t / a.tiles;
+    t %= a.tiles;
+    const int r = mat < 2 ? a.m : a.d, c = mat < 2 ? a.d : a.m;
+    const int p = std::min(r, c), np = (p + kNsbQ - 1) / kNsbQ;
+    const int i0 = (t / np) * kNsbQ, j0 = (t % np) * kNsbQ;
+    if (i0 >= p) return;  // uniform: tiles covers the largest matrix
+    const int64_t dm = (int64_t)a.d * a.m;
+    const float* G = a.G + (int64_t)s * 3 * dm + mat * dm;
+    const float* X = a.X + (int64_t)s * 3 * dm + mat * dm;
+    float* Q = a.Q + ((int64_t)s * 3 + mat) * p * p;
+    auto out = [&](auto& tl) {
+        tl.for_each([&](const float (&v)[2], int row, int col) {
+            if (i0 + row < p && j0 + col < p) Q[(int64_t)(i0 + row) * p + j0 + col] = v[0] + v[1];
+        });
+    };
+    if (r <= c) {  // Q = G X^T over the columns: rows of G and X are k-contiguous
+        TW tl;
+        const Opnd<float> A[2] = {{G + (int64_t)i0 * c, c, p - i0, c}, {X + (int64_t)i0 * c, c, p - i0, c}};
+        const Opnd<float> B[2] = {{X + (int64_t)j0 * c, c, p - j0, c}, {G + (int64_t)j0 * c, c, p - j0, c}};
+        tl.template run<PMD>(A, B, c, smem);
+        out(tl);
+    } else {       // Q = G^T X over the rows: columns of G and X, k-strided
+        TT tl;
+        const Opnd<float> A[2] = {{G + i0, c, p - i0, r}, {X + i0, c, p - i0, r}};
+        const Opnd<float> B[2] = {{X + j0, c, p - j0, r}, {G + j0, c, p - j0, r}};
+        tl.template run<PMD>(A, B, r, smem);
+        out(tl);
+    }
+}
+
+__global__ __launch_bounds__(kThreads, 2) void k_nsb_step(NsbArgs a) {
+    using TW = Tile<float, kNsbRows, kNsbCols, 2, 2, 1, 1, 1, false, true, false, 4, 2>;   // B k-strided
+    using TT = Tile<float, kNsbRows, kNsbCols, 2, 2, 1, 1, 1, false, false, false, 4, 2>;  // B symmetric rows
+    constexpr int LDSB = std::max(TW::LDS, TT::LDS);
+    __shared__ __attribute__((aligned(16))) char smem[LDSB];
+    const int per = a.nmat * a.tiles;
+    const int lb = xcd_block(gridDim.x);
+    const int s = lb / per;
+    int t = lb % per;
+    const int mat = a.mat0 + t / a.tiles;
+    t %= a.tiles;
+    const int r = mat < 2 ? a.m : a.d, c = mat < 2 ? a.d : a.m;
+    const int p = std::min(r, c);
+    const int nct = (c + kNsbCols - 1) / kNsbCols;
+    const int r0 = (t / nct) * kNsbRows, c0 = (t % nct) * kNsbCols;
+    if (r0 >= r) return;  // uniform: tiles covers the larger of the two orientations
+    const int64_t dm = (int64_t)a.d * a.m, mo = (int64_t)s * 3 * dm + mat * dm;
+    const float* G = a.G + mo;
+    const float* X = a.X + mo;
+    const float* P = a.P + ((int64_t)s * 3 + mat) * p * p;
+    const float* Q = a.Q + ((int64_t)s * 3 + mat) * p * p;
+    float* O = a.Gout + mo;
+    auto out = [&](auto& tl) {
+        tl.for_each([&](const float (&v)[1], int row, int col) {
+            if (r0 + row < r && c0 + col < c) {
+                const int64_t e = (int64_t)(r0 + row) * c + c0 + col;
+                O[e] = 1.5f * G[e] - 0.5f * v[0];
+            }
+        });
+    };
+    if (r <= c) {  // (Q + Q^T) X + P G: B is X or G read k-strided
+        TW tl;
+        const Opnd<float> A0[1] = {{Q + (int64_t)r0 * p, p, r - r0, p}};
+        const Opnd<float> B0[1] = {{X + c0, c, c - c0, r}};
+        const Opnd<float> A1[1] = {{P + (int64_t)r0 * p, p, r - r0, p}};
+        const Opnd<float> B1[1] = {{G + c0, c, c - c0, r}};
+        tl.template run<PM1>(A0, B0, r, smem);
+        tl.template run<PM1>(A1, B1, r, smem, true);
+        out(tl);
+    } else {       // G P + X (Q + Q^T): P and Q + Q^T are symmetric, so their rows serve as B
+        TT tl;
+        const Opnd<float> A0[1] = {{G + (int64_t)r0 * c, c, r - r0, c}};
+        const Opnd<float> B0[1] = {{P + (int64_t)c0 * p, p, c - c0, p}};
+        const Opnd<float> A1[1] = {{X + (int64_t)r0 * c, c, r - r0, c}};
+        const Opnd<float> B1[1] = {{Q + (int64_t)c0 * p, p, c - c0, p}};
+        tl.template run<PM1>(A0, B0, c, smem);
+        tl.template run<PM1>(A1, B1, c, smem, true);
+        out(tl);
+    }
+}
+
+// partial sums of <G, U> per block of 4096 elements of each learned matrix
+__global__ __launch_bounds__(kThreads) void k_nsb_dot(const float* G, const float* U, float* part, int64_t dm,
+                                                      int mat0, int nmat, int nblk) {
+    __shared__ float red[4];
+    const int per = nmat * nblk;
+    const int s = blockIdx.x / per, t = blockIdx.x % per;
+    const int mat = mat0 + t / nblk, blk = t % nblk;
+    const int64_t mo = (int64_t)s * 3 * dm + mat * dm;
+    float x = 0.f;
+    for (int64_t e = (int64_t)blk * kNsbElems + threadIdx.x; e < std::min<int64_t>((int64_t)(blk + 1) * kNsbElems, dm);
+         e += kThreads)
+        x += G[mo + e] * U[mo + e];
+    x = wave_sum(x);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) red[wave] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) part[((int64_t)s * 3 + mat) * nblk + blk] = red[0] + red[1] + red[2] + red[3];
+}
+
+// dU = G / (n + eps) - <G, U> U / ((n + eps)^2 n) (n = |U|, the second term absent at n = 0), then the
+// momentum: dMi = dM + dU, Gamma = dMi, dM <- beta dMi (dM null: Gamma = dU)
+struct NsbFinalArgs {
+    const float* G; const float* U; const float* pu; const float* pgu;  // partial sums of U^2 and <G, U>
+    float* Gamma; float* dM; float beta;
+    int64_t dm; int mat0, nmat, nblk;
+};
+
+__global__ __launch_bounds__(kThreads) void k_nsb_final(NsbFinalArgs a) {
+    const int per = a.nmat * a.nblk;
+    const int s = blockIdx.x / per, t = blockIdx.x % per;
+    const int mat = a.mat0 + t / a.nblk, blk = t % a.nblk;
+    const int64_t pb = ((int64_t)s * 3 + mat) * a.nblk;
+    float su = 0.f, sgu = 0.f;
+    for (int i = threadIdx.x & 63; i < a.nblk; i += 64) {
+        su += a.pu[pb + i];
+        sgu += a.pgu[pb + i];
+    }
+    const float n = sqrtf(wave_sum(su)), gu = wave_sum(sgu);
+    const float inv = 1.0f / (n + 1e-7f);
+    const float k2 = n > 0.f ? gu * inv * inv / n : 0.f;
+    const int64_t mo = (int64_t)s * 3 * a.dm + mat * a.dm;
+    for (int64_t e = (int64_t)blk * kNsbElems + threadIdx.x; e < std::min<int64_t>((int64_t)(blk + 1) * kNsbElems, a.dm);
+         e += kThreads) {
+        float du = a.G[mo + e] * inv - k2 * a.U[mo + e];
+        if (a.dM) {
+            du += a.dM[mo + e];
+            a.dM[mo + e] = a.beta * du;
+        }
+        a.Gamma[mo + e] = du;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
 // small kernels: dW <- dW_out (or zero) and dM <- 0; zero rows of the token gradients of chunks
 // that do not update; dW0 of each weight block from dW and the pending parts (fixed order)
 __global__ __launch_bounds__(kThreads) void k_fb_init(float* dW, const float* dWo, float* dM, int64_t n4) {
@@ -672,6 +840,7 @@ static int fb_parts(int64_t tiles, int64_t total) {
 
 struct FLayout {
     size_t fwd, hist, nrm, dW, dM, G, op, acp, qa, qh, pk, pv, pe, acck, accv, epart, part, total;
+    size_t urec, nsx, nsp, nsq, gb, pu, pgu;  // Muon: U of every update, iterates, Grams, Q + Q^T, G's pair, sums
     int nparts, nK;
     int64_t bcap, qcap;
 };
@@ -710,16 +879,25 @@ static FLayout make_flayout(const ttt_desc& D, const FbPlan& P) {
     const int64_t tiles = S * 2 * cdiv(m, kFwTile) * cdiv(d, kFwTile);
     L.nparts = fb_parts(tiles, (P.T > 0 ? L.bcap : 0) + L.qcap);
     L.part = take((size_t)L.nparts * S * 3 * dm * 4);
+    if (D.rule == TTT_UPD_MUON || D.rule == TTT_UPD_MUON_L2) {
+        const int64_t p = std::min(d, m), nblk = cdiv(dm, kNsbElems);
+        L.urec = take((size_t)P.T * S * 3 * dm * 4);
+        L.nsx = take((size_t)std::max(D.ns_iters, 1) * S * 3 * dm * 4);
+        L.nsp = take((size_t)std::max(D.ns_iters, 1) * S * 3 * p * p * 4);
+        L.nsq = take((size_t)S * 3 * p * p * 4);
+        L.gb = take((size_t)S * 3 * dm * 4);
+        L.pu = take((size_t)S * 3 * nblk * 4);
+        L.pgu = take((size_t)S * 3 * nblk * 4);
+    }
     L.total = off;
     return L;
 }
 
 ttt_status validate_full_bwd(const ttt_desc* D) {
-    if (D->last_layer_only || (D->rule != TTT_UPD_GD && D->rule != TTT_UPD_GD_L2) || D->chunk_rates ||
-        D->parallel_form)
+    const bool muon = D->rule == TTT_UPD_MUON || D->rule == TTT_UPD_MUON_L2;
+    if ((D->last_layer_only && !muon) || D->chunk_rates || (D->parallel_form && !D->last_layer_only))
         return fail(TTT_ERR_UNSUPPORTED,
-                    "the backward of the recurrence with all weights learning covers TTT_UPD_GD and TTT_UPD_GD_L2 "
-                    "(with or without momentum) with per-token rates");
+                    "the backward of the recurrence covers every rule (with or without momentum) with per-token rates");
     const int64_t S = (int64_t)D->B * D->H, d = D->d_h, m = D->m_h;
     const int64_t bmax = D->N < D->chunk ? D->N : D->chunk;
     const int64_t lim = 1LL << 31;
@@ -749,7 +927,10 @@ ttt_status run_full_backward(const ttt_desc& D, const T* q, const T* k, const T*
     const int S = D.B * D.H, d = D.d_h, m = D.m_h;
     const int64_t dm = (int64_t)d * m, dm3 = 3 * dm;
     const int64_t hs = (int64_t)S * dm3;  // one version of every scan's weights
-    const bool norm = D.rule == TTT_UPD_GD_L2, mom = D.momentum != 0.0f;
+    const bool norm = D.rule == TTT_UPD_GD_L2 || D.rule == TTT_UPD_MUON_L2, mom = D.momentum != 0.0f;
+    const bool muon = D.rule == TTT_UPD_MUON || D.rule == TTT_UPD_MUON_L2;
+    const int mat0 = D.last_layer_only ? 2 : 0, nmat = D.last_layer_only ? 1 : 3;
+    const int64_t pp = std::min(d, m);
     const float sign = D.ascent ? -1.0f : 1.0f;
     float* hist = (float*)(ws + L.hist);
     float* nrm = norm ? (float*)(ws + L.nrm) : nullptr;
@@ -760,13 +941,57 @@ ttt_status run_full_backward(const ttt_desc& D, const T* q, const T* k, const T*
     float* part = (float*)(ws + L.part);
     ttt_status rc;
     // the forward's record
-    if ((rc = ttt_run_history<T>(D, q, k, v, eta, W0, hist, nrm, ws + L.fwd, st)) != TTT_OK) return rc;
+    float* urec = muon ? (float*)(ws + L.urec) : nullptr;
+    if ((rc = ttt_run_history<T>(D, q, k, v, eta, W0, hist, nrm, urec, ws + L.fwd, st)) != TTT_OK) return rc;
     {
         ProfScope ps(PK_FB_MISC, st);
         hipLaunchKernelGGL(k_fb_init, dim3((unsigned)cdiv(hs / 4, kThreads)), dim3(kThreads), 0, st, dW, dWo, dM,
                            hs / 4);
     }
     if ((rc = check_launch("k_fb_init", st)) != TTT_OK) return rc;
+    // Muon at update ver: G holds the gradient of Newton-Schulz's output; it becomes Gamma
+    auto muon_backward = [&](int ver) -> ttt_status {
+        const float* U = urec + (int64_t)ver * hs;
+        float* X = (float*)(ws + L.nsx);
+        float* P = (float*)(ws + L.nsp);
+        float* pu = (float*)(ws + L.pu);
+        float* pgu = (float*)(ws + L.pgu);
+        const int nblk = (int)cdiv(dm, kNsbElems);  // the blocks of U^2's partial sums (4096 elements)
+        ttt_status r;
+        if ((r = ns_iterates(D, U, pu, X, P, st)) != TTT_OK) return r;
+        float* Gc = G;
+        float* Gn = (float*)(ws + L.gb);
+        const int np = (int)cdiv(pp, kNsbQ);
+        const int stt = (int)std::max(cdiv(m, kNsbRows) * cdiv(d, kNsbCols), cdiv(d, kNsbRows) * cdiv(m, kNsbCols));
+        for (int it = D.ns_iters - 1; it >= 0; --it) {
+            NsbArgs na{Gc, Gn, X + (int64_t)it * hs, P + (int64_t)it * S * 3 * pp * pp, (float*)(ws + L.nsq), d, m, mat0,
+                       nmat, np * np};
+            {
+                ProfScope ps(PK_FB_NSB, st);
+                hipLaunchKernelGGL(k_nsb_q, dim3((unsigned)((int64_t)S * nmat * na.tiles)), dim3(kThreads), 0, st, na);
+            }
+            if ((r = check_launch("k_nsb_q", st)) != TTT_OK) return r;
+            na.tiles = stt;
+            {
+                ProfScope ps(PK_FB_NSB, st);
+                hipLaunchKernelGGL(k_nsb_step, dim3((unsigned)((int64_t)S * nmat * stt)), dim3(kThreads), 0, st, na);
+            }
+            if ((r = check_launch("k_nsb_step", st)) != TTT_OK) return r;
+            std::swap(Gc, Gn);
+        }
+        {
+            ProfScope ps(PK_FB_NSB, st);
+            hipLaunchKernelGGL(k_nsb_dot, dim3((unsigned)((int64_t)S * nmat * nblk)), dim3(kThreads), 0, st,
+                               (const float*)Gc, U, pgu, dm, mat0, nmat, nblk);
+        }
+        if ((r = check_launch("k_nsb_dot", st)) != TTT_OK) return r;
+        NsbFinalArgs fa{Gc, U, pu, pgu, G, dM, D.momentum, dm, mat0, nmat, nblk};
+        {
+            ProfScope ps(PK_FB_NSB, st);
+            hipLaunchKernelGGL(k_nsb_final, dim3((unsigned)((int64_t)S * nmat * nblk)), dim3(kThreads), 0, st, fa);
+        }
+        return check_launch("k_nsb_final", st);
+    };
     const int ntm = (int)cdiv(m, kFwTile), ntd = (int)cdiv(d, kFwTile);
     int pending = 0;  // partial buffers holding sums the next prep (or the last step) adds
     for (int ver = P.T; ver >= 0; --ver) {
@@ -774,7 +999,8 @@ ttt_status run_full_backward(const ttt_desc& D, const T* q, const T* k, const T*
         const int ju = step ? P.step_chunk[ver] : -1, it = step ? P.step_it[ver] : 0;
         if (step) {
             FbPrepArgs pa{dW, part, pending, hs, norm ? hist + (int64_t)(ver + 1) * hs : nullptr,
-                          norm ? nrm + (int64_t)ver * S * (2 * m + d) : nullptr, dM, D.momentum, G, d, m, S};
+                          norm ? nrm + (int64_t)ver * S * (2 * m + d) : nullptr, dM, D.momentum, G, d, m, S,
+                          muon ? 1 : 0, D.last_layer_only ? 2 * m : 0};
             {
                 ProfScope ps(PK_FB_PREP, st);
                 hipLaunchKernelGGL(k_fb_prep, dim3((unsigned)cdiv((int64_t)S * (2 * m + d), kThreads / 64)),
@@ -782,6 +1008,7 @@ ttt_status run_full_backward(const ttt_desc& D, const T* q, const T* k, const T*
             }
             if ((rc = check_launch("k_fb_prep", st)) != TTT_OK) return rc;
             pending = 0;
+            if (muon && (rc = muon_backward(ver)) != TTT_OK) return rc;
         }
         const int64_t a0 = P.qlo[ver];
         const int la = (int)(P.qhi[ver] - P.qlo[ver]);

@@ -457,6 +457,7 @@ template <typename T> struct PrepArgs {
                                           // (mat - mbase) d m): 0 for [W1 | W3 | W2], 2 for W2 alone
     const float* beta_chunk;              // per-chunk momentum factors [scan][nchunk] (beta_chunk[s nchunk +
     int nchunk, jchunk;                   // jchunk] replaces beta), or null
+    float* Urec; int64_t urec_stride;     // U as fp32 (the backward's record), or null
 };
 
 __device__ __forceinline__ float block_sum(float x, float* red) {
@@ -480,6 +481,7 @@ __global__ __launch_bounds__(kThreads) void k_muon_prep(PrepArgs<T> a) {
     float* M = a.M ? a.M + s * a.m_stride + mo : nullptr;
     T* Xh = a.Xhi ? a.Xhi + s * a.x_stride + mo : nullptr;
     T* Xl = a.Xhi ? a.Xlo + s * a.x_stride + mo : nullptr;
+    float* Ur = a.Urec ? a.Urec + s * a.urec_stride + mo : nullptr;
     float ss = 0.f;
     const float beta = a.beta_chunk ? a.beta_chunk[(int64_t)s * a.nchunk + a.jchunk] : a.beta;
     const int64_t e0 = (int64_t)blk * kPrepElems;
@@ -510,6 +512,7 @@ __global__ __launch_bounds__(kThreads) void k_muon_prep(PrepArgs<T> a) {
                 u = beta * mv[j] + u;
                 M[e] = u;
             }
+            if (Ur) Ur[e] = u;
             if constexpr (sizeof(T) == 2) {
                 if (Xh) {
                     const uint16_t h = f2bf(u);
@@ -1158,7 +1161,8 @@ static bool has_mom(const ttt_desc& D) { return D.chunk_rates ? D.chunk_momentum
 template <typename T>
 static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const T* k, const T* v,
                           const float* eta, const float* W0, T* o, float* W_out, float* M_inout,
-                          char* ws, hipStream_t st, float* hist = nullptr, float* nrm = nullptr) {
+                          char* ws, hipStream_t st, float* hist = nullptr, float* nrm = nullptr,
+                          float* urec = nullptr) {
     const int S = D.B * D.H, d = D.d_h, m = D.m_h;
     const int64_t dm = (int64_t)d * m;
     const bool muon = is_muon(D);
@@ -1192,8 +1196,8 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
     for (int step = 0; step < nsteps && step < nc; ++step)
         if (D.mask != TTT_MASK_STRIDED || D.update_chunks[step]) last_upd = step;
     // hist (the backward's record): the weights before update i go to hist + i S 3 d m, the last
-    // update's result after them, and with the norm each update's row norms to nrm + i S (2m + d);
-    // then there is no output (o is null)
+    // update's result after them, with the norm each update's row norms to nrm + i S (2m + d), and
+    // with Muon each update's U (fp32) to urec + i S 3 d m; then there is no output (o is null)
     const int64_t hstride = (int64_t)S * 3 * dm;
     int ui = 0;  // updates so far
     {  // W0 -> shadows, and the master copy only if no update follows (the first update reads W0)
@@ -1272,6 +1276,10 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
                 PrepArgs<T> pa{G, L.g_stride, a.ksplit, a.gpart_stride, keep_g ? G : nullptr, M, 3 * dm, D.momentum, part,
                                L.nblk, split ? Xb[1] : nullptr, split ? Xlo : nullptr, L.x_stride, dm, mat0, nmat, 0,
                                D.chunk_rates ? D.chunk_momentum : nullptr, nchunks, ju};
+                if (urec) {
+                    pa.Urec = urec + ui * hstride;
+                    pa.urec_stride = 3 * dm;
+                }
                 {
                     ProfScope ps(PK_MUON_PREP, st);
                     hipLaunchKernelGGL(k_muon_prep<T>, dim3(S * nmat * L.nblk), dim3(kThreads), 0, st, pa);
@@ -1358,18 +1366,66 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
 
 // The forward recurrence run for its record alone (no output): every update's input weights and,
 // with the norm, its row norms, as described at run_ttt.
-size_t ttt_history_ws_bytes(const ttt_desc& D) { return make_layout(D, false, has_mom(D)).total; }
+size_t ttt_history_ws_bytes(const ttt_desc& D) { return make_layout(D, is_muon(D), has_mom(D)).total; }
 
 template <typename T>
 ttt_status ttt_run_history(const ttt_desc& D, const T* q, const T* k, const T* v, const float* eta, const float* W0,
-                           float* hist, float* nrm, char* ws, hipStream_t st) {
-    const Layout L = make_layout(D, false, has_mom(D));
-    return run_ttt<T>(D, L, q, k, v, eta, W0, nullptr, nullptr, nullptr, ws, st, hist, nrm);
+                           float* hist, float* nrm, float* urec, char* ws, hipStream_t st) {
+    const Layout L = make_layout(D, is_muon(D), has_mom(D));
+    return run_ttt<T>(D, L, q, k, v, eta, W0, nullptr, nullptr, nullptr, ws, st, hist, nrm, urec);
 }
 template ttt_status ttt_run_history<uint16_t>(const ttt_desc&, const uint16_t*, const uint16_t*, const uint16_t*,
-                                              const float*, const float*, float*, float*, char*, hipStream_t);
+                                              const float*, const float*, float*, float*, float*, char*, hipStream_t);
 template ttt_status ttt_run_history<float>(const ttt_desc&, const float*, const float*, const float*, const float*,
-                                           const float*, float*, float*, char*, hipStream_t);
+                                           const float*, float*, float*, float*, char*, hipStream_t);
+
+// Newton-Schulz iterates of every scan's U (fp32, for the backward): X_0 = U / (||U||_F + 1e-7),
+// then the forward's steps; X_k (k < ns_iters, and X_0 also when ns_iters is 0) at X + k S 3 d m
+// and its Gram matrix at P + k S 3 p^2, with the learned matrices' partial sums of U^2 in part
+// (S x 3 x nblk).  U, X: [S][3dm]; P: [S][3 p^2], p = min(d, m).
+ttt_status ns_iterates(const ttt_desc& D, const float* U, float* part, float* X, float* P, hipStream_t st) {
+    const int S = D.B * D.H, d = D.d_h, m = D.m_h;
+    const int64_t dm = (int64_t)d * m, p = std::min(d, m);
+    const int mat0 = D.last_layer_only ? 2 : 0, nmat = D.last_layer_only ? 1 : 3;
+    const int nblk = (int)cdiv(dm, kPrepElems);
+    ttt_status rc;
+    {
+        PrepArgs<float> pa{U, 3 * dm, 1, 0, nullptr, nullptr, 0, 0.f, part, nblk, nullptr, nullptr, 0, dm, mat0, nmat, 0,
+                           nullptr, 0, 0};
+        ProfScope ps(PK_MUON_PREP, st);
+        hipLaunchKernelGGL(k_muon_prep<float>, dim3(S * nmat * nblk), dim3(kThreads), 0, st, pa);
+    }
+    if ((rc = check_launch("k_muon_prep", st)) != TTT_OK) return rc;
+    {
+        NSArgs<float> na{U, 3 * dm, part, nblk, nullptr, nullptr, nullptr, X, 3 * dm, nullptr, 0, d, m, mat0, nmat, 0, 0};
+        ProfScope ps(PK_NS_INIT, st);
+        hipLaunchKernelGGL(k_ns_init<float>, dim3(S * nmat * nblk), dim3(kThreads), 0, st, na);
+    }
+    if ((rc = check_launch("k_ns_init", st)) != TTT_OK) return rc;
+    const bool gsmall = (int64_t)S * nmat * cdiv(p, 128) * (cdiv(p, 128) + 1) / 2 < 256;
+    const int gts = gsmall ? 64 : 128;
+    const int gt = (int)(cdiv(p, gts) * (cdiv(p, gts) + 1) / 2);
+    const int stt = (int)std::max(cdiv(m, kNSStepRows) * cdiv(d, kNSStepCols), cdiv(d, kNSStepRows) * cdiv(m, kNSStepCols));
+    const int64_t xs = (int64_t)S * 3 * dm, ps_ = (int64_t)S * 3 * p * p;
+    for (int k = 0; k < D.ns_iters; ++k) {
+        NSArgs<float> na{nullptr, 0, nullptr, nblk, X + k * xs, k + 1 < D.ns_iters ? X + (k + 1) * xs : nullptr, nullptr,
+                         nullptr, 3 * dm, P + k * ps_, 3 * p * p, d, m, mat0, nmat, gt, 0};
+        {
+            ProfScope ps(PK_NS_GRAM, st);
+            if (gsmall) hipLaunchKernelGGL((k_ns_gram<float, 64>), dim3(S * nmat * gt), dim3(kThreads), 0, st, na);
+            else hipLaunchKernelGGL((k_ns_gram<float, 128>), dim3(S * nmat * gt), dim3(kThreads), 0, st, na);
+        }
+        if ((rc = check_launch("k_ns_gram", st)) != TTT_OK) return rc;
+        if (k + 1 == D.ns_iters) break;  // the last iterate is not needed
+        na.tiles = stt;
+        {
+            ProfScope ps(PK_NS_STEP, st);
+            hipLaunchKernelGGL(k_ns_step<float>, dim3(S * nmat * stt), dim3(kThreads), 0, st, na);
+        }
+        if ((rc = check_launch("k_ns_step", st)) != TTT_OK) return rc;
+    }
+    return TTT_OK;
+}
 
 }  // namespace ttt
 

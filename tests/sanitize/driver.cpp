@@ -69,10 +69,10 @@ static void run_ttt(ttt_desc D) {
     ttt_status bs = ttt_backward_workspace_bytes(&D, &bneed);
     check_message(bs);
     if (s != TTT_OK) EXPECT(bs == s);
-    // (W2 alone, or all three weights learning with at most 65536 recorded updates)
+    // (W2 alone by GD, else the recurrence with at most 65536 recorded updates)
     const int64_t nupd = (D.N > 0 && D.chunk > 0 ? ((int64_t)D.N + D.chunk - 1) / D.chunk : 0) * (D.inner_steps > 1 ? D.inner_steps : 1);
-    const bool covered = (D.rule == TTT_UPD_GD || D.rule == TTT_UPD_GD_L2) && D.chunk_rates == 0 &&
-                         (D.last_layer_only == 1 || nupd <= 65536);
+    const bool gd = D.rule == TTT_UPD_GD || D.rule == TTT_UPD_GD_L2;
+    const bool covered = D.chunk_rates == 0 && ((D.last_layer_only == 1 && gd) || nupd <= 65536);
     if (s == TTT_OK && !covered) EXPECT(bs == TTT_ERR_UNSUPPORTED);
     const void* dO = (const void*)(P + (9ull << 36));
     void* dq = (void*)(P + (10ull << 36));

@@ -296,14 +296,15 @@ def bwd_desc(**kw):
     (dict(), C.TTT_OK), (dict(mask=C.MASK_UPDATE_THEN_APPLY, inner_steps=3, ascent=1), C.TTT_OK),
     (dict(parallel_form=1, w0_per_batch=1), C.TTT_OK), (dict(N=0), C.TTT_OK),
     # the layer whose inner loop trains W2 alone by GD (momentum and the L2 norm allowed), and the
-    # recurrence with all three weights learning by GD or GD + L2 (momentum allowed)
+    # recurrence (all three weights learning, or W2 alone with Muon) under every rule and momentum,
+    # up to 65536 recorded updates
     (dict(last_layer_only=0), C.TTT_OK), (dict(rule=C.UPD_GD_L2), C.TTT_OK),
     (dict(last_layer_only=0, rule=C.UPD_GD_L2, momentum=0.9, inner_steps=2, ascent=1), C.TTT_OK),
-    (dict(last_layer_only=0, rule=C.UPD_MUON_L2), C.TTT_ERR_UNSUPPORTED),
+    (dict(last_layer_only=0, rule=C.UPD_MUON_L2), C.TTT_OK), (dict(last_layer_only=0, N=1 << 20, chunk=8), C.TTT_ERR_UNSUPPORTED),
     (dict(last_layer_only=0, chunk_rates=1), C.TTT_ERR_UNSUPPORTED),
     (dict(last_layer_only=0, parallel_form=1), C.TTT_ERR_INVALID_ARGUMENT),
-    (dict(rule=C.UPD_GD_L2, momentum=0.9, inner_steps=3), C.TTT_OK), (dict(rule=C.UPD_MUON_L2), C.TTT_ERR_UNSUPPORTED),
-    (dict(rule=C.UPD_MUON), C.TTT_ERR_UNSUPPORTED), (dict(momentum=0.9), C.TTT_OK),
+    (dict(rule=C.UPD_GD_L2, momentum=0.9, inner_steps=3), C.TTT_OK), (dict(rule=C.UPD_MUON_L2), C.TTT_OK),
+    (dict(rule=C.UPD_MUON, momentum=0.9), C.TTT_OK), (dict(momentum=0.9), C.TTT_OK),
     (dict(chunk_rates=1), C.TTT_ERR_UNSUPPORTED), (dict(mask=C.MASK_TOKEN_CAUSAL), C.TTT_ERR_UNSUPPORTED),
     (dict(d_h=48), C.TTT_ERR_INVALID_ARGUMENT), (dict(mask=C.MASK_STRIDED), C.TTT_ERR_INVALID_ARGUMENT),
 ])

@@ -31,9 +31,10 @@ def split(W, d, m):
 
 
 def run(seed, B, H, N, d, m, chunk, mask, bf16, rule=O.UPD_GD_L2, flags=None, inner=1, ascent=False, momentum=0.0,
-        per_batch=False, dW_out=True, want_dW0=True):
+        per_batch=False, dW_out=True, want_dW0=True, last=False):
     say(f"full ttt_backward case B{B} H{H} N{N} d{d} m{m} b{chunk} mask{mask} bf16={bf16} rule={rule} flags={flags} "
-        f"inner{inner} ascent{ascent} momentum={momentum} per_batch={per_batch} dW_out={dW_out} want_dW0={want_dW0}")
+        f"inner{inner} ascent{ascent} momentum={momentum} per_batch={per_batch} dW_out={dW_out} want_dW0={want_dW0} "
+        f"last={last}")
     (q, k, v, eta, W0), (hq, hk, hv, he, W1, W3, W2) = full_ttt_inputs(seed, B, H, N, d, m, bf16)
     if per_batch:
         Ws = [np.zeros((B, H) + w.shape[1:], np.float32) for w in (W1, W3, W2)]
@@ -48,9 +49,10 @@ def run(seed, B, H, N, d, m, chunk, mask, bf16, rule=O.UPD_GD_L2, flags=None, in
     dt = torch.bfloat16 if bf16 else torch.float32
     got = T.ttt_backward(q, k, v, eta, W0, dev(dO, dt), chunk, mask, m_h=m,
                          dW_out=None if dWo is None else dev(pack(*dWo)), want_dW0=want_dW0, update_chunks=flags,
-                         inner_steps=inner, ascent=ascent, momentum=momentum, update_rule=rule, last_layer_only=False)
+                         inner_steps=inner, ascent=ascent, momentum=momentum, update_rule=rule, last_layer_only=last)
     torch.cuda.synchronize()
-    ref = O.ttt_backward_ref(hq, hk, hv, he, W1, W3, W2, chunk, mask, dO, dWo, flags, inner, ascent, momentum, rule)
+    ref = O.ttt_backward_ref(hq, hk, hv, he, W1, W3, W2, chunk, mask, dO, dWo, flags, inner, ascent, momentum, rule,
+                             last)
     tol = TOL[bf16]
     if N == 0:
         for g, r in zip(got[:4], ref[:4]):
@@ -99,6 +101,25 @@ def test_strided_inner_ascent(flags, inner, ascent, bf16):
                                                  (O.MASK_UPDATE_THEN_APPLY, O.UPD_GD, 2, 0.5)])
 def test_momentum(mask, rule, inner, mom, bf16):
     run(4, 1, 2, 308, 64, 160, 96, mask, bf16, rule=rule, inner=inner, momentum=mom)
+
+
+MUON_CASES = [
+    # mask, rule, strided flags, inner steps, ascent, momentum, W2 alone
+    (O.MASK_APPLY_THEN_UPDATE, O.UPD_MUON_L2, None, 1, False, 0.9, False),
+    (O.MASK_UPDATE_THEN_APPLY, O.UPD_MUON, None, 2, True, 0.0, False),
+    (O.MASK_STRIDED, O.UPD_MUON_L2, [0, 1, 1, 0], 1, False, 0.5, False),
+    (O.MASK_APPLY_THEN_UPDATE, O.UPD_MUON, None, 1, False, 0.9, True),
+    (O.MASK_UPDATE_THEN_APPLY, O.UPD_MUON_L2, None, 1, False, 0.9, True),
+]
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("mask,rule,flags,inner,ascent,mom,last", MUON_CASES)
+def test_muon(mask, rule, flags, inner, ascent, mom, last, bf16):
+    # Newton-Schulz walked back in fp32 on every update (five steps); m = 160 > d = 64 makes W1, W3
+    # tall and W2 wide
+    run(14, 1, 2, 308, 64, 160, 96, mask, bf16, rule=rule, flags=flags, inner=inner, ascent=ascent, momentum=mom,
+        last=last)
 
 
 @pytest.mark.parametrize("bf16", [False, True])
