@@ -603,7 +603,27 @@ def main():
             "mfma_frac": round(fflops / (msf * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
             "over_forward": round(msf / ms, 2), "training_step_ms": round(msf + ms, 3),
             "workspace_GB": round(wsf.numel() / 1e9, 2), "kernels_ms": fk}
-        del dOl, wsg, wsf
+        del wsf
+        # the Muon + momentum layer's backward (Newton-Schulz walked back in fp32 on every update)
+        print("[bench] extras: Muon + momentum backward, all weights learning", file=sys.stderr, flush=True)
+        Dm_, _ = T.ttt_desc(B, H, N, d, m, chunk, C.TTT_BF16, C.MASK_APPLY_THEN_UPDATE, C.UPD_MUON_L2, 5, 0.9)
+        wsm = torch.empty(T.ttt_backward_workspace_bytes(Dm_), dtype=torch.uint8, device="cuda")
+        mbwd = lambda: T.ttt_backward(q, k, v, eta, W0, dOl, chunk, C.MASK_APPLY_THEN_UPDATE, m_h=m,  # noqa: E731
+                                      update_rule=C.UPD_MUON_L2, momentum=0.9, last_layer_only=False, workspace=wsm)
+        msm = time_calls(torch, mbwd, 1, 1)
+        C.profile_select(None)
+        C.profile_enable(True)
+        C.profile_read()
+        mbwd()
+        torch.cuda.synchronize()
+        mk = {kn: round(t, 3) for kn, (t, n) in C.profile_read().items() if n}
+        C.profile_enable(False)
+        extras["lact_lm_muon_momentum_backward"] = {
+            "workload": f"B{B} H{H} N{N} d{d} m{m} chunk {chunk} bf16, apply-then-update, L2-Normalize(W - Muon(M)), "
+                        "M <- 0.9 M + g, 5 NS steps, all three weights learning: gradients of q, k, v, eta and W0",
+            "ms_per_call": round(msm, 3), "tokens_per_s": round(tokens / (msm * 1e-3)),
+            "workspace_GB": round(wsm.numel() / 1e9, 2), "kernels_ms": mk}
+        del dOl, wsg, wsm
         # Variant 2 of the paper's ablation: only W2 learns, momentum 0.9, per-token eta and Muon (5
         # Newton-Schulz steps) kept, no weight norm; chunk recurrence against the parallel form
         print("[bench] extras: Variant 2 (last layer, Muon + momentum), recurrence and parallel form",

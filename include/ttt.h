@@ -196,28 +196,32 @@ ttt_status ttt_forward_noalloc(const ttt_desc* desc, const void* q, const void* 
  * (linattn_backward_workspace_bytes); with TTT_UPD_GD_L2 also W2 after every step of every chunk in
  * fp32, and its row norms.  last_layer_only = 0: the forward's own workspace (ttt_workspace_bytes
  * without Muon), the weights before every update and after the last (fp32, 12 d_h m_h bytes per
- * scan and update), with TTT_UPD_GD_L2 every update's row norms, the running weight and momentum
+ * scan and update), with the norm every update's row norms, the running weight and momentum
  * gradients, the contraction operands of one update, and per-chunk intermediates (about
- * 14 m_h io-dtype elements and 12 m_h fp32 scratch bytes per token of one chunk and scan, plus
- * 3 m_h elements per token of the longest run of chunks that read one set of weights).
+ * 14 m_h io-dtype elements per token of one chunk and scan, plus 12 m_h fp32 scratch bytes in fp32,
+ * and 3 m_h elements per token of the longest run of chunks that read one set of weights); Muon
+ * adds each update's U (12 d_h m_h bytes per scan and update) and one update's fp32 Newton-Schulz
+ * iterates and Gram matrices.
  */
 ttt_status ttt_backward_workspace_bytes(const ttt_desc* desc, size_t* bytes);
 
 /*
- * Backward of ttt_forward for rule TTT_UPD_GD or TTT_UPD_GD_L2 with chunk_rates 0 (else
- * TTT_ERR_UNSUPPORTED); inner_steps, ascent, momentum, the chunked masks and w0_per_batch are as for
- * the forward.
+ * Backward of ttt_forward for any rule with chunk_rates 0 (else TTT_ERR_UNSUPPORTED); inner_steps,
+ * ascent, momentum, ns_iters, the chunked masks and w0_per_batch are as for the forward.  A
+ * recurrence of more than 65536 updates (chunks x inner steps) is TTT_ERR_UNSUPPORTED.
  *
- * last_layer_only = 0 (all three weights learning, parallel_form 0): the reverse of the chunk
- * recurrence (notes Eqs. (2)-(5), section 1.1): the forward runs again and records the weights
- * before every update; then, from the last update back, the gradient of an update's output weights
- * goes through the row norm's transpose, the step W - U, the momentum (M <- momentum M + g, which
- * starts from zero) and the chunk gradient g = grad_W sum eta L(f_W(k), v), whose own derivative in
- * W, k, v and eta (SiLU'' included) carries it on; the queries that read a set of weights add the
- * gradient of their outputs.
+ * last_layer_only = 0 (all three weights learning, parallel_form 0), or a Muon rule: the reverse of
+ * the chunk recurrence (notes Eqs. (2)-(6), section 1.1): the forward runs again and records the
+ * weights before every update (and, with Muon, each update's U); then, from the last update back,
+ * the gradient of an update's output weights goes through the row norm's transpose, the step
+ * W - U or W - Muon(U) (Newton-Schulz walked back from its iterates, ns_iters as in the forward),
+ * the momentum (M <- momentum M + g, which starts from zero) and the chunk gradient
+ * g = grad_W sum eta L(f_W(k), v), whose own derivative in W, k, v and eta (SiLU'' included)
+ * carries it on; the queries that read a set of weights add the gradient of their outputs.  With
+ * last_layer_only (Muon) W1 and W3 stay frozen.
  *
- * last_layer_only = 1 (the layer whose inner loop trains W2 alone; parallel_form is ignored, both
- * forms compute the same layer).  With W1 and W3
+ * last_layer_only = 1 with TTT_UPD_GD or TTT_UPD_GD_L2 (the layer whose inner loop trains W2
+ * alone; parallel_form is ignored, both forms compute the same layer).  With W1 and W3
  * frozen, phi(x) = SiLU(W1 x) * (W3 x) is fixed and W2 is the state of chunked linear attention with
  * queries phi(q), keys phi(k) and values v: each of an updating chunk's max(inner_steps, 1) steps
  * adds u = (ascent ? -1 : 1) * sum eta v phi(k)^T to W2, directly or, with momentum, through
@@ -242,8 +246,8 @@ ttt_status ttt_backward_workspace_bytes(const ttt_desc* desc, size_t* bytes);
  * io dtype with fp32 accumulation (bf16: phi, dA | dC, W1 | W3 and the linear-attention states and
  * state gradients are rounded to bf16 as contraction operands; the states are summed in fp32; with
  * all weights learning the weights and their gradients are carried in fp32 and rounded to bf16 as
- * operands, and so are the per-token intermediates), and every sum is taken in a fixed order, so
- * results do not depend on scheduling.
+ * operands, and so are the per-token intermediates; Muon's walk back runs in fp32), and every sum is
+ * taken in a fixed order, so results do not depend on scheduling.
  */
 ttt_status ttt_backward(const ttt_desc* desc, const void* q, const void* k, const void* v,
                         const float* eta, const float* W0, const void* dO, const float* dW_out,

@@ -132,6 +132,10 @@ def test_linear_attention_and_backwards_replay():
         C.check(st)
 
     replay_matches_eager("ttt_backward, all weights", fbwd, fouts)
+    # and through Muon (Newton-Schulz walked back on every update)
+    Df, _ = T.ttt_desc(1, 2, 308, 64, 160, 96, C.TTT_BF16, O.MASK_APPLY_THEN_UPDATE, C.UPD_MUON_L2, 5, 0.9)
+    wsf = torch.empty(max(1, T.ttt_backward_workspace_bytes(Df)), dtype=torch.uint8, device="cuda")
+    replay_matches_eager("ttt_backward, Muon", fbwd, fouts)
     # sliding-window attention
     Ds = C.SwaDesc(1, 2, 308, 64, 96, C.TTT_BF16)
     wss = torch.empty(max(1, T.swa_workspace_bytes(Ds)), dtype=torch.uint8, device="cuda")
