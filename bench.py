@@ -595,6 +595,23 @@ def main():
         # tiles (6 d m), dk (8 d m), dv (4 d m), dq (4 d m) and the weight gradients over keys and
         # queries (12 d m)
         fflops = tokens * H * 58 * d * m
+        # the training pair: the forward keeps a record, the backward reads it instead of running the
+        # forward again
+        rbytes, rws = T.ttt_record_bytes(Df)
+        rec = torch.empty(rbytes, dtype=torch.uint8, device="cuda")
+        wsr = torch.empty(max(1, rws), dtype=torch.uint8, device="cuda")
+        nbr = ctypes.c_size_t(0)
+        C.check(C.lib().ttt_backward_record_workspace_bytes(ctypes.byref(Df), ctypes.byref(nbr)))
+        wsb = torch.empty(nbr.value, dtype=torch.uint8, device="cuda")
+
+        def train_step():
+            T.ttt_forward_record(q, k, v, eta, W0, chunk, C.MASK_APPLY_THEN_UPDATE, C.UPD_GD_L2, m_h=m, out=o,
+                                 record=rec, workspace=wsr)
+            T.ttt_backward(q, k, v, eta, W0, dOl, chunk, C.MASK_APPLY_THEN_UPDATE, m_h=m, update_rule=C.UPD_GD_L2,
+                           last_layer_only=False, record=rec, workspace=wsb)
+
+        mst = time_calls(torch, train_step, st, 1)
+        del rec, wsr, wsb
         extras["lact_lm_gd_l2_backward"] = {
             "workload": f"B{B} H{H} N{N} d{d} m{m} chunk {chunk} bf16, apply-then-update, GD + L2 with all three "
                         "weights learning: gradients of q, k, v, eta and the per-head W0 from dO",
@@ -602,6 +619,7 @@ def main():
             "algorithmic_tflop": round(fflops / 1e12, 3),
             "mfma_frac": round(fflops / (msf * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
             "over_forward": round(msf / ms, 2), "training_step_ms": round(msf + ms, 3),
+            "training_step_with_record_ms": round(mst, 3),
             "workspace_GB": round(wsf.numel() / 1e9, 2), "kernels_ms": fk}
         del wsf
         # the Muon + momentum layer's backward (Newton-Schulz walked back in fp32 on every update)

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define TTT_ABI_VERSION 6
+#define TTT_ABI_VERSION 7
 
 typedef enum {
     TTT_OK = 0,
@@ -253,6 +253,44 @@ ttt_status ttt_backward(const ttt_desc* desc, const void* q, const void* k, cons
                         const float* eta, const float* W0, const void* dO, const float* dW_out,
                         void* dq, void* dk, void* dv, float* deta, float* dW0,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The training pair for the backward of the recurrence (the descriptors ttt_backward walks back:
+ * last_layer_only = 0, or a Muon rule; chunk_rates 0, at most 65536 updates).  A training step
+ * runs ttt_forward_record, which writes o and W_out as ttt_forward does (momentum from zero, its
+ * final value not returned) and keeps a record of the recurrence: the weights before every update
+ * and after the last (fp32), with the L2 rules every update's row norms, with Muon every update's
+ * Newton-Schulz input; then ttt_backward_record, which reads the record instead of running the
+ * forward again.  Results are those of ttt_backward, bit for bit.  The record is opaque device
+ * memory; its content is valid for the descriptor and inputs of the forward that wrote it.
+ *
+ * ttt_record_bytes: the record's size and the workspace ttt_forward_record needs.  Descriptors
+ * outside the pair's scope are TTT_ERR_UNSUPPORTED.
+ */
+ttt_status ttt_record_bytes(const ttt_desc* desc, size_t* record_bytes, size_t* workspace_bytes);
+
+/*
+ * The forward with a record.  Arguments as for ttt_forward (no momentum state: it starts from zero),
+ * plus record (device, 256-byte aligned, at least record_bytes from ttt_record_bytes;
+ * TTT_ERR_WORKSPACE if record_bytes is smaller).  No output, the record or the workspace may
+ * overlap an input or each other.
+ */
+ttt_status ttt_forward_record(const ttt_desc* desc, const void* q, const void* k, const void* v,
+                              const float* eta, const float* W0, void* o, float* W_out, void* record,
+                              size_t record_bytes, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Device workspace that ttt_backward_record needs, in bytes (ttt_backward's without the record and
+ * the forward's own workspace). */
+ttt_status ttt_backward_record_workspace_bytes(const ttt_desc* desc, size_t* bytes);
+
+/*
+ * ttt_backward from a record that ttt_forward_record wrote with the same descriptor and inputs: q,
+ * k, v, eta, dO, dW_out and the outputs as for ttt_backward; W0 is not read (the record holds it).
+ */
+ttt_status ttt_backward_record(const ttt_desc* desc, const void* q, const void* k, const void* v,
+                               const float* eta, const void* record, size_t record_bytes, const void* dO,
+                               const float* dW_out, void* dq, void* dk, void* dv, float* deta, float* dW0,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Device workspace that linattn_forward needs, in bytes.  Zero when the call runs the sequential

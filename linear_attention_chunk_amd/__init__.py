@@ -15,7 +15,7 @@ def __getattr__(name):
     if name in ("ttt_forward", "ttt_forward_noalloc", "linattn_forward", "pack_weights", "unpack_weights", "ttt_desc", "linattn_desc",
                 "ttt_workspace_bytes", "linattn_workspace_bytes", "swa_forward", "swa_workspace_bytes",
                 "linattn_backward", "linattn_backward_workspace_bytes", "ttt_backward",
-                "ttt_backward_workspace_bytes"):
+                "ttt_backward_workspace_bytes", "ttt_forward_record", "ttt_record_bytes"):
         from . import api
         return getattr(api, name)
     raise AttributeError(name)

@@ -20,6 +20,7 @@ UPD_GD, UPD_GD_L2, UPD_MUON_L2, UPD_MUON = range(4)
 EXPORTS = (
     "ttt_abi_version", "ttt_status_string", "ttt_last_error",
     "ttt_workspace_bytes", "ttt_forward", "ttt_forward_noalloc", "ttt_backward_workspace_bytes", "ttt_backward",
+    "ttt_record_bytes", "ttt_forward_record", "ttt_backward_record_workspace_bytes", "ttt_backward_record",
     "linattn_workspace_bytes", "linattn_forward", "linattn_backward_workspace_bytes", "linattn_backward",
     "swa_workspace_bytes", "swa_forward",
     "ttt_profile_enable", "ttt_profile_select", "ttt_profile_read", "ttt_profile_kernel_name",
@@ -89,6 +90,15 @@ def lib() -> ctypes.CDLL:
     L.ttt_backward_workspace_bytes.argtypes = [POINTER(TttDesc), POINTER(c_size_t)]
     L.ttt_backward.restype = c_int32
     L.ttt_backward.argtypes = [POINTER(TttDesc)] + [c_void_p] * 13 + [c_size_t, c_void_p]
+    L.ttt_record_bytes.restype = c_int32
+    L.ttt_record_bytes.argtypes = [POINTER(TttDesc), POINTER(c_size_t), POINTER(c_size_t)]
+    L.ttt_forward_record.restype = c_int32
+    L.ttt_forward_record.argtypes = [POINTER(TttDesc)] + [c_void_p] * 8 + [c_size_t, c_void_p, c_size_t, c_void_p]
+    L.ttt_backward_record_workspace_bytes.restype = c_int32
+    L.ttt_backward_record_workspace_bytes.argtypes = [POINTER(TttDesc), POINTER(c_size_t)]
+    L.ttt_backward_record.restype = c_int32
+    L.ttt_backward_record.argtypes = [POINTER(TttDesc)] + [c_void_p] * 5 + [c_size_t] + [c_void_p] * 8 + \
+        [c_size_t, c_void_p]
     L.linattn_workspace_bytes.restype = c_int32
     L.linattn_workspace_bytes.argtypes = [POINTER(LinattnDesc), POINTER(c_size_t)]
     L.linattn_forward.restype = c_int32

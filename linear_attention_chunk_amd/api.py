@@ -52,6 +52,13 @@ def _workspace(ws: Optional[torch.Tensor], nbytes: int, device) -> Optional[torc
     return ws
 
 
+def _need_bytes(t: torch.Tensor, name: str, nbytes: int, device):
+    """A contiguous uint8 device tensor of at least nbytes (a record)."""
+    _need(t, name, torch.uint8, device)
+    if t.numel() < nbytes:
+        raise ValueError(f"{name} holds {t.numel()} bytes, the call needs {nbytes}")
+
+
 def _flags(update_chunks, N: int, chunk: int, strided: bool, name="update_chunks"):
     """update_chunks must hold a flag for every chunk (the library reads ceil(N / chunk) of them)."""
     if update_chunks is None:
@@ -167,6 +174,36 @@ def ttt_forward(q, k, v, eta, W0, chunk: int, mask_mode: int = C.MASK_APPLY_THEN
     return o, W_out
 
 
+def ttt_record_bytes(desc: C.TttDesc):
+    """(record bytes, workspace bytes) of ttt_forward_record for this descriptor."""
+    r, w = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    C.check(C.lib().ttt_record_bytes(ctypes.byref(desc), ctypes.byref(r), ctypes.byref(w)))
+    return r.value, w.value
+
+
+def ttt_forward_record(q, k, v, eta, W0, chunk: int, mask_mode: int = C.MASK_APPLY_THEN_UPDATE,
+                       update_rule: int = C.UPD_GD_L2, *, m_h: Optional[int] = None, ns_iters: int = 5,
+                       momentum: float = 0.0, last_layer_only: bool = False, update_chunks=None,
+                       inner_steps: int = 1, ascent: bool = False, out: Optional[torch.Tensor] = None,
+                       record: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None):
+    """The training forward through ttt_forward_record of libttt.so: o and W_out as ttt_forward
+    returns them (momentum from zero), and the record that ttt_backward(..., record=) reads instead
+    of running the forward again (a uint8 device tensor, allocated here unless given).
+    Returns (o, W_out, record)."""
+    D, keep, o, W_out = _ttt_prepare(q, k, v, eta, W0, chunk, mask_mode, update_rule, m_h, ns_iters, momentum,
+                                     last_layer_only, update_chunks, None, True, out, inner_steps, ascent, False)
+    rbytes, wbytes = ttt_record_bytes(D)
+    record = _workspace(record, rbytes, q.device)
+    workspace = _workspace(workspace, wbytes, q.device)
+    st = C.lib().ttt_forward_record(ctypes.byref(D), _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(W0), _ptr(o),
+                                    _ptr(W_out), _ptr(record), ctypes.c_size_t(0 if record is None else record.numel()),
+                                    _ptr(workspace), ctypes.c_size_t(0 if workspace is None else workspace.numel()),
+                                    _stream_handle(stream))
+    del keep
+    C.check(st)
+    return o, W_out, record
+
+
 def ttt_forward_noalloc(q, k, v, eta, W0, chunk: int, mask_mode: int = C.MASK_APPLY_THEN_UPDATE,
                         update_rule: int = C.UPD_GD_L2, *, m_h: Optional[int] = None, ns_iters: int = 5,
                         momentum: float = 0.0, last_layer_only: bool = False, update_chunks=None,
@@ -199,10 +236,12 @@ def ttt_backward(q, k, v, eta, W0, dO, chunk: int, mask_mode: int = C.MASK_APPLY
                  m_h: Optional[int] = None, dW_out: Optional[torch.Tensor] = None, want_dW0: bool = True,
                  update_chunks=None, inner_steps: int = 1, ascent: bool = False, momentum: float = 0.0,
                  update_rule: int = C.UPD_GD, last_layer_only: bool = True, ns_iters: int = 5,
-                 workspace: Optional[torch.Tensor] = None, stream=None):
+                 record: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None):
     """Backward of ttt_forward (momentum as a forward call without M, i.e. from zero), through
     ttt_backward of libttt.so: with last_layer_only the layer whose inner loop trains W2 alone,
     otherwise the recurrence with all three weights learning; ns_iters as for ttt_forward (Muon).
+    record: the record ttt_forward_record wrote for the same inputs (through ttt_backward_record:
+    the forward is not run again; W0 is then not read).
 
     dO [B, H, N, d] is the gradient of o, dW_out ([B, H, 3*d*m] fp32 or None) that of W_out.
     Returns (dq, dk, dv, deta, dW0 or None); dW0 has W0's shape (per-head weights sum over the
@@ -229,14 +268,27 @@ def ttt_backward(q, k, v, eta, W0, dO, chunk: int, mask_mode: int = C.MASK_APPLY
     _flags(update_chunks, N, chunk, mask_mode == C.MASK_STRIDED)
     D, keep = ttt_desc(B, H, N, d, m_h, chunk, _DT[q.dtype], mask_mode, update_rule, ns_iters, momentum,
                        bool(last_layer_only), per_batch, update_chunks, inner_steps, ascent)
-    nbytes = ttt_backward_workspace_bytes(D)
+    if record is not None:
+        rbytes, _ = ttt_record_bytes(D)
+        _need_bytes(record, "record", rbytes, dev)
+        n = ctypes.c_size_t(0)
+        C.check(C.lib().ttt_backward_record_workspace_bytes(ctypes.byref(D), ctypes.byref(n)))
+        nbytes = n.value
+    else:
+        nbytes = ttt_backward_workspace_bytes(D)
     workspace = _workspace(workspace, nbytes, dev)
     dq, dkt, dvt = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     deta = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     dW0 = torch.empty_like(W0) if want_dW0 else None
-    st = C.lib().ttt_backward(ctypes.byref(D), _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(W0), _ptr(dO),
-                              _ptr(dW_out), _ptr(dq), _ptr(dkt), _ptr(dvt), _ptr(deta), _ptr(dW0), _ptr(workspace),
-                              ctypes.c_size_t(0 if workspace is None else workspace.numel()), _stream_handle(stream))
+    wsn = ctypes.c_size_t(0 if workspace is None else workspace.numel())
+    if record is not None:
+        st = C.lib().ttt_backward_record(ctypes.byref(D), _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(record),
+                                         ctypes.c_size_t(record.numel()), _ptr(dO), _ptr(dW_out), _ptr(dq), _ptr(dkt),
+                                         _ptr(dvt), _ptr(deta), _ptr(dW0), _ptr(workspace), wsn, _stream_handle(stream))
+    else:
+        st = C.lib().ttt_backward(ctypes.byref(D), _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(W0), _ptr(dO),
+                                  _ptr(dW_out), _ptr(dq), _ptr(dkt), _ptr(dvt), _ptr(deta), _ptr(dW0), _ptr(workspace),
+                                  wsn, _stream_handle(stream))
     del keep
     C.check(st)
     return dq, dkt, dvt, deta, dW0

@@ -152,12 +152,13 @@ ttt_status lin_chunked_bwd(const linattn_desc& D, const uint32_t (&flags)[32], c
 
 // The forward recurrence run for its record: the weights before each update at hist + i S 3 d m
 // (i = 0 .. updates, the last one the final weights) and, with the norm, each update's row norms
-// (|W - U| of the 2m + d rows) at nrm + i S (2m + d); no output.  ws: ttt_history_ws_bytes.
-// With Muon each update's U (the input of Newton-Schulz, fp32) goes to urec + i S 3 d m.
+// (|W - U| of the 2m + d rows) at nrm + i S (2m + d).  ws: ttt_history_ws_bytes.
+// With Muon each update's U (the input of Newton-Schulz, fp32) goes to urec + i S 3 d m.  o and
+// W_out are the forward's outputs (null: not written; with o null nothing is applied).
 size_t ttt_history_ws_bytes(const ttt_desc& D);
 template <typename T>
 ttt_status ttt_run_history(const ttt_desc& D, const T* q, const T* k, const T* v, const float* eta, const float* W0,
-                           float* hist, float* nrm, float* urec, char* ws, hipStream_t st);
+                           T* o, float* W_out, float* hist, float* nrm, float* urec, char* ws, hipStream_t st);
 // Newton-Schulz iterates of U for the backward (fp32): X_k at X + k S 3 d m (k < max(ns_iters, 1)),
 // the Gram matrix of X_k at P + k S 3 p^2 (k < ns_iters), the partial sums of U^2 in part
 // (S x 3 x ceil(d m / 4096)); the learned matrices only (W2 alone with last_layer_only).
@@ -166,11 +167,19 @@ ttt_status ns_iterates(const ttt_desc& D, const float* U, float* part, float* X,
 // The backward of the recurrence with all three weights learning (GD or GD + L2, momentum): the
 // descriptor checks beyond validate_ttt_desc, the workspace, and the run (arguments as for
 // ttt_backward, already checked).
+// With a record (from run_forward_record) the forward is not run again and the workspace is
+// full_bwd_ws_bytes(D, false); W0 is then not read.
 ttt_status validate_full_bwd(const ttt_desc* D);
-size_t full_bwd_ws_bytes(const ttt_desc& D);
+size_t full_bwd_ws_bytes(const ttt_desc& D, bool own_record = true);
 template <typename T>
 ttt_status run_full_backward(const ttt_desc& D, const T* q, const T* k, const T* v, const float* eta, const float* W0,
                              const T* dO, const float* dWo, T* dq, T* dk, T* dv, float* deta, float* dW0, char* ws,
-                             hipStream_t st);
+                             hipStream_t st, char* record = nullptr);
+// The training forward: o and W_out as ttt_forward writes them (momentum from zero), and the record
+// the backward of the recurrence reads (full_bwd_record_bytes); workspace ttt_history_ws_bytes.
+size_t full_bwd_record_bytes(const ttt_desc& D);
+template <typename T>
+ttt_status run_forward_record(const ttt_desc& D, const T* q, const T* k, const T* v, const float* eta, const float* W0,
+                              T* o, float* W_out, char* record, char* ws, hipStream_t st);
 
 }  // namespace ttt

@@ -398,23 +398,24 @@ extern "C" ttt_status ttt_backward_workspace_bytes(const ttt_desc* desc, size_t*
     return TTT_OK;
 }
 
-extern "C" ttt_status ttt_backward(const ttt_desc* desc, const void* q, const void* k, const void* v, const float* eta,
-                                   const float* W0, const void* dO, const float* dW_out, void* dq, void* dk, void* dv,
-                                   float* deta, float* dW0, void* workspace, size_t workspace_bytes, void* stream) {
-    clear_error();
-    ttt_status rc = validate_bwd(desc);
-    if (rc != TTT_OK) return rc;
-    const ttt_desc& D = *desc;
+namespace {
+// The argument checks of the backward entry points: required and aligned pointers, no output over
+// an input or another output, a workspace of `need` bytes, and every buffer inside a HIP allocation.
+// W0 or the record (rec, rec_bytes) is the weights' source.
+ttt_status check_bwd_args(const ttt_desc& D, const void* q, const void* k, const void* v, const float* eta,
+                          const float* W0, const void* rec, size_t rec_bytes, const void* dO, const float* dW_out,
+                          void* dq, void* dk, void* dv, float* deta, float* dW0, void* workspace,
+                          size_t workspace_bytes, size_t need) {
     const int64_t S = (int64_t)D.B * D.H;
-    if (S == 0) return TTT_OK;
     const bool t = D.N > 0;
-    if (!W0) return fail(TTT_ERR_INVALID_ARGUMENT, "W0 is NULL");
+    if (!W0 && !rec) return fail(TTT_ERR_INVALID_ARGUMENT, rec_bytes ? "record is NULL" : "W0 is NULL");
     if (t && (!q || !k || !v || !eta || !dO || !dq || !dk || !dv || !deta))
         return fail(TTT_ERR_INVALID_ARGUMENT, "q, k, v, eta, dO, dq, dk, dv and deta are required");
     const void* p16[] = {q, k, v, dO, dq, dk, dv, W0, dW_out, dW0};
     for (const void* p : p16)
         if (p && !aligned(p, 16))
             return fail(TTT_ERR_INVALID_ARGUMENT, "q, k, v, dO, dq, dk, dv, W0, dW_out, dW0 must be 16-byte aligned");
+    if (rec && !aligned(rec, 256)) return fail(TTT_ERR_INVALID_ARGUMENT, "record must be 256-byte aligned");
     const void* p4[] = {eta, deta};
     for (const void* p : p4)
         if (p && !aligned(p, 4)) return fail(TTT_ERR_INVALID_ARGUMENT, "eta and deta must be 4-byte aligned");
@@ -423,8 +424,8 @@ extern "C" ttt_status ttt_backward(const ttt_desc* desc, const void* q, const vo
     const size_t xb = t ? (size_t)S * D.N * D.d_h * es : 0, eb = t ? (size_t)S * D.N * 4 : 0;
     const size_t wb = (size_t)(D.w0_per_batch ? S : D.H) * dm3 * 4, wob = (size_t)S * dm3 * 4;
     const struct { const void* p; size_t n; const char* name; } ins[] = {
-        {q, xb, "q"}, {k, xb, "k"}, {v, xb, "v"}, {eta, eb, "eta"}, {W0, wb, "W0"}, {dO, xb, "dO"},
-        {dW_out, wob, "dW_out"}};
+        {q, xb, "q"}, {k, xb, "k"}, {v, xb, "v"}, {eta, eb, "eta"}, {W0, wb, "W0"}, {rec, rec_bytes, "record"},
+        {dO, xb, "dO"}, {dW_out, wob, "dW_out"}};
     const struct { const void* p; size_t n; const char* name; } outs[] = {
         {dq, xb, "dq"}, {dk, xb, "dk"}, {dv, xb, "dv"}, {deta, eb, "deta"}, {dW0, wb, "dW0"}};
     for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
@@ -435,17 +436,32 @@ extern "C" ttt_status ttt_backward(const ttt_desc* desc, const void* q, const vo
             if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n))
                 return fail(TTT_ERR_INVALID_ARGUMENT, "%s overlaps %s", outs[i].name, outs[j].name);
     }
-    const bool full = uses_full(D);
-    const BLayout L = full ? BLayout{} : make_blayout(D, dW0 != nullptr);
-    const size_t need = full ? full_bwd_ws_bytes(D) : L.total;
     if (need && (!workspace || workspace_bytes < need))
         return fail(TTT_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
     if (need && !aligned(workspace, 256)) return fail(TTT_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    ttt_status rc;
     for (const auto& b : ins)
         if ((rc = check_buffer(b.p, b.n, b.name)) != TTT_OK) return rc;
     for (const auto& b : outs)
         if ((rc = check_buffer(b.p, b.n, b.name)) != TTT_OK) return rc;
-    if ((rc = check_buffer(workspace, need, "workspace")) != TTT_OK) return rc;
+    return check_buffer(workspace, need, "workspace");
+}
+}  // namespace
+
+extern "C" ttt_status ttt_backward(const ttt_desc* desc, const void* q, const void* k, const void* v, const float* eta,
+                                   const float* W0, const void* dO, const float* dW_out, void* dq, void* dk, void* dv,
+                                   float* deta, float* dW0, void* workspace, size_t workspace_bytes, void* stream) {
+    clear_error();
+    ttt_status rc = validate_bwd(desc);
+    if (rc != TTT_OK) return rc;
+    const ttt_desc& D = *desc;
+    if ((int64_t)D.B * D.H == 0) return TTT_OK;
+    const bool full = uses_full(D);
+    const BLayout L = full ? BLayout{} : make_blayout(D, dW0 != nullptr);
+    const size_t need = full ? full_bwd_ws_bytes(D) : L.total;
+    if ((rc = check_bwd_args(D, q, k, v, eta, W0, nullptr, 0, dO, dW_out, dq, dk, dv, deta, dW0, workspace,
+                             workspace_bytes, need)) != TTT_OK)
+        return rc;
     hipStream_t st = (hipStream_t)stream;
     if (full) {
         if (D.io_dtype == TTT_BF16)
@@ -462,4 +478,112 @@ extern "C" ttt_status ttt_backward(const ttt_desc* desc, const void* q, const vo
                                       dW0, (char*)workspace, st);
     return run_backward<float>(D, L, (const float*)q, (const float*)k, (const float*)v, eta, W0, (const float*)dO,
                                dW_out, (float*)dq, (float*)dk, (float*)dv, deta, dW0, (char*)workspace, st);
+}
+
+// The training pair: the forward that keeps a record, and the backward that reads it.
+static ttt_status validate_record(const ttt_desc* desc) {
+    ttt_status rc = validate_ttt_desc(desc);
+    if (rc != TTT_OK) return rc;
+    if (!uses_full(*desc))
+        return fail(TTT_ERR_UNSUPPORTED,
+                    "the record serves the backward of the recurrence (all weights learning, or Muon); the layer "
+                    "whose inner loop trains W2 alone by GD takes ttt_backward");
+    return validate_full_bwd(desc);
+}
+
+extern "C" ttt_status ttt_record_bytes(const ttt_desc* desc, size_t* record_bytes, size_t* workspace_bytes) {
+    clear_error();
+    ttt_status rc = validate_record(desc);
+    if (rc != TTT_OK) return rc;
+    if (!record_bytes || !workspace_bytes)
+        return fail(TTT_ERR_INVALID_ARGUMENT, "record_bytes and workspace_bytes are required");
+    *record_bytes = full_bwd_record_bytes(*desc);
+    *workspace_bytes = ttt_history_ws_bytes(*desc);
+    return TTT_OK;
+}
+
+extern "C" ttt_status ttt_forward_record(const ttt_desc* desc, const void* q, const void* k, const void* v,
+                                         const float* eta, const float* W0, void* o, float* W_out, void* record,
+                                         size_t record_bytes, void* workspace, size_t workspace_bytes, void* stream) {
+    clear_error();
+    ttt_status rc = validate_record(desc);
+    if (rc != TTT_OK) return rc;
+    const ttt_desc& D = *desc;
+    const int64_t S = (int64_t)D.B * D.H;
+    if (S == 0) return TTT_OK;
+    const bool t = D.N > 0;
+    if (!W0 || !record) return fail(TTT_ERR_INVALID_ARGUMENT, "W0 and record are required");
+    if (t && (!q || !k || !v || !eta || !o)) return fail(TTT_ERR_INVALID_ARGUMENT, "q, k, v, eta and o are required");
+    const void* p16[] = {q, k, v, o, W0, W_out};
+    for (const void* p : p16)
+        if (p && !aligned(p, 16)) return fail(TTT_ERR_INVALID_ARGUMENT, "q, k, v, o, W0, W_out must be 16-byte aligned");
+    if (eta && !aligned(eta, 4)) return fail(TTT_ERR_INVALID_ARGUMENT, "eta must be 4-byte aligned");
+    if (!aligned(record, 256)) return fail(TTT_ERR_INVALID_ARGUMENT, "record must be 256-byte aligned");
+    const size_t es = D.io_dtype == TTT_BF16 ? 2 : 4;
+    const int64_t dm3 = 3 * (int64_t)D.d_h * D.m_h;
+    const size_t xb = t ? (size_t)S * D.N * D.d_h * es : 0, eb = t ? (size_t)S * D.N * 4 : 0;
+    const size_t wb = (size_t)(D.w0_per_batch ? S : D.H) * dm3 * 4, wob = (size_t)S * dm3 * 4;
+    const size_t rb = full_bwd_record_bytes(D), need = ttt_history_ws_bytes(D);
+    if (record_bytes < rb) return fail(TTT_ERR_WORKSPACE, "record of %zu bytes needed, %zu given", rb, record_bytes);
+    if (need && (!workspace || workspace_bytes < need))
+        return fail(TTT_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+    if (need && !aligned(workspace, 256)) return fail(TTT_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    const struct { const void* p; size_t n; const char* name; } ins[] = {
+        {q, xb, "q"}, {k, xb, "k"}, {v, xb, "v"}, {eta, eb, "eta"}, {W0, wb, "W0"}};
+    const struct { const void* p; size_t n; const char* name; } outs[] = {
+        {o, xb, "o"}, {W_out, wob, "W_out"}, {record, rb, "record"}, {workspace, need, "workspace"}};
+    for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+        for (const auto& in : ins)
+            if (overlaps(outs[i].p, outs[i].n, in.p, in.n))
+                return fail(TTT_ERR_INVALID_ARGUMENT, "%s overlaps the input %s", outs[i].name, in.name);
+        for (size_t j = 0; j < i; ++j)
+            if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n))
+                return fail(TTT_ERR_INVALID_ARGUMENT, "%s overlaps %s", outs[i].name, outs[j].name);
+    }
+    for (const auto& b : ins)
+        if ((rc = check_buffer(b.p, b.n, b.name)) != TTT_OK) return rc;
+    for (const auto& b : outs)
+        if ((rc = check_buffer(b.p, b.n, b.name)) != TTT_OK) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    if (D.io_dtype == TTT_BF16)
+        return run_forward_record<uint16_t>(D, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, eta, W0,
+                                            (uint16_t*)o, W_out, (char*)record, (char*)workspace, st);
+    return run_forward_record<float>(D, (const float*)q, (const float*)k, (const float*)v, eta, W0, (float*)o, W_out,
+                                     (char*)record, (char*)workspace, st);
+}
+
+extern "C" ttt_status ttt_backward_record_workspace_bytes(const ttt_desc* desc, size_t* bytes) {
+    clear_error();
+    ttt_status rc = validate_record(desc);
+    if (rc != TTT_OK) return rc;
+    if (!bytes) return fail(TTT_ERR_INVALID_ARGUMENT, "bytes is NULL");
+    *bytes = full_bwd_ws_bytes(*desc, false);
+    return TTT_OK;
+}
+
+extern "C" ttt_status ttt_backward_record(const ttt_desc* desc, const void* q, const void* k, const void* v,
+                                          const float* eta, const void* record, size_t record_bytes, const void* dO,
+                                          const float* dW_out, void* dq, void* dk, void* dv, float* deta, float* dW0,
+                                          void* workspace, size_t workspace_bytes, void* stream) {
+    clear_error();
+    ttt_status rc = validate_record(desc);
+    if (rc != TTT_OK) return rc;
+    const ttt_desc& D = *desc;
+    if ((int64_t)D.B * D.H == 0) return TTT_OK;
+    const size_t rb = full_bwd_record_bytes(D);
+    if (!record) return fail(TTT_ERR_INVALID_ARGUMENT, "record is NULL");
+    if (record_bytes < rb) return fail(TTT_ERR_WORKSPACE, "record of %zu bytes needed, %zu given", rb, record_bytes);
+    if ((rc = check_bwd_args(D, q, k, v, eta, nullptr, record, rb, dO, dW_out, dq, dk, dv, deta, dW0, workspace,
+                             workspace_bytes, full_bwd_ws_bytes(D, false))) != TTT_OK)
+        return rc;
+    hipStream_t st = (hipStream_t)stream;
+    // the record is read only; the backward's own buffers are all in the workspace
+    char* rec = const_cast<char*>(reinterpret_cast<const char*>(record));
+    if (D.io_dtype == TTT_BF16)
+        return run_full_backward<uint16_t>(D, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, eta, nullptr,
+                                           (const uint16_t*)dO, dW_out, (uint16_t*)dq, (uint16_t*)dk, (uint16_t*)dv,
+                                           deta, dW0, (char*)workspace, st, rec);
+    return run_full_backward<float>(D, (const float*)q, (const float*)k, (const float*)v, eta, nullptr,
+                                    (const float*)dO, dW_out, (float*)dq, (float*)dk, (float*)dv, deta, dW0,
+                                    (char*)workspace, st, rec);
 }

@@ -838,14 +838,33 @@ static int fb_parts(int64_t tiles, int64_t total) {
     return best;
 }
 
+// The record of a forward (the weights before every update and after the last, fp32; with the norm
+// every update's row norms; with Muon every update's U), as offsets into one buffer
+struct FRecord {
+    size_t hist, nrm, urec, total;
+};
+
+static FRecord record_layout(const ttt_desc& D, const FbPlan& P) {
+    FRecord R{};
+    const int64_t S = (int64_t)D.B * D.H, d = D.d_h, m = D.m_h, dm = d * m;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { const size_t o = off; off += align256(bytes); return o; };
+    R.hist = take((size_t)(P.T + 1) * S * 3 * dm * 4);
+    if (D.rule == TTT_UPD_GD_L2 || D.rule == TTT_UPD_MUON_L2) R.nrm = take((size_t)P.T * S * (2 * m + d) * 4);
+    if (D.rule == TTT_UPD_MUON || D.rule == TTT_UPD_MUON_L2) R.urec = take((size_t)P.T * S * 3 * dm * 4);
+    R.total = off;
+    return R;
+}
+
 struct FLayout {
-    size_t fwd, hist, nrm, dW, dM, G, op, acp, qa, qh, pk, pv, pe, acck, accv, epart, part, total;
-    size_t urec, nsx, nsp, nsq, gb, pu, pgu;  // Muon: U of every update, iterates, Grams, Q + Q^T, G's pair, sums
+    size_t fwd, rec, dW, dM, G, op, acp, qa, qh, pk, pv, pe, acck, accv, epart, part, total;
+    size_t nsx, nsp, nsq, gb, pu, pgu;  // Muon: iterates, Grams, Q + Q^T, G's pair, partial sums
     int nparts, nK;
     int64_t bcap, qcap;
 };
 
-static FLayout make_flayout(const ttt_desc& D, const FbPlan& P) {
+// own_record: the workspace holds the forward's workspace and the record (else the caller's record)
+static FLayout make_flayout(const ttt_desc& D, const FbPlan& P, bool own_record) {
     FLayout L{};
     const int64_t S = (int64_t)D.B * D.H, d = D.d_h, m = D.m_h, dm = d * m;
     const size_t es = D.io_dtype == TTT_BF16 ? 2 : 4;
@@ -854,9 +873,10 @@ static FLayout make_flayout(const ttt_desc& D, const FbPlan& P) {
     L.nK = (int)(cdiv(L.bcap, kFbRows) * cdiv(m, kFbCols));
     size_t off = 0;
     auto take = [&](size_t bytes) { const size_t o = off; off += align256(bytes); return o; };
-    L.fwd = take(ttt_history_ws_bytes(D));
-    L.hist = take((size_t)(P.T + 1) * S * 3 * dm * 4);
-    if (D.rule == TTT_UPD_GD_L2) L.nrm = take((size_t)P.T * S * (2 * m + d) * 4);
+    if (own_record) {
+        L.fwd = take(ttt_history_ws_bytes(D));
+        L.rec = take(record_layout(D, P).total);
+    }
     L.dW = take((size_t)S * 3 * dm * 4);
     if (D.momentum != 0.0f) L.dM = take((size_t)S * 3 * dm * 4);
     L.G = take((size_t)S * 3 * dm * 4);
@@ -881,7 +901,6 @@ static FLayout make_flayout(const ttt_desc& D, const FbPlan& P) {
     L.part = take((size_t)L.nparts * S * 3 * dm * 4);
     if (D.rule == TTT_UPD_MUON || D.rule == TTT_UPD_MUON_L2) {
         const int64_t p = std::min(d, m), nblk = cdiv(dm, kNsbElems);
-        L.urec = take((size_t)P.T * S * 3 * dm * 4);
         L.nsx = take((size_t)std::max(D.ns_iters, 1) * S * 3 * dm * 4);
         L.nsp = take((size_t)std::max(D.ns_iters, 1) * S * 3 * p * p * 4);
         L.nsq = take((size_t)S * 3 * p * p * 4);
@@ -913,17 +932,18 @@ ttt_status validate_full_bwd(const ttt_desc* D) {
     return TTT_OK;
 }
 
-size_t full_bwd_ws_bytes(const ttt_desc& D) {
+size_t full_bwd_ws_bytes(const ttt_desc& D, bool own_record) {
     const FbPlan P = fb_plan(D);
-    return make_flayout(D, P).total;
+    return make_flayout(D, P, own_record).total;
 }
 
 template <typename T>
 ttt_status run_full_backward(const ttt_desc& D, const T* q, const T* k, const T* v, const float* eta, const float* W0,
                              const T* dO, const float* dWo, T* dq, T* dk, T* dv, float* deta, float* dW0, char* ws,
-                             hipStream_t st) {
+                             hipStream_t st, char* record) {
     const FbPlan P = fb_plan(D);
-    const FLayout L = make_flayout(D, P);
+    const FLayout L = make_flayout(D, P, record == nullptr);
+    const FRecord R = record_layout(D, P);
     const int S = D.B * D.H, d = D.d_h, m = D.m_h;
     const int64_t dm = (int64_t)d * m, dm3 = 3 * dm;
     const int64_t hs = (int64_t)S * dm3;  // one version of every scan's weights
@@ -932,17 +952,20 @@ ttt_status run_full_backward(const ttt_desc& D, const T* q, const T* k, const T*
     const int mat0 = D.last_layer_only ? 2 : 0, nmat = D.last_layer_only ? 1 : 3;
     const int64_t pp = std::min(d, m);
     const float sign = D.ascent ? -1.0f : 1.0f;
-    float* hist = (float*)(ws + L.hist);
-    float* nrm = norm ? (float*)(ws + L.nrm) : nullptr;
+    char* rec = record ? record : ws + L.rec;
+    float* hist = (float*)(rec + R.hist);
+    float* nrm = norm ? (float*)(rec + R.nrm) : nullptr;
     float* dW = (float*)(ws + L.dW);
     float* dM = mom ? (float*)(ws + L.dM) : nullptr;
     float* G = (float*)(ws + L.G);
     T* op = (T*)(ws + L.op);
     float* part = (float*)(ws + L.part);
     ttt_status rc;
-    // the forward's record
-    float* urec = muon ? (float*)(ws + L.urec) : nullptr;
-    if ((rc = ttt_run_history<T>(D, q, k, v, eta, W0, hist, nrm, urec, ws + L.fwd, st)) != TTT_OK) return rc;
+    // the forward's record, unless the caller brings it
+    float* urec = muon ? (float*)(rec + R.urec) : nullptr;
+    if (!record && (rc = ttt_run_history<T>(D, q, k, v, eta, W0, (T*)nullptr, nullptr, hist, nrm, urec, ws + L.fwd,
+                                            st)) != TTT_OK)
+        return rc;
     {
         ProfScope ps(PK_FB_MISC, st);
         hipLaunchKernelGGL(k_fb_init, dim3((unsigned)cdiv(hs / 4, kThreads)), dim3(kThreads), 0, st, dW, dWo, dM,
@@ -1101,9 +1124,28 @@ ttt_status run_full_backward(const ttt_desc& D, const T* q, const T* k, const T*
 
 template ttt_status run_full_backward<uint16_t>(const ttt_desc&, const uint16_t*, const uint16_t*, const uint16_t*,
                                                 const float*, const float*, const uint16_t*, const float*, uint16_t*,
-                                                uint16_t*, uint16_t*, float*, float*, char*, hipStream_t);
+                                                uint16_t*, uint16_t*, float*, float*, char*, hipStream_t, char*);
 template ttt_status run_full_backward<float>(const ttt_desc&, const float*, const float*, const float*, const float*,
                                              const float*, const float*, const float*, float*, float*, float*, float*,
-                                             float*, char*, hipStream_t);
+                                             float*, char*, hipStream_t, char*);
+
+size_t full_bwd_record_bytes(const ttt_desc& D) { return record_layout(D, fb_plan(D)).total; }
+
+template <typename T>
+ttt_status run_forward_record(const ttt_desc& D, const T* q, const T* k, const T* v, const float* eta, const float* W0,
+                              T* o, float* W_out, char* record, char* ws, hipStream_t st) {
+    const FbPlan P = fb_plan(D);
+    const FRecord R = record_layout(D, P);
+    const bool norm = D.rule == TTT_UPD_GD_L2 || D.rule == TTT_UPD_MUON_L2;
+    const bool muon = D.rule == TTT_UPD_MUON || D.rule == TTT_UPD_MUON_L2;
+    return ttt_run_history<T>(D, q, k, v, eta, W0, o, W_out, (float*)(record + R.hist),
+                              norm ? (float*)(record + R.nrm) : nullptr, muon ? (float*)(record + R.urec) : nullptr, ws,
+                              st);
+}
+template ttt_status run_forward_record<uint16_t>(const ttt_desc&, const uint16_t*, const uint16_t*, const uint16_t*,
+                                                 const float*, const float*, uint16_t*, float*, char*, char*,
+                                                 hipStream_t);
+template ttt_status run_forward_record<float>(const ttt_desc&, const float*, const float*, const float*, const float*,
+                                              const float*, float*, float*, char*, char*, hipStream_t);
 
 }  // namespace ttt

@@ -1197,7 +1197,8 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
         if (D.mask != TTT_MASK_STRIDED || D.update_chunks[step]) last_upd = step;
     // hist (the backward's record): the weights before update i go to hist + i S 3 d m, the last
     // update's result after them, with the norm each update's row norms to nrm + i S (2m + d), and
-    // with Muon each update's U (fp32) to urec + i S 3 d m; then there is no output (o is null)
+    // with Muon each update's U (fp32) to urec + i S 3 d m; W_out is then a copy of the last entry.
+    // With o null nothing is applied.
     const int64_t hstride = (int64_t)S * 3 * dm;
     int ui = 0;  // updates so far
     {  // W0 -> shadows, and the master copy only if no update follows (the first update reads W0)
@@ -1349,7 +1350,7 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
                 u.src_per_head = D.w0_per_batch ? 0 : 1;
                 w_in_master = true;
             }
-            if (final_upd && W_out) {
+            if (final_upd && W_out && !hist) {
                 u.dst = W_out;  // [B][H][3 d m], the same stride as the master copy
                 u.shadows = step < nsteps - 1;
             }
@@ -1357,8 +1358,9 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
             cur ^= 1;
         }
     }
-    if (W_out && last_upd < 0) {  // no update wrote W_out
-        hipError_t e = hipMemcpyAsync(W_out, Wf[cur], (size_t)S * 3 * dm * 4, hipMemcpyDeviceToDevice, st);
+    if (W_out && (hist || last_upd < 0)) {  // no update wrote W_out: the record's last entry, or the master copy
+        hipError_t e = hipMemcpyAsync(W_out, hist ? hist + ui * hstride : Wf[cur], (size_t)S * 3 * dm * 4,
+                                      hipMemcpyDeviceToDevice, st);
         if (e != hipSuccess) return fail(TTT_ERR_DEVICE, "copying W_out: %s", hipGetErrorString(e));
     }
     return TTT_OK;
@@ -1370,14 +1372,15 @@ size_t ttt_history_ws_bytes(const ttt_desc& D) { return make_layout(D, is_muon(D
 
 template <typename T>
 ttt_status ttt_run_history(const ttt_desc& D, const T* q, const T* k, const T* v, const float* eta, const float* W0,
-                           float* hist, float* nrm, float* urec, char* ws, hipStream_t st) {
+                           T* o, float* W_out, float* hist, float* nrm, float* urec, char* ws, hipStream_t st) {
     const Layout L = make_layout(D, is_muon(D), has_mom(D));
-    return run_ttt<T>(D, L, q, k, v, eta, W0, nullptr, nullptr, nullptr, ws, st, hist, nrm, urec);
+    return run_ttt<T>(D, L, q, k, v, eta, W0, o, W_out, nullptr, ws, st, hist, nrm, urec);
 }
 template ttt_status ttt_run_history<uint16_t>(const ttt_desc&, const uint16_t*, const uint16_t*, const uint16_t*,
-                                              const float*, const float*, float*, float*, float*, char*, hipStream_t);
+                                              const float*, const float*, uint16_t*, float*, float*, float*, float*,
+                                              char*, hipStream_t);
 template ttt_status ttt_run_history<float>(const ttt_desc&, const float*, const float*, const float*, const float*,
-                                           const float*, float*, float*, float*, char*, hipStream_t);
+                                           const float*, float*, float*, float*, float*, float*, char*, hipStream_t);
 
 // Newton-Schulz iterates of every scan's U (fp32, for the backward): X_0 = U / (||U||_F + 1e-7),
 // then the forward's steps; X_k (k < ns_iters, and X_0 also when ns_iters is 0) at X + k S 3 d m

@@ -88,6 +88,24 @@ static void run_ttt(ttt_desc D) {
     if (bs == TTT_OK && bneed > 0 && (int64_t)D.B * D.H > 0)
         EXPECT(ttt_backward(&D, q, k, v, eta, W0, dO, nullptr, dq, dk, dv, deta, dW0, bws, bneed - 1, nullptr) ==
                TTT_ERR_WORKSPACE);
+    // the training pair: the recurrence's backward only, then the same buffer checks
+    size_t rb = 0, rw = 0, bw = 0;
+    ttt_status rs = ttt_record_bytes(&D, &rb, &rw);
+    check_message(rs);
+    if (s != TTT_OK) EXPECT(rs == s);
+    if (s == TTT_OK && bs == TTT_OK && (!gd || D.last_layer_only == 0)) EXPECT(rs == TTT_OK);
+    if (rs == TTT_OK && (int64_t)D.B * D.H > 0) {
+        void* rec = (void*)(P + (16ull << 36));
+        ttt_status fr = ttt_forward_record(&D, q, k, v, eta, W0, o, Wout, rec, rb, ws, rw, nullptr);
+        check_message(fr);
+        EXPECT(fr == TTT_ERR_DEVICE || fr == TTT_ERR_INVALID_ARGUMENT);
+        EXPECT(ttt_backward_record_workspace_bytes(&D, &bw) == TTT_OK);
+        ttt_status br = ttt_backward_record(&D, q, k, v, eta, rec, rb, dO, nullptr, dq, dk, dv, deta, dW0, bws, bw, nullptr);
+        check_message(br);
+        EXPECT(br == TTT_ERR_DEVICE || br == TTT_ERR_INVALID_ARGUMENT);
+        EXPECT(ttt_backward_record(&D, q, k, v, eta, rec, rb - 1, dO, nullptr, dq, dk, dv, deta, dW0, bws, bw, nullptr) ==
+               TTT_ERR_WORKSPACE);
+    }
 }
 
 static void run_lin(linattn_desc D) {

@@ -39,7 +39,7 @@ def test_library_loads_and_exports_every_symbol():
 
 def test_version_and_status_strings():
     L = C.lib()
-    assert L.ttt_abi_version() == 6
+    assert L.ttt_abi_version() == 7
     for s in range(5):
         assert L.ttt_status_string(s)
     assert L.ttt_status_string(99) == b"unknown status"
@@ -391,6 +391,61 @@ def test_full_backward_workspace():
         expect += al(1 * S * chunk * 4) + al(S * qcap * 2 * m * 2) + al(S * qcap * m * 2)
         expect += al(1 * S * 3 * dm * 4)  # one part: 16 tiles, and parts under 1024 positions are not taken
         assert n.value == expect, (rule, mom, steps)
+
+
+def test_training_record_sizes_and_rejects():
+    """The record: the weights before every update and after the last (fp32), the row norms of every
+    update (L2 rules), every update's Newton-Schulz input (Muon); ttt_forward_record's workspace is
+    the forward's (no parallel form); the backward from a record needs the backward's workspace
+    without the record and the forward's.  Descriptors outside the recurrence's backward, NULL,
+    short or misaligned records and overlaps are refused before anything is enqueued."""
+    L = C.lib()
+    al = lambda x: (x + 255) // 256 * 256
+    B, H, N, d, m, chunk = 2, 4, 256, 64, 128, 64
+    S, dm, T = B * H, d * m, 4
+    r, w, n, full = ctypes.c_size_t(0), ctypes.c_size_t(0), ctypes.c_size_t(0), ctypes.c_size_t(0)
+    for rule, extra in ((C.UPD_GD, 0), (C.UPD_GD_L2, al(T * S * (2 * m + d) * 4)),
+                        (C.UPD_MUON_L2, al(T * S * (2 * m + d) * 4) + al(T * S * 3 * dm * 4))):
+        D = desc(rule=rule, momentum=0.9)
+        assert L.ttt_record_bytes(ctypes.byref(D), ctypes.byref(r), ctypes.byref(w)) == C.TTT_OK
+        assert r.value == al((T + 1) * S * 3 * dm * 4) + extra
+        assert w.value == ws_bytes(D)[1]
+        assert L.ttt_backward_record_workspace_bytes(ctypes.byref(D), ctypes.byref(n)) == C.TTT_OK
+        assert L.ttt_backward_workspace_bytes(ctypes.byref(D), ctypes.byref(full)) == C.TTT_OK
+        assert n.value == full.value - al(w.value) - al(r.value)
+    # W2 alone by GD takes ttt_backward; per-chunk rates have no backward
+    for kw in (dict(last_layer_only=1, rule=C.UPD_GD), dict(chunk_rates=1)):
+        assert L.ttt_record_bytes(ctypes.byref(desc(**kw)), ctypes.byref(r), ctypes.byref(w)) == C.TTT_ERR_UNSUPPORTED
+    assert L.ttt_record_bytes(ctypes.byref(desc()), None, ctypes.byref(w)) == C.TTT_ERR_INVALID_ARGUMENT
+    D = desc()
+    assert L.ttt_record_bytes(ctypes.byref(D), ctypes.byref(r), ctypes.byref(w)) == C.TTT_OK
+    G = 1 << 30
+    q, k, v, eta, W0, o, Wo = (P16 + i * G for i in range(7))
+    rec, ws = P16 + (1 << 36), P16 + (1 << 37)
+
+    def fwd(rp=rec, rn=r.value, oo=o):
+        return L.ttt_forward_record(ctypes.byref(D), q, k, v, eta, W0, oo, Wo, rp, rn, ws, w.value, None)
+
+    assert fwd(rp=None) == C.TTT_ERR_INVALID_ARGUMENT
+    assert fwd(rp=rec + 16) == C.TTT_ERR_INVALID_ARGUMENT                 # not 256-aligned
+    assert fwd(rn=r.value - 1) == C.TTT_ERR_WORKSPACE
+    assert fwd(rp=o) == C.TTT_ERR_INVALID_ARGUMENT                        # the record over o
+    assert b"overlaps" in L.ttt_last_error()
+    assert fwd(oo=q + 64) == C.TTT_ERR_INVALID_ARGUMENT                   # o over q
+    assert L.ttt_backward_record_workspace_bytes(ctypes.byref(D), ctypes.byref(n)) == C.TTT_OK
+    OB = P16 + (1 << 38)
+    dq, dk, dv, deta, dW0 = (OB + i * G for i in range(5))
+    dO = P16 + 8 * G
+
+    def bwd(rp=rec, rn=r.value, dqq=dq):
+        return L.ttt_backward_record(ctypes.byref(D), q, k, v, eta, rp, rn, dO, None, dqq, dk, dv, deta, dW0, ws,
+                                     n.value, None)
+
+    assert bwd(rp=None) == C.TTT_ERR_INVALID_ARGUMENT
+    assert bwd(rn=r.value - 1) == C.TTT_ERR_WORKSPACE
+    assert bwd(rp=rec + 16) == C.TTT_ERR_INVALID_ARGUMENT
+    assert bwd(dqq=rec + 64) == C.TTT_ERR_INVALID_ARGUMENT                # dq over the record
+    assert L.ttt_forward_record(ctypes.byref(desc(B=0)), *([None] * 8), 0, None, 0, None) == C.TTT_OK
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -181,3 +181,29 @@ def test_full_size_sampled():
             assert_close(gg, r, TOL[True], f"{name}[{b},{h}]")
     for t in got:
         assert torch.isfinite(t).all()
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("mask,rule,mom,inner,last", [(O.MASK_APPLY_THEN_UPDATE, O.UPD_GD_L2, 0.0, 1, False),
+                                                      (O.MASK_UPDATE_THEN_APPLY, O.UPD_MUON_L2, 0.9, 2, False),
+                                                      (O.MASK_APPLY_THEN_UPDATE, O.UPD_MUON, 0.5, 1, True)])
+def test_training_record(mask, rule, mom, inner, last, bf16):
+    # the training pair: ttt_forward_record's o and W_out are ttt_forward's, and the backward from the
+    # record is ttt_backward's, bit for bit (the same kernels in the same order)
+    say(f"training record case mask{mask} rule{rule} momentum{mom} inner{inner} last={last} bf16={bf16}")
+    B, H, N, d, m, chunk = 2, 2, 308, 64, 160, 96
+    (q, k, v, eta, W0), _ = full_ttt_inputs(15, B, H, N, d, m, bf16)
+    dO, dWo = synth.make_ttt_grads(15, B, H, N, d, m, bf16)
+    dt = torch.bfloat16 if bf16 else torch.float32
+    kw = dict(m_h=m, momentum=mom, inner_steps=inner, last_layer_only=last)
+    o, W, rec = T.ttt_forward_record(q, k, v, eta, W0, chunk, mask, rule, **kw)
+    o_ref, W_ref = T.ttt_forward(q, k, v, eta, W0, chunk, mask, rule, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(W, W_ref)
+    args = (q, k, v, eta, W0, dev(dO, dt), chunk, mask)
+    bkw = dict(m_h=m, dW_out=dev(pack(*dWo)), momentum=mom, inner_steps=inner, update_rule=rule, last_layer_only=last)
+    a = T.ttt_backward(*args, **bkw)
+    b = T.ttt_backward(*args, record=rec, **bkw)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
