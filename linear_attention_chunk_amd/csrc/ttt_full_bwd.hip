@@ -595,15 +595,22 @@ __global__ __launch_bounds__(kThreads, 2) void k_nsb_q(NsbArgs a) {
     t %= a.tiles;
     const int r = mat < 2 ? a.m : a.d, c = mat < 2 ? a.d : a.m;
     const int p = std::min(r, c), np = (p + kNsbQ - 1) / kNsbQ;
-    const int i0 = (t / np) * kNsbQ, j0 = (t % np) * kNsbQ;
-    if (i0 >= p) return;  // uniform: tiles covers the largest matrix
+    // Q + Q^T is symmetric: only tiles on or above the diagonal are computed (tile t of np (np + 1) / 2,
+    // row-major over the upper triangle), and an off-diagonal tile also writes its mirror block
+    int ti = 0;
+    while (t >= np - ti) t -= np - ti++;  // uniform: row ti of the upper triangle, column ti + t
+    const int i0 = ti * kNsbQ, j0 = (ti + t) * kNsbQ;
     const int64_t dm = (int64_t)a.d * a.m;
     const float* G = a.G + (int64_t)s * 3 * dm + mat * dm;
     const float* X = a.X + (int64_t)s * 3 * dm + mat * dm;
     float* Q = a.Q + ((int64_t)s * 3 + mat) * p * p;
     auto out = [&](auto& tl) {
         tl.for_each([&](const float (&v)[2], int row, int col) {
-            if (i0 + row < p && j0 + col < p) Q[(int64_t)(i0 + row) * p + j0 + col] = v[0] + v[1];
+            if (i0 + row < p && j0 + col < p) {
+                const float x = v[0] + v[1];
+                Q[(int64_t)(i0 + row) * p + j0 + col] = x;
+                if (i0 != j0) Q[(int64_t)(j0 + col) * p + i0 + row] = x;
+            }
         });
     };
     if (r <= c) {  // Q = G X^T over the columns: rows of G and X are k-contiguous
@@ -988,7 +995,7 @@ ttt_status run_full_backward(const ttt_desc& D, const T* q, const T* k, const T*
         const int stt = (int)std::max(cdiv(m, kNsbRows) * cdiv(d, kNsbCols), cdiv(d, kNsbRows) * cdiv(m, kNsbCols));
         for (int it = D.ns_iters - 1; it >= 0; --it) {
             NsbArgs na{Gc, Gn, X + (int64_t)it * hs, P + (int64_t)it * S * 3 * pp * pp, (float*)(ws + L.nsq), d, m, mat0,
-                       nmat, np * np};
+                       nmat, np * (np + 1) / 2};
             {
                 ProfScope ps(PK_FB_NSB, st);
                 hipLaunchKernelGGL(k_nsb_q, dim3((unsigned)((int64_t)S * nmat * na.tiles)), dim3(kThreads), 0, st, na);
