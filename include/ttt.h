@@ -246,7 +246,8 @@ ttt_status ttt_backward_workspace_bytes(const ttt_desc* desc, size_t* bytes);
  * io dtype with fp32 accumulation (bf16: phi, dA | dC, W1 | W3 and the linear-attention states and
  * state gradients are rounded to bf16 as contraction operands; the states are summed in fp32; with
  * all weights learning the weights and their gradients are carried in fp32 and rounded to bf16 as
- * operands, and so are the per-token intermediates; Muon's walk back runs in fp32), and every sum is
+ * operands, and so are the per-token intermediates; Muon's walk back carries the gradient in fp32
+ * with io-dtype operands), and every sum is
  * taken in a fixed order, so results do not depend on scheduling.
  */
 ttt_status ttt_backward(const ttt_desc* desc, const void* q, const void* k, const void* v,

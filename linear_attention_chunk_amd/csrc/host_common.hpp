@@ -159,10 +159,11 @@ size_t ttt_history_ws_bytes(const ttt_desc& D);
 template <typename T>
 ttt_status ttt_run_history(const ttt_desc& D, const T* q, const T* k, const T* v, const float* eta, const float* W0,
                            T* o, float* W_out, float* hist, float* nrm, float* urec, char* ws, hipStream_t st);
-// Newton-Schulz iterates of U for the backward (fp32): X_k at X + k S 3 d m (k < max(ns_iters, 1)),
-// the Gram matrix of X_k at P + k S 3 p^2 (k < ns_iters), the partial sums of U^2 in part
-// (S x 3 x ceil(d m / 4096)); the learned matrices only (W2 alone with last_layer_only).
-ttt_status ns_iterates(const ttt_desc& D, const float* U, float* part, float* X, float* P, hipStream_t st);
+// Newton-Schulz steps from X_0 at X for the backward: for k < ns_iters the Gram matrix of X_k at
+// P + k S 3 p^2 and, but for the last, X_{k+1} at X + (k + 1) S 3 d m (bf16: hi planes, the lo plane
+// Xlo carried in place); the learned matrices only (W2 alone with last_layer_only).
+template <typename T>
+ttt_status ns_steps(const ttt_desc& D, T* X, T* Xlo, T* P, hipStream_t st);
 
 // The backward of the recurrence with all three weights learning (GD or GD + L2, momentum): the
 // descriptor checks beyond validate_ttt_desc, the workspace, and the run (arguments as for

@@ -562,29 +562,33 @@ __global__ __launch_bounds__(kThreads, 2) void k_fb_dw(FbDwArgs<T> a) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Newton-Schulz walked back (Muon), in fp32, for every scan's learned matrices at once.  With X the
-// iterate of a step and G the gradient of its output, the gradient of its input is
+// Newton-Schulz walked back (Muon) for every scan's learned matrices at once.  With X the iterate of
+// a step and G the gradient of its output, the gradient of its input is
 //   wide X (rows <= columns):  1.5 G - 0.5 [(Q + Q^T) X + (X X^T) G],  Q = G X^T
 //   tall X:                    1.5 G - 0.5 [G (X^T X) + X (Q + Q^T)],  Q = G^T X
 // (the forward steps on the side with the smaller Gram matrix, as the tall form does transposed).
 // k_nsb_q writes Q + Q^T, k_nsb_step the new gradient (to the other buffer: every tile reads G), and
-// the start X_0 = U / (|U| + 1e-7) is taken back by k_nsb_dot and k_nsb_final.
+// the start X_0 = U / (|U| + 1e-7) is taken back by k_nsb_dot and k_nsb_final.  G is carried in fp32;
+// the products take T operands (bf16: G's bf16 shadow, the iterates' hi planes and bf16 Gram
+// matrices, as the forward's steps take them; fp32: the fp32 values themselves).
 struct PMD { static constexpr int a[2] = {0, 1}; static constexpr int b[2] = {0, 1}; };
 constexpr int kNsbQ = 64;                      // Q tiles
 constexpr int kNsbRows = 128, kNsbCols = 64;   // step tiles
-constexpr int kNsbElems = 4096;                // elements per block of the dot and final kernels
+constexpr int kNsbElems = 4096;                // elements per block of the elementwise kernels
 
-struct NsbArgs {
-    const float* G; float* Gout;     // [S][3dm]
-    const float* X;                  // the step's iterate [S][3dm]
-    const float* P;                  // its Gram matrix [S][3 p^2]
-    float* Q;                        // Q + Q^T [S][3 p^2]
+template <typename T> struct NsbArgs {
+    const float* G; const T* Gs;     // the gradient [S][3dm] (fp32) and its operand copy
+    float* Gout; T* Gsout;           // the next gradient and its operand copy (fp32: the same buffer)
+    const T* X;                      // the step's iterate [S][3dm]
+    const T* P;                      // its Gram matrix [S][3 p^2]
+    T* Q;                            // Q + Q^T [S][3 p^2]
     int d, m, mat0, nmat, tiles;     // tiles per matrix
 };
 
-__global__ __launch_bounds__(kThreads, 2) void k_nsb_q(NsbArgs a) {
-    using TW = Tile<float, kNsbQ, kNsbQ, 2, 2, 2, 2, 2, false, false, false, 4, 2>;
-    using TT = Tile<float, kNsbQ, kNsbQ, 2, 2, 2, 2, 2, true, true, false, 4, 2>;
+template <typename T>
+__global__ __launch_bounds__(kThreads, 2) void k_nsb_q(NsbArgs<T> a) {
+    using TW = Tile<T, kNsbQ, kNsbQ, 2, 2, 2, 2, 2, false, false, false, 4, 2>;
+    using TT = Tile<T, kNsbQ, kNsbQ, 2, 2, 2, 2, 2, true, true, false, 4, 2>;
     constexpr int LDSB = std::max(TW::LDS, TT::LDS);
     __shared__ __attribute__((aligned(16))) char smem[LDSB];
     const int per = a.nmat * a.tiles;
@@ -601,13 +605,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_nsb_q(NsbArgs a) {
     while (t >= np - ti) t -= np - ti++;  // uniform: row ti of the upper triangle, column ti + t
     const int i0 = ti * kNsbQ, j0 = (ti + t) * kNsbQ;
     const int64_t dm = (int64_t)a.d * a.m;
-    const float* G = a.G + (int64_t)s * 3 * dm + mat * dm;
-    const float* X = a.X + (int64_t)s * 3 * dm + mat * dm;
-    float* Q = a.Q + ((int64_t)s * 3 + mat) * p * p;
+    const T* G = a.Gs + (int64_t)s * 3 * dm + mat * dm;
+    const T* X = a.X + (int64_t)s * 3 * dm + mat * dm;
+    T* Q = a.Q + ((int64_t)s * 3 + mat) * p * p;
     auto out = [&](auto& tl) {
         tl.for_each([&](const float (&v)[2], int row, int col) {
             if (i0 + row < p && j0 + col < p) {
-                const float x = v[0] + v[1];
+                const T x = Elt<T>::st(v[0] + v[1]);
                 Q[(int64_t)(i0 + row) * p + j0 + col] = x;
                 if (i0 != j0) Q[(int64_t)(j0 + col) * p + i0 + row] = x;
             }
@@ -615,22 +619,23 @@ __global__ __launch_bounds__(kThreads, 2) void k_nsb_q(NsbArgs a) {
     };
     if (r <= c) {  // Q = G X^T over the columns: rows of G and X are k-contiguous
         TW tl;
-        const Opnd<float> A[2] = {{G + (int64_t)i0 * c, c, p - i0, c}, {X + (int64_t)i0 * c, c, p - i0, c}};
-        const Opnd<float> B[2] = {{X + (int64_t)j0 * c, c, p - j0, c}, {G + (int64_t)j0 * c, c, p - j0, c}};
+        const Opnd<T> A[2] = {{G + (int64_t)i0 * c, c, p - i0, c}, {X + (int64_t)i0 * c, c, p - i0, c}};
+        const Opnd<T> B[2] = {{X + (int64_t)j0 * c, c, p - j0, c}, {G + (int64_t)j0 * c, c, p - j0, c}};
         tl.template run<PMD>(A, B, c, smem);
         out(tl);
     } else {       // Q = G^T X over the rows: columns of G and X, k-strided
         TT tl;
-        const Opnd<float> A[2] = {{G + i0, c, p - i0, r}, {X + i0, c, p - i0, r}};
-        const Opnd<float> B[2] = {{X + j0, c, p - j0, r}, {G + j0, c, p - j0, r}};
+        const Opnd<T> A[2] = {{G + i0, c, p - i0, r}, {X + i0, c, p - i0, r}};
+        const Opnd<T> B[2] = {{X + j0, c, p - j0, r}, {G + j0, c, p - j0, r}};
         tl.template run<PMD>(A, B, r, smem);
         out(tl);
     }
 }
 
-__global__ __launch_bounds__(kThreads, 2) void k_nsb_step(NsbArgs a) {
-    using TW = Tile<float, kNsbRows, kNsbCols, 2, 2, 1, 1, 1, false, true, false, 4, 2>;   // B k-strided
-    using TT = Tile<float, kNsbRows, kNsbCols, 2, 2, 1, 1, 1, false, false, false, 4, 2>;  // B symmetric rows
+template <typename T>
+__global__ __launch_bounds__(kThreads, 2) void k_nsb_step(NsbArgs<T> a) {
+    using TW = Tile<T, kNsbRows, kNsbCols, 2, 2, 1, 1, 1, false, true, false, 4, 2>;   // B k-strided
+    using TT = Tile<T, kNsbRows, kNsbCols, 2, 2, 1, 1, 1, false, false, false, 4, 2>;  // B symmetric rows
     constexpr int LDSB = std::max(TW::LDS, TT::LDS);
     __shared__ __attribute__((aligned(16))) char smem[LDSB];
     const int per = a.nmat * a.tiles;
@@ -646,36 +651,64 @@ __global__ __launch_bounds__(kThreads, 2) void k_nsb_step(NsbArgs a) {
     if (r0 >= r) return;  // uniform: tiles covers the larger of the two orientations
     const int64_t dm = (int64_t)a.d * a.m, mo = (int64_t)s * 3 * dm + mat * dm;
     const float* G = a.G + mo;
-    const float* X = a.X + mo;
-    const float* P = a.P + ((int64_t)s * 3 + mat) * p * p;
-    const float* Q = a.Q + ((int64_t)s * 3 + mat) * p * p;
+    const T* Gs = a.Gs + mo;
+    const T* X = a.X + mo;
+    const T* P = a.P + ((int64_t)s * 3 + mat) * p * p;
+    const T* Q = a.Q + ((int64_t)s * 3 + mat) * p * p;
     float* O = a.Gout + mo;
+    T* Os = a.Gsout + mo;
     auto out = [&](auto& tl) {
         tl.for_each([&](const float (&v)[1], int row, int col) {
             if (r0 + row < r && c0 + col < c) {
                 const int64_t e = (int64_t)(r0 + row) * c + c0 + col;
-                O[e] = 1.5f * G[e] - 0.5f * v[0];
+                const float x = 1.5f * G[e] - 0.5f * v[0];
+                O[e] = x;
+                if constexpr (sizeof(T) == 2) Os[e] = Elt<T>::st(x);
             }
         });
     };
     if (r <= c) {  // (Q + Q^T) X + P G: B is X or G read k-strided
         TW tl;
-        const Opnd<float> A0[1] = {{Q + (int64_t)r0 * p, p, r - r0, p}};
-        const Opnd<float> B0[1] = {{X + c0, c, c - c0, r}};
-        const Opnd<float> A1[1] = {{P + (int64_t)r0 * p, p, r - r0, p}};
-        const Opnd<float> B1[1] = {{G + c0, c, c - c0, r}};
+        const Opnd<T> A0[1] = {{Q + (int64_t)r0 * p, p, r - r0, p}};
+        const Opnd<T> B0[1] = {{X + c0, c, c - c0, r}};
+        const Opnd<T> A1[1] = {{P + (int64_t)r0 * p, p, r - r0, p}};
+        const Opnd<T> B1[1] = {{Gs + c0, c, c - c0, r}};
         tl.template run<PM1>(A0, B0, r, smem);
         tl.template run<PM1>(A1, B1, r, smem, true);
         out(tl);
     } else {       // G P + X (Q + Q^T): P and Q + Q^T are symmetric, so their rows serve as B
         TT tl;
-        const Opnd<float> A0[1] = {{G + (int64_t)r0 * c, c, r - r0, c}};
-        const Opnd<float> B0[1] = {{P + (int64_t)c0 * p, p, c - c0, p}};
-        const Opnd<float> A1[1] = {{X + (int64_t)r0 * c, c, r - r0, c}};
-        const Opnd<float> B1[1] = {{Q + (int64_t)c0 * p, p, c - c0, p}};
+        const Opnd<T> A0[1] = {{Gs + (int64_t)r0 * c, c, r - r0, c}};
+        const Opnd<T> B0[1] = {{P + (int64_t)c0 * p, p, c - c0, p}};
+        const Opnd<T> A1[1] = {{X + (int64_t)r0 * c, c, r - r0, c}};
+        const Opnd<T> B1[1] = {{Q + (int64_t)c0 * p, p, c - c0, p}};
         tl.template run<PM1>(A0, B0, c, smem);
         tl.template run<PM1>(A1, B1, c, smem, true);
         out(tl);
+    }
+}
+
+// X_0 = U / (|U| + 1e-7) as the steps' operand (bf16: hi plane to X, lo plane to Xlo), and with
+// Gs the operand copy of the fp32 gradient G, for the learned matrices; pu holds U's partial sums
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_nsb_x0(const float* U, const float* pu, T* X, T* Xlo, const float* G,
+                                                     T* Gs, int64_t dm, int mat0, int nmat, int nblk) {
+    const int per = nmat * nblk;
+    const int s = blockIdx.x / per, t = blockIdx.x % per;
+    const int mat = mat0 + t / nblk, blk = t % nblk;
+    float su = 0.f;
+    for (int i = threadIdx.x & 63; i < nblk; i += 64) su += pu[((int64_t)s * 3 + mat) * nblk + i];
+    const float inv = 1.0f / (sqrtf(wave_sum(su)) + 1e-7f);
+    const int64_t mo = (int64_t)s * 3 * dm + mat * dm;
+    for (int64_t e = (int64_t)blk * kNsbElems + threadIdx.x; e < std::min<int64_t>((int64_t)(blk + 1) * kNsbElems, dm);
+         e += kThreads) {
+        const float x = U[mo + e] * inv;
+        const T h = Elt<T>::st(x);
+        X[mo + e] = h;
+        if constexpr (sizeof(T) == 2) {
+            Xlo[mo + e] = f2bf(x - bf2f(h));
+            Gs[mo + e] = f2bf(G[mo + e]);
+        }
     }
 }
 
@@ -865,7 +898,8 @@ static FRecord record_layout(const ttt_desc& D, const FbPlan& P) {
 
 struct FLayout {
     size_t fwd, rec, dW, dM, G, op, acp, qa, qh, pk, pv, pe, acck, accv, epart, part, total;
-    size_t nsx, nsp, nsq, gb, pu, pgu;  // Muon: iterates, Grams, Q + Q^T, G's pair, partial sums
+    size_t nsx, nsxl, gs[2], nsp, nsq, gb, pu, pgu;  // Muon: iterates (and lo plane), G's operand copies,
+                                                      // Grams, Q + Q^T, G's pair, partial sums
     int nparts, nK;
     int64_t bcap, qcap;
 };
@@ -908,9 +942,14 @@ static FLayout make_flayout(const ttt_desc& D, const FbPlan& P, bool own_record)
     L.part = take((size_t)L.nparts * S * 3 * dm * 4);
     if (D.rule == TTT_UPD_MUON || D.rule == TTT_UPD_MUON_L2) {
         const int64_t p = std::min(d, m), nblk = cdiv(dm, kNsbElems);
-        L.nsx = take((size_t)std::max(D.ns_iters, 1) * S * 3 * dm * 4);
-        L.nsp = take((size_t)std::max(D.ns_iters, 1) * S * 3 * p * p * 4);
-        L.nsq = take((size_t)S * 3 * p * p * 4);
+        L.nsx = take((size_t)std::max(D.ns_iters, 1) * S * 3 * dm * es);
+        if (es == 2) {
+            L.nsxl = take((size_t)S * 3 * dm * es);
+            L.gs[0] = take((size_t)S * 3 * dm * es);
+            L.gs[1] = take((size_t)S * 3 * dm * es);
+        }
+        L.nsp = take((size_t)std::max(D.ns_iters, 1) * S * 3 * p * p * es);
+        L.nsq = take((size_t)S * 3 * p * p * es);
         L.gb = take((size_t)S * 3 * dm * 4);
         L.pu = take((size_t)S * 3 * nblk * 4);
         L.pgu = take((size_t)S * 3 * nblk * 4);
@@ -982,43 +1021,62 @@ ttt_status run_full_backward(const ttt_desc& D, const T* q, const T* k, const T*
     // Muon at update ver: G holds the gradient of Newton-Schulz's output; it becomes Gamma
     auto muon_backward = [&](int ver) -> ttt_status {
         const float* U = urec + (int64_t)ver * hs;
-        float* X = (float*)(ws + L.nsx);
-        float* P = (float*)(ws + L.nsp);
+        T* X = (T*)(ws + L.nsx);
+        T* Xlo = sizeof(T) == 2 ? (T*)(ws + L.nsxl) : nullptr;
+        T* P = (T*)(ws + L.nsp);
+        T* Q = (T*)(ws + L.nsq);
         float* pu = (float*)(ws + L.pu);
         float* pgu = (float*)(ws + L.pgu);
-        const int nblk = (int)cdiv(dm, kNsbElems);  // the blocks of U^2's partial sums (4096 elements)
+        const int nblk = (int)cdiv(dm, kNsbElems);
+        const unsigned eg = (unsigned)((int64_t)S * nmat * nblk);
         ttt_status r;
-        if ((r = ns_iterates(D, U, pu, X, P, st)) != TTT_OK) return r;
+        // |U| (as partial sums), X_0 and the gradient's operand copy, then the forward's steps again
+        {
+            ProfScope ps(PK_FB_NSB, st);
+            hipLaunchKernelGGL(k_nsb_dot, dim3(eg), dim3(kThreads), 0, st, U, U, pu, dm, mat0, nmat, nblk);
+        }
+        if ((r = check_launch("k_nsb_dot", st)) != TTT_OK) return r;
+        T* gs[2] = {sizeof(T) == 2 ? (T*)(ws + L.gs[0]) : (T*)G, sizeof(T) == 2 ? (T*)(ws + L.gs[1]) : (T*)(ws + L.gb)};
+        {
+            ProfScope ps(PK_FB_NSB, st);
+            hipLaunchKernelGGL(k_nsb_x0<T>, dim3(eg), dim3(kThreads), 0, st, U, (const float*)pu, X, Xlo, (const float*)G,
+                               gs[0], dm, mat0, nmat, nblk);
+        }
+        if ((r = check_launch("k_nsb_x0", st)) != TTT_OK) return r;
+        if ((r = ns_steps<T>(D, X, Xlo, P, st)) != TTT_OK) return r;
         float* Gc = G;
         float* Gn = (float*)(ws + L.gb);
         const int np = (int)cdiv(pp, kNsbQ);
         const int stt = (int)std::max(cdiv(m, kNsbRows) * cdiv(d, kNsbCols), cdiv(d, kNsbRows) * cdiv(m, kNsbCols));
+        int cur = 0;
         for (int it = D.ns_iters - 1; it >= 0; --it) {
-            NsbArgs na{Gc, Gn, X + (int64_t)it * hs, P + (int64_t)it * S * 3 * pp * pp, (float*)(ws + L.nsq), d, m, mat0,
-                       nmat, np * (np + 1) / 2};
+            NsbArgs<T> na{Gc, gs[cur], Gn, gs[cur ^ 1], X + (int64_t)it * hs, P + (int64_t)it * S * 3 * pp * pp, Q, d, m,
+                          mat0, nmat, np * (np + 1) / 2};
             {
                 ProfScope ps(PK_FB_NSB, st);
-                hipLaunchKernelGGL(k_nsb_q, dim3((unsigned)((int64_t)S * nmat * na.tiles)), dim3(kThreads), 0, st, na);
+                hipLaunchKernelGGL(k_nsb_q<T>, dim3((unsigned)((int64_t)S * nmat * na.tiles)), dim3(kThreads), 0, st,
+                                   na);
             }
             if ((r = check_launch("k_nsb_q", st)) != TTT_OK) return r;
             na.tiles = stt;
             {
                 ProfScope ps(PK_FB_NSB, st);
-                hipLaunchKernelGGL(k_nsb_step, dim3((unsigned)((int64_t)S * nmat * stt)), dim3(kThreads), 0, st, na);
+                hipLaunchKernelGGL(k_nsb_step<T>, dim3((unsigned)((int64_t)S * nmat * stt)), dim3(kThreads), 0, st, na);
             }
             if ((r = check_launch("k_nsb_step", st)) != TTT_OK) return r;
             std::swap(Gc, Gn);
+            cur ^= 1;
         }
         {
             ProfScope ps(PK_FB_NSB, st);
-            hipLaunchKernelGGL(k_nsb_dot, dim3((unsigned)((int64_t)S * nmat * nblk)), dim3(kThreads), 0, st,
-                               (const float*)Gc, U, pgu, dm, mat0, nmat, nblk);
+            hipLaunchKernelGGL(k_nsb_dot, dim3(eg), dim3(kThreads), 0, st, (const float*)Gc, U, pgu, dm, mat0, nmat,
+                               nblk);
         }
         if ((r = check_launch("k_nsb_dot", st)) != TTT_OK) return r;
         NsbFinalArgs fa{Gc, U, pu, pgu, G, dM, D.momentum, dm, mat0, nmat, nblk};
         {
             ProfScope ps(PK_FB_NSB, st);
-            hipLaunchKernelGGL(k_nsb_final, dim3((unsigned)((int64_t)S * nmat * nblk)), dim3(kThreads), 0, st, fa);
+            hipLaunchKernelGGL(k_nsb_final, dim3(eg), dim3(kThreads), 0, st, fa);
         }
         return check_launch("k_nsb_final", st);
     };

@@ -1382,53 +1382,42 @@ template ttt_status ttt_run_history<uint16_t>(const ttt_desc&, const uint16_t*, 
 template ttt_status ttt_run_history<float>(const ttt_desc&, const float*, const float*, const float*, const float*,
                                            const float*, float*, float*, float*, float*, float*, char*, hipStream_t);
 
-// Newton-Schulz iterates of every scan's U (fp32, for the backward): X_0 = U / (||U||_F + 1e-7),
-// then the forward's steps; X_k (k < ns_iters, and X_0 also when ns_iters is 0) at X + k S 3 d m
-// and its Gram matrix at P + k S 3 p^2, with the learned matrices' partial sums of U^2 in part
-// (S x 3 x nblk).  U, X: [S][3dm]; P: [S][3 p^2], p = min(d, m).
-ttt_status ns_iterates(const ttt_desc& D, const float* U, float* part, float* X, float* P, hipStream_t st) {
+// Newton-Schulz steps from X_0 (for the backward): for k < ns_iters the Gram matrix of X_k goes to
+// P + k S 3 p^2 and, but for the last, X_{k+1} to X + (k + 1) S 3 d m (bf16: hi planes, with the lo
+// plane Xlo carried in place as the forward's steps do).  X, Xlo: [S][3dm]; P: [S][3 p^2].
+template <typename T>
+ttt_status ns_steps(const ttt_desc& D, T* X, T* Xlo, T* P, hipStream_t st) {
     const int S = D.B * D.H, d = D.d_h, m = D.m_h;
     const int64_t dm = (int64_t)d * m, p = std::min(d, m);
     const int mat0 = D.last_layer_only ? 2 : 0, nmat = D.last_layer_only ? 1 : 3;
     const int nblk = (int)cdiv(dm, kPrepElems);
     ttt_status rc;
-    {
-        PrepArgs<float> pa{U, 3 * dm, 1, 0, nullptr, nullptr, 0, 0.f, part, nblk, nullptr, nullptr, 0, dm, mat0, nmat, 0,
-                           nullptr, 0, 0};
-        ProfScope ps(PK_MUON_PREP, st);
-        hipLaunchKernelGGL(k_muon_prep<float>, dim3(S * nmat * nblk), dim3(kThreads), 0, st, pa);
-    }
-    if ((rc = check_launch("k_muon_prep", st)) != TTT_OK) return rc;
-    {
-        NSArgs<float> na{U, 3 * dm, part, nblk, nullptr, nullptr, nullptr, X, 3 * dm, nullptr, 0, d, m, mat0, nmat, 0, 0};
-        ProfScope ps(PK_NS_INIT, st);
-        hipLaunchKernelGGL(k_ns_init<float>, dim3(S * nmat * nblk), dim3(kThreads), 0, st, na);
-    }
-    if ((rc = check_launch("k_ns_init", st)) != TTT_OK) return rc;
     const bool gsmall = (int64_t)S * nmat * cdiv(p, 128) * (cdiv(p, 128) + 1) / 2 < 256;
     const int gts = gsmall ? 64 : 128;
     const int gt = (int)(cdiv(p, gts) * (cdiv(p, gts) + 1) / 2);
     const int stt = (int)std::max(cdiv(m, kNSStepRows) * cdiv(d, kNSStepCols), cdiv(d, kNSStepRows) * cdiv(m, kNSStepCols));
     const int64_t xs = (int64_t)S * 3 * dm, ps_ = (int64_t)S * 3 * p * p;
     for (int k = 0; k < D.ns_iters; ++k) {
-        NSArgs<float> na{nullptr, 0, nullptr, nblk, X + k * xs, k + 1 < D.ns_iters ? X + (k + 1) * xs : nullptr, nullptr,
-                         nullptr, 3 * dm, P + k * ps_, 3 * p * p, d, m, mat0, nmat, gt, 0};
+        NSArgs<T> na{nullptr, 0, nullptr, nblk, X + k * xs, k + 1 < D.ns_iters ? X + (k + 1) * xs : nullptr,
+                     sizeof(T) == 2 ? Xlo : nullptr, nullptr, 3 * dm, P + k * ps_, 3 * p * p, d, m, mat0, nmat, gt, 0};
         {
             ProfScope ps(PK_NS_GRAM, st);
-            if (gsmall) hipLaunchKernelGGL((k_ns_gram<float, 64>), dim3(S * nmat * gt), dim3(kThreads), 0, st, na);
-            else hipLaunchKernelGGL((k_ns_gram<float, 128>), dim3(S * nmat * gt), dim3(kThreads), 0, st, na);
+            if (gsmall) hipLaunchKernelGGL((k_ns_gram<T, 64>), dim3(S * nmat * gt), dim3(kThreads), 0, st, na);
+            else hipLaunchKernelGGL((k_ns_gram<T, 128>), dim3(S * nmat * gt), dim3(kThreads), 0, st, na);
         }
         if ((rc = check_launch("k_ns_gram", st)) != TTT_OK) return rc;
         if (k + 1 == D.ns_iters) break;  // the last iterate is not needed
         na.tiles = stt;
         {
             ProfScope ps(PK_NS_STEP, st);
-            hipLaunchKernelGGL(k_ns_step<float>, dim3(S * nmat * stt), dim3(kThreads), 0, st, na);
+            hipLaunchKernelGGL(k_ns_step<T>, dim3(S * nmat * stt), dim3(kThreads), 0, st, na);
         }
         if ((rc = check_launch("k_ns_step", st)) != TTT_OK) return rc;
     }
     return TTT_OK;
 }
+template ttt_status ns_steps<uint16_t>(const ttt_desc&, uint16_t*, uint16_t*, uint16_t*, hipStream_t);
+template ttt_status ns_steps<float>(const ttt_desc&, float*, float*, float*, hipStream_t);
 
 }  // namespace ttt
 
