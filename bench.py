@@ -188,6 +188,9 @@ def main():
     ap.add_argument("--update", choices=["gd_l2", "muon_momentum", "last_layer_gd_parallel"], default="gd_l2",
                     help="update rule of the timed layer (the headline metric uses gd_l2); last_layer_gd_parallel: "
                          "only W2 learns, W - g, in the parallel static-kernel form")
+    ap.add_argument("--profile-backward", choices=["gd_l2", "muon_momentum"], default=None,
+                    help="time only the layer's backward with all weights learning (for kernel traces) and print "
+                         "its own JSON line instead of the headline's")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first copy a 1 GiB device buffer three times (a known-size kernel that scales "
                          "hardware byte counters)")
@@ -240,6 +243,21 @@ def main():
             print(f"[bench] inputs of batch {b} ready", file=sys.stderr, flush=True)
     Wh = [synth.head_weights(args.seed, h, d, m) for h in range(H)]
     W0 = torch.from_numpy(np.stack([np.concatenate([w[0].ravel(), w[1].ravel(), w[2].ravel()]) for w in Wh])).cuda()
+    if args.profile_backward:  # the backward alone, on the headline's inputs
+        rb, bb = {"gd_l2": (C.UPD_GD_L2, 0.0), "muon_momentum": (C.UPD_MUON_L2, 0.9)}[args.profile_backward]
+        gb = torch.Generator(device="cuda")
+        gb.manual_seed(3600 + args.seed)
+        dOb = (torch.randn((B, H, N, d), generator=gb, device="cuda") / d ** 0.5).to(torch.bfloat16)
+        Db, _ = T.ttt_desc(B, H, N, d, m, chunk, C.TTT_BF16, C.MASK_APPLY_THEN_UPDATE, rb, 5, bb)
+        wsb = torch.empty(T.ttt_backward_workspace_bytes(Db), dtype=torch.uint8, device="cuda")
+        msb = time_calls(torch, lambda: T.ttt_backward(q, k, v, eta, W0, dOb, chunk, C.MASK_APPLY_THEN_UPDATE, m_h=m,
+                                                       update_rule=rb, momentum=bb, last_layer_only=False,
+                                                       workspace=wsb), args.steps, args.warmup)
+        print(json.dumps({"profile_backward": args.profile_backward, "ms_per_call": round(msb, 3),
+                          "calls": args.steps + args.warmup,
+                          "workload": f"B{B} H{H} N{N} d{d} m{m} chunk {chunk} bf16, apply-then-update, all weights "
+                                      "learning"}))
+        return
     rule, beta = {"gd_l2": (C.UPD_GD_L2, 0.0), "muon_momentum": (C.UPD_MUON_L2, 0.9),
                   "last_layer_gd_parallel": (C.UPD_GD, 0.0)}[args.update]
     par = args.update == "last_layer_gd_parallel"
