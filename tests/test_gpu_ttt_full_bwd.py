@@ -207,3 +207,19 @@ def test_training_record(mask, rule, mom, inner, last, bf16):
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_muon_orientations_and_small_shapes(bf16):
+    # d > m makes W1, W3 wide and W2 tall (the other side of every Newton-Schulz product); a 48-token
+    # chunk leaves single partial tiles; d = m = 32 is the smallest head
+    run(16, 1, 2, 200, 128, 64, 48, O.MASK_APPLY_THEN_UPDATE, bf16, rule=O.UPD_MUON_L2, momentum=0.9)
+    run(17, 1, 2, 130, 32, 32, 64, O.MASK_UPDATE_THEN_APPLY, bf16, rule=O.UPD_MUON, inner=2)
+    run(18, 1, 2, 130, 128, 64, 130, O.MASK_FULL, bf16, rule=O.UPD_GD_L2, momentum=0.5)
+
+
+def test_muon_weight_layouts_and_empty():
+    run(19, 2, 2, 260, 64, 128, 128, O.MASK_APPLY_THEN_UPDATE, True, rule=O.UPD_MUON_L2, momentum=0.9,
+        per_batch=True)
+    run(20, 3, 2, 260, 64, 128, 128, O.MASK_UPDATE_THEN_APPLY, False, rule=O.UPD_MUON, momentum=0.9)
+    run(21, 2, 2, 0, 64, 96, 64, O.MASK_APPLY_THEN_UPDATE, True, rule=O.UPD_MUON_L2, momentum=0.9)
