@@ -584,6 +584,19 @@ def main():
         # linear-attention backward over d_k = m, d_v = d (the chunk states again, the query-gradient
         # sums, dphi(q), dphi(k), dv: 10 d m), dq and dk (8 d m), dW1 and dW3 (8 d m)
         gflops = tokens * H * 34 * d * m
+        # the same layer trained through its recurrence: the forward keeping its record, then the
+        # recurrence walked back (W1, W3 frozen), against the parallel forward and its backward
+        rb_, rw_ = T.ttt_record_bytes(Dg)
+        recg = torch.empty(rb_, dtype=torch.uint8, device="cuda")
+        wsr_ = torch.empty(max(1, rw_), dtype=torch.uint8, device="cuda")
+
+        def rec_step():
+            T.ttt_forward_record(q, k, v, eta, W0, chunk, C.MASK_APPLY_THEN_UPDATE, C.UPD_GD, m_h=m,
+                                 last_layer_only=True, out=o, record=recg, workspace=wsr_)
+            T.ttt_backward(q, k, v, eta, W0, dOl, chunk, C.MASK_APPLY_THEN_UPDATE, m_h=m, record=recg)
+
+        msr = time_calls(torch, rec_step, 1, 1)
+        del recg, wsr_
         extras["lact_lm_last_layer_gd_backward"] = {
             "workload": f"B{B} H{H} N{N} d{d} m{m} chunk {chunk} bf16, apply-then-update, only W2 learns (plain "
                         "GD): gradients of q, k, v, eta and the per-head W0 from dO",
@@ -591,7 +604,9 @@ def main():
             "algorithmic_tflop": round(gflops / 1e12, 3),
             "mfma_frac": round(gflops / (msg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
             "over_parallel_forward": round(msg / msp[True], 2),
-            "training_step_ms": round(msg + msp[True], 3), "kernels_ms": gk}
+            "training_step_ms": round(msg + msp[True], 3),
+            "recurrence_training_step_ms": round(msr, 3),
+            "parallel_form_training_speedup": round(msr / (msg + msp[True]), 2), "kernels_ms": gk}
         # the headline layer's backward (all three weights learning, GD + L2): the forward again for its
         # record, then the reverse of the chunk recurrence
         print("[bench] extras: GD + L2 backward, all weights learning", file=sys.stderr, flush=True)

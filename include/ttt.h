@@ -256,8 +256,9 @@ ttt_status ttt_backward(const ttt_desc* desc, const void* q, const void* k, cons
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * The training pair for the backward of the recurrence (the descriptors ttt_backward walks back:
- * last_layer_only = 0, or a Muon rule; chunk_rates 0, at most 65536 updates).  A training step
+ * The training pair for the backward of the recurrence (any rule, chunk_rates 0, at most 65536
+ * updates; the layer whose inner loop trains W2 alone by GD included, which ttt_backward takes
+ * through linear attention instead, as its parallel form computes it).  A training step
  * runs ttt_forward_record, which writes o and W_out as ttt_forward does (momentum from zero, its
  * final value not returned) and keeps a record of the recurrence: the weights before every update
  * and after the last (fp32), with the L2 rules every update's row norms, with Muon every update's
@@ -266,7 +267,9 @@ ttt_status ttt_backward(const ttt_desc* desc, const void* q, const void* k, cons
  * memory; its content is valid for the descriptor and inputs of the forward that wrote it.
  *
  * ttt_record_bytes: the record's size and the workspace ttt_forward_record needs.  Descriptors
- * outside the pair's scope are TTT_ERR_UNSUPPORTED.
+ * outside the pair's scope are TTT_ERR_UNSUPPORTED.  With last_layer_only and TTT_UPD_GD or
+ * TTT_UPD_GD_L2 the pair's results equal ttt_backward's within rounding (not bit for bit: the two
+ * take different routes).
  */
 ttt_status ttt_record_bytes(const ttt_desc* desc, size_t* record_bytes, size_t* workspace_bytes);
 

@@ -481,13 +481,11 @@ extern "C" ttt_status ttt_backward(const ttt_desc* desc, const void* q, const vo
 }
 
 // The training pair: the forward that keeps a record, and the backward that reads it.
+// The pair always walks the recurrence back, the layer whose inner loop trains W2 alone by GD
+// included (ttt_backward takes that one through linear attention instead, as its parallel form does)
 static ttt_status validate_record(const ttt_desc* desc) {
     ttt_status rc = validate_ttt_desc(desc);
     if (rc != TTT_OK) return rc;
-    if (!uses_full(*desc))
-        return fail(TTT_ERR_UNSUPPORTED,
-                    "the record serves the backward of the recurrence (all weights learning, or Muon); the layer "
-                    "whose inner loop trains W2 alone by GD takes ttt_backward");
     return validate_full_bwd(desc);
 }
 

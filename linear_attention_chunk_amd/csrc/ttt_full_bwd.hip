@@ -959,8 +959,7 @@ static FLayout make_flayout(const ttt_desc& D, const FbPlan& P, bool own_record)
 }
 
 ttt_status validate_full_bwd(const ttt_desc* D) {
-    const bool muon = D->rule == TTT_UPD_MUON || D->rule == TTT_UPD_MUON_L2;
-    if ((D->last_layer_only && !muon) || D->chunk_rates || (D->parallel_form && !D->last_layer_only))
+    if (D->chunk_rates || (D->parallel_form && !D->last_layer_only))
         return fail(TTT_ERR_UNSUPPORTED,
                     "the backward of the recurrence covers every rule (with or without momentum) with per-token rates");
     const int64_t S = (int64_t)D->B * D->H, d = D->d_h, m = D->m_h;

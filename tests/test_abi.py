@@ -413,9 +413,11 @@ def test_training_record_sizes_and_rejects():
         assert L.ttt_backward_record_workspace_bytes(ctypes.byref(D), ctypes.byref(n)) == C.TTT_OK
         assert L.ttt_backward_workspace_bytes(ctypes.byref(D), ctypes.byref(full)) == C.TTT_OK
         assert n.value == full.value - al(w.value) - al(r.value)
-    # W2 alone by GD takes ttt_backward; per-chunk rates have no backward
-    for kw in (dict(last_layer_only=1, rule=C.UPD_GD), dict(chunk_rates=1)):
-        assert L.ttt_record_bytes(ctypes.byref(desc(**kw)), ctypes.byref(r), ctypes.byref(w)) == C.TTT_ERR_UNSUPPORTED
+    # W2 alone by GD walks the recurrence back too (the pair's route); per-chunk rates have no backward
+    assert L.ttt_record_bytes(ctypes.byref(desc(last_layer_only=1, rule=C.UPD_GD)), ctypes.byref(r),
+                              ctypes.byref(w)) == C.TTT_OK
+    assert L.ttt_record_bytes(ctypes.byref(desc(chunk_rates=1)), ctypes.byref(r), ctypes.byref(w)) == \
+        C.TTT_ERR_UNSUPPORTED
     assert L.ttt_record_bytes(ctypes.byref(desc()), None, ctypes.byref(w)) == C.TTT_ERR_INVALID_ARGUMENT
     D = desc()
     assert L.ttt_record_bytes(ctypes.byref(D), ctypes.byref(r), ctypes.byref(w)) == C.TTT_OK

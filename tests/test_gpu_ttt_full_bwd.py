@@ -223,3 +223,28 @@ def test_muon_weight_layouts_and_empty():
         per_batch=True)
     run(20, 3, 2, 260, 64, 128, 128, O.MASK_UPDATE_THEN_APPLY, False, rule=O.UPD_MUON, momentum=0.9)
     run(21, 2, 2, 0, 64, 96, 64, O.MASK_APPLY_THEN_UPDATE, True, rule=O.UPD_MUON_L2, momentum=0.9)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("rule,mom", [(O.UPD_GD, 0.0), (O.UPD_GD_L2, 0.9)])
+def test_training_record_last_layer(rule, mom, bf16):
+    # W2 alone by GD: the pair walks the recurrence back (with W1, W3 frozen), where ttt_backward
+    # goes through linear attention over phi; both against the oracle
+    say(f"training record, last layer, rule{rule} momentum{mom} bf16={bf16}")
+    B, H, N, d, m, chunk = 1, 2, 308, 64, 160, 96
+    (q, k, v, eta, W0), (hq, hk, hv, he, W1, W3, W2) = full_ttt_inputs(22, B, H, N, d, m, bf16)
+    dO, dWo = synth.make_ttt_grads(22, B, H, N, d, m, bf16)
+    dt = torch.bfloat16 if bf16 else torch.float32
+    kw = dict(m_h=m, momentum=mom, last_layer_only=True)
+    _, _, rec = T.ttt_forward_record(q, k, v, eta, W0, chunk, O.MASK_APPLY_THEN_UPDATE, rule, **kw)
+    got = T.ttt_backward(q, k, v, eta, W0, dev(dO, dt), chunk, O.MASK_APPLY_THEN_UPDATE, dW_out=dev(pack(*dWo)),
+                         update_rule=rule, record=rec, **kw)
+    torch.cuda.synchronize()
+    ref = O.ttt_lastlayer_backward_ref(hq, hk, hv, he, W1, W3, W2, chunk, O.MASK_APPLY_THEN_UPDATE, dO, dWo,
+                                       momentum=mom, rule=rule)
+    tol = TOL[bf16]
+    for name, g, r in zip(("dq", "dk", "dv"), got[:3], ref[:3]):
+        assert_close(host(g), r, tol, name, chunk)
+    assert_close(host(got[3]), ref[3], tol, "deta")
+    for name, g, r in zip(("dW1", "dW3", "dW2"), split(host(got[4]), d, m), ref[4]):
+        assert_close(g, r, tol, name)
