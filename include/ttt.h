@@ -35,6 +35,10 @@
  *     kernel (every launch is then followed by a stream synchronisation: a debugging aid, not for
  *     streams under graph capture).  ttt_last_error() gives a message for the latest failed call
  *     on the calling thread.
+ *   - Pass choice (testing aid): chunked linear attention's chunk updates and scan over chunks run
+ *     either as one fused pass or as two (the updates to memory, then the scan), chosen by shape;
+ *     the environment variable TTT_LIN_PASS, read on every call, forces "fused" or "split" where
+ *     no step runs between the two (not for Muon's parallel form).  Both give the same results.
  *   - Aliasing: o must not overlap q, k, v or eta.  W_out may not overlap W0.
  *   - Thread safety: calls on different streams may run concurrently; the only mutable global
  *     state is the per-thread error message and the optional launch profiler below.

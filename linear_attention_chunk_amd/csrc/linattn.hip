@@ -20,6 +20,8 @@
 // tril(Q K^T) (eta o V) and refreshes S after every sub-block.  The next sub-block's q, k, v and eta
 // are loaded into registers while the current one is computed.
 #include <algorithm>
+#include <cstdlib>
+#include <cstring>
 #include <type_traits>
 
 #include "host_common.hpp"
@@ -548,6 +550,113 @@ __global__ __launch_bounds__(kThreads) void k_lin_scan(ScanArgs<T> a) {
 // as one io-dtype plane (bf16: the state rounded once, as the products' other operands are).
 constexpr int kStatePlanes = 1;
 
+// The chunk updates and the scan in one pass (when no step runs between them).  A workgroup owns a
+// 64 x 64 tile of one scan's state, kept in registers in fp32 in the accumulator layout, and walks
+// the chunks in order: each chunk's update of its tile is the delta kernel's eta-weighted product
+// over the chunk's tokens (MFMA, accumulators zeroed per chunk), added to the state with the scan's
+// momentum, repeats and sign.  The loads run as one pipeline over the whole sequence: a stage is a
+// whole 256-token (fp32: 128-token) slice of v and k, and the next stage, which may belong to the
+// next updating chunk, is in flight while the current one is in the MFMAs, so that at one
+// workgroup per CU a stage's memory latency hides behind the previous stage.  The state each
+// chunk's queries see leaves straight from the accumulator layout as one io-dtype plane; S_out and
+// the momentum leave as the scan writes them.  dS never reaches memory.
+constexpr int kDscanTile = 64, kDscanSeg = 8;
+template <typename T> struct DscanArgs {
+    const T* k; const T* v; const float* eta; T* Sc;
+    LinStateIO io;
+    int64_t N; int dk, dv, chunk, nc, mode, ntv, ntk;
+    uint32_t flags[32];
+};
+template <typename T>
+using DscanTile = Tile<T, kDscanTile, kDscanTile, kDscanSeg, 2, 1, 1, 1, true, true, true, 4, 1>;
+
+template <typename T, bool FULL>
+__global__ __launch_bounds__(kThreads, 1) void k_lin_dscan(DscanArgs<T> a) {
+    using TD = DscanTile<T>;
+    constexpr int TS = kDscanTile, E = TD::ELEMS, KS = TD::KSTEP;
+    __shared__ __attribute__((aligned(16))) char smem[TD::LDS];
+    const int per = a.ntv * a.ntk;
+    const int lb = xcd_block(gridDim.x);
+    const int scan = lb / per, t = lb % per;
+    const int r0 = (t / a.ntk) * TS, c0 = (t % a.ntk) * TS;
+    const LinStateIO& io = a.io;
+    const bool post = a.mode == TTT_MASK_UPDATE_THEN_APPLY || a.mode == TTT_MASK_FULL;
+    const int64_t dvk = (int64_t)a.dv * a.dk;
+    auto updates = [&](int c) { return a.mode != TTT_MASK_STRIDED || ((a.flags[c >> 5] >> (c & 31)) & 1u); };
+    auto tokens = [&](int c) { return (int)std::min<int64_t>(a.chunk, a.N - (int64_t)c * a.chunk); };
+    auto next_upd = [&](int c) {
+        while (c < a.nc && !updates(c)) ++c;
+        return c;
+    };
+    // stage s of chunk c: the chunk's v and k slices from token s * KSTEP on
+    auto issue = [&](typename TD::Regs& g, int c, int s) {
+        const int64_t tok = (int64_t)scan * a.N + (int64_t)c * a.chunk;
+        const int nl = tokens(c);
+        Opnd<T> A[1] = {{a.v + tok * a.dv + r0, a.dv, a.dv - r0, nl}};
+        A[0].kscale = a.eta + tok;
+        const Opnd<T> B[1] = {{a.k + tok * a.dk + c0, a.dk, a.dk - c0, nl}};
+        TD::template issue<FULL>(g, A, B, s * KS);
+    };
+    float st[E], mm[E];
+    TD::for_each_pos([&](int idx, int row, int col) {
+        const bool in = FULL || (r0 + row < a.dv && c0 + col < a.dk);
+        const int64_t e = (int64_t)(r0 + row) * a.dk + c0 + col;
+        st[idx] = (io.S0 && in) ? io.S0[(io.s0_heads ? scan % io.s0_heads : scan) * io.s0_stride + e] : 0.f;
+        mm[idx] = (io.M0 && in) ? io.msign * io.M0[(int64_t)scan * io.m_stride + e] : 0.f;
+    });
+    auto put = [&](int c) {  // the state chunk c's queries see
+        T* dst = a.Sc + ((int64_t)scan * a.nc + c) * dvk;
+        TD::for_each_pos([&](int idx, int row, int col) {
+            if (FULL || (r0 + row < a.dv && c0 + col < a.dk))
+                dst[(int64_t)(r0 + row) * a.dk + c0 + col] = Elt<T>::st(st[idx]);
+        });
+    };
+    TD tl;
+    typename TD::Regs g;
+    int ic = next_upd(0), is = 0;  // the stage in flight in g
+    if (ic < a.nc) issue(g, ic, 0);
+    for (int c = 0; c < a.nc; ++c) {
+        if (!post) put(c);
+        if (c == ic) {  // an updating chunk: its stages are the ones in flight
+            tl.zero();
+            const int ns = (tokens(c) + KS - 1) / KS;
+            for (int s = 0; s < ns; ++s) {
+                lds_barrier();  // every wave is done with the previous stage
+                TD::template put<FULL>(g, smem);
+                if (s + 1 < ns) {
+                    is = s + 1;
+                } else {
+                    ic = next_upd(c + 1);
+                    is = 0;
+                }
+                if (ic < a.nc) issue(g, ic, is);
+                lds_barrier();
+                tl.template compute<PM1>(smem);
+            }
+            TD::for_each_pos([&](int idx, int, int) {
+                const int i = idx / (TD::FN * 16), j = (idx / 16) % TD::FN, r = idx % 16;
+                const float d = io.dsign * tl.acc[0][i][j][r];
+                for (int k = 0; k < io.reps; ++k) {
+                    if (io.mom) {
+                        mm[idx] = io.beta * mm[idx] + d;
+                        st[idx] += mm[idx];
+                    } else {
+                        st[idx] += d;
+                    }
+                }
+            });
+        }
+        if (post) put(c);
+    }
+    TD::for_each_pos([&](int idx, int row, int col) {
+        if (FULL || (r0 + row < a.dv && c0 + col < a.dk)) {
+            const int64_t e = (int64_t)(r0 + row) * a.dk + c0 + col;
+            if (io.Sout) io.Sout[(int64_t)scan * io.sout_stride + e] = st[idx];
+            if (io.Mout) io.Mout[(int64_t)scan * io.m_stride + e] = io.msign * mm[idx];
+        }
+    });
+}
+
 // o (chunk c's tokens x d_v) = q_c S_c^T, contracting over d_k
 template <typename T> struct ApplyArgs {
     const T* q; const T* Sc; T* o;
@@ -827,6 +936,23 @@ static ttt_status launch_scan(const linattn_desc& D, int64_t nc, int mode, const
     return check_launch("k_lin_scan", st);
 }
 
+// The fused pass is latency-bound (one stage in flight per workgroup), so it pays only where its
+// 64 x 64 state tiles make at least one workgroup per CU and the chunk updates it keeps out of
+// memory (4 d_v d_k bytes per chunk, written and read back) are at least half of the chunk's k and
+// v bytes; d_k and d_v of 256 at most, where the delta kernel's 128-wide MFMA tiles do not win on
+// arithmetic.  Token-causal blocks (128 tokens) take the two-pass path.  The environment variable
+// TTT_LIN_PASS, read on every call, overrides the choice ("fused" or "split"): both passes give the
+// same bits, so tests run small cases through each.
+static bool dscan_pays(const linattn_desc& D, int64_t S, int64_t chunk) {
+    if (const char* e = getenv("TTT_LIN_PASS")) {
+        if (!strcmp(e, "fused")) return true;
+        if (!strcmp(e, "split")) return false;
+    }
+    if (D.mask == TTT_MASK_TOKEN_CAUSAL || D.d_k > 256 || D.d_v > 256) return false;
+    const int64_t wgs = S * cdiv(D.d_v, kDscanTile) * cdiv(D.d_k, kDscanTile);
+    return wgs >= 256 && 4 * (int64_t)D.d_v * D.d_k >= chunk * (D.d_k + D.d_v);
+}
+
 template <typename T>
 static ttt_status run_lin_parallel(const linattn_desc& D, LinArgs<T> a, char* ws, hipStream_t st,
                                    const LinStateIO& io) {
@@ -835,16 +961,46 @@ static ttt_status run_lin_parallel(const linattn_desc& D, LinArgs<T> a, char* ws
     const int64_t S = (int64_t)D.B * D.H, nc = cdiv(D.N, chunk), dvk = (int64_t)D.d_v * D.d_k;
     float* dS = (float*)ws;
     T* Sc = (T*)(ws + align256((size_t)(S * nc * dvk * 4)));  // kStatePlanes io-dtype planes per chunk
-    // 1. per-chunk updates
-    ttt_status rc = launch_delta<T, true>(D, chunk, nc, D.mask, a.flags, a.k, a.v, a.eta, dS, st);
-    if (rc != TTT_OK) return rc;
-    // (the caller's step between the updates and the scan, which may hand the scan another buffer)
-    const float* scan_src = dS;
-    if (io.between && (rc = io.between(io.between_ctx, dS, &scan_src, st)) != TTT_OK) return rc;
-    // 2. states seen by each chunk, and S_out (a causal block sees the state before it)
-    rc = launch_scan<T>(D, nc, causal ? TTT_MASK_APPLY_THEN_UPDATE : D.mask, a.flags, scan_src, Sc, io, 0,
-                        kStatePlanes, st);
-    if (rc != TTT_OK) return rc;
+    ttt_status rc;
+    const int smode = causal ? TTT_MASK_APPLY_THEN_UPDATE : D.mask;  // a causal block sees the state before it
+    if (!io.between && dscan_pays(D, S, chunk)) {
+        // 1 + 2 in one pass
+        DscanArgs<T> ds{};
+        ds.k = a.k;
+        ds.v = a.v;
+        ds.eta = a.eta;
+        ds.Sc = Sc;
+        ds.io = io;
+        ds.N = D.N;
+        ds.dk = D.d_k;
+        ds.dv = D.d_v;
+        ds.chunk = (int)chunk;
+        ds.nc = (int)nc;
+        ds.mode = smode;
+        for (int w = 0; w < 32; ++w) ds.flags[w] = a.flags[w];
+        ds.ntv = (int)cdiv(D.d_v, kDscanTile);
+        ds.ntk = (int)cdiv(D.d_k, kDscanTile);
+        // unmasked staging when every tile is whole and every chunk a whole number of stages
+        const bool full = D.d_v % kDscanTile == 0 && D.d_k % kDscanTile == 0 && chunk % DscanTile<T>::KSTEP == 0 &&
+                          D.N % DscanTile<T>::KSTEP == 0;
+        const dim3 grid((unsigned)(S * ds.ntv * ds.ntk));
+        {
+            ProfScope ps(PK_LIN_SCAN, st);
+            if (full) hipLaunchKernelGGL((k_lin_dscan<T, true>), grid, dim3(kThreads), 0, st, ds);
+            else hipLaunchKernelGGL((k_lin_dscan<T, false>), grid, dim3(kThreads), 0, st, ds);
+        }
+        if ((rc = check_launch("k_lin_dscan", st)) != TTT_OK) return rc;
+    } else {
+        // 1. per-chunk updates
+        rc = launch_delta<T, true>(D, chunk, nc, D.mask, a.flags, a.k, a.v, a.eta, dS, st);
+        if (rc != TTT_OK) return rc;
+        // (the caller's step between the updates and the scan, which may hand the scan another buffer)
+        const float* scan_src = dS;
+        if (io.between && (rc = io.between(io.between_ctx, dS, &scan_src, st)) != TTT_OK) return rc;
+        // 2. states seen by each chunk, and S_out
+        rc = launch_scan<T>(D, nc, smode, a.flags, scan_src, Sc, io, 0, kStatePlanes, st);
+        if (rc != TTT_OK) return rc;
+    }
     // 3. apply
     ApplyArgs<T> aa{};
     aa.q = a.q;

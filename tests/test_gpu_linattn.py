@@ -31,6 +31,7 @@ def run(seed, B, H, N, dk, dv, chunk, mask, bf16, S0=False, flags=None):
     # per (batch, head), per chunk (of 128 tokens in token-causal mode) and per row as well
     assert_close(host(o), o_ref, TOL[bf16], "o", chunk if mask != O.MASK_TOKEN_CAUSAL else 128)
     assert_close(host(S), S_ref, TOL[bf16], "S_out")
+    return o, S
 
 
 @pytest.mark.parametrize("bf16", [False, True])
@@ -52,6 +53,34 @@ def test_strided_chunk_parallel(bf16):
     run(5, 1, 2, 700, 64, 64, 128, O.MASK_STRIDED, bf16, S0=True, flags=[1, 0, 1, 1, 0, 1])
     # and the all-zero flags: the state never moves
     run(6, 1, 1, 300, 64, 64, 128, O.MASK_STRIDED, bf16, S0=True, flags=[0, 0, 0])
+
+
+PASS_CASES = [
+    # seed, B, H, N, d_k, d_v, chunk, mask, S0, strided flags
+    (21, 1, 3, 300, 64, 96, 80, O.MASK_APPLY_THEN_UPDATE, True, None),    # ragged chunk, partial tiles
+    (22, 1, 3, 300, 64, 96, 80, O.MASK_UPDATE_THEN_APPLY, True, None),
+    (23, 2, 1, 150, 32, 64, 150, O.MASK_FULL, True, None),
+    (24, 1, 2, 700, 64, 64, 128, O.MASK_STRIDED, True, [1, 0, 1, 1, 0, 1]),
+    (25, 1, 1, 300, 64, 64, 128, O.MASK_STRIDED, True, [0, 0, 0]),
+    (26, 1, 2, 1024, 128, 128, 256, O.MASK_APPLY_THEN_UPDATE, False, None),  # whole tiles and stages
+    (27, 1, 2, 1100, 96, 160, 512, O.MASK_UPDATE_THEN_APPLY, True, None),    # several stages per chunk
+    (28, 1, 1, 600, 384, 160, 64, O.MASK_TOKEN_CAUSAL, True, None),
+]
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("case", PASS_CASES)
+def test_fused_and_split_passes(case, bf16, monkeypatch):
+    # the chunk updates and the scan as one fused pass and as two: each against the oracle, and the
+    # two bit for bit (the same token sums in the same order, the same fp32 state additions)
+    seed, B, H, N, dk, dv, chunk, mask, S0, flags = case
+    got = {}
+    for p in ("fused", "split"):
+        monkeypatch.setenv("TTT_LIN_PASS", p)
+        say(f"pass {p}")
+        got[p] = run(seed, B, H, N, dk, dv, chunk, mask, bf16, S0=S0, flags=flags)
+    for a, b in zip(got["fused"], got["split"]):
+        assert torch.equal(a, b)
 
 
 @pytest.mark.parametrize("bf16", [False, True])
@@ -121,9 +150,10 @@ def test_linear_attention_workload_full_size(mask):
         assert_close(host(S[b, h]), S_ref, 2e-2, "S_out")
 
 
+@pytest.mark.parametrize("lin_pass", ["fused", "split"])
 @pytest.mark.parametrize("mask,chunk", [(O.MASK_APPLY_THEN_UPDATE, 128), (O.MASK_UPDATE_THEN_APPLY, 128),
                                         (O.MASK_TOKEN_CAUSAL, 64), (O.MASK_APPLY_THEN_UPDATE, 16)])
-def test_nan_in_v_reaches_exactly_the_outputs_that_depend_on_it(mask, chunk):
+def test_nan_in_v_reaches_exactly_the_outputs_that_depend_on_it(mask, chunk, lin_pass, monkeypatch):
     """A NaN in value entry e of token t enters the state's row e only, so only column e of the
     outputs can turn NaN, and every other output and every other scan keep the bits of the run
     without it.  Under the chunked masks the NaN set is exactly the tokens that see token t (from
@@ -131,6 +161,7 @@ def test_nan_in_v_reaches_exactly_the_outputs_that_depend_on_it(mask, chunk):
     128, sequential kernel at chunk 16.  In token-causal mode every t' >= t sees it; the intra-block
     product P v of the 128-token block holding t also multiplies the NaN by the zeros of the causal
     mask, so the block's earlier tokens turn NaN as well (0 * NaN is NaN in any MFMA)."""
+    monkeypatch.setenv("TTT_LIN_PASS", lin_pass)  # (both ways through the chunk updates and the scan)
     B, H, N, dk, dv = 1, 2, 512, 64, 64
     q, k, v, eta = synth.make_linattn_inputs(43, B, H, N, dk, dv, True)
     dt = torch.bfloat16

@@ -327,6 +327,16 @@ def test_parallel_form_last_layer(mask, mom, inner, ascent, flags, bf16):
               ascent=ascent, parallel=True)
 
 
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("mask,mom,inner,ascent,flags", PARALLEL_CASES)
+def test_parallel_form_last_layer_fused_pass(mask, mom, inner, ascent, flags, bf16, monkeypatch):
+    # the same through the linear attention's fused update-and-scan pass (which the shape alone
+    # would not pick here): W0 as the state per head, the momentum, repeats and sign of the steps
+    monkeypatch.setenv("TTT_LIN_PASS", "fused")
+    run_small(30, 1, 2, 308, 64, 160, 96, mask, O.UPD_GD, bf16, mom, last=True, flags=flags, inner=inner,
+              ascent=ascent, parallel=True)
+
+
 PARALLEL_MUON_CASES = [
     # mask, momentum, ascent, strided flags, Newton-Schulz steps
     (O.MASK_APPLY_THEN_UPDATE, 0.9, False, None, 5),
@@ -382,9 +392,12 @@ def test_parallel_form_full_mask(bf16):
     run_small(31, 2, 1, 200, 32, 96, 200, O.MASK_FULL, O.UPD_GD, bf16, last=True, parallel=True)
 
 
-def test_parallel_form_matches_recurrence():
+@pytest.mark.parametrize("lin_pass", ["fused", "split"])
+def test_parallel_form_matches_recurrence(lin_pass, monkeypatch):
     # several 256-token feature tiles and 128-wide state tiles: the parallel form with W0 given per
-    # (batch, head) against the chunk recurrence with W0 per head, momentum carried in M
+    # (batch, head) against the chunk recurrence with W0 per head, momentum carried in M (and out of
+    # it), through either pass of the linear attention's chunk updates and scan
+    monkeypatch.setenv("TTT_LIN_PASS", lin_pass)
     B, H, N, d, m, chunk = 2, 2, 1100, 128, 384, 256
     say(f"parallel form vs recurrence B{B} H{H} N{N} d{d} m{m} b{chunk}")
     (q, k, v, eta, W0), _ = full_ttt_inputs(32, B, H, N, d, m, True)
