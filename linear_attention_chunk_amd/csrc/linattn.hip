@@ -936,6 +936,39 @@ static ttt_status launch_scan(const linattn_desc& D, int64_t nc, int mode, const
     return check_launch("k_lin_scan", st);
 }
 
+// Chunk updates and scan in one pass (k_lin_dscan): the states each chunk's queries see, as one
+// io-dtype plane per chunk, with the entry/exit state and momentum of io (no step between them).
+template <typename T>
+static ttt_status launch_dscan(const linattn_desc& D, int64_t chunk, int64_t nc, int mode, const uint32_t (&flags)[32],
+                               const T* k, const T* v, const float* eta, T* Sc, const LinStateIO& io, hipStream_t st) {
+    const int64_t S = (int64_t)D.B * D.H;
+    DscanArgs<T> ds{};
+    ds.k = k;
+    ds.v = v;
+    ds.eta = eta;
+    ds.Sc = Sc;
+    ds.io = io;
+    ds.N = D.N;
+    ds.dk = D.d_k;
+    ds.dv = D.d_v;
+    ds.chunk = (int)chunk;
+    ds.nc = (int)nc;
+    ds.mode = mode;
+    for (int w = 0; w < 32; ++w) ds.flags[w] = flags[w];
+    ds.ntv = (int)cdiv(D.d_v, kDscanTile);
+    ds.ntk = (int)cdiv(D.d_k, kDscanTile);
+    // unmasked staging when every tile is whole and every chunk a whole number of stages
+    const bool full = D.d_v % kDscanTile == 0 && D.d_k % kDscanTile == 0 && chunk % DscanTile<T>::KSTEP == 0 &&
+                      D.N % DscanTile<T>::KSTEP == 0;
+    const dim3 grid((unsigned)(S * ds.ntv * ds.ntk));
+    {
+        ProfScope ps(PK_LIN_SCAN, st);
+        if (full) hipLaunchKernelGGL((k_lin_dscan<T, true>), grid, dim3(kThreads), 0, st, ds);
+        else hipLaunchKernelGGL((k_lin_dscan<T, false>), grid, dim3(kThreads), 0, st, ds);
+    }
+    return check_launch("k_lin_dscan", st);
+}
+
 // The fused pass is latency-bound (one stage in flight per workgroup), so it pays only where its
 // 64 x 64 state tiles make at least one workgroup per CU and the chunk updates it keeps out of
 // memory (4 d_v d_k bytes per chunk, written and read back) are at least half of the chunk's k and
@@ -965,31 +998,7 @@ static ttt_status run_lin_parallel(const linattn_desc& D, LinArgs<T> a, char* ws
     const int smode = causal ? TTT_MASK_APPLY_THEN_UPDATE : D.mask;  // a causal block sees the state before it
     if (!io.between && dscan_pays(D, S, chunk)) {
         // 1 + 2 in one pass
-        DscanArgs<T> ds{};
-        ds.k = a.k;
-        ds.v = a.v;
-        ds.eta = a.eta;
-        ds.Sc = Sc;
-        ds.io = io;
-        ds.N = D.N;
-        ds.dk = D.d_k;
-        ds.dv = D.d_v;
-        ds.chunk = (int)chunk;
-        ds.nc = (int)nc;
-        ds.mode = smode;
-        for (int w = 0; w < 32; ++w) ds.flags[w] = a.flags[w];
-        ds.ntv = (int)cdiv(D.d_v, kDscanTile);
-        ds.ntk = (int)cdiv(D.d_k, kDscanTile);
-        // unmasked staging when every tile is whole and every chunk a whole number of stages
-        const bool full = D.d_v % kDscanTile == 0 && D.d_k % kDscanTile == 0 && chunk % DscanTile<T>::KSTEP == 0 &&
-                          D.N % DscanTile<T>::KSTEP == 0;
-        const dim3 grid((unsigned)(S * ds.ntv * ds.ntk));
-        {
-            ProfScope ps(PK_LIN_SCAN, st);
-            if (full) hipLaunchKernelGGL((k_lin_dscan<T, true>), grid, dim3(kThreads), 0, st, ds);
-            else hipLaunchKernelGGL((k_lin_dscan<T, false>), grid, dim3(kThreads), 0, st, ds);
-        }
-        if ((rc = check_launch("k_lin_dscan", st)) != TTT_OK) return rc;
+        if ((rc = launch_dscan<T>(D, chunk, nc, smode, a.flags, a.k, a.v, a.eta, Sc, io, st)) != TTT_OK) return rc;
     } else {
         // 1. per-chunk updates
         rc = launch_delta<T, true>(D, chunk, nc, D.mask, a.flags, a.k, a.v, a.eta, dS, st);
@@ -1462,7 +1471,6 @@ ttt_status lin_chunked_bwd(const linattn_desc& D, const uint32_t (&flags)[32], c
     ttt_status rc;
     if (D.N > 0) {
         // the states the chunks' queries saw
-        if ((rc = launch_delta<T, true>(D, chunk, nc, D.mask, flags, k, v, eta, dS, st)) != TTT_OK) return rc;
         LinStateIO fio;
         fio.S0 = io.S0;
         fio.s0_stride = io.s0_stride;
@@ -1471,8 +1479,13 @@ ttt_status lin_chunked_bwd(const linattn_desc& D, const uint32_t (&flags)[32], c
         fio.reps = io.reps;
         fio.mom = io.mom;
         fio.beta = io.beta;
-        if (io.norm) rc = row_scan(dS, Sc, fio, 0);
-        else rc = launch_scan<T>(D, nc, D.mask, flags, dS, Sc, fio, 0, kBwdPlanes, st);
+        if (!io.norm && dscan_pays(D, S, chunk)) {
+            rc = launch_dscan<T>(D, chunk, nc, D.mask, flags, k, v, eta, Sc, fio, st);
+        } else {
+            if ((rc = launch_delta<T, true>(D, chunk, nc, D.mask, flags, k, v, eta, dS, st)) != TTT_OK) return rc;
+            if (io.norm) rc = row_scan(dS, Sc, fio, 0);
+            else rc = launch_scan<T>(D, nc, D.mask, flags, dS, Sc, fio, 0, kBwdPlanes, st);
+        }
         if (rc != TTT_OK) return rc;
         // D_c = sum over the chunk of dO q^T, every chunk
         if ((rc = launch_delta<T, false>(D, chunk, nc, TTT_MASK_APPLY_THEN_UPDATE, all, q, dO, nullptr, dS, st)) !=

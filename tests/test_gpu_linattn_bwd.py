@@ -84,6 +84,31 @@ def test_wide_heads(bf16):
     run(9, 1, 1, 600, 96, 160, 256, O.MASK_UPDATE_THEN_APPLY, bf16, S0=False)
 
 
+PASS_CASES = [
+    # seed, B, H, N, d_k, d_v, chunk, mask, strided flags
+    (21, 1, 3, 300, 64, 96, 80, O.MASK_APPLY_THEN_UPDATE, None),
+    (22, 1, 3, 300, 64, 96, 80, O.MASK_UPDATE_THEN_APPLY, None),
+    (23, 2, 1, 150, 32, 64, 150, O.MASK_FULL, None),
+    (24, 1, 2, 700, 64, 64, 128, O.MASK_STRIDED, [1, 0, 1, 1, 0, 1]),
+    (25, 1, 2, 1024, 128, 128, 256, O.MASK_APPLY_THEN_UPDATE, None),
+]
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("case", PASS_CASES)
+def test_fused_and_split_passes(case, bf16, monkeypatch):
+    # the forward states rebuilt by the fused update-and-scan pass and by the two-pass one: each
+    # against the oracle, and the two bit for bit
+    seed, B, H, N, dk, dv, chunk, mask, flags = case
+    got = {}
+    for p in ("fused", "split"):
+        monkeypatch.setenv("TTT_LIN_PASS", p)
+        say(f"pass {p}")
+        got[p], _ = run(seed, B, H, N, dk, dv, chunk, mask, bf16, flags=flags)
+    for a, b in zip(got["fused"], got["split"]):
+        assert torch.equal(a, b)
+
+
 def test_small_chunks_and_defaults():
     # many small chunks (each a partial tile); no S0, no dS_out, no dS0 requested
     run(7, 1, 2, 200, 64, 64, 16, O.MASK_APPLY_THEN_UPDATE, True, S0=False, dS_out=False, want_dS0=False)

@@ -110,6 +110,16 @@ def test_momentum(mask, chunk, flags, inner, ascent, mom, bf16):
     run(11, 1, 2, 308, 64, 160, chunk, mask, bf16, flags=flags, inner=inner, ascent=ascent, momentum=mom)
 
 
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("mask,chunk,flags,inner,ascent,mom", MOMENTUM_CASES)
+def test_momentum_fused_pass(mask, chunk, flags, inner, ascent, mom, bf16, monkeypatch):
+    # the same with the forward states rebuilt by the linear attention's fused update-and-scan pass
+    # (which these shapes alone would not pick): W2 per head as the entry state, the momentum, the
+    # repeats and the sign of the steps
+    monkeypatch.setenv("TTT_LIN_PASS", "fused")
+    run(11, 1, 2, 308, 64, 160, chunk, mask, bf16, flags=flags, inner=inner, ascent=ascent, momentum=mom)
+
+
 L2_CASES = [
     # mask, chunk, strided flags, inner steps, ascent, momentum
     (O.MASK_APPLY_THEN_UPDATE, 96, None, 1, False, 0.0),
