@@ -706,33 +706,36 @@ __global__ __launch_bounds__(kThreads, 2) void k_lin_apply(ApplyArgs<T> a) {
 // tokens; the delta and scan kernels give every block the state S_c before it (apply-then-update
 // order), and this kernel adds the block's own causal term.  For query token i of the block
 //   o_i = S_c q_i + sum over the block's tokens j <= i of eta_j (k_j . q_i) v_j,
-// that is o = q S_c^T + tril(q k^T) diag(eta) v.  One workgroup takes a block and 128 columns of
-// d_v.  q k^T and q S_c^T are one contraction over d_k with two accumulators (q staged once).  The
-// masked, eta-scaled q k^T block is rounded to the io dtype straight into the A regions of the LDS
-// stages of the P v product (v through the transposing stager), as the sequential kernel rounds it.
-// P v is added to q S_c^T through an fp32 LDS buffer, because the transposing stager leaves P v in
-// another column order.
-constexpr int kCausalBlock = 128;
+// that is o = q S_c^T + tril(q k^T) diag(eta) v.  One workgroup takes 64 query rows of a block and
+// 128 columns of d_v (the two row halves of a block are neighbours, so k, v and S_c come from the
+// same L2).  q k^T and q S_c^T are one contraction over d_k with two accumulators (q staged once).
+// The masked, eta-scaled q k^T rows are rounded to the io dtype straight into the A regions of the
+// LDS stages of the P v product (v through the transposing stager), as the sequential kernel rounds
+// them; the first half's rows see only the block's first 64 keys, so its P v stops there.  P v is
+// added to q S_c^T through an fp32 LDS buffer, because the transposing stager leaves P v in another
+// column order.
+constexpr int kCausalBlock = 128, kCausalRows = 64;
 
-// One workgroup per CU: its three accumulators and v's early-loaded stages need more than the 256
-// VGPRs that two workgroups per CU would leave each wave.
 template <typename T>
-__global__ __launch_bounds__(kThreads, 1) void k_lin_apply_causal(ApplyArgs<T> a) {  // fp32: 147 KB LDS
+__global__ __launch_bounds__(kThreads, 2) void k_lin_apply_causal(ApplyArgs<T> a) {
     static_assert(kStatePlanes == 1, "q S_c^T is one accumulator");
-    using TQ = Tile<T, kCausalBlock, kCausalBlock, 1, 2, 1, 2, 2, false, false>;  // q k^T and q S_c^T
-    using TD = Tile<T, kCausalBlock, kApplyCols, 2, 2, 1, 1, 1, false, true>;     // P v, P in LDS
+    using TQ = Tile<T, kCausalRows, kCausalBlock, 1, 2, 1, 2, 2, false, false>;  // q k^T and q S_c^T
+    using TD = Tile<T, kCausalRows, kApplyCols, 2, 2, 1, 1, 1, false, true>;     // P v, P in LDS
     constexpr int NST = kCausalBlock / TD::KSTEP;  // key-token stages of P v, all resident
     constexpr int OP = kApplyCols + 4;             // fp32 combine-buffer pitch (floats)
-    constexpr int LDSB = std::max(std::max(TQ::LDS, NST * TD::STAGE), kCausalBlock * OP * 4);
-    static_assert(kCausalBlock % TD::KSTEP == 0 && kApplyRows == kCausalBlock && kApplyCols == kCausalBlock,
+    constexpr int LDSB = std::max(std::max(TQ::LDS, NST * TD::STAGE), kCausalRows * OP * 4);
+    static_assert(kCausalBlock % TD::KSTEP == 0 && kCausalBlock == 2 * kCausalRows && kApplyCols == kCausalBlock,
                   "block and tile shapes");
     __shared__ __attribute__((aligned(16))) char smem[LDSB];
     const int lb = xcd_block(gridDim.x);
-    const int unit = lb / a.ntv, cv = lb % a.ntv;
+    const int unit = lb / (2 * a.ntv), cv = (lb / 2) % a.ntv, h = lb % 2;
     const int scan = unit / a.nc, c = unit % a.nc;
-    const int c0 = cv * kApplyCols;
+    const int c0 = cv * kApplyCols, r0 = h * kCausalRows;
     const int64_t tok = (int64_t)scan * a.N + (int64_t)c * kCausalBlock;
     const int nl = (int)std::min<int64_t>(kCausalBlock, a.N - (int64_t)c * kCausalBlock);
+    const int nr = nl - r0;  // query rows of this workgroup
+    if (nr <= 0) return;     // a ragged last block without a second half
+    const int nst = h ? NST : NST / 2;  // the key stages these rows see
 
     // v's stages are loaded first, so they are in flight during the first contraction
     const Opnd<T> Bv = {a.v + tok * a.dv + c0, a.dv, a.dv - c0, nl};  // rows: d_v columns; k: tokens
@@ -740,6 +743,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_lin_apply_causal(ApplyArgs<T> a
     typename TD::SB gv[NST];
 #pragma unroll
     for (int st = 0; st < NST; ++st) {
+        if (st >= nst) break;
         if (vfull) gv[st].template load<true>(Bv, st * TD::KSTEP);
         else gv[st].template load<false>(Bv, st * TD::KSTEP);
     }
@@ -751,7 +755,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_lin_apply_causal(ApplyArgs<T> a
 
     // P = q k^T over the block (rows: query tokens, columns: key tokens) and q S_c^T (columns: d_v)
     const int64_t dvk = (int64_t)a.dv * a.dk;
-    const Opnd<T> Aq[1] = {{a.q + tok * a.dk, a.dk, nl, a.dk}};
+    const Opnd<T> Aq[1] = {{a.q + (tok + r0) * a.dk, a.dk, nr, a.dk}};
     const Opnd<T> Bks[2] = {{a.k + tok * a.dk, a.dk, nl, a.dk},
                             {a.Sc + (int64_t)unit * dvk + (int64_t)c0 * a.dk, a.dk, a.dv - c0, a.dk}};
     TQ tq;
@@ -760,14 +764,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_lin_apply_causal(ApplyArgs<T> a
     {
         int idx = 0;
         tq.for_each([&](const float (&v)[2], int row, int col) {
-            const float val = (col <= row && col < nl) ? v[0] * ek[(idx / 16) % TQ::FN] : 0.f;
+            const float val = (col <= r0 + row && col < nl) ? v[0] * ek[(idx / 16) % TQ::FN] : 0.f;
             ++idx;
-            *reinterpret_cast<T*>(smem + (col / TD::KSTEP) * TD::STAGE + row * TD::PITCH +
-                                  (col % TD::KSTEP) * (int)sizeof(T)) = Elt<T>::st(val);
+            if (col < nst * TD::KSTEP)
+                *reinterpret_cast<T*>(smem + (col / TD::KSTEP) * TD::STAGE + row * TD::PITCH +
+                                      (col % TD::KSTEP) * (int)sizeof(T)) = Elt<T>::st(val);
         });
     }
 #pragma unroll
     for (int st = 0; st < NST; ++st) {
+        if (st >= nst) break;
         if (vfull) gv[st].template store<true>(smem + st * TD::STAGE + TD::A_BYTES);
         else gv[st].template store<false>(smem + st * TD::STAGE + TD::A_BYTES);
     }
@@ -775,19 +781,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_lin_apply_causal(ApplyArgs<T> a
     TD td;
     td.zero();
 #pragma unroll
-    for (int st = 0; st < NST; ++st) td.template compute<PM1>(smem + st * TD::STAGE);
+    for (int st = 0; st < NST; ++st) {
+        if (st >= nst) break;
+        td.template compute<PM1>(smem + st * TD::STAGE);
+    }
     lds_barrier();  // every wave is done with P v's stages
     float* buf = reinterpret_cast<float*>(smem);
     td.for_each([&](const float (&v)[1], int row, int col) { buf[row * OP + col] = v[0]; });
     __syncthreads();
-    T* O = a.o + tok * a.dv + c0;
+    T* O = a.o + (tok + r0) * a.dv + c0;
     auto epi = [&](auto check) {
         tq.for_each([&](const float (&v)[2], int row, int col) {
-            if (!decltype(check)::value || (row < nl && c0 + col < a.dv))
+            if (!decltype(check)::value || (row < nr && c0 + col < a.dv))
                 O[(uint32_t)row * (uint32_t)a.dv + (uint32_t)col] = Elt<T>::st(v[1] + buf[row * OP + col]);
         });
     };
-    if (nl == kCausalBlock && c0 + kApplyCols <= a.dv) epi(std::false_type{});
+    if (nr >= kCausalRows && c0 + kApplyCols <= a.dv) epi(std::false_type{});
     else epi(std::true_type{});
 }
 
@@ -1028,8 +1037,8 @@ static ttt_status run_lin_parallel(const linattn_desc& D, LinArgs<T> a, char* ws
     aa.eta = a.eta;
     {
         ProfScope ps(PK_LIN_APPLY, st);
-        if (causal)  // one token tile per block
-            hipLaunchKernelGGL(k_lin_apply_causal<T>, dim3((unsigned)(S * nc * aa.ntv)), dim3(kThreads), 0, st, aa);
+        if (causal)  // two workgroups of query rows per block
+            hipLaunchKernelGGL(k_lin_apply_causal<T>, dim3((unsigned)(S * nc * aa.ntv * 2)), dim3(kThreads), 0, st, aa);
         else
             hipLaunchKernelGGL(k_lin_apply<T>, dim3((unsigned)(S * nc * aa.ntt * aa.ntv)), dim3(kThreads), 0, st, aa);
     }

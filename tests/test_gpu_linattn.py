@@ -159,8 +159,9 @@ def test_nan_in_v_reaches_exactly_the_outputs_that_depend_on_it(mask, chunk, lin
     without it.  Under the chunked masks the NaN set is exactly the tokens that see token t (from
     the next chunk on, or from t's own chunk under update-then-apply): chunk-parallel path at chunk
     128, sequential kernel at chunk 16.  In token-causal mode every t' >= t sees it; the intra-block
-    product P v of the 128-token block holding t also multiplies the NaN by the zeros of the causal
-    mask, so the block's earlier tokens turn NaN as well (0 * NaN is NaN in any MFMA)."""
+    product P v of the 64 query rows holding t (a 128-token block's P v runs in two 64-row halves,
+    the first over the block's first 64 keys only) also multiplies the NaN by the zeros of the causal
+    mask, so those rows' earlier tokens turn NaN as well (0 * NaN is NaN in any MFMA)."""
     monkeypatch.setenv("TTT_LIN_PASS", lin_pass)  # (both ways through the chunk updates and the scan)
     B, H, N, dk, dv = 1, 2, 512, 64, 64
     q, k, v, eta = synth.make_linattn_inputs(43, B, H, N, dk, dv, True)
@@ -173,7 +174,7 @@ def test_nan_in_v_reaches_exactly_the_outputs_that_depend_on_it(mask, chunk, lin
     o_n, S_n = T.linattn_forward(qd, kd, vn, ed, chunk, mask)
     torch.cuda.synchronize()
     if mask == O.MASK_TOKEN_CAUSAL:
-        first = (t // 128) * 128
+        first = (t // 64) * 64
     elif mask == O.MASK_UPDATE_THEN_APPLY:
         first = (t // chunk) * chunk
     else:
