@@ -719,7 +719,7 @@ constexpr int kCausalBlock = 128, kCausalRows = 64;
 template <typename T>
 __global__ __launch_bounds__(kThreads, 2) void k_lin_apply_causal(ApplyArgs<T> a) {
     static_assert(kStatePlanes == 1, "q S_c^T is one accumulator");
-    using TQ = Tile<T, kCausalRows, kCausalBlock, 1, 2, 1, 2, 2, false, false>;  // q k^T and q S_c^T
+    using TQ = Tile<T, kCausalRows, kCausalBlock, 2, 2, 1, 2, 2, false, false, false, 4, 1>;  // q k^T, q S_c^T
     using TD = Tile<T, kCausalRows, kApplyCols, 2, 2, 1, 1, 1, false, true>;     // P v, P in LDS
     constexpr int NST = kCausalBlock / TD::KSTEP;  // key-token stages of P v, all resident
     constexpr int OP = kApplyCols + 4;             // fp32 combine-buffer pitch (floats)
