@@ -669,7 +669,7 @@ constexpr int kApplyRows = 128, kApplyCols = 128;
 template <typename T>
 __global__ __launch_bounds__(kThreads, 2) void k_lin_apply(ApplyArgs<T> a) {
     constexpr int PLANES = kStatePlanes;
-    using TA = Tile<T, kApplyRows, kApplyCols, 1, 2, 1, PLANES, PLANES, false, false>;
+    using TA = Tile<T, kApplyRows, kApplyCols, 2, 2, 1, PLANES, PLANES, false, false>;  // 64-wide stages
     using PM = typename std::conditional<PLANES == 2, PMQ, PM1>::type;
     __shared__ __attribute__((aligned(16))) char smem[TA::LDS];
     const int lb = xcd_block(gridDim.x);
