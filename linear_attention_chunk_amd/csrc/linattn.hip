@@ -559,7 +559,10 @@ constexpr int kStatePlanes = 1;
 // next updating chunk, is in flight while the current one is in the MFMAs, so that at one
 // workgroup per CU a stage's memory latency hides behind the previous stage.  The state each
 // chunk's queries see leaves straight from the accumulator layout as one io-dtype plane; S_out and
-// the momentum leave as the scan writes them.  dS never reaches memory.
+// the momentum leave as the scan writes them.  dS never reaches memory.  Chunks of half a stage
+// (128 tokens in bf16, token-causal mode's blocks) go two to a stage (PAIR): the stage's first
+// half of k windows forms one chunk's update, the second half the next chunk's, each in
+// accumulators of its own.
 constexpr int kDscanTile = 64, kDscanSeg = 8;
 template <typename T> struct DscanArgs {
     const T* k; const T* v; const float* eta; T* Sc;
@@ -570,10 +573,11 @@ template <typename T> struct DscanArgs {
 template <typename T>
 using DscanTile = Tile<T, kDscanTile, kDscanTile, kDscanSeg, 2, 1, 1, 1, true, true, true, 4, 1>;
 
-template <typename T, bool FULL>
+template <typename T, bool FULL, bool PAIR>
 __global__ __launch_bounds__(kThreads, 1) void k_lin_dscan(DscanArgs<T> a) {
     using TD = DscanTile<T>;
     constexpr int TS = kDscanTile, E = TD::ELEMS, KS = TD::KSTEP;
+    constexpr int HW = kDscanSeg;  // k windows in half a stage
     __shared__ __attribute__((aligned(16))) char smem[TD::LDS];
     const int per = a.ntv * a.ntk;
     const int lb = xcd_block(gridDim.x);
@@ -588,10 +592,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_lin_dscan(DscanArgs<T> a) {
         while (c < a.nc && !updates(c)) ++c;
         return c;
     };
-    // stage s of chunk c: the chunk's v and k slices from token s * KSTEP on
+    // stage s of chunk c: the chunk's v and k slices from token s * KSTEP on (PAIR: chunks c and
+    // c + 1, c even, in one stage)
     auto issue = [&](typename TD::Regs& g, int c, int s) {
         const int64_t tok = (int64_t)scan * a.N + (int64_t)c * a.chunk;
-        const int nl = tokens(c);
+        const int nl = PAIR ? (int)std::min<int64_t>(2 * a.chunk, a.N - (int64_t)c * a.chunk) : tokens(c);
         Opnd<T> A[1] = {{a.v + tok * a.dv + r0, a.dv, a.dv - r0, nl}};
         A[0].kscale = a.eta + tok;
         const Opnd<T> B[1] = {{a.k + tok * a.dk + c0, a.dk, a.dk - c0, nl}};
@@ -611,8 +616,51 @@ __global__ __launch_bounds__(kThreads, 1) void k_lin_dscan(DscanArgs<T> a) {
                 dst[(int64_t)(r0 + row) * a.dk + c0 + col] = Elt<T>::st(st[idx]);
         });
     };
+    auto add = [&](const TD& tl) {  // a chunk's update into the state
+        TD::for_each_pos([&](int idx, int, int) {
+            const int i = idx / (TD::FN * 16), j = (idx / 16) % TD::FN, r = idx % 16;
+            const float d = io.dsign * tl.acc[0][i][j][r];
+            for (int k = 0; k < io.reps; ++k) {
+                if (io.mom) {
+                    mm[idx] = io.beta * mm[idx] + d;
+                    st[idx] += mm[idx];
+                } else {
+                    st[idx] += d;
+                }
+            }
+        });
+    };
     TD tl;
     typename TD::Regs g;
+    if constexpr (PAIR) {
+        // one stage per pair of chunks; a pair neither of whose chunks updates is not loaded
+        auto pair_upd = [&](int c) { return c < a.nc && (updates(c) || (c + 1 < a.nc && updates(c + 1))); };
+        auto next_pair = [&](int c) {
+            while (c < a.nc && !pair_upd(c)) c += 2;
+            return c;
+        };
+        TD tl2;
+        int ic = next_pair(0);
+        if (ic < a.nc) issue(g, ic, 0);
+        for (int c = 0; c < a.nc; c += 2) {
+            if (c == ic) {
+                tl.zero();
+                tl2.zero();
+                lds_barrier();  // every wave is done with the previous stage
+                TD::template put<FULL>(g, smem);
+                ic = next_pair(c + 2);
+                if (ic < a.nc) issue(g, ic, 0);
+                lds_barrier();
+                tl.template compute_win<PM1, 0, HW>(smem);
+                tl2.template compute_win<PM1, HW, 2 * HW>(smem);
+            }
+            for (int j = 0; j < 2 && c + j < a.nc; ++j) {
+                if (!post) put(c + j);
+                if (updates(c + j)) add(j ? tl2 : tl);
+                if (post) put(c + j);
+            }
+        }
+    } else {
     int ic = next_upd(0), is = 0;  // the stage in flight in g
     if (ic < a.nc) issue(g, ic, 0);
     for (int c = 0; c < a.nc; ++c) {
@@ -633,20 +681,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_lin_dscan(DscanArgs<T> a) {
                 lds_barrier();
                 tl.template compute<PM1>(smem);
             }
-            TD::for_each_pos([&](int idx, int, int) {
-                const int i = idx / (TD::FN * 16), j = (idx / 16) % TD::FN, r = idx % 16;
-                const float d = io.dsign * tl.acc[0][i][j][r];
-                for (int k = 0; k < io.reps; ++k) {
-                    if (io.mom) {
-                        mm[idx] = io.beta * mm[idx] + d;
-                        st[idx] += mm[idx];
-                    } else {
-                        st[idx] += d;
-                    }
-                }
-            });
+            add(tl);
         }
         if (post) put(c);
+    }
     }
     TD::for_each_pos([&](int idx, int row, int col) {
         if (FULL || (r0 + row < a.dv && c0 + col < a.dk)) {
@@ -966,14 +1004,22 @@ static ttt_status launch_dscan(const linattn_desc& D, int64_t chunk, int64_t nc,
     for (int w = 0; w < 32; ++w) ds.flags[w] = flags[w];
     ds.ntv = (int)cdiv(D.d_v, kDscanTile);
     ds.ntk = (int)cdiv(D.d_k, kDscanTile);
-    // unmasked staging when every tile is whole and every chunk a whole number of stages
-    const bool full = D.d_v % kDscanTile == 0 && D.d_k % kDscanTile == 0 && chunk % DscanTile<T>::KSTEP == 0 &&
-                      D.N % DscanTile<T>::KSTEP == 0;
+    // two chunks to a stage where a chunk is half of one; unmasked staging when every tile is whole
+    // and every stage full
+    constexpr int KS = DscanTile<T>::KSTEP;
+    const bool pair = 2 * chunk == KS;
+    const bool full = D.d_v % kDscanTile == 0 && D.d_k % kDscanTile == 0 && (pair || chunk % KS == 0) && D.N % KS == 0;
     const dim3 grid((unsigned)(S * ds.ntv * ds.ntk));
     {
         ProfScope ps(PK_LIN_SCAN, st);
-        if (full) hipLaunchKernelGGL((k_lin_dscan<T, true>), grid, dim3(kThreads), 0, st, ds);
-        else hipLaunchKernelGGL((k_lin_dscan<T, false>), grid, dim3(kThreads), 0, st, ds);
+        auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, st, ds); };
+        if (pair) {
+            if (full) go(k_lin_dscan<T, true, true>);
+            else go(k_lin_dscan<T, false, true>);
+        } else {
+            if (full) go(k_lin_dscan<T, true, false>);
+            else go(k_lin_dscan<T, false, false>);
+        }
     }
     return check_launch("k_lin_dscan", st);
 }
@@ -982,15 +1028,17 @@ static ttt_status launch_dscan(const linattn_desc& D, int64_t chunk, int64_t nc,
 // 64 x 64 state tiles make at least one workgroup per CU and the chunk updates it keeps out of
 // memory (4 d_v d_k bytes per chunk, written and read back) are at least half of the chunk's k and
 // v bytes; d_k and d_v of 256 at most, where the delta kernel's 128-wide MFMA tiles do not win on
-// arithmetic.  Token-causal blocks (128 tokens) take the two-pass path.  The environment variable
-// TTT_LIN_PASS, read on every call, overrides the choice ("fused" or "split"): both passes give the
-// same bits, so tests run small cases through each.
+// arithmetic.  Token-causal blocks (128 tokens) take it where they go two to a stage (bf16).  The
+// environment variable TTT_LIN_PASS, read on every call, overrides the choice ("fused" or
+// "split"): both passes give the same bits, so tests run small cases through each.
+template <typename T>
 static bool dscan_pays(const linattn_desc& D, int64_t S, int64_t chunk) {
     if (const char* e = getenv("TTT_LIN_PASS")) {
         if (!strcmp(e, "fused")) return true;
         if (!strcmp(e, "split")) return false;
     }
-    if (D.mask == TTT_MASK_TOKEN_CAUSAL || D.d_k > 256 || D.d_v > 256) return false;
+    if (D.d_k > 256 || D.d_v > 256) return false;
+    if (D.mask == TTT_MASK_TOKEN_CAUSAL && 2 * chunk != DscanTile<T>::KSTEP) return false;
     const int64_t wgs = S * cdiv(D.d_v, kDscanTile) * cdiv(D.d_k, kDscanTile);
     return wgs >= 256 && 4 * (int64_t)D.d_v * D.d_k >= chunk * (D.d_k + D.d_v);
 }
@@ -1005,7 +1053,7 @@ static ttt_status run_lin_parallel(const linattn_desc& D, LinArgs<T> a, char* ws
     T* Sc = (T*)(ws + align256((size_t)(S * nc * dvk * 4)));  // kStatePlanes io-dtype planes per chunk
     ttt_status rc;
     const int smode = causal ? TTT_MASK_APPLY_THEN_UPDATE : D.mask;  // a causal block sees the state before it
-    if (!io.between && dscan_pays(D, S, chunk)) {
+    if (!io.between && dscan_pays<T>(D, S, chunk)) {
         // 1 + 2 in one pass
         if ((rc = launch_dscan<T>(D, chunk, nc, smode, a.flags, a.k, a.v, a.eta, Sc, io, st)) != TTT_OK) return rc;
     } else {
@@ -1488,7 +1536,7 @@ ttt_status lin_chunked_bwd(const linattn_desc& D, const uint32_t (&flags)[32], c
         fio.reps = io.reps;
         fio.mom = io.mom;
         fio.beta = io.beta;
-        if (!io.norm && dscan_pays(D, S, chunk)) {
+        if (!io.norm && dscan_pays<T>(D, S, chunk)) {
             rc = launch_dscan<T>(D, chunk, nc, D.mask, flags, k, v, eta, Sc, fio, st);
         } else {
             if ((rc = launch_delta<T, true>(D, chunk, nc, D.mask, flags, k, v, eta, dS, st)) != TTT_OK) return rc;

@@ -503,6 +503,39 @@ struct Tile {
         __builtin_amdgcn_s_setprio(0);
     }
 
+    // compute() over the stage's 32-byte k windows W0 .. W1 - 1 only (k from W0 * 32 / sizeof(T) on)
+    template <class PM, int W0, int W1>
+    __device__ __forceinline__ void compute_win(const char* st) {
+        static_assert(0 <= W0 && W0 < W1 && W1 <= SEG * 2, "windows of one stage");
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int wm = wave / WGN, wn = wave % WGN;
+        const int lrow = lane & 31, lk = (lane >> 5) * 16;
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int win = W0; win < W1; ++win) {
+            u32x4_t af[NA][FM], bfr[NB][FN];
+#pragma unroll
+            for (int a = 0; a < NA; ++a)
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+                    af[a][i] = *reinterpret_cast<const u32x4_t*>(
+                        st + a * A_BYTES + (wm * WM + i * 32 + lrow) * PITCH + win * 32 + lk);
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    bfr[b][j] = *reinterpret_cast<const u32x4_t*>(
+                        st + NA * A_BYTES + b * B_BYTES + (wn * WN + j * 32 + lrow) * PITCH + win * 32 + lk);
+#pragma unroll
+            for (int p = 0; p < NP; ++p)
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) Mma32<T>::mma(acc[p][i][j], af[PM::a[p]][i], bfr[PM::b[p]][j]);
+        }
+        __builtin_amdgcn_s_setprio(0);
+    }
+
     static constexpr int ELEMS = FM * FN * 16;  // accumulator elements per thread and accumulator
 
     // f(int idx, int row, int col) over the positions for_each visits, in the same order

@@ -65,6 +65,12 @@ PASS_CASES = [
     (26, 1, 2, 1024, 128, 128, 256, O.MASK_APPLY_THEN_UPDATE, False, None),  # whole tiles and stages
     (27, 1, 2, 1100, 96, 160, 512, O.MASK_UPDATE_THEN_APPLY, True, None),    # several stages per chunk
     (28, 1, 1, 600, 384, 160, 64, O.MASK_TOKEN_CAUSAL, True, None),
+    # chunks of 128 tokens go two to a 256-token bf16 stage in the fused pass: whole pairs, an odd
+    # chunk count with a ragged last chunk, and strided pairs with one, both or neither updating
+    (29, 1, 2, 1024, 128, 128, 128, O.MASK_UPDATE_THEN_APPLY, True, None),
+    (30, 1, 2, 600, 96, 160, 128, O.MASK_APPLY_THEN_UPDATE, True, None),
+    (31, 1, 2, 1100, 64, 64, 128, O.MASK_STRIDED, True, [1, 0, 0, 0, 1, 1, 0, 1, 1]),
+    (32, 1, 1, 1024, 128, 64, 128, O.MASK_TOKEN_CAUSAL, False, None),
 ]
 
 
