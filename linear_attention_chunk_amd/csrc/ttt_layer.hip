@@ -567,8 +567,9 @@ __global__ __launch_bounds__(kThreads) void k_ns_init(NSArgs<T> a) {
 
 // Gram tiles of TS x TS: one 64-wide LDS stage (37 KB at TS = 128), so three workgroups share a CU
 template <typename T, bool KS, int TS> using NSTile = Tile<T, TS, TS, 2, 2, 1, 1, 1, KS, KS, false, 4, 1>;
-template <typename T> using NSStepTall = Tile<T, 128, 64, 2, 2, 1, 1, 1, false, false>;
-template <typename T> using NSStepWide = Tile<T, 128, 64, 2, 2, 1, 1, 1, false, true>;
+// step tiles: two LDS stages, or (FULL: every tile in range) one stage at three workgroups per CU
+template <typename T, bool FULL> using NSStepTall = Tile<T, 128, 64, 2, 2, 1, 1, 1, false, false, false, 4, FULL ? 1 : 2>;
+template <typename T, bool FULL> using NSStepWide = Tile<T, 128, 64, 2, 2, 1, 1, 1, false, true, false, 4, FULL ? 1 : 2>;
 constexpr int kNSStepRows = 128, kNSStepCols = 64;
 
 // The Gram matrix is symmetric: only its tiles on or above the diagonal are computed (tile t of
@@ -667,10 +668,13 @@ template <> struct NSQuad<float> {
 // The iterate values this thread updates are loaded before the contraction, so their latency hides
 // behind it.  Each position belongs to one tile, so the lo plane is read and rewritten in place;
 // the hi plane is read by every tile's contraction and is written to the other buffer.
-template <typename T>
-__global__ __launch_bounds__(kThreads, 2) void k_ns_step(NSArgs<T> a) {
+// FULL: every tile of the launch lies inside its matrix (d and m multiples of 128); the tiles then
+// take one LDS stage and three workgroups share a CU, so that one workgroup's pipeline fill and
+// epilogue overlap the others' contractions.
+template <typename T, bool FULL>
+__global__ __launch_bounds__(kThreads, FULL ? 3 : 2) void k_ns_step(NSArgs<T> a) {
     constexpr bool kLo = sizeof(T) == 2;
-    __shared__ __attribute__((aligned(16))) char smem[NSStepTall<T>::LDS];
+    __shared__ __attribute__((aligned(16))) char smem[NSStepTall<T, FULL>::LDS];
     const int64_t dm = (int64_t)a.d * a.m;
     const int per = a.nmat * a.tiles;
     const int lb = xcd_block(gridDim.x);
@@ -697,7 +701,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_ns_step(NSArgs<T> a) {
     };
     auto body = [&](auto& tl, const auto& A, const auto& B, int K) {
         using TT = typename std::remove_reference<decltype(tl)>::type;
-        if (r0 + TT::BM <= r && c0 + TT::BN <= c) {
+        if (FULL || (r0 + TT::BM <= r && c0 + TT::BN <= c)) {
             // full tiles: rows gathered in LDS, the iterate read and written four elements at a time
             static_assert(TT::RV_LDS <= (int)sizeof(smem), "row bands fit the tile's LDS");
             NSQuad<T> xv[TT::RV_N];
@@ -714,7 +718,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_ns_step(NSArgs<T> a) {
                 if (Xf) *reinterpret_cast<float4*>(Xf + e) = xn;
                 else NSQuad<T>::store(Xo, Xl, e, xn);
             });
-        } else {
+        } else if constexpr (!FULL) {
             // partial tiles, element by element; a position outside the matrix reads the corner and
             // is not stored
             float xv[TT::ELEMS];
@@ -743,16 +747,25 @@ __global__ __launch_bounds__(kThreads, 2) void k_ns_step(NSArgs<T> a) {
         }
     };
     if (r > c) {  // P = X Gram; Gram is symmetric, so its rows serve as the B operand
-        NSStepTall<T> tl;
+        NSStepTall<T, FULL> tl;
         const Opnd<T> A[1] = {{X + (int64_t)r0 * c, c, r - r0, c}};
         const Opnd<T> B[1] = {{Gm + (int64_t)c0 * p, p, c - c0, p}};
         body(tl, A, B, c);
     } else {      // P = Gram X; B[j][i] = X[i][j] is read k-strided
-        NSStepWide<T> tl;
+        NSStepWide<T, FULL> tl;
         const Opnd<T> A[1] = {{Gm + (int64_t)r0 * p, p, r - r0, p}};
         const Opnd<T> B[1] = {{X + c0, c, c - c0, r}};
         body(tl, A, B, r);
     }
+}
+
+// The step over grid tiles, with the full-tile workgroups when every tile lies inside its matrix
+template <typename T>
+static void launch_ns_step(const NSArgs<T>& na, unsigned grid, hipStream_t st) {
+    if (na.d % 128 == 0 && na.m % 128 == 0)
+        hipLaunchKernelGGL((k_ns_step<T, true>), dim3(grid), dim3(kThreads), 0, st, na);
+    else
+        hipLaunchKernelGGL((k_ns_step<T, false>), dim3(grid), dim3(kThreads), 0, st, na);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1005,7 +1018,7 @@ static ttt_status par_muon_between(void* ctx, float* dS, const float** src, hipS
         na.tiles = stt;
         {
             ProfScope ps(PK_NS_STEP, st);
-            hipLaunchKernelGGL(k_ns_step<T>, dim3((unsigned)(nmx * stt)), dim3(kThreads), 0, st, na);
+            launch_ns_step<T>(na, (unsigned)(nmx * stt), st);
         }
         if ((rc = check_launch("k_ns_step", st)) != TTT_OK) return rc;
     }
@@ -1327,7 +1340,7 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
                     na.tiles = stt;
                     {
                         ProfScope ps(PK_NS_STEP, st);
-                        hipLaunchKernelGGL(k_ns_step<T>, dim3(S * nmat * stt), dim3(kThreads), 0, st, na);
+                        launch_ns_step<T>(na, (unsigned)(S * nmat * stt), st);
                     }
                     if ((rc = check_launch("k_ns_step", st)) != TTT_OK) return rc;
                 }
@@ -1410,7 +1423,7 @@ ttt_status ns_steps(const ttt_desc& D, T* X, T* Xlo, T* P, hipStream_t st) {
         na.tiles = stt;
         {
             ProfScope ps(PK_NS_STEP, st);
-            hipLaunchKernelGGL(k_ns_step<T>, dim3(S * nmat * stt), dim3(kThreads), 0, st, na);
+            launch_ns_step<T>(na, (unsigned)(S * nmat * stt), st);
         }
         if ((rc = check_launch("k_ns_step", st)) != TTT_OK) return rc;
     }
