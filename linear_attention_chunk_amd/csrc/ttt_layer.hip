@@ -567,7 +567,7 @@ __global__ __launch_bounds__(kThreads) void k_ns_init(NSArgs<T> a) {
 
 // Gram tiles of TS x TS: one 64-wide LDS stage (37 KB at TS = 128), so three workgroups share a CU
 template <typename T, bool KS, int TS> using NSTile = Tile<T, TS, TS, 2, 2, 1, 1, 1, KS, KS, false, 4, 1>;
-// step tiles: two LDS stages, or (FULL: every tile in range) one stage at three workgroups per CU
+// step tiles: two LDS stages, or (FULL: every tile in range) one stage at four workgroups per CU
 template <typename T, bool FULL> using NSStepTall = Tile<T, 128, 64, 2, 2, 1, 1, 1, false, false, false, 4, FULL ? 1 : 2>;
 template <typename T, bool FULL> using NSStepWide = Tile<T, 128, 64, 2, 2, 1, 1, 1, false, true, false, 4, FULL ? 1 : 2>;
 constexpr int kNSStepRows = 128, kNSStepCols = 64;
@@ -669,10 +669,10 @@ template <> struct NSQuad<float> {
 // behind it.  Each position belongs to one tile, so the lo plane is read and rewritten in place;
 // the hi plane is read by every tile's contraction and is written to the other buffer.
 // FULL: every tile of the launch lies inside its matrix (d and m multiples of 128); the tiles then
-// take one LDS stage and three workgroups share a CU, so that one workgroup's pipeline fill and
-// epilogue overlap the others' contractions.
+// take one LDS stage, read the iterate in the epilogue, and four workgroups share a CU, so that one
+// workgroup's pipeline fill and epilogue overlap the others' contractions.
 template <typename T, bool FULL>
-__global__ __launch_bounds__(kThreads, FULL ? 3 : 2) void k_ns_step(NSArgs<T> a) {
+__global__ __launch_bounds__(kThreads, FULL ? 4 : 2) void k_ns_step(NSArgs<T> a) {
     constexpr bool kLo = sizeof(T) == 2;
     __shared__ __attribute__((aligned(16))) char smem[NSStepTall<T, FULL>::LDS];
     const int64_t dm = (int64_t)a.d * a.m;
@@ -703,15 +703,21 @@ __global__ __launch_bounds__(kThreads, FULL ? 3 : 2) void k_ns_step(NSArgs<T> a)
         using TT = typename std::remove_reference<decltype(tl)>::type;
         if (FULL || (r0 + TT::BM <= r && c0 + TT::BN <= c)) {
             // full tiles: rows gathered in LDS, the iterate read and written four elements at a time
+            // (FULL: the iterate is read in the epilogue, which the other workgroups on the CU hide;
+            // else it is loaded before the contraction)
             static_assert(TT::RV_LDS <= (int)sizeof(smem), "row bands fit the tile's LDS");
-            NSQuad<T> xv[TT::RV_N];
-            TT::rows_via_lds_pos([&](int idx, int, int row, int col) {
-                xv[idx].load(Xh, Xl, (uint32_t)row * (uint32_t)c + (uint32_t)col);
-            });
+            NSQuad<T> xv[FULL ? 1 : TT::RV_N];
+            if constexpr (!FULL)
+                TT::rows_via_lds_pos([&](int idx, int, int row, int col) {
+                    xv[idx].load(Xh, Xl, (uint32_t)row * (uint32_t)c + (uint32_t)col);
+                });
             tl.template run<PM1>(A, B, K, smem);
             const float sc = scale();
             tl.rows_via_lds(smem, [&](int idx, int, int row, int col, const float4& v) {
-                const float4 x = xv[idx].value();
+                NSQuad<T> xq;
+                if constexpr (FULL) xq.load(Xh, Xl, (uint32_t)row * (uint32_t)c + (uint32_t)col);
+                else xq = xv[idx];
+                const float4 x = xq.value();
                 const float4 xn = make_float4(sc * (1.5f * x.x - 0.5f * v.x), sc * (1.5f * x.y - 0.5f * v.y),
                                               sc * (1.5f * x.z - 0.5f * v.z), sc * (1.5f * x.w - 0.5f * v.w));
                 const uint32_t e = (uint32_t)row * (uint32_t)c + (uint32_t)col;
