@@ -565,7 +565,7 @@ __global__ __launch_bounds__(kThreads) void k_ns_init(NSArgs<T> a) {
     }
 }
 
-// Gram tiles of TS x TS: one 64-wide LDS stage (37 KB at TS = 128), so three workgroups share a CU
+// Gram tiles of TS x TS: one 64-wide LDS stage (18 KB at TS = 64)
 template <typename T, bool KS, int TS> using NSTile = Tile<T, TS, TS, 2, 2, 1, 1, 1, KS, KS, false, 4, 1>;
 // step tiles: two LDS stages, or (FULL: every tile in range) one stage at four workgroups per CU
 template <typename T, bool FULL> using NSStepTall = Tile<T, 128, 64, 2, 2, 1, 1, 1, false, false, false, 4, FULL ? 1 : 2>;
@@ -574,10 +574,10 @@ constexpr int kNSStepRows = 128, kNSStepCols = 64;
 
 // The Gram matrix is symmetric: only its tiles on or above the diagonal are computed (tile t of
 // np (np + 1) / 2, row-major over the upper triangle), and an off-diagonal tile also writes its
-// mirror block, transposed through LDS so that those stores are whole rows as well.  Tiles are
-// TS = 128 wide, or 64 when the 128-wide ones would leave most CUs idle (few, small matrices).
+// mirror block, transposed through LDS so that those stores are whole rows as well.  The launch
+// takes TS = 64 (launch_ns_gram).
 template <typename T, int TS>
-__global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 3 : 2) void k_ns_gram(NSArgs<T> a) {  // fp32: 67 KB LDS
+__global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 3 : 2) void k_ns_gram(NSArgs<T> a) {
     constexpr int kTP = TS + 16 / (int)sizeof(T);  // transposed-tile pitch (elements)
     constexpr int LDSB = std::max(NSTile<T, false, TS>::LDS, TS * kTP * (int)sizeof(T));
     __shared__ __attribute__((aligned(16))) char smem[LDSB];
@@ -763,6 +763,18 @@ __global__ __launch_bounds__(kThreads, FULL ? 4 : 2) void k_ns_step(NSArgs<T> a)
         const Opnd<T> B[1] = {{X + c0, c, c - c0, r}};
         body(tl, A, B, r);
     }
+}
+
+// The Gram matrices of nmats matrices (sets na.tiles).  64 x 64 tiles: 64 VGPRs and 18 KB of LDS, so
+// up to eight workgroups share a CU and hide each other's pipeline fill and epilogue; 128 x 128 tiles
+// carry twice the MFMA work per operand byte but fit only three per CU, and were slower even at the
+// LaCT LM shape (2.92 against 2.73 ms per call).
+template <typename T>
+static void launch_ns_gram(NSArgs<T> na, int64_t nmats, hipStream_t st) {
+    constexpr int TS = 64;
+    const int np = (int)cdiv(std::min(na.d, na.m), TS);
+    na.tiles = np * (np + 1) / 2;
+    hipLaunchKernelGGL((k_ns_gram<T, TS>), dim3((unsigned)(nmats * na.tiles)), dim3(kThreads), 0, st, na);
 }
 
 // The step over grid tiles, with the full-tile workgroups when every tile lies inside its matrix
@@ -1005,20 +1017,15 @@ static ttt_status par_muon_between(void* ctx, float* dS, const float** src, hipS
     const int64_t p = std::min(d, m);
     NSArgs<T> na{nullptr, 0, nullptr, L.nblk, first, Xb[0], Xlo, nullptr, dm, (T*)(c.ws + L.gram), p * p, (int)d,
                  (int)m, 2, 1, 0, 2};
-    const bool gsmall = nmx * cdiv(p, 128) * (cdiv(p, 128) + 1) / 2 < 256;
-    const int gts = gsmall ? 64 : 128;
-    const int gt = (int)(cdiv(p, gts) * (cdiv(p, gts) + 1) / 2);
     const int stt = (int)std::max(cdiv(m, kNSStepRows) * cdiv(d, kNSStepCols), cdiv(d, kNSStepRows) * cdiv(m, kNSStepCols));
     for (int it = 0; it < D.ns_iters; ++it) {
         na.Xin = it == 0 ? first : Xb[(it - 1) & 1];
         na.Xout = Xb[it & 1];
         na.part = it == 0 ? part : nullptr;
         na.Xf = (sizeof(T) == 2 && it == D.ns_iters - 1) ? Xf : nullptr;
-        na.tiles = gt;
         {
             ProfScope ps(PK_NS_GRAM, st);
-            if (gsmall) hipLaunchKernelGGL((k_ns_gram<T, 64>), dim3((unsigned)(nmx * gt)), dim3(kThreads), 0, st, na);
-            else hipLaunchKernelGGL((k_ns_gram<T, 128>), dim3((unsigned)(nmx * gt)), dim3(kThreads), 0, st, na);
+            launch_ns_gram<T>(na, nmx, st);
         }
         if ((rc = check_launch("k_ns_gram", st)) != TTT_OK) return rc;
         na.tiles = stt;
@@ -1324,10 +1331,6 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
                 NSArgs<T> na{nullptr, 0, nullptr, L.nblk, first, Xb[0], Xlo, nullptr, L.x_stride, (T*)(ws + L.gram),
                              L.gram_stride, d, m, mat0, nmat, 0};
                 const int p = d < m ? d : m;
-                // upper-triangle Gram tiles of 128, or of 64 when the 128-wide ones fill under 256 CUs
-                const bool gsmall = (int64_t)S * nmat * cdiv(p, 128) * (cdiv(p, 128) + 1) / 2 < 256;
-                const int gts = gsmall ? 64 : 128;
-                const int gt = (int)(cdiv(p, gts) * (cdiv(p, gts) + 1) / 2);
                 // step tiles: the larger of the tall (m x d) and wide (d x m) tilings
                 const int stt = (int)std::max(cdiv(m, kNSStepRows) * cdiv(d, kNSStepCols),
                                               cdiv(d, kNSStepRows) * cdiv(m, kNSStepCols));
@@ -1336,11 +1339,9 @@ static ttt_status run_ttt(const ttt_desc& D, const Layout& L, const T* q, const 
                     na.Xout = Xb[it & 1];
                     na.part = it == 0 ? part : nullptr;
                     na.Xf = (sizeof(T) == 2 && it == D.ns_iters - 1) ? Xf : nullptr;
-                    na.tiles = gt;
                     {
                         ProfScope ps(PK_NS_GRAM, st);
-                        if (gsmall) hipLaunchKernelGGL((k_ns_gram<T, 64>), dim3(S * nmat * gt), dim3(kThreads), 0, st, na);
-                        else hipLaunchKernelGGL((k_ns_gram<T, 128>), dim3(S * nmat * gt), dim3(kThreads), 0, st, na);
+                        launch_ns_gram<T>(na, (int64_t)S * nmat, st);
                     }
                     if ((rc = check_launch("k_ns_gram", st)) != TTT_OK) return rc;
                     na.tiles = stt;
@@ -1411,18 +1412,14 @@ ttt_status ns_steps(const ttt_desc& D, T* X, T* Xlo, T* P, hipStream_t st) {
     const int mat0 = D.last_layer_only ? 2 : 0, nmat = D.last_layer_only ? 1 : 3;
     const int nblk = (int)cdiv(dm, kPrepElems);
     ttt_status rc;
-    const bool gsmall = (int64_t)S * nmat * cdiv(p, 128) * (cdiv(p, 128) + 1) / 2 < 256;
-    const int gts = gsmall ? 64 : 128;
-    const int gt = (int)(cdiv(p, gts) * (cdiv(p, gts) + 1) / 2);
     const int stt = (int)std::max(cdiv(m, kNSStepRows) * cdiv(d, kNSStepCols), cdiv(d, kNSStepRows) * cdiv(m, kNSStepCols));
     const int64_t xs = (int64_t)S * 3 * dm, ps_ = (int64_t)S * 3 * p * p;
     for (int k = 0; k < D.ns_iters; ++k) {
         NSArgs<T> na{nullptr, 0, nullptr, nblk, X + k * xs, k + 1 < D.ns_iters ? X + (k + 1) * xs : nullptr,
-                     sizeof(T) == 2 ? Xlo : nullptr, nullptr, 3 * dm, P + k * ps_, 3 * p * p, d, m, mat0, nmat, gt, 0};
+                     sizeof(T) == 2 ? Xlo : nullptr, nullptr, 3 * dm, P + k * ps_, 3 * p * p, d, m, mat0, nmat, 0, 0};
         {
             ProfScope ps(PK_NS_GRAM, st);
-            if (gsmall) hipLaunchKernelGGL((k_ns_gram<T, 64>), dim3(S * nmat * gt), dim3(kThreads), 0, st, na);
-            else hipLaunchKernelGGL((k_ns_gram<T, 128>), dim3(S * nmat * gt), dim3(kThreads), 0, st, na);
+            launch_ns_gram<T>(na, (int64_t)S * nmat, st);
         }
         if ((rc = check_launch("k_ns_gram", st)) != TTT_OK) return rc;
         if (k + 1 == D.ns_iters) break;  // the last iterate is not needed

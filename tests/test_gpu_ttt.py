@@ -110,11 +110,11 @@ def test_tall_and_wide_muon_fp32():
 
 
 def test_muon_gram_mirror_fp32():
-    # p = min(d, m) = 160 spans two 128-wide Gram tiles, the second partial: the off-diagonal tile
-    # also writes its mirror block; both Gram sides (m > d, then d > m)
+    # p = min(d, m) = 160 spans three 64-wide Gram tiles, the last partial: the off-diagonal tiles
+    # also write their mirror blocks; both Gram sides (m > d, then d > m)
     run_small(12, 1, 1, 256, 160, 320, 128, O.MASK_APPLY_THEN_UPDATE, O.UPD_MUON_L2, False, ns=3)
     run_small(13, 1, 1, 256, 320, 160, 128, O.MASK_UPDATE_THEN_APPLY, O.UPD_MUON, False, ns=2)
-    # 32 scans: enough 128-wide Gram tiles that the kernel keeps them (fewer scans take 64-wide ones)
+    # 32 scans in one launch (each XCD takes a contiguous range of the blocks)
     run_small(21, 8, 4, 128, 160, 320, 128, O.MASK_APPLY_THEN_UPDATE, O.UPD_MUON_L2, False, ns=2)
 
 
@@ -123,6 +123,14 @@ def test_newton_schulz_tiles_bf16():
     # with full 128 x 64 step tiles beside ragged ones; the iterate is the bf16 hi + lo pair
     run_small(24, 1, 1, 256, 160, 320, 128, O.MASK_APPLY_THEN_UPDATE, O.UPD_MUON_L2, True, ns=3)
     run_small(25, 1, 2, 300, 160, 320, 128, O.MASK_UPDATE_THEN_APPLY, O.UPD_MUON, True, momentum=0.9, ns=5)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_newton_schulz_full_step_tiles(bf16):
+    # d and m multiples of 128: every step tile lies inside its matrix, and the step runs its
+    # full-tile workgroups (one LDS stage, the iterate read in the epilogue); both orientations
+    run_small(40, 1, 2, 300, 128, 256, 128, O.MASK_APPLY_THEN_UPDATE, O.UPD_MUON_L2, bf16, momentum=0.9, ns=5)
+    run_small(41, 2, 1, 256, 256, 128, 128, O.MASK_UPDATE_THEN_APPLY, O.UPD_MUON, bf16, ns=3)
 
 
 @pytest.mark.parametrize("bf16", [False, True])
