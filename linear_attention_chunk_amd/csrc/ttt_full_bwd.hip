@@ -632,10 +632,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_nsb_q(NsbArgs<T> a) {
     }
 }
 
-template <typename T>
-__global__ __launch_bounds__(kThreads, 2) void k_nsb_step(NsbArgs<T> a) {
-    using TW = Tile<T, kNsbRows, kNsbCols, 2, 2, 1, 1, 1, false, true, false, 4, 2>;   // B k-strided
-    using TT = Tile<T, kNsbRows, kNsbCols, 2, 2, 1, 1, 1, false, false, false, 4, 2>;  // B symmetric rows
+// FULL: every tile lies inside its matrix (d and m multiples of 128); the tiles then take one LDS
+// stage and four workgroups share a CU, so that one workgroup's pipeline fill and epilogue overlap
+// the others' contractions (the forward's Newton-Schulz step does the same)
+template <typename T, bool FULL>
+__global__ __launch_bounds__(kThreads, FULL ? 4 : 2) void k_nsb_step(NsbArgs<T> a) {
+    using TW = Tile<T, kNsbRows, kNsbCols, 2, 2, 1, 1, 1, false, true, false, 4, FULL ? 1 : 2>;   // B k-strided
+    using TT = Tile<T, kNsbRows, kNsbCols, 2, 2, 1, 1, 1, false, false, false, 4, FULL ? 1 : 2>;  // B symmetric rows
     constexpr int LDSB = std::max(TW::LDS, TT::LDS);
     __shared__ __attribute__((aligned(16))) char smem[LDSB];
     const int per = a.nmat * a.tiles;
@@ -659,7 +662,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_nsb_step(NsbArgs<T> a) {
     T* Os = a.Gsout + mo;
     auto out = [&](auto& tl) {
         tl.for_each([&](const float (&v)[1], int row, int col) {
-            if (r0 + row < r && c0 + col < c) {
+            if (FULL || (r0 + row < r && c0 + col < c)) {
                 const int64_t e = (int64_t)(r0 + row) * c + c0 + col;
                 const float x = 1.5f * G[e] - 0.5f * v[0];
                 O[e] = x;
@@ -674,6 +677,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_nsb_step(NsbArgs<T> a) {
         const Opnd<T> A1[1] = {{P + (int64_t)r0 * p, p, r - r0, p}};
         const Opnd<T> B1[1] = {{Gs + c0, c, c - c0, r}};
         tl.template run<PM1>(A0, B0, r, smem);
+        if (FULL) lds_barrier();  // one LDS stage: every wave is done with the first product's last stage
         tl.template run<PM1>(A1, B1, r, smem, true);
         out(tl);
     } else {       // G P + X (Q + Q^T): P and Q + Q^T are symmetric, so their rows serve as B
@@ -683,6 +687,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_nsb_step(NsbArgs<T> a) {
         const Opnd<T> A1[1] = {{X + (int64_t)r0 * c, c, r - r0, c}};
         const Opnd<T> B1[1] = {{Q + (int64_t)c0 * p, p, c - c0, p}};
         tl.template run<PM1>(A0, B0, c, smem);
+        if (FULL) lds_barrier();  // one LDS stage: every wave is done with the first product's last stage
         tl.template run<PM1>(A1, B1, c, smem, true);
         out(tl);
     }
@@ -1060,7 +1065,9 @@ ttt_status run_full_backward(const ttt_desc& D, const T* q, const T* k, const T*
             na.tiles = stt;
             {
                 ProfScope ps(PK_FB_NSB, st);
-                hipLaunchKernelGGL(k_nsb_step<T>, dim3((unsigned)((int64_t)S * nmat * stt)), dim3(kThreads), 0, st, na);
+                const dim3 grid((unsigned)((int64_t)S * nmat * stt));
+                if (d % 128 == 0 && m % 128 == 0) hipLaunchKernelGGL((k_nsb_step<T, true>), grid, dim3(kThreads), 0, st, na);
+                else hipLaunchKernelGGL((k_nsb_step<T, false>), grid, dim3(kThreads), 0, st, na);
             }
             if ((r = check_launch("k_nsb_step", st)) != TTT_OK) return r;
             std::swap(Gc, Gn);

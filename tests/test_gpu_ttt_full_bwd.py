@@ -218,6 +218,14 @@ def test_muon_orientations_and_small_shapes(bf16):
     run(18, 1, 2, 130, 128, 64, 130, O.MASK_FULL, bf16, rule=O.UPD_GD_L2, momentum=0.5)
 
 
+@pytest.mark.parametrize("bf16", [False, True])
+def test_muon_full_step_tiles(bf16):
+    # d and m multiples of 128: the walk back's step tiles all lie inside their matrices and run the
+    # full-tile workgroups (one LDS stage); W1, W3 tall and W2 wide, then the other way round
+    run(22, 1, 2, 300, 128, 256, 128, O.MASK_APPLY_THEN_UPDATE, bf16, rule=O.UPD_MUON_L2, momentum=0.9)
+    run(23, 1, 1, 256, 256, 128, 128, O.MASK_UPDATE_THEN_APPLY, bf16, rule=O.UPD_MUON)
+
+
 def test_muon_weight_layouts_and_empty():
     run(19, 2, 2, 260, 64, 128, 128, O.MASK_APPLY_THEN_UPDATE, True, rule=O.UPD_MUON_L2, momentum=0.9,
         per_batch=True)
