@@ -585,10 +585,11 @@ template <typename T> struct NsbArgs {
     int d, m, mat0, nmat, tiles;     // tiles per matrix
 };
 
+// one LDS stage (37 KB), so that four workgroups share a CU and hide each other's pipeline fill
 template <typename T>
-__global__ __launch_bounds__(kThreads, 2) void k_nsb_q(NsbArgs<T> a) {
-    using TW = Tile<T, kNsbQ, kNsbQ, 2, 2, 2, 2, 2, false, false, false, 4, 2>;
-    using TT = Tile<T, kNsbQ, kNsbQ, 2, 2, 2, 2, 2, true, true, false, 4, 2>;
+__global__ __launch_bounds__(kThreads, 4) void k_nsb_q(NsbArgs<T> a) {
+    using TW = Tile<T, kNsbQ, kNsbQ, 2, 2, 2, 2, 2, false, false, false, 4, 1>;
+    using TT = Tile<T, kNsbQ, kNsbQ, 2, 2, 2, 2, 2, true, true, false, 4, 1>;
     constexpr int LDSB = std::max(TW::LDS, TT::LDS);
     __shared__ __attribute__((aligned(16))) char smem[LDSB];
     const int per = a.nmat * a.tiles;
