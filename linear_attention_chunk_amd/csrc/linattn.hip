@@ -416,8 +416,8 @@ template <typename T> struct DeltaArgs {
 constexpr int kDeltaRows = 128, kDeltaCols = 128;
 
 template <typename T, bool SCALE = true>
-__global__ __launch_bounds__(kThreads, 2) void k_lin_delta(DeltaArgs<T> a) {
-    using TD = Tile<T, kDeltaRows, kDeltaCols, 2, 2, 1, 1, 1, true, true, SCALE>;
+__global__ __launch_bounds__(kThreads, 3) void k_lin_delta(DeltaArgs<T> a) {
+    using TD = Tile<T, kDeltaRows, kDeltaCols, 2, 2, 1, 1, 1, true, true, SCALE, 4, 1>;  // one LDS stage, three per CU
     __shared__ __attribute__((aligned(16))) char smem[TD::LDS];
     const int lb = xcd_block(gridDim.x);
     const int per = a.ntv * a.ntk;
@@ -705,9 +705,10 @@ template <typename T> struct ApplyArgs {
 constexpr int kApplyRows = 128, kApplyCols = 128;
 
 template <typename T>
-__global__ __launch_bounds__(kThreads, 2) void k_lin_apply(ApplyArgs<T> a) {
+__global__ __launch_bounds__(kThreads, 3) void k_lin_apply(ApplyArgs<T> a) {
     constexpr int PLANES = kStatePlanes;
-    using TA = Tile<T, kApplyRows, kApplyCols, 2, 2, 1, PLANES, PLANES, false, false>;  // 64-wide stages
+    // 64-wide k-steps in one LDS stage (37 KB), three workgroups per CU
+    using TA = Tile<T, kApplyRows, kApplyCols, 2, 2, 1, PLANES, PLANES, false, false, false, 4, 1>;
     using PM = typename std::conditional<PLANES == 2, PMQ, PM1>::type;
     __shared__ __attribute__((aligned(16))) char smem[TA::LDS];
     const int lb = xcd_block(gridDim.x);
